@@ -1,0 +1,362 @@
+"""Pins of the CPU checker against values fixed by the pages' formats and by mathematics.
+
+Each test ties one oracle function to something other than itself: hand-derived
+fixtures under tests/golden/, numpy's IEEE binary16 conversion, closed forms,
+exact integer matrix products, invariants (scaling, permutation, error bounds)
+and brute force on tiny inputs.  None needs a GPU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from block_quantized_few_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _rng_normal(shape, sigma, seed):
+    return synth.gaussian(shape, sigma, seed).numpy()
+
+
+# --------------------------------------------------------------- fp16 ---
+def test_f16_decode_all_patterns_match_numpy():
+    h = np.arange(1 << 16, dtype=np.uint16)
+    ours = O.f16_to_f32(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_encode_matches_numpy_rne():
+    # every half value, every midpoint between neighbours (ties) and their fp32 neighbours
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    v = h.view(np.float16).astype(np.float64)
+    mids = (v[:-1] + v[1:]) / 2
+    cand = np.concatenate([v, mids, -v, -mids]).astype(np.float32)
+    cand = np.concatenate([cand, np.nextafter(cand, np.float32(np.inf)), np.nextafter(cand, np.float32(-np.inf))])
+    cand = np.concatenate([cand, _rng_normal((20000,), 3.0, 11), np.float32([65519.0, 65520.0, 1e-8, 6e-8])])
+    cand = cand[np.abs(cand) < 65520.0]
+    ours, ov = O.f32_to_f16(cand)
+    assert not ov
+    ref = cand.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_f16_encode_overflow_flags():
+    out, ov = O.f32_to_f16(np.float32([65520.0]))
+    assert ov and out[0] == 0x7C00
+
+
+# ---------------------------------------------------- weight quantizers ---
+@pytest.mark.parametrize("fmt,name", [(O.Q8_0, "q8_0_pow2_blocks.json"), (O.Q4_0, "q4_0_pow2_blocks.json")])
+def test_weight_quantizer_golden(fmt, name):
+    g = _gold(name)
+    for case in g["cases"]:
+        w = (np.array(case["k"], np.float64) * 2.0 ** g["scale_exp2"]).astype(np.float32)[None, :]
+        blk = O.quantize_weights(fmt, w)[0, 0]
+        d16 = int(blk[0]) | (int(blk[1]) << 8)
+        assert d16 == int(case["d16"], 16)
+        if fmt == O.Q8_0:
+            assert list(blk[2:].view(np.int8)) == case["codes"]
+        else:
+            assert [int(b) for b in blk[2:]] == [int(b, 16) for b in case["bytes"]]
+        deq = O.dequantize(fmt, blk[None, None, :], 1, 32)[0]
+        assert list(deq / 2.0 ** g["scale_exp2"] if d16 else deq) == [float(c) for c in case["codes"]]
+
+
+@pytest.mark.parametrize("fmt,qmax", [(O.Q8_0, 127), (O.Q4_0, 7)])
+def test_weight_quantizer_invariants(fmt, qmax):
+    n, k = 64, 256
+    w = _rng_normal((n, k), 0.02, 21)
+    w[3, 32:64] = 0.0  # an all-zero block
+    blocks = O.quantize_weights(fmt, w)
+    deq = O.dequantize(fmt, blocks, n, k)
+    d = O.f16_to_f32(blocks[:, :, 0].astype(np.uint16) | (blocks[:, :, 1].astype(np.uint16) << 8)).astype(np.float64)
+    codes = np.round(deq / np.where(d == 0, 1, d).repeat(32, axis=1))
+    # the largest code of every nonzero block is +-qmax; errors within half a step (+ clamp slack)
+    amax_code = np.abs(codes).reshape(n, k // 32, 32).max(axis=2)
+    nz = d > 0
+    assert np.all(amax_code[nz] == qmax)
+    assert np.all(d[~nz] == 0) and np.all(deq[3, 32:64] == 0)
+    err = np.abs(deq - w.astype(np.float64)).reshape(n, k // 32, 32).max(axis=2)
+    assert np.all(err <= d * 0.5 + 1e-12 + d * qmax * 2.0 ** -10)
+    # scale is fp16(amax/qmax): within half an fp16 ulp of amax/qmax
+    amax = np.abs(w).reshape(n, k // 32, 32).max(axis=2).astype(np.float64)
+    assert np.all(np.abs(d - amax / qmax) <= (amax / qmax) * 2.0 ** -11 * 1.0001)
+
+
+# ------------------------------------------------ activation quantizer ---
+def test_act_quantizer_golden():
+    g = _gold("q8_acts_blocks.json")
+    tiny = np.float32(2.0 ** -149)
+    for case in g["cases"]:
+        if "x" in case:
+            x = np.array(case["x"], np.float32)
+            d = np.float32(case["d"])
+        else:
+            x = np.array(case["x_units_2m149"], np.float32) * tiny
+            d = np.float32(case["d_units_2m149"]) * tiny
+        qx, dx, sx = O.quantize_acts(x[None, :])
+        assert list(qx[0]) == case["q"], case["name"]
+        assert dx[0, 0].view(np.uint32) == d.view(np.uint32), case["name"]
+        assert sx[0, 0] == sum(case["q"])
+
+
+def test_act_quantizer_invariants():
+    rows, k = 4, 4096
+    x = synth.gaussian_outliers((rows, k), 1.0, 31).numpy()
+    qx, dx, sx = O.quantize_acts(x)
+    q = qx.astype(np.int64).reshape(rows, k // 32, 32)
+    xb = x.reshape(rows, k // 32, 32).astype(np.float64)
+    d = dx.astype(np.float64)[..., None]
+    assert np.all(np.abs(q).max(axis=2) == 127)  # the amax element always lands on +-127
+    assert np.all(np.abs(q * d - xb) <= d * 0.5 * (1 + 1e-6))
+    assert np.array_equal(sx, q.sum(axis=2))
+    # scale invariance: x * 2^j gives the same codes and d * 2^j exactly
+    for j in (-20, -3, 5, 40):
+        qx2, dx2, _ = O.quantize_acts((x.astype(np.float64) * 2.0 ** j).astype(np.float32))
+        assert np.array_equal(qx2, qx)
+        assert np.array_equal(dx2, (dx.astype(np.float64) * 2.0 ** j).astype(np.float32))
+
+
+# ---------------------------------------------------------- block dots ---
+def _unpack_codes(fmt, blocks):
+    """Independent unpacking of canonical blocks into signed codes [n][k]."""
+    n, nb, _ = blocks.shape
+    if fmt == O.Q8_0:
+        return blocks[:, :, 2:].view(np.int8).astype(np.int64).reshape(n, nb * 32)
+    p = blocks[:, :, 2:].astype(np.int64)
+    c = np.concatenate([p & 0xF, p >> 4], axis=2)
+    return (c - 8).reshape(n, nb * 32)
+
+
+def test_blockdots_hand():
+    a, c = np.float32(0.37), np.float32(2.5)
+    ones = np.ones(32, np.float32)
+    alt = np.tile(np.float32([1, -1]), 16)
+    spike = np.zeros(32, np.float32)
+    spike[5] = a
+    xs = np.zeros(32, np.float32)
+    xs[0], xs[5] = 127, 50
+    cases = {
+        "q8 all max": (O.Q8_0, a * ones, c * ones),
+        "q8 alternating vs all max": (O.Q8_0, a * alt, c * ones),
+        "q8 spike": (O.Q8_0, spike, xs),
+        "q4 all max": (O.Q4_0, a * ones, c * ones),
+        "q4 all min": (O.Q4_0, -a * ones, c * ones),
+    }
+    expect = {case["name"]: case["expect"] for case in _gold("blockdots_hand.json")["cases"]}
+    for name, (fmt, w, x) in cases.items():
+        blocks = O.quantize_weights(fmt, w[None, :])
+        qx, _, _ = O.quantize_acts(x[None, :])
+        assert O.blockdots(fmt, blocks, 1, 32, qx)[0, 0, 0] == expect[name], name
+    # a Q4_0 block made by hand with every nibble 0 (code -8), against q_x = -127
+    blk = np.zeros((1, 1, 18), np.uint8)
+    blk[0, 0, 0:2] = (0x00, 0x3C)  # d = 1.0
+    qx, _, _ = O.quantize_acts((-c * ones)[None, :])
+    assert O.blockdots(O.Q4_0, blk, 1, 32, qx)[0, 0, 0] == expect["q4 code zero"]
+
+
+@pytest.mark.parametrize("fmt", [O.Q8_0, O.Q4_0])
+def test_blockdots_brute_force_and_offset_fold(fmt):
+    for seed, (n, k, rows) in enumerate([(1, 32, 1), (3, 64, 2), (8, 128, 5), (5, 96, 16)]):
+        w = _rng_normal((n, k), 0.02, 100 + seed)
+        x = _rng_normal((rows, k), 1.0, 200 + seed)
+        blocks = O.quantize_weights(fmt, w)
+        qx, _, sx = O.quantize_acts(x)
+        got = O.blockdots(fmt, blocks, n, k, qx)
+        codes = _unpack_codes(fmt, blocks)
+        ref = np.einsum("nbi,rbi->rnb", codes.reshape(n, k // 32, 32), qx.astype(np.int64).reshape(rows, k // 32, 32))
+        assert np.array_equal(got, ref)
+        if fmt == O.Q4_0:  # sum (c-8) q == sum c q - 8 sum q
+            craw = (codes + 8).reshape(n, k // 32, 32)
+            fold = np.einsum("nbi,rbi->rnb", craw, qx.astype(np.int64).reshape(rows, k // 32, 32)) - 8 * sx[:, None, :]
+            assert np.array_equal(got, fold)
+
+
+# ---------------------------------------------------------------- GEMV ---
+def _int_weight_blocks(fmt, n, k, seed):
+    """Integer weights whose block scale is exactly 1.0 (each block holds +-qmax)."""
+    qmax = 127 if fmt == O.Q8_0 else 7
+    r = np.random.default_rng(seed)
+    wi = r.integers(-qmax, qmax + 1, size=(n, k))
+    wi[:, ::32] = qmax * np.where(r.integers(0, 2, size=(n, k // 32)) == 0, 1, -1)
+    return wi, O.quantize_weights(fmt, wi.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", [O.Q8_0, O.Q4_0])
+def test_gemv_integer_case_is_exact_matvec(fmt):
+    n, k, rows = 40, 512, 3
+    wi, blocks = _int_weight_blocks(fmt, n, k, 5)
+    r = np.random.default_rng(6)
+    xi = r.integers(-127, 128, size=(rows, k))
+    xi[:, 7::32] = 127  # every block's amax is 127 -> d_x = 1
+    y = O.gemv_q(fmt, blocks, n, k, xi.astype(np.float32))
+    ref = xi @ wi.T  # exact in int64, |ref| < 2^24 so exact in fp32 too
+    assert np.array_equal(y, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", [O.Q8_0, O.Q4_0])
+def test_gemv_invariants(fmt):
+    n, k, rows = 24, 1024, 4
+    w = _rng_normal((n, k), 0.02, 41)
+    x = _rng_normal((rows, k), 1.0, 42)
+    blocks = O.quantize_weights(fmt, w)
+    y = O.gemv_q(fmt, blocks, n, k, x)
+    # power-of-two scaling of x scales y exactly
+    for j in (-7, 9):
+        y2 = O.gemv_q(fmt, blocks, n, k, (x.astype(np.float64) * 2.0 ** j).astype(np.float32))
+        assert np.array_equal(y2, (y.astype(np.float64) * 2.0 ** j).astype(np.float32))
+    # permuting weight rows permutes outputs
+    perm = np.random.default_rng(3).permutation(n)
+    assert np.array_equal(O.gemv_q(fmt, blocks[perm], n, k, x), y[:, perm])
+    # each row alone equals the row inside the batch
+    for r in range(rows):
+        assert np.array_equal(O.gemv_q(fmt, blocks, n, k, x[r:r + 1])[0], y[r])
+    # fp64 definition: sum over dequantized weights times dequantized activations
+    qx, dx, _ = O.quantize_acts(x)
+    xhat = qx.astype(np.float64) * np.repeat(dx.astype(np.float64), 32, axis=1)
+    what = O.dequantize(fmt, blocks, n, k)
+    ref = xhat @ what.T
+    scale = np.abs(xhat) @ np.abs(what).T
+    assert np.all(np.abs(y - ref) <= 1e-7 * scale + 1e-30)
+    # quantization bound against the unquantized product
+    d_w = np.repeat(O.f16_to_f32(blocks[:, :, 0].astype(np.uint16) | (blocks[:, :, 1].astype(np.uint16) << 8)), 32,
+                    axis=1).astype(np.float64)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    slack = np.abs(x.astype(np.float64)) @ (np.abs(w - what) ).T + \
+        (np.abs(x.astype(np.float64) - xhat)) @ np.abs(what).T
+    assert np.all(np.abs(y - exact) <= slack * (1 + 1e-6) + 1e-6 * scale)
+    assert np.all(np.abs(w - what) <= d_w * 0.5 + d_w * (127 if fmt == O.Q8_0 else 7) * 2.0 ** -10)
+
+
+def test_gemv_rows_subset_matches_full():
+    n, k = 50, 256
+    w = _rng_normal((n, k), 0.02, 51)
+    x = _rng_normal((3, k), 1.0, 52)
+    for fmt in (O.Q8_0, O.Q4_0):
+        blocks = O.quantize_weights(fmt, w)
+        full = O.gemv_q(fmt, blocks, n, k, x, threads=3)
+        sel = np.array([0, 7, 49, 13])
+        assert np.array_equal(O.gemv_q_rows(fmt, blocks, n, k, x, sel), full[:, sel])
+    w16, _ = O.f32_to_f16(w)
+    full = O.gemv_f16(w16, x, threads=4)
+    assert np.array_equal(O.gemv_f16_rows(w16, x, np.array([3, 0])), full[:, [3, 0]])
+
+
+# ------------------------------------------------------------- f16 lane ---
+def test_f16_gemv_integer_exact_and_random():
+    r = np.random.default_rng(8)
+    n, k, rows = 30, 640, 5
+    wi = r.integers(-64, 65, size=(n, k))
+    xi = r.integers(-100, 101, size=(rows, k))
+    w16, _ = O.f32_to_f16(wi.astype(np.float32))
+    y = O.gemv_f16(w16, xi.astype(np.float32))
+    assert np.array_equal(y, (xi @ wi.T).astype(np.float32))
+    w = _rng_normal((n, k), 0.02, 61)
+    x = _rng_normal((rows, k), 1.0, 62)
+    w16 = w.astype(np.float16)  # numpy's own RNE rounding
+    y = O.gemv_f16(w16.view(np.uint16), x)
+    ref = x.astype(np.float64) @ w16.astype(np.float64).T
+    assert np.all(np.abs(y - ref) <= np.abs(ref) * 2.0 ** -24 + 1e-30)
+
+
+# -------------------------------------------------------------- grouped ---
+def test_grouped_equals_per_assignment_integer_case():
+    E, n, k = 6, 16, 128
+    blocks = []
+    mats = []
+    for e in range(E):
+        wi, b = _int_weight_blocks(O.Q8_0, n, k, 70 + e)
+        mats.append(wi)
+        blocks.append(b)
+    blocks = np.stack(blocks)
+    r = np.random.default_rng(9)
+    xi = r.integers(-127, 128, size=(5, k))
+    xi[:, 3::32] = -127
+    expert = np.array([2, 0, 5, 2, 9, -1, 1, 3], np.int32)
+    x_index = np.array([0, 4, 1, 3, 0, 2, 7, 2], np.int32)
+    y, bad = O.gemv_q8_0_grouped(blocks, E, n, k, xi.astype(np.float32), expert, x_index)
+    assert bad == 3  # expert 9, expert -1, x_index 7 are out of range
+    for j in range(expert.size):
+        if 0 <= expert[j] < E and 0 <= x_index[j] < 5:
+            assert np.array_equal(y[j], (mats[expert[j]] @ xi[x_index[j]]).astype(np.float32))
+        else:
+            assert np.all(np.isnan(y[j]))
+
+
+# ------------------------------------------------------------- MoE glue ---
+def test_route_topk_closed_forms():
+    E = 16
+    logits = np.zeros((2, E), np.float32)
+    logits[0, [3, 9, 1]] = [math.log(3.0), 2.0, 2.0]  # 9 and 1 tie at 2.0 -> lower index first
+    logits[1, :] = np.arange(E, dtype=np.float32)[::-1]
+    ex, p = O.route_topk(logits, 4)
+    assert list(ex[0]) == [1, 9, 3, 0]
+    z = 2 * math.e ** 2 + 3.0 + (E - 3)
+    assert np.allclose(p[0], [math.e ** 2 / z, math.e ** 2 / z, 3.0 / z, 1.0 / z], rtol=1e-14)
+    assert list(ex[1]) == [0, 1, 2, 3]
+    zz = sum(math.exp(-i) for i in range(E))
+    assert np.allclose(p[1], [math.exp(-i) / zz for i in range(4)], rtol=1e-14)
+
+
+def test_swiglu_closed_forms():
+    g = np.float32([0.0, 1.0, -1.0, 30.0, -30.0, 2.0])
+    u = np.float32([5.0, 1.0, 2.0, 1.0, 1.0, -3.0])
+    h = O.swiglu(g, u)
+    ref = [0.0, 1 / (1 + math.exp(-1)), -2 / (1 + math.e), 30 / (1 + math.exp(-30)), -30 / (1 + math.exp(30)),
+           -3 * 2 / (1 + math.exp(-2))]
+    assert np.array_equal(h, np.float32(ref))
+
+
+def test_moe_step_composes_its_pieces():
+    """The step equals router GEMV -> top-k -> per-pick FFN -> weighted sum + shared FFN."""
+    hidden, ffn, E, topk, rows = 128, 64, 12, 3, 2
+    router = _rng_normal((E, hidden), 0.02, 81)
+    r16, _ = O.f32_to_f16(router)
+    q = lambda t, s: O.quantize_weights(O.Q8_0, _rng_normal(t, 0.02, s))
+    gate = np.stack([q((ffn, hidden), 900 + e) for e in range(E)])
+    up = np.stack([q((ffn, hidden), 950 + e) for e in range(E)])
+    down = np.stack([q((hidden, ffn), 990 + e) for e in range(E)])
+    sg, su, sd = q((ffn, hidden), 1), q((ffn, hidden), 2), q((hidden, ffn), 3)
+    x = _rng_normal((rows, hidden), 1.0, 82)
+    y, ex, p, logits = O.moe_step(x, r16, topk, gate, up, down, ffn, sg, su, sd)
+    assert np.array_equal(logits, O.gemv_f16(r16, x))
+    ex2, p2 = O.route_topk(logits, topk)
+    assert np.array_equal(ex, ex2) and np.array_equal(p, p2)
+
+    def ffn_out(g_, u_, d_, xr):
+        hg = O.gemv_q(O.Q8_0, g_, ffn, hidden, xr[None])
+        hu = O.gemv_q(O.Q8_0, u_, ffn, hidden, xr[None])
+        return O.gemv_q(O.Q8_0, d_, hidden, ffn, O.swiglu(hg, hu))[0].astype(np.float64)
+
+    for r in range(rows):
+        acc = np.zeros(hidden)
+        for s in range(topk):
+            acc += p[r, s] * ffn_out(gate[ex[r, s]], up[ex[r, s]], down[ex[r, s]], x[r])
+        ref = (acc + ffn_out(sg, su, sd, x[r])).astype(np.float32)
+        assert np.array_equal(y[r], ref)
+
+
+# --------------------------------------------------- input generator ---
+def test_synth_matches_scalar_splitmix_and_is_gaussian():
+    import torch
+    seed = synth.tensor_seed(3, 5, 7)
+    idx = torch.tensor([0, 1, 2, 1000, 123456789, 2 ** 40], dtype=torch.int64)
+    got = synth.splitmix64(seed, idx)
+    ref = [synth.splitmix64_scalar(seed, int(i)) for i in idx]
+    assert [int(v) & ((1 << 64) - 1) for v in got] == ref
+    # published first output of SplitMix64 from state 0 (Vigna's reference code)
+    assert synth.splitmix64_scalar(0, 0) == 0xE220A8397B1DCDAF
+    g = synth.gaussian((200000,), 2.0, seed).numpy().astype(np.float64)
+    assert abs(g.mean()) < 0.03 and abs(g.std() - 2.0) < 0.02
