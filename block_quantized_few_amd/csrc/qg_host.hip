@@ -1,0 +1,160 @@
+// qg_host.hip -- host side of libqgemv: status reporting, device check,
+// size queries and the canonical-block <-> device-image packing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "qg_internal.h"
+#include "qg_layout.h"
+
+namespace qg {
+
+static thread_local int t_last_status = QG_OK;
+static thread_local char t_detail[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_detail, sizeof t_detail, fmt, ap);
+  va_end(ap);
+  t_last_status = status;
+  return status;
+}
+
+int ok() {
+  t_last_status = QG_OK;
+  t_detail[0] = 0;
+  return QG_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QG_OK;
+  return fail(QG_ELAUNCH, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+int check_device() {
+  static std::mutex mu;
+  static std::vector<int> verdict;  // per device: 0 unknown, 1 gfx950, -1 other
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QG_EDEVICE, "no HIP device: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)verdict.size() <= dev) verdict.resize(dev + 1, 0);
+  if (verdict[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(QG_EDEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (verdict[dev] < 0) return fail(QG_EDEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (verdict[dev] < 0) return fail(QG_EDEVICE, "device %d is not gfx950", dev);
+  return QG_OK;
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" {
+
+const char* qg_status_string(int status) {
+  switch (status) {
+    case QG_OK: return "ok";
+    case QG_EINVAL: return "invalid argument";
+    case QG_ESHAPE: return "shape out of range";
+    case QG_EROWS: return "rows outside 0..16";
+    case QG_EALIGN: return "misaligned pointer";
+    case QG_EWORKSPACE: return "workspace too small";
+    case QG_ELAUNCH: return "HIP launch failed";
+    case QG_EDEVICE: return "not a gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+int qg_last_error_detail(char* buf, size_t len) {
+  if (buf && len) {
+    strncpy(buf, t_detail, len - 1);
+    buf[len - 1] = 0;
+  }
+  return t_last_status;
+}
+
+size_t qg_image_bytes(int fmt, int64_t n, int64_t k) {
+  if (n < 1 || k < 1) return 0;
+  if (fmt == QG_FMT_F16) return k % 8 ? 0 : (size_t)n * (size_t)k * 2;
+  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return 0;
+  if (k % QK) return 0;
+  return image_total_bytes(fmt, n, k);
+}
+
+size_t qg_workspace_bytes(int rows, int64_t k) {
+  if (rows < 1 || rows > QG_MAX_PREP_ROWS || k < QK || k % QK) return 0;
+  return prep_layout(rows, k).total;
+}
+
+size_t qg_grouped_workspace_bytes(int x_rows, int64_t k, int m) {
+  if (x_rows < 1 || x_rows > QG_MAX_PREP_ROWS || k < QK || k % QK || m < 0 || m > QG_MAX_ASSIGN) return 0;
+  return grouped_layout(x_rows, k, m).total;
+}
+
+static int check_pack_args(int fmt, const void* a, int64_t n, int64_t k, const void* b) {
+  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1) or Q4_0 (2)", fmt);
+  if (!a || !b) return fail(QG_EINVAL, "null buffer");
+  if (n < 1 || k < QK || k % QK) return fail(QG_ESHAPE, "n=%lld k=%lld (need n >= 1, k a positive multiple of 32)",
+                                             (long long)n, (long long)k);
+  return QG_OK;
+}
+
+int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image) {
+  int st = check_pack_args(fmt, blocks, n, k, image);
+  if (st) return st;
+  const uint8_t* src = (const uint8_t*)blocks;
+  uint8_t* dst = (uint8_t*)image;
+  memset(dst, 0, image_total_bytes(fmt, n, k));
+  int64_t kb = kb_of(k), kbp = kbp_of(k);
+  uint16_t* scales = (uint16_t*)(dst + image_scale_offset(fmt, n, k));
+  int cb = fmt == QG_FMT_Q8_0 ? Q8_CANON : Q4_CANON;
+  for (int64_t o = 0; o < n; o++)
+    for (int64_t b = 0; b < kb; b++) {
+      const uint8_t* blk = src + (o * kb + b) * cb;
+      scales[o * kbp + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+      if (fmt == QG_FMT_Q8_0) {
+        size_t lo = q8_lo_offset(o, b, kbp);
+        memcpy(dst + lo, blk + 2, 16);
+        memcpy(dst + lo + 256, blk + 18, 16);
+      } else {
+        memcpy(dst + q4_offset(o, b, kbp), blk + 2, 16);
+      }
+    }
+  return ok();
+}
+
+int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* blocks) {
+  int st = check_pack_args(fmt, image, n, k, blocks);
+  if (st) return st;
+  const uint8_t* src = (const uint8_t*)image;
+  uint8_t* dst = (uint8_t*)blocks;
+  int64_t kb = kb_of(k), kbp = kbp_of(k);
+  const uint16_t* scales = (const uint16_t*)(src + image_scale_offset(fmt, n, k));
+  int cb = fmt == QG_FMT_Q8_0 ? Q8_CANON : Q4_CANON;
+  for (int64_t o = 0; o < n; o++)
+    for (int64_t b = 0; b < kb; b++) {
+      uint8_t* blk = dst + (o * kb + b) * cb;
+      uint16_t d = scales[o * kbp + b];
+      blk[0] = (uint8_t)(d & 0xff);
+      blk[1] = (uint8_t)(d >> 8);
+      if (fmt == QG_FMT_Q8_0) {
+        size_t lo = q8_lo_offset(o, b, kbp);
+        memcpy(blk + 2, src + lo, 16);
+        memcpy(blk + 18, src + lo + 256, 16);
+      } else {
+        memcpy(blk + 2, src + q4_offset(o, b, kbp), 16);
+      }
+    }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+/*
+ * qgemv.h -- C ABI of the few-row block-quantized GEMV library for MI355X
+ * (gfx950), built as block_quantized_few_amd/libqgemv.so.
+ *
+ * What it computes.  The decode-time projection of 1..16 activation rows
+ * against one weight matrix W [n][k], y[r][o] = sum_k W[o][k] * x[r][k], in the
+ * two device lanes of the dasLLAMA audio-towers page (feature commit): the q8
+ * lane, where block-quantized weights meet q8-quantized activations through
+ * exact integer block dots, and the f16 lane, halfword weights accumulated in
+ * fp32.  Rows past eight are tiled inside the callee, in one weight pass, so a
+ * caller can never launch rows past the kernel's tile (router-GEMV commit of
+ * the same page; balanced groups past eight rows, commit 16880fe of the
+ * dasLLAMA llama-leg page).  A grouped variant streams each routed expert
+ * once for all rows routed to it (llama-leg page: the routed model's N-row
+ * command).
+ *
+ * Formats.
+ *   Q8_0: 32-weight blocks, fp16 scale d = fp16(max|w|/127), int8 codes
+ *         q = round-half-away(w/d) in [-127, 127].  Canonical block
+ *         {uint16 d; int8 q[32]} = 34 bytes.
+ *   Q4_0: 32-weight blocks, d = fp16(max|w|/7), 4-bit codes c = q + 8 in
+ *         [0, 15]; canonical block {uint16 d; uint8 p[16]} = 18 bytes, byte j
+ *         holding c_j (low nibble) and c_{j+16} (high nibble).
+ *   q8 activations: per row and 32-block, d_x = max|x|/127 (IEEE fp32
+ *         division), q = round-half-away(x/d_x) clamped to [-127, 127] (0 when
+ *         d_x == 0), s_x = sum q.  Quantized on the device, bit-exact with a
+ *         plain CPU evaluation of that definition.
+ *   y[r][o] = sum_b d_w[o][b] * d_x[r][b] * isum[r][o][b], where isum is the
+ *         exact int32 dot of block b's codes (Q4_0 codes stand for c - 8).
+ *         The fp32 summation order is fixed per output and does not depend on
+ *         `rows`: a row computed inside a batch of 16 has the same bits as the
+ *         row computed alone.
+ *
+ * Device image.  Weights live on the device in the library's own layout,
+ * made either by qg_pack_image (from canonical blocks, on the host) or by
+ * qg_quantize_weights (from fp32 weights, on the device).  Each row is padded
+ * with zero blocks to a multiple of 16 blocks (512 weights); for k a multiple
+ * of 512 the image holds exactly the canonical bytes per weight.
+ *
+ * Conventions.
+ *   - Pointers are device pointers unless marked (host).  `stream` is a
+ *     hipStream_t (NULL = the null stream).  Device calls enqueue work on
+ *     `stream` and return without synchronizing, except the functions marked
+ *     "synchronizes".
+ *   - The caller owns every buffer; the library allocates no device memory,
+ *     frees nothing and keeps no pointer past a return.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     negative status means nothing was launched and no output was touched;
+ *     qg_last_error_detail() then names the argument and its value (per
+ *     thread).  QG_ELAUNCH reports a HIP launch failure.
+ *   - rows == 0 is a successful no-op.  rows > 16 is QG_EROWS, never a
+ *     silently truncated tile.
+ *   - Shapes: n >= 1; k % 32 == 0 (q8 lane) or k % 8 == 0 (f16 lane).
+ *   - Alignment: images and workspaces 256 bytes; x, f16 weights and q8 row
+ *     buffers 16 bytes; y 4 bytes.
+ *   - x must be finite; the result for NaN/Inf inputs is unspecified.
+ *   - Calls are stateless and re-entrant; two calls that share a workspace
+ *     must be ordered on one stream.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* qg_stream; /* a hipStream_t */
+
+enum {
+  QG_OK = 0,
+  QG_EINVAL = -1,     /* null pointer, unknown format, bad count */
+  QG_ESHAPE = -2,     /* n, k or another extent out of range */
+  QG_EROWS = -3,      /* rows outside 0..16 */
+  QG_EALIGN = -4,     /* a pointer misses its alignment */
+  QG_EWORKSPACE = -5, /* workspace smaller than the size query returned */
+  QG_ELAUNCH = -6,    /* a HIP call or kernel launch failed */
+  QG_EDEVICE = -7     /* the current device is not a gfx950 GPU */
+};
+
+enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3 };
+
+#define QG_MAX_ROWS 16        /* activation rows per GEMV call */
+#define QG_MAX_PREP_ROWS 8192 /* rows one qg_prepare_rows call quantizes */
+#define QG_MAX_ASSIGN 2048    /* assignments per grouped call */
+#define QG_MAX_SET 8          /* projections per qgemv_set call */
+
+/* ------------------------------------------------------------ host only --- */
+
+/* Bytes of the device image of an n x k matrix in `fmt` (Q8_0, Q4_0: padded
+ * layout above; F16: 2*n*k).  Returns 0 for an invalid format or shape. */
+size_t qg_image_bytes(int fmt, int64_t n, int64_t k);
+
+/* Host -> host.  Converts canonical blocks (Q8_0 / Q4_0, n * k/32 blocks, row
+ * major) to the device layout in `image` (qg_image_bytes bytes, host memory;
+ * copy it to the device afterwards).  Pad blocks are written as zeros. */
+int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image);
+
+/* Host -> host inverse of qg_pack_image (pad blocks are dropped). */
+int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* blocks);
+
+/* Bytes of the workspace that holds `rows` quantized activation rows of
+ * length k (codes, scales and code sums).  0 for an invalid shape. */
+size_t qg_workspace_bytes(int rows, int64_t k);
+
+/* Bytes of the workspace of qgemv_q8_0_grouped for x_rows activation rows of
+ * length k and m assignments.  0 for an invalid shape. */
+size_t qg_grouped_workspace_bytes(int x_rows, int64_t k, int m);
+
+/* Static description of a status code. */
+const char* qg_status_string(int status);
+
+/* Copies this thread's detail of the last failed call into buf (host),
+ * NUL-terminated; returns the status of that call (QG_OK if none failed). */
+int qg_last_error_detail(char* buf, size_t len);
+
+/* ---------------------------------------------------------------- device --- */
+
+/* Quantizes fp32 weights w [n][k] (device) into a device image of `fmt`
+ * (Q8_0 or Q4_0) by the block rules above.  Requires max|w|/qmax to fit fp16.
+ * Offline preparation, not part of the per-token path. */
+int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, qg_stream stream);
+
+/* A1 of the q8 lane: quantizes rows x [rows][k] (1 <= rows <= QG_MAX_PREP_ROWS)
+ * into the workspace `ws` (qg_workspace_bytes(rows, k) bytes) in the layout the
+ * GEMV kernels read. */
+int qg_prepare_rows(const float* x, int rows, int64_t k, void* ws, size_t ws_bytes, qg_stream stream);
+
+/* q8 lane GEMV on rows already prepared in `ws` (by qg_prepare_rows with the
+ * same rows and k): y [rows][n] fp32, row stride n.  fmt = Q8_0 or Q4_0. */
+int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
+                   qg_stream stream);
+
+/* Q8_0 weights x q8 activations: qg_prepare_rows then qgemv_prepared.
+ * x [rows][k] fp32, y [rows][n] fp32, ws of qg_workspace_bytes(rows, k). */
+int qgemv_q8_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+               size_t ws_bytes, qg_stream stream);
+
+/* Q4_0 weights x q8 activations; arguments as qgemv_q8_0. */
+int qgemv_q4_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+               size_t ws_bytes, qg_stream stream);
+
+/* f16 lane: y [rows][n] = w [n][k] (fp16, row major) . x [rows][k] (fp32),
+ * fp32 accumulation, x kept in fp32. */
+int gemv_f16(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream);
+
+/* Several independent q8-lane projections with the same row count in one
+ * launch (a decode layer's Q/K/V/O/gate/up/down).  Each entry's rows must
+ * already be prepared in its `ws`.  1 <= count <= QG_MAX_SET. */
+typedef struct {
+  const void* w_image;
+  int64_t n;
+  int64_t k;
+  const void* ws; /* prepared rows for this projection's input */
+  float* y;       /* [rows][n] */
+} qg_proj;
+int qgemv_set(int fmt, const qg_proj* projs /*host*/, int count, int rows, qg_stream stream);
+
+/* Prepares several activation sets in one launch (count <= QG_MAX_SET). */
+typedef struct {
+  const float* x; /* [rows][k] */
+  int64_t k;
+  void* ws;
+  size_t ws_bytes;
+} qg_act;
+int qg_prepare_rows_set(const qg_act* acts /*host*/, int count, int rows, qg_stream stream);
+
+/* Grouped routed-expert GEMV, Q8_0.  w_images holds n_experts device images
+ * back to back, each qg_image_bytes(Q8_0, n, k) bytes.  For assignment j < m:
+ * y[j] = W_{expert[j]} . q8(x[x_index[j]]).  Each touched expert's weights are
+ * streamed once for up to 16 of its assignments.  expert and x_index are
+ * device int32 arrays; an entry out of range is skipped (y[j] untouched) and
+ * counted in the workspace, readable with qg_grouped_status.  x [x_rows][k],
+ * 1 <= x_rows <= QG_MAX_PREP_ROWS, 0 <= m <= QG_MAX_ASSIGN; with m == 0, y, expert
+ * and x_index may be null and only the status words are written. */
+int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64_t k, const float* x, int x_rows,
+                       const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, size_t ws_bytes,
+                       qg_stream stream);
+
+/* Synchronizes `stream`, then reads the count of skipped assignments of the
+ * last grouped call on `ws` into *bad (host). */
+int qg_grouped_status(const void* ws, int32_t* bad, qg_stream stream);
+
+/* MoE glue around the grouped GEMV (routed decode step with an ungated shared
+ * expert).
+ * qg_moe_route: per row, softmax over n_experts logits (max subtracted) and
+ *   the topk experts by logit, ties to the lower index, in descending order;
+ *   writes rows*slots assignments, slots = topk + (shared_expert >= 0): slot
+ *   s < topk is (expert, x_index = r, weight = softmax probability), the last
+ *   slot is (shared_expert, r, 1.0).  1 <= topk <= 32, n_experts <= 1024. */
+int qg_moe_route(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
+                 int32_t* x_index, float* weight, qg_stream stream);
+
+/* h[j][i] = silu(gu[j][i]) * gu[j][ffn + i], silu(g) = g / (1 + exp(-g)),
+ * for j < m, i < ffn (gate rows first, then up rows, in one output row). */
+int qg_swiglu(const float* gu, int m, int64_t ffn, float* h, qg_stream stream);
+
+/* y[r] = sum over s < slots, in slot order, of weight[r*slots+s] * o[r*slots+s]
+ * (o rows of length hidden). */
+int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int64_t hidden, float* y,
+                   qg_stream stream);
+
+/* ------------------------------------------------------ test-only hooks --- */
+
+/* A1 in the plain layout: qx [rows][k] int8, dx [rows][k/32] fp32, sx
+ * [rows][k/32] int32 (sum of the block's codes). */
+int qg_quantize_rows_q8(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, qg_stream stream);
+
+/* A3 alone: isum [rows][n][k/32] int32 = exact block dots of the image's codes
+ * with qx [rows][k] (plain layout), rows <= 16. */
+int qgemv_blockdots(int fmt, const void* w_image, int64_t n, int64_t k, const int8_t* qx, int rows, int32_t* isum,
+                    qg_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMV_H */

@@ -1,0 +1,122 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol the
+header declares, answers its host-only queries, packs images, and refuses bad
+arguments with the documented status before touching HIP."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from block_quantized_few_amd import qgemv as q
+from block_quantized_few_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 20, names
+    L = C.CDLL(q.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(q._SIGS), set(names) ^ set(q._SIGS)
+
+
+def test_sizes():
+    assert q.image_bytes(q.Q8_0, 1024, 1024) == 1024 * 1024 // 32 * 34
+    assert q.image_bytes(q.Q4_0, 3072, 3072) == 3072 * 3072 // 32 * 18
+    assert q.image_bytes(q.Q8_0, 128256, 4096) == 558170112
+    assert q.image_bytes(q.F16, 128256, 4096) == 1050673152
+    assert q.image_bytes(q.Q8_0, 1024, 1000) == 0  # k not a multiple of 32
+    assert q.image_bytes(q.F16, 8, 12) == 0
+    assert q.image_bytes(7, 8, 32) == 0
+    # a ragged k is padded to whole 16-block groups
+    assert q.image_bytes(q.Q8_0, 3, 96) >= 3 * 512 // 32 * 34
+    assert q.workspace_bytes(0, 1024) == 0 and q.workspace_bytes(17, 1024) > 0
+    assert q.workspace_bytes(1, 33) == 0
+    assert q.grouped_workspace_bytes(16, 2048, 136) > q.workspace_bytes(16, 2048)
+    assert q.grouped_workspace_bytes(16, 2048, q.MAX_ASSIGN + 1) == 0
+
+
+@pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0])
+@pytest.mark.parametrize("n,k", [(5, 32), (7, 512), (3, 800), (2, 8192)])
+def test_pack_unpack_roundtrip(fmt, n, k):
+    w = synth.gaussian((n, k), 0.02, synth.tensor_seed(9, 1)).numpy()
+    blocks = O.quantize_weights(fmt, w)
+    img = q.pack_image(fmt, blocks, n, k)
+    assert img.size == q.image_bytes(fmt, n, k)
+    assert np.array_equal(q.unpack_image(fmt, img, n, k), blocks)
+
+
+def test_pack_layout_of_one_q8_block():
+    # block b of row o: low half at o*kbp*32 + (b//16)*512 + (b%16)*16, high half +256, scale plane after
+    n, k = 2, 1024  # kb = kbp = 32
+    blocks = np.zeros((n, k // 32, 34), np.uint8)
+    blocks[1, 17, 0:2] = (0x34, 0x12)
+    blocks[1, 17, 2:34] = np.arange(1, 33, dtype=np.uint8)
+    img = q.pack_image(q.Q8_0, blocks, n, k)
+    lo = 1 * 32 * 32 + 1 * 512 + 1 * 16
+    assert list(img[lo:lo + 16]) == list(range(1, 17))
+    assert list(img[lo + 256:lo + 272]) == list(range(17, 33))
+    scale_off = (n * 32 * 32 + 255) // 256 * 256
+    assert img[scale_off + 2 * (1 * 32 + 17)] == 0x34 and img[scale_off + 2 * (1 * 32 + 17) + 1] == 0x12
+
+
+def _status(fn, *args):
+    L = q.lib()
+    st = getattr(L, fn)(*args)
+    buf = C.create_string_buffer(512)
+    assert L.qg_last_error_detail(buf, 512) == st
+    return st, buf.value.decode()
+
+
+A = 256 * 64  # a 256-byte aligned fake address (never dereferenced: validation fails first)
+V = C.c_void_p
+
+
+def test_validation_refuses_before_any_hip_call():
+    MB = 1 << 20
+    st, msg = _status("qgemv_q8_0", V(A), 1024, 1024, V(A), 17, V(A), V(A), MB, None)
+    assert st == -3 and "rows=17" in msg
+    st, msg = _status("qgemv_q8_0", V(A), 1024, 1000, V(A), 1, V(A), V(A), MB, None)
+    assert st == -2 and "k=1000" in msg
+    st, msg = _status("qgemv_q8_0", V(A), 0, 1024, V(A), 1, V(A), V(A), MB, None)
+    assert st == -2 and "n=0" in msg
+    st, msg = _status("qgemv_q4_0", None, 1024, 1024, V(A), 1, V(A), V(A), MB, None)
+    assert st == -1 and "w_image" in msg
+    st, msg = _status("qgemv_q4_0", V(A + 16), 1024, 1024, V(A), 1, V(A), V(A), MB, None)
+    assert st == -4 and "w_image" in msg
+    st, msg = _status("qgemv_q8_0", V(A), 1024, 1024, V(A + 4), 1, V(A), V(A), MB, None)
+    assert st == -4 and "x" in msg
+    st, msg = _status("qgemv_q8_0", V(A), 1024, 1024, V(A), 2, V(A), V(A), 100, None)
+    assert st == -5 and "ws_bytes=100" in msg
+    st, msg = _status("gemv_f16", V(A), 64, 12, V(A), 1, V(A), None)
+    assert st == -2
+    st, msg = _status("qgemv_prepared", 9, V(A), 64, 64, V(A), 1, V(A), None)
+    assert st == -1 and "fmt=9" in msg
+    st, msg = _status("qgemv_q8_0_grouped", V(A), 8, 64, 64, V(A), 1, V(A), V(A), q.MAX_ASSIGN + 1, V(A), V(A),
+                      MB, None)
+    assert st == -2
+    st, msg = _status("qg_moe_route", V(A), 1, 2000, 8, -1, V(A), V(A), V(A), None)
+    assert st == -2
+    assert q.status_string(-3) == "rows outside 0..16"
+
+
+def test_rows_zero_is_a_noop():
+    st, _ = _status("qgemv_q8_0", V(A), 1024, 1024, V(A), 0, V(A), V(A), 0, None)
+    assert st == 0
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="a GPU is present")
+def test_valid_call_without_gpu_reports_device():
+    st, msg = _status("qgemv_q8_0", V(A), 64, 64, V(A), 1, V(A), V(A), 1 << 20, None)
+    assert st == -7, msg

@@ -1,0 +1,114 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times, on sampled outputs the oracle computes one by one.
+
+LM head 128256 x 4096 (Q8_0 and f16) at rows 1, 8, 16; the Llama-3.2-1B-shaped
+Q8_0 decode layer (seven projections, one set launch) at rows 1 and 16; the
+Llama-3.2-3B-shaped Q4_0 layer at rows 1, 2, 4, 8."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_quantized_few_amd import qgemv as q
+from helpers import TOL, bits, gauss, log, rel_err, rel_err_f16
+
+pytestmark = pytest.mark.gpu
+
+LAYER_1B = [("wq", 2048, 2048), ("wk", 512, 2048), ("wv", 512, 2048), ("wo", 2048, 2048), ("gate", 8192, 2048),
+            ("up", 8192, 2048), ("down", 2048, 8192)]
+LAYER_3B = [("wq", 3072, 3072), ("wk", 1024, 3072), ("wv", 1024, 3072), ("wo", 3072, 3072), ("gate", 8192, 3072),
+            ("up", 8192, 3072), ("down", 3072, 8192)]
+
+
+def _sample(n, count, seed):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], r.integers(0, n, count)]))
+
+
+def test_lm_head_q8_0():
+    n, k = 128256, 4096
+    log("LM head Q8_0: weights")
+    w = gauss((n, k), 0.02, 4, 0, device="cuda").cpu().numpy()
+    blocks = O.quantize_weights(O.Q8_0, w)
+    del w
+    img = torch.from_numpy(q.pack_image(q.Q8_0, blocks, n, k)).cuda()
+    sel = _sample(n, 512, 1)
+    ys = {}
+    for rows in (1, 8, 16):
+        log(f"LM head Q8_0 rows={rows}")
+        x = gauss((rows, k), 1.0, 4, 32 + rows).numpy()
+        y = q.qgemv_q8_0(img, n, k, torch.from_numpy(x).cuda())
+        yo = O.gemv_q_rows(O.Q8_0, blocks, n, k, x, sel, threads=16)
+        e = rel_err(y.cpu().numpy()[:, sel], yo, blocks, O.Q8_0, x, sel=sel)
+        log(f"  max rel err {e:.3e}")
+        assert e <= TOL
+        ys[rows] = (x, y)
+    # the first rows of the 16-row call equal calls with fewer rows of the same inputs
+    x16 = torch.from_numpy(ys[16][0]).cuda()
+    y8 = q.qgemv_q8_0(img, n, k, x16[:8].contiguous())
+    assert np.array_equal(bits(y8), bits(ys[16][1][:8]))
+
+
+def test_lm_head_f16():
+    n, k = 128256, 4096
+    log("LM head f16: weights")
+    w16 = gauss((n, k), 0.02, 4, 0, device="cuda").half().view(torch.int16)
+    w16_np = w16.cpu().numpy().view(np.uint16)
+    sel = _sample(n, 512, 2)
+    for rows in (1, 8, 16):
+        log(f"LM head f16 rows={rows}")
+        x = gauss((rows, k), 1.0, 4, 32 + rows).numpy()
+        y = q.gemv_f16(w16, torch.from_numpy(x).cuda())
+        yo = O.gemv_f16_rows(w16_np, x, sel, threads=16)
+        e = rel_err_f16(y.cpu().numpy()[:, sel], yo, w16_np[sel], x)
+        log(f"  max rel err {e:.3e}")
+        assert e <= TOL
+
+
+def _layer(fmt, ofmt, layer, wl):
+    blocks, imgs = [], []
+    for i, (_, n, k) in enumerate(layer):
+        w = gauss((n, k), 0.02, wl, i, device="cuda").cpu().numpy()
+        b = O.quantize_weights(ofmt, w)
+        blocks.append(b)
+        imgs.append(torch.from_numpy(q.pack_image(fmt, b, n, k)).cuda())
+    return blocks, imgs
+
+
+def _run_set(fmt, ofmt, layer, blocks, imgs, rows, wl, full):
+    k_in, k_dn = layer[0][2], layer[6][2]
+    x_in = gauss((rows, k_in), 1.0, wl, 32 + rows).numpy()
+    x_o = gauss((rows, k_in), 1.0, wl, 48 + rows).numpy()
+    x_dn = gauss((rows, k_dn), 1.0, wl, 64 + rows).numpy()
+    xs = [torch.from_numpy(a).cuda() for a in (x_in, x_o, x_dn)]
+    wss = [q.empty_ws(rows, a.shape[1]) for a in xs]
+    q.prepare_rows_set(xs, wss)
+    src = {"wo": 1, "down": 2}
+    projs, outs = [], []
+    for i, (name, n, k) in enumerate(layer):
+        j = src.get(name, 0)
+        y = torch.full((rows, n), float("nan"), device="cuda")
+        outs.append((y, (x_in, x_o, x_dn)[j]))
+        projs.append((imgs[i], n, k, wss[j], y))
+    q.qgemv_set(fmt, projs, rows)
+    for i, (name, n, k) in enumerate(layer):
+        y, x = outs[i]
+        sel = np.arange(n) if full else _sample(n, 256, i)
+        yo = O.gemv_q_rows(ofmt, blocks[i], n, k, x, sel, threads=16)
+        e = rel_err(y.cpu().numpy()[:, sel], yo, blocks[i], ofmt, x, sel=sel)
+        log(f"  {name} {n}x{k} rows={rows} max rel err {e:.3e}")
+        assert e <= TOL
+
+
+def test_llama1b_layer_q8_0_set():
+    blocks, imgs = _layer(q.Q8_0, O.Q8_0, LAYER_1B, 1)
+    for rows in (1, 16):
+        log(f"1B layer Q8_0 rows={rows}")
+        _run_set(q.Q8_0, O.Q8_0, LAYER_1B, blocks, imgs, rows, 1, full=rows == 1)
+
+
+def test_llama3b_layer_q4_0_set():
+    blocks, imgs = _layer(q.Q4_0, O.Q4_0, LAYER_3B, 2)
+    for rows in (1, 2, 4, 8):
+        log(f"3B layer Q4_0 rows={rows}")
+        _run_set(q.Q4_0, O.Q4_0, LAYER_3B, blocks, imgs, rows, 2, full=False)

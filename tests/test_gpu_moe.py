@@ -1,0 +1,76 @@
+"""Routed MoE decode step (router f16 GEMV, softmax top-8, grouped Q8_0 experts,
+SwiGLU, grouped down projection, weighted combine with a shared expert) on the
+GPU against the oracle's step, at the full expert shape: hidden 2048, 256
+experts of 512-wide FFNs, top-8, one shared expert; rows 1, 8, 9, 16."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_quantized_few_amd import qgemv as q
+from helpers import TOL, gauss, log, rel_err_f16
+
+pytestmark = pytest.mark.gpu
+
+HIDDEN, FFN, E, TOPK = 2048, 512, 256, 8
+WL = 3  # workload id of the routed-MoE step
+
+
+@pytest.fixture(scope="module")
+def moe():
+    log("building MoE weights")
+    router = gauss((E, HIDDEN), 0.02, WL, 0, device="cuda")
+    r16 = router.half().view(torch.int16)
+    gate, up, down, gu_imgs, dn_imgs = [], [], [], [], []
+    for e in range(E + 1):  # index E is the shared expert
+        tid = 1 + 3 * e
+        g = gauss((FFN, HIDDEN), 0.02, WL, tid, device="cuda").cpu().numpy()
+        u = gauss((FFN, HIDDEN), 0.02, WL, tid + 1, device="cuda").cpu().numpy()
+        d = gauss((HIDDEN, FFN), 0.02, WL, tid + 2, device="cuda").cpu().numpy()
+        gb, ub, db = (O.quantize_weights(O.Q8_0, a) for a in (g, u, d))
+        gate.append(gb)
+        up.append(ub)
+        down.append(db)
+        gu_imgs.append(q.pack_image(q.Q8_0, np.concatenate([gb, ub]), 2 * FFN, HIDDEN))
+        dn_imgs.append(q.pack_image(q.Q8_0, db, HIDDEN, FFN))
+    log("MoE weights ready")
+    return dict(r16=r16, r16_np=r16.cpu().numpy().view(np.uint16), gate=np.stack(gate[:E]), up=np.stack(up[:E]),
+                down=np.stack(down[:E]), sg=gate[E], su=up[E], sd=down[E], down_all=down,
+                gu=torch.from_numpy(np.concatenate(gu_imgs)).cuda(),
+                dn=torch.from_numpy(np.concatenate(dn_imgs)).cuda())
+
+
+@pytest.mark.parametrize("rows", [1, 8, 9, 16])
+def test_moe_step_matches_oracle(moe, rows):
+    log(f"moe rows={rows}")
+    x = gauss((rows, HIDDEN), 1.0, WL, 32 + rows).numpy()
+    y, (expert, x_index, weight), logits = q.moe_step(torch.from_numpy(x).cuda(), moe["r16"], E, TOPK, moe["gu"],
+                                                      moe["dn"], FFN, shared_expert=E)
+    yo, ex_o, p_o, logits_o = O.moe_step(x, moe["r16_np"], TOPK, moe["gate"], moe["up"], moe["down"], FFN,
+                                         moe["sg"], moe["su"], moe["sd"])
+    assert rel_err_f16(logits.cpu().numpy(), logits_o, moe["r16_np"], x) <= TOL
+    ex = expert.cpu().numpy().reshape(rows, TOPK + 1)
+    wt = weight.cpu().numpy().reshape(rows, TOPK + 1)
+    assert np.all(ex[:, TOPK] == E) and np.all(wt[:, TOPK] == 1.0)
+    assert np.array_equal(x_index.cpu().numpy().reshape(rows, TOPK + 1), np.repeat(np.arange(rows), TOPK + 1).reshape(rows, TOPK + 1))
+    yg = y.cpu().numpy().astype(np.float64)
+    for r in range(rows):
+        if not np.array_equal(ex[r, :TOPK], ex_o[r]):
+            # only a near-tie of the 8th and 9th logits may reorder the picks
+            srt = np.sort(logits_o[r].astype(np.float64))[::-1]
+            assert srt[TOPK - 1] - srt[TOPK] < 1e-4, (r, ex[r], ex_o[r])
+            log(f"  row {r}: near-tie in routing, output not compared")
+            continue
+        assert np.allclose(wt[r, :TOPK], p_o[r], rtol=1e-5, atol=1e-9)
+        # error bar: 2e-3 of sum over picks of p * sum|w_down||h| (+ shared), h from the oracle's pieces
+        denom = 0.0
+        for s, e in enumerate(list(ex_o[r]) + [E]):
+            gb, ub, db = (moe["gate"][e], moe["up"][e], moe["down"][e]) if e < E else (moe["sg"], moe["su"], moe["sd"])
+            hg = O.gemv_q(O.Q8_0, gb, FFN, HIDDEN, x[r:r + 1])
+            hu = O.gemv_q(O.Q8_0, ub, FFN, HIDDEN, x[r:r + 1])
+            h = O.swiglu(hg, hu).astype(np.float64)
+            d = np.abs(h) @ np.abs(O.dequantize(O.Q8_0, db, HIDDEN, FFN)).T
+            denom = denom + (p_o[r, s] if e < E else 1.0) * d[0]
+        err = np.abs(yg[r] - yo[r]) / denom
+        log(f"  row {r}: max rel err {err.max():.3e}")
+        assert err.max() <= TOL
