@@ -1,0 +1,431 @@
+#!/usr/bin/env python3
+"""Benchmark of the few-row block-quantized GEMV on one MI355X.
+
+Headline step: one decode layer of a Llama-3.2-1B-shaped model in the Q8_0
+lane at one activation row -- the q8 quantization of the layer's three input
+rows (one launch) and its seven projections Wq 2048x2048, Wk/Wv 512x2048, Wo
+2048x2048, gate/up 8192x2048, down 2048x8192 (one launch), 64,618,496 weight
+bytes.  The weights rotate through enough distinct copies (>= 1 GiB) that every
+step streams them from HBM, not from the 256 MB Infinity Cache.
+
+Prints one JSON line: weight GB/s of the step (value), the roofline of the
+GEMV kernel measured with HIP events on its own stream, the CPU oracle timed on
+a bounded sample, and (unless --no-sweep) the other workloads at 1..16 rows.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes as C
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "weight GB/s and % HBM roofline for Q8_0/Q4_0 GEMV at 1/8/16 rows"
+
+LAYER_1B = [("wq", 2048, 2048), ("wk", 512, 2048), ("wv", 512, 2048), ("wo", 2048, 2048), ("gate", 8192, 2048),
+            ("up", 8192, 2048), ("down", 2048, 8192)]
+LAYER_3B = [("wq", 3072, 3072), ("wk", 1024, 3072), ("wv", 1024, 3072), ("wo", 3072, 3072), ("gate", 8192, 3072),
+            ("up", 8192, 3072), ("down", 3072, 8192)]
+# which of the three input rows (block input, attention output, FFN hidden) feeds each projection
+LAYER_SRC = {"wo": 1, "down": 2}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--out", default=None, help="also write the JSON line (with the sweep) to this file")
+    return p.parse_args()
+
+
+class Timer:
+    """Times enqueued work with HIP events on torch's current stream.
+
+    A bounded sleep kernel holds the stream while the host enqueues, so the
+    measured interval is GPU time, not host launch time."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.cycles_per_ms = self._calibrate()
+
+    def _calibrate(self):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda._sleep(1000)
+        a.record()
+        t.cuda._sleep(2_000_000)
+        b.record()
+        t.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        return 2_000_000 / max(ms, 1e-3)
+
+    def hold(self, ms):
+        self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
+
+
+def ctypes_arr(struct, items):
+    arr = (struct * len(items))()
+    for i, it in enumerate(items):
+        arr[i] = it
+    return arr
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("qg_kernels.hip", "qg_layout.h"):
+        with open(os.path.join(ROOT, "block_quantized_few_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed PMC summary, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(f"{kernel}|{workload}")
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ layers ---
+class LayerSet:
+    """A decode layer's projections in one lane with rotating weight copies."""
+
+    def __init__(self, torch, q, synth, layer, fmt, workload, rows, copies=None):
+        self.torch, self.q = torch, q
+        self.layer, self.fmt, self.rows = layer, fmt, rows
+        self.wbytes = sum(q.image_bytes(fmt, n, k) for _, n, k in layer)
+        self.copies = copies or max(2, math.ceil((1 << 30) / self.wbytes))
+        self.imgs = []
+        for c in range(self.copies):
+            row = []
+            for i, (_, n, k) in enumerate(layer):
+                w = synth.gaussian((n, k), 0.02, synth.tensor_seed(workload, i, c), device="cuda")
+                row.append(q.quantize_weights(fmt, w))
+                del w
+            self.imgs.append(row)
+        self.set_rows(rows, synth, workload)
+
+    def set_rows(self, rows, synth, workload):
+        q, torch = self.q, self.torch
+        self.rows = rows
+        k_in, k_dn = self.layer[0][2], self.layer[6][2]
+        seeds = [(32 + rows, k_in), (48 + rows, k_in), (64 + rows, k_dn)]
+        self.xs = [synth.gaussian((rows, k), 1.0, synth.tensor_seed(workload, tid), device="cuda") for tid, k in seeds]
+        self.wss = [q.empty_ws(rows, x.shape[1]) for x in self.xs]
+        self.ys = [torch.empty((rows, n), dtype=torch.float32, device="cuda") for _, n, _ in self.layer]
+        self.acts = ctypes_arr(q._Act, [q._Act(x.data_ptr(), x.shape[1], w.data_ptr(), w.numel())
+                                        for x, w in zip(self.xs, self.wss)])
+        self.projs = []
+        for c in range(self.copies):
+            items = []
+            for i, (name, n, k) in enumerate(self.layer):
+                ws = self.wss[LAYER_SRC.get(name, 0)]
+                items.append(q._Proj(self.imgs[c][i].data_ptr(), n, k, ws.data_ptr(), self.ys[i].data_ptr()))
+            self.projs.append(ctypes_arr(q._Proj, items))
+
+    def alg_bytes_gemv(self):
+        """Algorithmic bytes of one set launch: weights + q8 rows (codes + fp32 scales) + fp32 outputs."""
+        act = 1.0 + 4.0 / 32 + (4.0 / 32 if self.fmt == self.q.Q4_0 else 0.0)
+        return self.wbytes + sum(self.rows * k * act + self.rows * n * 4 for _, n, k in self.layer)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: this build runs the GEMV on a single MI355X and has no multi-GPU "
+              "path; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from block_quantized_few_amd import qgemv as q
+    from block_quantized_few_amd import synth
+
+    torch.cuda.set_device(0)
+    L = q.lib()
+    stream = torch.cuda.current_stream()
+    sh = C.c_void_p(stream.cuda_stream)
+    timer = Timer(torch)
+
+    # ------------------------------------------------------------ headline ---
+    rows = 1
+    t_setup = time.time()
+    layer = LayerSet(torch, q, synth, LAYER_1B, q.Q8_0, 1, rows)
+    torch.cuda.synchronize()
+    print(f"[bench] 1B layer Q8_0: {layer.copies} copies x {layer.wbytes} B ready in {time.time() - t_setup:.1f}s",
+          file=sys.stderr, flush=True)
+
+    def step(i, ev=None):
+        c = i % layer.copies
+        L.qg_prepare_rows_set(layer.acts, 3, rows, sh)
+        if ev is not None:
+            ev[0].record(stream)
+        L.qgemv_set(q.Q8_0, layer.projs[c], 7, rows, sh)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    timer.hold(max(20.0, K * 0.08))
+    start.record(stream)
+    h0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    host_ms = (time.perf_counter() - h0) * 1e3
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    gemv_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    gemv_avg_ms = sum(gemv_ms) / K
+    # a host-side check that the layer outputs are finite (no silent garbage)
+    assert all(bool(torch.isfinite(y).all()) for y in layer.ys)
+
+    value = layer.wbytes / (ms_per_step * 1e-3) / 1e9
+    alg = layer.alg_bytes_gemv()
+    achieved = alg / (gemv_avg_ms * 1e-3) / 1e9
+    kname = "qgemv_set_kernel<Q8_0, rows 1, T 1>"
+    traffic = read_traffic("qgemv_set_kernel", "llama1b-layer-q8_0-rows1")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "pct_hbm_roofline": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "config": {"workload": "llama-3.2-1b-shaped decode layer, Q8_0 weights, q8 activations",
+                   "rows": rows, "projections": [f"{nm} {n}x{k}" for nm, n, k in LAYER_1B],
+                   "weight_bytes_per_step": layer.wbytes, "rotation_copies": layer.copies,
+                   "launches_per_step": 2, "parallelism": "single GPU"},
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": int(alg), "avg_launch_us": round(gemv_avg_ms * 1e3, 3),
+                     "median_launch_us": round(gemv_ms[K // 2] * 1e3, 3)},
+        "host_enqueue_ms": round(host_ms, 3),
+    }
+
+    # ---------------------------------------------------------- CPU oracle ---
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(torch, synth, layer)
+
+    # --------------------------------------------------------------- sweep ---
+    if not args.no_sweep:
+        result["sweep"] = sweep(torch, q, synth, L, sh, stream, timer, layer)
+
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+# ----------------------------------------------------------------- oracle ---
+def cpu_baseline(torch, synth, layer):
+    """The C oracle on the headline layer (copy 0, same rows), on the host's cores, for about 10 s."""
+    import oracle as O
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    blocks = []
+    for i, (_, n, k) in enumerate(LAYER_1B):
+        w = synth.gaussian((n, k), 0.02, synth.tensor_seed(1, i, 0), device="cuda").cpu().numpy()
+        blocks.append(O.quantize_weights(O.Q8_0, w))
+    xs = [x.cpu().numpy() for x in layer.xs]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for i, (name, n, k) in enumerate(LAYER_1B):
+            O.gemv_q(O.Q8_0, blocks[i], n, k, xs[LAYER_SRC.get(name, 0)], threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0:
+            break
+    return {"value": round(layer.wbytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "ms_per_step": round(el / reps * 1e3, 3),
+            "sample": f"the headline layer's 7 Q8_0 projections at rows={layer.rows}, {reps} reps in {el:.1f}s"}
+
+
+# ------------------------------------------------------------------ sweep ---
+def time_calls(torch, timer, stream, fn, iters):
+    for i in range(min(iters, 5)):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.hold(max(10.0, iters * 0.1))
+    a.record(stream)
+    for i in range(iters):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def entry(workload, lane, rows, wbytes, ms, launches):
+    gbps = wbytes / (ms * 1e-3) / 1e9
+    return {"workload": workload, "lane": lane, "rows": rows, "weight_bytes": int(wbytes), "launches": launches,
+            "us_per_call": round(ms * 1e3, 3), "weight_gbps": round(gbps, 1),
+            "pct_hbm": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+
+
+def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
+    out = []
+    ROWSW = [1, 2, 4, 8, 9, 16]
+    t0 = time.time()
+
+    # Q8_0 1024x1024, one GEMV (quantize + GEMV launches)
+    n = k = 1024
+    wb = q.image_bytes(q.Q8_0, n, k)
+    copies = math.ceil((1 << 30) / wb)
+    big = synth.gaussian((copies * n, k), 0.02, synth.tensor_seed(0, 0), device="cuda")
+    imgs = [q.quantize_weights(q.Q8_0, big[c * n:(c + 1) * n]) for c in range(copies)]
+    del big
+    for rows in ROWSW:
+        x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(0, 32 + rows), device="cuda")
+        y = torch.empty((rows, n), device="cuda")
+        ws = q.empty_ws(rows, k)
+        xp, yp, wp, wn = x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel()
+        ptrs = [im.data_ptr() for im in imgs]
+        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_q8_0(ptrs[i % copies], n, k, xp, rows, yp, wp, wn, sh),
+                        400)
+        out.append(entry("q8_0 1024x1024", "q8_0", rows, wb, ms, 2))
+    del imgs
+    print(f"[bench] sweep 1024x1024 done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # decode layers (set launch): 1B Q8_0 and 3B Q4_0
+    for lname, lay, fmt, wl, lane, obj in (("llama-3.2-1b layer", LAYER_1B, q.Q8_0, 1, "q8_0", layer1b),
+                                           ("llama-3.2-3b layer", LAYER_3B, q.Q4_0, 2, "q4_0", None)):
+        ls = obj or LayerSet(torch, q, synth, lay, fmt, wl, 1)
+        for rows in ROWSW:
+            ls.set_rows(rows, synth, wl)
+
+            def one(i, ls=ls, rows=rows, fmt=fmt):
+                L.qg_prepare_rows_set(ls.acts, 3, rows, sh)
+                L.qgemv_set(fmt, ls.projs[i % ls.copies], 7, rows, sh)
+
+            ms = time_calls(torch, timer, stream, one, 200)
+            out.append(entry(f"{lname} (7 projections)", lane, rows, ls.wbytes, ms, 2))
+        del ls
+        print(f"[bench] sweep {lname} done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    layer1b.set_rows(1, synth, 1)
+
+    # LM head 128256 x 4096, f16 and Q8_0, two copies each
+    n, k = 128256, 4096
+    w16 = []
+    q8 = []
+    for c in range(2):
+        w = synth.gaussian((n, k), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
+        w16.append(w.half())
+        q8.append(q.quantize_weights(q.Q8_0, w))
+        del w
+    for rows in (1, 2, 4, 8, 9, 16):
+        x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(4, 32 + rows), device="cuda")
+        y = torch.empty((rows, n), device="cuda")
+        ws = q.empty_ws(rows, k)
+        xp, yp, wp, wn = x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel()
+        p16 = [t.data_ptr() for t in w16]
+        p8 = [t.data_ptr() for t in q8]
+        ms = time_calls(torch, timer, stream, lambda i: L.gemv_f16(p16[i % 2], n, k, xp, rows, yp, sh), 40)
+        out.append(entry("lm head 128256x4096", "f16", rows, 2 * n * k, ms, 1))
+        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_q8_0(p8[i % 2], n, k, xp, rows, yp, wp, wn, sh), 40)
+        out.append(entry("lm head 128256x4096", "q8_0", rows, q.image_bytes(q.Q8_0, n, k), ms, 2))
+    del w16, q8
+    print(f"[bench] sweep lm head done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    out.extend(moe_sweep(torch, q, synth, L, sh, stream, timer))
+    print(f"[bench] sweep moe done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    return out
+
+
+def moe_sweep(torch, q, synth, L, sh, stream, timer):
+    """Routed MoE step: router f16 GEMV, top-8 routing, grouped gate/up, SwiGLU, grouped down, combine."""
+    hidden, ffn, E, topk = 2048, 512, 256, 8
+    nimg = E + 1  # index E: the shared expert
+    gu_b = q.image_bytes(q.Q8_0, 2 * ffn, hidden)
+    dn_b = q.image_bytes(q.Q8_0, hidden, ffn)
+    copies = 2
+    gus, dns = [], []
+    for c in range(copies):
+        gu = torch.empty(nimg * gu_b, dtype=torch.uint8, device="cuda")
+        dn = torch.empty(nimg * dn_b, dtype=torch.uint8, device="cuda")
+        for e in range(nimg):
+            w = synth.gaussian((2 * ffn, hidden), 0.02, synth.tensor_seed(3, 1 + 3 * e, c), device="cuda")
+            q.quantize_weights(q.Q8_0, w, gu[e * gu_b:(e + 1) * gu_b])
+            w = synth.gaussian((hidden, ffn), 0.02, synth.tensor_seed(3, 3 + 3 * e, c), device="cuda")
+            q.quantize_weights(q.Q8_0, w, dn[e * dn_b:(e + 1) * dn_b])
+        gus.append(gu)
+        dns.append(dn)
+    router = synth.gaussian((E, hidden), 0.02, synth.tensor_seed(3, 0), device="cuda").half()
+    out = []
+    for rows in (1, 8, 9, 16):
+        slots = topk + 1
+        m = rows * slots
+        nx = 64
+        xs = [synth.gaussian((rows, hidden), 1.0, synth.tensor_seed(3, 32 + rows, s), device="cuda") for s in range(nx)]
+        logits = torch.empty((rows, E), device="cuda")
+        expert = torch.empty(m, dtype=torch.int32, device="cuda")
+        xidx = torch.empty(m, dtype=torch.int32, device="cuda")
+        wgt = torch.empty(m, device="cuda")
+        gu_y = torch.empty((m, 2 * ffn), device="cuda")
+        h = torch.empty((m, ffn), device="cuda")
+        o = torch.empty((m, hidden), device="cuda")
+        y = torch.empty((rows, hidden), device="cuda")
+        ident = torch.arange(m, dtype=torch.int32, device="cuda")
+        ws1 = torch.empty(q.grouped_workspace_bytes(rows, hidden, m), dtype=torch.uint8, device="cuda")
+        ws2 = torch.empty(q.grouped_workspace_bytes(m, ffn, m), dtype=torch.uint8, device="cuda")
+        P = lambda t: t.data_ptr()
+        xps = [P(x) for x in xs]
+
+        def one(i):
+            c = i % copies
+            xp = xps[i % nx]
+            L.gemv_f16(P(router), E, hidden, xp, rows, P(logits), sh)
+            L.qg_moe_route(P(logits), rows, E, topk, E, P(expert), P(xidx), P(wgt), sh)
+            L.qgemv_q8_0_grouped(P(gus[c]), nimg, 2 * ffn, hidden, xp, rows, P(expert), P(xidx), m, P(gu_y), P(ws1),
+                                 ws1.numel(), sh)
+            L.qg_swiglu(P(gu_y), m, ffn, P(h), sh)
+            L.qgemv_q8_0_grouped(P(dns[c]), nimg, hidden, ffn, P(h), m, P(expert), P(ident), m, P(o), P(ws2),
+                                 ws2.numel(), sh)
+            L.qg_moe_combine(P(o), P(wgt), rows, slots, hidden, P(y), sh)
+
+        ms = time_calls(torch, timer, stream, one, 128)
+        # weight bytes actually streamed: router + every touched expert (the shared one included)
+        uniq = []
+        for s in range(nx):
+            one(s)
+            torch.cuda.synchronize()
+            uniq.append(len(set(expert.cpu().tolist())))
+        u = sum(uniq) / nx
+        wb = 2 * E * hidden + u * (gu_b + dn_b)
+        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms, 10)
+        e["unique_experts"] = round(u, 2)
+        out.append(e)
+    return out
+
+
+if __name__ == "__main__":
+    main()
