@@ -35,6 +35,16 @@ constexpr int FMT_Q8 = 1, FMT_Q4 = 2;
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Streaming load of weight bytes that are read exactly once: the non-temporal
+// hint keeps them from displacing the activation rows in the caches.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t ld2_stream(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ float h2f(uint16_t h) {
   _Float16 v;
   __builtin_memcpy(&v, &h, 2);
@@ -241,34 +251,121 @@ struct Prep {
   const int* nsx;
 };
 
+// Lanes that share one weight row, chosen from the row's block count alone so
+// that a row's fp32 summation order never depends on the launch: each lane
+// ends up holding about four blocks of every row it serves.
+__host__ __device__ inline int lanes_per_row(int kbp) {
+  if (kbp >= 256 && kbp % 64 == 0) return 64;
+  if (kbp >= 128 && kbp % 32 == 0) return 32;
+  return 16;
+}
+
+// LDS bytes of one staged block of one activation row (codes, scale, Q4 start).
+__host__ __device__ inline int x_block_bytes(int fmt) { return fmt == FMT_Q4 ? 40 : 36; }
+
 // Blocks per LDS chunk for R rows (multiple of 16, at most kbp).
 __host__ __device__ inline int chunk_blocks(int R, int fmt, int kbp, int budget) {
-  int per = R * (fmt == FMT_Q4 ? 40 : 36);
-  int cb = (budget / per) / GROUP * GROUP;
+  int cb = (budget / (R * x_block_bytes(fmt))) / GROUP * GROUP;
   if (cb < GROUP) cb = GROUP;
   return cb < kbp ? cb : kbp;
 }
 
-// One workgroup's tile: weight rows row0 .. row0 + 16*T - 1 of one image,
-// against R activation rows.  s_src[r] is the prepared row feeding activation
-// row r and s_dst[r] the output row it lands in (both in LDS).
+// Stage blocks [cb0, cb0 + cbn) of the R activation rows into LDS: codes
+// [R][cbn*32], then scales [R][cbn], then (Q4) start values [R][cbn].
+template <int FMT, int R>
+__device__ __forceinline__ void stage_rows(uint8_t* lds, const Prep& prep, const int* s_src, int kbp, int cb0,
+                                           int cbn) {
+  int8_t* l_codes = reinterpret_cast<int8_t*>(lds);
+  float* l_dx = reinterpret_cast<float*>(lds + (size_t)R * cbn * 32);
+  int* l_nsx = reinterpret_cast<int*>(lds + (size_t)R * cbn * 36);
+  const int tid = threadIdx.x;
+  const int cu = cbn * 2;  // 16-byte units of codes per row
+  for (int u = tid; u < R * cu; u += WG) {
+    const int r = u / cu, c = u - r * cu;
+    reinterpret_cast<uint4*>(l_codes)[u] =
+        reinterpret_cast<const uint4*>(prep.codes + (size_t)s_src[r] * kbp * 32 + (size_t)cb0 * 32)[c];
+  }
+  const int su = cbn / 4;  // 16-byte units of scales per row
+  for (int u = tid; u < R * su; u += WG) {
+    const int r = u / su, c = u - r * su;
+    reinterpret_cast<uint4*>(l_dx)[u] = reinterpret_cast<const uint4*>(prep.dx + (size_t)s_src[r] * kbp + cb0)[c];
+    if (FMT == FMT_Q4)
+      reinterpret_cast<uint4*>(l_nsx)[u] =
+          reinterpret_cast<const uint4*>(prep.nsx + (size_t)s_src[r] * kbp + cb0)[c];
+  }
+}
+
+// acc[t][r] += blocks [cb0, cb0 + cbn) of weight row t against activation row
+// r (staged in LDS with a row stride of cbn blocks).  Lane j of the row's lpr
+// lanes takes blocks j, j + lpr, ...; each block's integer dot is exact.
+template <int FMT, int R, int T>
+__device__ __forceinline__ void accumulate(float (&acc)[T][R], const uint8_t* const (&wrow)[T],
+                                           const uint16_t* const (&drow)[T], const uint8_t* lds, int cb0, int cbn,
+                                           int lpr, int j) {
+  const int8_t* l_codes = reinterpret_cast<const int8_t*>(lds);
+  const float* l_dx = reinterpret_cast<const float*>(lds + (size_t)R * cbn * 32);
+  const int* l_nsx = reinterpret_cast<const int*>(lds + (size_t)R * cbn * 36);
+  const int jo = (j % GROUP) * 16;
+#pragma unroll 2
+  for (int b = j; b < cbn; b += lpr) {
+    const int gb = cb0 + b;
+    uint4 wl[T], wh[T];
+    float dw[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      if (FMT == FMT_Q8) {
+        const uint8_t* p = wrow[t] + (size_t)(gb / GROUP) * 512 + jo;
+        wl[t] = ld16_stream(p);
+        wh[t] = ld16_stream(p + 256);
+      } else {
+        wl[t] = ld16_stream(wrow[t] + (size_t)gb * 16);
+      }
+      dw[t] = h2f(ld2_stream(drow[t] + gb));
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int8_t* xb = l_codes + (size_t)r * cbn * 32 + (b / GROUP) * 512 + jo;
+      const uint4 xl = ld16(xb), xh = ld16(xb + 256);
+      const float dxr = l_dx[r * cbn + b];
+      const int ns = FMT == FMT_Q4 ? l_nsx[r * cbn + b] : 0;
+#pragma unroll
+      for (int t = 0; t < T; t++) {
+        const int isum = FMT == FMT_Q8 ? dot_q8(wl[t], wh[t], xl, xh) : dot_q4(wl[t], xl, xh, ns);
+        acc[t][r] = __builtin_fmaf((float)isum, dw[t] * dxr, acc[t][r]);
+      }
+    }
+  }
+}
+
+// Sum over the lpr lanes of a row (fixed tree; every lane gets the same bits).
+__device__ __forceinline__ float sum_lanes(float v, int lpr) {
+  v = sum16(v);
+  if (lpr >= 32) v += __shfl_xor(v, 16);
+  if (lpr >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// One tile of one image: weight rows row0 + t*slots + s (t < T, slot s <
+// WG/lpr) against R activation rows.  s_src[r] names the prepared row that
+// feeds activation row r and s_dst[r] the output row it lands in (both LDS).
+// `staged`: all kbp blocks of the rows are already in LDS; otherwise they are
+// staged here in chunks that fit lds_bytes.
 template <int FMT, int R, int T>
 __device__ __forceinline__ void qgemv_tile(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ dsc,
-                                           int64_t N, int kbp, int64_t row0, Prep prep, const int* s_src,
+                                           int64_t N, int kbp, int64_t row0, const Prep& prep, const int* s_src,
                                            float* __restrict__ y, int64_t ldy, const int* s_dst, uint8_t* lds,
-                                           int cbmax) {
+                                           int lds_bytes, bool staged) {
   constexpr int CODE_B = FMT == FMT_Q8 ? 32 : 16;
-  const int tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
-  const int slot = lane / LPR, j = lane % LPR;
-
+  const int lpr = lanes_per_row(kbp);
+  const int slots = WG / lpr;
+  const int slot = threadIdx.x / lpr, j = threadIdx.x % lpr;
   int64_t n[T];
   bool valid[T];
   const uint8_t* wrow[T];
   const uint16_t* drow[T];
 #pragma unroll
   for (int t = 0; t < T; t++) {
-    n[t] = row0 + (int64_t)((wave * T + t) * SLOTS + slot);
+    n[t] = row0 + (int64_t)(t * slots + slot);
     valid[t] = n[t] < N;
     const int64_t nc = valid[t] ? n[t] : N - 1;  // out-of-range slots read a real row, store nothing
     wrow[t] = qs + nc * kbp * CODE_B;
@@ -279,72 +376,30 @@ __device__ __forceinline__ void qgemv_tile(const uint8_t* __restrict__ qs, const
   for (int t = 0; t < T; t++)
 #pragma unroll
     for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
-
-  for (int cb0 = 0; cb0 < kbp; cb0 += cbmax) {
-    const int cbn = min(cbmax, kbp - cb0);
-    int8_t* l_codes = reinterpret_cast<int8_t*>(lds);
-    float* l_dx = reinterpret_cast<float*>(lds + (size_t)R * cbn * 32);
-    int* l_nsx = reinterpret_cast<int*>(lds + (size_t)R * cbn * 36);
-    if (cb0) __syncthreads();
-    // Stage this chunk of every activation row (codes, scales, Q4 start values).
-    const int cu = cbn * 2;  // 16-byte units of codes per row
-    for (int u = tid; u < R * cu; u += WG) {
-      const int r = u / cu, c = u - r * cu;
-      reinterpret_cast<uint4*>(l_codes)[u] =
-          reinterpret_cast<const uint4*>(prep.codes + (size_t)s_src[r] * kbp * 32 + (size_t)cb0 * 32)[c];
-    }
-    const int su = cbn / 4;  // 16-byte units of scales per row
-    for (int u = tid; u < R * su; u += WG) {
-      const int r = u / su, c = u - r * su;
-      reinterpret_cast<uint4*>(l_dx)[u] =
-          reinterpret_cast<const uint4*>(prep.dx + (size_t)s_src[r] * kbp + cb0)[c];
-      if (FMT == FMT_Q4)
-        reinterpret_cast<uint4*>(l_nsx)[u] =
-            reinterpret_cast<const uint4*>(prep.nsx + (size_t)s_src[r] * kbp + cb0)[c];
-    }
-    __syncthreads();
-
-#pragma unroll 2
-    for (int b = j; b < cbn; b += LPR) {
-      const int gb = cb0 + b;
-      uint4 wl[T], wh[T];
-      float dw[T];
-#pragma unroll
-      for (int t = 0; t < T; t++) {
-        if (FMT == FMT_Q8) {
-          const uint8_t* p = wrow[t] + (size_t)(gb / GROUP) * 512 + j * 16;
-          wl[t] = ld16(p);
-          wh[t] = ld16(p + 256);
-        } else {
-          wl[t] = ld16(wrow[t] + (size_t)gb * 16);
-        }
-        dw[t] = h2f(drow[t][gb]);
-      }
-#pragma unroll
-      for (int r = 0; r < R; r++) {
-        const int8_t* xb = l_codes + (size_t)r * cbn * 32 + (b / GROUP) * 512 + j * 16;
-        const uint4 xl = ld16(xb), xh = ld16(xb + 256);
-        const float dxr = l_dx[r * cbn + b];
-        const int ns = FMT == FMT_Q4 ? l_nsx[r * cbn + b] : 0;
-#pragma unroll
-        for (int t = 0; t < T; t++) {
-          const int isum = FMT == FMT_Q8 ? dot_q8(wl[t], wh[t], xl, xh) : dot_q4(wl[t], xl, xh, ns);
-          acc[t][r] = __builtin_fmaf((float)isum, dw[t] * dxr, acc[t][r]);
-        }
-      }
+  if (staged) {
+    accumulate<FMT, R, T>(acc, wrow, drow, lds, 0, kbp, lpr, j);
+  } else {
+    const int cbmax = chunk_blocks(R, FMT, kbp, lds_bytes);
+    for (int cb0 = 0; cb0 < kbp; cb0 += cbmax) {
+      const int cbn = min(cbmax, kbp - cb0);
+      __syncthreads();  // earlier readers of LDS are done
+      stage_rows<FMT, R>(lds, prep, s_src, kbp, cb0, cbn);
+      __syncthreads();
+      accumulate<FMT, R, T>(acc, wrow, drow, lds, cb0, cbn, lpr, j);
     }
   }
 #pragma unroll
   for (int t = 0; t < T; t++)
 #pragma unroll
     for (int r = 0; r < R; r++) {
-      const float v = sum16(acc[t][r]);
+      const float v = sum_lanes(acc[t][r], lpr);
       if (valid[t] && j == r) y[(int64_t)s_dst[r] * ldy + n[t]] = v;
     }
 }
 
-// Up to QG_MAX_SET projections (same rows) in one launch; blockIdx.x walks
-// the projections' row tiles in order.
+// Up to QG_MAX_SET projections (same rows) in one launch.  Tiles are numbered
+// projection by projection; workgroup g takes tiles g, g + G, g + 2G, ... and
+// keeps a projection's activation rows in LDS while its tiles last.
 struct ProjDev {
   const uint8_t* qs;
   const uint16_t* dsc;
@@ -353,27 +408,40 @@ struct ProjDev {
   int64_t n;
   int kbp;
   int tiles;
+  int rows_per_tile;
 };
 struct SetArgs {
   ProjDev p[QG_MAX_SET];
   int count;
+  int total_tiles;
 };
 
 template <int FMT, int R, int T>
-__global__ __launch_bounds__(WG) void qgemv_set_kernel(SetArgs a, int cb_budget) {
+__global__ __launch_bounds__(WG) void qgemv_set_kernel(SetArgs a, int lds_bytes) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
-  int tile = blockIdx.x, p = 0;
-  while (p + 1 < a.count && tile >= a.p[p].tiles) tile -= a.p[p++].tiles;
-  if (threadIdx.x < R) {
+  if (threadIdx.x < QG_MAX_ROWS) {
     s_map[threadIdx.x] = threadIdx.x;
     s_map[QG_MAX_ROWS + threadIdx.x] = threadIdx.x;
   }
   __syncthreads();
-  const ProjDev& d = a.p[p];
-  const int cbmax = chunk_blocks(R, FMT, d.kbp, cb_budget);
-  qgemv_tile<FMT, R, T>(d.qs, d.dsc, d.n, d.kbp, (int64_t)tile * (WAVES * SLOTS * T), d.prep, s_map, d.y, d.n,
-                        s_map + QG_MAX_ROWS, lds, cbmax);
+  int staged = -1;
+  for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
+    int p = 0, t0 = tile;
+    while (p + 1 < a.count && t0 >= a.p[p].tiles) t0 -= a.p[p++].tiles;
+    const ProjDev& d = a.p[p];
+    const bool fits = R * d.kbp * x_block_bytes(FMT) <= lds_bytes;
+    if (fits && p != staged) {
+      __syncthreads();
+      stage_rows<FMT, R>(lds, d.prep, s_map, d.kbp, 0, d.kbp);
+      __syncthreads();
+      staged = p;
+    } else if (!fits) {
+      staged = -1;
+    }
+    qgemv_tile<FMT, R, T>(d.qs, d.dsc, d.n, d.kbp, (int64_t)t0 * d.rows_per_tile, d.prep, s_map, d.y, d.n,
+                          s_map + QG_MAX_ROWS, lds, lds_bytes, fits);
+  }
 }
 
 // ------------------------------------------------------------- grouped ---
@@ -441,7 +509,7 @@ __global__ __launch_bounds__(WG) void qgemv_grouped_kernel(const uint8_t* __rest
                                                            const int* __restrict__ sorted,
                                                            const int* __restrict__ items,
                                                            const int32_t* __restrict__ x_index, float* y,
-                                                           int cb_budget) {
+                                                           int lds_bytes) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   const int item = blockIdx.y;
@@ -455,12 +523,12 @@ __global__ __launch_bounds__(WG) void qgemv_grouped_kernel(const uint8_t* __rest
   __syncthreads();
   const uint8_t* img = images + (size_t)e * expert_bytes;
   const uint16_t* dsc = reinterpret_cast<const uint16_t*>(img + scale_off);
-  const int64_t row0 = (int64_t)blockIdx.x * (WAVES * SLOTS * T);
+  const int64_t row0 = (int64_t)blockIdx.x * ((WG / lanes_per_row(kbp)) * T);
   switch (cnt) {
 #define QG_CASE(RR)                                                                                                \
   case RR:                                                                                                         \
-    qgemv_tile<FMT_Q8, RR, T>(img, dsc, N, kbp, row0, prep, s_map, y, N, s_map + QG_MAX_ROWS, lds,              \
-                              chunk_blocks(RR, FMT_Q8, kbp, cb_budget));                                          \
+    qgemv_tile<FMT_Q8, RR, T>(img, dsc, N, kbp, row0, prep, s_map, y, N, s_map + QG_MAX_ROWS, lds, lds_bytes,    \
+                              false);                                                                             \
     break;
     QG_CASE(1) QG_CASE(2) QG_CASE(3) QG_CASE(4) QG_CASE(5) QG_CASE(6) QG_CASE(7) QG_CASE(8)
     QG_CASE(9) QG_CASE(10) QG_CASE(11) QG_CASE(12) QG_CASE(13) QG_CASE(14) QG_CASE(15) QG_CASE(16)
@@ -535,7 +603,7 @@ __global__ __launch_bounds__(WG) void gemv_f16_kernel(const uint16_t* __restrict
     for (int c = j; c * 8 < cen; c += LPR) {
       uint4 wv[T];
 #pragma unroll
-      for (int t = 0; t < T; t++) wv[t] = ld16(wrow[t] + c0 + c * 8);
+      for (int t = 0; t < T; t++) wv[t] = ld16_stream(wrow[t] + c0 + c * 8);
 #pragma unroll
       for (int r = 0; r < R; r++) {
         const float4 x0 = *reinterpret_cast<const float4*>(l_x + (size_t)r * ce + c * 8);
@@ -675,24 +743,44 @@ static int launched(const char* what) { return hip_status(hipGetLastError(), wha
 
 static unsigned grid1(int64_t threads, int per) { return (unsigned)((threads + per - 1) / per); }
 
-// Rows per workgroup tile: T = 2 when that still yields enough workgroups.
-static int pick_t(int64_t total_rows) {
-  return (total_rows + 31) / 32 >= 1024 ? 2 : 1;
+// Weight rows per lane group: T = 2 when that still yields enough tiles.
+static int pick_t(int64_t total_rows) { return (total_rows + 31) / 32 >= 1024 ? 2 : 1; }
+
+constexpr int LDS_MAX = 80 * 1024;  // staged activation rows: at least two workgroups per CU
+
+static int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  }
+  return cus;
+}
+
+// Workgroups to launch: no more than the device holds at once (the kernel
+// loops over the remaining tiles) and no more than there are tiles.
+template <typename K>
+static unsigned persistent_grid(K kernel, size_t lds, int64_t tiles) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WG, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t g = (int64_t)device_cus() * per_cu;
+  return (unsigned)(tiles < g ? tiles : g);
 }
 
 template <int FMT, int R, int T>
-static void launch_set_rt(const SetArgs& a, unsigned grid, hipStream_t s) {
-  int maxkbp = 0;
-  for (int i = 0; i < a.count; i++) maxkbp = a.p[i].kbp > maxkbp ? a.p[i].kbp : maxkbp;
-  const size_t lds = (size_t)R * chunk_blocks(R, FMT, maxkbp, LDS_BUDGET) * (FMT == FMT_Q4 ? 40 : 36);
-  hipLaunchKernelGGL((qgemv_set_kernel<FMT, R, T>), dim3(grid), dim3(WG), lds, s, a, LDS_BUDGET);
+static void launch_set_rt(const SetArgs& a, size_t lds, hipStream_t s) {
+  auto kern = qgemv_set_kernel<FMT, R, T>;
+  if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const unsigned grid = persistent_grid(kern, lds, a.total_tiles);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WG), lds, s, a, (int)lds);
 }
 
 template <int FMT, int T>
-static void launch_set_t(const SetArgs& a, int rows, unsigned grid, hipStream_t s) {
+static void launch_set_t(const SetArgs& a, int rows, size_t lds, hipStream_t s) {
   switch (rows) {
 #define QG_R(RR) \
-  case RR: launch_set_rt<FMT, RR, T>(a, grid, s); break;
+  case RR: launch_set_rt<FMT, RR, T>(a, lds, s); break;
     QG_R(1) QG_R(2) QG_R(3) QG_R(4) QG_R(5) QG_R(6) QG_R(7) QG_R(8)
     QG_R(9) QG_R(10) QG_R(11) QG_R(12) QG_R(13) QG_R(14) QG_R(15) QG_R(16)
 #undef QG_R
@@ -700,28 +788,27 @@ static void launch_set_t(const SetArgs& a, int rows, unsigned grid, hipStream_t 
 }
 
 static int launch_set(int fmt, SetArgs& a, int rows, hipStream_t s) {
-  // Longest rows first, so the heaviest tiles are dispatched first and the
-  // launch does not end on a tail of long tiles (stable insertion sort).
-  for (int i = 1; i < a.count; i++)
-    for (int j = i; j > 0 && a.p[j].kbp > a.p[j - 1].kbp; j--) {
-      ProjDev t = a.p[j];
-      a.p[j] = a.p[j - 1];
-      a.p[j - 1] = t;
-    }
-  int64_t total = 0;
-  for (int i = 0; i < a.count; i++) total += a.p[i].n;
-  const int T = pick_t(total);
+  int64_t total_rows = 0;
+  for (int i = 0; i < a.count; i++) total_rows += a.p[i].n;
+  const int T = pick_t(total_rows);
   int64_t tiles = 0;
+  size_t lds = 0;
   for (int i = 0; i < a.count; i++) {
-    a.p[i].tiles = (int)((a.p[i].n + 16 * T - 1) / (16 * T));
-    tiles += a.p[i].tiles;
+    ProjDev& d = a.p[i];
+    d.rows_per_tile = (WG / lanes_per_row(d.kbp)) * T;
+    d.tiles = (int)((d.n + d.rows_per_tile - 1) / d.rows_per_tile);
+    tiles += d.tiles;
+    const size_t x = (size_t)rows * d.kbp * x_block_bytes(fmt);
+    lds = x > lds ? x : lds;
   }
+  if (lds > (size_t)LDS_MAX) lds = LDS_MAX;  // larger rows are staged in chunks
+  a.total_tiles = (int)tiles;
   if (fmt == FMT_Q8) {
-    if (T == 2) launch_set_t<FMT_Q8, 2>(a, rows, (unsigned)tiles, s);
-    else launch_set_t<FMT_Q8, 1>(a, rows, (unsigned)tiles, s);
+    if (T == 2) launch_set_t<FMT_Q8, 2>(a, rows, lds, s);
+    else launch_set_t<FMT_Q8, 1>(a, rows, lds, s);
   } else {
-    if (T == 2) launch_set_t<FMT_Q4, 2>(a, rows, (unsigned)tiles, s);
-    else launch_set_t<FMT_Q4, 1>(a, rows, (unsigned)tiles, s);
+    if (T == 2) launch_set_t<FMT_Q4, 2>(a, rows, lds, s);
+    else launch_set_t<FMT_Q4, 1>(a, rows, lds, s);
   }
   return launched("qgemv_set_kernel");
 }
@@ -975,16 +1062,23 @@ int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64
   prep.nsx = (const int*)(w + G.prep + L.nsx);
   const int kbp = (int)kbp_of(k);
   const int T = pick_t(n * 8);
-  const unsigned tiles = (unsigned)((n + 16 * T - 1) / (16 * T));
-  const size_t lds = (size_t)QG_MAX_ROWS * chunk_blocks(QG_MAX_ROWS, FMT_Q8, kbp, LDS_BUDGET) * 36;
+  const int rpt = (WG / lanes_per_row(kbp)) * T;
+  const unsigned tiles = (unsigned)((n + rpt - 1) / rpt);
+  size_t lds = (size_t)QG_MAX_ROWS * kbp * x_block_bytes(FMT_Q8);
+  if (lds > (size_t)LDS_MAX) lds = LDS_MAX;
   const int64_t eb = (int64_t)image_total_bytes(QG_FMT_Q8_0, n, k);
   const size_t so = image_scale_offset(QG_FMT_Q8_0, n, k);
-  if (T == 2)
+  if (T == 2) {
+    if (lds > 64 * 1024)
+      hipFuncSetAttribute((const void*)qgemv_grouped_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(qgemv_grouped_kernel<2>, dim3(tiles, m), dim3(WG), lds, s, (const uint8_t*)w_images, eb, so, n,
                        kbp, prep, header, sorted, items, x_index, y, (int)lds);
-  else
+  } else {
+    if (lds > 64 * 1024)
+      hipFuncSetAttribute((const void*)qgemv_grouped_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(qgemv_grouped_kernel<1>, dim3(tiles, m), dim3(WG), lds, s, (const uint8_t*)w_images, eb, so, n,
                        kbp, prep, header, sorted, items, x_index, y, (int)lds);
+  }
   if (int st = launched("qgemv_grouped_kernel")) return st;
   return ok();
 }
