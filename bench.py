@@ -128,15 +128,16 @@ class LayerSet:
         self.xs = [synth.gaussian((rows, k), 1.0, synth.tensor_seed(workload, tid), device="cuda") for tid, k in seeds]
         self.wss = [q.empty_ws(rows, x.shape[1]) for x in self.xs]
         self.ys = [torch.empty((rows, n), dtype=torch.float32, device="cuda") for _, n, _ in self.layer]
-        self.acts = ctypes_arr(q._Act, [q._Act(x.data_ptr(), x.shape[1], w.data_ptr(), w.numel())
-                                        for x, w in zip(self.xs, self.wss)])
         self.projs = []
         for c in range(self.copies):
             items = []
             for i, (name, n, k) in enumerate(self.layer):
-                ws = self.wss[LAYER_SRC.get(name, 0)]
-                items.append(q._Proj(self.imgs[c][i].data_ptr(), n, k, ws.data_ptr(), self.ys[i].data_ptr()))
-            self.projs.append(ctypes_arr(q._Proj, items))
+                j = LAYER_SRC.get(name, 0)
+                items.append(q._ProjRows(self.imgs[c][i].data_ptr(), n, k, self.xs[j].data_ptr(),
+                                         self.wss[j].data_ptr(), self.wss[j].numel(), self.ys[i].data_ptr()))
+            self.projs.append(ctypes_arr(q._ProjRows, items))
+        # launches of one step: the GEMV set, plus one quantize launch above the fused row count
+        self.launches = 1 if rows <= q.FUSED_ROWS else 2
 
     def alg_bytes_gemv(self):
         """Algorithmic bytes of one set launch: weights + q8 rows (codes + fp32 scales) + fp32 outputs."""
@@ -170,42 +171,37 @@ def main():
     print(f"[bench] 1B layer Q8_0: {layer.copies} copies x {layer.wbytes} B ready in {time.time() - t_setup:.1f}s",
           file=sys.stderr, flush=True)
 
-    def step(i, ev=None):
-        c = i % layer.copies
-        L.qg_prepare_rows_set(layer.acts, 3, rows, sh)
-        if ev is not None:
-            ev[0].record(stream)
-        L.qgemv_set(q.Q8_0, layer.projs[c], 7, rows, sh)
-        if ev is not None:
-            ev[1].record(stream)
+    def step(i):
+        L.qgemv_set_rows(q.Q8_0, layer.projs[i % layer.copies], 7, rows, sh)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     timer.hold(max(20.0, K * 0.08))
     start.record(stream)
     h0 = time.perf_counter()
     for i in range(K):
-        step(i, evs[i])
+        step(i)
     host_ms = (time.perf_counter() - h0) * 1e3
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
-    gemv_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    gemv_avg_ms = sum(gemv_ms) / K
+    # At one row the step is one launch of the GEMV kernel (quantization fused), so the events around the
+    # K back-to-back steps on the kernel's own stream also give its average launch duration.
+    gemv_avg_ms = ms_per_step / layer.launches if layer.launches == 1 else None
+    gemv_ms = [gemv_avg_ms] * K
     # a host-side check that the layer outputs are finite (no silent garbage)
     assert all(bool(torch.isfinite(y).all()) for y in layer.ys)
 
     value = layer.wbytes / (ms_per_step * 1e-3) / 1e9
     alg = layer.alg_bytes_gemv()
     achieved = alg / (gemv_avg_ms * 1e-3) / 1e9
-    kname = "qgemv_set_kernel<Q8_0, rows 1, T 1>"
-    traffic = read_traffic("qgemv_set_kernel", "llama1b-layer-q8_0-rows1")
+    kname = "rl_set_kernel<Q8_0, rows 1, fused quantization>"
+    traffic = read_traffic("rl_set_kernel", "llama1b-layer-q8_0-rows1")
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -223,7 +219,7 @@ def main():
         "config": {"workload": "llama-3.2-1b-shaped decode layer, Q8_0 weights, q8 activations",
                    "rows": rows, "projections": [f"{nm} {n}x{k}" for nm, n, k in LAYER_1B],
                    "weight_bytes_per_step": layer.wbytes, "rotation_copies": layer.copies,
-                   "launches_per_step": 2, "parallelism": "single GPU"},
+                   "launches_per_step": layer.launches, "parallelism": "single GPU"},
         "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": int(alg), "avg_launch_us": round(gemv_avg_ms * 1e3, 3),
@@ -312,7 +308,7 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
         ptrs = [im.data_ptr() for im in imgs]
         ms = time_calls(torch, timer, stream, lambda i: L.qgemv_q8_0(ptrs[i % copies], n, k, xp, rows, yp, wp, wn, sh),
                         400)
-        out.append(entry("q8_0 1024x1024", "q8_0", rows, wb, ms, 2))
+        out.append(entry("q8_0 1024x1024", "q8_0", rows, wb, ms, 1 if rows <= q.FUSED_ROWS else 2))
     del imgs
     print(f"[bench] sweep 1024x1024 done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
@@ -324,11 +320,10 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
             ls.set_rows(rows, synth, wl)
 
             def one(i, ls=ls, rows=rows, fmt=fmt):
-                L.qg_prepare_rows_set(ls.acts, 3, rows, sh)
-                L.qgemv_set(fmt, ls.projs[i % ls.copies], 7, rows, sh)
+                L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh)
 
             ms = time_calls(torch, timer, stream, one, 200)
-            out.append(entry(f"{lname} (7 projections)", lane, rows, ls.wbytes, ms, 2))
+            out.append(entry(f"{lname} (7 projections)", lane, rows, ls.wbytes, ms, ls.launches))
         del ls
         print(f"[bench] sweep {lname} done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     layer1b.set_rows(1, synth, 1)
@@ -352,7 +347,8 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
         ms = time_calls(torch, timer, stream, lambda i: L.gemv_f16(p16[i % 2], n, k, xp, rows, yp, sh), 40)
         out.append(entry("lm head 128256x4096", "f16", rows, 2 * n * k, ms, 1))
         ms = time_calls(torch, timer, stream, lambda i: L.qgemv_q8_0(p8[i % 2], n, k, xp, rows, yp, wp, wn, sh), 40)
-        out.append(entry("lm head 128256x4096", "q8_0", rows, q.image_bytes(q.Q8_0, n, k), ms, 2))
+        out.append(entry("lm head 128256x4096", "q8_0", rows, q.image_bytes(q.Q8_0, n, k), ms,
+                         1 if rows <= q.FUSED_ROWS else 2))
     del w16, q8
     print(f"[bench] sweep lm head done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 

@@ -1,0 +1,306 @@
+// qg_api.hip -- the C ABI's device entry points: argument validation on the
+// host (a negative status means nothing was enqueued), then the launchers.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "qg_internal.h"
+#include "qg_launch.h"
+#include "qg_layout.h"
+
+using namespace qg;
+
+namespace {
+
+int check_fmt(int fmt) {
+  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1) or Q4_0 (2)", fmt);
+  return QG_OK;
+}
+
+int check_nk(int64_t n, int64_t k) {
+  if (n < 1 || n > (1LL << 31) - 16) return fail(QG_ESHAPE, "n=%lld outside 1..2^31-16", (long long)n);
+  if (k < QK || k % QK || k > (1LL << 24))
+    return fail(QG_ESHAPE, "k=%lld is not a positive multiple of 32 up to 2^24", (long long)k);
+  return QG_OK;
+}
+
+int check_rows(int rows) {
+  if (rows < 0 || rows > QG_MAX_ROWS) return fail(QG_EROWS, "rows=%d outside 0..%d", rows, QG_MAX_ROWS);
+  return QG_OK;
+}
+
+int check_image(const void* image, const char* name) {
+  if (!image) return fail(QG_EINVAL, "%s is null", name);
+  if (!aligned(image, 256)) return fail(QG_EALIGN, "%s %p is not 256-byte aligned", name, image);
+  return QG_OK;
+}
+
+int check_y(const float* y) {
+  if (!y) return fail(QG_EINVAL, "y is null");
+  if (!aligned(y, 4)) return fail(QG_EALIGN, "y %p is not 4-byte aligned", (const void*)y);
+  return QG_OK;
+}
+
+int check_x(const float* x, int rows, int64_t k, int max_rows) {
+  if (!x) return fail(QG_EINVAL, "x is null");
+  if (!aligned(x, 16)) return fail(QG_EALIGN, "x %p is not 16-byte aligned", (const void*)x);
+  if (rows < 1 || rows > max_rows) return fail(QG_EROWS, "rows=%d outside 1..%d", rows, max_rows);
+  if (k < QK || k % QK || k > (1LL << 24))
+    return fail(QG_ESHAPE, "k=%lld is not a positive multiple of 32 up to 2^24", (long long)k);
+  return QG_OK;
+}
+
+int check_ws(const void* ws, size_t have, size_t need, const char* what) {
+  if (!ws) return fail(QG_EINVAL, "%s workspace is null", what);
+  if (!aligned(ws, 256)) return fail(QG_EALIGN, "%s workspace %p is not 256-byte aligned", what, ws);
+  if (have < need) return fail(QG_EWORKSPACE, "ws_bytes=%zu < %zu needed for %s", have, need, what);
+  return QG_OK;
+}
+
+// Q8_0 / Q4_0 GEMV from fp32 rows: rows small enough are quantized inside the
+// GEMV launch, otherwise a quantize launch fills the workspace first.
+int qgemv_fmt(int fmt, const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+              size_t ws_bytes, qg_stream stream) {
+  if (int st = check_rows(rows)) return st;
+  if (int st = check_nk(n, k)) return st;
+  if (int st = check_image(w_image, "w_image")) return st;
+  if (int st = check_y(y)) return st;
+  if (rows == 0) return ok();
+  if (int st = check_x(x, rows, k, QG_MAX_ROWS)) return st;
+  if (int st = check_ws(ws, ws_bytes, prep_layout(rows, k).total, "the activation rows")) return st;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  ProjArg pa{w_image, n, k, ws, nullptr, y};
+  if (fuses_quantization(rows)) {
+    pa.x = x;
+  } else if (int st = launch_prepare(x, rows, k, ws, prep_in_fragment_order(rows), s)) {
+    return st;
+  }
+  if (int st = launch_qgemv_set(fmt, &pa, 1, rows, s)) return st;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, qg_stream stream) {
+  if (int st = check_fmt(fmt)) return st;
+  if (int st = check_nk(n, k)) return st;
+  if (!w) return fail(QG_EINVAL, "w is null");
+  if (!aligned(w, 16)) return fail(QG_EALIGN, "w %p is not 16-byte aligned", (const void*)w);
+  if (int st = check_image(image, "image")) return st;
+  if (int st = check_device()) return st;
+  if (int st = launch_quantize_weights(fmt, w, n, k, image, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qg_prepare_rows(const float* x, int rows, int64_t k, void* ws, size_t ws_bytes, qg_stream stream) {
+  if (int st = check_x(x, rows, k, QG_MAX_PREP_ROWS)) return st;
+  if (int st = check_ws(ws, ws_bytes, prep_layout(rows, k).total, "the activation rows")) return st;
+  if (int st = check_device()) return st;
+  if (int st = launch_prepare(x, rows, k, ws, prep_in_fragment_order(rows), (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qg_prepare_rows_set(const qg_act* acts, int count, int rows, qg_stream stream) {
+  if (!acts || count < 1 || count > QG_MAX_SET) return fail(QG_EINVAL, "count=%d outside 1..%d", count, QG_MAX_SET);
+  for (int i = 0; i < count; i++) {
+    if (int st = check_x(acts[i].x, rows, acts[i].k, QG_MAX_PREP_ROWS)) return fail(st, "acts[%d]: x/rows/k", i);
+    if (int st = check_ws(acts[i].ws, acts[i].ws_bytes, prep_layout(rows, acts[i].k).total, "acts[i]"))
+      return fail(st, "acts[%d]: workspace", i);
+  }
+  if (int st = check_device()) return st;
+  if (int st = launch_prepare_set(acts, count, rows, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
+                   qg_stream stream) {
+  if (int st = check_fmt(fmt)) return st;
+  if (int st = check_rows(rows)) return st;
+  if (int st = check_nk(n, k)) return st;
+  if (int st = check_image(w_image, "w_image")) return st;
+  if (int st = check_y(y)) return st;
+  if (rows == 0) return ok();
+  if (!ws) return fail(QG_EINVAL, "ws is null");
+  if (!aligned(ws, 256)) return fail(QG_EALIGN, "ws %p is not 256-byte aligned", ws);
+  if (int st = check_device()) return st;
+  ProjArg pa{w_image, n, k, ws, nullptr, y};
+  if (int st = launch_qgemv_set(fmt, &pa, 1, rows, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qgemv_q8_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+               size_t ws_bytes, qg_stream stream) {
+  return qgemv_fmt(QG_FMT_Q8_0, w_image, n, k, x, rows, y, ws, ws_bytes, stream);
+}
+
+int qgemv_q4_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+               size_t ws_bytes, qg_stream stream) {
+  return qgemv_fmt(QG_FMT_Q4_0, w_image, n, k, x, rows, y, ws, ws_bytes, stream);
+}
+
+int qgemv_set(int fmt, const qg_proj* projs, int count, int rows, qg_stream stream) {
+  if (int st = check_fmt(fmt)) return st;
+  if (!projs || count < 1 || count > QG_MAX_SET) return fail(QG_EINVAL, "count=%d outside 1..%d", count, QG_MAX_SET);
+  if (int st = check_rows(rows)) return st;
+  ProjArg pa[QG_MAX_SET];
+  for (int i = 0; i < count; i++) {
+    const qg_proj& p = projs[i];
+    if (int st = check_nk(p.n, p.k)) return fail(st, "projs[%d]: n=%lld k=%lld", i, (long long)p.n, (long long)p.k);
+    if (int st = check_image(p.w_image, "w_image")) return fail(st, "projs[%d].w_image null or misaligned", i);
+    if (int st = check_y(p.y)) return fail(st, "projs[%d].y null or misaligned", i);
+    if (!p.ws || !aligned(p.ws, 256)) return fail(QG_EALIGN, "projs[%d].ws null or misaligned", i);
+    pa[i] = ProjArg{p.w_image, p.n, p.k, p.ws, nullptr, p.y};
+  }
+  if (rows == 0) return ok();
+  if (int st = check_device()) return st;
+  if (int st = launch_qgemv_set(fmt, pa, count, rows, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qgemv_set_rows(int fmt, const qg_proj_rows* projs, int count, int rows, qg_stream stream) {
+  if (int st = check_fmt(fmt)) return st;
+  if (!projs || count < 1 || count > QG_MAX_SET) return fail(QG_EINVAL, "count=%d outside 1..%d", count, QG_MAX_SET);
+  if (int st = check_rows(rows)) return st;
+  ProjArg pa[QG_MAX_SET];
+  for (int i = 0; i < count; i++) {
+    const qg_proj_rows& p = projs[i];
+    if (int st = check_nk(p.n, p.k)) return fail(st, "projs[%d]: n=%lld k=%lld", i, (long long)p.n, (long long)p.k);
+    if (int st = check_image(p.w_image, "w_image")) return fail(st, "projs[%d].w_image null or misaligned", i);
+    if (int st = check_y(p.y)) return fail(st, "projs[%d].y null or misaligned", i);
+    if (rows) {
+      if (int st = check_x(p.x, rows, p.k, QG_MAX_ROWS)) return fail(st, "projs[%d].x null, misaligned or bad", i);
+    }
+    if (!fuses_quantization(rows) && rows) {
+      if (int st = check_ws(p.ws, p.ws_bytes, prep_layout(rows, p.k).total, "projs[i]"))
+        return fail(st, "projs[%d].ws missing or small (%zu bytes)", i, p.ws_bytes);
+    }
+    pa[i] = ProjArg{p.w_image, p.n, p.k, p.ws, nullptr, p.y};
+  }
+  if (rows == 0) return ok();
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (fuses_quantization(rows)) {
+    for (int i = 0; i < count; i++) pa[i].x = projs[i].x;
+  } else {
+    // one quantize launch for all distinct inputs
+    qg_act acts[QG_MAX_SET];
+    int na = 0;
+    for (int i = 0; i < count; i++) {
+      bool seen = false;
+      for (int j = 0; j < i; j++) seen = seen || (projs[j].x == projs[i].x && projs[j].ws == projs[i].ws);
+      if (!seen) acts[na++] = qg_act{projs[i].x, projs[i].k, projs[i].ws, projs[i].ws_bytes};
+    }
+    if (int st = launch_prepare_set(acts, na, rows, s)) return st;
+  }
+  if (int st = launch_qgemv_set(fmt, pa, count, rows, s)) return st;
+  return ok();
+}
+
+int gemv_f16(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream) {
+  if (int st = check_rows(rows)) return st;
+  if (n < 1 || n > (1LL << 31) - 1) return fail(QG_ESHAPE, "n=%lld outside 1..2^31-1", (long long)n);
+  if (k < 8 || k % 8 || k > (1LL << 24))
+    return fail(QG_ESHAPE, "k=%lld is not a positive multiple of 8 up to 2^24", (long long)k);
+  if (!w) return fail(QG_EINVAL, "w is null");
+  if (!aligned(w, 16)) return fail(QG_EALIGN, "w %p is not 16-byte aligned", (const void*)w);
+  if (int st = check_y(y)) return st;
+  if (rows == 0) return ok();
+  if (!x) return fail(QG_EINVAL, "x is null");
+  if (!aligned(x, 16)) return fail(QG_EALIGN, "x %p is not 16-byte aligned", (const void*)x);
+  if (int st = check_device()) return st;
+  if (int st = launch_gemv_f16(w, n, k, x, rows, y, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64_t k, const float* x, int x_rows,
+                       const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, size_t ws_bytes,
+                       qg_stream stream) {
+  if (n_experts < 1 || n_experts > (1 << 30)) return fail(QG_ESHAPE, "n_experts=%lld", (long long)n_experts);
+  if (m < 0 || m > QG_MAX_ASSIGN) return fail(QG_ESHAPE, "m=%d outside 0..%d", m, QG_MAX_ASSIGN);
+  if (int st = check_nk(n, k)) return st;
+  if (int st = check_image(w_images, "w_images")) return st;
+  if (m && check_y(y)) return check_y(y);
+  if (int st = check_x(x, x_rows, k, QG_MAX_PREP_ROWS)) return st;
+  if (m && (!expert || !x_index)) return fail(QG_EINVAL, "expert or x_index is null");
+  if (int st = check_ws(ws, ws_bytes, grouped_layout(x_rows, k, m).total, "the grouped call")) return st;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const GroupedLayout G = grouped_layout(x_rows, k, m);
+  if (int st = launch_prepare(x, x_rows, k, (uint8_t*)ws + G.prep, false, s)) return st;
+  if (int st = launch_grouped(w_images, n_experts, n, k, x_rows, expert, x_index, m, y, ws, s)) return st;
+  return ok();
+}
+
+int qg_grouped_status(const void* ws, int32_t* bad, qg_stream stream) {
+  if (!ws || !bad) return fail(QG_EINVAL, "null argument");
+  if (int st = check_device()) return st;
+  if (int st = hip_status(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize")) return st;
+  int32_t h[2];
+  if (int st = hip_status(hipMemcpy(h, ws, sizeof h, hipMemcpyDeviceToHost), "hipMemcpy")) return st;
+  *bad = h[1];
+  return ok();
+}
+
+int qg_moe_route(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
+                 int32_t* x_index, float* weight, qg_stream stream) {
+  if (!logits || !expert || !x_index || !weight) return fail(QG_EINVAL, "null buffer");
+  if (rows < 0 || rows > 65535) return fail(QG_EROWS, "rows=%d outside 0..65535", rows);
+  if (n_experts < 1 || n_experts > 1024) return fail(QG_ESHAPE, "n_experts=%d outside 1..1024", n_experts);
+  if (topk < 1 || topk > 32 || topk > n_experts) return fail(QG_ESHAPE, "topk=%d outside 1..min(32, n_experts)", topk);
+  if (rows == 0) return ok();
+  if (int st = check_device()) return st;
+  if (int st = launch_moe_route(logits, rows, n_experts, topk, shared_expert, expert, x_index, weight,
+                                (hipStream_t)stream))
+    return st;
+  return ok();
+}
+
+int qg_swiglu(const float* gu, int m, int64_t ffn, float* h, qg_stream stream) {
+  if (!gu || !h) return fail(QG_EINVAL, "null buffer");
+  if (m < 0 || ffn < 1) return fail(QG_ESHAPE, "m=%d ffn=%lld", m, (long long)ffn);
+  if (m == 0) return ok();
+  if (int st = check_device()) return st;
+  if (int st = launch_swiglu(gu, m, ffn, h, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int64_t hidden, float* y,
+                   qg_stream stream) {
+  if (!o || !weight || !y) return fail(QG_EINVAL, "null buffer");
+  if (rows < 0 || rows > 65535 || slots < 1 || hidden < 4 || hidden % 4)
+    return fail(QG_ESHAPE, "rows=%d slots=%d hidden=%lld (hidden must be a multiple of 4)", rows, slots,
+                (long long)hidden);
+  if (!aligned(o, 16) || !aligned(y, 16)) return fail(QG_EALIGN, "o and y must be 16-byte aligned");
+  if (rows == 0) return ok();
+  if (int st = check_device()) return st;
+  if (int st = launch_moe_combine(o, weight, rows, slots, hidden, y, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qg_quantize_rows_q8(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, qg_stream stream) {
+  if (int st = check_x(x, rows, k, QG_MAX_PREP_ROWS)) return st;
+  if (!qx || !dx || !sx) return fail(QG_EINVAL, "null output");
+  if (!aligned(qx, 16)) return fail(QG_EALIGN, "qx %p is not 16-byte aligned", (const void*)qx);
+  if (int st = check_device()) return st;
+  if (int st = launch_quantize_plain(x, rows, k, qx, dx, sx, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qgemv_blockdots(int fmt, const void* w_image, int64_t n, int64_t k, const int8_t* qx, int rows, int32_t* isum,
+                    qg_stream stream) {
+  if (int st = check_fmt(fmt)) return st;
+  if (int st = check_rows(rows)) return st;
+  if (int st = check_nk(n, k)) return st;
+  if (int st = check_image(w_image, "w_image")) return st;
+  if (!isum) return fail(QG_EINVAL, "isum is null");
+  if (!qx) return fail(QG_EINVAL, "qx is null");
+  if (!aligned(qx, 16)) return fail(QG_EALIGN, "qx %p is not 16-byte aligned", (const void*)qx);
+  if (rows == 0) return ok();
+  if (int st = check_device()) return st;
+  if (int st = launch_blockdots(fmt, w_image, n, k, qx, rows, isum, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// qg_device.h -- device primitives shared by the libqgemv kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qg_layout.h"
+
+namespace qg {
+
+constexpr int WAVE = 64;
+constexpr int FMT_Q8 = 1, FMT_Q4 = 2;
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Streaming loads of weight bytes that are read exactly once: the
+// non-temporal hint keeps them from displacing activation rows in the caches.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8_stream(const void* p) {
+  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint16_t ld2_stream(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  _Float16 v;
+  __builtin_memcpy(&v, &h, 2);
+  return (float)v;
+}
+
+// Exact int32 dot of one Q8_0 block (low/high 16 codes) with one q8 block.
+__device__ __forceinline__ int dot_q8(uint4 wl, uint4 wh, uint4 xl, uint4 xh) {
+  int s = 0;
+  s = __builtin_amdgcn_sdot4((int)wl.x, (int)xl.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)wl.y, (int)xl.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)wl.z, (int)xl.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)wl.w, (int)xl.w, s, false);
+  s = __builtin_amdgcn_sdot4((int)wh.x, (int)xh.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)wh.y, (int)xh.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)wh.z, (int)xh.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)wh.w, (int)xh.w, s, false);
+  return s;
+}
+
+// Exact int32 dot of one Q4_0 block (16 packed bytes) with one q8 block.  The
+// raw codes c in [0,15] enter the dot as they are; the -8 offset is folded in
+// through the start value nsx = -8 * sum(q_x).
+__device__ __forceinline__ int dot_q4(uint4 p, uint4 xl, uint4 xh, int nsx) {
+  const unsigned M = 0x0F0F0F0Fu;
+  int s = nsx;
+  s = __builtin_amdgcn_sdot4((int)(p.x & M), (int)xl.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)(p.y & M), (int)xl.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)(p.z & M), (int)xl.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)(p.w & M), (int)xl.w, s, false);
+  s = __builtin_amdgcn_sdot4((int)((p.x >> 4) & M), (int)xh.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)((p.y >> 4) & M), (int)xh.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)((p.z >> 4) & M), (int)xh.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)((p.w >> 4) & M), (int)xh.w, s, false);
+  return s;
+}
+
+// Cross-lane moves inside groups of four lanes (DPP quad permutes).
+__device__ __forceinline__ int quad_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int quad_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+
+// q8 quantization of one 32-block held by the four lanes of a quad, eight
+// elements each (lane 4m+q holds elements 8q..8q+7): d = amax/127 by IEEE
+// division, q = round-half-away(x/d) clamped to [-127, 127], all 0 when d == 0.
+// Every lane of the quad gets d and the block's code sum; each lane returns its
+// eight codes packed in element order.
+__device__ __forceinline__ void quantize_quarter(const float (&v)[8], unsigned& lo, unsigned& hi, float& d,
+                                                 int& block_sum) {
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(v[e]));
+  am = fmaxf(am, __int_as_float(quad_xor1(__float_as_int(am))));
+  am = fmaxf(am, __int_as_float(quad_xor2(__float_as_int(am))));
+  d = am / 127.0f;
+  int s = 0;
+  unsigned w[2] = {0u, 0u};
+  if (d != 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int q = (int)fminf(fmaxf(roundf(v[e] / d), -127.0f), 127.0f);
+      s += q;
+      w[e >> 2] |= ((unsigned)(q & 0xff)) << (8 * (e & 3));
+    }
+  }
+  lo = w[0];
+  hi = w[1];
+  s += quad_xor1(s);
+  s += quad_xor2(s);
+  block_sum = s;
+}
+
+}  // namespace qg

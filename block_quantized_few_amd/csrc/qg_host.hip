@@ -114,20 +114,16 @@ int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image
   const uint8_t* src = (const uint8_t*)blocks;
   uint8_t* dst = (uint8_t*)image;
   memset(dst, 0, image_total_bytes(fmt, n, k));
-  int64_t kb = kb_of(k), kbp = kbp_of(k);
+  const int64_t kb = kb_of(k), kbp = kbp_of(k);
   uint16_t* scales = (uint16_t*)(dst + image_scale_offset(fmt, n, k));
-  int cb = fmt == QG_FMT_Q8_0 ? Q8_CANON : Q4_CANON;
+  const int cb = fmt == QG_FMT_Q8_0 ? Q8_CANON : Q4_CANON;
   for (int64_t o = 0; o < n; o++)
     for (int64_t b = 0; b < kb; b++) {
       const uint8_t* blk = src + (o * kb + b) * cb;
-      scales[o * kbp + b] = (uint16_t)(blk[0] | (blk[1] << 8));
-      if (fmt == QG_FMT_Q8_0) {
-        size_t lo = q8_lo_offset(o, b, kbp);
-        memcpy(dst + lo, blk + 2, 16);
-        memcpy(dst + lo + 256, blk + 18, 16);
-      } else {
-        memcpy(dst + q4_offset(o, b, kbp), blk + 2, 16);
-      }
+      scales[scale_index(o, b, kbp)] = (uint16_t)(blk[0] | (blk[1] << 8));
+      uint8_t* cell = dst + cell_row_offset(fmt, o, b, kbp);
+      memcpy(cell, blk + 2, 16);
+      if (fmt == QG_FMT_Q8_0) memcpy(cell + 256, blk + 18, 16);
     }
   return ok();
 }
@@ -137,22 +133,18 @@ int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* bloc
   if (st) return st;
   const uint8_t* src = (const uint8_t*)image;
   uint8_t* dst = (uint8_t*)blocks;
-  int64_t kb = kb_of(k), kbp = kbp_of(k);
+  const int64_t kb = kb_of(k), kbp = kbp_of(k);
   const uint16_t* scales = (const uint16_t*)(src + image_scale_offset(fmt, n, k));
-  int cb = fmt == QG_FMT_Q8_0 ? Q8_CANON : Q4_CANON;
+  const int cb = fmt == QG_FMT_Q8_0 ? Q8_CANON : Q4_CANON;
   for (int64_t o = 0; o < n; o++)
     for (int64_t b = 0; b < kb; b++) {
       uint8_t* blk = dst + (o * kb + b) * cb;
-      uint16_t d = scales[o * kbp + b];
+      const uint16_t d = scales[scale_index(o, b, kbp)];
       blk[0] = (uint8_t)(d & 0xff);
       blk[1] = (uint8_t)(d >> 8);
-      if (fmt == QG_FMT_Q8_0) {
-        size_t lo = q8_lo_offset(o, b, kbp);
-        memcpy(blk + 2, src + lo, 16);
-        memcpy(blk + 18, src + lo + 256, 16);
-      } else {
-        memcpy(blk + 2, src + q4_offset(o, b, kbp), 16);
-      }
+      const uint8_t* cell = src + cell_row_offset(fmt, o, b, kbp);
+      memcpy(blk + 2, cell, 16);
+      if (fmt == QG_FMT_Q8_0) memcpy(blk + 18, cell + 256, 16);
     }
   return ok();
 }

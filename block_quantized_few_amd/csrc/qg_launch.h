@@ -1,0 +1,66 @@
+// qg_launch.h -- host-side launchers of the libqgemv kernels.  Arguments are
+// validated by the C-ABI layer before any of these is called; each returns
+// QG_OK or QG_ELAUNCH.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qgemv.h"
+#include "qg_layout.h"
+
+namespace qg {
+
+// Activation rows prepared in a workspace, as the GEMV kernels read them.
+struct Prep {
+  const int8_t* codes;
+  const float* dx;
+  const int* nsx;
+};
+Prep prep_view(const void* ws, int64_t rows, int64_t k);
+
+// A1: quantize rows x [rows][k] into a workspace (`ws` layout of qg_layout.h),
+// in row order or (frag) in the MFMA fragment order.
+int launch_prepare(const float* x, int rows, int64_t k, void* ws, bool frag, hipStream_t s);
+// Whether a GEMV of `rows` rows reads its prepared rows in fragment order.
+bool prep_in_fragment_order(int rows);
+// A1 for up to QG_MAX_SET activation sets (same row count) in one launch.
+int launch_prepare_set(const qg_act* acts, int count, int rows, hipStream_t s);
+// A1 in the plain layout with code sums (test hook).
+int launch_quantize_plain(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, hipStream_t s);
+// Offline weight quantization into a device image.
+int launch_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, hipStream_t s);
+// A3 test hook.
+int launch_blockdots(int fmt, const void* image, int64_t n, int64_t k, const int8_t* qx, int rows, int32_t* isum,
+                     hipStream_t s);
+
+// One projection of a q8-lane launch.
+struct ProjArg {
+  const void* image;
+  int64_t n, k;
+  const void* ws;  // prepared rows (ignored when x is set)
+  const float* x;  // fp32 rows, quantized inside the GEMV launch (rows <= 2)
+  float* y;        // [rows][n]
+};
+// Q8_0/Q4_0 GEMV for 1..16 rows over up to QG_MAX_SET projections, one launch.
+int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStream_t s);
+// Whether rows this small are quantized inside the GEMV launch.
+bool fuses_quantization(int rows);
+
+// Grouped routed-expert Q8_0 GEMV (plan + GEMV; rows already prepared in ws).
+int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
+                   const int32_t* x_index, int m, float* y, void* ws, hipStream_t s);
+
+// f16 lane.
+int launch_gemv_f16(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s);
+
+// MoE glue.
+int launch_moe_route(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
+                     int32_t* x_index, float* weight, hipStream_t s);
+int launch_swiglu(const float* gu, int m, int64_t ffn, float* h, hipStream_t s);
+int launch_moe_combine(const float* o, const float* weight, int rows, int slots, int64_t hidden, float* y,
+                       hipStream_t s);
+
+// Device facts, cached per process.
+int device_cus();
+
+}  // namespace qg

@@ -1,26 +1,38 @@
-// qg_layout.h -- byte layout of the library's device images and workspaces.
+// qg_layout.h -- byte layout of the library's device images and workspaces,
+// and the fixed partition of a row's blocks into partial sums.
 //
-// Internal to libqgemv; both the host packing code and the kernels include it.
+// Internal to libqgemv; the host packer and the kernels both include it.
 //
-// Weight image of an n x k matrix (k % 32 == 0), kb = k/32 blocks per row,
-// padded to kbp = roundup(kb, 16) blocks with zero blocks:
-//   Q8_0 code plane: n * kbp * 32 bytes.  Row o starts at o*kbp*32; its blocks
-//        come in groups of 16 (512 bytes): the first 256 bytes hold the low
-//        halves (codes 0..15) of the group's 16 blocks, 16 bytes each, the next
-//        256 bytes the high halves (codes 16..31).  A 16-lane row group then
-//        reads a whole group with two fully coalesced 256-byte loads, each lane
-//        holding one complete block.
-//   Q4_0 code plane: n * kbp * 16 bytes, block b of row o at (o*kbp + b)*16,
-//        the canonical nibble order kept (byte j: code j low, code j+16 high),
-//        so low nibbles give codes 0..15 and high nibbles codes 16..31.
-//   Scale plane: fp16 [n][kbp] at the next 256-byte boundary after the codes.
+// Weight image of an n x k matrix (k % 32 == 0).  kb = k/32 blocks per row,
+// padded to kbp = roundup(kb, 16) with zero blocks; rows padded to
+// np = roundup(n, 16) with zero rows.  Rows are grouped in tiles of 16, and a
+// tile stores its blocks one after another, each block holding the 16 rows:
+//   Q8_0 codes: tile t, block b at (t*kbp + b)*512: the low halves (codes
+//        0..15) of rows 0..15 at 16*i, then the high halves (codes 16..31) at
+//        256 + 16*i.  16 lanes that own 16 rows read 256 contiguous bytes, and
+//        one MFMA operand fragment (8 codes of each of 16 rows) is 512
+//        contiguous bytes.
+//   Q4_0 codes: tile t, block b at (t*kbp + b)*256: row i's 16 packed bytes at
+//        16*i in the canonical nibble order (byte j: code j low, code j+16
+//        high).
+//   Scales (fp16) at the next 256-byte boundary: (t*kbp + b)*16 + i.
+// For n % 16 == 0 and k % 512 == 0 the image holds exactly the canonical bytes
+// per weight.
 //
-// Prepared activation rows (workspace of `rows` rows of length k):
-//   codes  int8  [rows][kbp*32] in the same low/high half grouping as Q8_0;
-//   dx     fp32  [rows][kbp] block scales;
-//   nsx    int32 [rows][kbp] = -8 * (sum of the block's codes), the start value
-//          of a Q4_0 block dot (sum (c-8) q = sum c q - 8 sum q).
-//   Each plane starts on a 256-byte boundary; pad blocks are all zero.
+// Prepared activation rows (workspace of `rows` rows of length k), each plane
+// on a 256-byte boundary, pad blocks zero:
+//   codes int8 [rows][kbp*32] in element order;
+//   dx    fp32 [rows][kbp] block scales;
+//   nsx   int32 [rows][kbp] = -8 * (sum of the block's codes), the start value
+//         of a Q4_0 block dot (sum (c-8) q = sum c q - 8 sum q).
+//
+// Partition of a row's kbp blocks (depends on kbp only, never on the number of
+// activation rows, so a row's fp32 result is the same in every launch): P parts
+// (a power of two up to 32, about 8 blocks each) of BS = kbp/P blocks, grouped
+// as S (<= 4) "wave parts" of H (<= 8) "lane parts".  Wave part s covers blocks
+// [s*H*BS, (s+1)*H*BS); inside it lane part h takes the blocks s*H*BS + H*u + h,
+// u = 0..BS-1, accumulated in that order.  Lane parts are summed by a fixed
+// pairwise tree (((h0 + h1) + (h2 + h3)) + ...), wave parts left to right.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -30,38 +42,44 @@
 
 namespace qg {
 
-constexpr int QK = 32;           // weights per block
-constexpr int GROUP = 16;        // blocks per interleave group
-constexpr int Q8_CANON = 34;     // canonical block bytes
+constexpr int QK = 32;     // weights per block
+constexpr int GROUP = 16;  // block padding unit
+constexpr int TILE = 16;   // rows per tile
+constexpr int Q8_CANON = 34;
 constexpr int Q4_CANON = 18;
 
 QG_HD int64_t kb_of(int64_t k) { return k / QK; }
 QG_HD int64_t kbp_of(int64_t k) { return ((k / QK + GROUP - 1) / GROUP) * GROUP; }
+QG_HD int64_t np_of(int64_t n) { return ((n + TILE - 1) / TILE) * TILE; }
 QG_HD size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-QG_HD size_t code_bytes_per_block(int fmt) { return fmt == 1 ? 32 : 16; }
+// Bytes of one (tile, block) cell of the code plane.
+QG_HD size_t cell_bytes(int fmt) { return fmt == 1 ? 512 : 256; }
 
 QG_HD size_t image_code_bytes(int fmt, int64_t n, int64_t k) {
-  return (size_t)n * (size_t)kbp_of(k) * code_bytes_per_block(fmt);
+  return (size_t)(np_of(n) / TILE) * (size_t)kbp_of(k) * cell_bytes(fmt);
 }
 QG_HD size_t image_scale_offset(int fmt, int64_t n, int64_t k) { return align256(image_code_bytes(fmt, n, k)); }
 QG_HD size_t image_total_bytes(int fmt, int64_t n, int64_t k) {
-  return image_scale_offset(fmt, n, k) + align256((size_t)n * (size_t)kbp_of(k) * 2);
+  return image_scale_offset(fmt, n, k) + align256((size_t)np_of(n) * (size_t)kbp_of(k) * 2);
 }
 
-// Offset of the low half (Q8_0) of block b in row o; the high half is +256.
-QG_HD size_t q8_lo_offset(int64_t o, int64_t b, int64_t kbp) {
-  return (size_t)o * (size_t)kbp * 32 + (size_t)(b / GROUP) * 512 + (size_t)(b % GROUP) * 16;
+// Byte offset of row o's part of block b (Q8_0: its low half; the high half
+// is 256 bytes further).
+QG_HD size_t cell_row_offset(int fmt, int64_t o, int64_t b, int64_t kbp) {
+  return ((size_t)(o / TILE) * (size_t)kbp + (size_t)b) * cell_bytes(fmt) + (size_t)(o % TILE) * 16;
 }
-QG_HD size_t q4_offset(int64_t o, int64_t b, int64_t kbp) { return ((size_t)o * (size_t)kbp + (size_t)b) * 16; }
+// Index (in fp16 units) of row o's scale of block b.
+QG_HD size_t scale_index(int64_t o, int64_t b, int64_t kbp) {
+  return ((size_t)(o / TILE) * (size_t)kbp + (size_t)b) * TILE + (size_t)(o % TILE);
+}
 
-// Workspace of prepared rows.
 struct PrepLayout {
   size_t codes, dx, nsx, total;
 };
 QG_HD PrepLayout prep_layout(int64_t rows, int64_t k) {
   PrepLayout L;
-  int64_t kbp = kbp_of(k);
+  const int64_t kbp = kbp_of(k);
   L.codes = 0;
   L.dx = align256((size_t)rows * (size_t)kbp * 32);
   L.nsx = L.dx + align256((size_t)rows * (size_t)kbp * 4);
@@ -82,6 +100,21 @@ QG_HD GroupedLayout grouped_layout(int64_t x_rows, int64_t k, int64_t m) {
   G.prep = G.items + align256((size_t)(m > 0 ? m : 1) * 12);
   G.total = G.prep + prep_layout(x_rows, k).total;
   return G;
+}
+
+struct PartPlan {
+  int P, H, S, BS;
+};
+QG_HD PartPlan part_plan(int kbp) {
+  const int m = kbp / 8;  // parts of about eight blocks
+  int P = 1;
+  while (P * 2 <= m && P < 32 && kbp % (P * 2) == 0) P *= 2;
+  PartPlan pl;
+  pl.P = P;
+  pl.S = P < 4 ? P : 4;
+  pl.H = P / pl.S;
+  pl.BS = kbp / P;
+  return pl;
 }
 
 }  // namespace qg

@@ -1,0 +1,257 @@
+// qg_quant.hip -- activation quantizer (A1), offline weight quantizer, and
+// the block-dot test hook (A3).
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "qg_device.h"
+#include "qg_internal.h"
+#include "qg_launch.h"
+
+namespace qg {
+
+Prep prep_view(const void* ws, int64_t rows, int64_t k) {
+  const PrepLayout L = prep_layout(rows, k);
+  const uint8_t* w = (const uint8_t*)ws;
+  return Prep{(const int8_t*)(w + L.codes), (const float*)(w + L.dx), (const int*)(w + L.nsx)};
+}
+
+// Loads the eight fp32 elements of quarter q of block b of row r (zeros past
+// the row's kb real blocks).
+__device__ __forceinline__ void load_quarter(const float* __restrict__ x, int64_t k, int64_t r, int64_t b, int kb,
+                                             int q, bool active, float (&v)[8]) {
+  if (active && b < kb) {
+    const float4* src = reinterpret_cast<const float4*>(x + r * k + b * QK + q * 8);
+    const float4 a = src[0], c = src[1];
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; e++) v[e] = 0.0f;
+  }
+}
+
+// Where quarter q of block b of row r lands in a workspace of `rows` rows:
+// row order (codes [rows][kbp][32], dx/nsx [rows][kbp]) or, for the MFMA
+// path's 9..16 rows, fragment order (codes [kbp][4][rows][8], dx/nsx
+// [kbp][rows]).
+struct PrepDst {
+  int8_t* codes;
+  float* dx;
+  int* nsx;
+  int rows, kbp;
+  bool frag;
+  __device__ __forceinline__ void put(int64_t r, int64_t b, int q, unsigned lo, unsigned hi, float d, int sum) const {
+    const int64_t ci = frag ? ((b * 4 + q) * rows + r) * 8 : (r * kbp + b) * 32 + q * 8;
+    *reinterpret_cast<uint2*>(codes + ci) = make_uint2(lo, hi);
+    if (q == 0) {
+      const int64_t si = frag ? b * rows + r : r * kbp + b;
+      dx[si] = d;
+      nsx[si] = -8 * sum;
+    }
+  }
+};
+
+// Four lanes per 32-block over kbp blocks per row; pad blocks come out all
+// zero (scale 0, codes 0).
+__global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ x, int64_t k, int kb, PrepDst dst) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = t >> 2;
+  const int q = (int)(t & 3);
+  const bool active = blk < (int64_t)dst.rows * dst.kbp;  // whole quads are active or not
+  const int64_t r = active ? blk / dst.kbp : 0, b = active ? blk % dst.kbp : 0;
+  float v[8];
+  load_quarter(x, k, r, b, kb, q, active, v);
+  unsigned lo, hi;
+  float d;
+  int sum;
+  quantize_quarter(v, lo, hi, d, sum);
+  if (active) dst.put(r, b, q, lo, hi, d, sum);
+}
+
+// Same for several activation sets; blockIdx.y picks the set.
+struct PrepSet {
+  const float* x[QG_MAX_SET];
+  PrepDst dst[QG_MAX_SET];
+  int64_t k[QG_MAX_SET];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void prepare_set_kernel(PrepSet s) {
+  const int p = blockIdx.y;
+  const int64_t k = s.k[p];
+  const PrepDst& dst = s.dst[p];
+  const int kb = (int)kb_of(k);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = t >> 2;
+  const int q = (int)(t & 3);
+  const bool active = blk < (int64_t)dst.rows * dst.kbp;
+  const int64_t r = active ? blk / dst.kbp : 0, b = active ? blk % dst.kbp : 0;
+  float v[8];
+  load_quarter(s.x[p], k, r, b, kb, q, active, v);
+  unsigned lo, hi;
+  float d;
+  int sum;
+  quantize_quarter(v, lo, hi, d, sum);
+  if (active) dst.put(r, b, q, lo, hi, d, sum);
+}
+
+// Plain layout [rows][k] with the code sum (test hook).
+__global__ __launch_bounds__(256) void quantize_plain_kernel(const float* __restrict__ x, int rows, int64_t k, int kb,
+                                                             int8_t* __restrict__ qx, float* __restrict__ dx,
+                                                             int* __restrict__ sx) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = t >> 2;
+  const int q = (int)(t & 3);
+  const bool active = blk < (int64_t)rows * kb;
+  const int64_t r = active ? blk / kb : 0, b = active ? blk % kb : 0;
+  float v[8];
+  load_quarter(x, k, r, b, kb, q, active, v);
+  unsigned lo, hi;
+  float d;
+  int sum;
+  quantize_quarter(v, lo, hi, d, sum);
+  if (!active) return;
+  *reinterpret_cast<uint2*>(qx + r * k + b * 32 + q * 8) = make_uint2(lo, hi);
+  if (q == 0) {
+    dx[r * kb + b] = d;
+    sx[r * kb + b] = sum;
+  }
+}
+
+// One thread per (row, block) of the padded image.  d = fp16(amax/qmax) with
+// round-to-nearest-even, codes by IEEE division by the stored scale.
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                               int kb, int kbp, uint8_t* __restrict__ code,
+                                                               uint16_t* __restrict__ scale) {
+  const int64_t np = np_of(n);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= np * kbp) return;
+  const int64_t o = t / kbp, b = t % kbp;
+  unsigned packed[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint16_t d16 = 0;
+  if (o < n && b < kb) {
+    float v[32];
+    const float4* src = reinterpret_cast<const float4*>(w + o * k + b * QK);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float4 f = src[i];
+      v[4 * i] = f.x, v[4 * i + 1] = f.y, v[4 * i + 2] = f.z, v[4 * i + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+    const _Float16 h = (_Float16)(amax / (FMT == FMT_Q8 ? 127.0f : 7.0f));
+    __builtin_memcpy(&d16, &h, 2);
+    const float dq = (float)h;
+    if (FMT == FMT_Q8) {
+      if (dq != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+          const int q = (int)fminf(fmaxf(roundf(v[i] / dq), -127.0f), 127.0f);
+          packed[i >> 2] |= ((unsigned)(q & 0xff)) << (8 * (i & 3));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        int lo = 8, hi = 8;  // code 8 stands for 0
+        if (dq != 0.0f) {
+          lo = (int)fminf(fmaxf(roundf(v[i] / dq), -8.0f), 7.0f) + 8;
+          hi = (int)fminf(fmaxf(roundf(v[i + 16] / dq), -8.0f), 7.0f) + 8;
+        }
+        packed[i >> 2] |= ((unsigned)(lo | (hi << 4))) << (8 * (i & 3));
+      }
+    }
+  }
+  uint8_t* dst = code + cell_row_offset(FMT, o, b, kbp);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  if (FMT == FMT_Q8) *reinterpret_cast<uint4*>(dst + 256) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  scale[scale_index(o, b, kbp)] = d16;
+}
+
+// isum[r][o][b]: the exact block dot of the image's codes with qx (plain).
+template <int FMT>
+__global__ __launch_bounds__(256) void blockdots_kernel(const uint8_t* __restrict__ code, int64_t n, int kbp, int kb,
+                                                        const int8_t* __restrict__ qx, int rows, int64_t k,
+                                                        int* __restrict__ isum) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)rows * n * kb) return;
+  const int64_t b = t % kb, o = (t / kb) % n, r = t / ((int64_t)kb * n);
+  const int8_t* xq = qx + r * k + b * QK;
+  const uint4 xl = ld16(xq), xh = ld16(xq + 16);
+  const uint8_t* p = code + cell_row_offset(FMT, o, b, kbp);
+  int s;
+  if (FMT == FMT_Q8) {
+    s = dot_q8(ld16(p), ld16(p + 256), xl, xh);
+  } else {
+    int qsum = 0;
+    for (int i = 0; i < 32; i++) qsum += xq[i];
+    s = dot_q4(ld16(p), xl, xh, -8 * qsum);
+  }
+  isum[t] = s;
+}
+
+static unsigned grid1(int64_t threads, int per) { return (unsigned)((threads + per - 1) / per); }
+
+bool prep_in_fragment_order(int rows) { return rows > 8 && rows <= QG_MAX_ROWS; }
+
+static PrepDst prep_dst(void* ws, int rows, int64_t k, bool frag) {
+  const PrepLayout L = prep_layout(rows, k);
+  uint8_t* w = (uint8_t*)ws;
+  return PrepDst{(int8_t*)(w + L.codes), (float*)(w + L.dx), (int*)(w + L.nsx), rows, (int)kbp_of(k), frag};
+}
+
+int launch_prepare(const float* x, int rows, int64_t k, void* ws, bool frag, hipStream_t s) {
+  const int kbp = (int)kbp_of(k);
+  hipLaunchKernelGGL(prepare_kernel, dim3(grid1((int64_t)rows * kbp * 4, 256)), dim3(256), 0, s, x, k, (int)kb_of(k),
+                     prep_dst(ws, rows, k, frag));
+  return hip_status(hipGetLastError(), "prepare_kernel");
+}
+
+int launch_prepare_set(const qg_act* acts, int count, int rows, hipStream_t s) {
+  PrepSet ps;
+  memset(&ps, 0, sizeof ps);
+  ps.count = count;
+  int64_t maxkbp = 0;
+  for (int i = 0; i < count; i++) {
+    ps.x[i] = acts[i].x;
+    ps.k[i] = acts[i].k;
+    ps.dst[i] = prep_dst(acts[i].ws, rows, acts[i].k, prep_in_fragment_order(rows));
+    if (kbp_of(acts[i].k) > maxkbp) maxkbp = kbp_of(acts[i].k);
+  }
+  hipLaunchKernelGGL(prepare_set_kernel, dim3(grid1((int64_t)rows * maxkbp * 4, 256), count), dim3(256), 0, s, ps);
+  return hip_status(hipGetLastError(), "prepare_set_kernel");
+}
+
+int launch_quantize_plain(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, hipStream_t s) {
+  const int kb = (int)kb_of(k);
+  hipLaunchKernelGGL(quantize_plain_kernel, dim3(grid1((int64_t)rows * kb * 4, 256)), dim3(256), 0, s, x, rows, k, kb,
+                     qx, dx, sx);
+  return hip_status(hipGetLastError(), "quantize_plain_kernel");
+}
+
+int launch_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, hipStream_t s) {
+  uint8_t* img = (uint8_t*)image;
+  uint16_t* scale = (uint16_t*)(img + image_scale_offset(fmt, n, k));
+  const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
+  const unsigned g = grid1(np_of(n) * kbp, 256);
+  if (fmt == FMT_Q8)
+    hipLaunchKernelGGL(quantize_weights_kernel<FMT_Q8>, dim3(g), dim3(256), 0, s, w, n, k, kb, kbp, img, scale);
+  else
+    hipLaunchKernelGGL(quantize_weights_kernel<FMT_Q4>, dim3(g), dim3(256), 0, s, w, n, k, kb, kbp, img, scale);
+  return hip_status(hipGetLastError(), "quantize_weights_kernel");
+}
+
+int launch_blockdots(int fmt, const void* image, int64_t n, int64_t k, const int8_t* qx, int rows, int32_t* isum,
+                     hipStream_t s) {
+  const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
+  const unsigned g = grid1((int64_t)rows * n * kb, 256);
+  const uint8_t* img = (const uint8_t*)image;
+  if (fmt == FMT_Q8)
+    hipLaunchKernelGGL(blockdots_kernel<FMT_Q8>, dim3(g), dim3(256), 0, s, img, n, kbp, kb, qx, rows, k, isum);
+  else
+    hipLaunchKernelGGL(blockdots_kernel<FMT_Q4>, dim3(g), dim3(256), 0, s, img, n, kbp, kb, qx, rows, k, isum);
+  return hip_status(hipGetLastError(), "blockdots_kernel");
+}
+
+}  // namespace qg

@@ -18,6 +18,7 @@ MAX_ROWS = 16
 MAX_PREP_ROWS = 8192
 MAX_ASSIGN = 2048
 MAX_SET = 8
+FUSED_ROWS = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
@@ -32,6 +33,11 @@ class QGError(RuntimeError):
 
 class _Proj(C.Structure):
     _fields_ = [("w_image", C.c_void_p), ("n", C.c_int64), ("k", C.c_int64), ("ws", C.c_void_p), ("y", C.c_void_p)]
+
+
+class _ProjRows(C.Structure):
+    _fields_ = [("w_image", C.c_void_p), ("n", C.c_int64), ("k", C.c_int64), ("x", C.c_void_p), ("ws", C.c_void_p),
+                ("ws_bytes", C.c_size_t), ("y", C.c_void_p)]
 
 
 class _Act(C.Structure):
@@ -57,6 +63,7 @@ _SIGS = {
     "gemv_f16": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
     "qgemv_set": (C.c_int, [C.c_int, C.POINTER(_Proj), C.c_int, C.c_int, C.c_void_p]),
     "qg_prepare_rows_set": (C.c_int, [C.POINTER(_Act), C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_set_rows": (C.c_int, [C.c_int, C.POINTER(_ProjRows), C.c_int, C.c_int, C.c_void_p]),
     "qgemv_q8_0_grouped": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
                                      C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qg_grouped_status": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_void_p]),
@@ -225,6 +232,16 @@ def qgemv_set(fmt, projs, rows):
     for i, (image, n, k, ws, y) in enumerate(projs):
         arr[i] = _Proj(image.data_ptr(), n, k, ws.data_ptr(), y.data_ptr())
     _check(lib().qgemv_set(fmt, arr, len(projs), rows, _stream()))
+
+
+def qgemv_set_rows(fmt, projs, rows):
+    """projs: list of (image, n, k, x, ws, y); ws may be None when rows <= FUSED_ROWS."""
+    arr = (_ProjRows * len(projs))()
+    for i, (image, n, k, x, ws, y) in enumerate(projs):
+        _dev(x, torch.float32, "x")
+        arr[i] = _ProjRows(image.data_ptr(), n, k, x.data_ptr(), 0 if ws is None else ws.data_ptr(),
+                           0 if ws is None else ws.numel(), y.data_ptr())
+    _check(lib().qgemv_set_rows(fmt, arr, len(projs), rows, _stream()))
 
 
 def qgemv_q8_0_grouped(images, n_experts, n, k, x, expert, x_index, y=None, ws=None):

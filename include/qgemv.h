@@ -33,9 +33,12 @@
  *
  * Device image.  Weights live on the device in the library's own layout,
  * made either by qg_pack_image (from canonical blocks, on the host) or by
- * qg_quantize_weights (from fp32 weights, on the device).  Each row is padded
- * with zero blocks to a multiple of 16 blocks (512 weights); for k a multiple
- * of 512 the image holds exactly the canonical bytes per weight.
+ * qg_quantize_weights (from fp32 weights, on the device): rows in tiles of 16,
+ * each tile storing its blocks one after another with the 16 rows of a block
+ * side by side, codes and fp16 scales in separate planes.  Rows are padded to
+ * a multiple of 16 and blocks to a multiple of 16 (512 weights) with zeros;
+ * for n % 16 == 0 and k % 512 == 0 the image holds exactly the canonical bytes
+ * per weight.
  *
  * Conventions.
  *   - Pointers are device pointers unless marked (host).  `stream` is a
@@ -86,6 +89,7 @@ enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3 };
 #define QG_MAX_PREP_ROWS 8192 /* rows one qg_prepare_rows call quantizes */
 #define QG_MAX_ASSIGN 2048    /* assignments per grouped call */
 #define QG_MAX_SET 8          /* projections per qgemv_set call */
+#define QG_FUSED_ROWS 2       /* up to this many rows are quantized inside the GEMV launch */
 
 /* ------------------------------------------------------------ host only --- */
 
@@ -125,7 +129,8 @@ int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* ima
 
 /* A1 of the q8 lane: quantizes rows x [rows][k] (1 <= rows <= QG_MAX_PREP_ROWS)
  * into the workspace `ws` (qg_workspace_bytes(rows, k) bytes) in the layout the
- * GEMV kernels read. */
+ * GEMV kernels read for that row count (so a workspace serves GEMV calls with
+ * the same rows and k). */
 int qg_prepare_rows(const float* x, int rows, int64_t k, void* ws, size_t ws_bytes, qg_stream stream);
 
 /* q8 lane GEMV on rows already prepared in `ws` (by qg_prepare_rows with the
@@ -157,6 +162,24 @@ typedef struct {
   float* y;       /* [rows][n] */
 } qg_proj;
 int qgemv_set(int fmt, const qg_proj* projs /*host*/, int count, int rows, qg_stream stream);
+
+/* Several projections with the same row count straight from fp32 rows, the
+ * whole decode-layer step in as few launches as the row count allows: for
+ * rows <= QG_FUSED_ROWS the rows are quantized inside the GEMV launch (one
+ * launch, ws unused and may be null); otherwise one launch quantizes every
+ * distinct (x, ws) pair into its ws (qg_workspace_bytes(rows, k) bytes;
+ * projections that share x may share ws) and a second runs all GEMVs.
+ * 1 <= count <= QG_MAX_SET. */
+typedef struct {
+  const void* w_image;
+  int64_t n;
+  int64_t k;
+  const float* x; /* [rows][k] fp32 */
+  void* ws;
+  size_t ws_bytes;
+  float* y; /* [rows][n] */
+} qg_proj_rows;
+int qgemv_set_rows(int fmt, const qg_proj_rows* projs /*host*/, int count, int rows, qg_stream stream);
 
 /* Prepares several activation sets in one launch (count <= QG_MAX_SET). */
 typedef struct {

@@ -58,17 +58,31 @@ def test_pack_unpack_roundtrip(fmt, n, k):
 
 
 def test_pack_layout_of_one_q8_block():
-    # block b of row o: low half at o*kbp*32 + (b//16)*512 + (b%16)*16, high half +256, scale plane after
-    n, k = 2, 1024  # kb = kbp = 32
+    # row o, block b: tile t = o // 16, i = o % 16; low half at (t*kbp + b)*512 + 16*i, high half +256;
+    # scale (fp16) at scale plane + 2*((t*kbp + b)*16 + i)
+    n, k = 40, 1024  # kb = kbp = 32, three tiles (the last one padded)
     blocks = np.zeros((n, k // 32, 34), np.uint8)
-    blocks[1, 17, 0:2] = (0x34, 0x12)
-    blocks[1, 17, 2:34] = np.arange(1, 33, dtype=np.uint8)
+    o, b = 21, 17
+    blocks[o, b, 0:2] = (0x34, 0x12)
+    blocks[o, b, 2:34] = np.arange(1, 33, dtype=np.uint8)
     img = q.pack_image(q.Q8_0, blocks, n, k)
-    lo = 1 * 32 * 32 + 1 * 512 + 1 * 16
+    t, i = o // 16, o % 16
+    lo = (t * 32 + b) * 512 + 16 * i
     assert list(img[lo:lo + 16]) == list(range(1, 17))
     assert list(img[lo + 256:lo + 272]) == list(range(17, 33))
-    scale_off = (n * 32 * 32 + 255) // 256 * 256
-    assert img[scale_off + 2 * (1 * 32 + 17)] == 0x34 and img[scale_off + 2 * (1 * 32 + 17) + 1] == 0x12
+    scale_off = (48 * 32 * 32 + 255) // 256 * 256
+    si = scale_off + 2 * ((t * 32 + b) * 16 + i)
+    assert img[si] == 0x34 and img[si + 1] == 0x12
+    assert img.sum() == sum(range(1, 33)) + 0x34 + 0x12  # everything else, padding included, is zero
+
+
+def test_pack_layout_of_one_q4_block():
+    n, k = 16, 512
+    blocks = np.zeros((n, k // 32, 18), np.uint8)
+    blocks[5, 3, 2:18] = np.arange(16, dtype=np.uint8) * 17
+    img = q.pack_image(q.Q4_0, blocks, n, k)
+    cell = (0 * 16 + 3) * 256 + 16 * 5
+    assert list(img[cell:cell + 16]) == list(np.arange(16) * 17)
 
 
 def _status(fn, *args):

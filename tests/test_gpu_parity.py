@@ -224,3 +224,24 @@ def test_grouped_empty_assignment_list():
     e = torch.zeros(0, dtype=torch.int32, device="cuda")
     y, ws = q.qgemv_q8_0_grouped(img, 1, n, k, x, e, e)
     assert y.shape == (0, n) and q.grouped_status(ws) == 0
+
+
+def test_set_rows_equals_single_calls():
+    """The fp32-rows set launch (quantization fused for 1-2 rows, one shared quantize launch otherwise) gives
+    the same bits as one call per projection."""
+    layer = [(2048, 1024), (512, 1024), (1024, 4096), (300, 800)]
+    for fmt, ofmt in FMTS:
+        imgs = [oracle_image(ofmt, gauss((n, k), 0.02, 21, i).numpy())[1] for i, (n, k) in enumerate(layer)]
+        for rows in (1, 2, 3, 5, 16):
+            log(f"set_rows fmt={fmt} rows={rows}")
+            xs = {k: torch.from_numpy(gauss((rows, k), 1.0, 21, 32 + k % 97).numpy()).cuda() for _, k in layer}
+            wss = {k: q.empty_ws(rows, k) for _, k in layer}
+            projs, singles = [], []
+            fn = q.qgemv_q8_0 if fmt == q.Q8_0 else q.qgemv_q4_0
+            for (n, k), img in zip(layer, imgs):
+                y = torch.full((rows, n), float("nan"), device="cuda")
+                projs.append((img, n, k, xs[k], None if rows <= q.FUSED_ROWS else wss[k], y))
+                singles.append(fn(img, n, k, xs[k]))
+            q.qgemv_set_rows(fmt, projs, rows)
+            for p, ys in zip(projs, singles):
+                assert np.array_equal(bits(p[5]), bits(ys))
