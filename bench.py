@@ -2,10 +2,10 @@
 """Benchmark of the few-row block-quantized GEMV on one MI355X.
 
 Headline step: one decode layer of a Llama-3.2-1B-shaped model in the Q8_0
-lane at one activation row -- the q8 quantization of the layer's three input
-rows (one launch) and its seven projections Wq 2048x2048, Wk/Wv 512x2048, Wo
-2048x2048, gate/up 8192x2048, down 2048x8192 (one launch), 64,618,496 weight
-bytes.  The weights rotate through enough distinct copies (>= 1 GiB) that every
+lane at one activation row -- the seven projections Wq 2048x2048, Wk/Wv
+512x2048, Wo 2048x2048, gate/up 8192x2048, down 2048x8192 (64,618,496 weight
+bytes) with the q8 quantization of their three fp32 input rows, all in one
+launch.  The weights rotate through enough distinct copies (>= 1 GiB) that every
 step streams them from HBM, not from the 256 MB Infinity Cache.
 
 Prints one JSON line: weight GB/s of the step (value), the roofline of the
@@ -45,6 +45,12 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--out", default=None, help="also write the JSON line (with the sweep) to this file")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run a plain elementwise kernel over 256 MiB (reads 256 MiB, writes 256 MiB) five "
+                        "times, the known-size reference for the HBM byte counters")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                   help="reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) "
+                        "of a --calibrate-copy run into profiles/traffic.json, then exit")
     return p.parse_args()
 
 
@@ -82,10 +88,71 @@ def ctypes_arr(struct, items):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("qg_kernels.hip", "qg_layout.h"):
+    for f in ("qg_q8.hip", "qg_device.h", "qg_layout.h"):
         with open(os.path.join(ROOT, "block_quantized_few_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+COPY_BYTES = 256 << 20
+
+
+def calibrate_copy(torch):
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def pmc_per_dispatch(path, counter):
+    """{kernel name: [value per dispatch]} of one counter from a rocprofv3 counter_collection.csv."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def reduce_traffic(fetch_csv, write_csv):
+    """HBM bytes per launch of the headline kernel, from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by the factor that maps the same counter to the known bytes of the calibration kernel."""
+    fetch = pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = pmc_per_dispatch(write_csv, "WRITE_SIZE")
+
+    def pick(d, pat, big=False):
+        vals = [v for name, vs in d.items() if pat in name for v in vs]
+        if big:
+            vals = [v for v in vals if v * 1024 > COPY_BYTES / 2]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named like {pat!r} in the counter file")
+        return sum(vals) / len(vals), len(vals)
+
+    cf, _ = pick(fetch, "neg", big=True)
+    cw, _ = pick(write, "neg", big=True)
+    kf, nf = pick(fetch, "rl_set_kernel")
+    kw, nw = pick(write, "rl_set_kernel")
+    ff, fw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    rec = {"rl_set_kernel|llama1b-layer-q8_0-rows1": {
+        "hbm_bytes_per_launch": round(kf * 1024 * ff + kw * 1024 * fw),
+        "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kw, 1), "dispatches": [nf, nw],
+        "calibration": {"kernel": "torch.neg over 256 MiB fp32", "known_bytes_each_way": COPY_BYTES,
+                        "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                        "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
+        "source_hash": kernel_source_hash()}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def read_traffic(kernel, workload):
@@ -140,13 +207,25 @@ class LayerSet:
         self.launches = 1 if rows <= q.FUSED_ROWS else 2
 
     def alg_bytes_gemv(self):
-        """Algorithmic bytes of one set launch: weights + q8 rows (codes + fp32 scales) + fp32 outputs."""
+        """Algorithmic bytes of the GEMV launch: weights + activations + fp32 outputs.
+
+        Fused (rows <= FUSED_ROWS): each distinct fp32 activation set is read once.  Otherwise the launch
+        reads q8 rows (codes + fp32 scales, + int32 code sums for Q4_0) per projection."""
+        out = sum(self.rows * n * 4 for _, n, _k in self.layer)
+        if self.rows <= self.q.FUSED_ROWS:
+            srcs = {}
+            for name, _n, k in self.layer:
+                srcs[LAYER_SRC.get(name, 0)] = k
+            return self.wbytes + out + sum(self.rows * k * 4 for k in srcs.values())
         act = 1.0 + 4.0 / 32 + (4.0 / 32 if self.fmt == self.q.Q4_0 else 0.0)
-        return self.wbytes + sum(self.rows * k * act + self.rows * n * 4 for _, n, k in self.layer)
+        return self.wbytes + out + sum(self.rows * k * act for _, _n, k in self.layer)
 
 
 def main():
     args = parse()
+    if args.traffic:
+        reduce_traffic(*args.traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py measures one GPU: this build runs the GEMV on a single MI355X and has no multi-GPU "
@@ -162,6 +241,8 @@ def main():
     stream = torch.cuda.current_stream()
     sh = C.c_void_p(stream.cuda_stream)
     timer = Timer(torch)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
 
     # ------------------------------------------------------------ headline ---
     rows = 1
@@ -192,8 +273,8 @@ def main():
     ms_per_step = total_ms / K
     # At one row the step is one launch of the GEMV kernel (quantization fused), so the events around the
     # K back-to-back steps on the kernel's own stream also give its average launch duration.
-    gemv_avg_ms = ms_per_step / layer.launches if layer.launches == 1 else None
-    gemv_ms = [gemv_avg_ms] * K
+    assert layer.launches == 1
+    gemv_avg_ms = ms_per_step
     # a host-side check that the layer outputs are finite (no silent garbage)
     assert all(bool(torch.isfinite(y).all()) for y in layer.ys)
 
@@ -222,8 +303,7 @@ def main():
                    "launches_per_step": layer.launches, "parallelism": "single GPU"},
         "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": int(alg), "avg_launch_us": round(gemv_avg_ms * 1e3, 3),
-                     "median_launch_us": round(gemv_ms[K // 2] * 1e3, 3)},
+                     "alg_bytes_per_launch": int(alg), "avg_launch_us": round(gemv_avg_ms * 1e3, 3)},
         "host_enqueue_ms": round(host_ms, 3),
     }
 

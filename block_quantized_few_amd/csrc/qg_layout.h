@@ -104,7 +104,13 @@ QG_HD GroupedLayout grouped_layout(int64_t x_rows, int64_t k, int64_t m) {
 
 struct PartPlan {
   int P, H, S, BS;
+  int lgP, lgH, lgS;  // log2 of the powers of two P, H, S
 };
+QG_HD int ilog2(int v) {
+  int l = 0;
+  while ((1 << (l + 1)) <= v) l++;
+  return l;
+}
 QG_HD PartPlan part_plan(int kbp) {
   const int m = kbp / 8;  // parts of about eight blocks
   int P = 1;
@@ -114,6 +120,9 @@ QG_HD PartPlan part_plan(int kbp) {
   pl.S = P < 4 ? P : 4;
   pl.H = P / pl.S;
   pl.BS = kbp / P;
+  pl.lgP = ilog2(pl.P);
+  pl.lgH = ilog2(pl.H);
+  pl.lgS = ilog2(pl.S);
   return pl;
 }
 

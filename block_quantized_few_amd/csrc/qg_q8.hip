@@ -29,7 +29,7 @@
 
 namespace qg {
 
-constexpr int WG = 256;
+constexpr int WG = 512;
 constexpr int WAVES = WG / WAVE;
 constexpr int LDS_X_RL = 80 * 1024;   // staged rows, RL (leaves room for 2+ workgroups per CU)
 constexpr int FUSE_MAX_ROWS = 2;      // rows quantized inside the GEMV launch
@@ -40,67 +40,119 @@ __host__ __device__ inline int x_block_bytes(int fmt) { return fmt == FMT_Q4 ? 4
 // Slots are ordered (u, wave part, lane part), so lanes that step together read
 // neighbouring slots.
 __device__ __forceinline__ int slot_block(const PartPlan& pl, int u0, int slot) {
-  const int u = u0 + slot / pl.P, part = slot % pl.P;
-  return (part / pl.H) * pl.H * pl.BS + pl.H * u + (part % pl.H);
+  const int u = u0 + (slot >> pl.lgP), part = slot & (pl.P - 1);
+  return (part & ~(pl.H - 1)) * pl.BS + pl.H * u + (part & (pl.H - 1));
 }
+
+// Blocks per part per staging round of an RL tile whose R rows get lds_x bytes
+// of LDS: all BS at once, or a multiple of four (a round then starts on the
+// block that the lane's first register set holds).  lds_x always holds four
+// rounds' worth for any plan (P <= 32, R <= 16: 4 * 16 * 32 * 40 bytes).
+__host__ __device__ inline int rl_round(int lds_x, int R, const PartPlan& pl, int fmt) {
+  const int uc_max = lds_x / (R * pl.P * x_block_bytes(fmt));
+  return uc_max >= pl.BS ? pl.BS : (uc_max & ~3);
+}
+
+// Blocks a lane keeps in flight (memory parallelism comes from the many waves).
+__host__ __device__ constexpr int rl_lookahead(bool, int) { return 2; }
 
 // ------------------------------------------------------------- staging ---
 
 // RL layout: codes [R][nslot][32], dx [R][nslot], nsx [R][nslot].
-template <int FMT>
-__device__ void stage_rl(uint8_t* lds, const Prep& prep, const int* s_src, int R, int kbp, const PartPlan& pl,
-                         int u0, int nslot) {
+template <int FMT, int R>
+__device__ void stage_rl(uint8_t* lds, const Prep& prep, const int* s_src, int kbp, const PartPlan& pl, int u0,
+                         int nslot) {
   const int tid = threadIdx.x;
   uint4* lc = reinterpret_cast<uint4*>(lds);
   float* ld = reinterpret_cast<float*>(lds + (size_t)R * nslot * 32);
   int* ln = reinterpret_cast<int*>(lds + (size_t)R * nslot * 36);
-  for (int e = tid; e < R * nslot * 2; e += WG) {
-    const int r = e / (nslot * 2), rem = e - r * nslot * 2, slot = rem >> 1, half = rem & 1;
-    const int b = slot_block(pl, u0, slot);
-    lc[e] = ld16(prep.codes + ((size_t)s_src[r] * kbp + b) * 32 + half * 16);
-  }
-  for (int e = tid; e < R * nslot; e += WG) {
-    const int r = e / nslot, slot = e - r * nslot;
-    const int b = slot_block(pl, u0, slot);
-    ld[e] = prep.dx[(size_t)s_src[r] * kbp + b];
-    if (FMT == FMT_Q4) ln[e] = prep.nsx[(size_t)s_src[r] * kbp + b];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const size_t src = (size_t)s_src[r] * kbp;
+    for (int e = tid; e < nslot * 2; e += WG) {
+      const int b = slot_block(pl, u0, e >> 1);
+      lc[r * nslot * 2 + e] = ld16(prep.codes + (src + b) * 32 + (e & 1) * 16);
+    }
+    for (int e = tid; e < nslot; e += WG) {
+      const int b = slot_block(pl, u0, e);
+      ld[r * nslot + e] = prep.dx[src + b];
+      if (FMT == FMT_Q4) ln[r * nslot + e] = prep.nsx[src + b];
+    }
   }
 }
 
 // RL layout, quantizing fp32 rows on the way (all of kbp staged): four lanes per
-// block, the same arithmetic as the stand-alone quantizer.  The start values
-// are written for Q4_0 only (the Q8_0 staging area has no room for them).
+// block (work item e: quarter e & 3 of staged block e >> 2), the same
+// arithmetic as the stand-alone quantizer.  The start values are written for
+// Q4_0 only (the Q8_0 staging area has no room for them).
+//
+// Split in two so that a caller can issue its weight loads in between: the
+// memory counter a wave waits on retires loads in issue order, so activation
+// values loaded first can be quantized while the weight loads are in flight.
+constexpr int XQ_FIRST = 4;  // work items per thread whose loads are issued first
+
+struct XQuarter {
+  float4 a, c;
+};
+
+// Work item e of R <= 2 rows: row r = e / (4 * nslot), without a division.
+__device__ __forceinline__ int xq_row(int e, int nslot) { return e >= 4 * nslot ? 1 : 0; }
+
+__device__ __forceinline__ XQuarter xq_load(const float* __restrict__ x, int64_t k, int kb, int nslot,
+                                            const PartPlan& pl, int e, int total) {
+  const int q = e & 3, blk = e >> 2;
+  const int r = xq_row(e, nslot), slot = blk - r * nslot;
+  const int b = slot_block(pl, 0, slot);
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  XQuarter v;
+  v.a = z;
+  v.c = z;
+  if (e < total) {  // uniform over a wave: total is a multiple of 64
+    // pad blocks read the row's first quarter and use zeros
+    const bool ok = b < kb;
+    const float4* src = reinterpret_cast<const float4*>(x + (ok ? (int64_t)r * k + (int64_t)b * QK + q * 8 : 0));
+    const float4 a = src[0], c = src[1];
+    v.a = ok ? a : z;
+    v.c = ok ? c : z;
+  }
+  return v;
+}
+
 template <int FMT>
-__device__ void stage_rl_quantize(uint8_t* lds, const float* __restrict__ x, int64_t k, int kb, int R, int kbp,
-                                  const PartPlan& pl) {
-  const int tid = threadIdx.x;
-  const int nslot = kbp;
-  uint8_t* lc = lds;
-  float* ld = reinterpret_cast<float*>(lds + (size_t)R * nslot * 32);
-  int* ln = reinterpret_cast<int*>(lds + (size_t)R * nslot * 36);
-  const int total = R * nslot * 4;  // a multiple of 4: quads stay whole
-  for (int e = tid; e < total; e += WG) {
-    const int q = e & 3, blk = e >> 2;
-    const int r = blk / nslot, slot = blk - r * nslot;
-    const int b = slot_block(pl, 0, slot);
-    float v[8];
-    if (b < kb) {
-      const float4* src = reinterpret_cast<const float4*>(x + (int64_t)r * k + (int64_t)b * QK + q * 8);
-      const float4 a = src[0], c = src[1];
-      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
-    } else {
+__device__ __forceinline__ void xq_store(const XQuarter& xv, uint8_t* lds, int R, int nslot, int e, int total) {
+  if (e >= total) return;  // whole quads leave together: total and the stride are multiples of 4
+  const int q = e & 3, blk = e >> 2;
+  const int r = xq_row(e, nslot), slot = blk - r * nslot;
+  const float v[8] = {xv.a.x, xv.a.y, xv.a.z, xv.a.w, xv.c.x, xv.c.y, xv.c.z, xv.c.w};
+  unsigned lo, hi;
+  float d;
+  int sum;
+  quantize_quarter(v, lo, hi, d, sum);
+  *reinterpret_cast<uint2*>(lds + ((size_t)r * nslot + slot) * 32 + q * 8) = make_uint2(lo, hi);
+  if (q == 0) {
+    reinterpret_cast<float*>(lds + (size_t)R * nslot * 32)[r * nslot + slot] = d;
+    if (FMT == FMT_Q4) reinterpret_cast<int*>(lds + (size_t)R * nslot * 36)[r * nslot + slot] = -8 * sum;
+  }
+}
+
+// First part: load this thread's first XQ_FIRST work items.
+__device__ __forceinline__ void stage_quantize_begin(XQuarter (&xv)[XQ_FIRST], const float* __restrict__ x,
+                                                     int64_t k, int kb, int R, int kbp, const PartPlan& pl) {
+  const int total = R * kbp * 4;
 #pragma unroll
-      for (int i = 0; i < 8; i++) v[i] = 0.0f;
-    }
-    unsigned lo, hi;
-    float d;
-    int sum;
-    quantize_quarter(v, lo, hi, d, sum);
-    *reinterpret_cast<uint2*>(lc + ((size_t)r * nslot + slot) * 32 + q * 8) = make_uint2(lo, hi);
-    if (q == 0) {
-      ld[r * nslot + slot] = d;
-      if (FMT == FMT_Q4) ln[r * nslot + slot] = -8 * sum;
-    }
+  for (int j = 0; j < XQ_FIRST; j++) xv[j] = xq_load(x, k, kb, kbp, pl, threadIdx.x + j * WG, total);
+}
+
+// Second part: quantize them into LDS, then the rest of the work items.
+template <int FMT>
+__device__ __forceinline__ void stage_quantize_end(const XQuarter (&xv)[XQ_FIRST], uint8_t* lds,
+                                                   const float* __restrict__ x, int64_t k, int kb, int R, int kbp,
+                                                   const PartPlan& pl) {
+  const int total = R * kbp * 4;
+#pragma unroll
+  for (int j = 0; j < XQ_FIRST; j++) xq_store<FMT>(xv[j], lds, R, kbp, threadIdx.x + j * WG, total);
+  for (int e = threadIdx.x + XQ_FIRST * WG; e < total; e += WG) {
+    xq_store<FMT>(xq_load(x, k, kb, kbp, pl, e, total), lds, R, kbp, e, total);
   }
 }
 
@@ -120,72 +172,110 @@ struct TileArgs {
   int64_t ldy;
   const int* s_dst; // output row of each activation row (LDS)
   int lds_x;        // LDS bytes for staged rows
+  PartPlan pl;      // partition of kbp
+  int ucx;          // RL staging round (rl_round)
 };
 
+// One weight block of one row as a lane holds it.
+template <int FMT>
+struct WBlock {
+  uint4 lo;
+  uint4 hi;  // Q8_0 high half
+  uint16_t sc;
+};
+
+// Block b of the lane's row.  The address is the tile's base (uniform) plus a
+// 32-bit lane offset, so the loads take the scalar-base form.
+template <int FMT>
+__device__ __forceinline__ WBlock<FMT> load_block(const uint8_t* __restrict__ tcode, uint32_t woff,
+                                                  const uint16_t* __restrict__ tscale, uint32_t soff, int b) {
+  constexpr uint32_t CB = FMT == FMT_Q8 ? 512 : 256;
+  WBlock<FMT> w;
+  w.lo = ld16_stream(tcode + (woff + (uint32_t)b * CB));
+  if (FMT == FMT_Q8) w.hi = ld16_stream(tcode + (woff + (uint32_t)b * CB + 256));
+  w.sc = ld2_stream(tscale + (soff + (uint32_t)b * TILE));
+  return w;
+}
+
+// acc[r] = fma(isum, dw * dx, acc[r]) for one block, its activation blocks at
+// staged slot `slot`.
 template <int FMT, int R>
-__device__ __forceinline__ void rl_accumulate(float (&acc)[R], const uint8_t* __restrict__ wrow,
-                                              const uint16_t* __restrict__ srow, const uint8_t* lds, int nslot,
-                                              const PartPlan& pl, int s, int h, int u0, int uc) {
-  constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
-  const uint8_t* lc = lds;
+__device__ __forceinline__ void compute_block(float (&acc)[R], const WBlock<FMT>& w, const uint8_t* lds, int nslot,
+                                              int slot) {
   const float* ld = reinterpret_cast<const float*>(lds + (size_t)R * nslot * 32);
   const int* ln = reinterpret_cast<const int*>(lds + (size_t)R * nslot * 36);
-  const int bstart = s * pl.H * pl.BS + pl.H * u0 + h;
-  const int sstart = s * pl.H + h;
-#pragma unroll 4
-  for (int u = 0; u < uc; u++) {
-    const int b = bstart + pl.H * u;
-    const int slot = u * pl.P + sstart;
-    uint4 wl, wh;
-    wl = ld16_stream(wrow + (size_t)b * CB);
-    if (FMT == FMT_Q8) wh = ld16_stream(wrow + (size_t)b * CB + 256);
-    const float dw = h2f(ld2_stream(srow + (size_t)b * TILE));
+  const float dw = h2f(w.sc);
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      const uint8_t* xb = lc + ((size_t)r * nslot + slot) * 32;
-      const uint4 xl = ld16(xb), xh = ld16(xb + 16);
-      const float dxr = ld[r * nslot + slot];
-      const int isum = FMT == FMT_Q8 ? dot_q8(wl, wh, xl, xh) : dot_q4(wl, xl, xh, ln[r * nslot + slot]);
-      acc[r] = __builtin_fmaf((float)isum, dw * dxr, acc[r]);
-    }
+  for (int r = 0; r < R; r++) {
+    const uint8_t* xb = lds + ((size_t)r * nslot + slot) * 32;
+    const uint4 xl = ld16(xb), xh = ld16(xb + 16);
+    const float dxr = ld[r * nslot + slot];
+    const int isum = FMT == FMT_Q8 ? dot_q8(w.lo, w.hi, xl, xh) : dot_q4(w.lo, xl, xh, ln[r * nslot + slot]);
+    acc[r] = __builtin_fmaf((float)isum, dw * dxr, acc[r]);
   }
 }
 
-// One RL tile: weight rows row0 .. row0 + 256/P - 1.  `stage`: the activation
+// One RL tile: weight rows row0 .. row0 + WG/P - 1.  `stage`: the activation
 // rows are not in LDS yet.  Returns whether LDS now holds all of them (so the
 // next tile of the same rows may skip staging).
+//
+// A lane streams its part's blocks u = 0 .. BS-1 with LA blocks in flight:
+// the load of block u+LA is issued as block u is used.  The first LA are
+// issued before the activation rows are staged (and, when they are quantized
+// here, after their fp32 loads, which the wave's in-order memory counter then
+// returns first).
 template <int FMT, int R, bool FUSED>
 __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity, bool stage) {
-  const PartPlan pl = part_plan(ta.kbp);
-  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int rpw = WAVE / pl.H;  // rows per wave
-  const int g = wave / pl.S, s = wave % pl.S, h = lane / rpw, rl = lane % rpw;
+  static_assert(!FUSED || R <= FUSE_MAX_ROWS, "fused quantization stages at most two rows");
+  const PartPlan& pl = ta.pl;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
+  const int lg_rpw = 6 - pl.lgH, rpw = 1 << lg_rpw;  // rows per wave
+  const int g = wave >> pl.lgS, s = wave & (pl.S - 1), h = lane >> lg_rpw, rl = lane & (rpw - 1);
   const int64_t row = ta.row0 + g * rpw + rl;
   const bool valid = row < ta.n;
   const int64_t rc = valid ? row : ta.n - 1;  // out-of-range lanes read a real row, store nothing
-  const uint8_t* wrow = ta.code + cell_row_offset(FMT, rc, 0, ta.kbp);
-  const uint16_t* srow = ta.scale + scale_index(rc, 0, ta.kbp);
+  // tile base (uniform) + lane offset (< 2^32: a tile spans WG/P rows of kbp blocks)
+  const int64_t t0 = ta.row0 >> 4;
+  const uint8_t* tcode = ta.code + cell_row_offset(FMT, t0 * TILE, 0, ta.kbp);
+  const uint16_t* tscale = ta.scale + scale_index(t0 * TILE, 0, ta.kbp);
+  const uint32_t woff = (uint32_t)((rc >> 4) - t0) * (uint32_t)ta.kbp * (FMT == FMT_Q8 ? 512u : 256u) +
+                        (uint32_t)(rc & 15) * 16u;
+  const uint32_t soff = (uint32_t)((rc >> 4) - t0) * (uint32_t)ta.kbp * 16u + (uint32_t)(rc & 15);
 
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; r++) acc[r] = 0.0f;
-  const int uc_max = ta.lds_x / (R * pl.P * x_block_bytes(FMT));
-  const bool full = uc_max >= pl.BS;
-  if (full) {
-    if (stage) {
+  const int ucx = ta.ucx;
+  const bool full = ucx == pl.BS;          // every block staged at once
+  const int bpart = s * pl.H * pl.BS + h;  // this lane's block at u = 0
+  const int sbase = s * pl.H + h;          // its slot at u = 0 of a round
+
+  constexpr int LA = rl_lookahead(FUSED, R);
+  XQuarter xv[XQ_FIRST];
+  if (FUSED && stage) stage_quantize_begin(xv, ta.xf, ta.k, ta.kb, R, ta.kbp, pl);
+  WBlock<FMT> w[LA];
+#pragma unroll
+  for (int j = 0; j < LA; j++) w[j] = load_block<FMT>(tcode, woff, tscale, soff, bpart + pl.H * j);  // BS >= 8
+  __builtin_amdgcn_sched_barrier(0);
+  int u0 = 0, nslot = ucx << pl.lgP;
+  int next_round = (!full || stage) ? 0 : pl.BS;  // u at which activation rows are (re)staged
+  for (int u = 0; u < pl.BS; u += LA) {
+    if (u == next_round) {
+      u0 = u;
+      nslot = min(ucx, pl.BS - u) << pl.lgP;
+      next_round = full ? pl.BS : u + ucx;
       __syncthreads();
-      if (FUSED) stage_rl_quantize<FMT>(lds, ta.xf, ta.k, ta.kb, R, ta.kbp, pl);
-      else stage_rl<FMT>(lds, ta.prep, ta.s_src, R, ta.kbp, pl, 0, ta.kbp);
+      if (FUSED) stage_quantize_end<FMT>(xv, lds, ta.xf, ta.k, ta.kb, R, ta.kbp, pl);
+      else stage_rl<FMT, R>(lds, ta.prep, ta.s_src, ta.kbp, pl, u0, nslot);
       __syncthreads();
     }
-    rl_accumulate<FMT, R>(acc, wrow, srow, lds, ta.kbp, pl, s, h, 0, pl.BS);
-  } else {
-    for (int u0 = 0; u0 < pl.BS; u0 += uc_max) {
-      const int uc = min(uc_max, pl.BS - u0), nslot = uc * pl.P;
-      __syncthreads();
-      stage_rl<FMT>(lds, ta.prep, ta.s_src, R, ta.kbp, pl, u0, nslot);
-      __syncthreads();
-      rl_accumulate<FMT, R>(acc, wrow, srow, lds, nslot, pl, s, h, u0, uc);
+    const int slot = ((u - u0) << pl.lgP) + sbase;
+#pragma unroll
+    for (int j = 0; j < LA; j++) {
+      if (u + j < pl.BS) {
+        compute_block<FMT, R>(acc, w[j], lds, nslot, slot + (j << pl.lgP));
+        if (u + j + LA < pl.BS) w[j] = load_block<FMT>(tcode, woff, tscale, soff, bpart + pl.H * (u + j + LA));
+      }
     }
   }
   // lane parts: ((h0 + h1) + (h2 + h3)) + ...; every lane of the row gets the same bits
@@ -275,10 +365,10 @@ template <int FMT, int H>
 __device__ void mf_tile(const TileArgs& ta, int R, float* red, int parity) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
   constexpr int NT = H >= 4 ? 1 : 4 / H;
-  const PartPlan pl = part_plan(ta.kbp);
-  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int g = wave / pl.S, s = wave % pl.S;
-  const int i = lane % 16, q = lane / 16;
+  const PartPlan& pl = ta.pl;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
+  const int g = wave >> pl.lgS, s = wave & (pl.S - 1);
+  const int i = lane & 15, q = lane >> 4;
   const int64_t ntiles = np_of(ta.n) / TILE;
   const int64_t wrow0 = ta.row0 + (int64_t)g * TILE * NT;  // first row of this wave's tiles
   const uint8_t* abase[NT];
@@ -354,6 +444,8 @@ struct ProjDev {
   int kb, kbp;
   int tiles;
   int rows_per_tile;
+  PartPlan pl;
+  int ucx;  // RL staging round
 };
 struct SetArgs {
   ProjDev p[QG_MAX_SET];
@@ -385,6 +477,8 @@ __device__ __forceinline__ TileArgs tile_args(const ProjDev& d, int64_t row0, co
   ta.ldy = d.n;
   ta.s_dst = s_map + QG_MAX_ROWS;
   ta.lds_x = lds_x;
+  ta.pl = d.pl;
+  ta.ucx = d.ucx;
   return ta;
 }
 
@@ -392,7 +486,7 @@ __device__ __forceinline__ TileArgs tile_args(const ProjDev& d, int64_t row0, co
 // w + G, w + 2G, ... and keeps a projection's activation rows in LDS while its
 // tiles last.
 template <int FMT, int R, bool FUSED>
-__global__ __launch_bounds__(WG) void rl_set_kernel(SetArgs a, int lds_x) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void rl_set_kernel(SetArgs a, int lds_x) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
@@ -407,7 +501,7 @@ __global__ __launch_bounds__(WG) void rl_set_kernel(SetArgs a, int lds_x) {
     staged = full ? p : -1;
     // the combine area alternates only between tiles that pass its barrier, so
     // a buffer is rewritten only after everyone has read it
-    if (part_plan(d.kbp).S > 1) parity ^= 1;
+    if (d.pl.S > 1) parity ^= 1;
   }
 }
 
@@ -423,7 +517,7 @@ __global__ __launch_bounds__(WG) void mf_set_kernel(SetArgs a, int R) {
     while (p + 1 < a.count && t0 >= a.p[p].tiles) t0 -= a.p[p++].tiles;
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, 0);
-    const PartPlan pl = part_plan(d.kbp);
+    const PartPlan& pl = d.pl;
     if (pl.H == 1) mf_tile<FMT, 1>(ta, R, red, parity);
     else if (pl.H == 2) mf_tile<FMT, 2>(ta, R, red, parity);
     else if (pl.H == 4) mf_tile<FMT, 4>(ta, R, red, parity);
@@ -498,12 +592,14 @@ __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __res
 }
 
 template <int R>
-__device__ __forceinline__ void grouped_rows(const TileArgs& ta, uint8_t* lds, float* red) {
+__device__ __forceinline__ void grouped_rows(TileArgs ta, uint8_t* lds, float* red) {
+  ta.ucx = rl_round(ta.lds_x, R, ta.pl, FMT_Q8);
   rl_tile<FMT_Q8, R, false>(ta, lds, red, 0, true);
 }
 
 __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__ images, int64_t expert_bytes,
-                                                     size_t scale_off, int64_t n, int64_t k, int kbp, Prep prep,
+                                                     size_t scale_off, int64_t n, int64_t k, int kbp, PartPlan pl,
+                                                     Prep prep,
                                                      const int* __restrict__ header, const int* __restrict__ sorted,
                                                      const int* __restrict__ items,
                                                      const int32_t* __restrict__ x_index, float* y, int lds_x) {
@@ -526,7 +622,7 @@ __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__
   ta.kbp = kbp;
   ta.kb = (int)kb_of(k);
   ta.k = k;
-  ta.row0 = (int64_t)blockIdx.x * (WG / part_plan(kbp).P);
+  ta.row0 = (int64_t)blockIdx.x * (WG >> pl.lgP);
   ta.prep = prep;
   ta.xf = nullptr;
   ta.s_src = s_map;
@@ -534,6 +630,8 @@ __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__
   ta.ldy = n;
   ta.s_dst = s_map + QG_MAX_ROWS;
   ta.lds_x = lds_x;
+  ta.pl = pl;
+  ta.ucx = 0;  // set per row count
   float* red = reinterpret_cast<float*>(lds + lds_x);
   switch (cnt) {
 #define QG_CASE(RR) \
@@ -611,11 +709,22 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
   memset(&a, 0, sizeof a);
   a.count = count;
   const bool mf = prep_in_fragment_order(rows);
+  // Tiles of projections with longer rows come first: their workgroups stage
+  // the most activation blocks, so they get the earliest start.  The order
+  // changes no result (each projection has its own output).
+  int order[QG_MAX_SET];
+  for (int i = 0; i < count; i++) order[i] = i;
+  for (int i = 1; i < count; i++)
+    for (int j = i; j > 0 && projs[order[j]].k > projs[order[j - 1]].k; j--) {
+      const int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
   bool fused = true;
   int64_t tiles = 0;
   size_t need = 0;
   for (int i = 0; i < count; i++) {
-    const ProjArg& pa = projs[i];
+    const ProjArg& pa = projs[order[i]];
     ProjDev& d = a.p[i];
     const uint8_t* img = (const uint8_t*)pa.image;
     d.code = img;
@@ -628,6 +737,7 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
     d.kb = (int)kb_of(pa.k);
     d.kbp = (int)kbp_of(pa.k);
     const PartPlan pl = part_plan(d.kbp);
+    d.pl = pl;
     d.rows_per_tile = mf ? (WAVES / pl.S) * TILE * mf_tiles_per_wave(pl.H) : WG / pl.P;
     d.tiles = (int)((pa.n + d.rows_per_tile - 1) / d.rows_per_tile);
     tiles += d.tiles;
@@ -639,6 +749,7 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
   const size_t cap = LDS_X_RL;
   fused = fused && !mf && need <= cap;  // the fused path stages every row whole
   const int lds_x = (int)((need < cap ? need : cap) + 15) / 16 * 16;
+  for (int i = 0; i < count; i++) a.p[i].ucx = rl_round(lds_x, rows, a.p[i].pl, fmt);
   if (mf) {
     if (fmt == FMT_Q8) launch_mf<FMT_Q8>(a, rows, s);
     else launch_mf<FMT_Q4>(a, rows, s);
@@ -670,7 +781,7 @@ int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, 
   if (lds > 64 * 1024) hipFuncSetAttribute((const void*)grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int64_t eb = (int64_t)image_total_bytes(QG_FMT_Q8_0, n, k);
   const size_t so = image_scale_offset(QG_FMT_Q8_0, n, k);
-  hipLaunchKernelGGL(grouped_kernel, dim3(tiles, m), dim3(WG), lds, s, (const uint8_t*)images, eb, so, n, k, kbp,
+  hipLaunchKernelGGL(grouped_kernel, dim3(tiles, m), dim3(WG), lds, s, (const uint8_t*)images, eb, so, n, k, kbp, pl,
                      prep_view(w + G.prep, x_rows, k), header, sorted, items, x_index, y, lds_x);
   return hip_status(hipGetLastError(), "grouped_kernel");
 }

@@ -15,7 +15,7 @@ from helpers import TOL, bits, gauss, log, oracle_image, outliers, rel_err, rel_
 pytestmark = pytest.mark.gpu
 
 FMTS = [(q.Q8_0, O.Q8_0), (q.Q4_0, O.Q4_0)]
-ROWS = [1, 2, 3, 4, 7, 8, 9, 15, 16]
+ROWS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 15, 16]
 
 
 def _special_blocks(x):
