@@ -89,7 +89,7 @@ __device__ void stage_rl(uint8_t* lds, const Prep& prep, const int* s_src, int k
 // Split in two so that a caller can issue its weight loads in between: the
 // memory counter a wave waits on retires loads in issue order, so activation
 // values loaded first can be quantized while the weight loads are in flight.
-constexpr int XQ_FIRST = 4;  // work items per thread whose loads are issued first
+constexpr int XQ_FIRST = 2;  // work items per thread whose loads are issued first
 
 struct XQuarter {
   float4 a, c;
