@@ -228,7 +228,7 @@ template <int FMT, int R, bool FUSED>
 __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity, bool stage) {
   static_assert(!FUSED || R <= FUSE_MAX_ROWS, "fused quantization stages at most two rows");
   const PartPlan& pl = ta.pl;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
   const int lg_rpw = 6 - pl.lgH, rpw = 1 << lg_rpw;  // rows per wave
   const int g = wave >> pl.lgS, s = wave & (pl.S - 1), h = lane >> lg_rpw, rl = lane & (rpw - 1);
   const int64_t row = ta.row0 + g * rpw + rl;
@@ -306,54 +306,136 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
 
 // ------------------------------------------------------------- MF tile ---
 
-// NT 16-row image tiles per wave (so that a wave keeps NT * H >= 4 independent
-// MFMA accumulations in flight and reuses each activation fragment NT times).
-__host__ __device__ inline int mf_tiles_per_wave(int H) { return H >= 4 ? 1 : 4 / H; }
+// NT 16-row image tiles per wave, so that a wave keeps several independent
+// MFMA accumulations in flight and reuses each activation fragment NT times.
+__host__ __device__ constexpr int mf_tiles_per_wave(int H) { return H >= 4 ? 1 : 2; }
 
-template <int FMT, int H, int NT>
-__device__ __forceinline__ void mf_accumulate(float (&acc)[NT][H][4], const uint8_t* const (&abase)[NT],
-                                              const uint16_t* const (&sbase)[NT], const Prep& prep, int R,
-                                              const PartPlan& pl, int s, int i, int q) {
+// One step of an MF wave: HC lane parts of one u for NT image tiles (two or
+// four MFMAs); the wave keeps two steps in flight.
+template <int FMT, int HC, int NT>
+struct MfStep {
+  uint2 a[NT][HC];  // A fragments: 8 codes of row i (Q4_0: 16 nibbles)
+  uint2 w[NT][HC];  // fp16 scales of rows 4q .. 4q+3
+  long x[HC];       // B fragments: 8 codes of activation row i
+  float dx[HC];
+  int ns[HC];       // Q4_0 start value -8 * sum(q_x)
+};
+
+// Where an MF wave reads: per image tile a base shared by the wave plus a lane
+// offset, so every load takes the scalar-base form and the addresses cost no
+// vector registers.
+template <int NT>
+struct MfAddr {
+  const uint8_t* code[NT];    // tile's code plane (wave-uniform)
+  const uint16_t* scale[NT];  // tile's scales (wave-uniform)
+  uint32_t aoff;              // lane's A-fragment byte offset in a cell
+  uint32_t soff;              // lane's first scale (fp16 units) in a cell
+  const int8_t* xc;           // prepared codes, fragment order (uniform)
+  const float* xd;
+  const int* xn;
+  uint32_t xoff;  // lane's B-fragment byte offset in a block's fragments
+  int R;
+};
+
+template <int FMT, int HC, int NT>
+__device__ __forceinline__ void mf_load(MfStep<FMT, HC, NT>& st, const MfAddr<NT>& ad, int i, int b0) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
-  const bool col = i < R;
+#pragma unroll
+  for (int hh = 0; hh < HC; hh++) {
+    const size_t b = (size_t)(b0 + hh);
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      st.a[t][hh] = ld8_stream(ad.code[t] + b * CB + ad.aoff);
+      st.w[t][hh] = ld8_stream(ad.scale[t] + b * TILE + ad.soff);
+    }
+    // lanes past the R rows read row R-1 again: their MFMA columns are never stored
+    st.x[hh] = *reinterpret_cast<const long*>(ad.xc + b * 32 * ad.R + ad.xoff);
+    st.dx[hh] = ad.xd[b * ad.R + i];
+    st.ns[hh] = FMT == FMT_Q4 ? ad.xn[b * ad.R + i] : 0;
+  }
+}
+
+template <int FMT, int HC, int NT>
+__device__ __forceinline__ void mf_compute(float (&acc)[NT][HC][4], const MfStep<FMT, HC, NT>& st, int sh) {
+#pragma unroll
+  for (int hh = 0; hh < HC; hh++)
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      uint2 av = st.a[t][hh];
+      if (FMT == FMT_Q4) {
+        av.x = (av.x >> sh) & 0x0F0F0F0Fu;
+        av.y = (av.y >> sh) & 0x0F0F0F0Fu;
+      }
+      long a;
+      __builtin_memcpy(&a, &av, 8);
+      const int ns = st.ns[hh];
+      v4i c = {ns, ns, ns, ns};
+      c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, st.x[hh], c, 0, 0, 0);
+      const uint2 wv = st.w[t][hh];
+      const float dw[4] = {h2f((uint16_t)(wv.x & 0xffff)), h2f((uint16_t)(wv.x >> 16)),
+                           h2f((uint16_t)(wv.y & 0xffff)), h2f((uint16_t)(wv.y >> 16))};
+#pragma unroll
+      for (int v = 0; v < 4; v++) acc[t][hh][v] = __builtin_fmaf((float)c[v], dw[v] * st.dx[hh], acc[t][hh][v]);
+    }
+}
+
+// After the last step of a half: add its HC lane parts by the pairwise tree
+// into `res` (second half: res = first + second, the tree's top node), and
+// clear the accumulators.
+template <int HC, int NT>
+__device__ __forceinline__ void mf_fold(float (&acc)[NT][HC][4], float (&res)[NT][4], bool second) {
+#pragma unroll
+  for (int t = 0; t < NT; t++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      float a[HC];
+#pragma unroll
+      for (int h = 0; h < HC; h++) a[h] = acc[t][h][v];
+#pragma unroll
+      for (int st = 1; st < HC; st *= 2)
+#pragma unroll
+        for (int h = 0; h + st < HC; h += 2 * st) a[h] = a[h] + a[h + st];
+      res[t][v] = second ? res[t][v] + a[0] : a[0];
+#pragma unroll
+      for (int h = 0; h < HC; h++) acc[t][h][v] = 0.0f;
+    }
+}
+
+// The wave's part of the partition, as NH = H/HC halves of HC lane parts: for
+// each half, u = 0 .. BS-1, one step (HC lane parts x NT tiles) per u.  Each lane part accumulates its blocks in u order; the halves are the two
+// subtrees of the lane-part tree.  Two steps are in flight.
+template <int FMT, int H, int NT>
+__device__ __forceinline__ void mf_accumulate(float (&res)[NT][4], const MfAddr<NT>& ad, const PartPlan& pl, int s,
+                                              int i, int q) {
+  constexpr int HC = H >= 4 ? 4 : H;
+  constexpr int NH = H / HC;  // 1, or 2 for H == 8
+  const int ic = i < ad.R ? i : ad.R - 1;  // activation row this lane reads
   const int sh = (q >> 1) * 4;
-  // rows prepared in fragment order: codes [kbp][4][R][8], dx and nsx [kbp][R]
-  const int8_t* xc = prep.codes + ((size_t)q * R + i) * 8;
-  const float* xd = prep.dx + i;
-  const int* xn = prep.nsx + i;
-  for (int u = 0; u < pl.BS; u++) {
+  const int BS = pl.BS;
+  const int bs0 = s * H * BS;
+  const int nsteps = BS * NH;  // >= 8
+  auto first_block = [&](int j) {
+    const int half = (NH == 2 && j >= BS) ? 1 : 0;
+    return bs0 + H * (j - half * BS) + half * HC;
+  };
+  float acc[NT][HC][4];
 #pragma unroll
-    for (int h = 0; h < H; h++) {
-      const int b = s * H * pl.BS + H * u + h;
-      uint2 av[NT], dwv[NT];
+  for (int t = 0; t < NT; t++)
 #pragma unroll
-      for (int t = 0; t < NT; t++) {
-        av[t] = ld8_stream(abase[t] + (size_t)b * CB);
-        dwv[t] = ld8_stream(sbase[t] + (size_t)b * TILE);
-      }
-      long bv = 0;
-      float dxj = 0.0f;
-      int ns = 0;
-      if (col) {
-        bv = *reinterpret_cast<const long*>(xc + (size_t)b * 32 * R);
-        dxj = xd[(size_t)b * R];
-        if (FMT == FMT_Q4) ns = xn[(size_t)b * R];
-      }
+    for (int h = 0; h < HC; h++)
 #pragma unroll
-      for (int t = 0; t < NT; t++) {
-        if (FMT == FMT_Q4) {
-          av[t].x = (av[t].x >> sh) & 0x0F0F0F0Fu;
-          av[t].y = (av[t].y >> sh) & 0x0F0F0F0Fu;
-        }
-        long a;
-        __builtin_memcpy(&a, &av[t], 8);
-        v4i c = {ns, ns, ns, ns};
-        c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bv, c, 0, 0, 0);
-        const float dw[4] = {h2f((uint16_t)(dwv[t].x & 0xffff)), h2f((uint16_t)(dwv[t].x >> 16)),
-                             h2f((uint16_t)(dwv[t].y & 0xffff)), h2f((uint16_t)(dwv[t].y >> 16))};
-#pragma unroll
-        for (int v = 0; v < 4; v++) acc[t][h][v] = __builtin_fmaf((float)c[v], dw[v] * dxj, acc[t][h][v]);
-      }
+      for (int v = 0; v < 4; v++) acc[t][h][v] = 0.0f;
+  MfStep<FMT, HC, NT> s0, s1;
+  mf_load(s0, ad, ic, first_block(0));
+  mf_load(s1, ad, ic, first_block(1));
+  for (int j = 0; j < nsteps; j += 2) {
+    mf_compute<FMT, HC, NT>(acc, s0, sh);
+    if (j + 2 < nsteps) mf_load(s0, ad, ic, first_block(j + 2));
+    if (j + 1 == BS || j + 1 == nsteps) mf_fold<HC, NT>(acc, res, j + 1 > BS);
+    if (j + 1 < nsteps) {
+      mf_compute<FMT, HC, NT>(acc, s1, sh);
+      if (j + 3 < nsteps) mf_load(s1, ad, ic, first_block(j + 3));
+      if (j + 2 == BS || j + 2 == nsteps) mf_fold<HC, NT>(acc, res, j + 2 > BS);
     }
   }
 }
@@ -364,46 +446,31 @@ __device__ __forceinline__ void mf_accumulate(float (&acc)[NT][H][4], const uint
 template <int FMT, int H>
 __device__ void mf_tile(const TileArgs& ta, int R, float* red, int parity) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
-  constexpr int NT = H >= 4 ? 1 : 4 / H;
+  constexpr int NT = mf_tiles_per_wave(H);
   const PartPlan& pl = ta.pl;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
   const int g = wave >> pl.lgS, s = wave & (pl.S - 1);
   const int i = lane & 15, q = lane >> 4;
   const int64_t ntiles = np_of(ta.n) / TILE;
   const int64_t wrow0 = ta.row0 + (int64_t)g * TILE * NT;  // first row of this wave's tiles
-  const uint8_t* abase[NT];
-  const uint16_t* sbase[NT];
+  MfAddr<NT> ad;
 #pragma unroll
   for (int t = 0; t < NT; t++) {
-    const int64_t it0 = wrow0 / TILE + t;
-    const int64_t it = it0 < ntiles ? it0 : ntiles - 1;
-    abase[t] = ta.code + ((size_t)it * ta.kbp) * CB +
-               (FMT == FMT_Q8 ? (q >> 1) * 256 + i * 16 + (q & 1) * 8 : i * 16 + (q & 1) * 8);
-    sbase[t] = ta.scale + ((size_t)it * ta.kbp) * TILE + 4 * q;
+    const int64_t it0 = (wrow0 >> 4) + t;
+    const int64_t it = it0 < ntiles ? it0 : ntiles - 1;  // past the last tile: reread it, store nothing
+    ad.code[t] = ta.code + ((size_t)it * ta.kbp) * CB;
+    ad.scale[t] = ta.scale + ((size_t)it * ta.kbp) * TILE;
   }
-  float acc[NT][H][4];
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int h = 0; h < H; h++)
-#pragma unroll
-      for (int v = 0; v < 4; v++) acc[t][h][v] = 0.0f;
-  mf_accumulate<FMT, H, NT>(acc, abase, sbase, ta.prep, R, pl, s, i, q);
-  // lane parts by the pairwise tree ((h0 + h1) + (h2 + h3)) + ...
+  ad.aoff = FMT == FMT_Q8 ? (q >> 1) * 256 + i * 16 + (q & 1) * 8 : i * 16 + (q & 1) * 8;
+  ad.soff = 4 * q;
+  // rows prepared in fragment order: codes [kbp][4][R][8], dx and nsx [kbp][R]
+  ad.xc = ta.prep.codes;
+  ad.xd = ta.prep.dx;
+  ad.xn = ta.prep.nsx;
+  ad.xoff = (uint32_t)((q * R + (i < R ? i : R - 1)) * 8);
+  ad.R = R;
   float res[NT][4];
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      float a[H];
-#pragma unroll
-      for (int h = 0; h < H; h++) a[h] = acc[t][h][v];
-#pragma unroll
-      for (int st = 1; st < H; st *= 2)
-#pragma unroll
-        for (int h = 0; h + st < H; h += 2 * st) a[h] = a[h] + a[h + st];
-      res[t][v] = a[0];
-    }
+  mf_accumulate<FMT, H, NT>(res, ad, pl, s, i, q);
   if (pl.S > 1) {
     float* rb = red + parity * (WAVES * WAVE * 4 * NT);
 #pragma unroll
@@ -506,7 +573,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void rl
 }
 
 template <int FMT>
-__global__ __launch_bounds__(WG) void mf_set_kernel(SetArgs a, int R) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q8 ? 4 : 3))) void mf_set_kernel(SetArgs a, int R) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
@@ -700,7 +767,7 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
 template <int FMT>
 static void launch_mf(const SetArgs& a, int rows, hipStream_t s) {
   auto kern = mf_set_kernel<FMT>;
-  const size_t lds = 2 * WAVES * WAVE * 4 * 4 * 4;  // combine area: two parities, up to 4 tiles per wave
+  const size_t lds = 2 * WAVES * WAVE * 4 * mf_tiles_per_wave(1) * 4;  // combine area: two parities
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, rows);
 }
 
