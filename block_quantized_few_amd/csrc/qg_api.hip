@@ -72,7 +72,7 @@ int qgemv_fmt(int fmt, const void* w_image, int64_t n, int64_t k, const float* x
   ProjArg pa{w_image, n, k, ws, nullptr, y};
   if (fuses_quantization(rows)) {
     pa.x = x;
-  } else if (int st = launch_prepare(x, rows, k, ws, prep_in_fragment_order(rows), s)) {
+  } else if (int st = launch_prepare(x, rows, k, ws, prep_layout(rows, k), s)) {
     return st;
   }
   if (int st = launch_qgemv_set(fmt, &pa, 1, rows, s)) return st;
@@ -98,7 +98,7 @@ int qg_prepare_rows(const float* x, int rows, int64_t k, void* ws, size_t ws_byt
   if (int st = check_x(x, rows, k, QG_MAX_PREP_ROWS)) return st;
   if (int st = check_ws(ws, ws_bytes, prep_layout(rows, k).total, "the activation rows")) return st;
   if (int st = check_device()) return st;
-  if (int st = launch_prepare(x, rows, k, ws, prep_in_fragment_order(rows), (hipStream_t)stream)) return st;
+  if (int st = launch_prepare(x, rows, k, ws, prep_layout(rows, k), (hipStream_t)stream)) return st;
   return ok();
 }
 
@@ -228,7 +228,7 @@ int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64
   if (int st = check_device()) return st;
   hipStream_t s = (hipStream_t)stream;
   const GroupedLayout G = grouped_layout(x_rows, k, m);
-  if (int st = launch_prepare(x, x_rows, k, (uint8_t*)ws + G.prep, false, s)) return st;
+  if (int st = launch_prepare(x, x_rows, k, (uint8_t*)ws + G.prep, prep_layout_rows(x_rows, k), s)) return st;
   if (int st = launch_grouped(w_images, n_experts, n, k, x_rows, expert, x_index, m, y, ws, s)) return st;
   return ok();
 }

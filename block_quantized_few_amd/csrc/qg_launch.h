@@ -16,13 +16,10 @@ struct Prep {
   const float* dx;
   const int* nsx;
 };
-Prep prep_view(const void* ws, int64_t rows, int64_t k);
+Prep prep_view(const void* ws, const PrepLayout& L);
 
-// A1: quantize rows x [rows][k] into a workspace (`ws` layout of qg_layout.h),
-// in row order or (frag) in the MFMA fragment order.
-int launch_prepare(const float* x, int rows, int64_t k, void* ws, bool frag, hipStream_t s);
-// Whether a GEMV of `rows` rows reads its prepared rows in fragment order.
-bool prep_in_fragment_order(int rows);
+// A1: quantize rows x [rows][k] into a workspace in the order L (qg_layout.h).
+int launch_prepare(const float* x, int rows, int64_t k, void* ws, const PrepLayout& L, hipStream_t s);
 // A1 for up to QG_MAX_SET activation sets (same row count) in one launch.
 int launch_prepare_set(const qg_act* acts, int count, int rows, hipStream_t s);
 // A1 in the plain layout with code sums (test hook).

@@ -20,12 +20,19 @@
 // per weight.
 //
 // Prepared activation rows (workspace of `rows` rows of length k), each plane
-// on a 256-byte boundary, pad blocks zero:
-//   codes int8 [rows][kbp*32] in element order;
-//   dx    fp32 [rows][kbp] block scales;
-//   nsx   int32 [rows][kbp] = -8 * (sum of the block's codes), the start value
-//         of a Q4_0 block dot (sum (c-8) q = sum c q - 8 sum q).
-//
+// on a 256-byte boundary, pad blocks zero, in one of two orders:
+//   row order (1..2 rows, and the grouped path):
+//     codes int8 [rows][kbp*32] in element order;
+//     dx    fp32 [rows][kbp] block scales;
+//     nsx   int32 [rows][kbp] = -8 * (sum of the block's codes), the start
+//           value of a Q4_0 block dot (sum (c-8) q = sum c q - 8 sum q).
+//   pair order (3..16 rows; the operand order of the K=64 int8 MFMA): blocks
+//     in pairs p = (2p, 2p+1), rows in groups g of eight (G = ceil(rows/8)
+//     groups; rows past `rows` are zero).  Chunk (p, g) is 1 KB of codes: 64
+//     lanes x 16 bytes, lane l = 16*q + i (i < 16, q < 4) holding, when
+//     (i < 8) == (q < 2), codes 16*(q%2) .. 16*(q%2)+15 of row 8g + i%8 of
+//     block 2p + i/8, and zeros otherwise; then dx and nsx [p][g][16] for
+//     (row 8g + i%8, block 2p + i/8) at index i.
 // Partition of a row's kbp blocks (depends on kbp only, never on the number of
 // activation rows, so a row's fp32 result is the same in every launch): P parts
 // (a power of two up to 32, about 8 blocks each) of BS = kbp/P blocks, grouped
@@ -76,15 +83,35 @@ QG_HD size_t scale_index(int64_t o, int64_t b, int64_t kbp) {
 
 struct PrepLayout {
   size_t codes, dx, nsx, total;
+  bool pairs;  // pair order
+  int groups;  // row groups of eight (pair order)
 };
-QG_HD PrepLayout prep_layout(int64_t rows, int64_t k) {
+QG_HD bool prep_pairs(int64_t rows) { return rows >= 3 && rows <= 16; }
+QG_HD PrepLayout prep_layout_rows(int64_t rows, int64_t k) {
   PrepLayout L;
   const int64_t kbp = kbp_of(k);
   L.codes = 0;
   L.dx = align256((size_t)rows * (size_t)kbp * 32);
   L.nsx = L.dx + align256((size_t)rows * (size_t)kbp * 4);
   L.total = L.nsx + align256((size_t)rows * (size_t)kbp * 4);
+  L.pairs = false;
+  L.groups = 0;
   return L;
+}
+QG_HD PrepLayout prep_layout_pairs(int64_t rows, int64_t k) {
+  PrepLayout L;
+  const size_t chunks = (size_t)(kbp_of(k) / 2) * (size_t)((rows + 7) / 8);
+  L.codes = 0;
+  L.dx = align256(chunks * 1024);
+  L.nsx = L.dx + align256(chunks * 64);
+  L.total = L.nsx + align256(chunks * 64);
+  L.pairs = true;
+  L.groups = (int)((rows + 7) / 8);
+  return L;
+}
+// The order a GEMV of `rows` rows reads.
+QG_HD PrepLayout prep_layout(int64_t rows, int64_t k) {
+  return prep_pairs(rows) ? prep_layout_pairs(rows, k) : prep_layout_rows(rows, k);
 }
 
 // Workspace of a grouped call: header, sorted assignment list, work items,
@@ -98,7 +125,7 @@ QG_HD GroupedLayout grouped_layout(int64_t x_rows, int64_t k, int64_t m) {
   G.sorted = 256;
   G.items = G.sorted + align256((size_t)(m > 0 ? m : 1) * 4);
   G.prep = G.items + align256((size_t)(m > 0 ? m : 1) * 12);
-  G.total = G.prep + prep_layout(x_rows, k).total;
+  G.total = G.prep + prep_layout_rows(x_rows, k).total;
   return G;
 }
 

@@ -10,13 +10,14 @@
 // Two kernels share one weight layout (16-row tiles, block-major; see
 // qg_layout.h) and one partition of each row's blocks, so they produce the
 // same bits for a row:
-//   * RL ("lanes own rows", 1..8 rows and the grouped path): a lane owns one
+//   * RL ("lanes own rows", 1..2 rows and the grouped path): a lane owns one
 //     weight row and streams its blocks with 16-byte loads; the integer dot of
 //     each block is exact inside the lane (v_dot4_i32_i8); activation blocks
-//     are read from LDS by the whole lane group at once (broadcast).
-//   * MF (9..16 rows): a wave owns 16 weight rows; one v_mfma_i32_16x16x32_i8
-//     per block gives the exact block dots of 16 weight rows x 16 activation
-//     rows, which the lanes then scale and accumulate in fp32.
+//     are read from LDS by the whole lane group at once (broadcast).  At 1..2
+//     rows the launch quantizes its fp32 rows itself.
+//   * MP ("pairs", 3..16 rows): one v_mfma_i32_16x16x64_i8 gives the exact
+//     dots of two blocks of 16 weight rows against 8 activation rows (two for
+//     16 rows); the lanes then scale and accumulate in fp32.
 // Both accumulate, per row and activation row, acc = fma(isum, dw * dx, acc)
 // over the blocks of each part in the partition's order, then add lane parts
 // by a fixed tree and wave parts left to right.
@@ -304,156 +305,128 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
   return full;
 }
 
-// ------------------------------------------------------------- MF tile ---
+// ------------------------------------------------------------- MP tile ---
+//
+// "Pair" kernel for 3..16 rows: one v_mfma_i32_16x16x64_i8 takes two weight
+// blocks (b, b+1) of 16 rows against 8 activation rows.  A lane (i, q) feeds
+// the weights of row i: half q%2 of block b + q/2 (for a Q8_0 cell that is 16
+// contiguous bytes, so the wave reads the two cells, 1 KB, at once).  The
+// prepared activation chunk puts row j's codes of block b in the columns
+// j < 8 and of block b+1 in the columns 8 + j, with zeros where the other
+// block's weights would meet them, so column j holds the exact int32 dot of
+// block b and column 8 + j that of block b+1.
+//
+// With H >= 2 lane parts, blocks b and b+1 at the same u are lane parts h and
+// h+1 (h even): columns j and 8 + j accumulate the two lane parts, and the
+// first level of the lane-part tree adds lanes i and i^8.  With H == 1 they
+// are u and u+1 of the one lane part: lane i adds its own block, then its
+// partner's, in that order.
 
-// NT 16-row image tiles per wave, so that a wave keeps several independent
-// MFMA accumulations in flight and reuses each activation fragment NT times.
-__host__ __device__ constexpr int mf_tiles_per_wave(int H) { return H >= 4 ? 1 : 2; }
+// Split of a tile's work over waves (H >= 2 means S == 4): W2 waves share a
+// wave part, each taking PPW lane-part pairs, and NT 16-row image tiles (one
+// with two row groups, whose activation fragments then take the registers).
+// About 16-32 KB of weights per wave whatever k is.
+__host__ __device__ constexpr int mp_w2(int H) { return H >= 4 ? 2 : 1; }
+__host__ __device__ constexpr int mp_nt(int H, int G) { return H == 8 || G == 2 ? 1 : 2; }
+constexpr int MP_NT_MAX = 2;
 
-// One step of an MF wave: HC lane parts of one u for NT image tiles (two or
-// four MFMAs); the wave keeps two steps in flight.
-template <int FMT, int HC, int NT>
-struct MfStep {
-  uint2 a[NT][HC];  // A fragments: 8 codes of row i (Q4_0: 16 nibbles)
-  uint2 w[NT][HC];  // fp16 scales of rows 4q .. 4q+3
-  long x[HC];       // B fragments: 8 codes of activation row i
-  float dx[HC];
-  int ns[HC];       // Q4_0 start value -8 * sum(q_x)
+__device__ __forceinline__ float lane_xor8(float v) {
+  // DPP row_ror:8 within each row of 16 lanes: lane i reads lane i ^ 8
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+// One step: one block pair for NT tiles and G row groups.
+template <int NT, int G>
+struct MpStep {
+  uint4 a[NT];  // weight codes (16 bytes)
+  uint2 w[NT];  // fp16 scales of rows 4q .. 4q+3 of the lane's block
+  uint4 x[G];   // activation chunk (16 bytes)
+  float dx[G];
+  int ns[G];
 };
 
-// Where an MF wave reads: per image tile a base shared by the wave plus a lane
-// offset, so every load takes the scalar-base form and the addresses cost no
-// vector registers.
 template <int NT>
-struct MfAddr {
-  const uint8_t* code[NT];    // tile's code plane (wave-uniform)
-  const uint16_t* scale[NT];  // tile's scales (wave-uniform)
-  uint32_t aoff;              // lane's A-fragment byte offset in a cell
-  uint32_t soff;              // lane's first scale (fp16 units) in a cell
-  const int8_t* xc;           // prepared codes, fragment order (uniform)
+struct MpAddr {
+  const uint8_t* code[NT];    // tile code planes (wave-uniform)
+  const uint16_t* scale[NT];  // tile scales (wave-uniform)
+  uint32_t aoff, soff;        // lane offsets: bytes in a cell pair, fp16 units in a scale pair
+  const uint8_t* xc;          // pair-order chunks (uniform)
   const float* xd;
   const int* xn;
-  uint32_t xoff;  // lane's B-fragment byte offset in a block's fragments
-  int R;
+  int groups;  // row groups in the workspace
 };
 
-template <int FMT, int HC, int NT>
-__device__ __forceinline__ void mf_load(MfStep<FMT, HC, NT>& st, const MfAddr<NT>& ad, int i, int b0) {
+template <int FMT, int NT, int G>
+__device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad, int lane, int b) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
 #pragma unroll
-  for (int hh = 0; hh < HC; hh++) {
-    const size_t b = (size_t)(b0 + hh);
+  for (int t = 0; t < NT; t++) {
+    st.a[t] = ld16_stream(ad.code[t] + (size_t)b * CB + ad.aoff);
+    st.w[t] = ld8_stream(ad.scale[t] + (size_t)b * TILE + ad.soff);
+  }
+  const size_t chunk0 = (size_t)(b >> 1) * ad.groups;
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
-      st.a[t][hh] = ld8_stream(ad.code[t] + b * CB + ad.aoff);
-      st.w[t][hh] = ld8_stream(ad.scale[t] + b * TILE + ad.soff);
-    }
-    // lanes past the R rows read row R-1 again: their MFMA columns are never stored
-    st.x[hh] = *reinterpret_cast<const long*>(ad.xc + b * 32 * ad.R + ad.xoff);
-    st.dx[hh] = ad.xd[b * ad.R + i];
-    st.ns[hh] = FMT == FMT_Q4 ? ad.xn[b * ad.R + i] : 0;
+  for (int g = 0; g < G; g++) {
+    st.x[g] = ld16(ad.xc + ((chunk0 + g) * 64 + lane) * 16);
+    st.dx[g] = ad.xd[(chunk0 + g) * 16 + (lane & 15)];
+    st.ns[g] = FMT == FMT_Q4 ? ad.xn[(chunk0 + g) * 16 + (lane & 15)] : 0;
   }
 }
 
-template <int FMT, int HC, int NT>
-__device__ __forceinline__ void mf_compute(float (&acc)[NT][HC][4], const MfStep<FMT, HC, NT>& st, int sh) {
+template <int FMT, int NT, int G, int PP, bool SEQ>
+__device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, const MpStep<NT, G>& st, int sh) {
 #pragma unroll
-  for (int hh = 0; hh < HC; hh++)
+  for (int t = 0; t < NT; t++) {
+    uint4 av = st.a[t];
+    if (FMT == FMT_Q4) {
+      av.x = (av.x >> sh) & 0x0F0F0F0Fu;
+      av.y = (av.y >> sh) & 0x0F0F0F0Fu;
+      av.z = (av.z >> sh) & 0x0F0F0F0Fu;
+      av.w = (av.w >> sh) & 0x0F0F0F0Fu;
+    }
+    const v4i a = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+    const uint2 wv = st.w[t];
+    const float dw[4] = {h2f((uint16_t)(wv.x & 0xffff)), h2f((uint16_t)(wv.x >> 16)), h2f((uint16_t)(wv.y & 0xffff)),
+                         h2f((uint16_t)(wv.y >> 16))};
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
-      uint2 av = st.a[t][hh];
-      if (FMT == FMT_Q4) {
-        av.x = (av.x >> sh) & 0x0F0F0F0Fu;
-        av.y = (av.y >> sh) & 0x0F0F0F0Fu;
-      }
-      long a;
-      __builtin_memcpy(&a, &av, 8);
-      const int ns = st.ns[hh];
+    for (int g = 0; g < G; g++) {
+      const v4i bx = {(int)st.x[g].x, (int)st.x[g].y, (int)st.x[g].z, (int)st.x[g].w};
+      const int ns = st.ns[g];
       v4i c = {ns, ns, ns, ns};
-      c = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, st.x[hh], c, 0, 0, 0);
-      const uint2 wv = st.w[t][hh];
-      const float dw[4] = {h2f((uint16_t)(wv.x & 0xffff)), h2f((uint16_t)(wv.x >> 16)),
-                           h2f((uint16_t)(wv.y & 0xffff)), h2f((uint16_t)(wv.y >> 16))};
+      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx, c, 0, 0, 0);
 #pragma unroll
-      for (int v = 0; v < 4; v++) acc[t][hh][v] = __builtin_fmaf((float)c[v], dw[v] * st.dx[hh], acc[t][hh][v]);
-    }
-}
-
-// After the last step of a half: add its HC lane parts by the pairwise tree
-// into `res` (second half: res = first + second, the tree's top node), and
-// clear the accumulators.
-template <int HC, int NT>
-__device__ __forceinline__ void mf_fold(float (&acc)[NT][HC][4], float (&res)[NT][4], bool second) {
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      float a[HC];
-#pragma unroll
-      for (int h = 0; h < HC; h++) a[h] = acc[t][h][v];
-#pragma unroll
-      for (int st = 1; st < HC; st *= 2)
-#pragma unroll
-        for (int h = 0; h + st < HC; h += 2 * st) a[h] = a[h] + a[h + st];
-      res[t][v] = second ? res[t][v] + a[0] : a[0];
-#pragma unroll
-      for (int h = 0; h < HC; h++) acc[t][h][v] = 0.0f;
-    }
-}
-
-// The wave's part of the partition, as NH = H/HC halves of HC lane parts: for
-// each half, u = 0 .. BS-1, one step (HC lane parts x NT tiles) per u.  Each lane part accumulates its blocks in u order; the halves are the two
-// subtrees of the lane-part tree.  Two steps are in flight.
-template <int FMT, int H, int NT>
-__device__ __forceinline__ void mf_accumulate(float (&res)[NT][4], const MfAddr<NT>& ad, const PartPlan& pl, int s,
-                                              int i, int q) {
-  constexpr int HC = H >= 4 ? 4 : H;
-  constexpr int NH = H / HC;  // 1, or 2 for H == 8
-  const int ic = i < ad.R ? i : ad.R - 1;  // activation row this lane reads
-  const int sh = (q >> 1) * 4;
-  const int BS = pl.BS;
-  const int bs0 = s * H * BS;
-  const int nsteps = BS * NH;  // >= 8
-  auto first_block = [&](int j) {
-    const int half = (NH == 2 && j >= BS) ? 1 : 0;
-    return bs0 + H * (j - half * BS) + half * HC;
-  };
-  float acc[NT][HC][4];
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int h = 0; h < HC; h++)
-#pragma unroll
-      for (int v = 0; v < 4; v++) acc[t][h][v] = 0.0f;
-  MfStep<FMT, HC, NT> s0, s1;
-  mf_load(s0, ad, ic, first_block(0));
-  mf_load(s1, ad, ic, first_block(1));
-  for (int j = 0; j < nsteps; j += 2) {
-    mf_compute<FMT, HC, NT>(acc, s0, sh);
-    if (j + 2 < nsteps) mf_load(s0, ad, ic, first_block(j + 2));
-    if (j + 1 == BS || j + 1 == nsteps) mf_fold<HC, NT>(acc, res, j + 1 > BS);
-    if (j + 1 < nsteps) {
-      mf_compute<FMT, HC, NT>(acc, s1, sh);
-      if (j + 3 < nsteps) mf_load(s1, ad, ic, first_block(j + 3));
-      if (j + 2 == BS || j + 2 == nsteps) mf_fold<HC, NT>(acc, res, j + 2 > BS);
+      for (int v = 0; v < 4; v++) {
+        const float f = (float)c[v], m = dw[v] * st.dx[g];
+        float& r = acc[t][PP == 1 ? 0 : pp][g][v];
+        if (SEQ) {
+          // block b (this lane), then block b+1 (lane i ^ 8)
+          const float pf = lane_xor8(f), pm = lane_xor8(m);
+          r = __builtin_fmaf(f, m, r);
+          r = __builtin_fmaf(pf, pm, r);
+        } else {
+          r = __builtin_fmaf(f, m, r);
+        }
+      }
     }
   }
 }
 
-// One MF tile: 16-row image tiles, NT per wave, (4/S) waves' worth per tile;
-// the R activation rows are the MFMA's 16 columns (the rest zero), read from
-// the workspace in fragment order.
-template <int FMT, int H>
-__device__ void mf_tile(const TileArgs& ta, int R, float* red, int parity) {
+// One MP tile: groups of S*W2 waves, each group NT 16-row image tiles; G
+// groups of eight activation rows from the pair-order workspace.
+template <int FMT, int H, int G>
+__device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
-  constexpr int NT = mf_tiles_per_wave(H);
+  constexpr bool SEQ = H == 1;
+  constexpr int W2 = mp_w2(H), NT = mp_nt(H, G);
+  constexpr int PPW = SEQ ? 1 : H / 2 / W2;  // lane-part pairs per wave (1 or 2)
   const PartPlan& pl = ta.pl;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
-  const int g = wave >> pl.lgS, s = wave & (pl.S - 1);
+  const int gw = pl.S * W2;  // waves per group
+  const int g = wave / gw, wg = wave - g * gw, s = wg / W2, hw = wg - s * W2;
   const int i = lane & 15, q = lane >> 4;
   const int64_t ntiles = np_of(ta.n) / TILE;
-  const int64_t wrow0 = ta.row0 + (int64_t)g * TILE * NT;  // first row of this wave's tiles
-  MfAddr<NT> ad;
+  const int64_t wrow0 = ta.row0 + (int64_t)g * TILE * NT;  // first row of this group's tiles
+  MpAddr<NT> ad;
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     const int64_t it0 = (wrow0 >> 4) + t;
@@ -461,41 +434,101 @@ __device__ void mf_tile(const TileArgs& ta, int R, float* red, int parity) {
     ad.code[t] = ta.code + ((size_t)it * ta.kbp) * CB;
     ad.scale[t] = ta.scale + ((size_t)it * ta.kbp) * TILE;
   }
-  ad.aoff = FMT == FMT_Q8 ? (q >> 1) * 256 + i * 16 + (q & 1) * 8 : i * 16 + (q & 1) * 8;
-  ad.soff = 4 * q;
-  // rows prepared in fragment order: codes [kbp][4][R][8], dx and nsx [kbp][R]
-  ad.xc = ta.prep.codes;
+  ad.aoff = FMT == FMT_Q8 ? (uint32_t)(q * 256 + i * 16) : (uint32_t)((q >> 1) * 256 + i * 16);
+  ad.soff = (uint32_t)((i >> 3) * 16 + 4 * q);
+  ad.xc = reinterpret_cast<const uint8_t*>(ta.prep.codes);
   ad.xd = ta.prep.dx;
   ad.xn = ta.prep.nsx;
-  ad.xoff = (uint32_t)((q * R + (i < R ? i : R - 1)) * 8);
-  ad.R = R;
-  float res[NT][4];
-  mf_accumulate<FMT, H, NT>(res, ad, pl, s, i, q);
-  if (pl.S > 1) {
-    float* rb = red + parity * (WAVES * WAVE * 4 * NT);
+  ad.groups = (R + 7) >> 3;
+  const int sh = (q & 1) * 4;
+
+  const int BS = pl.BS;
+  const int nsteps = SEQ ? BS / 2 : BS * PPW;  // >= 4 (BS >= 8, even when H == 1)
+  const int bs0 = s * H * BS + 2 * hw * PPW;
+  // first block of step j
+  auto blk = [&](int j) {
+    if (SEQ) return bs0 + 2 * j;
+    const int u = PPW == 2 ? j >> 1 : j, pp = PPW == 2 ? j & 1 : 0;
+    return bs0 + H * u + 2 * pp;
+  };
+  float acc[NT][PPW][G][4];
 #pragma unroll
-    for (int t = 0; t < NT; t++)
+  for (int t = 0; t < NT; t++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) rb[((wave * NT + t) * WAVE + lane) * 4 + v] = res[t][v];
-    __syncthreads();
-    if (s != 0) return;
+    for (int p = 0; p < PPW; p++)
 #pragma unroll
-    for (int t = 0; t < NT; t++)
+      for (int gg = 0; gg < G; gg++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        float x = rb[(((g * pl.S) * NT + t) * WAVE + lane) * 4 + v];
-        for (int s2 = 1; s2 < pl.S; s2++) x += rb[(((g * pl.S + s2) * NT + t) * WAVE + lane) * 4 + v];
-        res[t][v] = x;
-      }
+        for (int v = 0; v < 4; v++) acc[t][p][gg][v] = 0.0f;
+  MpStep<NT, G> s0, s1;
+  mp_load<FMT, NT, G>(s0, ad, lane, blk(0));
+  mp_load<FMT, NT, G>(s1, ad, lane, blk(1));
+  for (int j = 0; j < nsteps; j += 2) {
+    mp_compute<FMT, NT, G, PPW, SEQ>(acc, 0, s0, sh);
+    if (j + 2 < nsteps) mp_load<FMT, NT, G>(s0, ad, lane, blk(j + 2));
+    if (j + 1 < nsteps) {
+      mp_compute<FMT, NT, G, PPW, SEQ>(acc, 1, s1, sh);
+      if (j + 3 < nsteps) mp_load<FMT, NT, G>(s1, ad, lane, blk(j + 3));
+    }
   }
-  if (i < R) {
+  // the wave's pairs by the lane-part tree: (h + h^1) across lanes i, i^8, then pair + pair
+  float res[NT][G][4];
+#pragma unroll
+  for (int t = 0; t < NT; t++)
+#pragma unroll
+    for (int gg = 0; gg < G; gg++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        float val = acc[t][0][gg][v];
+        if (!SEQ) {
+          val = val + lane_xor8(val);
+          if (PPW == 2) val = val + (acc[t][PPW - 1][gg][v] + lane_xor8(acc[t][PPW - 1][gg][v]));
+        }
+        res[t][gg][v] = val;
+      }
+  // then the W2 pair groups of a wave part (the tree's upper level), then wave parts left to right
+  if (gw > 1) {
+    constexpr int NV = NT * G * 4;
+    float* rb = red + parity * (WAVES * WAVE * MP_NT_MAX * 2 * 4);
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int64_t row = wrow0 + t * TILE + 4 * q + v;
-        if (row < ta.n) ta.y[(int64_t)ta.s_dst[i] * ta.ldy + row] = res[t][v];
+      for (int gg = 0; gg < G; gg++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) rb[(wave * NV + (t * G + gg) * 4 + v) * WAVE + lane] = res[t][gg][v];
+    __syncthreads();
+    if (wg != 0) return;
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+      for (int gg = 0; gg < G; gg++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const int o = ((t * G + gg) * 4 + v) * WAVE + lane;
+          const int w0 = g * gw;
+          float x = 0.0f;
+          for (int s2 = 0; s2 < pl.S; s2++) {
+            float part = rb[(w0 + s2 * W2) * NV * WAVE + o];
+            if (W2 == 2) part = part + rb[(w0 + s2 * W2 + 1) * NV * WAVE + o];
+            x = s2 == 0 ? part : x + part;
+          }
+          res[t][gg][v] = x;
+        }
+  }
+  if (i < 8) {
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+      const int ar = gg * 8 + i;  // activation row of this lane's column
+      if (ar < R) {
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            const int64_t row = wrow0 + t * TILE + 4 * q + v;
+            if (row < ta.n) ta.y[(int64_t)ta.s_dst[ar] * ta.ldy + row] = res[t][gg][v];
+          }
       }
+    }
   }
 }
 
@@ -572,8 +605,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void rl
   }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q8 ? 4 : 3))) void mf_set_kernel(SetArgs a, int R) {
+template <int FMT, int G>
+__global__ __launch_bounds__(WG) void mp_set_kernel(SetArgs a, int R) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
@@ -585,10 +618,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, 0);
     const PartPlan& pl = d.pl;
-    if (pl.H == 1) mf_tile<FMT, 1>(ta, R, red, parity);
-    else if (pl.H == 2) mf_tile<FMT, 2>(ta, R, red, parity);
-    else if (pl.H == 4) mf_tile<FMT, 4>(ta, R, red, parity);
-    else mf_tile<FMT, 8>(ta, R, red, parity);
+    if (pl.H == 1) mp_tile<FMT, 1, G>(ta, R, red, parity);
+    else if (pl.H == 2) mp_tile<FMT, 2, G>(ta, R, red, parity);
+    else if (pl.H == 4) mp_tile<FMT, 4, G>(ta, R, red, parity);
+    else mp_tile<FMT, 8, G>(ta, R, red, parity);
     if (pl.S > 1) parity ^= 1;
   }
 }
@@ -764,10 +797,10 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
   }
 }
 
-template <int FMT>
-static void launch_mf(const SetArgs& a, int rows, hipStream_t s) {
-  auto kern = mf_set_kernel<FMT>;
-  const size_t lds = 2 * WAVES * WAVE * 4 * mf_tiles_per_wave(1) * 4;  // combine area: two parities
+template <int FMT, int G>
+static void launch_mp(const SetArgs& a, int rows, hipStream_t s) {
+  auto kern = mp_set_kernel<FMT, G>;
+  const size_t lds = 2 * WAVES * WAVE * MP_NT_MAX * 2 * 4 * 4;  // combine area: two parities
   hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, rows);
 }
 
@@ -775,7 +808,7 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
   SetArgs a;
   memset(&a, 0, sizeof a);
   a.count = count;
-  const bool mf = prep_in_fragment_order(rows);
+  const bool mf = prep_pairs(rows);  // 3..16 rows: the pair kernel
   // Tiles of projections with longer rows come first: their workgroups stage
   // the most activation blocks, so they get the earliest start.  The order
   // changes no result (each projection has its own output).
@@ -796,7 +829,7 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
     const uint8_t* img = (const uint8_t*)pa.image;
     d.code = img;
     d.scale = (const uint16_t*)(img + image_scale_offset(fmt, pa.n, pa.k));
-    d.prep = pa.ws ? prep_view(pa.ws, rows, pa.k) : Prep{nullptr, nullptr, nullptr};
+    d.prep = pa.ws ? prep_view(pa.ws, prep_layout(rows, pa.k)) : Prep{nullptr, nullptr, nullptr};
     d.xf = pa.x;
     d.y = pa.y;
     d.n = pa.n;
@@ -805,7 +838,7 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
     d.kbp = (int)kbp_of(pa.k);
     const PartPlan pl = part_plan(d.kbp);
     d.pl = pl;
-    d.rows_per_tile = mf ? (WAVES / pl.S) * TILE * mf_tiles_per_wave(pl.H) : WG / pl.P;
+    d.rows_per_tile = mf ? (WAVES / (pl.S * mp_w2(pl.H))) * TILE * mp_nt(pl.H, rows > 8 ? 2 : 1) : WG / pl.P;
     d.tiles = (int)((pa.n + d.rows_per_tile - 1) / d.rows_per_tile);
     tiles += d.tiles;
     const size_t x = (size_t)rows * d.kbp * x_block_bytes(fmt);
@@ -818,13 +851,18 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
   const int lds_x = (int)((need < cap ? need : cap) + 15) / 16 * 16;
   for (int i = 0; i < count; i++) a.p[i].ucx = rl_round(lds_x, rows, a.p[i].pl, fmt);
   if (mf) {
-    if (fmt == FMT_Q8) launch_mf<FMT_Q8>(a, rows, s);
-    else launch_mf<FMT_Q4>(a, rows, s);
+    if (rows <= 8) {
+      if (fmt == FMT_Q8) launch_mp<FMT_Q8, 1>(a, rows, s);
+      else launch_mp<FMT_Q4, 1>(a, rows, s);
+    } else {
+      if (fmt == FMT_Q8) launch_mp<FMT_Q8, 2>(a, rows, s);
+      else launch_mp<FMT_Q4, 2>(a, rows, s);
+    }
   } else {
     if (fmt == FMT_Q8) launch_rl_rows<FMT_Q8>(a, rows, fused, lds_x, s);
     else launch_rl_rows<FMT_Q4>(a, rows, fused, lds_x, s);
   }
-  return hip_status(hipGetLastError(), mf ? "mf_set_kernel" : "rl_set_kernel");
+  return hip_status(hipGetLastError(), mf ? "mp_set_kernel" : "rl_set_kernel");
 }
 
 int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
@@ -849,7 +887,7 @@ int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, 
   const int64_t eb = (int64_t)image_total_bytes(QG_FMT_Q8_0, n, k);
   const size_t so = image_scale_offset(QG_FMT_Q8_0, n, k);
   hipLaunchKernelGGL(grouped_kernel, dim3(tiles, m), dim3(WG), lds, s, (const uint8_t*)images, eb, so, n, k, kbp, pl,
-                     prep_view(w + G.prep, x_rows, k), header, sorted, items, x_index, y, lds_x);
+                     prep_view(w + G.prep, prep_layout_rows(x_rows, k)), header, sorted, items, x_index, y, lds_x);
   return hip_status(hipGetLastError(), "grouped_kernel");
 }
 

@@ -9,8 +9,7 @@
 
 namespace qg {
 
-Prep prep_view(const void* ws, int64_t rows, int64_t k) {
-  const PrepLayout L = prep_layout(rows, k);
+Prep prep_view(const void* ws, const PrepLayout& L) {
   const uint8_t* w = (const uint8_t*)ws;
   return Prep{(const int8_t*)(w + L.codes), (const float*)(w + L.dx), (const int*)(w + L.nsx)};
 }
@@ -29,37 +28,48 @@ __device__ __forceinline__ void load_quarter(const float* __restrict__ x, int64_
   }
 }
 
-// Where quarter q of block b of row r lands in a workspace of `rows` rows:
-// row order (codes [rows][kbp][32], dx/nsx [rows][kbp]) or, for the MFMA
-// path's 9..16 rows, fragment order (codes [kbp][4][rows][8], dx/nsx
-// [kbp][rows]).
+// Where quarter q of block b of row r lands in a workspace (the orders of
+// qg_layout.h).  In pair order each quarter also clears the matching quarter
+// of its zero partner lane, so every chunk is fully written.
 struct PrepDst {
   int8_t* codes;
   float* dx;
   int* nsx;
-  int rows, kbp;
-  bool frag;
+  int rows;    // rows to quantize (pair order: padded to a multiple of 8)
+  int kbp;
+  int groups;  // 0: row order; else pair order with this many row groups
   __device__ __forceinline__ void put(int64_t r, int64_t b, int q, unsigned lo, unsigned hi, float d, int sum) const {
-    const int64_t ci = frag ? ((b * 4 + q) * rows + r) * 8 : (r * kbp + b) * 32 + q * 8;
-    *reinterpret_cast<uint2*>(codes + ci) = make_uint2(lo, hi);
+    if (groups) {
+      const int par = (int)(b & 1), i = (int)(r & 7) + 8 * par, half = q >> 1;
+      const int64_t chunk = (b >> 1) * groups + (r >> 3);
+      const int64_t lane = (half + 2 * par) * 16 + i, zlane = (half + 2 * (1 - par)) * 16 + i;
+      *reinterpret_cast<uint2*>(codes + (chunk * 64 + lane) * 16 + (q & 1) * 8) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(codes + (chunk * 64 + zlane) * 16 + (q & 1) * 8) = make_uint2(0u, 0u);
+      if (q == 0) {
+        dx[chunk * 16 + i] = d;
+        nsx[chunk * 16 + i] = -8 * sum;
+      }
+      return;
+    }
+    *reinterpret_cast<uint2*>(codes + (r * kbp + b) * 32 + q * 8) = make_uint2(lo, hi);
     if (q == 0) {
-      const int64_t si = frag ? b * rows + r : r * kbp + b;
-      dx[si] = d;
-      nsx[si] = -8 * sum;
+      dx[r * kbp + b] = d;
+      nsx[r * kbp + b] = -8 * sum;
     }
   }
 };
 
 // Four lanes per 32-block over kbp blocks per row; pad blocks come out all
 // zero (scale 0, codes 0).
-__global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ x, int64_t k, int kb, PrepDst dst) {
+__global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ x, int64_t k, int kb, int xrows,
+                                                      PrepDst dst) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t blk = t >> 2;
   const int q = (int)(t & 3);
   const bool active = blk < (int64_t)dst.rows * dst.kbp;  // whole quads are active or not
   const int64_t r = active ? blk / dst.kbp : 0, b = active ? blk % dst.kbp : 0;
   float v[8];
-  load_quarter(x, k, r, b, kb, q, active, v);
+  load_quarter(x, k, r, b, kb, q, active && r < xrows, v);  // pad rows quantize to zeros
   unsigned lo, hi;
   float d;
   int sum;
@@ -73,6 +83,7 @@ struct PrepSet {
   PrepDst dst[QG_MAX_SET];
   int64_t k[QG_MAX_SET];
   int count;
+  int xrows;
 };
 
 __global__ __launch_bounds__(256) void prepare_set_kernel(PrepSet s) {
@@ -86,7 +97,7 @@ __global__ __launch_bounds__(256) void prepare_set_kernel(PrepSet s) {
   const bool active = blk < (int64_t)dst.rows * dst.kbp;
   const int64_t r = active ? blk / dst.kbp : 0, b = active ? blk % dst.kbp : 0;
   float v[8];
-  load_quarter(s.x[p], k, r, b, kb, q, active, v);
+  load_quarter(s.x[p], k, r, b, kb, q, active && r < s.xrows, v);
   unsigned lo, hi;
   float d;
   int sum;
@@ -193,18 +204,16 @@ __global__ __launch_bounds__(256) void blockdots_kernel(const uint8_t* __restric
 
 static unsigned grid1(int64_t threads, int per) { return (unsigned)((threads + per - 1) / per); }
 
-bool prep_in_fragment_order(int rows) { return rows > 8 && rows <= QG_MAX_ROWS; }
-
-static PrepDst prep_dst(void* ws, int rows, int64_t k, bool frag) {
-  const PrepLayout L = prep_layout(rows, k);
+static PrepDst prep_dst(void* ws, const PrepLayout& L, int rows, int64_t k) {
   uint8_t* w = (uint8_t*)ws;
-  return PrepDst{(int8_t*)(w + L.codes), (float*)(w + L.dx), (int*)(w + L.nsx), rows, (int)kbp_of(k), frag};
+  return PrepDst{(int8_t*)(w + L.codes), (float*)(w + L.dx), (int*)(w + L.nsx), L.pairs ? L.groups * 8 : rows,
+                 (int)kbp_of(k), L.pairs ? L.groups : 0};
 }
 
-int launch_prepare(const float* x, int rows, int64_t k, void* ws, bool frag, hipStream_t s) {
-  const int kbp = (int)kbp_of(k);
-  hipLaunchKernelGGL(prepare_kernel, dim3(grid1((int64_t)rows * kbp * 4, 256)), dim3(256), 0, s, x, k, (int)kb_of(k),
-                     prep_dst(ws, rows, k, frag));
+int launch_prepare(const float* x, int rows, int64_t k, void* ws, const PrepLayout& L, hipStream_t s) {
+  const PrepDst dst = prep_dst(ws, L, rows, k);
+  hipLaunchKernelGGL(prepare_kernel, dim3(grid1((int64_t)dst.rows * dst.kbp * 4, 256)), dim3(256), 0, s, x, k,
+                     (int)kb_of(k), rows, dst);
   return hip_status(hipGetLastError(), "prepare_kernel");
 }
 
@@ -212,14 +221,16 @@ int launch_prepare_set(const qg_act* acts, int count, int rows, hipStream_t s) {
   PrepSet ps;
   memset(&ps, 0, sizeof ps);
   ps.count = count;
-  int64_t maxkbp = 0;
+  ps.xrows = rows;
+  int64_t maxblk = 0;
   for (int i = 0; i < count; i++) {
     ps.x[i] = acts[i].x;
     ps.k[i] = acts[i].k;
-    ps.dst[i] = prep_dst(acts[i].ws, rows, acts[i].k, prep_in_fragment_order(rows));
-    if (kbp_of(acts[i].k) > maxkbp) maxkbp = kbp_of(acts[i].k);
+    ps.dst[i] = prep_dst(acts[i].ws, prep_layout(rows, acts[i].k), rows, acts[i].k);
+    const int64_t blk = (int64_t)ps.dst[i].rows * ps.dst[i].kbp;
+    if (blk > maxblk) maxblk = blk;
   }
-  hipLaunchKernelGGL(prepare_set_kernel, dim3(grid1((int64_t)rows * maxkbp * 4, 256), count), dim3(256), 0, s, ps);
+  hipLaunchKernelGGL(prepare_set_kernel, dim3(grid1(maxblk * 4, 256), count), dim3(256), 0, s, ps);
   return hip_status(hipGetLastError(), "prepare_set_kernel");
 }
 

@@ -43,7 +43,13 @@ def test_sizes():
     assert q.image_bytes(q.Q8_0, 3, 96) >= 3 * 512 // 32 * 34
     assert q.workspace_bytes(0, 1024) == 0 and q.workspace_bytes(17, 1024) > 0
     assert q.workspace_bytes(1, 33) == 0
-    assert q.grouped_workspace_bytes(16, 2048, 136) > q.workspace_bytes(16, 2048)
+    # row order for 1-2 rows: codes + fp32 scales + int32 start values per block
+    assert q.workspace_bytes(2, 2048) == 2 * 2048 + 2 * 64 * 4 * 2
+    # pair order for 3-16 rows: per block pair and group of eight rows a 1 KB chunk + 16 scales + 16 start values
+    assert q.workspace_bytes(8, 2048) == 32 * 1 * (1024 + 64 + 64)
+    assert q.workspace_bytes(16, 2048) == 32 * 2 * (1024 + 64 + 64)
+    assert q.workspace_bytes(3, 2048) == q.workspace_bytes(8, 2048)
+    assert q.grouped_workspace_bytes(16, 2048, 136) > 16 * 2048 + 136 * 4
     assert q.grouped_workspace_bytes(16, 2048, q.MAX_ASSIGN + 1) == 0
 
 
