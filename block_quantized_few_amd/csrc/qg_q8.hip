@@ -90,7 +90,7 @@ __device__ void stage_rl(uint8_t* lds, const Prep& prep, const int* s_src, int k
 // Split in two so that a caller can issue its weight loads in between: the
 // memory counter a wave waits on retires loads in issue order, so activation
 // values loaded first can be quantized while the weight loads are in flight.
-constexpr int XQ_FIRST = 2;  // work items per thread whose loads are issued first
+constexpr int XQ_FIRST = 1;  // work items per thread whose loads are issued first
 
 struct XQuarter {
   float4 a, c;
@@ -586,7 +586,10 @@ __device__ __forceinline__ TileArgs tile_args(const ProjDev& d, int64_t row0, co
 // w + G, w + 2G, ... and keeps a projection's activation rows in LDS while its
 // tiles last.
 template <int FMT, int R, bool FUSED>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void rl_set_kernel(SetArgs a, int lds_x) {
+// (At most 80 registers -- 96 for two Q8_0 rows, which would spill -- so that
+// three 512-thread workgroups fit a CU and a layer's tiles are resident at
+// once.)
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q8 && R == 2 ? 5 : 6))) void rl_set_kernel(SetArgs a, int lds_x) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
@@ -785,16 +788,8 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
     else launch_rl<FMT, 2, true>(a, lds_x, s);
     return;
   }
-  switch (rows) {
-    case 1: launch_rl<FMT, 1, false>(a, lds_x, s); break;
-    case 2: launch_rl<FMT, 2, false>(a, lds_x, s); break;
-    case 3: launch_rl<FMT, 3, false>(a, lds_x, s); break;
-    case 4: launch_rl<FMT, 4, false>(a, lds_x, s); break;
-    case 5: launch_rl<FMT, 5, false>(a, lds_x, s); break;
-    case 6: launch_rl<FMT, 6, false>(a, lds_x, s); break;
-    case 7: launch_rl<FMT, 7, false>(a, lds_x, s); break;
-    default: launch_rl<FMT, 8, false>(a, lds_x, s); break;
-  }
+  if (rows == 1) launch_rl<FMT, 1, false>(a, lds_x, s);
+  else launch_rl<FMT, 2, false>(a, lds_x, s);
 }
 
 template <int FMT, int G>
