@@ -329,6 +329,7 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
 __host__ __device__ constexpr int mp_w2(int H) { return H >= 4 ? 2 : 1; }
 __host__ __device__ constexpr int mp_nt(int H, int G) { return H == 8 || G == 2 ? 1 : 2; }
 constexpr int MP_NT_MAX = 2;
+constexpr int MP_NV_MAX = 8;  // floats per lane a wave passes to the combine (NT * G * 4)
 
 __device__ __forceinline__ float lane_xor8(float v) {
   // DPP row_ror:8 within each row of 16 lanes: lane i reads lane i ^ 8
@@ -339,31 +340,32 @@ __device__ __forceinline__ float lane_xor8(float v) {
 template <int NT, int G>
 struct MpStep {
   uint4 a[NT];  // weight codes (16 bytes)
-  uint2 w[NT];  // fp16 scales of rows 4q .. 4q+3 of the lane's block
   uint4 x[G];   // activation chunk (16 bytes)
   float dx[G];
   int ns[G];
+  uint2 w[NT];  // fp16 scales of rows 4q .. 4q+3 of the lane's block (from the staged copy)
+  int b;        // first block of the pair
 };
 
 template <int NT>
 struct MpAddr {
-  const uint8_t* code[NT];    // tile code planes (wave-uniform)
-  const uint16_t* scale[NT];  // tile scales (wave-uniform)
-  uint32_t aoff, soff;        // lane offsets: bytes in a cell pair, fp16 units in a scale pair
-  const uint8_t* xc;          // pair-order chunks (uniform)
+  const uint8_t* code[NT];  // tile code planes (wave-uniform)
+  uint32_t aoff;            // lane offset: bytes in a cell pair
+  const uint8_t* xc;        // pair-order chunks (uniform)
   const float* xd;
   const int* xn;
-  int groups;  // row groups in the workspace
+  int groups;               // row groups in the workspace
+  const uint16_t* sl[NT];   // the wave's staged scales of each tile (LDS), from block sb0 on
+  int sb0;
+  uint32_t soff;            // lane offset in a staged block pair (fp16 units)
 };
 
 template <int FMT, int NT, int G>
 __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad, int lane, int b) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
 #pragma unroll
-  for (int t = 0; t < NT; t++) {
-    st.a[t] = ld16_stream(ad.code[t] + (size_t)b * CB + ad.aoff);
-    st.w[t] = ld8_stream(ad.scale[t] + (size_t)b * TILE + ad.soff);
-  }
+  for (int t = 0; t < NT; t++) st.a[t] = ld16_stream(ad.code[t] + (size_t)b * CB + ad.aoff);
+  st.b = b;
   const size_t chunk0 = (size_t)(b >> 1) * ad.groups;
 #pragma unroll
   for (int g = 0; g < G; g++) {
@@ -373,8 +375,17 @@ __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad,
   }
 }
 
+// The step's weight scales, from the wave's staged copy.
+template <int NT, int G>
+__device__ __forceinline__ void mp_load_w(MpStep<NT, G>& st, const MpAddr<NT>& ad) {
+#pragma unroll
+  for (int t = 0; t < NT; t++)
+    st.w[t] = *reinterpret_cast<const uint2*>(ad.sl[t] + (st.b - ad.sb0) * TILE + ad.soff);
+}
+
 template <int FMT, int NT, int G, int PP, bool SEQ>
-__device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, const MpStep<NT, G>& st, int sh) {
+__device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, const MpStep<NT, G>& st,
+                                           const MpAddr<NT>& ad, int sh) {
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     uint4 av = st.a[t];
@@ -414,7 +425,7 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
 // One MP tile: groups of S*W2 waves, each group NT 16-row image tiles; G
 // groups of eight activation rows from the pair-order workspace.
 template <int FMT, int H, int G>
-__device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity) {
+__device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity, uint16_t* scl, int sc_stride) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
   constexpr bool SEQ = H == 1;
   constexpr int W2 = mp_w2(H), NT = mp_nt(H, G);
@@ -427,12 +438,14 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity) {
   const int64_t ntiles = np_of(ta.n) / TILE;
   const int64_t wrow0 = ta.row0 + (int64_t)g * TILE * NT;  // first row of this group's tiles
   MpAddr<NT> ad;
+  const uint16_t* scale[NT];
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     const int64_t it0 = (wrow0 >> 4) + t;
     const int64_t it = it0 < ntiles ? it0 : ntiles - 1;  // past the last tile: reread it, store nothing
     ad.code[t] = ta.code + ((size_t)it * ta.kbp) * CB;
-    ad.scale[t] = ta.scale + ((size_t)it * ta.kbp) * TILE;
+    scale[t] = ta.scale + ((size_t)it * ta.kbp) * TILE;
+    ad.sl[t] = scl + (wave * NT + t) * sc_stride;
   }
   ad.aoff = FMT == FMT_Q8 ? (uint32_t)(q * 256 + i * 16) : (uint32_t)((q >> 1) * 256 + i * 16);
   ad.soff = (uint32_t)((i >> 3) * 16 + 4 * q);
@@ -460,15 +473,47 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity) {
       for (int gg = 0; gg < G; gg++)
 #pragma unroll
         for (int v = 0; v < 4; v++) acc[t][p][gg][v] = 0.0f;
+  // The weight scales of the wave part's blocks [sb0, sb0 + H*BS) of each tile
+  // go to the wave's own LDS region once (16 lanes would otherwise load the
+  // same four scales every step).  Their loads are issued first, then the
+  // first two steps', so waiting for them waits for nothing else.
+  ad.sb0 = s * H * pl.BS;
+  const int nsv = H * pl.BS * 2;  // 16-byte pieces per tile (kbp/S blocks x 32 bytes)
+  uint4 sv[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; t++)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; k2++) {
+      const int e = lane + WAVE * k2;
+      if (e < nsv) sv[t][k2] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
+    }
   MpStep<NT, G> s0, s1;
   mp_load<FMT, NT, G>(s0, ad, lane, blk(0));
   mp_load<FMT, NT, G>(s1, ad, lane, blk(1));
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(ad.sl[t]));
+#pragma unroll
+    for (int k2 = 0; k2 < 2; k2++) {
+      const int e = lane + WAVE * k2;
+      if (e < nsv) dst[e] = sv[t][k2];
+    }
+    for (int e = lane + 2 * WAVE; e < nsv; e += WAVE) dst[e] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
+  }
+  mp_load_w(s0, ad);
+  mp_load_w(s1, ad);
   for (int j = 0; j < nsteps; j += 2) {
-    mp_compute<FMT, NT, G, PPW, SEQ>(acc, 0, s0, sh);
-    if (j + 2 < nsteps) mp_load<FMT, NT, G>(s0, ad, lane, blk(j + 2));
+    mp_compute<FMT, NT, G, PPW, SEQ>(acc, 0, s0, ad, sh);
+    if (j + 2 < nsteps) {
+      mp_load<FMT, NT, G>(s0, ad, lane, blk(j + 2));
+      mp_load_w(s0, ad);
+    }
     if (j + 1 < nsteps) {
-      mp_compute<FMT, NT, G, PPW, SEQ>(acc, 1, s1, sh);
-      if (j + 3 < nsteps) mp_load<FMT, NT, G>(s1, ad, lane, blk(j + 3));
+      mp_compute<FMT, NT, G, PPW, SEQ>(acc, 1, s1, ad, sh);
+      if (j + 3 < nsteps) {
+        mp_load<FMT, NT, G>(s1, ad, lane, blk(j + 3));
+        mp_load_w(s1, ad);
+      }
     }
   }
   // the wave's pairs by the lane-part tree: (h + h^1) across lanes i, i^8, then pair + pair
@@ -489,7 +534,7 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity) {
   // then the W2 pair groups of a wave part (the tree's upper level), then wave parts left to right
   if (gw > 1) {
     constexpr int NV = NT * G * 4;
-    float* rb = red + parity * (WAVES * WAVE * MP_NT_MAX * 2 * 4);
+    float* rb = red + parity * (WAVES * WAVE * MP_NV_MAX);
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
@@ -609,11 +654,13 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q
 }
 
 template <int FMT, int G>
-__global__ __launch_bounds__(WG) void mp_set_kernel(SetArgs a, int R) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp_set_kernel(SetArgs a, int R,
+                                                                                           int sc_stride) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
   float* red = reinterpret_cast<float*>(lds);
+  uint16_t* scl = reinterpret_cast<uint16_t*>(lds + 2 * WAVES * WAVE * MP_NV_MAX * 4);
   int parity = 0;
   for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
     int p = 0, t0 = tile;
@@ -621,10 +668,10 @@ __global__ __launch_bounds__(WG) void mp_set_kernel(SetArgs a, int R) {
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, 0);
     const PartPlan& pl = d.pl;
-    if (pl.H == 1) mp_tile<FMT, 1, G>(ta, R, red, parity);
-    else if (pl.H == 2) mp_tile<FMT, 2, G>(ta, R, red, parity);
-    else if (pl.H == 4) mp_tile<FMT, 4, G>(ta, R, red, parity);
-    else mp_tile<FMT, 8, G>(ta, R, red, parity);
+    if (pl.H == 1) mp_tile<FMT, 1, G>(ta, R, red, parity, scl, sc_stride);
+    else if (pl.H == 2) mp_tile<FMT, 2, G>(ta, R, red, parity, scl, sc_stride);
+    else if (pl.H == 4) mp_tile<FMT, 4, G>(ta, R, red, parity, scl, sc_stride);
+    else mp_tile<FMT, 8, G>(ta, R, red, parity, scl, sc_stride);
     if (pl.S > 1) parity ^= 1;
   }
 }
@@ -795,8 +842,14 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
 template <int FMT, int G>
 static void launch_mp(const SetArgs& a, int rows, hipStream_t s) {
   auto kern = mp_set_kernel<FMT, G>;
-  const size_t lds = 2 * WAVES * WAVE * MP_NT_MAX * 2 * 4 * 4;  // combine area: two parities
-  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, rows);
+  // combine area (two parities), then each wave's staged scales: NT tiles of kbp/S blocks x 16 fp16
+  int sc_stride = 0;
+  for (int i = 0; i < a.count; i++) {
+    const int v = a.p[i].kbp / a.p[i].pl.S * TILE;
+    sc_stride = v > sc_stride ? v : sc_stride;
+  }
+  const size_t lds = 2 * WAVES * WAVE * MP_NV_MAX * 4 + (size_t)WAVES * MP_NT_MAX * sc_stride * 2;
+  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, rows, sc_stride);
 }
 
 int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStream_t s) {
