@@ -438,7 +438,8 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
 
 
 def moe_sweep(torch, q, synth, L, sh, stream, timer):
-    """Routed MoE step: router f16 GEMV, top-8 routing, grouped gate/up, SwiGLU, grouped down, combine."""
+    """Routed MoE step (qg_moe_step): router f16 GEMV, top-8 routing + plan, grouped gate/up, SwiGLU + q8,
+    grouped down, combine -- six launches."""
     hidden, ffn, E, topk = 2048, 512, 256, 8
     nimg = E + 1  # index E: the shared expert
     gu_b = q.image_bytes(q.Q8_0, 2 * ffn, hidden)
@@ -464,29 +465,16 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
         xs = [synth.gaussian((rows, hidden), 1.0, synth.tensor_seed(3, 32 + rows, s), device="cuda") for s in range(nx)]
         logits = torch.empty((rows, E), device="cuda")
         expert = torch.empty(m, dtype=torch.int32, device="cuda")
-        xidx = torch.empty(m, dtype=torch.int32, device="cuda")
         wgt = torch.empty(m, device="cuda")
-        gu_y = torch.empty((m, 2 * ffn), device="cuda")
-        h = torch.empty((m, ffn), device="cuda")
-        o = torch.empty((m, hidden), device="cuda")
         y = torch.empty((rows, hidden), device="cuda")
-        ident = torch.arange(m, dtype=torch.int32, device="cuda")
-        ws1 = torch.empty(q.grouped_workspace_bytes(rows, hidden, m), dtype=torch.uint8, device="cuda")
-        ws2 = torch.empty(q.grouped_workspace_bytes(m, ffn, m), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(q.moe_workspace_bytes(rows, E, hidden, ffn, topk, True), dtype=torch.uint8, device="cuda")
         P = lambda t: t.data_ptr()
         xps = [P(x) for x in xs]
 
         def one(i):
             c = i % copies
-            xp = xps[i % nx]
-            L.gemv_f16(P(router), E, hidden, xp, rows, P(logits), sh)
-            L.qg_moe_route(P(logits), rows, E, topk, E, P(expert), P(xidx), P(wgt), sh)
-            L.qgemv_q8_0_grouped(P(gus[c]), nimg, 2 * ffn, hidden, xp, rows, P(expert), P(xidx), m, P(gu_y), P(ws1),
-                                 ws1.numel(), sh)
-            L.qg_swiglu(P(gu_y), m, ffn, P(h), sh)
-            L.qgemv_q8_0_grouped(P(dns[c]), nimg, hidden, ffn, P(h), m, P(expert), P(ident), m, P(o), P(ws2),
-                                 ws2.numel(), sh)
-            L.qg_moe_combine(P(o), P(wgt), rows, slots, hidden, P(y), sh)
+            L.qg_moe_step(P(router), E, hidden, ffn, topk, 1, P(gus[c]), P(dns[c]), xps[i % nx], rows, P(y),
+                          P(logits), P(expert), P(wgt), P(ws), ws.numel(), sh)
 
         ms = time_calls(torch, timer, stream, one, 128)
         # weight bytes actually streamed: router + every touched expert (the shared one included)
@@ -497,7 +485,7 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
             uniq.append(len(set(expert.cpu().tolist())))
         u = sum(uniq) / nx
         wb = 2 * E * hidden + u * (gu_b + dn_b)
-        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms, 10)
+        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms, 6)
         e["unique_experts"] = round(u, 2)
         out.append(e)
     return out

@@ -279,6 +279,62 @@ int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int
   return ok();
 }
 
+static int check_moe(int rows, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared) {
+  if (rows < 0 || rows > QG_MAX_ROWS) return fail(QG_EROWS, "rows=%d outside 0..%d", rows, QG_MAX_ROWS);
+  if (n_experts < 1 || n_experts > 1024) return fail(QG_ESHAPE, "n_experts=%d outside 1..1024", n_experts);
+  if (topk < 1 || topk > 32 || topk > n_experts) return fail(QG_ESHAPE, "topk=%d outside 1..min(32, n_experts)", topk);
+  if (shared != 0 && shared != 1) return fail(QG_EINVAL, "shared=%d is not 0 or 1", shared);
+  if (hidden < QK || hidden % QK) return fail(QG_ESHAPE, "hidden=%lld is not a positive multiple of 32", (long long)hidden);
+  if (ffn < QK || ffn % QK) return fail(QG_ESHAPE, "ffn=%lld is not a positive multiple of 32", (long long)ffn);
+  return QG_OK;
+}
+
+size_t qg_moe_workspace_bytes(int rows, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared) {
+  if (rows < 1 || check_moe(rows, n_experts, hidden, ffn, topk, shared)) return 0;
+  return moe_layout(rows, n_experts, hidden, ffn, topk + shared).total;
+}
+
+int qg_moe_step(const uint16_t* router, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
+                const void* gu_images, const void* down_images, const float* x, int rows, float* y, float* logits,
+                int32_t* expert, float* weight, void* ws, size_t ws_bytes, qg_stream stream) {
+  if (int st = check_moe(rows, n_experts, hidden, ffn, topk, shared)) return st;
+  if (!router || !gu_images || !down_images || !x || !y) return fail(QG_EINVAL, "null buffer");
+  if (int st = check_image(gu_images, "gu_images")) return st;
+  if (int st = check_image(down_images, "down_images")) return st;
+  if (int st = check_y(y)) return st;
+  if (!aligned(x, 16)) return fail(QG_EALIGN, "x %p is not 16-byte aligned", (const void*)x);
+  if (rows == 0) return ok();
+  const int slots = topk + shared, m = rows * slots;
+  const MoeLayout M = moe_layout(rows, n_experts, hidden, ffn, slots);
+  if (int st = check_ws(ws, ws_bytes, M.total, "the MoE step")) return st;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  float* lg = logits ? logits : (float*)(w + M.logits);
+  int32_t* ex = expert ? expert : (int32_t*)(w + M.expert);
+  float* wt = weight ? weight : (float*)(w + M.weight);
+  int32_t* xi = (int32_t*)(w + M.x_index);
+  int* header = (int*)(w + M.header);
+  int* sorted = (int*)(w + M.sorted);
+  int* items = (int*)(w + M.items);
+  float* gu = (float*)(w + M.gu);
+  float* o = (float*)(w + M.o);
+  const int n_images = n_experts + shared;
+  if (int st = launch_gemv_f16(router, n_experts, hidden, x, rows, lg, s)) return st;
+  if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
+                               x, hidden, w + M.xprep, s))
+    return st;
+  if (int st = launch_grouped_planned(gu_images, n_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi,
+                                      m, gu, s))
+    return st;
+  if (int st = launch_swiglu_q8(gu, m, ffn, w + M.hprep, s)) return st;
+  if (int st = launch_grouped_planned(down_images, n_images, hidden, ffn, w + M.hprep, m, header, sorted, items,
+                                      nullptr, m, o, s))
+    return st;
+  if (int st = launch_moe_combine(o, wt, rows, slots, hidden, y, s)) return st;
+  return ok();
+}
+
 int qg_quantize_rows_q8(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, qg_stream stream) {
   if (int st = check_x(x, rows, k, QG_MAX_PREP_ROWS)) return st;
   if (!qx || !dx || !sx) return fail(QG_EINVAL, "null output");

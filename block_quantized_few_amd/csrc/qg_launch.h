@@ -47,6 +47,20 @@ bool fuses_quantization(int rows);
 int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
                    const int32_t* x_index, int m, float* y, void* ws, hipStream_t s);
 
+// Grouped GEMV on a plan already in `ws` (header, sorted, items at the
+// grouped layout's offsets) and rows prepared at `prep` in row order;
+// x_index == nullptr: the activation row of assignment a is a.
+int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int64_t k, const void* prep, int x_rows,
+                           const int* header, const int* sorted, const int* items, const int32_t* x_index, int m,
+                           float* y, hipStream_t s);
+
+// Fused MoE pieces: routing + plan + input quantization (one workgroup), and
+// SwiGLU quantized for the down projection.
+int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
+                    float* weight, int32_t* x_index, int* header, int* sorted, int* items, const float* x, int64_t k,
+                    void* xprep, hipStream_t s);
+int launch_swiglu_q8(const float* gu, int m, int64_t ffn, void* hprep, hipStream_t s);
+
 // f16 lane.
 int launch_gemv_f16(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s);
 

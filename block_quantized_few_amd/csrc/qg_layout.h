@@ -129,6 +129,30 @@ QG_HD GroupedLayout grouped_layout(int64_t x_rows, int64_t k, int64_t m) {
   return G;
 }
 
+// Workspace of a fused routed-MoE step (qg_moe_step): rows <= 16 input rows,
+// m = rows * slots assignments, slots = topk (+1 with a shared expert).
+constexpr int QG_MOE_MAX_M = 16 * 33;
+struct MoeLayout {
+  size_t header, expert, weight, x_index, sorted, items, logits, xprep, gu, hprep, o, total;
+};
+QG_HD MoeLayout moe_layout(int64_t rows, int64_t n_experts, int64_t hidden, int64_t ffn, int64_t slots) {
+  const int64_t m = rows * slots;
+  MoeLayout M;
+  M.header = 0;
+  M.expert = 256;
+  M.weight = M.expert + align256((size_t)m * 4);
+  M.x_index = M.weight + align256((size_t)m * 4);
+  M.sorted = M.x_index + align256((size_t)m * 4);
+  M.items = M.sorted + align256((size_t)m * 4);
+  M.logits = M.items + align256((size_t)m * 12);
+  M.xprep = M.logits + align256((size_t)rows * n_experts * 4);
+  M.gu = M.xprep + prep_layout_rows(rows, hidden).total;
+  M.hprep = M.gu + align256((size_t)m * 2 * ffn * 4);
+  M.o = M.hprep + prep_layout_rows(m, ffn).total;
+  M.total = M.o + align256((size_t)m * hidden * 4);
+  return M;
+}
+
 struct PartPlan {
   int P, H, S, BS;
   int lgP, lgH, lgS;  // log2 of the powers of two P, H, S

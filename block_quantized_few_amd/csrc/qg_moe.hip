@@ -11,27 +11,26 @@ namespace qg {
 constexpr int ROUTE_MAX_E = 1024;
 constexpr int ROUTE_PER_LANE = ROUTE_MAX_E / WAVE;
 
-// One wave per row.  Softmax over all experts in double (max subtracted; each
-// lane sums its experts in order, then a fixed butterfly), and the topk
-// experts by logit, ties to the lower index, in descending order.
-__global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__ logits, int E, int topk,
-                                                       int shared_expert, int32_t* __restrict__ expert,
-                                                       int32_t* __restrict__ x_index, float* __restrict__ weight) {
-  const int r = blockIdx.x, lane = threadIdx.x;
-  const int slots = topk + (shared_expert >= 0 ? 1 : 0);
+// Routing of one row by one wave: softmax over the E logits in fp32 (max
+// subtracted; each lane sums its experts in index order, then a fixed
+// butterfly over the lanes), and the topk experts by logit, ties to the lower
+// index, in descending order.  Lane 0 returns the picks in ex[] / wt[].
+__device__ void route_row(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int nper = (E + WAVE - 1) / WAVE;
   float l[ROUTE_PER_LANE];
-  double mx = -INFINITY;
+  float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < ROUTE_PER_LANE; i++) {
     const int e = lane + WAVE * i;
-    l[i] = e < E ? logits[(int64_t)r * E + e] : -INFINITY;
-    mx = fmax(mx, (double)l[i]);
+    l[i] = (i < nper && e < E) ? lrow[e] : -INFINITY;
+    mx = fmaxf(mx, l[i]);
   }
-  for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
-  double sum = 0.0;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < ROUTE_PER_LANE; i++)
-    if (lane + WAVE * i < E) sum += exp((double)l[i] - mx);
+    if (i < nper && lane + WAVE * i < E) sum += expf(l[i] - mx);
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
   unsigned taken = 0;
   for (int k = 0; k < topk; k++) {
@@ -40,7 +39,7 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
 #pragma unroll
     for (int i = 0; i < ROUTE_PER_LANE; i++) {
       const int e = lane + WAVE * i;
-      if (e < E && !(taken >> i & 1u) && (l[i] > bv || (l[i] == bv && e < bi))) {
+      if (i < nper && e < E && !(taken >> i & 1u) && (l[i] > bv || (l[i] == bv && e < bi))) {
         bv = l[i];
         bi = e;
       }
@@ -55,15 +54,148 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
     }
     if (bi % WAVE == lane) taken |= 1u << (bi / WAVE);
     if (lane == 0) {
-      expert[(int64_t)r * slots + k] = bi;
-      x_index[(int64_t)r * slots + k] = r;
-      weight[(int64_t)r * slots + k] = (float)(exp((double)bv - mx) / sum);
+      ex[k] = bi;
+      wt[k] = expf(bv - mx) / sum;
     }
   }
-  if (lane == 0 && shared_expert >= 0) {
-    expert[(int64_t)r * slots + topk] = shared_expert;
-    x_index[(int64_t)r * slots + topk] = r;
-    weight[(int64_t)r * slots + topk] = 1.0f;
+}
+
+// One wave per row.
+__global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__ logits, int E, int topk,
+                                                       int shared_expert, int32_t* __restrict__ expert,
+                                                       int32_t* __restrict__ x_index, float* __restrict__ weight) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const int slots = topk + (shared_expert >= 0 ? 1 : 0);
+  __shared__ int s_ex[32];
+  __shared__ float s_wt[32];
+  route_row(logits + (int64_t)r * E, E, topk, s_ex, s_wt);
+  if (lane < slots) {
+    const bool sh = lane == topk;
+    expert[(int64_t)r * slots + lane] = sh ? shared_expert : s_ex[lane];
+    x_index[(int64_t)r * slots + lane] = r;
+    weight[(int64_t)r * slots + lane] = sh ? 1.0f : s_wt[lane];
+  }
+}
+
+// The plan of a routed MoE step, one workgroup: route every row (a wave per
+// row), then order the assignments by (expert, index) into work items of at
+// most 16 rows of one expert (the grouped GEMV's plan; the down projection
+// reuses it), and quantize the input rows into row order (A1).
+__global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict__ logits, int rows, int E, int topk,
+                                                        int shared_expert, int32_t* __restrict__ expert,
+                                                        float* __restrict__ weight, int32_t* __restrict__ x_index,
+                                                        int* __restrict__ header,
+                                                        int* __restrict__ sorted, int* __restrict__ items,
+                                                        const float* __restrict__ x, int64_t k, int8_t* __restrict__ xq,
+                                                        float* __restrict__ xd, int* __restrict__ xn) {
+  __shared__ int s_e[QG_MOE_MAX_M];
+  __shared__ int s_start[QG_MOE_MAX_M];
+  __shared__ int s_pos[QG_MOE_MAX_M];
+  __shared__ float s_w[QG_MOE_MAX_M];
+  const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
+  const int slots = topk + (shared_expert >= 0 ? 1 : 0);
+  const int m = rows * slots;
+  for (int r = wave; r < rows; r += nt / WAVE) {
+    route_row(logits + (int64_t)r * E, E, topk, s_e + r * slots, s_w + r * slots);
+    if (lane == 0 && shared_expert >= 0) {
+      s_e[r * slots + topk] = shared_expert;
+      s_w[r * slots + topk] = 1.0f;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < m; j += nt) {
+    expert[j] = s_e[j];
+    weight[j] = s_w[j];
+    x_index[j] = j / slots;
+    const int e = s_e[j];
+    int rank = 0, within = 0;
+    for (int i = 0; i < m; i++) {
+      const int f = s_e[i];
+      rank += (f < e) || (f == e && i < j);
+      within += (f == e && i < j);
+    }
+    s_pos[rank] = j;
+    s_start[rank] = (within % QG_MAX_ROWS) == 0;
+    sorted[rank] = j;
+  }
+  __syncthreads();
+  // inclusive scan of the item starts (m <= QG_MOE_MAX_M <= nt: one value per thread)
+  for (int off = 1; off < m; off <<= 1) {
+    const int v = tid < m ? s_start[tid] + (tid >= off ? s_start[tid - off] : 0) : 0;
+    __syncthreads();
+    if (tid < m) s_start[tid] = v;
+    __syncthreads();
+  }
+  if (tid < m) {
+    const int item = s_start[tid] - 1;
+    if (tid == 0 || s_start[tid - 1] != s_start[tid]) {
+      int cnt = 1;
+      while (tid + cnt < m && s_start[tid + cnt] == s_start[tid]) cnt++;
+      items[3 * item] = s_e[s_pos[tid]];
+      items[3 * item + 1] = tid;
+      items[3 * item + 2] = cnt;
+    }
+  }
+  if (tid == 0) {
+    header[0] = m ? s_start[m - 1] : 0;
+    header[1] = 0;
+  }
+  // A1 of the input rows, row order: four lanes per 32-block
+  const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
+  for (int e = tid; e < rows * kbp * 4; e += nt) {  // rows * kbp * 4 is a multiple of 64: quads stay whole
+    const int q = e & 3, blk = e >> 2, r = blk / kbp, b = blk - r * kbp;
+    float v[8];
+    if (b < kb) {
+      const float4* src = reinterpret_cast<const float4*>(x + (int64_t)r * k + (int64_t)b * QK + q * 8);
+      const float4 a = src[0], c = src[1];
+      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = 0.0f;
+    }
+    unsigned lo, hi;
+    float d;
+    int sum;
+    quantize_quarter(v, lo, hi, d, sum);
+    *reinterpret_cast<uint2*>(xq + ((int64_t)r * kbp + b) * 32 + q * 8) = make_uint2(lo, hi);
+    if (q == 0) {
+      xd[r * kbp + b] = d;
+      xn[r * kbp + b] = -8 * sum;
+    }
+  }
+}
+
+// SwiGLU of m assignments, h = silu(g) * u in fp32, quantized at once into
+// row order (m rows of ffn) for the down projection: four lanes per 32-block.
+__global__ __launch_bounds__(256) void swiglu_q8_kernel(const float* __restrict__ gu, int m, int64_t ffn, int kbp,
+                                                        int8_t* __restrict__ hq, float* __restrict__ hd,
+                                                        int* __restrict__ hn) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = t >> 2;
+  const int q = (int)(t & 3);
+  const bool active = blk < (int64_t)m * kbp;  // whole quads are active or not
+  const int64_t j = active ? blk / kbp : 0, b = active ? blk % kbp : 0;
+  float v[8];
+  if (active && b < ffn / QK) {
+    const float* g = gu + j * 2 * ffn + b * QK + q * 8;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float gv = g[i], uv = g[ffn + i];
+      v[i] = gv / (1.0f + expf(-gv)) * uv;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = 0.0f;
+  }
+  unsigned lo, hi;
+  float d;
+  int sum;
+  quantize_quarter(v, lo, hi, d, sum);
+  if (!active) return;
+  *reinterpret_cast<uint2*>(hq + (j * kbp + b) * 32 + q * 8) = make_uint2(lo, hi);
+  if (q == 0) {
+    hd[j * kbp + b] = d;
+    hn[j * kbp + b] = -8 * sum;
   }
 }
 
@@ -104,6 +236,26 @@ int launch_moe_route(const float* logits, int rows, int n_experts, int topk, int
   hipLaunchKernelGGL(moe_route_kernel, dim3(rows), dim3(64), 0, s, logits, n_experts, topk, shared_expert, expert,
                      x_index, weight);
   return hip_status(hipGetLastError(), "moe_route_kernel");
+}
+
+int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
+                    float* weight, int32_t* x_index, int* header, int* sorted, int* items, const float* x, int64_t k,
+                    void* xprep, hipStream_t s) {
+  const PrepLayout L = prep_layout_rows(rows, k);
+  uint8_t* w = (uint8_t*)xprep;
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, logits, rows, n_experts, topk, shared_expert, expert,
+                     weight, x_index, header, sorted, items, x, k, (int8_t*)(w + L.codes), (float*)(w + L.dx),
+                     (int*)(w + L.nsx));
+  return hip_status(hipGetLastError(), "moe_plan_kernel");
+}
+
+int launch_swiglu_q8(const float* gu, int m, int64_t ffn, void* hprep, hipStream_t s) {
+  const PrepLayout L = prep_layout_rows(m, ffn);
+  uint8_t* w = (uint8_t*)hprep;
+  const int kbp = (int)kbp_of(ffn);
+  hipLaunchKernelGGL(swiglu_q8_kernel, dim3(grid1((int64_t)m * kbp * 4, 256)), dim3(256), 0, s, gu, m, ffn, kbp,
+                     (int8_t*)(w + L.codes), (float*)(w + L.dx), (int*)(w + L.nsx));
+  return hip_status(hipGetLastError(), "swiglu_q8_kernel");
 }
 
 int launch_swiglu(const float* gu, int m, int64_t ffn, float* h, hipStream_t s) {

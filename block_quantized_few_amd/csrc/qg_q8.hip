@@ -760,7 +760,7 @@ __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__
   const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
   if (threadIdx.x < cnt) {
     const int a = sorted[start + threadIdx.x];
-    s_map[threadIdx.x] = x_index[a];
+    s_map[threadIdx.x] = x_index ? x_index[a] : a;
     s_map[QG_MAX_ROWS + threadIdx.x] = a;
   }
   __syncthreads();
@@ -913,16 +913,10 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
   return hip_status(hipGetLastError(), mf ? "mp_set_kernel" : "rl_set_kernel");
 }
 
-int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
-                   const int32_t* x_index, int m, float* y, void* ws, hipStream_t s) {
-  const GroupedLayout G = grouped_layout(x_rows, k, m);
-  uint8_t* w = (uint8_t*)ws;
-  int* header = (int*)(w + G.header);
-  int* sorted = (int*)(w + G.sorted);
-  int* items = (int*)(w + G.items);
-  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(1024), 0, s, expert, x_index, m, n_experts, x_rows, header,
-                     sorted, items);
-  if (int st = hip_status(hipGetLastError(), "grouped_plan_kernel")) return st;
+int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int64_t k, const void* prep, int x_rows,
+                           const int* header, const int* sorted, const int* items, const int32_t* x_index, int m,
+                           float* y, hipStream_t s) {
+  (void)n_experts;
   if (m == 0) return QG_OK;
   const int kbp = (int)kbp_of(k);
   const PartPlan pl = part_plan(kbp);
@@ -935,8 +929,21 @@ int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, 
   const int64_t eb = (int64_t)image_total_bytes(QG_FMT_Q8_0, n, k);
   const size_t so = image_scale_offset(QG_FMT_Q8_0, n, k);
   hipLaunchKernelGGL(grouped_kernel, dim3(tiles, m), dim3(WG), lds, s, (const uint8_t*)images, eb, so, n, k, kbp, pl,
-                     prep_view(w + G.prep, prep_layout_rows(x_rows, k)), header, sorted, items, x_index, y, lds_x);
+                     prep_view(prep, prep_layout_rows(x_rows, k)), header, sorted, items, x_index, y, lds_x);
   return hip_status(hipGetLastError(), "grouped_kernel");
+}
+
+int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
+                   const int32_t* x_index, int m, float* y, void* ws, hipStream_t s) {
+  const GroupedLayout G = grouped_layout(x_rows, k, m);
+  uint8_t* w = (uint8_t*)ws;
+  int* header = (int*)(w + G.header);
+  int* sorted = (int*)(w + G.sorted);
+  int* items = (int*)(w + G.items);
+  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(1024), 0, s, expert, x_index, m, n_experts, x_rows, header,
+                     sorted, items);
+  if (int st = hip_status(hipGetLastError(), "grouped_plan_kernel")) return st;
+  return launch_grouped_planned(images, n_experts, n, k, w + G.prep, x_rows, header, sorted, items, x_index, m, y, s);
 }
 
 }  // namespace qg

@@ -71,6 +71,10 @@ _SIGS = {
                                C.c_void_p]),
     "qg_swiglu": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p]),
     "qg_moe_combine": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_void_p, C.c_void_p]),
+    "qg_moe_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_int]),
+    "qg_moe_step": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_size_t, C.c_void_p]),
     "qg_quantize_rows_q8": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_void_p]),
     "qgemv_blockdots": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
@@ -294,6 +298,29 @@ def moe_combine(o, weight, rows, slots, y=None):
         y = torch.empty((rows, hidden), dtype=torch.float32, device=o.device)
     _check(lib().qg_moe_combine(_p(o), _p(weight), rows, slots, hidden, _p(y), _stream()))
     return y
+
+
+def moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared):
+    return lib().qg_moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, int(shared))
+
+
+def moe_step_fused(x, router16, n_experts, topk, gu_images, down_images, ffn, shared=True, ws=None):
+    """The routed MoE step of moe_step in six launches (qg_moe_step).  Returns y and the routing
+    (expert, weight) as [rows * slots] tensors, and the router logits."""
+    _dev(x, torch.float32, "x")
+    rows, hidden = x.shape
+    slots = topk + (1 if shared else 0)
+    dev = x.device
+    y = torch.empty((rows, hidden), dtype=torch.float32, device=dev)
+    logits = torch.empty((rows, n_experts), dtype=torch.float32, device=dev)
+    expert = torch.empty(rows * slots, dtype=torch.int32, device=dev)
+    weight = torch.empty(rows * slots, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(1, moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared)), dtype=torch.uint8,
+                         device=dev)
+    _check(lib().qg_moe_step(_p(router16), n_experts, hidden, ffn, topk, int(shared), _p(gu_images), _p(down_images),
+                             _p(x), rows, _p(y), _p(logits), _p(expert), _p(weight), _p(ws), ws.numel(), _stream()))
+    return y, (expert, weight), logits
 
 
 def quantize_rows_q8(x):

@@ -225,6 +225,25 @@ int qg_swiglu(const float* gu, int m, int64_t ffn, float* h, qg_stream stream);
 int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int64_t hidden, float* y,
                    qg_stream stream);
 
+/* A routed-MoE decode step in six launches, the composition of the calls
+ * above: router logits (f16 lane, n_experts x hidden), routing as
+ * qg_moe_route, grouped gate/up GEMV, SwiGLU quantized for the down
+ * projection, grouped down GEMV, weighted combine.  gu_images holds
+ * n_experts + shared Q8_0 images of [2*ffn][hidden] (gate rows, then up rows)
+ * back to back; down_images the same experts' [hidden][ffn]; with shared = 1
+ * image n_experts is an ungated shared expert joining every row with weight
+ * 1 (the last slot).  x [rows][hidden], y [rows][hidden] fp32, 1 <= rows <= 16
+ * (0 is a no-op), 1 <= topk <= min(32, n_experts), n_experts <= 1024, hidden
+ * and ffn multiples of 32.  logits [rows][n_experts], expert and weight
+ * [rows][slots] (slots = topk + shared) receive the routing when not null.
+ * ws: qg_moe_workspace_bytes bytes.  Rows of 9..16 run in the same launches.
+ * The step follows the routed feed-forward of the llama-leg page's routed-slot
+ * commit 2243ccc and the drama page's MoE series commits. */
+size_t qg_moe_workspace_bytes(int rows, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared);
+int qg_moe_step(const uint16_t* router, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
+                const void* gu_images, const void* down_images, const float* x, int rows, float* y, float* logits,
+                int32_t* expert, float* weight, void* ws, size_t ws_bytes, qg_stream stream);
+
 /* ------------------------------------------------------ test-only hooks --- */
 
 /* A1 in the plain layout: qx [rows][k] int8, dx [rows][k/32] fp32, sx

@@ -128,6 +128,22 @@ def test_validation_refuses_before_any_hip_call():
     assert st == -2
     st, msg = _status("qg_moe_route", V(A), 1, 2000, 8, -1, V(A), V(A), V(A), None)
     assert st == -2
+    # qg_moe_step: router, E, hidden, ffn, topk, shared, gu, down, x, rows, y, logits, expert, weight, ws, bytes
+    moe = lambda **kw: _status("qg_moe_step", V(A), kw.get("E", 256), kw.get("hidden", 2048), kw.get("ffn", 512),
+                               kw.get("topk", 8), kw.get("shared", 1), V(A), V(A), V(A), kw.get("rows", 1), V(A),
+                               None, None, None, V(A), kw.get("bytes", 1 << 30), None)
+    st, msg = moe(rows=17)
+    assert st == -3 and "rows=17" in msg
+    st, msg = moe(topk=0)
+    assert st == -2 and "topk=0" in msg
+    st, msg = moe(shared=2)
+    assert st == -1 and "shared=2" in msg
+    st, msg = moe(ffn=500)
+    assert st == -2 and "ffn=500" in msg
+    st, msg = moe(bytes=100)
+    assert st == -5
+    assert q.moe_workspace_bytes(16, 256, 2048, 512, 8, True) > 16 * 9 * (2048 + 1024) * 4
+    assert q.moe_workspace_bytes(17, 256, 2048, 512, 8, True) == 0
     assert q.status_string(-3) == "rows outside 0..16"
 
 

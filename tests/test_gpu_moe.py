@@ -74,3 +74,21 @@ def test_moe_step_matches_oracle(moe, rows):
         err = np.abs(yg[r] - yo[r]) / denom
         log(f"  row {r}: max rel err {err.max():.3e}")
         assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("rows", [1, 8, 9, 16])
+def test_fused_moe_step_equals_composition(moe, rows):
+    """qg_moe_step (six launches, one plan for both grouped GEMVs, SwiGLU quantized in place) gives the
+    bits of the composition of the separate calls."""
+    log(f"fused moe rows={rows}")
+    x = torch.from_numpy(gauss((rows, HIDDEN), 1.0, WL, 32 + rows).numpy()).cuda()
+    y, (expert, _, weight), logits = q.moe_step(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN, shared_expert=E)
+    yf, (expert_f, weight_f), logits_f = q.moe_step_fused(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN)
+    assert torch.equal(logits_f, logits)
+    assert torch.equal(expert_f, expert)
+    assert torch.equal(weight_f, weight)
+    assert torch.equal(yf, y)
+    # a second call on a smaller row count through the same workspace size class
+    if rows > 1:
+        yf1, _, _ = q.moe_step_fused(x[:1].contiguous(), moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN)
+        assert torch.equal(yf1[0], yf[0])
