@@ -414,7 +414,7 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
     q8 = []
     for c in range(2):
         w = synth.gaussian((n, k), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
-        w16.append(w.half())
+        w16.append(q.f16_image(w.half()))
         q8.append(q.quantize_weights(q.Q8_0, w))
         del w
     for rows in (1, 2, 4, 8, 9, 16):
@@ -456,7 +456,7 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
             q.quantize_weights(q.Q8_0, w, dn[e * dn_b:(e + 1) * dn_b])
         gus.append(gu)
         dns.append(dn)
-    router = synth.gaussian((E, hidden), 0.02, synth.tensor_seed(3, 0), device="cuda").half()
+    router = q.f16_image(synth.gaussian((E, hidden), 0.02, synth.tensor_seed(3, 0), device="cuda").half())
     out = []
     for rows in (1, 8, 9, 16):
         slots = topk + 1

@@ -198,19 +198,33 @@ int qgemv_set_rows(int fmt, const qg_proj_rows* projs, int count, int rows, qg_s
   return ok();
 }
 
-int gemv_f16(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream) {
-  if (int st = check_rows(rows)) return st;
+static int check_f16_nk(int64_t n, int64_t k) {
   if (n < 1 || n > (1LL << 31) - 1) return fail(QG_ESHAPE, "n=%lld outside 1..2^31-1", (long long)n);
   if (k < 8 || k % 8 || k > (1LL << 24))
     return fail(QG_ESHAPE, "k=%lld is not a positive multiple of 8 up to 2^24", (long long)k);
+  return QG_OK;
+}
+
+int qg_f16_image(const uint16_t* w, int64_t n, int64_t k, void* image, qg_stream stream) {
+  if (int st = check_f16_nk(n, k)) return st;
   if (!w) return fail(QG_EINVAL, "w is null");
   if (!aligned(w, 16)) return fail(QG_EALIGN, "w %p is not 16-byte aligned", (const void*)w);
+  if (int st = check_image(image, "image")) return st;
+  if (int st = check_device()) return st;
+  if (int st = launch_f16_pack(w, n, k, image, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int gemv_f16(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream) {
+  if (int st = check_rows(rows)) return st;
+  if (int st = check_f16_nk(n, k)) return st;
+  if (int st = check_image(w_image, "w_image")) return st;
   if (int st = check_y(y)) return st;
   if (rows == 0) return ok();
   if (!x) return fail(QG_EINVAL, "x is null");
   if (!aligned(x, 16)) return fail(QG_EALIGN, "x %p is not 16-byte aligned", (const void*)x);
   if (int st = check_device()) return st;
-  if (int st = launch_gemv_f16(w, n, k, x, rows, y, (hipStream_t)stream)) return st;
+  if (int st = launch_gemv_f16(w_image, n, k, x, rows, y, (hipStream_t)stream)) return st;
   return ok();
 }
 
@@ -294,11 +308,12 @@ size_t qg_moe_workspace_bytes(int rows, int n_experts, int64_t hidden, int64_t f
   return moe_layout(rows, n_experts, hidden, ffn, topk + shared).total;
 }
 
-int qg_moe_step(const uint16_t* router, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
+int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
                 const void* gu_images, const void* down_images, const float* x, int rows, float* y, float* logits,
                 int32_t* expert, float* weight, void* ws, size_t ws_bytes, qg_stream stream) {
   if (int st = check_moe(rows, n_experts, hidden, ffn, topk, shared)) return st;
-  if (!router || !gu_images || !down_images || !x || !y) return fail(QG_EINVAL, "null buffer");
+  if (!router_image || !gu_images || !down_images || !x || !y) return fail(QG_EINVAL, "null buffer");
+  if (int st = check_image(router_image, "router_image")) return st;
   if (int st = check_image(gu_images, "gu_images")) return st;
   if (int st = check_image(down_images, "down_images")) return st;
   if (int st = check_y(y)) return st;
@@ -320,7 +335,7 @@ int qg_moe_step(const uint16_t* router, int n_experts, int64_t hidden, int64_t f
   float* gu = (float*)(w + M.gu);
   float* o = (float*)(w + M.o);
   const int n_images = n_experts + shared;
-  if (int st = launch_gemv_f16(router, n_experts, hidden, x, rows, lg, s)) return st;
+  if (int st = launch_gemv_f16(router_image, n_experts, hidden, x, rows, lg, s)) return st;
   if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
                                x, hidden, w + M.xprep, s))
     return st;

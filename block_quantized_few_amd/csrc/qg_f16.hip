@@ -1,6 +1,25 @@
 // qg_f16.hip -- the f16 lane: halfword weights, fp32 activations, fp32
 // accumulation (the reference lane of the dasLLAMA audio-towers page,
-// feature commit).
+// feature commit), on v_mfma_f32_16x16x32_f16.
+//
+// Weight image.  The row-major [n][k] halfword matrix is repacked once into
+// 16-row tiles of 32-column steps: tile t, step s is one 1 KB block in which
+// lane l = i + 16q of a wave finds its 16 bytes at 16*l, the halfwords
+// w[16t + i][32s + 8q .. 32s + 8q + 7] -- exactly the A operand the MFMA
+// wants from that lane.  A tile's steps follow each other, tiles follow each
+// other; rows past n and columns past k are zero.  One wave load of a step is
+// then 1 KB of consecutive bytes (row-major weights give 16 rows x 64 bytes
+// per load, which the memory system serves markedly slower).
+//
+// Arithmetic.  A lane (i, q) feeds the MFMA its 8 weights and the same 8 k
+// of activation row i; the activation goes in as two halfword terms,
+// hi = f16(x * 2^-e) and lo = f16(x * 2^-e - hi), so x * 2^-e = hi + lo to
+// about 2^-22 relative, and both terms meet the exact halfword weights in
+// fp32.  The power of two 2^-e puts the largest |x| of the wave's k range of
+// that row in [2^14, 2^15) (the halfword range); the wave's fp32 sum is scaled
+// back by 2^e (exact).  The S waves of a workgroup take S contiguous k ranges,
+// added left to right at the end.  A row's result depends on its own
+// activations, K and N only, never on the other rows of the call.
 #include <hip/hip_runtime.h>
 
 #include "qg_device.h"
@@ -9,114 +28,195 @@
 
 namespace qg {
 
-constexpr int F16_WG = 256;
-constexpr int F16_LPR = 16;                     // lanes per weight row
-constexpr int F16_SLOTS = F16_WG / F16_LPR;     // rows per workgroup step
-constexpr int F16_LDS = 48 * 1024;              // staged fp32 activation chunk
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Sum over the 16 lanes of a row (pairs, quads, half-rows by mirror, rows by
-// mirror); every lane receives the same bits.
-__device__ __forceinline__ float sum16(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-  return v;
+constexpr int FM_STEP_HALVES = 512;  // halfwords of one (tile, step) block
+constexpr int FM_NT_BIG = 8;         // tiles per step of the kernel on large N
+constexpr int FM_LA_BIG = 2;         // and its steps in flight
+constexpr int64_t FM_ROT = 7;        // start-step stride between neighbouring tiles
+
+// ------------------------------------------------------------------ pack ---
+// One thread per 16-byte chunk of the image.
+__global__ void f16_pack_kernel(const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ks,
+                                uint4* __restrict__ img, int64_t chunks) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  const int lane = (int)(c & 63);
+  const int64_t blk = c >> 6, t = blk / ks, s = blk - t * ks;
+  const int64_t row = 16 * t + (lane & 15), k0 = 32 * s + 8 * (lane >> 4);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < N && k0 < K) v = *reinterpret_cast<const uint4*>(w + row * K + k0);  // K % 8 == 0
+  img[c] = v;
 }
 
-// Lane j of a row's 16 lanes reads 8 halfwords (16 bytes) at j, j+16, ... and
-// multiplies them with fp32 activations staged in LDS: one fma per weight and
-// row (fp16 -> fp32 conversion is exact), rows kept in fp32.
-template <int R, int T>
-__global__ __launch_bounds__(F16_WG) void gemv_f16_kernel(const uint16_t* __restrict__ w, int64_t N, int64_t K,
-                                                          const float* __restrict__ x, float* __restrict__ y, int ce) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  float* l_x = reinterpret_cast<float*>(lds);
-  const int tid = threadIdx.x;
-  const int slot = tid / F16_LPR, j = tid % F16_LPR;
-  const int64_t row0 = (int64_t)blockIdx.x * (F16_SLOTS * T);
-  int64_t n[T];
-  bool valid[T];
-  const uint16_t* wrow[T];
-#pragma unroll
-  for (int t = 0; t < T; t++) {
-    n[t] = row0 + (int64_t)(t * F16_SLOTS + slot);
-    valid[t] = n[t] < N;
-    wrow[t] = w + (valid[t] ? n[t] : N - 1) * K;
-  }
-  float acc[T][R];
-#pragma unroll
-  for (int t = 0; t < T; t++)
-#pragma unroll
-    for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+int launch_f16_pack(const uint16_t* w, int64_t n, int64_t k, void* image, hipStream_t s) {
+  const int64_t ks = f16_steps(k), chunks = f16_tiles(n) * ks * 64;
+  const int64_t g = (chunks + 255) / 256;
+  hipLaunchKernelGGL(f16_pack_kernel, dim3((unsigned)g), dim3(256), 0, s, w, n, k, ks,
+                     reinterpret_cast<uint4*>(image), chunks);
+  return hip_status(hipGetLastError(), "f16_pack_kernel");
+}
 
-  for (int64_t c0 = 0; c0 < K; c0 += ce) {
-    const int cen = (int)min((int64_t)ce, K - c0);  // multiple of 8
-    if (c0) __syncthreads();
-    const int cu = cen / 4;
-    for (int u = tid; u < R * cu; u += F16_WG) {
-      const int r = u / cu, c = u - r * cu;
-      reinterpret_cast<float4*>(l_x + (size_t)r * ce)[c] = reinterpret_cast<const float4*>(x + r * K + c0)[c];
+// ------------------------------------------------------------------ GEMV ---
+template <int NT>
+struct FmStep {
+  uint4 a[NT];  // weights of NT 16-row tiles
+  float4 x[2];  // 8 activations
+};
+
+template <int NT>
+__device__ __forceinline__ void fm_load(FmStep<NT>& st, const uint16_t* const (&wt)[NT], const float* xrow,
+                                        int64_t kend, int64_t s) {
+  const int64_t k0 = s * 32;
+  const bool in = k0 < kend;  // kend = K - 8q; K % 8 == 0: the lane's 8 activations are all in or all out
+#pragma unroll
+  for (int t = 0; t < NT; t++) st.a[t] = ld16_stream(wt[t] + s * FM_STEP_HALVES);  // zero-padded image
+  st.x[0] = in ? *reinterpret_cast<const float4*>(xrow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+  st.x[1] = in ? *reinterpret_cast<const float4*>(xrow + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int NT>
+__device__ __forceinline__ void fm_compute(v4f (&c)[NT], const FmStep<NT>& st, float scale) {
+  const float v[8] = {st.x[0].x, st.x[0].y, st.x[0].z, st.x[0].w, st.x[1].x, st.x[1].y, st.x[1].z, st.x[1].w};
+  v8h hi, lo;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const float sv = v[j] * scale;
+    const _Float16 h = (_Float16)sv;
+    hi[j] = h;
+    lo[j] = (_Float16)(sv - (float)h);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    v8h a;
+    __builtin_memcpy(&a, &st.a[t], 16);
+    c[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, hi, c[t], 0, 0, 0);
+    c[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, lo, c[t], 0, 0, 0);
+  }
+}
+
+// NT 16-row tiles per workgroup step (a tile group), S waves (k ranges), LA
+// steps in flight; persistent over tile groups.
+template <int NT, int S, int LA>
+__global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __restrict__ img, int64_t N, int64_t K,
+                                                            const float* __restrict__ x, int R,
+                                                            float* __restrict__ y, int64_t groups) {
+  __shared__ float red[S * NT * 4 * WAVE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
+  const int i = lane & 15, q = lane >> 4;
+  const int64_t ks = (K + 31) / 32, tiles = (N + 15) / 16;
+  const int64_t s0 = ks * wave / S, s1 = ks * (wave + 1) / S;  // this wave's k steps
+  const int xr = i < R ? i : R - 1;                             // activation row of this lane's column
+  const float* xrow = x + (int64_t)xr * K + 8 * q;
+  const int64_t kend = K - 8 * q;  // the lane reads k0 + 8q .. k0 + 8q + 7 while k0 < kend
+  const int64_t nst = s1 - s0;
+  const uint16_t* wt[NT];
+  int64_t lc = s0;  // next step to load
+  FmStep<NT> f[LA];
+  // Points the wave at tile group grp and puts its first LA steps in flight.
+  // The wave walks its k range from a group-dependent starting step, wrapping
+  // round: groups in flight together then read different k offsets.
+  auto start = [&](int64_t grp) {
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      const int64_t tt = grp * NT + t;
+      wt[t] = img + (tt < tiles ? tt : tiles - 1) * ks * FM_STEP_HALVES + 8 * lane;  // past the end: reread
     }
-    __syncthreads();
-#pragma unroll 2
-    for (int c = j; c * 8 < cen; c += F16_LPR) {
-      uint4 wv[T];
+    lc = s0 + (nst ? (grp * FM_ROT) % nst : 0);
 #pragma unroll
-      for (int t = 0; t < T; t++) wv[t] = ld16_stream(wrow[t] + c0 + c * 8);
+    for (int j = 0; j < LA; j++)
+      if (j < nst) {
+        fm_load<NT>(f[j], wt, xrow, kend, lc);
+        lc = lc + 1 == s1 ? s0 : lc + 1;
+      }
+  };
+  if (blockIdx.x < groups) start(blockIdx.x);
+
+  // the scale of this column over the wave's k range (from the steps in flight
+  // when they cover it, else from a pass of its own)
+  auto amax8 = [](float4 a, float4 b) {
+    return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                 fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+  };
+  float amax = 0.0f;
+  if (nst <= LA && blockIdx.x < groups) {
 #pragma unroll
-      for (int r = 0; r < R; r++) {
-        const float4 x0 = *reinterpret_cast<const float4*>(l_x + (size_t)r * ce + c * 8);
-        const float4 x1 = *reinterpret_cast<const float4*>(l_x + (size_t)r * ce + c * 8 + 4);
-        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int j = 0; j < LA; j++)
+      if (j < nst) amax = fmaxf(amax, amax8(f[j].x[0], f[j].x[1]));  // zeros past k
+  } else {
+    for (int64_t st = s0; st < s1; st++) {
+      const int64_t k0 = st * 32;
+      if (k0 < kend)
+        amax = fmaxf(amax, amax8(*reinterpret_cast<const float4*>(xrow + k0),
+                                 *reinterpret_cast<const float4*>(xrow + k0 + 4)));
+    }
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  int ex = 0;
+  if (amax > 0.0f) frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+  const int se = min(max(15 - ex, -126), 126);
+  const float scale = ldexpf(1.0f, se);
+
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    v4f c[NT];
 #pragma unroll
-        for (int t = 0; t < T; t++) {
-          const unsigned wu[4] = {wv[t].x, wv[t].y, wv[t].z, wv[t].w};
-          float a = acc[t][r];
+    for (int t = 0; t < NT; t++) c[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int64_t st = 0; st < nst; st += LA) {
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            a = __builtin_fmaf(h2f((uint16_t)(wu[e] & 0xffff)), xv[2 * e], a);
-            a = __builtin_fmaf(h2f((uint16_t)(wu[e] >> 16)), xv[2 * e + 1], a);
+      for (int j = 0; j < LA; j++) {
+        if (st + j < nst) {
+          fm_compute<NT>(c, f[j], scale);
+          if (st + j + LA < nst) {
+            fm_load<NT>(f[j], wt, xrow, kend, lc);
+            lc = lc + 1 == s1 ? s0 : lc + 1;
           }
-          acc[t][r] = a;
         }
       }
     }
-  }
+    // every step is consumed: the next group's first loads fly during the reduction
+    if (grp + gridDim.x < groups) start(grp + gridDim.x);
+    // k ranges left to right (each scaled back first)
+    __syncthreads();
 #pragma unroll
-  for (int t = 0; t < T; t++)
+    for (int t = 0; t < NT; t++)
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      const float v = sum16(acc[t][r]);
-      if (valid[t] && j == r) y[(int64_t)r * N + n[t]] = v;
+      for (int v = 0; v < 4; v++) red[((wave * NT + t) * 4 + v) * WAVE + lane] = ldexpf(c[t][v], -se);
+    __syncthreads();
+    if (wave == 0 && i < R) {
+#pragma unroll
+      for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          float acc = red[(t * 4 + v) * WAVE + lane];
+          for (int s2 = 1; s2 < S; s2++) acc += red[((s2 * NT + t) * 4 + v) * WAVE + lane];
+          const int64_t row = (grp * NT + t) * 16 + 4 * q + v;
+          if (row < N) y[(int64_t)i * N + row] = acc;
+        }
     }
-}
-
-template <int R, int T>
-static void launch_f16_rt(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y, hipStream_t s) {
-  int ce = (F16_LDS / (R * 4)) / 128 * 128;
-  if (ce < 128) ce = 128;
-  const int64_t kr = (k + 127) / 128 * 128;
-  if (ce > kr) ce = (int)kr;
-  const unsigned grid = (unsigned)((n + F16_SLOTS * T - 1) / (F16_SLOTS * T));
-  hipLaunchKernelGGL((gemv_f16_kernel<R, T>), dim3(grid), dim3(F16_WG), (size_t)R * ce * 4, s, w, n, k, x, y, ce);
-}
-
-template <int T>
-static void launch_f16_t(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y,
-                         hipStream_t s) {
-  switch (rows) {
-#define QG_R(RR) \
-  case RR: launch_f16_rt<RR, T>(w, n, k, x, y, s); break;
-    QG_R(1) QG_R(2) QG_R(3) QG_R(4) QG_R(5) QG_R(6) QG_R(7) QG_R(8)
-    QG_R(9) QG_R(10) QG_R(11) QG_R(12) QG_R(13) QG_R(14) QG_R(15) QG_R(16)
-#undef QG_R
   }
 }
 
-int launch_gemv_f16(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s) {
-  if ((n + 31) / 32 >= 1024) launch_f16_t<2>(w, n, k, x, rows, y, s);
-  else launch_f16_t<1>(w, n, k, x, rows, y, s);
+template <int NT, int S, int LA>
+static void launch_f16(const uint16_t* img, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s) {
+  auto kern = gemv_f16_kernel<NT, S, LA>;
+  const int64_t groups = (f16_tiles(n) + NT - 1) / NT;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, S * WAVE, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t g = (int64_t)device_cus() * per_cu;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(groups < g ? groups : g)), dim3(S * WAVE), 0, s, img, n, k, x, rows, y,
+                     groups);
+}
+
+int launch_gemv_f16(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s) {
+  const uint16_t* img = static_cast<const uint16_t*>(image);
+  const int64_t t16 = f16_tiles(n);
+  // few tiles: more waves per tile (shorter k ranges) to keep loads in flight
+  if (t16 >= 4096) launch_f16<FM_NT_BIG, 4, FM_LA_BIG>(img, n, k, x, rows, y, s);
+  else if (t16 >= 256) launch_f16<1, 4, 4>(img, n, k, x, rows, y, s);
+  else launch_f16<1, 16, 4>(img, n, k, x, rows, y, s);
   return hip_status(hipGetLastError(), "gemv_f16_kernel");
 }
 

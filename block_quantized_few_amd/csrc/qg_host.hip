@@ -84,7 +84,7 @@ int qg_last_error_detail(char* buf, size_t len) {
 
 size_t qg_image_bytes(int fmt, int64_t n, int64_t k) {
   if (n < 1 || k < 1) return 0;
-  if (fmt == QG_FMT_F16) return k % 8 ? 0 : (size_t)n * (size_t)k * 2;
+  if (fmt == QG_FMT_F16) return k % 8 ? 0 : (size_t)f16_image_bytes(n, k);
   if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return 0;
   if (k % QK) return 0;
   return image_total_bytes(fmt, n, k);
@@ -101,16 +101,44 @@ size_t qg_grouped_workspace_bytes(int x_rows, int64_t k, int m) {
 }
 
 static int check_pack_args(int fmt, const void* a, int64_t n, int64_t k, const void* b) {
-  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1) or Q4_0 (2)", fmt);
+  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0 && fmt != QG_FMT_F16)
+    return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1), Q4_0 (2) or F16 (3)", fmt);
   if (!a || !b) return fail(QG_EINVAL, "null buffer");
+  if (fmt == QG_FMT_F16) {
+    if (n < 1 || k < 8 || k % 8)
+      return fail(QG_ESHAPE, "n=%lld k=%lld (need n >= 1, k a positive multiple of 8)", (long long)n, (long long)k);
+    return QG_OK;
+  }
   if (n < 1 || k < QK || k % QK) return fail(QG_ESHAPE, "n=%lld k=%lld (need n >= 1, k a positive multiple of 32)",
                                              (long long)n, (long long)k);
   return QG_OK;
 }
 
+// F16 image chunk c (16 bytes) <-> row-major [n][k] halfwords: chunk l of the
+// (tile, step) block holds 8 halfwords of row 16*tile + l % 16 at column
+// 32*step + 8*(l / 16).
+static void f16_pack_host(const uint16_t* w, int64_t n, int64_t k, uint16_t* img, bool unpack) {
+  const int64_t ks = f16_steps(k), tiles = f16_tiles(n);
+  for (int64_t t = 0; t < tiles; t++)
+    for (int64_t s = 0; s < ks; s++)
+      for (int l = 0; l < 64; l++) {
+        const int64_t row = 16 * t + l % 16, k0 = 32 * s + 8 * (l / 16);
+        uint16_t* chunk = img + ((t * ks + s) * 64 + l) * 8;
+        if (row >= n || k0 >= k) continue;
+        uint16_t* src = const_cast<uint16_t*>(w) + row * k + k0;
+        if (unpack) memcpy(src, chunk, 16);
+        else memcpy(chunk, src, 16);
+      }
+}
+
 int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image) {
   int st = check_pack_args(fmt, blocks, n, k, image);
   if (st) return st;
+  if (fmt == QG_FMT_F16) {
+    memset(image, 0, (size_t)f16_image_bytes(n, k));
+    f16_pack_host((const uint16_t*)blocks, n, k, (uint16_t*)image, false);
+    return ok();
+  }
   const uint8_t* src = (const uint8_t*)blocks;
   uint8_t* dst = (uint8_t*)image;
   memset(dst, 0, image_total_bytes(fmt, n, k));
@@ -131,6 +159,10 @@ int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image
 int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* blocks) {
   int st = check_pack_args(fmt, image, n, k, blocks);
   if (st) return st;
+  if (fmt == QG_FMT_F16) {
+    f16_pack_host((uint16_t*)blocks, n, k, (uint16_t*)image, true);
+    return ok();
+  }
   const uint8_t* src = (const uint8_t*)image;
   uint8_t* dst = (uint8_t*)blocks;
   const int64_t kb = kb_of(k), kbp = kbp_of(k);

@@ -71,6 +71,11 @@ QG_HD size_t image_total_bytes(int fmt, int64_t n, int64_t k) {
   return image_scale_offset(fmt, n, k) + align256((size_t)np_of(n) * (size_t)kbp_of(k) * 2);
 }
 
+// F16 image: 16-row tiles of 32-column steps, 1 KB per (tile, step).
+QG_HD int64_t f16_steps(int64_t k) { return (k + 31) / 32; }
+QG_HD int64_t f16_tiles(int64_t n) { return (n + 15) / 16; }
+QG_HD int64_t f16_image_bytes(int64_t n, int64_t k) { return f16_tiles(n) * f16_steps(k) * 1024; }
+
 // Byte offset of row o's part of block b (Q8_0: its low half; the high half
 // is 256 bytes further).
 QG_HD size_t cell_row_offset(int fmt, int64_t o, int64_t b, int64_t kbp) {

@@ -60,6 +60,7 @@ _SIGS = {
                              C.c_size_t, C.c_void_p]),
     "qgemv_q4_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                              C.c_size_t, C.c_void_p]),
+    "qg_f16_image": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
     "gemv_f16": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
     "qgemv_set": (C.c_int, [C.c_int, C.POINTER(_Proj), C.c_int, C.c_int, C.c_void_p]),
     "qg_prepare_rows_set": (C.c_int, [C.POINTER(_Act), C.c_int, C.c_int, C.c_void_p]),
@@ -136,8 +137,13 @@ def grouped_workspace_bytes(x_rows, k, m):
 
 
 def pack_image(fmt, blocks, n, k):
-    """Canonical blocks (numpy uint8) -> device-layout image bytes (numpy uint8)."""
-    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    """Canonical blocks (numpy uint8; F16: the [n][k] halfwords, any 16-bit dtype) -> device-layout image
+    bytes (numpy uint8)."""
+    if fmt == F16:
+        blocks = np.ascontiguousarray(blocks).view(np.uint16)
+        if blocks.shape != (n, k):
+            raise ValueError(f"F16 weights must be [{n}][{k}] halfwords")
+    blocks = np.ascontiguousarray(blocks).view(np.uint8) if fmt == F16 else np.ascontiguousarray(blocks, dtype=np.uint8)
     out = np.empty(image_bytes(fmt, n, k), np.uint8)
     _check(lib().qg_pack_image(fmt, blocks.ctypes.data_as(C.c_void_p), n, k, out.ctypes.data_as(C.c_void_p)))
     return out
@@ -145,7 +151,7 @@ def pack_image(fmt, blocks, n, k):
 
 def unpack_image(fmt, image, n, k):
     image = np.ascontiguousarray(image, dtype=np.uint8)
-    out = np.empty((n, k // 32, 34 if fmt == Q8_0 else 18), np.uint8)
+    out = np.empty((n, k), np.uint16) if fmt == F16 else np.empty((n, k // 32, 34 if fmt == Q8_0 else 18), np.uint8)
     _check(lib().qg_unpack_image(fmt, image.ctypes.data_as(C.c_void_p), n, k, out.ctypes.data_as(C.c_void_p)))
     return out
 
@@ -217,16 +223,25 @@ def qgemv_q4_0(image, n, k, x, y=None, ws=None):
     return _qgemv(lib().qgemv_q4_0, image, n, k, x, y, ws)
 
 
-def gemv_f16(w16, x, y=None):
+def f16_image(w16, out=None):
+    """The F16 image (qg_f16_image) of a row-major [n][k] halfword device matrix."""
     _dev(w16, None, "w16")
     if w16.dtype not in (torch.float16, torch.int16, torch.uint16):
         raise ValueError("w16 must hold fp16 bits")
-    _dev(x, torch.float32, "x")
     n, k = w16.shape
+    if out is None:
+        out = torch.empty(max(1, image_bytes(F16, n, k)), dtype=torch.uint8, device=w16.device)
+    _check(lib().qg_f16_image(_p(w16), n, k, _p(out), _stream()))
+    return out
+
+
+def gemv_f16(image, n, k, x, y=None):
+    """f16 lane: y [rows][n] from the F16 image of W [n][k] and x [rows][k] fp32."""
+    _dev(x, torch.float32, "x")
     rows = x.shape[0]
     if y is None:
         y = torch.empty((rows, n), dtype=torch.float32, device=x.device)
-    _check(lib().gemv_f16(_p(w16), n, k, _p(x), rows, _p(y), _stream()))
+    _check(lib().gemv_f16(_p(image), n, k, _p(x), rows, _p(y), _stream()))
     return y
 
 
@@ -304,7 +319,7 @@ def moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared):
     return lib().qg_moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, int(shared))
 
 
-def moe_step_fused(x, router16, n_experts, topk, gu_images, down_images, ffn, shared=True, ws=None):
+def moe_step_fused(x, router_image, n_experts, topk, gu_images, down_images, ffn, shared=True, ws=None):
     """The routed MoE step of moe_step in six launches (qg_moe_step).  Returns y and the routing
     (expert, weight) as [rows * slots] tensors, and the router logits."""
     _dev(x, torch.float32, "x")
@@ -318,7 +333,7 @@ def moe_step_fused(x, router16, n_experts, topk, gu_images, down_images, ffn, sh
     if ws is None:
         ws = torch.empty(max(1, moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared)), dtype=torch.uint8,
                          device=dev)
-    _check(lib().qg_moe_step(_p(router16), n_experts, hidden, ffn, topk, int(shared), _p(gu_images), _p(down_images),
+    _check(lib().qg_moe_step(_p(router_image), n_experts, hidden, ffn, topk, int(shared), _p(gu_images), _p(down_images),
                              _p(x), rows, _p(y), _p(logits), _p(expert), _p(weight), _p(ws), ws.numel(), _stream()))
     return y, (expert, weight), logits
 
@@ -342,10 +357,10 @@ def blockdots(fmt, image, n, k, qx):
 
 
 # ------------------------------------------------------------- MoE step ---
-def moe_step(x, router16, n_experts, topk, gu_images, down_images, ffn, shared_expert=None):
+def moe_step(x, router_image, n_experts, topk, gu_images, down_images, ffn, shared_expert=None):
     """Routed MoE decode step, composed of library calls only.
 
-    router16: fp16 [n_experts][hidden]; gu_images: n_experts (+1 shared) stacked Q8_0
+    router_image: F16 image of the fp16 [n_experts][hidden] router; gu_images: n_experts (+1 shared) stacked Q8_0
     images of [2*ffn][hidden] (gate rows, then up rows); down_images: the same
     experts' [hidden][ffn] images.  The shared expert, if given, is the stacked
     index `shared_expert` and joins every row with weight 1.
@@ -353,7 +368,7 @@ def moe_step(x, router16, n_experts, topk, gu_images, down_images, ffn, shared_e
     """
     rows, hidden = x.shape
     n_images = n_experts + (1 if shared_expert is not None else 0)
-    logits = gemv_f16(router16, x)
+    logits = gemv_f16(router_image, n_experts, hidden, x)
     expert, x_index, weight = moe_route(logits, topk, -1 if shared_expert is None else shared_expert)
     m = expert.numel()
     gu, _ = qgemv_q8_0_grouped(gu_images, n_images, 2 * ffn, hidden, x, expert, x_index)

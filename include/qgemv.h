@@ -40,6 +40,15 @@
  * for n % 16 == 0 and k % 512 == 0 the image holds exactly the canonical bytes
  * per weight.
  *
+ * F16 image.  The f16 lane reads halfword weights from an image too, made by
+ * qg_f16_image (device) or qg_pack_image(QG_FMT_F16, ...) (host) from the
+ * row-major [n][k] halfword matrix: rows in tiles of 16, columns in steps of
+ * 32; tile t, step s is one 1 KB block whose 16-byte chunk l = i + 16*j holds
+ * w[16t + i][32s + 8j .. 32s + 8j + 7] (j = 0..3), steps of a tile in order,
+ * tiles in order, rows past n and columns past k zero.  That is the operand
+ * order of the matrix core's 16x16x32 halfword product, so one wave load is
+ * 1 KB of consecutive bytes.  Size: ceil(n/16) * ceil(k/32) * 1024 bytes.
+ *
  * Conventions.
  *   - Pointers are device pointers unless marked (host).  `stream` is a
  *     hipStream_t (NULL = the null stream).  Device calls enqueue work on
@@ -93,16 +102,17 @@ enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3 };
 
 /* ------------------------------------------------------------ host only --- */
 
-/* Bytes of the device image of an n x k matrix in `fmt` (Q8_0, Q4_0: padded
- * layout above; F16: 2*n*k).  Returns 0 for an invalid format or shape. */
+/* Bytes of the device image of an n x k matrix in `fmt` (Q8_0, Q4_0, F16:
+ * the padded layouts above).  Returns 0 for an invalid format or shape. */
 size_t qg_image_bytes(int fmt, int64_t n, int64_t k);
 
 /* Host -> host.  Converts canonical blocks (Q8_0 / Q4_0, n * k/32 blocks, row
- * major) to the device layout in `image` (qg_image_bytes bytes, host memory;
- * copy it to the device afterwards).  Pad blocks are written as zeros. */
+ * major; F16: the row-major [n][k] halfwords, k % 8 == 0) to the device
+ * layout in `image` (qg_image_bytes bytes, host memory; copy it to the device
+ * afterwards).  Padding is written as zeros. */
 int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image);
 
-/* Host -> host inverse of qg_pack_image (pad blocks are dropped). */
+/* Host -> host inverse of qg_pack_image (padding is dropped). */
 int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* blocks);
 
 /* Bytes of the workspace that holds `rows` quantized activation rows of
@@ -147,9 +157,17 @@ int qgemv_q8_0(const void* w_image, int64_t n, int64_t k, const float* x, int ro
 int qgemv_q4_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
                size_t ws_bytes, qg_stream stream);
 
-/* f16 lane: y [rows][n] = w [n][k] (fp16, row major) . x [rows][k] (fp32),
- * fp32 accumulation, x kept in fp32. */
-int gemv_f16(const uint16_t* w, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream);
+/* Device -> device: the F16 image (qg_image_bytes(QG_FMT_F16, n, k) bytes,
+ * 256-byte aligned) of the row-major [n][k] halfword matrix w (16-byte
+ * aligned, k % 8 == 0). */
+int qg_f16_image(const uint16_t* w, int64_t n, int64_t k, void* image, qg_stream stream);
+
+/* f16 lane: y [rows][n] = W [n][k] (fp16, as the F16 image w_image) . x
+ * [rows][k] (fp32), fp32 products and sums; x enters the halfword products as
+ * two halfword terms per value (about 22 significant bits, scaled by a power
+ * of two per row and k range), so the result is fp32-accurate.  A row's bits
+ * do not depend on the other rows of the call. */
+int gemv_f16(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream);
 
 /* Several independent q8-lane projections with the same row count in one
  * launch (a decode layer's Q/K/V/O/gate/up/down).  Each entry's rows must
@@ -226,7 +244,8 @@ int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int
                    qg_stream stream);
 
 /* A routed-MoE decode step in six launches, the composition of the calls
- * above: router logits (f16 lane, n_experts x hidden), routing as
+ * above: router logits (f16 lane: router_image is the F16 image of the
+ * n_experts x hidden router), routing as
  * qg_moe_route, grouped gate/up GEMV, SwiGLU quantized for the down
  * projection, grouped down GEMV, weighted combine.  gu_images holds
  * n_experts + shared Q8_0 images of [2*ffn][hidden] (gate rows, then up rows)
@@ -240,7 +259,7 @@ int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int
  * The step follows the routed feed-forward of the llama-leg page's routed-slot
  * commit 2243ccc and the drama page's MoE series commits. */
 size_t qg_moe_workspace_bytes(int rows, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared);
-int qg_moe_step(const uint16_t* router, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
+int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
                 const void* gu_images, const void* down_images, const float* x, int rows, float* y, float* logits,
                 int32_t* expert, float* weight, void* ws, size_t ws_bytes, qg_stream stream);
 

@@ -38,6 +38,8 @@ def test_sizes():
     assert q.image_bytes(q.F16, 128256, 4096) == 1050673152
     assert q.image_bytes(q.Q8_0, 1024, 1000) == 0  # k not a multiple of 32
     assert q.image_bytes(q.F16, 8, 12) == 0
+    # F16 image: 16-row tiles x 32-column steps, 1 KB each, padded with zeros
+    assert q.image_bytes(q.F16, 33, 104) == 3 * 4 * 1024
     assert q.image_bytes(7, 8, 32) == 0
     # a ragged k is padded to whole 16-block groups
     assert q.image_bytes(q.Q8_0, 3, 96) >= 3 * 512 // 32 * 34
@@ -91,6 +93,22 @@ def test_pack_layout_of_one_q4_block():
     assert list(img[cell:cell + 16]) == list(np.arange(16) * 17)
 
 
+@pytest.mark.parametrize("n,k", [(16, 32), (33, 104), (5, 8), (40, 200)])
+def test_f16_image_layout(n, k):
+    # chunk l = i + 16*j of (tile t, step s) holds w[16t + i][32s + 8j : 32s + 8j + 8]: the zero-padded
+    # matrix cut into [t][i][s][j][8] and reordered to [t][s][j][i][8]
+    rng = np.random.default_rng(n * 1000 + k)
+    w = rng.integers(0, 1 << 16, size=(n, k), dtype=np.uint64).astype(np.uint16)
+    T, S = -(-n // 16), -(-k // 32)
+    pad = np.zeros((T * 16, S * 32), np.uint16)
+    pad[:n, :k] = w
+    want = pad.reshape(T, 16, S, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    img = q.pack_image(q.F16, w, n, k)
+    assert img.size == q.image_bytes(q.F16, n, k) == want.size * 2
+    assert np.array_equal(img.view(np.uint16), want)
+    assert np.array_equal(q.unpack_image(q.F16, img, n, k), w)
+
+
 def _status(fn, *args):
     L = q.lib()
     st = getattr(L, fn)(*args)
@@ -121,6 +139,14 @@ def test_validation_refuses_before_any_hip_call():
     assert st == -5 and "ws_bytes=100" in msg
     st, msg = _status("gemv_f16", V(A), 64, 12, V(A), 1, V(A), None)
     assert st == -2
+    st, msg = _status("gemv_f16", V(A + 16), 64, 64, V(A), 1, V(A), None)
+    assert st == -4 and "w_image" in msg
+    st, msg = _status("qg_f16_image", V(A), 64, 12, V(A), None)
+    assert st == -2 and "k=12" in msg
+    st, msg = _status("qg_f16_image", V(A + 8), 64, 64, V(A), None)
+    assert st == -4 and "w " in msg
+    st, msg = _status("qg_f16_image", V(A), 64, 64, V(A + 16), None)
+    assert st == -4 and "image" in msg
     st, msg = _status("qgemv_prepared", 9, V(A), 64, 64, V(A), 1, V(A), None)
     assert st == -1 and "fmt=9" in msg
     st, msg = _status("qgemv_q8_0_grouped", V(A), 8, 64, 64, V(A), 1, V(A), V(A), q.MAX_ASSIGN + 1, V(A), V(A),

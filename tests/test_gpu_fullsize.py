@@ -54,11 +54,12 @@ def test_lm_head_f16():
     log("LM head f16: weights")
     w16 = gauss((n, k), 0.02, 4, 0, device="cuda").half().view(torch.int16)
     w16_np = w16.cpu().numpy().view(np.uint16)
+    img = q.f16_image(w16)
     sel = _sample(n, 512, 2)
     for rows in (1, 8, 16):
         log(f"LM head f16 rows={rows}")
         x = gauss((rows, k), 1.0, 4, 32 + rows).numpy()
-        y = q.gemv_f16(w16, torch.from_numpy(x).cuda())
+        y = q.gemv_f16(img, n, k, torch.from_numpy(x).cuda())
         yo = O.gemv_f16_rows(w16_np, x, sel, threads=16)
         e = rel_err_f16(y.cpu().numpy()[:, sel], yo, w16_np[sel], x)
         log(f"  max rel err {e:.3e}")

@@ -34,7 +34,7 @@ def moe():
         gu_imgs.append(q.pack_image(q.Q8_0, np.concatenate([gb, ub]), 2 * FFN, HIDDEN))
         dn_imgs.append(q.pack_image(q.Q8_0, db, HIDDEN, FFN))
     log("MoE weights ready")
-    return dict(r16=r16, r16_np=r16.cpu().numpy().view(np.uint16), gate=np.stack(gate[:E]), up=np.stack(up[:E]),
+    return dict(r16=q.f16_image(r16), r16_np=r16.cpu().numpy().view(np.uint16), gate=np.stack(gate[:E]), up=np.stack(up[:E]),
                 down=np.stack(down[:E]), sg=gate[E], su=up[E], sd=down[E], down_all=down,
                 gu=torch.from_numpy(np.concatenate(gu_imgs)).cuda(),
                 dn=torch.from_numpy(np.concatenate(dn_imgs)).cuda())

@@ -162,11 +162,13 @@ def test_f16_parity(n, k):
     w = gauss((n, k), 0.02, 17, 12).numpy()
     w16, _ = O.f32_to_f16(w)
     wd = torch.from_numpy(w16.view(np.int16)).cuda()
+    img = q.f16_image(wd)
+    assert np.array_equal(img.cpu().numpy(), q.pack_image(q.F16, w16, n, k)), "device F16 image"
     worst = 0.0
     for rows in ROWS:
         log(f"gemv_f16 n={n} k={k} rows={rows}")
         x = outliers((rows, k), 1.0, 17, 32 + rows).numpy()
-        y = q.gemv_f16(wd, torch.from_numpy(x).cuda()).cpu().numpy()
+        y = q.gemv_f16(img, n, k, torch.from_numpy(x).cuda()).cpu().numpy()
         yo = O.gemv_f16(w16, x, threads=8)
         e = rel_err_f16(y, yo, w16, x)
         worst = max(worst, e)
@@ -178,11 +180,11 @@ def test_f16_parity(n, k):
 def test_f16_rows_in_a_batch_equal_rows_alone():
     n, k = 500, 2048
     w16, _ = O.f32_to_f16(gauss((n, k), 0.02, 18, 13).numpy())
-    wd = torch.from_numpy(w16.view(np.int16)).cuda()
+    img = q.f16_image(torch.from_numpy(w16.view(np.int16)).cuda())
     x = torch.from_numpy(gauss((16, k), 1.0, 18, 14).numpy()).cuda()
-    y16 = q.gemv_f16(wd, x)
+    y16 = q.gemv_f16(img, n, k, x)
     for r in range(16):
-        assert np.array_equal(bits(y16[r]), bits(q.gemv_f16(wd, x[r:r + 1].contiguous())[0]))
+        assert np.array_equal(bits(y16[r]), bits(q.gemv_f16(img, n, k, x[r:r + 1].contiguous())[0]))
 
 
 # -------------------------------------------------------------- grouped ---
