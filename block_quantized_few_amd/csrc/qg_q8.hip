@@ -323,13 +323,16 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
 // partner's, in that order.
 
 // Split of a tile's work over waves (H >= 2 means S == 4): W2 waves share a
-// wave part, each taking PPW lane-part pairs, and NT 16-row image tiles (one
-// with two row groups, whose activation fragments then take the registers).
-// About 16-32 KB of weights per wave whatever k is.
+// wave part, each taking PPW lane-part pairs, and NT 16-row image tiles that
+// share each step's activation chunk.  Two widths: narrow (more, smaller
+// tiles: more waves to hide latency) and wide (NT as large as 128 registers
+// allow: the activation chunk is loaded once per NT KB of weights, and fewer
+// tiles fit the workgroups resident at once).
 __host__ __device__ constexpr int mp_w2(int H) { return H >= 4 ? 2 : 1; }
-__host__ __device__ constexpr int mp_nt(int H, int G) { return H == 8 || G == 2 ? 1 : 2; }
-constexpr int MP_NT_MAX = 2;
-constexpr int MP_NV_MAX = 8;  // floats per lane a wave passes to the combine (NT * G * 4)
+__host__ __device__ constexpr int mp_nt(int H, int G, bool wide) {
+  return wide ? (H == 2 || H == 4 ? (G == 2 ? 2 : 4) : (G == 2 ? 1 : 2)) : (H == 8 || G == 2 ? 1 : 2);
+}
+constexpr int MP_NV_MAX = 16;  // floats per lane a wave passes to the combine (NT * G * 4)
 
 __device__ __forceinline__ float lane_xor8(float v) {
   // DPP row_ror:8 within each row of 16 lanes: lane i reads lane i ^ 8
@@ -343,8 +346,7 @@ struct MpStep {
   uint4 x[G];   // activation chunk (16 bytes)
   float dx[G];
   int ns[G];
-  uint2 w[NT];  // fp16 scales of rows 4q .. 4q+3 of the lane's block (from the staged copy)
-  int b;        // first block of the pair
+  int b;  // first block of the pair
 };
 
 template <int NT>
@@ -375,14 +377,6 @@ __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad,
   }
 }
 
-// The step's weight scales, from the wave's staged copy.
-template <int NT, int G>
-__device__ __forceinline__ void mp_load_w(MpStep<NT, G>& st, const MpAddr<NT>& ad) {
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-    st.w[t] = *reinterpret_cast<const uint2*>(ad.sl[t] + (st.b - ad.sb0) * TILE + ad.soff);
-}
-
 template <int FMT, int NT, int G, int PP, bool SEQ>
 __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, const MpStep<NT, G>& st,
                                            const MpAddr<NT>& ad, int sh) {
@@ -396,7 +390,8 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
       av.w = (av.w >> sh) & 0x0F0F0F0Fu;
     }
     const v4i a = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
-    const uint2 wv = st.w[t];
+    // fp16 scales of rows 4q .. 4q+3 of the lane's block, from the wave's staged copy
+    const uint2 wv = *reinterpret_cast<const uint2*>(ad.sl[t] + (st.b - ad.sb0) * TILE + ad.soff);
     const float dw[4] = {h2f((uint16_t)(wv.x & 0xffff)), h2f((uint16_t)(wv.x >> 16)), h2f((uint16_t)(wv.y & 0xffff)),
                          h2f((uint16_t)(wv.y >> 16))};
 #pragma unroll
@@ -424,11 +419,11 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
 
 // One MP tile: groups of S*W2 waves, each group NT 16-row image tiles; G
 // groups of eight activation rows from the pair-order workspace.
-template <int FMT, int H, int G>
-__device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity, uint16_t* scl, int sc_stride) {
+template <int FMT, int H, int G, bool WIDE>
+__device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
   constexpr bool SEQ = H == 1;
-  constexpr int W2 = mp_w2(H), NT = mp_nt(H, G);
+  constexpr int W2 = mp_w2(H), NT = mp_nt(H, G, WIDE);
   constexpr int PPW = SEQ ? 1 : H / 2 / W2;  // lane-part pairs per wave (1 or 2)
   const PartPlan& pl = ta.pl;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
@@ -437,6 +432,7 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity, uint1
   const int i = lane & 15, q = lane >> 4;
   const int64_t ntiles = np_of(ta.n) / TILE;
   const int64_t wrow0 = ta.row0 + (int64_t)g * TILE * NT;  // first row of this group's tiles
+  const int sc_stride = pl.H * pl.BS * TILE;                // fp16 scales of one tile's wave part
   MpAddr<NT> ad;
   const uint16_t* scale[NT];
 #pragma unroll
@@ -479,41 +475,25 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity, uint1
   // first two steps', so waiting for them waits for nothing else.
   ad.sb0 = s * H * pl.BS;
   const int nsv = H * pl.BS * 2;  // 16-byte pieces per tile (kbp/S blocks x 32 bytes)
-  uint4 sv[NT][2];
+  uint4 sv[NT];
 #pragma unroll
   for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int k2 = 0; k2 < 2; k2++) {
-      const int e = lane + WAVE * k2;
-      if (e < nsv) sv[t][k2] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
-    }
+    if (lane < nsv) sv[t] = ld16(scale[t] + (size_t)ad.sb0 * TILE + lane * 8);
   MpStep<NT, G> s0, s1;
   mp_load<FMT, NT, G>(s0, ad, lane, blk(0));
   mp_load<FMT, NT, G>(s1, ad, lane, blk(1));
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(ad.sl[t]));
-#pragma unroll
-    for (int k2 = 0; k2 < 2; k2++) {
-      const int e = lane + WAVE * k2;
-      if (e < nsv) dst[e] = sv[t][k2];
-    }
-    for (int e = lane + 2 * WAVE; e < nsv; e += WAVE) dst[e] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
+    if (lane < nsv) dst[lane] = sv[t];
+    for (int e = lane + WAVE; e < nsv; e += WAVE) dst[e] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
   }
-  mp_load_w(s0, ad);
-  mp_load_w(s1, ad);
   for (int j = 0; j < nsteps; j += 2) {
     mp_compute<FMT, NT, G, PPW, SEQ>(acc, 0, s0, ad, sh);
-    if (j + 2 < nsteps) {
-      mp_load<FMT, NT, G>(s0, ad, lane, blk(j + 2));
-      mp_load_w(s0, ad);
-    }
+    if (j + 2 < nsteps) mp_load<FMT, NT, G>(s0, ad, lane, blk(j + 2));
     if (j + 1 < nsteps) {
       mp_compute<FMT, NT, G, PPW, SEQ>(acc, 1, s1, ad, sh);
-      if (j + 3 < nsteps) {
-        mp_load<FMT, NT, G>(s1, ad, lane, blk(j + 3));
-        mp_load_w(s1, ad);
-      }
+      if (j + 3 < nsteps) mp_load<FMT, NT, G>(s1, ad, lane, blk(j + 3));
     }
   }
   // the wave's pairs by the lane-part tree: (h + h^1) across lanes i, i^8, then pair + pair
@@ -534,31 +514,33 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, int parity, uint1
   // then the W2 pair groups of a wave part (the tree's upper level), then wave parts left to right
   if (gw > 1) {
     constexpr int NV = NT * G * 4;
-    float* rb = red + parity * (WAVES * WAVE * MP_NV_MAX);
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
       for (int gg = 0; gg < G; gg++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) rb[(wave * NV + (t * G + gg) * 4 + v) * WAVE + lane] = res[t][gg][v];
+        for (int v = 0; v < 4; v++) red[(wave * NV + (t * G + gg) * 4 + v) * WAVE + lane] = res[t][gg][v];
     __syncthreads();
-    if (wg != 0) return;
+    if (wg == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; t++)
+      for (int t = 0; t < NT; t++)
 #pragma unroll
-      for (int gg = 0; gg < G; gg++)
+        for (int gg = 0; gg < G; gg++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-          const int o = ((t * G + gg) * 4 + v) * WAVE + lane;
-          const int w0 = g * gw;
-          float x = 0.0f;
-          for (int s2 = 0; s2 < pl.S; s2++) {
-            float part = rb[(w0 + s2 * W2) * NV * WAVE + o];
-            if (W2 == 2) part = part + rb[(w0 + s2 * W2 + 1) * NV * WAVE + o];
-            x = s2 == 0 ? part : x + part;
+          for (int v = 0; v < 4; v++) {
+            const int o = ((t * G + gg) * 4 + v) * WAVE + lane;
+            const int w0 = g * gw;
+            float x = 0.0f;
+            for (int s2 = 0; s2 < pl.S; s2++) {
+              float part = red[(w0 + s2 * W2) * NV * WAVE + o];
+              if (W2 == 2) part = part + red[(w0 + s2 * W2 + 1) * NV * WAVE + o];
+              x = s2 == 0 ? part : x + part;
+            }
+            res[t][gg][v] = x;
           }
-          res[t][gg][v] = x;
-        }
+    }
+    __syncthreads();  // the combine area is free for the next tile
+    if (wg != 0) return;
   }
   if (i < 8) {
 #pragma unroll
@@ -653,26 +635,23 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q
   }
 }
 
-template <int FMT, int G>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp_set_kernel(SetArgs a, int R,
-                                                                                           int sc_stride) {
+template <int FMT, int G, bool WIDE>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp_set_kernel(SetArgs a, int R) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
-  float* red = reinterpret_cast<float*>(lds);
-  uint16_t* scl = reinterpret_cast<uint16_t*>(lds + 2 * WAVES * WAVE * MP_NV_MAX * 4);
-  int parity = 0;
+  float* red = reinterpret_cast<float*>(lds);  // combine area, then the waves' staged scales
+  uint16_t* scl = reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4);
   for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
     int p = 0, t0 = tile;
     while (p + 1 < a.count && t0 >= a.p[p].tiles) t0 -= a.p[p++].tiles;
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, 0);
     const PartPlan& pl = d.pl;
-    if (pl.H == 1) mp_tile<FMT, 1, G>(ta, R, red, parity, scl, sc_stride);
-    else if (pl.H == 2) mp_tile<FMT, 2, G>(ta, R, red, parity, scl, sc_stride);
-    else if (pl.H == 4) mp_tile<FMT, 4, G>(ta, R, red, parity, scl, sc_stride);
-    else mp_tile<FMT, 8, G>(ta, R, red, parity, scl, sc_stride);
-    if (pl.S > 1) parity ^= 1;
+    if (pl.H == 1) mp_tile<FMT, 1, G, WIDE>(ta, R, red, scl);
+    else if (pl.H == 2) mp_tile<FMT, 2, G, WIDE>(ta, R, red, scl);
+    else if (pl.H == 4) mp_tile<FMT, 4, G, WIDE>(ta, R, red, scl);
+    else mp_tile<FMT, 8, G, WIDE>(ta, R, red, scl);
   }
 }
 
@@ -812,7 +791,7 @@ int device_cus() {
 // loop over the remaining tiles) and no more than there are tiles.
 template <typename K>
 static unsigned persistent_grid(K kernel, size_t lds, int64_t tiles) {
-  if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds > 48 * 1024) hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WG, lds) != hipSuccess || per_cu < 1) per_cu = 1;
   const int64_t g = (int64_t)device_cus() * per_cu;
@@ -839,17 +818,40 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
   else launch_rl<FMT, 2, false>(a, lds_x, s);
 }
 
-template <int FMT, int G>
-static void launch_mp(const SetArgs& a, int rows, hipStream_t s) {
-  auto kern = mp_set_kernel<FMT, G>;
-  // combine area (two parities), then each wave's staged scales: NT tiles of kbp/S blocks x 16 fp16
-  int sc_stride = 0;
+// Tiles of the pair kernel at width `wide`; returns the LDS bytes it needs
+// (combine area, then each wave's staged scales: NT tiles of kbp/S blocks x
+// 16 fp16).
+static size_t mp_fill(SetArgs& a, int G, bool wide) {
+  int64_t tiles = 0;
+  size_t sc = 0;
   for (int i = 0; i < a.count; i++) {
-    const int v = a.p[i].kbp / a.p[i].pl.S * TILE;
-    sc_stride = v > sc_stride ? v : sc_stride;
+    ProjDev& d = a.p[i];
+    const int nt = mp_nt(d.pl.H, G, wide);
+    d.rows_per_tile = (WAVES / (d.pl.S * mp_w2(d.pl.H))) * TILE * nt;
+    d.tiles = (int)((d.n + d.rows_per_tile - 1) / d.rows_per_tile);
+    tiles += d.tiles;
+    const size_t v = (size_t)nt * (d.kbp / d.pl.S) * TILE * 2;
+    sc = v > sc ? v : sc;
   }
-  const size_t lds = 2 * WAVES * WAVE * MP_NV_MAX * 4 + (size_t)WAVES * MP_NT_MAX * sc_stride * 2;
-  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, rows, sc_stride);
+  a.total_tiles = (int)tiles;
+  return (size_t)WAVES * WAVE * MP_NV_MAX * 4 + WAVES * sc;
+}
+
+// The pair kernel runs in rounds of the workgroups resident at once; a round
+// costs about a tile's latency chain.  Wide tiles win when they need fewer
+// rounds at 9-16 rows (half the activation-chunk loads), and at 3-8 rows
+// when they fit one round that narrow tiles overflow.
+template <int FMT, int G>
+static void launch_mp(SetArgs a, int rows, hipStream_t s) {
+  auto kn = mp_set_kernel<FMT, G, false>;
+  auto kw = mp_set_kernel<FMT, G, true>;
+  SetArgs aw = a;
+  const size_t ln = mp_fill(a, G, false), lw = mp_fill(aw, G, true);
+  const unsigned gn = persistent_grid(kn, ln, a.total_tiles), gw = persistent_grid(kw, lw, aw.total_tiles);
+  const int64_t rn = (a.total_tiles + gn - 1) / gn, rw = (aw.total_tiles + gw - 1) / gw;
+  const bool wide = G == 2 ? rw < rn : (rn > 1 && rw == 1);
+  if (wide) hipLaunchKernelGGL(kw, dim3(gw), dim3(WG), lw, s, aw, rows);
+  else hipLaunchKernelGGL(kn, dim3(gn), dim3(WG), ln, s, a, rows);
 }
 
 int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStream_t s) {
@@ -886,7 +888,7 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
     d.kbp = (int)kbp_of(pa.k);
     const PartPlan pl = part_plan(d.kbp);
     d.pl = pl;
-    d.rows_per_tile = mf ? (WAVES / (pl.S * mp_w2(pl.H))) * TILE * mp_nt(pl.H, rows > 8 ? 2 : 1) : WG / pl.P;
+    d.rows_per_tile = WG / pl.P;  // RL tiles; the pair kernel sets its own
     d.tiles = (int)((pa.n + d.rows_per_tile - 1) / d.rows_per_tile);
     tiles += d.tiles;
     const size_t x = (size_t)rows * d.kbp * x_block_bytes(fmt);

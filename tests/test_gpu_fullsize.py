@@ -76,11 +76,14 @@ def _layer(fmt, ofmt, layer, wl):
     return blocks, imgs
 
 
-def _run_set(fmt, ofmt, layer, blocks, imgs, rows, wl, full):
+def _run_set(fmt, ofmt, layer, blocks, imgs, rows, wl, full, xin=None, check=True):
     k_in, k_dn = layer[0][2], layer[6][2]
-    x_in = gauss((rows, k_in), 1.0, wl, 32 + rows).numpy()
-    x_o = gauss((rows, k_in), 1.0, wl, 48 + rows).numpy()
-    x_dn = gauss((rows, k_dn), 1.0, wl, 64 + rows).numpy()
+    if xin is None:
+        x_in = gauss((rows, k_in), 1.0, wl, 32 + rows).numpy()
+        x_o = gauss((rows, k_in), 1.0, wl, 48 + rows).numpy()
+        x_dn = gauss((rows, k_dn), 1.0, wl, 64 + rows).numpy()
+    else:
+        x_in, x_o, x_dn = xin
     xs = [torch.from_numpy(a).cuda() for a in (x_in, x_o, x_dn)]
     wss = [q.empty_ws(rows, a.shape[1]) for a in xs]
     q.prepare_rows_set(xs, wss)
@@ -93,23 +96,40 @@ def _run_set(fmt, ofmt, layer, blocks, imgs, rows, wl, full):
         projs.append((imgs[i], n, k, wss[j], y))
     q.qgemv_set(fmt, projs, rows)
     for i, (name, n, k) in enumerate(layer):
+        if not check:
+            break
         y, x = outs[i]
         sel = np.arange(n) if full else _sample(n, 256, i)
         yo = O.gemv_q_rows(ofmt, blocks[i], n, k, x, sel, threads=16)
         e = rel_err(y.cpu().numpy()[:, sel], yo, blocks[i], ofmt, x, sel=sel)
         log(f"  {name} {n}x{k} rows={rows} max rel err {e:.3e}")
         assert e <= TOL
+    return [y for y, _ in outs], (x_in, x_o, x_dn)
+
+
+def _rows_alone(fmt, ofmt, layer, blocks, imgs, ys, xin, wl, which):
+    """Rows of a full-size batch (its tiling and kernel chosen for that row count) have the bits of the
+    same rows computed alone (the one-row kernel)."""
+    for r in which:
+        one = tuple(np.ascontiguousarray(a[r:r + 1]) for a in xin)
+        y1, _ = _run_set(fmt, ofmt, layer, blocks, imgs, 1, wl, False, xin=one, check=False)
+        for i, (name, n, k) in enumerate(layer):
+            assert np.array_equal(bits(ys[i][r]), bits(y1[i][0])), f"{name} row {r}"
 
 
 def test_llama1b_layer_q8_0_set():
     blocks, imgs = _layer(q.Q8_0, O.Q8_0, LAYER_1B, 1)
     for rows in (1, 16):
         log(f"1B layer Q8_0 rows={rows}")
-        _run_set(q.Q8_0, O.Q8_0, LAYER_1B, blocks, imgs, rows, 1, full=rows == 1)
+        ys, xin = _run_set(q.Q8_0, O.Q8_0, LAYER_1B, blocks, imgs, rows, 1, full=rows == 1)
+    log("1B layer Q8_0: rows 0 and 15 of 16 alone")
+    _rows_alone(q.Q8_0, O.Q8_0, LAYER_1B, blocks, imgs, ys, xin, 1, (0, 15))
 
 
 def test_llama3b_layer_q4_0_set():
     blocks, imgs = _layer(q.Q4_0, O.Q4_0, LAYER_3B, 2)
     for rows in (1, 2, 4, 8):
         log(f"3B layer Q4_0 rows={rows}")
-        _run_set(q.Q4_0, O.Q4_0, LAYER_3B, blocks, imgs, rows, 2, full=False)
+        ys, xin = _run_set(q.Q4_0, O.Q4_0, LAYER_3B, blocks, imgs, rows, 2, full=False)
+    log("3B layer Q4_0: rows 0 and 7 of 8 alone")
+    _rows_alone(q.Q4_0, O.Q4_0, LAYER_3B, blocks, imgs, ys, xin, 2, (0, 7))
