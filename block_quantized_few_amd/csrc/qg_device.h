@@ -99,4 +99,40 @@ __device__ __forceinline__ void quantize_quarter(const float (&v)[8], unsigned& 
   block_sum = s;
 }
 
+// Work items of a grouped GEMV of at most this many rows run in the
+// small-item kernel (few registers, many workgroups per CU); larger ones in
+// the kernel built for up to 16 rows.
+constexpr int GROUPED_SMALL_ROWS = 2;
+
+// The last step of a grouped plan (one workgroup, every thread calls it):
+// work item it < ni is (s_ie[it], s_is[it], s_ic[it]) = (expert, first sorted
+// position, rows).  The items go to `items` with those of at most
+// GROUPED_SMALL_ROWS rows first (in no fixed order within a class: each
+// item's outputs are its own); header[0] and header[2] receive the item count
+// and the small-item count.  s_slot: LDS scratch of ni ints; s_cnt: two LDS
+// ints.
+__device__ inline void store_items_small_first(const int* s_ie, const int* s_is, const int* s_ic, int ni, int* s_slot,
+                                               int* s_cnt, int* __restrict__ items, int* __restrict__ header) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid == 0) s_cnt[0] = s_cnt[1] = 0;
+  __syncthreads();
+  for (int it = tid; it < ni; it += nt) {
+    const bool small = s_ic[it] <= GROUPED_SMALL_ROWS;
+    const int c = atomicAdd(&s_cnt[small ? 0 : 1], 1);
+    s_slot[it] = small ? c : -1 - c;
+  }
+  __syncthreads();
+  const int nsmall = s_cnt[0];
+  for (int it = tid; it < ni; it += nt) {
+    const int sl = s_slot[it], dst = sl >= 0 ? sl : nsmall - 1 - sl;
+    items[3 * dst] = s_ie[it];
+    items[3 * dst + 1] = s_is[it];
+    items[3 * dst + 2] = s_ic[it];
+  }
+  if (tid == 0) {
+    header[0] = ni;
+    header[2] = nsmall;
+  }
+}
+
 }  // namespace qg

@@ -92,6 +92,8 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
   __shared__ int s_start[QG_MOE_MAX_M];
   __shared__ int s_pos[QG_MOE_MAX_M];
   __shared__ float s_w[QG_MOE_MAX_M];
+  __shared__ int s_ie[QG_MOE_MAX_M], s_is[QG_MOE_MAX_M], s_ic[QG_MOE_MAX_M];  // work items
+  __shared__ int s_cnt[2];
   const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
   const int slots = topk + (shared_expert >= 0 ? 1 : 0);
   const int m = rows * slots;
@@ -131,15 +133,14 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
     if (tid == 0 || s_start[tid - 1] != s_start[tid]) {
       int cnt = 1;
       while (tid + cnt < m && s_start[tid + cnt] == s_start[tid]) cnt++;
-      items[3 * item] = s_e[s_pos[tid]];
-      items[3 * item + 1] = tid;
-      items[3 * item + 2] = cnt;
+      s_ie[item] = s_e[s_pos[tid]];
+      s_is[item] = tid;
+      s_ic[item] = cnt;
     }
   }
-  if (tid == 0) {
-    header[0] = m ? s_start[m - 1] : 0;
-    header[1] = 0;
-  }
+  if (tid == 0) header[1] = 0;
+  __syncthreads();
+  store_items_small_first(s_ie, s_is, s_ic, m ? s_start[m - 1] : 0, s_pos, s_cnt, items, header);
   // A1 of the input rows, row order: four lanes per 32-block
   const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
   for (int e = tid; e < rows * kbp * 4; e += nt) {  // rows * kbp * 4 is a multiple of 64: quads stay whole

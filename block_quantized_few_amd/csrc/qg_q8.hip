@@ -360,14 +360,30 @@ struct MpAddr {
   const uint16_t* sl[NT];   // the wave's staged scales of each tile (LDS), from block sb0 on
   int sb0;
   uint32_t soff;            // lane offset in a staged block pair (fp16 units)
+  // Gathered row order (rows picked by the tile's s_src map): this lane's
+  // element (row * kbp + its block's offset in the pair) per row group, and
+  // whether its bytes meet its column's block (else they are zero).
+  int64_t gsrc[2];
+  int ghalf;  // 0 or 16: the half of the block's codes
+  bool gon;
 };
 
-template <int FMT, int NT, int G>
+template <int FMT, int NT, int G, bool GATHER>
 __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad, int lane, int b) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
 #pragma unroll
   for (int t = 0; t < NT; t++) st.a[t] = ld16_stream(ad.code[t] + (size_t)b * CB + ad.aoff);
   st.b = b;
+  if (GATHER) {
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+      const int64_t e = ad.gsrc[g] + b;
+      st.x[g] = ad.gon ? ld16(ad.xc + (size_t)e * 32 + ad.ghalf) : make_uint4(0u, 0u, 0u, 0u);
+      st.dx[g] = ad.xd[e];
+      st.ns[g] = FMT == FMT_Q4 ? ad.xn[e] : 0;
+    }
+    return;
+  }
   const size_t chunk0 = (size_t)(b >> 1) * ad.groups;
 #pragma unroll
   for (int g = 0; g < G; g++) {
@@ -418,12 +434,13 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
 }
 
 // One MP tile: groups of S*W2 waves, each group NT 16-row image tiles; G
-// groups of eight activation rows from the pair-order workspace.
-template <int FMT, int H, int G, bool WIDE>
+// groups of eight activation rows from the pair-order workspace, or (GATHER)
+// from a row-order workspace through the tile's s_src map.
+template <int FMT, int H, int G, int NT, bool GATHER>
 __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
   constexpr bool SEQ = H == 1;
-  constexpr int W2 = mp_w2(H), NT = mp_nt(H, G, WIDE);
+  constexpr int W2 = mp_w2(H);
   constexpr int PPW = SEQ ? 1 : H / 2 / W2;  // lane-part pairs per wave (1 or 2)
   const PartPlan& pl = ta.pl;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
@@ -449,6 +466,15 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
   ad.xd = ta.prep.dx;
   ad.xn = ta.prep.nsx;
   ad.groups = (R + 7) >> 3;
+  if (GATHER) {
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+      const int ar = min(gg * 8 + (i & 7), R - 1);  // columns past R read a real row, store nothing
+      ad.gsrc[gg] = (int64_t)ta.s_src[ar] * ta.kbp + (i >> 3);
+    }
+    ad.ghalf = (q & 1) * 16;
+    ad.gon = (i < 8) == (q < 2);
+  }
   const int sh = (q & 1) * 4;
 
   const int BS = pl.BS;
@@ -480,8 +506,8 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
   for (int t = 0; t < NT; t++)
     if (lane < nsv) sv[t] = ld16(scale[t] + (size_t)ad.sb0 * TILE + lane * 8);
   MpStep<NT, G> s0, s1;
-  mp_load<FMT, NT, G>(s0, ad, lane, blk(0));
-  mp_load<FMT, NT, G>(s1, ad, lane, blk(1));
+  mp_load<FMT, NT, G, GATHER>(s0, ad, lane, blk(0));
+  mp_load<FMT, NT, G, GATHER>(s1, ad, lane, blk(1));
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(ad.sl[t]));
@@ -490,10 +516,10 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
   }
   for (int j = 0; j < nsteps; j += 2) {
     mp_compute<FMT, NT, G, PPW, SEQ>(acc, 0, s0, ad, sh);
-    if (j + 2 < nsteps) mp_load<FMT, NT, G>(s0, ad, lane, blk(j + 2));
+    if (j + 2 < nsteps) mp_load<FMT, NT, G, GATHER>(s0, ad, lane, blk(j + 2));
     if (j + 1 < nsteps) {
       mp_compute<FMT, NT, G, PPW, SEQ>(acc, 1, s1, ad, sh);
-      if (j + 3 < nsteps) mp_load<FMT, NT, G>(s1, ad, lane, blk(j + 3));
+      if (j + 3 < nsteps) mp_load<FMT, NT, G, GATHER>(s1, ad, lane, blk(j + 3));
     }
   }
   // the wave's pairs by the lane-part tree: (h + h^1) across lanes i, i^8, then pair + pair
@@ -648,10 +674,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, 0);
     const PartPlan& pl = d.pl;
-    if (pl.H == 1) mp_tile<FMT, 1, G, WIDE>(ta, R, red, scl);
-    else if (pl.H == 2) mp_tile<FMT, 2, G, WIDE>(ta, R, red, scl);
-    else if (pl.H == 4) mp_tile<FMT, 4, G, WIDE>(ta, R, red, scl);
-    else mp_tile<FMT, 8, G, WIDE>(ta, R, red, scl);
+    if (pl.H == 1) mp_tile<FMT, 1, G, mp_nt(1, G, WIDE), false>(ta, R, red, scl);
+    else if (pl.H == 2) mp_tile<FMT, 2, G, mp_nt(2, G, WIDE), false>(ta, R, red, scl);
+    else if (pl.H == 4) mp_tile<FMT, 4, G, mp_nt(4, G, WIDE), false>(ta, R, red, scl);
+    else mp_tile<FMT, 8, G, mp_nt(8, G, WIDE), false>(ta, R, red, scl);
   }
 }
 
@@ -666,7 +692,8 @@ __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __res
   __shared__ int s_e[QG_MAX_ASSIGN];
   __shared__ int s_pos[QG_MAX_ASSIGN];  // sorted position -> assignment
   __shared__ int s_start[QG_MAX_ASSIGN];  // 1 where a work item starts
-  __shared__ int s_bad, s_valid;
+  __shared__ int s_ie[QG_MAX_ASSIGN], s_is[QG_MAX_ASSIGN], s_ic[QG_MAX_ASSIGN];  // work items
+  __shared__ int s_bad, s_valid, s_cnt[2];
   const int tid = threadIdx.x, nt = blockDim.x;
   if (tid == 0) {
     s_bad = 0;
@@ -709,15 +736,14 @@ __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __res
     if (first) {
       int cnt = 1;
       while (p + cnt < nv && s_start[p + cnt] == s_start[p]) cnt++;
-      items[3 * item] = s_e[s_pos[p]];
-      items[3 * item + 1] = p;
-      items[3 * item + 2] = cnt;
+      s_ie[item] = s_e[s_pos[p]];
+      s_is[item] = p;
+      s_ic[item] = cnt;
     }
   }
-  if (tid == 0) {
-    header[0] = nv ? s_start[nv - 1] : 0;
-    header[1] = s_bad;
-  }
+  if (tid == 0) header[1] = s_bad;
+  __syncthreads();
+  store_items_small_first(s_ie, s_is, s_ic, nv ? s_start[nv - 1] : 0, s_pos, s_cnt, items, header);
 }
 
 template <int R>
@@ -726,49 +752,109 @@ __device__ __forceinline__ void grouped_rows(TileArgs ta, uint8_t* lds, float* r
   rl_tile<FMT_Q8, R, false>(ta, lds, red, 0, true);
 }
 
+// Items of at most GROUPED_SMALL_ROWS rows (the plan puts them first):
+// lanes-own-rows tiles, persistent over the (item, tile) units.
 __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__ images, int64_t expert_bytes,
                                                      size_t scale_off, int64_t n, int64_t k, int kbp, PartPlan pl,
                                                      Prep prep,
                                                      const int* __restrict__ header, const int* __restrict__ sorted,
                                                      const int* __restrict__ items,
-                                                     const int32_t* __restrict__ x_index, float* y, int lds_x) {
+                                                     const int32_t* __restrict__ x_index, float* y, int lds_x,
+                                                     int tiles) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
-  const int item = blockIdx.y;
-  if (item >= header[0]) return;  // uniform over the workgroup, before any barrier
-  const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
-  if (threadIdx.x < cnt) {
-    const int a = sorted[start + threadIdx.x];
-    s_map[threadIdx.x] = x_index ? x_index[a] : a;
-    s_map[QG_MAX_ROWS + threadIdx.x] = a;
-  }
-  __syncthreads();
-  const uint8_t* img = images + (size_t)e * expert_bytes;
-  TileArgs ta;
-  ta.code = img;
-  ta.scale = reinterpret_cast<const uint16_t*>(img + scale_off);
-  ta.n = n;
-  ta.kbp = kbp;
-  ta.kb = (int)kb_of(k);
-  ta.k = k;
-  ta.row0 = (int64_t)blockIdx.x * (WG >> pl.lgP);
-  ta.prep = prep;
-  ta.xf = nullptr;
-  ta.s_src = s_map;
-  ta.y = y;
-  ta.ldy = n;
-  ta.s_dst = s_map + QG_MAX_ROWS;
-  ta.lds_x = lds_x;
-  ta.pl = pl;
-  ta.ucx = 0;  // set per row count
+  const int units = header[2] * tiles;
   float* red = reinterpret_cast<float*>(lds + lds_x);
-  switch (cnt) {
-#define QG_CASE(RR) \
-  case RR: grouped_rows<RR>(ta, lds, red); break;
-    QG_CASE(1) QG_CASE(2) QG_CASE(3) QG_CASE(4) QG_CASE(5) QG_CASE(6) QG_CASE(7) QG_CASE(8)
-    QG_CASE(9) QG_CASE(10) QG_CASE(11) QG_CASE(12) QG_CASE(13) QG_CASE(14) QG_CASE(15) QG_CASE(16)
-#undef QG_CASE
-    default: break;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {  // uniform over the workgroup
+    const int item = u / tiles, tile = u - item * tiles;
+    const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
+    __syncthreads();  // the previous unit is done with s_map and LDS
+    if (threadIdx.x < cnt) {
+      const int a = sorted[start + threadIdx.x];
+      s_map[threadIdx.x] = x_index ? x_index[a] : a;
+      s_map[QG_MAX_ROWS + threadIdx.x] = a;
+    }
+    __syncthreads();
+    const uint8_t* img = images + (size_t)e * expert_bytes;
+    TileArgs ta;
+    ta.code = img;
+    ta.scale = reinterpret_cast<const uint16_t*>(img + scale_off);
+    ta.n = n;
+    ta.kbp = kbp;
+    ta.kb = (int)kb_of(k);
+    ta.k = k;
+    ta.row0 = (int64_t)tile * (WG >> pl.lgP);
+    ta.prep = prep;
+    ta.xf = nullptr;
+    ta.s_src = s_map;
+    ta.y = y;
+    ta.ldy = n;
+    ta.s_dst = s_map + QG_MAX_ROWS;
+    ta.lds_x = lds_x;
+    ta.pl = pl;
+    ta.ucx = 0;  // set per row count
+    if (cnt == 1) grouped_rows<1>(ta, lds, red);
+    else if (cnt == 2) grouped_rows<2>(ta, lds, red);
+  }
+}
+
+// Rows of a grouped item in the pair kernel's tiles (one 16-row image tile per
+// wave group), the activation rows gathered from the row-order workspace.
+template <int G>
+__device__ __forceinline__ void grouped_mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
+  switch (ta.pl.H) {
+    case 1: mp_tile<FMT_Q8, 1, G, 1, true>(ta, R, red, scl); break;
+    case 2: mp_tile<FMT_Q8, 2, G, 1, true>(ta, R, red, scl); break;
+    case 4: mp_tile<FMT_Q8, 4, G, 1, true>(ta, R, red, scl); break;
+    default: mp_tile<FMT_Q8, 8, G, 1, true>(ta, R, red, scl); break;
+  }
+}
+
+// Rows per tile of grouped_mp_kernel.
+static inline int grouped_mp_rows(const PartPlan& pl) { return (WAVES / (pl.S * mp_w2(pl.H))) * TILE; }
+
+// Items of more than GROUPED_SMALL_ROWS rows, persistent over their (item,
+// tile) units.
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void grouped_mp_kernel(
+    const uint8_t* __restrict__ images, int64_t expert_bytes, size_t scale_off, int64_t n, int64_t k, int kbp,
+    PartPlan pl, Prep prep, const int* __restrict__ header, const int* __restrict__ sorted,
+    const int* __restrict__ items, const int32_t* __restrict__ x_index, float* y, int tiles) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_map[2 * QG_MAX_ROWS];
+  float* red = reinterpret_cast<float*>(lds);  // combine area, then the waves' staged scales
+  uint16_t* scl = reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4);
+  const int nsmall = header[2], units = (header[0] - nsmall) * tiles;
+  const int rpt = (WAVES / (pl.S * mp_w2(pl.H))) * TILE;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {  // uniform over the workgroup
+    const int item = nsmall + u / tiles, tile = u % tiles;
+    const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
+    __syncthreads();  // the previous unit is done with s_map
+    if (threadIdx.x < cnt) {
+      const int a = sorted[start + threadIdx.x];
+      s_map[threadIdx.x] = x_index ? x_index[a] : a;
+      s_map[QG_MAX_ROWS + threadIdx.x] = a;
+    }
+    __syncthreads();
+    const uint8_t* img = images + (size_t)e * expert_bytes;
+    TileArgs ta;
+    ta.code = img;
+    ta.scale = reinterpret_cast<const uint16_t*>(img + scale_off);
+    ta.n = n;
+    ta.kbp = kbp;
+    ta.kb = (int)kb_of(k);
+    ta.k = k;
+    ta.row0 = (int64_t)tile * rpt;
+    ta.prep = prep;
+    ta.xf = nullptr;
+    ta.s_src = s_map;
+    ta.y = y;
+    ta.ldy = n;
+    ta.s_dst = s_map + QG_MAX_ROWS;
+    ta.lds_x = 0;
+    ta.pl = pl;
+    ta.ucx = 0;
+    if (cnt > 8) grouped_mp_tile<2>(ta, cnt, red, scl);
+    else grouped_mp_tile<1>(ta, cnt, red, scl);
   }
 }
 
@@ -923,16 +1009,33 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
   const int kbp = (int)kbp_of(k);
   const PartPlan pl = part_plan(kbp);
   const int rpt = WG / pl.P;
-  const unsigned tiles = (unsigned)((n + rpt - 1) / rpt);
-  const size_t need = (size_t)QG_MAX_ROWS * kbp * x_block_bytes(FMT_Q8);
-  const int lds_x = (int)((need < (size_t)LDS_X_RL ? need : (size_t)LDS_X_RL) + 15) / 16 * 16;
-  const size_t lds = (size_t)lds_x + WAVES * WAVE * QG_MAX_ROWS * 4;
-  if (lds > 64 * 1024) hipFuncSetAttribute((const void*)grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int tiles = (int)((n + rpt - 1) / rpt);
   const int64_t eb = (int64_t)image_total_bytes(QG_FMT_Q8_0, n, k);
   const size_t so = image_scale_offset(QG_FMT_Q8_0, n, k);
-  hipLaunchKernelGGL(grouped_kernel, dim3(tiles, m), dim3(WG), lds, s, (const uint8_t*)images, eb, so, n, k, kbp, pl,
-                     prep_view(prep, prep_layout_rows(x_rows, k)), header, sorted, items, x_index, y, lds_x);
-  return hip_status(hipGetLastError(), "grouped_kernel");
+  const Prep pv = prep_view(prep, prep_layout_rows(x_rows, k));
+  // LDS of a class: its largest row count staged (up to the RL cap), then the combine area
+  auto lds_x_for = [&](int rows) {
+    const size_t need = (size_t)rows * kbp * x_block_bytes(FMT_Q8);
+    return (int)((need < (size_t)LDS_X_RL ? need : (size_t)LDS_X_RL) + 15) / 16 * 16;
+  };
+  // small items: at most m of them; items of more rows: at most m / (GROUPED_SMALL_ROWS + 1)
+  const int lx_s = lds_x_for(GROUPED_SMALL_ROWS);
+  const size_t lds_s = (size_t)lx_s + WAVES * WAVE * GROUPED_SMALL_ROWS * 4;
+  const unsigned gs = persistent_grid(grouped_kernel, lds_s, (int64_t)m * tiles);
+  hipLaunchKernelGGL(grouped_kernel, dim3(gs), dim3(WG), lds_s, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv,
+                     header, sorted, items, x_index, y, lx_s, tiles);
+  if (int st = hip_status(hipGetLastError(), "grouped_kernel")) return st;
+  const int mb = m / (GROUPED_SMALL_ROWS + 1);
+  if (mb > 0) {
+    const int rpt = grouped_mp_rows(pl);
+    const int tb = (int)((n + rpt - 1) / rpt);
+    const size_t lds_b = (size_t)WAVES * WAVE * MP_NV_MAX * 4 + (size_t)WAVES * (kbp / pl.S) * TILE * 2;
+    const unsigned gb = persistent_grid(grouped_mp_kernel, lds_b, (int64_t)mb * tb);
+    hipLaunchKernelGGL(grouped_mp_kernel, dim3(gb), dim3(WG), lds_b, s, (const uint8_t*)images, eb, so, n, k, kbp, pl,
+                       pv, header, sorted, items, x_index, y, tb);
+    if (int st = hip_status(hipGetLastError(), "grouped_mp_kernel")) return st;
+  }
+  return QG_OK;
 }
 
 int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
