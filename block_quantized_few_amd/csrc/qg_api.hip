@@ -339,12 +339,13 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
   if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
                                x, hidden, w + M.xprep, s))
     return st;
+  // an expert meets a row at most once (distinct top-k picks, a separate shared image): items have <= rows rows
   if (int st = launch_grouped_planned(gu_images, n_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi,
-                                      m, gu, s))
+                                      m, rows, gu, s))
     return st;
   if (int st = launch_swiglu_q8(gu, m, ffn, w + M.hprep, s)) return st;
   if (int st = launch_grouped_planned(down_images, n_images, hidden, ffn, w + M.hprep, m, header, sorted, items,
-                                      nullptr, m, o, s))
+                                      nullptr, m, rows, o, s))
     return st;
   if (int st = launch_moe_combine(o, wt, rows, slots, hidden, y, s)) return st;
   return ok();

@@ -50,9 +50,11 @@ int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, 
 // Grouped GEMV on a plan already in `ws` (header, sorted, items at the
 // grouped layout's offsets) and rows prepared at `prep` in row order;
 // x_index == nullptr: the activation row of assignment a is a.
+// max_item_rows: an upper bound on the rows of one work item (the kernel for
+// items of more than two rows is launched only when it can have work).
 int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int64_t k, const void* prep, int x_rows,
                            const int* header, const int* sorted, const int* items, const int32_t* x_index, int m,
-                           float* y, hipStream_t s);
+                           int max_item_rows, float* y, hipStream_t s);
 
 // Fused MoE pieces: routing + plan + input quantization (one workgroup), and
 // SwiGLU quantized for the down projection.

@@ -11,53 +11,114 @@ namespace qg {
 constexpr int ROUTE_MAX_E = 1024;
 constexpr int ROUTE_PER_LANE = ROUTE_MAX_E / WAVE;
 
+// Wave-wide reductions without LDS: DPP within each row of 16 lanes (pairs,
+// quads, half-row mirror, row mirror: every lane of the row ends with the
+// row's value), then the four rows' values read from lanes 0, 16, 32, 48 and
+// combined as (r0 . r1) . (r2 . r3).  Every lane gets the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+// (value, index) with the larger value, ties to the lower index (selects,
+// no branches).
+__device__ __forceinline__ void pick(float& v, int& i, float ov, int oi) {
+  const bool better = (ov > v) | ((ov == v) & (oi < i));
+  v = better ? ov : v;
+  i = better ? oi : i;
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  pick(v, i, dpp_f<CTRL>(v), dpp_i<CTRL>(i));
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<0xB1>(v, i);
+  argmax_step<0x4E>(v, i);
+  argmax_step<0x141>(v, i);
+  argmax_step<0x140>(v, i);
+  float v0 = lane_f(v, 0), v2 = lane_f(v, 32);
+  int i0 = __builtin_amdgcn_readlane(i, 0), i2 = __builtin_amdgcn_readlane(i, 32);
+  pick(v0, i0, lane_f(v, 16), __builtin_amdgcn_readlane(i, 16));
+  pick(v2, i2, lane_f(v, 48), __builtin_amdgcn_readlane(i, 48));
+  pick(v0, i0, v2, i2);
+  v = v0;
+  i = i0;
+}
+
 // Routing of one row by one wave: softmax over the E logits in fp32 (max
-// subtracted; each lane sums its experts in index order, then a fixed
-// butterfly over the lanes), and the topk experts by logit, ties to the lower
-// index, in descending order.  Lane 0 returns the picks in ex[] / wt[].
-__device__ void route_row(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
+// subtracted; each lane sums its experts in index order, then the fixed
+// wave_sum tree), and the topk experts by logit, ties to the lower index, in
+// descending order.  Lane 0 returns the picks in ex[] / wt[].  NPER: logits
+// per lane (E <= 64 * NPER).
+template <int NPER>
+__device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
   const int lane = threadIdx.x & (WAVE - 1);
-  const int nper = (E + WAVE - 1) / WAVE;
-  float l[ROUTE_PER_LANE];
+  float l[NPER];
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < ROUTE_PER_LANE; i++) {
+  for (int i = 0; i < NPER; i++) {
     const int e = lane + WAVE * i;
-    l[i] = (i < nper && e < E) ? lrow[e] : -INFINITY;
+    l[i] = e < E ? lrow[e] : -INFINITY;
     mx = fmaxf(mx, l[i]);
   }
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = wave_max(mx);
   float sum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < ROUTE_PER_LANE; i++)
-    if (i < nper && lane + WAVE * i < E) sum += expf(l[i] - mx);
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  unsigned taken = 0;
+  for (int i = 0; i < NPER; i++) {
+    const float t = expf(l[i] - mx);
+    sum += lane + WAVE * i < E ? t : 0.0f;
+  }
+  sum = wave_sum(sum);
+  unsigned avail = 0;  // bit i: entry i is a real expert not picked yet
+#pragma unroll
+  for (int i = 0; i < NPER; i++) avail |= (lane + WAVE * i < E ? 1u : 0u) << i;
   for (int k = 0; k < topk; k++) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < ROUTE_PER_LANE; i++) {
+    for (int i = 0; i < NPER; i++) {
       const int e = lane + WAVE * i;
-      if (i < nper && e < E && !(taken >> i & 1u) && (l[i] > bv || (l[i] == bv && e < bi))) {
-        bv = l[i];
-        bi = e;
-      }
+      const bool ok = (avail >> i) & 1u;
+      const bool better = ok & ((l[i] > bv) | ((l[i] == bv) & (e < bi)));
+      bv = better ? l[i] : bv;
+      bi = better ? e : bi;
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi % WAVE == lane) taken |= 1u << (bi / WAVE);
+    wave_argmax(bv, bi);
+    avail &= ~((bi % WAVE == lane ? 1u : 0u) << (bi / WAVE));
     if (lane == 0) {
       ex[k] = bi;
       wt[k] = expf(bv - mx) / sum;
     }
   }
+}
+
+__device__ __forceinline__ void route_row(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
+  if (E <= 4 * WAVE) route_row_n<4>(lrow, E, topk, ex, wt);
+  else if (E <= 8 * WAVE) route_row_n<8>(lrow, E, topk, ex, wt);
+  else route_row_n<ROUTE_PER_LANE>(lrow, E, topk, ex, wt);
 }
 
 // One wave per row.
@@ -80,7 +141,8 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
 // The plan of a routed MoE step, one workgroup: route every row (a wave per
 // row), then order the assignments by (expert, index) into work items of at
 // most 16 rows of one expert (the grouped GEMV's plan; the down projection
-// reuses it), and quantize the input rows into row order (A1).
+// reuses it).  Workgroups 1.. quantize the input rows into row order (A1)
+// meanwhile.
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict__ logits, int rows, int E, int topk,
                                                         int shared_expert, int32_t* __restrict__ expert,
                                                         float* __restrict__ weight, int32_t* __restrict__ x_index,
@@ -95,6 +157,33 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
   __shared__ int s_ie[QG_MOE_MAX_M], s_is[QG_MOE_MAX_M], s_ic[QG_MOE_MAX_M];  // work items
   __shared__ int s_cnt[2];
   const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
+  if (blockIdx.x > 0) {
+    // workgroups 1..: A1 of the input rows, row order, four lanes per 32-block
+    const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
+    const int e = (blockIdx.x - 1) * nt + tid;
+    if (e >= rows * kbp * 4) return;  // rows * kbp * 4 is a multiple of 64: whole waves leave
+    const int q = e & 3, blk = e >> 2, r = blk / kbp, b = blk - r * kbp;
+    float v[8];
+    if (b < kb) {
+      const float4* src = reinterpret_cast<const float4*>(x + (int64_t)r * k + (int64_t)b * QK + q * 8);
+      const float4 a = src[0], c = src[1];
+      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = 0.0f;
+    }
+    unsigned lo, hi;
+    float d;
+    int sum;
+    quantize_quarter(v, lo, hi, d, sum);
+    *reinterpret_cast<uint2*>(xq + ((int64_t)r * kbp + b) * 32 + q * 8) = make_uint2(lo, hi);
+    if (q == 0) {
+      xd[r * kbp + b] = d;
+      xn[r * kbp + b] = -8 * sum;
+    }
+    return;
+  }
+  // workgroup 0: routing and the plan
   const int slots = topk + (shared_expert >= 0 ? 1 : 0);
   const int m = rows * slots;
   for (int r = wave; r < rows; r += nt / WAVE) {
@@ -141,29 +230,6 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
   if (tid == 0) header[1] = 0;
   __syncthreads();
   store_items_small_first(s_ie, s_is, s_ic, m ? s_start[m - 1] : 0, s_pos, s_cnt, items, header);
-  // A1 of the input rows, row order: four lanes per 32-block
-  const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
-  for (int e = tid; e < rows * kbp * 4; e += nt) {  // rows * kbp * 4 is a multiple of 64: quads stay whole
-    const int q = e & 3, blk = e >> 2, r = blk / kbp, b = blk - r * kbp;
-    float v[8];
-    if (b < kb) {
-      const float4* src = reinterpret_cast<const float4*>(x + (int64_t)r * k + (int64_t)b * QK + q * 8);
-      const float4 a = src[0], c = src[1];
-      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; i++) v[i] = 0.0f;
-    }
-    unsigned lo, hi;
-    float d;
-    int sum;
-    quantize_quarter(v, lo, hi, d, sum);
-    *reinterpret_cast<uint2*>(xq + ((int64_t)r * kbp + b) * 32 + q * 8) = make_uint2(lo, hi);
-    if (q == 0) {
-      xd[r * kbp + b] = d;
-      xn[r * kbp + b] = -8 * sum;
-    }
-  }
 }
 
 // SwiGLU of m assignments, h = silu(g) * u in fp32, quantized at once into
@@ -244,7 +310,8 @@ int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int 
                     void* xprep, hipStream_t s) {
   const PrepLayout L = prep_layout_rows(rows, k);
   uint8_t* w = (uint8_t*)xprep;
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, logits, rows, n_experts, topk, shared_expert, expert,
+  const int64_t quads = (int64_t)rows * kbp_of(k) * 4;  // input-row quantization: workgroups 1..
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1 + (unsigned)((quads + 1023) / 1024)), dim3(1024), 0, s, logits, rows, n_experts, topk, shared_expert, expert,
                      weight, x_index, header, sorted, items, x, k, (int8_t*)(w + L.codes), (float*)(w + L.dx),
                      (int*)(w + L.nsx));
   return hip_status(hipGetLastError(), "moe_plan_kernel");

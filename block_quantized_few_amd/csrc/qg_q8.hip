@@ -1003,7 +1003,7 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
 
 int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int64_t k, const void* prep, int x_rows,
                            const int* header, const int* sorted, const int* items, const int32_t* x_index, int m,
-                           float* y, hipStream_t s) {
+                           int max_item_rows, float* y, hipStream_t s) {
   (void)n_experts;
   if (m == 0) return QG_OK;
   const int kbp = (int)kbp_of(k);
@@ -1025,7 +1025,7 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
   hipLaunchKernelGGL(grouped_kernel, dim3(gs), dim3(WG), lds_s, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv,
                      header, sorted, items, x_index, y, lx_s, tiles);
   if (int st = hip_status(hipGetLastError(), "grouped_kernel")) return st;
-  const int mb = m / (GROUPED_SMALL_ROWS + 1);
+  const int mb = max_item_rows > GROUPED_SMALL_ROWS ? m / (GROUPED_SMALL_ROWS + 1) : 0;
   if (mb > 0) {
     const int rpt = grouped_mp_rows(pl);
     const int tb = (int)((n + rpt - 1) / rpt);
@@ -1048,7 +1048,8 @@ int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, 
   hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(1024), 0, s, expert, x_index, m, n_experts, x_rows, header,
                      sorted, items);
   if (int st = hip_status(hipGetLastError(), "grouped_plan_kernel")) return st;
-  return launch_grouped_planned(images, n_experts, n, k, w + G.prep, x_rows, header, sorted, items, x_index, m, y, s);
+  return launch_grouped_planned(images, n_experts, n, k, w + G.prep, x_rows, header, sorted, items, x_index, m,
+                                QG_MAX_ROWS, y, s);
 }
 
 }  // namespace qg
