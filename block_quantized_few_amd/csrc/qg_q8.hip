@@ -225,7 +225,7 @@ __device__ __forceinline__ void compute_block(float (&acc)[R], const WBlock<FMT>
 // issued before the activation rows are staged (and, when they are quantized
 // here, after their fp32 loads, which the wave's in-order memory counter then
 // returns first).
-template <int FMT, int R, bool FUSED>
+template <int FMT, int R, bool FUSED, int LA = rl_lookahead(FUSED, R)>
 __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity, bool stage) {
   static_assert(!FUSED || R <= FUSE_MAX_ROWS, "fused quantization stages at most two rows");
   const PartPlan& pl = ta.pl;
@@ -251,7 +251,6 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
   const int bpart = s * pl.H * pl.BS + h;  // this lane's block at u = 0
   const int sbase = s * pl.H + h;          // its slot at u = 0 of a round
 
-  constexpr int LA = rl_lookahead(FUSED, R);
   XQuarter xv[XQ_FIRST];
   if (FUSED && stage) stage_quantize_begin(xv, ta.xf, ta.k, ta.kb, R, ta.kbp, pl);
   WBlock<FMT> w[LA];
@@ -746,10 +745,12 @@ __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __res
   store_items_small_first(s_ie, s_is, s_ic, nv ? s_start[nv - 1] : 0, s_pos, s_cnt, items, header);
 }
 
+constexpr int GROUPED_LA = 4;  // blocks in flight per lane in the small-item kernel
+
 template <int R>
 __device__ __forceinline__ void grouped_rows(TileArgs ta, uint8_t* lds, float* red) {
   ta.ucx = rl_round(ta.lds_x, R, ta.pl, FMT_Q8);
-  rl_tile<FMT_Q8, R, false>(ta, lds, red, 0, true);
+  rl_tile<FMT_Q8, R, false, GROUPED_LA>(ta, lds, red, 0, true);
 }
 
 // Items of at most GROUPED_SMALL_ROWS rows (the plan puts them first):
