@@ -71,8 +71,8 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 // Routing of one row by one wave: softmax over the E logits in fp32 (max
 // subtracted; each lane sums its experts in index order, then the fixed
 // wave_sum tree), and the topk experts by logit, ties to the lower index, in
-// descending order.  Lane 0 returns the picks in ex[] / wt[].  NPER: logits
-// per lane (E <= 64 * NPER).
+// descending order, written to ex[] / wt[] (lane k writes pick k).  NPER:
+// logits per lane (E <= 64 * NPER).
 template <int NPER>
 __device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
   const int lane = threadIdx.x & (WAVE - 1);
@@ -92,6 +92,8 @@ __device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int
     sum += lane + WAVE * i < E ? t : 0.0f;
   }
   sum = wave_sum(sum);
+  float mv = 0.0f;  // this lane's pick (lane k: the k-th)
+  int mi = 0;
   unsigned avail = 0;  // bit i: entry i is a real expert not picked yet
 #pragma unroll
   for (int i = 0; i < NPER; i++) avail |= (lane + WAVE * i < E ? 1u : 0u) << i;
@@ -108,10 +110,12 @@ __device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int
     }
     wave_argmax(bv, bi);
     avail &= ~((bi % WAVE == lane ? 1u : 0u) << (bi / WAVE));
-    if (lane == 0) {
-      ex[k] = bi;
-      wt[k] = expf(bv - mx) / sum;
-    }
+    mv = lane == k ? bv : mv;  // lane k keeps pick k
+    mi = lane == k ? bi : mi;
+  }
+  if (lane < topk) {
+    ex[lane] = mi;
+    wt[lane] = expf(mv - mx) / sum;
   }
 }
 
@@ -151,10 +155,12 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
                                                         const float* __restrict__ x, int64_t k, int8_t* __restrict__ xq,
                                                         float* __restrict__ xd, int* __restrict__ xn) {
   __shared__ int s_e[QG_MOE_MAX_M];
-  __shared__ int s_start[QG_MOE_MAX_M];
   __shared__ int s_pos[QG_MOE_MAX_M];
   __shared__ float s_w[QG_MOE_MAX_M];
   __shared__ int s_ie[QG_MOE_MAX_M], s_is[QG_MOE_MAX_M], s_ic[QG_MOE_MAX_M];  // work items
+  __shared__ unsigned s_mask[ROUTE_MAX_E + 1];  // bit r: row r picked expert e
+  __shared__ int s_off[ROUTE_MAX_E + 1];        // (assignments, touched experts) before expert e, packed
+  __shared__ int s_wsum[1024 / WAVE];
   __shared__ int s_cnt[2];
   const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
   if (blockIdx.x > 0) {
@@ -193,43 +199,52 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
       s_w[r * slots + topk] = 1.0f;
     }
   }
+  // Counting sort by expert.  An expert meets a row at most once (distinct
+  // top-k picks; the shared expert is index E), so with rows <= 16 every
+  // touched expert is one work item, and an assignment's place among its
+  // expert's is the number of earlier rows in the expert's row mask.
+  const int ne = E + 1;  // experts 0..E-1 and the shared expert E
+  for (int e = tid; e < ne; e += nt) s_mask[e] = 0u;
   __syncthreads();
+  for (int j = tid; j < m; j += nt) atomicOr(&s_mask[s_e[j]], 1u << (j / slots));
+  __syncthreads();
+  // exclusive scan over experts of (count | touched << 16), two experts per thread
+  const int e0 = 2 * tid, e1 = e0 + 1;
+  const unsigned m0 = e0 < ne ? s_mask[e0] : 0u, m1 = e1 < ne ? s_mask[e1] : 0u;
+  const int v0 = __popc(m0) | (m0 ? 1 << 16 : 0), v1 = __popc(m1) | (m1 ? 1 << 16 : 0);
+  int inc = v0 + v1;  // inclusive scan within the wave
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    inc += lane >= off ? o : 0;
+  }
+  if (lane == WAVE - 1) s_wsum[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; w++) base += s_wsum[w];
+  const int ex0 = base + inc - (v0 + v1);  // before expert e0
+  if (e0 < ne) s_off[e0] = ex0;
+  if (e1 < ne) s_off[e1] = ex0 + v0;
+  __syncthreads();
+  int nitems = 0;
+  for (int w = 0; w < nt / WAVE; w++) nitems += s_wsum[w];
+  nitems >>= 16;
   for (int j = tid; j < m; j += nt) {
-    expert[j] = s_e[j];
+    const int e = s_e[j], r = j / slots;
+    const unsigned mk = s_mask[e];
+    const int rank = (s_off[e] & 0xffff) + __popc(mk & ((1u << r) - 1u));
+    expert[j] = e;
     weight[j] = s_w[j];
-    x_index[j] = j / slots;
-    const int e = s_e[j];
-    int rank = 0, within = 0;
-    for (int i = 0; i < m; i++) {
-      const int f = s_e[i];
-      rank += (f < e) || (f == e && i < j);
-      within += (f == e && i < j);
-    }
-    s_pos[rank] = j;
-    s_start[rank] = (within % QG_MAX_ROWS) == 0;
+    x_index[j] = r;
     sorted[rank] = j;
-  }
-  __syncthreads();
-  // inclusive scan of the item starts (m <= QG_MOE_MAX_M <= nt: one value per thread)
-  for (int off = 1; off < m; off <<= 1) {
-    const int v = tid < m ? s_start[tid] + (tid >= off ? s_start[tid - off] : 0) : 0;
-    __syncthreads();
-    if (tid < m) s_start[tid] = v;
-    __syncthreads();
-  }
-  if (tid < m) {
-    const int item = s_start[tid] - 1;
-    if (tid == 0 || s_start[tid - 1] != s_start[tid]) {
-      int cnt = 1;
-      while (tid + cnt < m && s_start[tid + cnt] == s_start[tid]) cnt++;
-      s_ie[item] = s_e[s_pos[tid]];
-      s_is[item] = tid;
-      s_ic[item] = cnt;
-    }
+    if (mk & ((1u << r) - 1u)) continue;  // the expert's first row makes its item
+    const int item = s_off[e] >> 16;
+    s_ie[item] = e;
+    s_is[item] = s_off[e] & 0xffff;
+    s_ic[item] = __popc(mk);
   }
   if (tid == 0) header[1] = 0;
   __syncthreads();
-  store_items_small_first(s_ie, s_is, s_ic, m ? s_start[m - 1] : 0, s_pos, s_cnt, items, header);
+  store_items_small_first(s_ie, s_is, s_ic, nitems, s_pos, s_cnt, items, header);
 }
 
 // SwiGLU of m assignments, h = silu(g) * u in fp32, quantized at once into
