@@ -637,11 +637,14 @@ __device__ __forceinline__ TileArgs tile_args(const ProjDev& d, int64_t row0, co
 // Tiles are numbered projection by projection; workgroup w takes tiles w,
 // w + G, w + 2G, ... and keeps a projection's activation rows in LDS while its
 // tiles last.
-template <int FMT, int R, bool FUSED>
-// (At most 80 registers -- 96 for two Q8_0 rows, which would spill -- so that
-// three 512-thread workgroups fit a CU and a layer's tiles are resident at
-// once.)
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q8 && R == 2 ? 5 : 6))) void rl_set_kernel(SetArgs a, int lds_x) {
+// LA: blocks in flight per lane -- 2 when the launch fills the GPU (the many
+// waves give the memory parallelism; at most 80 registers, 96 for two Q8_0
+// rows, which would spill, so that three 512-thread workgroups fit a CU and a
+// layer's tiles are resident at once), 8 for launches of at most one
+// workgroup per CU (latency-bound: a lane's blocks all in flight at once).
+template <int FMT, int R, bool FUSED, int LA>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(LA > 2 ? 2 : (FMT == FMT_Q8 && R == 2 ? 5 : 6))))
+void rl_set_kernel(SetArgs a, int lds_x) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
@@ -652,7 +655,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(FMT == FMT_Q
     while (p + 1 < a.count && t0 >= a.p[p].tiles) t0 -= a.p[p++].tiles;
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, lds_x);
-    const bool full = rl_tile<FMT, R, FUSED>(ta, lds, red, parity, p != staged);
+    const bool full = rl_tile<FMT, R, FUSED, LA>(ta, lds, red, parity, p != staged);
     staged = full ? p : -1;
     // the combine area alternates only between tiles that pass its barrier, so
     // a buffer is rewritten only after everyone has read it
@@ -889,9 +892,16 @@ bool fuses_quantization(int rows) { return rows >= 1 && rows <= FUSE_MAX_ROWS; }
 
 template <int FMT, int R, bool FUSED>
 static void launch_rl(const SetArgs& a, int lds_x, hipStream_t s) {
-  auto kern = rl_set_kernel<FMT, R, FUSED>;
   const size_t lds = (size_t)lds_x + 2 * WAVES * WAVE * R * 4;
-  hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, lds_x);
+  bool small = a.total_tiles <= device_cus();
+  for (int i = 0; i < a.count; i++) small = small && a.p[i].ucx == a.p[i].pl.BS;  // staged whole (LA | rounds)
+  if (small) {
+    auto kern = rl_set_kernel<FMT, R, FUSED, 8>;
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, lds_x);
+  } else {
+    auto kern = rl_set_kernel<FMT, R, FUSED, 2>;
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, lds_x);
+  }
 }
 
 template <int FMT>
