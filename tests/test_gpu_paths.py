@@ -1,0 +1,88 @@
+"""GPU tests of code paths the shape-driven kernel choices reach only at particular sizes: routing over
+more than 256 experts, grouped items on the pair tile for every lane-part count, and the wide pair tiles for
+Q4_0 at 9-16 rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_quantized_few_amd import qgemv as q
+from helpers import TOL, bits, gauss, log, oracle_image, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("E", [8, 64, 256, 300, 1000])
+def test_routing_matches_oracle(E):
+    """Top-k experts (ties to the lower index) and softmax weights of qg_moe_route against the oracle, for
+    expert counts that take each logits-per-lane width (4, 8, 16)."""
+    rows = 16
+    rng = np.random.default_rng(E)
+    logits = gauss((rows, E), 1.0, 22, E).numpy()
+    # exact ties, some of them among the top picks
+    for r in range(rows):
+        a, b = rng.choice(E, size=2, replace=False)
+        logits[r, b] = logits[r, a]
+        logits[r, (a + 1) % E] = logits[r].max()
+    for topk in sorted({1, min(8, E), min(32, E)}):
+        log(f"routing E={E} topk={topk}")
+        ex, _, wt = q.moe_route(torch.from_numpy(logits).cuda(), topk)
+        ex_o, p_o = O.route_topk(logits, topk)
+        assert np.array_equal(ex.cpu().numpy().reshape(rows, topk), ex_o)
+        assert np.allclose(wt.cpu().numpy().reshape(rows, topk), p_o, rtol=1e-5, atol=1e-9)
+
+
+@pytest.mark.parametrize("k", [512, 2048, 3072, 4096, 8192])
+def test_grouped_items_on_every_tile_shape(k):
+    """Work items of 16, 9, 5, 3 and 1-2 rows (the pair tile with two row groups, with one, and the lean
+    small-item tile) for k whose partition has 1, 2, 4 or 8 lane parts (k = 3072: twelve blocks per part):
+    every assignment's row equals the same row through the one-row GEMV, bit for bit."""
+    E, n, x_rows = 5, 80, 20
+    blocks, imgs = [], []
+    for e in range(E):
+        b, img = oracle_image(O.Q8_0, gauss((n, k), 0.02, 23, 100 * e + k % 97).numpy())
+        blocks.append(b)
+        imgs.append(img)
+    stacked = torch.cat(imgs)
+    x = gauss((x_rows, k), 1.0, 23, 7).numpy()
+    xd = torch.from_numpy(x).cuda()
+    rng = np.random.default_rng(k)
+    counts = [16, 9, 5, 3, 2]  # expert e gets counts[e] assignments
+    expert = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    perm = rng.permutation(expert.size)
+    expert = expert[perm]
+    x_index = rng.integers(0, x_rows, size=expert.size).astype(np.int32)
+    m = expert.size
+    log(f"grouped k={k} m={m}")
+    y = torch.full((m, n), float("nan"), device="cuda")
+    q.qgemv_q8_0_grouped(stacked, E, n, k, xd, torch.from_numpy(expert).cuda(), torch.from_numpy(x_index).cuda(),
+                         y=y)
+    yg = y.cpu().numpy()
+    for j in range(m):
+        dense = q.qgemv_q8_0(imgs[expert[j]], n, k, xd[x_index[j]:x_index[j] + 1].contiguous())
+        assert np.array_equal(bits(y[j]), bits(dense[0])), (j, expert[j])
+    # and the oracle, on a few assignments
+    for j in (0, m // 2, m - 1):
+        xr = x[x_index[j]:x_index[j] + 1]
+        yo = O.gemv_q(O.Q8_0, blocks[expert[j]], n, k, xr)
+        assert rel_err(yg[j:j + 1], yo, blocks[expert[j]], O.Q8_0, xr) <= TOL
+
+
+def test_q4_0_wide_tiles_at_16_rows():
+    """Q4_0 at 16 rows on a matrix whose narrow tiling needs two rounds of resident workgroups (so the launch
+    takes the wide tiles): sampled outputs against the oracle, and rows 0 and 15 against the same rows
+    alone."""
+    n, k, rows = 16384, 4096, 16
+    w = gauss((n, k), 0.02, 24, 0).numpy()
+    blocks, img = oracle_image(O.Q4_0, w)
+    x = gauss((rows, k), 1.0, 24, 1).numpy()
+    xd = torch.from_numpy(x).cuda()
+    y = q.qgemv_q4_0(img, n, k, xd)
+    sel = np.sort(np.random.default_rng(24).choice(n, size=256, replace=False))
+    yo = O.gemv_q_rows(O.Q4_0, blocks, n, k, x, sel, threads=16)
+    e = rel_err(y.cpu().numpy()[:, sel], yo, blocks, O.Q4_0, x, sel=sel)
+    log(f"Q4_0 {n}x{k} rows={rows} max rel err {e:.3e}")
+    assert e <= TOL
+    for r in (0, rows - 1):
+        y1 = q.qgemv_q4_0(img, n, k, xd[r:r + 1].contiguous())
+        assert np.array_equal(bits(y[r]), bits(y1[0]))
