@@ -58,6 +58,7 @@ def lib():
         L.orc_route_topk.restype = ci
         L.orc_route_topk.argtypes = [p, ci, i64, ci, p, p]
         L.orc_swiglu.argtypes = [p, p, i64, p]
+        L.orc_add_rmsnorm.argtypes = [p, p, p, C.c_double, ci, i64, p, p]
         L.orc_moe_step.restype = ci
         L.orc_moe_step.argtypes = [p, ci, i64, p, i64, ci, p, p, p, i64, p, p, p, p, p, p, p]
         _lib = L
@@ -201,6 +202,19 @@ def swiglu(g, u):
     h = np.empty(g.shape, np.float32)
     lib().orc_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h))
     return h
+
+
+def add_rmsnorm(x, residual, gamma, eps):
+    """h = x + residual (fp32), y = h / sqrt(mean(h^2) + eps) * gamma (float64)."""
+    x = _c(x, np.float32)
+    rows, k = x.shape
+    res = None if residual is None else _c(residual, np.float32)
+    gamma = _c(gamma, np.float32)
+    h = np.empty((rows, k), np.float32)
+    y = np.empty((rows, k), np.float64)
+    lib().orc_add_rmsnorm(_ptr(x), None if res is None else _ptr(res), _ptr(gamma), float(eps), rows, k, _ptr(h),
+                          _ptr(y))
+    return h, y
 
 
 def moe_step(x, router16, topk, gate, up, down, ffn, sgate, sup, sdown):

@@ -462,6 +462,29 @@ void orc_swiglu(const float* g, const float* u, int64_t count, float* h) {
   }
 }
 
+/* Residual add and RMS norm, the step before a projection group ([B] backbone
+ * section: the add and norm before the MoE also write the normed rows'
+ * quantized groups, in the order and rounding of the separate quantization
+ * they replace; [C] lists the add+rms fold with its requant arm).
+ *   h = x + residual (fp32 add; residual may be NULL: h = x)
+ *   y = h / sqrt(mean(h^2) + eps) * gamma, evaluated in double.
+ * h is returned in fp32 (one correctly rounded add, the same on any device),
+ * y in double; the q8 codes of the normed rows are A1 of the fp32 y. */
+void orc_add_rmsnorm(const float* x, const float* residual, const float* gamma, double eps, int rows, int64_t k,
+                     float* h, double* y) {
+  for (int r = 0; r < rows; r++) {
+    const float* xr = x + (int64_t)r * k;
+    float* hr = h + (int64_t)r * k;
+    double ss = 0.0;
+    for (int64_t i = 0; i < k; i++) {
+      hr[i] = residual ? xr[i] + residual[(int64_t)r * k + i] : xr[i];
+      ss += (double)hr[i] * (double)hr[i];
+    }
+    const double inv = 1.0 / sqrt(ss / (double)k + eps);
+    for (int64_t i = 0; i < k; i++) y[(int64_t)r * k + i] = (double)hr[i] * inv * (double)gamma[i];
+  }
+}
+
 /* One expert's FFN on one activation row: gate and up (n=ffn, k=hidden),
  * SwiGLU, q8 re-quantization of h, down (n=hidden, k=ffn). */
 static void expert_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down, int64_t hidden, int64_t ffn,

@@ -348,6 +348,50 @@ def test_moe_step_composes_its_pieces():
         assert np.array_equal(y[r], ref)
 
 
+# ------------------------------------------------- add + RMS norm ---
+def test_add_rmsnorm_hand_values_and_closed_forms():
+    # [3, 4]: mean of squares 12.5, so y = [3, 4] / sqrt(12.5)
+    _, y = O.add_rmsnorm(np.array([[3.0, 4.0]], np.float32), None, np.ones(2, np.float32), 0.0)
+    assert np.allclose(y[0], [3 / np.sqrt(12.5), 4 / np.sqrt(12.5)], rtol=1e-15)
+    assert np.allclose(y[0], [0.8485281374238570, 1.1313708498984760], rtol=1e-14)
+    # the mean divides by k, not k - 1: [1, -1] is already normalized
+    _, y = O.add_rmsnorm(np.array([[1.0, -1.0]], np.float32), None, np.array([2.0, 0.5], np.float32), 0.0)
+    assert np.array_equal(y[0], [2.0, -0.5])
+    # a constant row normalizes to its sign times gamma
+    g = np.array([0.5, 1.5, -2.0, 3.0], np.float32)
+    _, y = O.add_rmsnorm(np.full((1, 4), -7.25, np.float32), None, g, 0.0)
+    assert np.allclose(y[0], -g.astype(np.float64), rtol=1e-15)
+    # eps keeps a zero row finite (and zero)
+    _, y = O.add_rmsnorm(np.zeros((1, 32), np.float32), None, np.ones(32, np.float32), 1e-6)
+    assert np.array_equal(y, np.zeros((1, 32)))
+    # eps enters under the root: x = [1, 1], eps = 3 -> 1 / sqrt(1 + 3) = 0.5
+    _, y = O.add_rmsnorm(np.ones((1, 2), np.float32), None, np.ones(2, np.float32), 3.0)
+    assert np.allclose(y[0], [0.5, 0.5], rtol=1e-15)
+
+
+def test_add_rmsnorm_invariants():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 96)).astype(np.float32)
+    res = rng.standard_normal((3, 96)).astype(np.float32)
+    g = rng.standard_normal(96).astype(np.float32)
+    h, y = O.add_rmsnorm(x, res, g, 1e-5)
+    assert np.array_equal(h, x + res)  # one fp32 add per element
+    _, y2 = O.add_rmsnorm(x + res, None, g, 1e-5)
+    assert np.array_equal(y, y2)
+    # gamma is a per-column factor; doubling it doubles y exactly
+    _, y3 = O.add_rmsnorm(x, res, 2 * g, 1e-5)
+    assert np.array_equal(y3, 2 * y)
+    # scale invariance with eps = 0 (powers of two keep the fp32 inputs exact)
+    _, ya = O.add_rmsnorm(x, None, g, 0.0)
+    _, yb = O.add_rmsnorm(x * 8, None, g, 0.0)
+    assert np.allclose(ya, yb, rtol=1e-14)
+    # rows are independent, and the unit-gamma result has mean square 1
+    _, y1 = O.add_rmsnorm(x[1:2], res[1:2], g, 1e-5)
+    assert np.array_equal(y1[0], y[1])
+    _, yu = O.add_rmsnorm(x, None, np.ones(96, np.float32), 0.0)
+    assert np.allclose((yu ** 2).mean(axis=1), 1.0, rtol=1e-13)
+
+
 # --------------------------------------------------- input generator ---
 def test_synth_matches_scalar_splitmix_and_is_gaussian():
     import torch
