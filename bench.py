@@ -392,6 +392,28 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
     del imgs
     print(f"[bench] sweep 1024x1024 done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
+    # residual add + RMS norm + A1 in one launch (qg_add_rmsnorm_prepare), next to A1 alone (qg_prepare_rows)
+    # of the same rows; bytes: x, residual and gamma read, h and the workspace written
+    for k in (2048, 8192):
+        gamma = (1.0 + synth.gaussian((k,), 0.1, synth.tensor_seed(6, 2), device="cuda")).contiguous()
+        for rows in (1, 8, 16):
+            x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(6, 32 + rows), device="cuda")
+            res = synth.gaussian((rows, k), 0.5, synth.tensor_seed(6, 48 + rows), device="cuda")
+            h = torch.empty_like(x)
+            ws = q.empty_ws(rows, k)
+            xp, rp, gp, hp, wp, wn = x.data_ptr(), res.data_ptr(), gamma.data_ptr(), h.data_ptr(), ws.data_ptr(), ws.numel()
+            nb = 4 * rows * k * 3 + 4 * k + q.workspace_bytes(rows, k)
+            ms = time_calls(torch, timer, stream,
+                            lambda i: L.qg_add_rmsnorm_prepare(xp, rp, gp, 1e-5, rows, k, hp, None, wp, wn, sh), 400)
+            e = entry(f"add + rmsnorm + q8 prepare, k={k}", "fp32 -> q8", rows, nb, ms, 1)
+            e["note"] = "weight_bytes here: activation bytes moved"
+            out.append(e)
+            ms = time_calls(torch, timer, stream, lambda i: L.qg_prepare_rows(xp, rows, k, wp, wn, sh), 400)
+            e = entry(f"q8 prepare alone, k={k}", "fp32 -> q8", rows, 4 * rows * k + q.workspace_bytes(rows, k), ms, 1)
+            e["note"] = "weight_bytes here: activation bytes moved"
+            out.append(e)
+    print(f"[bench] sweep norm done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
     # decode layers (set launch): 1B Q8_0 and 3B Q4_0
     for lname, lay, fmt, wl, lane, obj in (("llama-3.2-1b layer", LAYER_1B, q.Q8_0, 1, "q8_0", layer1b),
                                            ("llama-3.2-3b layer", LAYER_3B, q.Q4_0, 2, "q4_0", None)):

@@ -102,6 +102,28 @@ int qg_prepare_rows(const float* x, int rows, int64_t k, void* ws, size_t ws_byt
   return ok();
 }
 
+int qg_add_rmsnorm_prepare(const float* x, const float* residual, const float* gamma, float eps, int rows, int64_t k,
+                           float* h_out, float* y_out, void* ws, size_t ws_bytes, qg_stream stream) {
+  if (rows == 0) return ok();
+  if (int st = check_x(x, rows, k, QG_MAX_PREP_ROWS)) return st;
+  if (!gamma) return fail(QG_EINVAL, "gamma is null");
+  if (!aligned(gamma, 16)) return fail(QG_EALIGN, "gamma %p is not 16-byte aligned", (const void*)gamma);
+  if (residual && !aligned(residual, 16))
+    return fail(QG_EALIGN, "residual %p is not 16-byte aligned", (const void*)residual);
+  if (h_out && !aligned(h_out, 16)) return fail(QG_EALIGN, "h_out %p is not 16-byte aligned", (const void*)h_out);
+  if (y_out && !aligned(y_out, 16)) return fail(QG_EALIGN, "y_out %p is not 16-byte aligned", (const void*)y_out);
+  if (!(eps >= 0.0f) || eps > 1e30f) return fail(QG_EINVAL, "eps=%g is not a finite value >= 0", (double)eps);
+  if (ws) {
+    if (int st = check_ws(ws, ws_bytes, prep_layout(rows, k).total, "the normed rows")) return st;
+  } else if (!h_out && !y_out) {
+    return fail(QG_EINVAL, "no output: ws, h_out and y_out are all null");
+  }
+  if (int st = check_device()) return st;
+  if (int st = launch_add_rmsnorm_prepare(x, residual, gamma, eps, rows, k, h_out, y_out, ws, (hipStream_t)stream))
+    return st;
+  return ok();
+}
+
 int qg_prepare_rows_set(const qg_act* acts, int count, int rows, qg_stream stream) {
   if (!acts || count < 1 || count > QG_MAX_SET) return fail(QG_EINVAL, "count=%d outside 1..%d", count, QG_MAX_SET);
   for (int i = 0; i < count; i++) {

@@ -20,6 +20,9 @@ Prep prep_view(const void* ws, const PrepLayout& L);
 
 // A1: quantize rows x [rows][k] into a workspace in the order L (qg_layout.h).
 int launch_prepare(const float* x, int rows, int64_t k, void* ws, const PrepLayout& L, hipStream_t s);
+// h = x + res, y = RMS norm of h times gamma, A1 of y into ws (prep_layout(rows, k)) when ws is not null.
+int launch_add_rmsnorm_prepare(const float* x, const float* res, const float* gamma, float eps, int rows, int64_t k,
+                               float* h_out, float* y_out, void* ws, hipStream_t s);
 // A1 for up to QG_MAX_SET activation sets (same row count) in one launch.
 int launch_prepare_set(const qg_act* acts, int count, int rows, hipStream_t s);
 // A1 in the plain layout with code sums (test hook).

@@ -210,6 +210,127 @@ static PrepDst prep_dst(void* ws, const PrepLayout& L, int rows, int64_t k) {
                  (int)kbp_of(k), L.pairs ? L.groups : 0};
 }
 
+// ------------------------------------------------------ add + RMS norm ---
+//
+// The step before a projection group: h = x + residual, y = h * inv * gamma
+// with inv = 1 / sqrt(mean(h^2) + eps), and A1 of y into the workspace in the
+// layout the GEMV reads -- the bytes prepare_kernel writes for the same fp32
+// y.  One workgroup per workspace row (pair order pads to 8-row groups; pad
+// rows come out zero).  The sum of squares has a fixed order: each thread adds
+// its float4 chunks t, t + 1024, ... element by element, the waves reduce by a
+// DPP tree, and the sixteen wave sums add left to right.  x, residual, h and
+// y may alias (each element is read and written by one thread, and y is
+// written only after every thread has finished reading for the sum).
+constexpr int NORM_WG = 1024;
+
+__device__ __forceinline__ float norm_wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // pairs
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quads
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // 8-lane mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // 16-lane mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__global__ __launch_bounds__(NORM_WG) void add_rmsnorm_prepare_kernel(const float* x, const float* res,
+                                                                      const float* __restrict__ gamma, float eps,
+                                                                      int xrows, int64_t k, int kb, float* h_out,
+                                                                      float* y_out, PrepDst dst, bool write_ws) {
+  __shared__ float s_part[NORM_WG / WAVE];
+  const int r = blockIdx.x, tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+  const bool real = r < xrows;  // uniform over the workgroup
+  const float* xr = x + (int64_t)r * k;
+  const float* rr = res ? res + (int64_t)r * k : nullptr;
+  float inv = 0.0f;
+  if (real) {
+    float ss = 0.0f;
+    const int64_t nc = k / 4;
+    for (int64_t c0 = tid; c0 < nc; c0 += 2 * NORM_WG) {  // two chunks' loads in flight
+      float4 hv[2], rv[2];
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int64_t c = c0 + u * NORM_WG;
+        hv[u] = c < nc ? reinterpret_cast<const float4*>(xr)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        rv[u] = rr && c < nc ? reinterpret_cast<const float4*>(rr)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int64_t c = c0 + u * NORM_WG;
+        if (c >= nc) break;
+        float4 h = hv[u];
+        if (rr) {
+          h.x += rv[u].x;
+          h.y += rv[u].y;
+          h.z += rv[u].z;
+          h.w += rv[u].w;
+        }
+        if (h_out) reinterpret_cast<float4*>(h_out + (int64_t)r * k)[c] = h;
+        ss += h.x * h.x;
+        ss += h.y * h.y;
+        ss += h.z * h.z;
+        ss += h.w * h.w;
+      }
+    }
+    ss = norm_wave_sum(ss);
+    if (lane == 0) s_part[wave] = ss;
+    __syncthreads();
+    float tot = s_part[0];
+    for (int w = 1; w < NORM_WG / WAVE; w++) tot += s_part[w];
+    inv = 1.0f / sqrtf(tot / (float)k + eps);
+  }
+  // four lanes per 32-block; kbp * 4 is a multiple of 64, so whole waves leave the loop together
+  // (a thread's pass-1 chunks and its blocks here differ, hence the barrier above)
+  for (int64_t t = tid; t < (int64_t)dst.kbp * 4; t += NORM_WG) {
+    const int64_t b = t >> 2;
+    const int q = (int)(t & 3);
+    float v[8];
+    if (real && b < kb) {
+      const int64_t e0 = b * QK + q * 8;
+      // h again: from h_out when it was written (it may alias x or the residual), else recomputed
+      const float* hs = h_out ? h_out + (int64_t)r * k : xr;
+      const float4 a0 = *reinterpret_cast<const float4*>(hs + e0), a1 = *reinterpret_cast<const float4*>(hs + e0 + 4);
+      float h[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      if (rr && !h_out) {
+        const float4 b0 = *reinterpret_cast<const float4*>(rr + e0), b1 = *reinterpret_cast<const float4*>(rr + e0 + 4);
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) h[j] += bb[j];
+      }
+      const float4 g0 = *reinterpret_cast<const float4*>(gamma + e0), g1 = *reinterpret_cast<const float4*>(gamma + e0 + 4);
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int j = 0; j < 8; j++) v[j] = (h[j] * inv) * gg[j];
+      if (y_out) {
+        float* yo = y_out + (int64_t)r * k + e0;
+        *reinterpret_cast<float4*>(yo) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(yo + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; j++) v[j] = 0.0f;
+    }
+    unsigned lo, hi;
+    float d;
+    int sum;
+    quantize_quarter(v, lo, hi, d, sum);
+    if (write_ws) dst.put(r, b, q, lo, hi, d, sum);
+  }
+}
+
+int launch_add_rmsnorm_prepare(const float* x, const float* res, const float* gamma, float eps, int rows, int64_t k,
+                               float* h_out, float* y_out, void* ws, hipStream_t s) {
+  const PrepLayout L = prep_layout(rows, k);
+  PrepDst dst = prep_dst(ws, L, rows, k);
+  const bool write_ws = ws != nullptr;
+  if (!write_ws) dst.rows = rows;  // no workspace: the real rows only
+  hipLaunchKernelGGL(add_rmsnorm_prepare_kernel, dim3((unsigned)dst.rows), dim3(NORM_WG), 0, s, x, res, gamma, eps,
+                     rows, k, (int)kb_of(k), h_out, y_out, dst, write_ws);
+  return hip_status(hipGetLastError(), "add_rmsnorm_prepare_kernel");
+}
+
 int launch_prepare(const float* x, int rows, int64_t k, void* ws, const PrepLayout& L, hipStream_t s) {
   const PrepDst dst = prep_dst(ws, L, rows, k);
   hipLaunchKernelGGL(prepare_kernel, dim3(grid1((int64_t)dst.rows * dst.kbp * 4, 256)), dim3(256), 0, s, x, k,

@@ -54,6 +54,8 @@ _SIGS = {
     "qg_last_error_detail": (C.c_int, [C.c_char_p, C.c_size_t]),
     "qg_quantize_weights": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
     "qg_prepare_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qg_add_rmsnorm_prepare": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_float, C.c_int, C.c_int64,
+                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qgemv_prepared": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
                                  C.c_void_p]),
     "qgemv_q8_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
@@ -213,6 +215,21 @@ def _qgemv(fn, image, n, k, x, y, ws):
         ws = empty_ws(max(rows, 1), k, x.device)
     _check(fn(_p(image), n, k, _p(x), rows, _p(y), _p(ws), ws.numel(), _stream()))
     return y
+
+
+def add_rmsnorm_prepare(x, gamma, eps, residual=None, ws=None, h_out=None, y_out=None):
+    """qg_add_rmsnorm_prepare: h = x + residual, y = RMS norm of h times gamma, A1 of y into ws (a new
+    workspace when ws is None and neither h_out nor y_out is asked for).  Returns (ws, h_out, y_out)."""
+    _dev(x, torch.float32, "x")
+    _dev(gamma, torch.float32, "gamma")
+    rows, k = x.shape
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    if ws is None and h_out is None and y_out is None:
+        ws = empty_ws(max(rows, 1), k, x.device)
+    _check(lib().qg_add_rmsnorm_prepare(_p(x), _p(residual), _p(gamma), float(eps), rows, k, _p(h_out), _p(y_out),
+                                        _p(ws), 0 if ws is None else ws.numel(), _stream()))
+    return ws, h_out, y_out
 
 
 def qgemv_q8_0(image, n, k, x, y=None, ws=None):

@@ -143,6 +143,24 @@ int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* ima
  * the same rows and k). */
 int qg_prepare_rows(const float* x, int rows, int64_t k, void* ws, size_t ws_bytes, qg_stream stream);
 
+/* The step before a projection group, in one launch: residual add, RMS norm
+ * and A1 (the drama page's backbone section: the add and norm before the MoE
+ * write the normed rows' quantized groups in the order and rounding of the
+ * separate quantization they replace; the llama-leg page's add+rms requant
+ * arm).  Per row r of x [rows][k] (fp32):
+ *   h = x + residual                    (residual may be null: h = x)
+ *   y = h * (1 / sqrt(mean(h^2) + eps)) * gamma   (gamma [k])
+ * in fp32: the sum of squares in a fixed order (per thread, then a wave tree,
+ * then the sixteen waves left to right), so y is reproducible bit for bit.
+ * Writes h to h_out and y to y_out when they are not null (both [rows][k];
+ * they may alias x or residual), and, when ws is not null, A1 of y into ws
+ * (qg_workspace_bytes(rows, k) bytes) in the layout the GEMV reads for `rows`
+ * rows -- the same bytes qg_prepare_rows writes for y.  1 <= rows <= 8192
+ * (0 is a no-op), k a multiple of 32, eps >= 0; at least one of ws, h_out,
+ * y_out must be given. */
+int qg_add_rmsnorm_prepare(const float* x, const float* residual, const float* gamma, float eps, int rows, int64_t k,
+                           float* h_out, float* y_out, void* ws, size_t ws_bytes, qg_stream stream);
+
 /* q8 lane GEMV on rows already prepared in `ws` (by qg_prepare_rows with the
  * same rows and k): y [rows][n] fp32, row stride n.  fmt = Q8_0 or Q4_0. */
 int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,

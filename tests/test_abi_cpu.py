@@ -154,6 +154,29 @@ def test_validation_refuses_before_any_hip_call():
     assert st == -2
     st, msg = _status("qg_moe_route", V(A), 1, 2000, 8, -1, V(A), V(A), V(A), None)
     assert st == -2
+    # qg_add_rmsnorm_prepare: x, residual, gamma, eps, rows, k, h_out, y_out, ws, ws_bytes
+    norm = lambda **kw: _status("qg_add_rmsnorm_prepare", V(kw.get("x", A)), None, V(kw.get("gamma", A)),
+                                C.c_float(kw.get("eps", 1e-5)), kw.get("rows", 2), kw.get("k", 2048), None,
+                                V(kw["y"]) if "y" in kw else None, V(kw["ws"]) if "ws" in kw else V(A),
+                                kw.get("bytes", MB), None)
+    st, msg = norm(k=100)
+    assert st == -2 and "k=100" in msg
+    st, msg = norm(rows=8193)
+    assert st == -3 and "rows=8193" in msg
+    st, msg = norm(gamma=0)
+    assert st == -1 and "gamma" in msg
+    st, msg = norm(gamma=A + 4)
+    assert st == -4 and "gamma" in msg
+    st, msg = norm(eps=-1.0)
+    assert st == -1 and "eps" in msg
+    st, msg = norm(ws=0)
+    assert st == -1 and "no output" in msg
+    st, msg = norm(bytes=100)
+    assert st == -5 and "ws_bytes=100" in msg
+    st, msg = norm(rows=0)
+    assert st == 0
+    st, msg = norm(ws=0, y=A)
+    assert st == -7  # a valid call: no GPU here
     # qg_moe_step: router, E, hidden, ffn, topk, shared, gu, down, x, rows, y, logits, expert, weight, ws, bytes
     moe = lambda **kw: _status("qg_moe_step", V(A), kw.get("E", 256), kw.get("hidden", 2048), kw.get("ffn", 512),
                                kw.get("topk", 8), kw.get("shared", 1), V(A), V(A), V(A), kw.get("rows", 1), V(A),
