@@ -59,6 +59,15 @@ def lib():
         L.orc_route_topk.argtypes = [p, ci, i64, ci, p, p]
         L.orc_swiglu.argtypes = [p, p, i64, p]
         L.orc_add_rmsnorm.argtypes = [p, p, p, C.c_double, ci, i64, p, p]
+        L.orc_e4m3_encode_array.argtypes = [p, p, i64]
+        L.orc_e4m3_decode.restype = C.c_double
+        L.orc_e4m3_decode.argtypes = [C.c_uint8]
+        L.orc_quantize_fp8_weights.restype = ci
+        L.orc_quantize_fp8_weights.argtypes = [p, i64, i64, p, p]
+        L.orc_quantize_fp8_acts.restype = ci
+        L.orc_quantize_fp8_acts.argtypes = [p, ci, i64, p, p]
+        L.orc_gemv_fp8.restype = ci
+        L.orc_gemv_fp8.argtypes = [p, p, i64, i64, p, ci, p, i64, p, ci]
         L.orc_moe_step.restype = ci
         L.orc_moe_step.argtypes = [p, ci, i64, p, i64, ci, p, p, p, i64, p, p, p, p, p, p, p]
         _lib = L
@@ -202,6 +211,57 @@ def swiglu(g, u):
     h = np.empty(g.shape, np.float32)
     lib().orc_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h))
     return h
+
+
+# ------------------------------------------------------------ FP8 lane ---
+FP8_GROUP = 128
+
+
+def e4m3_encode(v):
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e4m3_encode_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def e4m3_decode(codes):
+    codes = np.asarray(codes, np.uint8)
+    table = np.array([lib().orc_e4m3_decode(c) for c in range(256)], np.float64)
+    return table[codes]
+
+
+def quantize_fp8_weights(w):
+    """[n][k] fp32 -> (codes [n][k] uint8, scales [ceil(n/128)][k/128] fp32)."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    codes = np.empty((n, k), np.uint8)
+    scales = np.empty(((n + FP8_GROUP - 1) // FP8_GROUP, k // FP8_GROUP), np.float32)
+    assert lib().orc_quantize_fp8_weights(_ptr(w), n, k, _ptr(codes), _ptr(scales)) == 0
+    return codes, scales
+
+
+def quantize_fp8_acts(x):
+    x = _c(x, np.float32)
+    rows, k = x.shape
+    codes = np.empty((rows, k), np.uint8)
+    scales = np.empty((rows, k // FP8_GROUP), np.float32)
+    assert lib().orc_quantize_fp8_acts(_ptr(x), rows, k, _ptr(codes), _ptr(scales)) == 0
+    return codes, scales
+
+
+def gemv_fp8(codes, scales, x, sel=None, threads=1):
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    x = _c(x, np.float32)
+    n, k = codes.shape
+    rows = x.shape[0]
+    if sel is not None:
+        sel = _c(sel, np.int64)
+    ns = n if sel is None else sel.size
+    y = np.empty((rows, ns), np.float32)
+    assert lib().orc_gemv_fp8(_ptr(codes), _ptr(scales), n, k, _ptr(x), rows, None if sel is None else _ptr(sel),
+                              0 if sel is None else sel.size, _ptr(y), threads) == 0
+    return y
 
 
 def add_rmsnorm(x, residual, gamma, eps):

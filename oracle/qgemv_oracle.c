@@ -354,6 +354,148 @@ int orc_gemv_q_rows(int fmt, const uint8_t* blocks, int64_t n, int64_t k, const 
   return qgemv_common(fmt, blocks, n, k, x, rows, sel, nsel, y, threads);
 }
 
+/* ------------------------------------------------------------ FP8 lane --- */
+/* Block-FP8 ([B] backbone section: block-FP8 expert weights, dynamic 1 x 128
+ * FP8 activation groups; neither the element format nor the weight block is
+ * printed there -- the plainest reading is the OCP 8-bit format E4M3 (4
+ * exponent bits, bias 7, 3 mantissa bits, largest finite 448, no infinities),
+ * fp32 scales amax / 448, activation groups of 128 consecutive k of one row,
+ * and weight blocks of 128 rows x 128 k).  Encoding: round to nearest, ties
+ * to even, magnitudes past 448 saturate to 448. */
+#define FP8_GROUP 128
+#define FP8_MAX 448.0
+
+uint8_t orc_e4m3_encode(float f) {
+  const uint8_t sign = signbit(f) ? 0x80 : 0x00;
+  double a = fabs((double)f);
+  if (a >= FP8_MAX) return sign | 0x7E; /* saturate (0x7F is NaN) */
+  if (a < ldexp(1.0, -6)) {             /* subnormal: multiples of 2^-9 */
+    int m = (int)round_half_even(a * 512.0);
+    return sign | (uint8_t)m; /* m == 8 is the smallest normal, 0x08 */
+  }
+  int e;
+  double fr = frexp(a, &e); /* a = fr * 2^e, fr in [0.5, 1) */
+  e -= 1;                   /* a = (2 fr) * 2^e, 2 fr in [1, 2) */
+  int m = (int)round_half_even((2.0 * fr - 1.0) * 8.0);
+  if (m == 8) {
+    m = 0;
+    e += 1;
+  }
+  if (e > 8 || (e == 8 && m > 6)) return sign | 0x7E;
+  return sign | (uint8_t)(((e + 7) << 3) | m);
+}
+
+void orc_e4m3_encode_array(const float* in, uint8_t* out, int64_t count) {
+  for (int64_t i = 0; i < count; i++) out[i] = orc_e4m3_encode(in[i]);
+}
+
+double orc_e4m3_decode(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Quantize a group: s = amax / 448 (IEEE fp32 division), codes = e4m3(v / s)
+ * with the fp32 quotient; all zero when amax == 0. */
+static float fp8_group(const float* v, int64_t count, int64_t stride, uint8_t* codes, int64_t cstride) {
+  float am = 0.0f;
+  for (int64_t i = 0; i < count; i++) {
+    float a = fabsf(v[i * stride]);
+    if (a > am) am = a;
+  }
+  volatile float s = am / 448.0f;
+  for (int64_t i = 0; i < count; i++) codes[i * cstride] = s != 0.0f ? orc_e4m3_encode(v[i * stride] / s) : 0;
+  return s;
+}
+
+/* Weights [n][k] -> codes [n][k] + scales [ceil(n/128)][k/128] (row-major),
+ * one scale per 128 x 128 block (the last block row may be shorter). */
+int orc_quantize_fp8_weights(const float* w, int64_t n, int64_t k, uint8_t* codes, float* scales) {
+  if (k % FP8_GROUP || n < 1) return -1;
+  const int64_t kg = k / FP8_GROUP, nb = (n + FP8_GROUP - 1) / FP8_GROUP;
+  for (int64_t bi = 0; bi < nb; bi++)
+    for (int64_t g = 0; g < kg; g++) {
+      const int64_t r0 = bi * FP8_GROUP, r1 = r0 + FP8_GROUP < n ? r0 + FP8_GROUP : n;
+      float am = 0.0f;
+      for (int64_t o = r0; o < r1; o++)
+        for (int64_t i = 0; i < FP8_GROUP; i++) {
+          float a = fabsf(w[o * k + g * FP8_GROUP + i]);
+          if (a > am) am = a;
+        }
+      volatile float s = am / 448.0f;
+      scales[bi * kg + g] = s;
+      for (int64_t o = r0; o < r1; o++)
+        for (int64_t i = 0; i < FP8_GROUP; i++) {
+          const int64_t e = o * k + g * FP8_GROUP + i;
+          codes[e] = s != 0.0f ? orc_e4m3_encode(w[e] / s) : 0;
+        }
+    }
+  return 0;
+}
+
+/* Activations [rows][k] -> codes [rows][k] + scales [rows][k/128]. */
+int orc_quantize_fp8_acts(const float* x, int rows, int64_t k, uint8_t* codes, float* scales) {
+  if (k % FP8_GROUP) return -1;
+  const int64_t kg = k / FP8_GROUP;
+  for (int r = 0; r < rows; r++)
+    for (int64_t g = 0; g < kg; g++)
+      scales[r * kg + g] = fp8_group(x + r * k + g * FP8_GROUP, FP8_GROUP, 1, codes + r * k + g * FP8_GROUP, 1);
+  return 0;
+}
+
+typedef struct {
+  const uint8_t* wc;
+  const float* ws;
+  int64_t n, k, kg;
+  const uint8_t* xc;
+  const float* xs;
+  int rows;
+  const int64_t* sel;
+  int64_t out_n;
+  float* y;
+} fp8_ctx;
+
+/* y[r][o] = sum_g s_w[o/128][g] * s_x[r][g] * sum_{k in g} w(o,k) x(r,k),
+ * the group sums exact (products of two E4M3 values and their sum of 128 fit
+ * a double exactly), ascending g in double, rounded once to float. */
+static void fp8_range(void* p, int64_t lo, int64_t hi) {
+  fp8_ctx* c = (fp8_ctx*)p;
+  for (int64_t t = lo; t < hi; t++) {
+    const int64_t o = c->sel ? c->sel[t] : t;
+    for (int r = 0; r < c->rows; r++) {
+      double acc = 0.0;
+      for (int64_t g = 0; g < c->kg; g++) {
+        double dot = 0.0;
+        for (int i = 0; i < FP8_GROUP; i++) {
+          const int64_t e = g * FP8_GROUP + i;
+          dot += orc_e4m3_decode(c->wc[o * c->k + e]) * orc_e4m3_decode(c->xc[(int64_t)r * c->k + e]);
+        }
+        acc += (double)c->ws[(o / FP8_GROUP) * c->kg + g] * (double)c->xs[(int64_t)r * c->kg + g] * dot;
+      }
+      c->y[(int64_t)r * c->out_n + t] = (float)acc;
+    }
+  }
+}
+
+/* FP8 GEMV from fp32 activations (quantized per 1 x 128 group first); with
+ * sel, only the output rows sel[0..nsel) (y is [rows][nsel]). */
+int orc_gemv_fp8(const uint8_t* wcodes, const float* wscales, int64_t n, int64_t k, const float* x, int rows,
+                 const int64_t* sel, int64_t nsel, float* y, int threads) {
+  if (k % FP8_GROUP || rows < 0) return -1;
+  for (int64_t i = 0; sel && i < nsel; i++)
+    if (sel[i] < 0 || sel[i] >= n) return -1;
+  const int64_t kg = k / FP8_GROUP;
+  uint8_t* xc = (uint8_t*)malloc((size_t)(rows * k) + 1);
+  float* xs = (float*)malloc(sizeof(float) * (size_t)(rows * kg) + 1);
+  orc_quantize_fp8_acts(x, rows, k, xc, xs);
+  fp8_ctx c = {wcodes, wscales, n, k, kg, xc, xs, rows, sel, sel ? nsel : n, y};
+  parallel_for(sel ? nsel : n, threads, fp8_range, &c);
+  free(xc);
+  free(xs);
+  return 0;
+}
+
 /* ------------------------------------------------------------ f16 lane --- */
 
 typedef struct {

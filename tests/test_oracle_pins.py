@@ -348,6 +348,92 @@ def test_moe_step_composes_its_pieces():
         assert np.array_equal(y[r], ref)
 
 
+# --------------------------------------------------------- FP8 lane ---
+def test_e4m3_hand_values():
+    v = np.array([1.0, 448.0, 2 ** -6, 2 ** -9, 2 ** -10, 3 * 2 ** -10, 1.0625, 1.1875, 500.0, -2.5, 0.0, -0.0, 1e9],
+                 np.float32)
+    # 1.0625 and 1.1875 are ties between mantissas 0/1 and 1/2: even wins; 2^-10 and 3*2^-10 are subnormal
+    # ties; past 448 saturates; the sign bit survives zero
+    want = [0x38, 0x7E, 0x08, 0x01, 0x00, 0x02, 0x38, 0x3A, 0x7E, 0xC2, 0x00, 0x80, 0x7E]
+    assert O.e4m3_encode(v).tolist() == want
+
+
+def test_e4m3_against_torch_float8():
+    import torch
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)  # 0x7F, 0xFF: NaN
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(O.e4m3_decode(codes), ref)
+    assert np.array_equal(O.e4m3_encode(ref.astype(np.float32)), codes)  # every code round-trips
+    # in range, PyTorch's conversion (round to nearest even) is the same encoding
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-12, 8, 20000))).astype(np.float32)
+    v = v[np.abs(v) < 448]
+    assert np.array_equal(O.e4m3_encode(v), torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_fp8_quantizers():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    x[1, 128:] = 0.0  # an all-zero group
+    xc, xs = O.quantize_fp8_acts(x)
+    assert xs[1, 1] == 0.0 and not xc[1, 128:].any()
+    for r in range(3):
+        for g in range(2):
+            grp = x[r, 128 * g:128 * (g + 1)]
+            if not grp.any():
+                continue
+            assert xs[r, g] == np.float32(np.abs(grp).max()) / np.float32(448)
+            i = np.abs(grp).argmax()  # the largest element lands on +-448
+            assert xc[r, 128 * g + i] & 0x7F == 0x7E
+    # weight blocks of 128 x 128: one scale each; a block's codes depend on that block alone
+    w = rng.standard_normal((200, 256)).astype(np.float32)
+    wc, ws = O.quantize_fp8_weights(w)
+    assert ws.shape == (2, 2)
+    w2 = w.copy()
+    w2[:128, :128] *= 100
+    wc2, ws2 = O.quantize_fp8_weights(w2)
+    assert np.array_equal(wc2[128:], wc[128:]) and np.array_equal(wc2[:, 128:], wc[:, 128:])
+    assert ws2[0, 0] == np.float32(np.abs(w2[:128, :128]).max()) / np.float32(448)
+    assert np.array_equal(ws2.ravel()[1:], ws.ravel()[1:])
+
+
+def test_fp8_gemv_exact_integer_case():
+    # every weight block and activation group holds a 448 (scale exactly 1) and small integers (exact in
+    # E4M3): the GEMV is the integer matrix product
+    rng = np.random.default_rng(6)
+    n, k, rows = 150, 384, 3
+    w = rng.integers(-16, 17, size=(n, k)).astype(np.float32)
+    x = rng.integers(-16, 17, size=(rows, k)).astype(np.float32)
+    for bi in range(0, n, 128):
+        for g in range(k // 128):
+            w[bi, 128 * g] = 448
+    for g in range(k // 128):
+        x[:, 128 * g + 5] = -448
+    wc, ws = O.quantize_fp8_weights(w)
+    assert np.all(ws == 1.0)
+    y = O.gemv_fp8(wc, ws, x)
+    ref = x.astype(np.int64) @ w.astype(np.int64).T
+    assert np.array_equal(y.astype(np.int64), ref) and np.array_equal(y, ref.astype(np.float32))
+    sel = np.array([0, 77, 149])
+    assert np.array_equal(O.gemv_fp8(wc, ws, x, sel=sel, threads=3), y[:, sel])
+
+
+def test_fp8_gemv_scales_and_brute_force():
+    rng = np.random.default_rng(7)
+    n, k, rows = 40, 256, 2
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    wc, ws = O.quantize_fp8_weights(w)
+    xc, xs = O.quantize_fp8_acts(x)
+    # dequantized operands, a plain float64 matrix product
+    wd = O.e4m3_decode(wc) * np.repeat(np.repeat(ws.astype(np.float64), 128, 0)[:n], 128, 1)
+    xd = O.e4m3_decode(xc) * np.repeat(xs.astype(np.float64), 128, 1)
+    y = O.gemv_fp8(wc, ws, x)
+    assert np.allclose(y, xd @ wd.T, rtol=1e-6, atol=1e-9)
+    # and the quantization error is that of 3-bit mantissas
+    assert np.abs(y - x.astype(np.float64) @ w.astype(np.float64).T).max() <= 0.15 * (np.abs(x) @ np.abs(w).T).max()
+
+
 # ------------------------------------------------- add + RMS norm ---
 def test_add_rmsnorm_hand_values_and_closed_forms():
     # [3, 4]: mean of squares 12.5, so y = [3, 4] / sqrt(12.5)
