@@ -23,6 +23,13 @@ int check_nk(int64_t n, int64_t k) {
   return QG_OK;
 }
 
+int check_fp8_nk(int64_t n, int64_t k) {
+  if (n < 1 || n > (1LL << 31) - 16) return fail(QG_ESHAPE, "n=%lld outside 1..2^31-16", (long long)n);
+  if (k < 128 || k % 128 || k > (1LL << 24))
+    return fail(QG_ESHAPE, "k=%lld is not a positive multiple of 128 up to 2^24", (long long)k);
+  return QG_OK;
+}
+
 int check_rows(int rows) {
   if (rows < 0 || rows > QG_MAX_ROWS) return fail(QG_EROWS, "rows=%d outside 0..%d", rows, QG_MAX_ROWS);
   return QG_OK;
@@ -84,13 +91,57 @@ int qgemv_fmt(int fmt, const void* w_image, int64_t n, int64_t k, const float* x
 extern "C" {
 
 int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, qg_stream stream) {
-  if (int st = check_fmt(fmt)) return st;
-  if (int st = check_nk(n, k)) return st;
+  if (fmt != QG_FMT_FP8)
+    if (int st = check_fmt(fmt)) return st;
+  if (int st = fmt == QG_FMT_FP8 ? check_fp8_nk(n, k) : check_nk(n, k)) return st;
   if (!w) return fail(QG_EINVAL, "w is null");
   if (!aligned(w, 16)) return fail(QG_EALIGN, "w %p is not 16-byte aligned", (const void*)w);
   if (int st = check_image(image, "image")) return st;
   if (int st = check_device()) return st;
+  if (fmt == QG_FMT_FP8) {
+    if (int st = launch_fp8_quantize_weights(w, n, k, image, (hipStream_t)stream)) return st;
+    return ok();
+  }
   if (int st = launch_quantize_weights(fmt, w, n, k, image, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qg_prepare_fp8(const float* x, int rows, int64_t k, void* ws, size_t ws_bytes, qg_stream stream) {
+  if (int st = check_x(x, rows, k, QG_MAX_PREP_ROWS)) return st;
+  if (k % 128) return fail(QG_ESHAPE, "k=%lld is not a multiple of 128", (long long)k);
+  if (int st = check_ws(ws, ws_bytes, fp8_ws_bytes(rows, k), "the FP8 activation rows")) return st;
+  if (int st = check_device()) return st;
+  if (int st = launch_fp8_prepare(x, rows, k, ws, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qgemv_fp8_prepared(const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
+                       qg_stream stream) {
+  if (int st = check_rows(rows)) return st;
+  if (int st = check_fp8_nk(n, k)) return st;
+  if (int st = check_image(w_image, "w_image")) return st;
+  if (int st = check_y(y)) return st;
+  if (rows == 0) return ok();
+  if (!ws) return fail(QG_EINVAL, "ws is null");
+  if (!aligned(ws, 256)) return fail(QG_EALIGN, "ws %p is not 256-byte aligned", ws);
+  if (int st = check_device()) return st;
+  if (int st = launch_gemv_fp8(w_image, n, k, ws, rows, y, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int qgemv_fp8(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+              size_t ws_bytes, qg_stream stream) {
+  if (int st = check_rows(rows)) return st;
+  if (int st = check_fp8_nk(n, k)) return st;
+  if (int st = check_image(w_image, "w_image")) return st;
+  if (int st = check_y(y)) return st;
+  if (rows == 0) return ok();
+  if (int st = check_x(x, rows, k, QG_MAX_ROWS)) return st;
+  if (int st = check_ws(ws, ws_bytes, fp8_ws_bytes(rows, k), "the FP8 activation rows")) return st;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (int st = launch_fp8_prepare(x, rows, k, ws, s)) return st;
+  if (int st = launch_gemv_fp8(w_image, n, k, ws, rows, y, s)) return st;
   return ok();
 }
 

@@ -1,0 +1,272 @@
+// qg_fp8.hip -- the FP8 lane: block-FP8 weights and dynamic 1 x 128 FP8
+// activation groups (the drama page's backbone section: its MoE experts are
+// block-FP8 and its activations are quantized per 1 x 128 group as they are
+// produced), on gfx950's v_mfma_scale_f32_16x16x128_f8f6f4.
+//
+// Formats.  Elements are OCP E4M3 (bias 7, three mantissa bits, largest
+// finite 448, round to nearest even, saturating).  A weight block is 128 rows x
+// 128 columns with one fp32 scale amax / 448; an activation group is 128
+// consecutive columns of one row with its own fp32 scale.  One 16x16x128 MFMA
+// covers exactly one group: its fp32 result for (weight row, activation row)
+// is the group's dot of the codes, which the kernel multiplies by the two
+// scales and adds, group after group.
+//
+// Weight image.  16-row tiles of 128-column groups: tile t, group g is one
+// 2 KB block in which lane l = i + 16q of a wave finds its 32 bytes at 32*l,
+// the codes of row 16t + i, columns 128g + 32q .. 128g + 32q + 31 (the MFMA's
+// A operand; its B operand pairs byte e of lane (j, q) with byte e of lane
+// (i, q)).  Groups of a tile follow each other, tiles follow each other, rows
+// past n are zero.  Then (256-byte aligned) the fp32 block scales
+// [ceil(n/128)][k/128], row major.
+#include <hip/hip_runtime.h>
+
+#include "qg_device.h"
+#include "qg_internal.h"
+#include "qg_launch.h"
+
+namespace qg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int F8_GROUP = 128;
+constexpr int F8_STEP_BYTES = 2048;  // one (tile, group) block
+constexpr int F8_E8M0_ONE = 127;     // MFMA operand scale 2^0
+
+// E4M3 code of f: round to nearest even on the fp32 mantissa, magnitudes from
+// 448 up saturate to 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fabsf(f);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // subnormal: multiples of 2^-9 (8: min normal)
+  const uint32_t ab = __float_as_uint(a);
+  int e = (int)(ab >> 23) - 127;
+  uint32_t keep = (ab >> 20) & 7u;
+  const uint32_t rest = ab & 0xFFFFFu;
+  keep += (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ? 1u : 0u;
+  if (keep == 8u) {
+    keep = 0u;
+    e += 1;
+  }
+  if (e > 8 || (e == 8 && keep > 6u)) return sign | 0x7Eu;
+  return sign | ((uint32_t)(e + 7) << 3) | keep;
+}
+
+// ------------------------------------------------------- weight image ---
+// One workgroup per (128-row block, group): thread t takes row t / 2, half t % 2
+// of the group (64 columns).
+__global__ __launch_bounds__(256) void fp8_quantize_weights_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                                   int64_t kg, int64_t np16,
+                                                                   uint8_t* __restrict__ img,
+                                                                   float* __restrict__ scales) {
+  __shared__ float s_max[256 / WAVE];
+  const int64_t bi = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+  const int64_t o = bi * F8_GROUP + (tid >> 1);
+  const int h = tid & 1;
+  float v[64];
+  float am = 0.0f;
+  const float* src = w + o * k + g * F8_GROUP + 64 * h;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const float4 a = o < n ? reinterpret_cast<const float4*>(src)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[4 * j] = a.x, v[4 * j + 1] = a.y, v[4 * j + 2] = a.z, v[4 * j + 3] = a.w;
+    am = fmaxf(am, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+  }
+  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if (lane == 0) s_max[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float s = am / 448.0f;
+  if (tid == 0) scales[bi * kg + g] = s;
+  if (o >= np16) return;  // past the image's last tile
+  const int64_t t = o >> 4, i = o & 15;
+  uint8_t* dst = img + (t * kg + g) * F8_STEP_BYTES;
+#pragma unroll
+  for (int qq = 0; qq < 2; qq++) {  // lanes i + 16q, q = 2h + qq: 32 columns each
+    uint32_t wd[8];
+#pragma unroll
+    for (int d = 0; d < 8; d++) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+        const float x = v[qq * 32 + d * 4 + b];
+        word |= (s != 0.0f ? e4m3_code(x / s) : 0u) << (8 * b);
+      }
+      wd[d] = word;
+    }
+    uint4* p = reinterpret_cast<uint4*>(dst + (i + 16 * (2 * h + qq)) * 32);
+    p[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    p[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+  }
+}
+
+int launch_fp8_quantize_weights(const float* w, int64_t n, int64_t k, void* image, hipStream_t s) {
+  const int64_t kg = k / F8_GROUP, nb = (n + F8_GROUP - 1) / F8_GROUP;
+  uint8_t* img = static_cast<uint8_t*>(image);
+  float* scales = reinterpret_cast<float*>(img + fp8_scale_offset(n, k));
+  hipLaunchKernelGGL(fp8_quantize_weights_kernel, dim3((unsigned)nb, (unsigned)kg), dim3(256), 0, s, w, n, k, kg,
+                     f16_tiles(n) * 16, img, scales);
+  return hip_status(hipGetLastError(), "fp8_quantize_weights_kernel");
+}
+
+// ---------------------------------------------------- activation groups ---
+// One wave per (row, group): two columns per lane.  Codes [rows][k] then fp32
+// scales [rows][k/128] (the FP8 workspace).
+__global__ __launch_bounds__(256) void fp8_prepare_kernel(const float* __restrict__ x, int rows, int64_t k, int64_t kg,
+                                                          uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int64_t wi = (int64_t)blockIdx.x * (256 / WAVE) + (threadIdx.x / WAVE);
+  const int lane = threadIdx.x % WAVE;
+  if (wi >= (int64_t)rows * kg) return;  // whole waves
+  const int64_t r = wi / kg, g = wi - r * kg;
+  const float2 v = reinterpret_cast<const float2*>(x + r * k + g * F8_GROUP)[lane];
+  float am = fmaxf(fabsf(v.x), fabsf(v.y));
+  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  const float s = am / 448.0f;
+  const uint32_t c0 = s != 0.0f ? e4m3_code(v.x / s) : 0u, c1 = s != 0.0f ? e4m3_code(v.y / s) : 0u;
+  reinterpret_cast<uint16_t*>(codes + r * k + g * F8_GROUP)[lane] = (uint16_t)(c0 | (c1 << 8));
+  if (lane == 0) scales[wi] = s;
+}
+
+int launch_fp8_prepare(const float* x, int rows, int64_t k, void* ws, hipStream_t s) {
+  const int64_t kg = k / F8_GROUP;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int64_t waves = (int64_t)rows * kg;
+  hipLaunchKernelGGL(fp8_prepare_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, rows, k, kg, w,
+                     reinterpret_cast<float*>(w + fp8_ws_scale_offset(rows, k)));
+  return hip_status(hipGetLastError(), "fp8_prepare_kernel");
+}
+
+// ----------------------------------------------------------------- GEMV ---
+template <int NT>
+struct F8Step {
+  uint4 a[NT][2];  // 32 weight codes per tile
+  uint4 b[2];      // 32 activation codes
+  float sx;        // the activation group's scale
+  float sw[NT];    // the weight blocks' scales
+};
+
+template <int NT>
+__device__ __forceinline__ void f8_load(F8Step<NT>& st, const uint8_t* const (&wt)[NT], const float* const (&wsr)[NT],
+                                        const uint8_t* xc, const float* xs, int64_t g) {
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    const uint4* p = reinterpret_cast<const uint4*>(wt[t] + g * F8_STEP_BYTES);
+    st.a[t][0] = ld16_stream(p);
+    st.a[t][1] = ld16_stream(p + 1);
+    st.sw[t] = wsr[t][g];
+  }
+  const uint4* xb = reinterpret_cast<const uint4*>(xc + g * F8_GROUP);
+  st.b[0] = xb[0];
+  st.b[1] = xb[1];
+  st.sx = xs[g];
+}
+
+template <int NT>
+__device__ __forceinline__ void f8_compute(v4f (&acc)[NT], const F8Step<NT>& st) {
+  v8i b;
+  __builtin_memcpy(&b, &st.b, 32);
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    v8i a;
+    __builtin_memcpy(&a, &st.a[t], 32);
+    const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                    F8_E8M0_ONE, 0, F8_E8M0_ONE);
+    const float m = st.sw[t] * st.sx;
+#pragma unroll
+    for (int v = 0; v < 4; v++) acc[t][v] = __builtin_fmaf(c[v], m, acc[t][v]);
+  }
+}
+
+// NT 16-row tiles per workgroup step, S waves over contiguous group ranges
+// (added left to right at the end), LA groups in flight; persistent over tile
+// groups.  A row's result depends on its own activations, K and N only.
+template <int NT, int S, int LA>
+__global__ __launch_bounds__(S * WAVE) void gemv_fp8_kernel(const uint8_t* __restrict__ img,
+                                                            const float* __restrict__ wsc, int64_t N, int64_t K,
+                                                            const uint8_t* __restrict__ xcodes,
+                                                            const float* __restrict__ xscales, int R,
+                                                            float* __restrict__ y, int64_t tgroups) {
+  __shared__ float red[S * NT * 4 * WAVE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
+  const int i = lane & 15, q = lane >> 4;
+  const int64_t kg = K / F8_GROUP, tiles = (N + 15) / 16;
+  const int64_t g0 = kg * wave / S, g1 = kg * (wave + 1) / S;  // this wave's groups
+  const int64_t ng = g1 - g0;
+  const int xr = i < R ? i : R - 1;  // activation row of this lane's column
+  const uint8_t* xc = xcodes + (int64_t)xr * K + 32 * q;
+  const float* xs = xscales + (int64_t)xr * kg;
+  for (int64_t grp = blockIdx.x; grp < tgroups; grp += gridDim.x) {
+    const uint8_t* wt[NT];
+    const float* wsr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      int64_t tt = grp * NT + t;
+      tt = tt < tiles ? tt : tiles - 1;  // past the end: reread, store nothing
+      wt[t] = img + tt * kg * F8_STEP_BYTES + 32 * lane;
+      wsr[t] = wsc + (tt >> 3) * kg;  // 8 tiles per 128-row block
+    }
+    v4f acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+    // groups in order g0 .. g1 - 1, LA in flight
+    F8Step<NT> f[LA];
+#pragma unroll
+    for (int j = 0; j < LA; j++)
+      if (j < ng) f8_load<NT>(f[j], wt, wsr, xc, xs, g0 + j);
+    for (int64_t st = 0; st < ng; st += LA) {
+#pragma unroll
+      for (int j = 0; j < LA; j++) {
+        if (st + j < ng) {
+          f8_compute<NT>(acc, f[j]);
+          if (st + j + LA < ng) f8_load<NT>(f[j], wt, wsr, xc, xs, g0 + st + j + LA);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) red[((wave * NT + t) * 4 + v) * WAVE + lane] = acc[t][v];
+    __syncthreads();
+    if (wave == 0 && i < R) {
+#pragma unroll
+      for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          float a = red[(t * 4 + v) * WAVE + lane];
+          for (int s2 = 1; s2 < S; s2++) a += red[((s2 * NT + t) * 4 + v) * WAVE + lane];
+          const int64_t row = (grp * NT + t) * 16 + 4 * q + v;
+          if (row < N) y[(int64_t)i * N + row] = a;
+        }
+    }
+  }
+}
+
+template <int NT, int S, int LA>
+static void launch_fp8_t(const uint8_t* img, const float* wsc, int64_t n, int64_t k, const uint8_t* xc,
+                         const float* xs, int rows, float* y, hipStream_t s) {
+  auto kern = gemv_fp8_kernel<NT, S, LA>;
+  const int64_t groups = (f16_tiles(n) + NT - 1) / NT;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, S * WAVE, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t g = (int64_t)device_cus() * per_cu;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(groups < g ? groups : g)), dim3(S * WAVE), 0, s, img, wsc, n, k, xc, xs,
+                     rows, y, groups);
+}
+
+int launch_gemv_fp8(const void* image, int64_t n, int64_t k, const void* ws, int rows, float* y, hipStream_t s) {
+  const uint8_t* img = static_cast<const uint8_t*>(image);
+  const float* wsc = reinterpret_cast<const float*>(img + fp8_scale_offset(n, k));
+  const uint8_t* xc = static_cast<const uint8_t*>(ws);
+  const float* xs = reinterpret_cast<const float*>(xc + fp8_ws_scale_offset(rows, k));
+  const int64_t t16 = f16_tiles(n);
+  if (t16 >= 4096) launch_fp8_t<4, 4, 2>(img, wsc, n, k, xc, xs, rows, y, s);
+  else if (t16 >= 256) launch_fp8_t<1, 4, 4>(img, wsc, n, k, xc, xs, rows, y, s);
+  else launch_fp8_t<1, 8, 4>(img, wsc, n, k, xc, xs, rows, y, s);
+  return hip_status(hipGetLastError(), "gemv_fp8_kernel");
+}
+
+}  // namespace qg

@@ -85,9 +85,15 @@ int qg_last_error_detail(char* buf, size_t len) {
 size_t qg_image_bytes(int fmt, int64_t n, int64_t k) {
   if (n < 1 || k < 1) return 0;
   if (fmt == QG_FMT_F16) return k % 8 ? 0 : (size_t)f16_image_bytes(n, k);
+  if (fmt == QG_FMT_FP8) return k % 128 ? 0 : fp8_image_bytes(n, k);
   if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return 0;
   if (k % QK) return 0;
   return image_total_bytes(fmt, n, k);
+}
+
+size_t qg_fp8_workspace_bytes(int rows, int64_t k) {
+  if (rows < 1 || rows > QG_MAX_PREP_ROWS || k < 128 || k % 128) return 0;
+  return fp8_ws_bytes(rows, k);
 }
 
 size_t qg_workspace_bytes(int rows, int64_t k) {
@@ -101,9 +107,14 @@ size_t qg_grouped_workspace_bytes(int x_rows, int64_t k, int m) {
 }
 
 static int check_pack_args(int fmt, const void* a, int64_t n, int64_t k, const void* b) {
-  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0 && fmt != QG_FMT_F16)
-    return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1), Q4_0 (2) or F16 (3)", fmt);
+  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0 && fmt != QG_FMT_F16 && fmt != QG_FMT_FP8)
+    return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1), Q4_0 (2), F16 (3) or FP8 (4)", fmt);
   if (!a || !b) return fail(QG_EINVAL, "null buffer");
+  if (fmt == QG_FMT_FP8) {
+    if (n < 1 || k < 128 || k % 128)
+      return fail(QG_ESHAPE, "n=%lld k=%lld (need n >= 1, k a positive multiple of 128)", (long long)n, (long long)k);
+    return QG_OK;
+  }
   if (fmt == QG_FMT_F16) {
     if (n < 1 || k < 8 || k % 8)
       return fail(QG_ESHAPE, "n=%lld k=%lld (need n >= 1, k a positive multiple of 8)", (long long)n, (long long)k);
@@ -131,9 +142,33 @@ static void f16_pack_host(const uint16_t* w, int64_t n, int64_t k, uint16_t* img
       }
 }
 
+// FP8 image chunk <-> canonical codes [n][k] + scales [ceil(n/128)][k/128]:
+// the 32 bytes of lane l = i + 16q of (tile t, group g) are the codes of row
+// 16t + i, columns 128g + 32q .. + 31; the scales are copied as they are.
+static void fp8_pack_host(uint8_t* canon, int64_t n, int64_t k, uint8_t* img, bool unpack) {
+  const int64_t kg = k / 128, tiles = f16_tiles(n), nb = (n + 127) / 128;
+  for (int64_t t = 0; t < tiles; t++)
+    for (int64_t g = 0; g < kg; g++)
+      for (int l = 0; l < 64; l++) {
+        const int64_t row = 16 * t + l % 16, k0 = 128 * g + 32 * (l / 16);
+        uint8_t* chunk = img + ((t * kg + g) * 64 + l) * 32;
+        if (row >= n) continue;
+        if (unpack) memcpy(canon + row * k + k0, chunk, 32);
+        else memcpy(chunk, canon + row * k + k0, 32);
+      }
+  uint8_t* sc = img + fp8_scale_offset(n, k);
+  if (unpack) memcpy(canon + n * k, sc, (size_t)(nb * kg * 4));
+  else memcpy(sc, canon + n * k, (size_t)(nb * kg * 4));
+}
+
 int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image) {
   int st = check_pack_args(fmt, blocks, n, k, image);
   if (st) return st;
+  if (fmt == QG_FMT_FP8) {
+    memset(image, 0, fp8_image_bytes(n, k));
+    fp8_pack_host((uint8_t*)blocks, n, k, (uint8_t*)image, false);
+    return ok();
+  }
   if (fmt == QG_FMT_F16) {
     memset(image, 0, (size_t)f16_image_bytes(n, k));
     f16_pack_host((const uint16_t*)blocks, n, k, (uint16_t*)image, false);
@@ -159,6 +194,10 @@ int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image
 int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* blocks) {
   int st = check_pack_args(fmt, image, n, k, blocks);
   if (st) return st;
+  if (fmt == QG_FMT_FP8) {
+    fp8_pack_host((uint8_t*)blocks, n, k, (uint8_t*)image, true);
+    return ok();
+  }
   if (fmt == QG_FMT_F16) {
     f16_pack_host((uint16_t*)blocks, n, k, (uint16_t*)image, true);
     return ok();

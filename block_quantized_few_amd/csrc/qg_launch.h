@@ -69,6 +69,9 @@ int launch_swiglu_q8(const float* gu, int m, int64_t ffn, void* hprep, hipStream
 // f16 lane.
 int launch_gemv_f16(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s);
 int launch_f16_pack(const uint16_t* w, int64_t n, int64_t k, void* image, hipStream_t s);
+int launch_fp8_quantize_weights(const float* w, int64_t n, int64_t k, void* image, hipStream_t s);
+int launch_fp8_prepare(const float* x, int rows, int64_t k, void* ws, hipStream_t s);
+int launch_gemv_fp8(const void* image, int64_t n, int64_t k, const void* ws, int rows, float* y, hipStream_t s);
 
 // MoE glue.
 int launch_moe_route(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,

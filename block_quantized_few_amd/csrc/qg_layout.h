@@ -76,6 +76,18 @@ QG_HD int64_t f16_steps(int64_t k) { return (k + 31) / 32; }
 QG_HD int64_t f16_tiles(int64_t n) { return (n + 15) / 16; }
 QG_HD int64_t f16_image_bytes(int64_t n, int64_t k) { return f16_tiles(n) * f16_steps(k) * 1024; }
 
+// FP8 image: 16-row tiles of 128-column groups, 2 KB per (tile, group), then
+// (256-byte aligned) the fp32 scales of 128 x 128 blocks [ceil(n/128)][k/128].
+// FP8 workspace: codes [rows][k], then (aligned) fp32 scales [rows][k/128].
+QG_HD size_t fp8_scale_offset(int64_t n, int64_t k) { return align256((size_t)f16_tiles(n) * (size_t)(k / 128) * 2048); }
+QG_HD size_t fp8_image_bytes(int64_t n, int64_t k) {
+  return fp8_scale_offset(n, k) + align256((size_t)((n + 127) / 128) * (size_t)(k / 128) * 4);
+}
+QG_HD size_t fp8_ws_scale_offset(int64_t rows, int64_t k) { return align256((size_t)rows * (size_t)k); }
+QG_HD size_t fp8_ws_bytes(int64_t rows, int64_t k) {
+  return fp8_ws_scale_offset(rows, k) + align256((size_t)rows * (size_t)(k / 128) * 4);
+}
+
 // Byte offset of row o's part of block b (Q8_0: its low half; the high half
 // is 256 bytes further).
 QG_HD size_t cell_row_offset(int fmt, int64_t o, int64_t b, int64_t kbp) {

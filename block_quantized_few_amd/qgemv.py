@@ -13,7 +13,7 @@ import os
 import numpy as np
 import torch
 
-Q8_0, Q4_0, F16 = 1, 2, 3
+Q8_0, Q4_0, F16, FP8 = 1, 2, 3, 4
 MAX_ROWS = 16
 MAX_PREP_ROWS = 8192
 MAX_ASSIGN = 2048
@@ -49,6 +49,12 @@ _SIGS = {
     "qg_pack_image": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p]),
     "qg_unpack_image": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p]),
     "qg_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64]),
+    "qg_fp8_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64]),
+    "qg_prepare_fp8": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qgemv_fp8_prepared": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
+                                     C.c_void_p]),
+    "qgemv_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
+                            C.c_size_t, C.c_void_p]),
     "qg_grouped_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64, C.c_int]),
     "qg_status_string": (C.c_char_p, [C.c_int]),
     "qg_last_error_detail": (C.c_int, [C.c_char_p, C.c_size_t]),
@@ -151,9 +157,30 @@ def pack_image(fmt, blocks, n, k):
     return out
 
 
+def pack_fp8(codes, scales):
+    """Canonical block-FP8 weights (codes [n][k] uint8, scales [ceil(n/128)][k/128] fp32) -> FP8 image bytes."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    if scales.shape != ((n + 127) // 128, k // 128):
+        raise ValueError("scales must be [ceil(n/128)][k/128]")
+    canon = np.concatenate([codes.ravel(), scales.view(np.uint8).ravel()])
+    return pack_image(FP8, canon, n, k)
+
+
+def unpack_fp8(image, n, k):
+    canon = unpack_image(FP8, image, n, k)
+    return canon[:n * k].reshape(n, k), canon[n * k:].view(np.float32).reshape((n + 127) // 128, k // 128)
+
+
 def unpack_image(fmt, image, n, k):
     image = np.ascontiguousarray(image, dtype=np.uint8)
-    out = np.empty((n, k), np.uint16) if fmt == F16 else np.empty((n, k // 32, 34 if fmt == Q8_0 else 18), np.uint8)
+    if fmt == FP8:
+        out = np.empty(n * k + ((n + 127) // 128) * (k // 128) * 4, np.uint8)
+    elif fmt == F16:
+        out = np.empty((n, k), np.uint16)
+    else:
+        out = np.empty((n, k // 32, 34 if fmt == Q8_0 else 18), np.uint8)
     _check(lib().qg_unpack_image(fmt, image.ctypes.data_as(C.c_void_p), n, k, out.ctypes.data_as(C.c_void_p)))
     return out
 
@@ -214,6 +241,38 @@ def _qgemv(fn, image, n, k, x, y, ws):
     if ws is None:
         ws = empty_ws(max(rows, 1), k, x.device)
     _check(fn(_p(image), n, k, _p(x), rows, _p(y), _p(ws), ws.numel(), _stream()))
+    return y
+
+
+def fp8_workspace_bytes(rows, k):
+    return int(lib().qg_fp8_workspace_bytes(rows, k))
+
+
+def prepare_fp8(x, ws=None):
+    """FP8 activation groups of x [rows][k] (qg_prepare_fp8): the workspace tensor."""
+    _dev(x, torch.float32, "x")
+    rows, k = x.shape
+    if ws is None:
+        ws = torch.empty(max(1, fp8_workspace_bytes(rows, k)), dtype=torch.uint8, device=x.device)
+    _check(lib().qg_prepare_fp8(_p(x), rows, k, _p(ws), ws.numel(), _stream()))
+    return ws
+
+
+def qgemv_fp8(image, n, k, x, y=None, ws=None):
+    _dev(x, torch.float32, "x")
+    rows = x.shape[0]
+    if y is None:
+        y = torch.empty((rows, n), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, fp8_workspace_bytes(max(rows, 1), k)), dtype=torch.uint8, device=x.device)
+    _check(lib().qgemv_fp8(_p(image), n, k, _p(x), rows, _p(y), _p(ws), ws.numel(), _stream()))
+    return y
+
+
+def qgemv_fp8_prepared(image, n, k, ws, rows, y=None):
+    if y is None:
+        y = torch.empty((rows, n), dtype=torch.float32, device=ws.device)
+    _check(lib().qgemv_fp8_prepared(_p(image), n, k, _p(ws), rows, _p(y), _stream()))
     return y
 
 

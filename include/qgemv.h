@@ -49,6 +49,20 @@
  * order of the matrix core's 16x16x32 halfword product, so one wave load is
  * 1 KB of consecutive bytes.  Size: ceil(n/16) * ceil(k/32) * 1024 bytes.
  *
+ * FP8 lane (block-FP8 weights, dynamic 1 x 128 FP8 activation groups: the
+ * drama page's backbone section).  Elements are OCP E4M3 (largest finite 448;
+ * round to nearest even, saturating).  Weights: one fp32 scale amax/448 per
+ * block of 128 rows x 128 columns, codes e4m3(w / scale); canonical form
+ * codes [n][k] bytes followed by the scales [ceil(n/128)][k/128] fp32.
+ * Activations: per row and group of 128 columns, scale amax/448 and codes
+ * e4m3(x / scale) (qg_prepare_fp8; workspace codes [rows][k], then, 256-byte
+ * aligned, scales [rows][k/128]).  y[r][o] = sum_g s_w s_x (sum over the
+ * group's 128 code products), the group sum from the matrix core's 16x16x128
+ * FP8 product in fp32.  Image: 16-row tiles of 128-column groups, 2 KB per
+ * (tile, group) with lane l = i + 16j's 32 bytes the codes of row 16t + i,
+ * columns 128g + 32j .. + 31; then (256-byte aligned) the scales as in the
+ * canonical form.  k must be a multiple of 128.
+ *
  * Conventions.
  *   - Pointers are device pointers unless marked (host).  `stream` is a
  *     hipStream_t (NULL = the null stream).  Device calls enqueue work on
@@ -92,7 +106,7 @@ enum {
   QG_EDEVICE = -7     /* the current device is not a gfx950 GPU */
 };
 
-enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3 };
+enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3, QG_FMT_FP8 = 4 };
 
 #define QG_MAX_ROWS 16        /* activation rows per GEMV call */
 #define QG_MAX_PREP_ROWS 8192 /* rows one qg_prepare_rows call quantizes */
@@ -114,6 +128,10 @@ int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image
 
 /* Host -> host inverse of qg_pack_image (padding is dropped). */
 int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* blocks);
+
+/* Bytes of the FP8 workspace of `rows` activation rows of length k (k a
+ * multiple of 128); 0 for an invalid shape. */
+size_t qg_fp8_workspace_bytes(int rows, int64_t k);
 
 /* Bytes of the workspace that holds `rows` quantized activation rows of
  * length k (codes, scales and code sums).  0 for an invalid shape. */
@@ -186,6 +204,20 @@ int qg_f16_image(const uint16_t* w, int64_t n, int64_t k, void* image, qg_stream
  * of two per row and k range), so the result is fp32-accurate.  A row's bits
  * do not depend on the other rows of the call. */
 int gemv_f16(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream);
+
+/* FP8 lane, activation groups: x [rows][k] fp32 (1 <= rows <= 8192) into the
+ * FP8 workspace ws (qg_fp8_workspace_bytes(rows, k) bytes). */
+int qg_prepare_fp8(const float* x, int rows, int64_t k, void* ws, size_t ws_bytes, qg_stream stream);
+
+/* FP8 lane GEMV on rows prepared by qg_prepare_fp8 (same rows and k):
+ * y [rows][n] fp32, 0 <= rows <= 16.  w_image: the FP8 image (qg_pack_image
+ * or qg_quantize_weights with QG_FMT_FP8). */
+int qgemv_fp8_prepared(const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
+                       qg_stream stream);
+
+/* qg_prepare_fp8 then qgemv_fp8_prepared: x [rows][k] fp32, y [rows][n]. */
+int qgemv_fp8(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+              size_t ws_bytes, qg_stream stream);
 
 /* Several independent q8-lane projections with the same row count in one
  * launch (a decode layer's Q/K/V/O/gate/up/down).  Each entry's rows must

@@ -109,6 +109,28 @@ def test_f16_image_layout(n, k):
     assert np.array_equal(q.unpack_image(q.F16, img, n, k), w)
 
 
+@pytest.mark.parametrize("n,k", [(16, 128), (33, 256), (200, 384)])
+def test_fp8_image_layout(n, k):
+    # lane l = i + 16j of (tile t, group g) holds codes[16t + i][128g + 32j : 128g + 32j + 32]: the zero-padded
+    # codes cut into [t][i][g][j][32] and reordered to [t][g][j][i][32]; then the scales, 256-byte aligned
+    rng = np.random.default_rng(n + k)
+    codes = rng.integers(0, 256, size=(n, k), dtype=np.uint64).astype(np.uint8)
+    scales = rng.random(((n + 127) // 128, k // 128)).astype(np.float32)
+    T, G = -(-n // 16), k // 128
+    pad = np.zeros((T * 16, k), np.uint8)
+    pad[:n] = codes
+    want = pad.reshape(T, 16, G, 4, 32).transpose(0, 2, 3, 1, 4).reshape(-1)
+    img = q.pack_fp8(codes, scales)
+    assert img.size == q.image_bytes(q.FP8, n, k)
+    assert np.array_equal(img[:want.size], want)
+    off = -(-want.size // 256) * 256
+    assert np.array_equal(img[off:off + scales.nbytes].view(np.float32), scales.ravel())
+    c2, s2 = q.unpack_fp8(img, n, k)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+    assert q.image_bytes(q.FP8, n, 100) == 0
+    assert q.fp8_workspace_bytes(3, k) == 3 * k + (-(-3 * k) % 256) + 256 * (-(-(3 * (k // 128) * 4) // 256))
+
+
 def _status(fn, *args):
     L = q.lib()
     st = getattr(L, fn)(*args)
@@ -154,6 +176,21 @@ def test_validation_refuses_before_any_hip_call():
     assert st == -2
     st, msg = _status("qg_moe_route", V(A), 1, 2000, 8, -1, V(A), V(A), V(A), None)
     assert st == -2
+    # FP8 lane: k a multiple of 128, rows within bounds, workspace size
+    st, msg = _status("qgemv_fp8", V(A), 64, 96, V(A), 1, V(A), V(A), MB, None)
+    assert st == -2 and "k=96" in msg
+    st, msg = _status("qgemv_fp8", V(A), 64, 256, V(A), 17, V(A), V(A), MB, None)
+    assert st == -3
+    st, msg = _status("qgemv_fp8", V(A), 64, 256, V(A), 2, V(A), V(A), 100, None)
+    assert st == -5 and "ws_bytes=100" in msg
+    st, msg = _status("qg_prepare_fp8", V(A), 2, 200, V(A), MB, None)
+    assert st == -2
+    st, msg = _status("qgemv_fp8_prepared", V(A + 16), 64, 256, V(A), 1, V(A), None)
+    assert st == -4 and "w_image" in msg
+    st, msg = _status("qg_quantize_weights", q.FP8, V(A), 64, 96, V(A), None)
+    assert st == -2 and "k=96" in msg
+    st, msg = _status("qgemv_fp8", V(A), 64, 256, V(A), 0, V(A), V(A), 0, None)
+    assert st == 0
     # qg_add_rmsnorm_prepare: x, residual, gamma, eps, rows, k, h_out, y_out, ws, ws_bytes
     norm = lambda **kw: _status("qg_add_rmsnorm_prepare", V(kw.get("x", A)), None, V(kw.get("gamma", A)),
                                 C.c_float(kw.get("eps", 1e-5)), kw.get("rows", 2), kw.get("k", 2048), None,
