@@ -12,12 +12,13 @@
 // scales and adds, group after group.
 //
 // Weight image.  16-row tiles of 128-column groups: tile t, group g is one
-// 2 KB block in which lane l = i + 16q of a wave finds its 32 bytes at 32*l,
-// the codes of row 16t + i, columns 128g + 32q .. 128g + 32q + 31 (the MFMA's
-// A operand; its B operand pairs byte e of lane (j, q) with byte e of lane
-// (i, q)).  Groups of a tile follow each other, tiles follow each other, rows
-// past n are zero.  Then (256-byte aligned) the fp32 block scales
-// [ceil(n/128)][k/128], row major.
+// 2 KB block holding, for lane l = i + 16q of a wave, the codes of row 16t + i,
+// columns 128g + 32q .. 128g + 32q + 31 (the MFMA's A operand; its B operand
+// pairs byte e of lane (j, q) with byte e of lane (i, q)): the first 16 of them
+// at 16*l, the other 16 at 1024 + 16*l, so that each of the wave's two 16-byte
+// loads reads 1 KB of consecutive bytes.  Groups of a tile follow each other,
+// tiles follow each other, rows past n are zero.  Then (256-byte aligned) the
+// fp32 block scales [ceil(n/128)][k/128], row major.
 #include <hip/hip_runtime.h>
 
 #include "qg_device.h"
@@ -31,7 +32,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int F8_GROUP = 128;
 constexpr int F8_STEP_BYTES = 2048;  // one (tile, group) block
+constexpr int F8_HALF_U4 = 64;       // second 16 bytes of a lane: 1 KB on, in uint4
 constexpr int F8_E8M0_ONE = 127;     // MFMA operand scale 2^0
+constexpr int64_t F8_ROT = 7;        // start-group stride between neighbouring tile groups
 
 // E4M3 code of f: round to nearest even on the fp32 mantissa, magnitudes from
 // 448 up saturate to 448 (0x7E).
@@ -96,9 +99,9 @@ __global__ __launch_bounds__(256) void fp8_quantize_weights_kernel(const float* 
       }
       wd[d] = word;
     }
-    uint4* p = reinterpret_cast<uint4*>(dst + (i + 16 * (2 * h + qq)) * 32);
+    uint4* p = reinterpret_cast<uint4*>(dst + (i + 16 * (2 * h + qq)) * 16);
     p[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    p[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    p[F8_HALF_U4] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
   }
 }
 
@@ -154,7 +157,7 @@ __device__ __forceinline__ void f8_load(F8Step<NT>& st, const uint8_t* const (&w
   for (int t = 0; t < NT; t++) {
     const uint4* p = reinterpret_cast<const uint4*>(wt[t] + g * F8_STEP_BYTES);
     st.a[t][0] = ld16_stream(p);
-    st.a[t][1] = ld16_stream(p + 1);
+    st.a[t][1] = ld16_stream(p + F8_HALF_U4);
     st.sw[t] = wsr[t][g];
   }
   const uint4* xb = reinterpret_cast<const uint4*>(xc + g * F8_GROUP);
@@ -181,7 +184,9 @@ __device__ __forceinline__ void f8_compute(v4f (&acc)[NT], const F8Step<NT>& st)
 
 // NT 16-row tiles per workgroup step, S waves over contiguous group ranges
 // (added left to right at the end), LA groups in flight; persistent over tile
-// groups.  A row's result depends on its own activations, K and N only.
+// groups.  A row's result depends on its own activations, K, N and S only: a
+// wave starts its range at a group set by the tile's index / 4, the same for
+// NT = 1, 2 and 4, whatever the rows.
 template <int NT, int S, int LA>
 __global__ __launch_bounds__(S * WAVE) void gemv_fp8_kernel(const uint8_t* __restrict__ img,
                                                             const float* __restrict__ wsc, int64_t N, int64_t K,
@@ -197,33 +202,48 @@ __global__ __launch_bounds__(S * WAVE) void gemv_fp8_kernel(const uint8_t* __res
   const int xr = i < R ? i : R - 1;  // activation row of this lane's column
   const uint8_t* xc = xcodes + (int64_t)xr * K + 32 * q;
   const float* xs = xscales + (int64_t)xr * kg;
-  for (int64_t grp = blockIdx.x; grp < tgroups; grp += gridDim.x) {
-    const uint8_t* wt[NT];
-    const float* wsr[NT];
+  const uint8_t* wt[NT];
+  const float* wsr[NT];
+  int64_t lc = g0;  // next group to load
+  F8Step<NT> f[LA];
+  // Points the wave at tile group grp and puts its first LA groups in flight.
+  // The wave walks its groups from a tile-dependent start, wrapping round, so
+  // that tile groups in flight together read different offsets.
+  auto start = [&](int64_t grp) {
 #pragma unroll
     for (int t = 0; t < NT; t++) {
       int64_t tt = grp * NT + t;
       tt = tt < tiles ? tt : tiles - 1;  // past the end: reread, store nothing
-      wt[t] = img + tt * kg * F8_STEP_BYTES + 32 * lane;
+      wt[t] = img + tt * kg * F8_STEP_BYTES + 16 * lane;
       wsr[t] = wsc + (tt >> 3) * kg;  // 8 tiles per 128-row block
     }
+    lc = g0 + (ng ? ((grp * NT >> 2) * F8_ROT) % ng : 0);
+#pragma unroll
+    for (int j = 0; j < LA; j++)
+      if (j < ng) {
+        f8_load<NT>(f[j], wt, wsr, xc, xs, lc);
+        lc = lc + 1 == g1 ? g0 : lc + 1;
+      }
+  };
+  if (blockIdx.x < tgroups) start(blockIdx.x);
+  for (int64_t grp = blockIdx.x; grp < tgroups; grp += gridDim.x) {
     v4f acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
-    // groups in order g0 .. g1 - 1, LA in flight
-    F8Step<NT> f[LA];
-#pragma unroll
-    for (int j = 0; j < LA; j++)
-      if (j < ng) f8_load<NT>(f[j], wt, wsr, xc, xs, g0 + j);
     for (int64_t st = 0; st < ng; st += LA) {
 #pragma unroll
       for (int j = 0; j < LA; j++) {
         if (st + j < ng) {
           f8_compute<NT>(acc, f[j]);
-          if (st + j + LA < ng) f8_load<NT>(f[j], wt, wsr, xc, xs, g0 + st + j + LA);
+          if (st + j + LA < ng) {
+            f8_load<NT>(f[j], wt, wsr, xc, xs, lc);
+            lc = lc + 1 == g1 ? g0 : lc + 1;
+          }
         }
       }
     }
+    // every group is consumed: the next tile group's first loads fly during the reduction
+    if (grp + gridDim.x < tgroups) start(grp + gridDim.x);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NT; t++)
@@ -263,7 +283,11 @@ int launch_gemv_fp8(const void* image, int64_t n, int64_t k, const void* ws, int
   const uint8_t* xc = static_cast<const uint8_t*>(ws);
   const float* xs = reinterpret_cast<const float*>(xc + fp8_ws_scale_offset(rows, k));
   const int64_t t16 = f16_tiles(n);
-  if (t16 >= 4096) launch_fp8_t<4, 4, 2>(img, wsc, n, k, xc, xs, rows, y, s);
+  // For each n the same S (so the same sums) at every row count; above 8 rows
+  // wider tiles share each activation load where there are tiles enough.
+  if (t16 >= 4096 && rows > 8) launch_fp8_t<4, 2, 2>(img, wsc, n, k, xc, xs, rows, y, s);
+  else if (t16 >= 4096) launch_fp8_t<2, 2, 2>(img, wsc, n, k, xc, xs, rows, y, s);
+  else if (t16 >= 512 && rows > 8) launch_fp8_t<2, 4, 2>(img, wsc, n, k, xc, xs, rows, y, s);
   else if (t16 >= 256) launch_fp8_t<1, 4, 4>(img, wsc, n, k, xc, xs, rows, y, s);
   else launch_fp8_t<1, 8, 4>(img, wsc, n, k, xc, xs, rows, y, s);
   return hip_status(hipGetLastError(), "gemv_fp8_kernel");

@@ -143,18 +143,21 @@ static void f16_pack_host(const uint16_t* w, int64_t n, int64_t k, uint16_t* img
 }
 
 // FP8 image chunk <-> canonical codes [n][k] + scales [ceil(n/128)][k/128]:
-// the 32 bytes of lane l = i + 16q of (tile t, group g) are the codes of row
-// 16t + i, columns 128g + 32q .. + 31; the scales are copied as they are.
+// lane l = i + 16q of (tile t, group g) holds the codes of row 16t + i,
+// columns 128g + 32q .. + 31, the first 16 at 16*l and the other 16 at
+// 1024 + 16*l of the 2 KB block; the scales are copied as they are.
 static void fp8_pack_host(uint8_t* canon, int64_t n, int64_t k, uint8_t* img, bool unpack) {
   const int64_t kg = k / 128, tiles = f16_tiles(n), nb = (n + 127) / 128;
   for (int64_t t = 0; t < tiles; t++)
     for (int64_t g = 0; g < kg; g++)
       for (int l = 0; l < 64; l++) {
         const int64_t row = 16 * t + l % 16, k0 = 128 * g + 32 * (l / 16);
-        uint8_t* chunk = img + ((t * kg + g) * 64 + l) * 32;
         if (row >= n) continue;
-        if (unpack) memcpy(canon + row * k + k0, chunk, 32);
-        else memcpy(chunk, canon + row * k + k0, 32);
+        for (int h = 0; h < 2; h++) {
+          uint8_t* chunk = img + (t * kg + g) * 2048 + h * 1024 + l * 16;
+          if (unpack) memcpy(canon + row * k + k0 + 16 * h, chunk, 16);
+          else memcpy(chunk, canon + row * k + k0 + 16 * h, 16);
+        }
       }
   uint8_t* sc = img + fp8_scale_offset(n, k);
   if (unpack) memcpy(canon + n * k, sc, (size_t)(nb * kg * 4));

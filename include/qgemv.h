@@ -59,9 +59,10 @@
  * aligned, scales [rows][k/128]).  y[r][o] = sum_g s_w s_x (sum over the
  * group's 128 code products), the group sum from the matrix core's 16x16x128
  * FP8 product in fp32.  Image: 16-row tiles of 128-column groups, 2 KB per
- * (tile, group) with lane l = i + 16j's 32 bytes the codes of row 16t + i,
- * columns 128g + 32j .. + 31; then (256-byte aligned) the scales as in the
- * canonical form.  k must be a multiple of 128.
+ * (tile, group) in which lane l = i + 16j finds the codes of row 16t + i,
+ * columns 128g + 32j .. + 31, the first 16 at byte 16l and the other 16 at
+ * byte 1024 + 16l; then (256-byte aligned) the scales as in the canonical
+ * form.  k must be a multiple of 128.
  *
  * Conventions.
  *   - Pointers are device pointers unless marked (host).  `stream` is a

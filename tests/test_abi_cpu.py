@@ -111,15 +111,16 @@ def test_f16_image_layout(n, k):
 
 @pytest.mark.parametrize("n,k", [(16, 128), (33, 256), (200, 384)])
 def test_fp8_image_layout(n, k):
-    # lane l = i + 16j of (tile t, group g) holds codes[16t + i][128g + 32j : 128g + 32j + 32]: the zero-padded
-    # codes cut into [t][i][g][j][32] and reordered to [t][g][j][i][32]; then the scales, 256-byte aligned
+    # lane l = i + 16j of (tile t, group g) holds codes[16t + i][128g + 32j : 128g + 32j + 32] as two 16-byte
+    # halves h, at 16l and 1024 + 16l: the zero-padded codes cut into [t][i][g][j][h][16] and reordered to
+    # [t][g][h][j][i][16]; then the scales, 256-byte aligned
     rng = np.random.default_rng(n + k)
     codes = rng.integers(0, 256, size=(n, k), dtype=np.uint64).astype(np.uint8)
     scales = rng.random(((n + 127) // 128, k // 128)).astype(np.float32)
     T, G = -(-n // 16), k // 128
     pad = np.zeros((T * 16, k), np.uint8)
     pad[:n] = codes
-    want = pad.reshape(T, 16, G, 4, 32).transpose(0, 2, 3, 1, 4).reshape(-1)
+    want = pad.reshape(T, 16, G, 4, 2, 16).transpose(0, 2, 4, 3, 1, 5).reshape(-1)
     img = q.pack_fp8(codes, scales)
     assert img.size == q.image_bytes(q.FP8, n, k)
     assert np.array_equal(img[:want.size], want)

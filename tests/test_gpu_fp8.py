@@ -71,8 +71,9 @@ def test_fp8_gemv_parity(n, k):
     assert worst < 5e-5
 
 
-def test_fp8_rows_in_a_batch_equal_rows_alone():
-    n, k = 500, 2048
+@pytest.mark.parametrize("n", [500, 9000])  # 9000: wider tiles above 8 rows
+def test_fp8_rows_in_a_batch_equal_rows_alone(n):
+    k = 2048
     codes, scales = O.quantize_fp8_weights(gauss((n, k), 0.02, 29, 0).numpy())
     img = torch.from_numpy(q.pack_fp8(codes, scales)).cuda()
     x = torch.from_numpy(gauss((16, k), 1.0, 29, 1).numpy()).cuda()
@@ -103,9 +104,14 @@ def test_fp8_lm_head_sampled():
     wd = _dequant_w(codes, scales, len(sel))
     for rows in (1, 8, 16):
         x = gauss((rows, k), 1.0, 30, 32 + rows).numpy()
-        y = q.qgemv_fp8(img, n, k, torch.from_numpy(x).cuda()).cpu().numpy()[:, sel]
+        xd = torch.from_numpy(x).cuda()
+        yd = q.qgemv_fp8(img, n, k, xd)
+        y = yd.cpu().numpy()[:, sel]
         yo = O.gemv_fp8(codes, scales, x, threads=8)
         xc, xs = O.quantize_fp8_acts(x)
         e = _err(y, yo, wd, _dequant_x(xc, xs))
         log(f"  rows={rows} max error {e:.3e}")
         assert e <= TOL
+        # above 8 rows the launch takes wider tiles: the sums, and so the bits, stay those of a row alone
+        for r in (0, rows - 1):
+            assert torch.equal(yd[r], q.qgemv_fp8(img, n, k, xd[r:r + 1].contiguous())[0])
