@@ -426,19 +426,36 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
 
             ms = time_calls(torch, timer, stream, one, 200)
             out.append(entry(f"{lname} (7 projections)", lane, rows, ls.wbytes, ms, ls.launches))
+            if rows > q.FUSED_ROWS:
+                # the GEMV launch alone, on rows quantized once beforehand
+                acts = ctypes_arr(q._Act, [q._Act(x.data_ptr(), x.shape[1], w.data_ptr(), w.numel())
+                                           for x, w in zip(ls.xs, ls.wss)])
+                L.qg_prepare_rows_set(acts, len(ls.xs), rows, sh)
+                pre = [ctypes_arr(q._Proj, [q._Proj(ls.imgs[c][i].data_ptr(), n_, k_,
+                                                    ls.wss[LAYER_SRC.get(nm, 0)].data_ptr(), ls.ys[i].data_ptr())
+                                            for i, (nm, n_, k_) in enumerate(ls.layer)]) for c in range(ls.copies)]
+
+                def gemv(i, pre=pre, rows=rows, fmt=fmt):
+                    L.qgemv_set(fmt, pre[i % len(pre)], 7, rows, sh)
+
+                ms = time_calls(torch, timer, stream, gemv, 200)
+                out.append(entry(f"{lname} (7 projections), prepared rows", lane, rows, ls.wbytes, ms, 1))
         del ls
         print(f"[bench] sweep {lname} done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     layer1b.set_rows(1, synth, 1)
 
-    # LM head 128256 x 4096, f16 and Q8_0, two copies each
+    # LM head 128256 x 4096, f16, Q8_0 and FP8 (block-FP8 weights, 1 x 128 activation groups), two copies each
     n, k = 128256, 4096
     w16 = []
     q8 = []
+    f8 = []
     for c in range(2):
         w = synth.gaussian((n, k), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
         w16.append(q.f16_image(w.half()))
         q8.append(q.quantize_weights(q.Q8_0, w))
+        f8.append(q.quantize_weights(q.FP8, w))
         del w
+    f8b = q.image_bytes(q.FP8, n, k)
     for rows in (1, 2, 4, 8, 9, 16):
         x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(4, 32 + rows), device="cuda")
         y = torch.empty((rows, n), device="cuda")
@@ -446,12 +463,19 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
         xp, yp, wp, wn = x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel()
         p16 = [t.data_ptr() for t in w16]
         p8 = [t.data_ptr() for t in q8]
+        pf = [t.data_ptr() for t in f8]
         ms = time_calls(torch, timer, stream, lambda i: L.gemv_f16(p16[i % 2], n, k, xp, rows, yp, sh), 40)
         out.append(entry("lm head 128256x4096", "f16", rows, 2 * n * k, ms, 1))
         ms = time_calls(torch, timer, stream, lambda i: L.qgemv_q8_0(p8[i % 2], n, k, xp, rows, yp, wp, wn, sh), 40)
         out.append(entry("lm head 128256x4096", "q8_0", rows, q.image_bytes(q.Q8_0, n, k), ms,
                          1 if rows <= q.FUSED_ROWS else 2))
-    del w16, q8
+        wsf = q.prepare_fp8(x)
+        fp, fn = wsf.data_ptr(), wsf.numel()
+        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_fp8(pf[i % 2], n, k, xp, rows, yp, fp, fn, sh), 40)
+        out.append(entry("lm head 128256x4096", "fp8", rows, f8b, ms, 2))
+        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_fp8_prepared(pf[i % 2], n, k, fp, rows, yp, sh), 40)
+        out.append(entry("lm head 128256x4096, prepared rows", "fp8", rows, f8b, ms, 1))
+    del w16, q8, f8
     print(f"[bench] sweep lm head done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     out.extend(moe_sweep(torch, q, synth, L, sh, stream, timer))

@@ -331,6 +331,8 @@ __host__ __device__ constexpr int mp_w2(int H) { return H >= 4 ? 2 : 1; }
 __host__ __device__ constexpr int mp_nt(int H, int G, bool wide) {
   return wide ? (H == 2 || H == 4 ? (G == 2 ? 2 : 4) : (G == 2 ? 1 : 2)) : (H == 8 || G == 2 ? 1 : 2);
 }
+// block-pair steps in flight per wave (even: step j's lane-part pair is j & 1)
+__host__ __device__ constexpr int mp_la(int NT, int G) { return NT * G == 1 ? 4 : 2; }
 constexpr int MP_NV_MAX = 16;  // floats per lane a wave passes to the combine (NT * G * 4)
 
 __device__ __forceinline__ float lane_xor8(float v) {
@@ -504,21 +506,24 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
 #pragma unroll
   for (int t = 0; t < NT; t++)
     if (lane < nsv) sv[t] = ld16(scale[t] + (size_t)ad.sb0 * TILE + lane * 8);
-  MpStep<NT, G> s0, s1;
-  mp_load<FMT, NT, G, GATHER>(s0, ad, lane, blk(0));
-  mp_load<FMT, NT, G, GATHER>(s1, ad, lane, blk(1));
+  constexpr int MP_LA = mp_la(NT, G);
+  MpStep<NT, G> st[MP_LA];
+#pragma unroll
+  for (int jj = 0; jj < MP_LA; jj++)
+    if (jj < nsteps) mp_load<FMT, NT, G, GATHER>(st[jj], ad, lane, blk(jj));
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(ad.sl[t]));
     if (lane < nsv) dst[lane] = sv[t];
     for (int e = lane + WAVE; e < nsv; e += WAVE) dst[e] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
   }
-  for (int j = 0; j < nsteps; j += 2) {
-    mp_compute<FMT, NT, G, PPW, SEQ>(acc, 0, s0, ad, sh);
-    if (j + 2 < nsteps) mp_load<FMT, NT, G, GATHER>(s0, ad, lane, blk(j + 2));
-    if (j + 1 < nsteps) {
-      mp_compute<FMT, NT, G, PPW, SEQ>(acc, 1, s1, ad, sh);
-      if (j + 3 < nsteps) mp_load<FMT, NT, G, GATHER>(s1, ad, lane, blk(j + 3));
+  for (int j = 0; j < nsteps; j += MP_LA) {
+#pragma unroll
+    for (int jj = 0; jj < MP_LA; jj++) {
+      if (j + jj < nsteps) {
+        mp_compute<FMT, NT, G, PPW, SEQ>(acc, jj & 1, st[jj], ad, sh);
+        if (j + jj + MP_LA < nsteps) mp_load<FMT, NT, G, GATHER>(st[jj], ad, lane, blk(j + jj + MP_LA));
+      }
     }
   }
   // the wave's pairs by the lane-part tree: (h + h^1) across lanes i, i^8, then pair + pair
