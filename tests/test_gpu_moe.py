@@ -79,7 +79,7 @@ def test_moe_step_matches_oracle(moe, rows):
 @pytest.mark.parametrize("rows", [1, 8, 9, 16])
 def test_fused_moe_step_equals_composition(moe, rows):
     """qg_moe_step (six launches, one plan for both grouped GEMVs, SwiGLU quantized in place) gives the
-    bits of the composition of the separate calls."""
+    bits of the composition of the separate calls, call after call through the same workspace."""
     log(f"fused moe rows={rows}")
     x = torch.from_numpy(gauss((rows, HIDDEN), 1.0, WL, 32 + rows).numpy()).cuda()
     y, (expert, _, weight), logits = q.moe_step(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN, shared_expert=E)
@@ -88,6 +88,12 @@ def test_fused_moe_step_equals_composition(moe, rows):
     assert torch.equal(expert_f, expert)
     assert torch.equal(weight_f, weight)
     assert torch.equal(yf, y)
+    # nothing carries over between calls, whatever the workspace held
+    ws = torch.full((q.moe_workspace_bytes(rows, E, HIDDEN, FFN, TOPK, True),), 0xA5, dtype=torch.uint8,
+                    device="cuda")
+    for _ in range(3):
+        yr, _, _ = q.moe_step_fused(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN, ws=ws)
+        assert torch.equal(yr, y)
     # a second call on a smaller row count through the same workspace size class
     if rows > 1:
         yf1, _, _ = q.moe_step_fused(x[:1].contiguous(), moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN)
