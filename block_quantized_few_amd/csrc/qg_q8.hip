@@ -365,6 +365,7 @@ struct MpAddr {
   // element (row * kbp + its block's offset in the pair) per row group, and
   // whether its bytes meet its column's block (else they are zero).
   int64_t gsrc[2];
+  bool xon;   // the lane's 16 bytes of a pair-order chunk are codes, not the zeros (not loaded)
   int ghalf;  // 0 or 16: the half of the block's codes
   bool gon;
 };
@@ -388,7 +389,7 @@ __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad,
   const size_t chunk0 = (size_t)(b >> 1) * ad.groups;
 #pragma unroll
   for (int g = 0; g < G; g++) {
-    st.x[g] = ld16(ad.xc + ((chunk0 + g) * 64 + lane) * 16);
+    st.x[g] = ad.xon ? ld16(ad.xc + ((chunk0 + g) * 64 + lane) * 16) : make_uint4(0u, 0u, 0u, 0u);
     st.dx[g] = ad.xd[(chunk0 + g) * 16 + (lane & 15)];
     st.ns[g] = FMT == FMT_Q4 ? ad.xn[(chunk0 + g) * 16 + (lane & 15)] : 0;
   }
@@ -437,8 +438,8 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
 // One MP tile: groups of S*W2 waves, each group NT 16-row image tiles; G
 // groups of eight activation rows from the pair-order workspace, or (GATHER)
 // from a row-order workspace through the tile's s_src map.
-template <int FMT, int H, int G, int NT, bool GATHER>
-__device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
+template <int FMT, int H, int G, int NT, bool GATHER, bool PF = false>
+__device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, int count = 1, int64_t row_stride = 0) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
   constexpr bool SEQ = H == 1;
   constexpr int W2 = mp_w2(H);
@@ -449,24 +450,18 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
   const int g = wave / gw, wg = wave - g * gw, s = wg / W2, hw = wg - s * W2;
   const int i = lane & 15, q = lane >> 4;
   const int64_t ntiles = np_of(ta.n) / TILE;
-  const int64_t wrow0 = ta.row0 + (int64_t)g * TILE * NT;  // first row of this group's tiles
-  const int sc_stride = pl.H * pl.BS * TILE;                // fp16 scales of one tile's wave part
+  const int sc_stride = pl.H * pl.BS * TILE;  // fp16 scales of one tile's wave part
   MpAddr<NT> ad;
   const uint16_t* scale[NT];
 #pragma unroll
-  for (int t = 0; t < NT; t++) {
-    const int64_t it0 = (wrow0 >> 4) + t;
-    const int64_t it = it0 < ntiles ? it0 : ntiles - 1;  // past the last tile: reread it, store nothing
-    ad.code[t] = ta.code + ((size_t)it * ta.kbp) * CB;
-    scale[t] = ta.scale + ((size_t)it * ta.kbp) * TILE;
-    ad.sl[t] = scl + (wave * NT + t) * sc_stride;
-  }
+  for (int t = 0; t < NT; t++) ad.sl[t] = scl + (wave * NT + t) * sc_stride;
   ad.aoff = FMT == FMT_Q8 ? (uint32_t)(q * 256 + i * 16) : (uint32_t)((q >> 1) * 256 + i * 16);
   ad.soff = (uint32_t)((i >> 3) * 16 + 4 * q);
   ad.xc = reinterpret_cast<const uint8_t*>(ta.prep.codes);
   ad.xd = ta.prep.dx;
   ad.xn = ta.prep.nsx;
   ad.groups = (R + 7) >> 3;
+  ad.xon = (i < 8) == (q < 2);
   if (GATHER) {
 #pragma unroll
     for (int gg = 0; gg < G; gg++) {
@@ -487,105 +482,134 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
     const int u = PPW == 2 ? j >> 1 : j, pp = PPW == 2 ? j & 1 : 0;
     return bs0 + H * u + 2 * pp;
   };
-  float acc[NT][PPW][G][4];
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int p = 0; p < PPW; p++)
-#pragma unroll
-      for (int gg = 0; gg < G; gg++)
-#pragma unroll
-        for (int v = 0; v < 4; v++) acc[t][p][gg][v] = 0.0f;
   // The weight scales of the wave part's blocks [sb0, sb0 + H*BS) of each tile
-  // go to the wave's own LDS region once (16 lanes would otherwise load the
-  // same four scales every step).  Their loads are issued first, then the
-  // first two steps', so waiting for them waits for nothing else.
+  // go to the wave's own LDS region once per tile (16 lanes would otherwise
+  // load the same four scales every step).  Their loads are issued first, then
+  // the first steps', so waiting for them waits for nothing else.
   ad.sb0 = s * H * pl.BS;
   const int nsv = H * pl.BS * 2;  // 16-byte pieces per tile (kbp/S blocks x 32 bytes)
-  uint4 sv[NT];
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-    if (lane < nsv) sv[t] = ld16(scale[t] + (size_t)ad.sb0 * TILE + lane * 8);
   constexpr int MP_LA = mp_la(NT, G);
+  uint4 sv[NT];
   MpStep<NT, G> st[MP_LA];
+  int64_t wrow0 = 0;  // first row of this group's tiles
+  // Points the wave at the tile group starting at row0 and issues its scale
+  // loads and its first MP_LA steps.
+  auto start = [&](int64_t row0) {
+    wrow0 = row0 + (int64_t)g * TILE * NT;
 #pragma unroll
-  for (int jj = 0; jj < MP_LA; jj++)
-    if (jj < nsteps) mp_load<FMT, NT, G, GATHER>(st[jj], ad, lane, blk(jj));
+    for (int t = 0; t < NT; t++) {
+      const int64_t it0 = (wrow0 >> 4) + t;
+      const int64_t it = it0 < ntiles ? it0 : ntiles - 1;  // past the last tile: reread it, store nothing
+      ad.code[t] = ta.code + ((size_t)it * ta.kbp) * CB;
+      scale[t] = ta.scale + ((size_t)it * ta.kbp) * TILE;
+    }
 #pragma unroll
-  for (int t = 0; t < NT; t++) {
-    uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(ad.sl[t]));
-    if (lane < nsv) dst[lane] = sv[t];
-    for (int e = lane + WAVE; e < nsv; e += WAVE) dst[e] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
-  }
-  for (int j = 0; j < nsteps; j += MP_LA) {
+    for (int t = 0; t < NT; t++)
+      if (lane < nsv) sv[t] = ld16(scale[t] + (size_t)ad.sb0 * TILE + lane * 8);
 #pragma unroll
-    for (int jj = 0; jj < MP_LA; jj++) {
-      if (j + jj < nsteps) {
-        mp_compute<FMT, NT, G, PPW, SEQ>(acc, jj & 1, st[jj], ad, sh);
-        if (j + jj + MP_LA < nsteps) mp_load<FMT, NT, G, GATHER>(st[jj], ad, lane, blk(j + jj + MP_LA));
+    for (int jj = 0; jj < MP_LA; jj++)
+      if (jj < nsteps) mp_load<FMT, NT, G, GATHER>(st[jj], ad, lane, blk(jj));
+  };
+  // The started tile's scales into the wave's LDS region (the wave is done
+  // reading the previous tile's).
+  auto stage = [&]() {
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(ad.sl[t]));
+      if (lane < nsv) dst[lane] = sv[t];
+      for (int e = lane + WAVE; e < nsv; e += WAVE) dst[e] = ld16(scale[t] + (size_t)ad.sb0 * TILE + e * 8);
+    }
+  };
+  start(ta.row0);
+  stage();
+  // The workgroup's tiles of this projection: row0, row0 + row_stride, ...
+  // (PF: the next one's loads are in flight while this one is combined and
+  // stored; otherwise one tile per call).
+  for (int c = 0; c < (PF ? count : 1); c++) {
+    float acc[NT][PPW][G][4];
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+      for (int p = 0; p < PPW; p++)
+#pragma unroll
+        for (int gg = 0; gg < G; gg++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) acc[t][p][gg][v] = 0.0f;
+    for (int j = 0; j < nsteps; j += MP_LA) {
+#pragma unroll
+      for (int jj = 0; jj < MP_LA; jj++) {
+        if (j + jj < nsteps) {
+          mp_compute<FMT, NT, G, PPW, SEQ>(acc, jj & 1, st[jj], ad, sh);
+          if (j + jj + MP_LA < nsteps) mp_load<FMT, NT, G, GATHER>(st[jj], ad, lane, blk(j + jj + MP_LA));
+        }
       }
     }
-  }
-  // the wave's pairs by the lane-part tree: (h + h^1) across lanes i, i^8, then pair + pair
-  float res[NT][G][4];
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int gg = 0; gg < G; gg++)
-#pragma unroll
-      for (int v = 0; v < 4; v++) {
-        float val = acc[t][0][gg][v];
-        if (!SEQ) {
-          val = val + lane_xor8(val);
-          if (PPW == 2) val = val + (acc[t][PPW - 1][gg][v] + lane_xor8(acc[t][PPW - 1][gg][v]));
-        }
-        res[t][gg][v] = val;
-      }
-  // then the W2 pair groups of a wave part (the tree's upper level), then wave parts left to right
-  if (gw > 1) {
-    constexpr int NV = NT * G * 4;
+    // the wave's pairs by the lane-part tree: (h + h^1) across lanes i, i^8, then pair + pair
+    float res[NT][G][4];
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
       for (int gg = 0; gg < G; gg++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) red[(wave * NV + (t * G + gg) * 4 + v) * WAVE + lane] = res[t][gg][v];
-    __syncthreads();
-    if (wg == 0) {
+        for (int v = 0; v < 4; v++) {
+          float val = acc[t][0][gg][v];
+          if (!SEQ) {
+            val = val + lane_xor8(val);
+            if (PPW == 2) val = val + (acc[t][PPW - 1][gg][v] + lane_xor8(acc[t][PPW - 1][gg][v]));
+          }
+          res[t][gg][v] = val;
+        }
+    const int64_t row_out = wrow0;
+    const bool more = PF && c + 1 < count;
+    if (more) start(ta.row0 + (int64_t)(c + 1) * row_stride);
+    // then the W2 pair groups of a wave part (the tree's upper level), then wave parts left to right
+    bool store = true;
+    if (gw > 1) {
+      constexpr int NV = NT * G * 4;
 #pragma unroll
       for (int t = 0; t < NT; t++)
 #pragma unroll
         for (int gg = 0; gg < G; gg++)
 #pragma unroll
-          for (int v = 0; v < 4; v++) {
-            const int o = ((t * G + gg) * 4 + v) * WAVE + lane;
-            const int w0 = g * gw;
-            float x = 0.0f;
-            for (int s2 = 0; s2 < pl.S; s2++) {
-              float part = red[(w0 + s2 * W2) * NV * WAVE + o];
-              if (W2 == 2) part = part + red[(w0 + s2 * W2 + 1) * NV * WAVE + o];
-              x = s2 == 0 ? part : x + part;
-            }
-            res[t][gg][v] = x;
-          }
-    }
-    __syncthreads();  // the combine area is free for the next tile
-    if (wg != 0) return;
-  }
-  if (i < 8) {
-#pragma unroll
-    for (int gg = 0; gg < G; gg++) {
-      const int ar = gg * 8 + i;  // activation row of this lane's column
-      if (ar < R) {
+          for (int v = 0; v < 4; v++) red[(wave * NV + (t * G + gg) * 4 + v) * WAVE + lane] = res[t][gg][v];
+      __syncthreads();
+      if (wg == 0) {
 #pragma unroll
         for (int t = 0; t < NT; t++)
 #pragma unroll
-          for (int v = 0; v < 4; v++) {
-            const int64_t row = wrow0 + t * TILE + 4 * q + v;
-            if (row < ta.n) ta.y[(int64_t)ta.s_dst[ar] * ta.ldy + row] = res[t][gg][v];
-          }
+          for (int gg = 0; gg < G; gg++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+              const int o = ((t * G + gg) * 4 + v) * WAVE + lane;
+              const int w0 = g * gw;
+              float x = 0.0f;
+              for (int s2 = 0; s2 < pl.S; s2++) {
+                float part = red[(w0 + s2 * W2) * NV * WAVE + o];
+                if (W2 == 2) part = part + red[(w0 + s2 * W2 + 1) * NV * WAVE + o];
+                x = s2 == 0 ? part : x + part;
+              }
+              res[t][gg][v] = x;
+            }
+      }
+      __syncthreads();  // the combine area is free for the next tile
+      store = wg == 0;
+    }
+    if (store && i < 8) {
+#pragma unroll
+      for (int gg = 0; gg < G; gg++) {
+        const int ar = gg * 8 + i;  // activation row of this lane's column
+        if (ar < R) {
+#pragma unroll
+          for (int t = 0; t < NT; t++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+              const int64_t row = row_out + t * TILE + 4 * q + v;
+              if (row < ta.n) ta.y[(int64_t)ta.s_dst[ar] * ta.ldy + row] = res[t][gg][v];
+            }
+        }
       }
     }
+    if (more) stage();
   }
 }
 
@@ -668,23 +692,32 @@ void rl_set_kernel(SetArgs a, int lds_x) {
   }
 }
 
-template <int FMT, int G, bool WIDE>
+// PF: each workgroup's tiles of a projection in one mp_tile call, the next
+// tile's loads in flight while a tile is combined (for launches of several
+// rounds; it costs registers).
+template <int FMT, int G, bool WIDE, bool PF>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp_set_kernel(SetArgs a, int R) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
   float* red = reinterpret_cast<float*>(lds);  // combine area, then the waves' staged scales
   uint16_t* scl = reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4);
-  for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
+  constexpr bool MP_PF = PF && !WIDE && FMT == FMT_Q8;
+  for (int tile = blockIdx.x; tile < a.total_tiles;) {
     int p = 0, t0 = tile;
     while (p + 1 < a.count && t0 >= a.p[p].tiles) t0 -= a.p[p++].tiles;
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, 0);
     const PartPlan& pl = d.pl;
-    if (pl.H == 1) mp_tile<FMT, 1, G, mp_nt(1, G, WIDE), false>(ta, R, red, scl);
-    else if (pl.H == 2) mp_tile<FMT, 2, G, mp_nt(2, G, WIDE), false>(ta, R, red, scl);
-    else if (pl.H == 4) mp_tile<FMT, 4, G, mp_nt(4, G, WIDE), false>(ta, R, red, scl);
-    else mp_tile<FMT, 8, G, mp_nt(8, G, WIDE), false>(ta, R, red, scl);
+    // this workgroup's tiles of the projection, t0, t0 + G, ..., in one call
+    // (narrow Q8_0 tiles; the others have no registers to spare for it)
+    const int cnt = MP_PF ? (d.tiles - 1 - t0) / (int)gridDim.x + 1 : 1;
+    const int64_t stride = (int64_t)gridDim.x * d.rows_per_tile;
+    if (pl.H == 1) mp_tile<FMT, 1, G, mp_nt(1, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
+    else if (pl.H == 2) mp_tile<FMT, 2, G, mp_nt(2, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
+    else if (pl.H == 4) mp_tile<FMT, 4, G, mp_nt(4, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
+    else mp_tile<FMT, 8, G, mp_nt(8, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
+    tile += cnt * (int)gridDim.x;
   }
 }
 
@@ -942,18 +975,30 @@ static size_t mp_fill(SetArgs& a, int G, bool wide) {
 // The pair kernel runs in rounds of the workgroups resident at once; a round
 // costs about a tile's latency chain.  Wide tiles win when they need fewer
 // rounds at 9-16 rows (half the activation-chunk loads), and at 3-8 rows
-// when they fit one round that narrow tiles overflow.
+// when they fit one round that narrow tiles overflow.  Narrow Q8_0 tiles over
+// several rounds take the kernel that prefetches across a workgroup's tiles.
 template <int FMT, int G>
 static void launch_mp(SetArgs a, int rows, hipStream_t s) {
-  auto kn = mp_set_kernel<FMT, G, false>;
-  auto kw = mp_set_kernel<FMT, G, true>;
+  auto kn = mp_set_kernel<FMT, G, false, false>;
+  auto kw = mp_set_kernel<FMT, G, true, false>;
   SetArgs aw = a;
   const size_t ln = mp_fill(a, G, false), lw = mp_fill(aw, G, true);
   const unsigned gn = persistent_grid(kn, ln, a.total_tiles), gw = persistent_grid(kw, lw, aw.total_tiles);
   const int64_t rn = (a.total_tiles + gn - 1) / gn, rw = (aw.total_tiles + gw - 1) / gw;
   const bool wide = G == 2 ? rw < rn : (rn > 1 && rw == 1);
-  if (wide) hipLaunchKernelGGL(kw, dim3(gw), dim3(WG), lw, s, aw, rows);
-  else hipLaunchKernelGGL(kn, dim3(gn), dim3(WG), ln, s, a, rows);
+  if (wide) {
+    hipLaunchKernelGGL(kw, dim3(gw), dim3(WG), lw, s, aw, rows);
+    return;
+  }
+  if constexpr (FMT == FMT_Q8) {
+    if (rn > 1) {
+      auto kp = mp_set_kernel<FMT, G, false, true>;  // the occupancy of kn (128 registers at most)
+      if (ln > 48 * 1024) hipFuncSetAttribute((const void*)kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ln);
+      hipLaunchKernelGGL(kp, dim3(gn), dim3(WG), ln, s, a, rows);
+      return;
+    }
+  }
+  hipLaunchKernelGGL(kn, dim3(gn), dim3(WG), ln, s, a, rows);
 }
 
 int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStream_t s) {
