@@ -43,10 +43,13 @@ def test_lm_head_q8_0():
         log(f"  max rel err {e:.3e}")
         assert e <= TOL
         ys[rows] = (x, y)
-    # the first rows of the 16-row call equal calls with fewer rows of the same inputs
+    # the first rows of the 16-row call equal calls with fewer rows of the same inputs (the pair tile over
+    # several rounds of workgroups at 8 and 16 rows, the one-row kernel at 1)
     x16 = torch.from_numpy(ys[16][0]).cuda()
     y8 = q.qgemv_q8_0(img, n, k, x16[:8].contiguous())
     assert np.array_equal(bits(y8), bits(ys[16][1][:8]))
+    y1 = q.qgemv_q8_0(img, n, k, x16[:1].contiguous())
+    assert np.array_equal(bits(y1), bits(ys[16][1][:1]))
 
 
 def test_lm_head_f16():
