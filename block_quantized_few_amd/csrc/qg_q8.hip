@@ -794,8 +794,46 @@ __device__ __forceinline__ void grouped_rows(TileArgs ta, uint8_t* lds, float* r
   rl_tile<FMT_Q8, R, false, GROUPED_LA>(ta, lds, red, 0, true);
 }
 
-// Items of at most GROUPED_SMALL_ROWS rows (the plan puts them first):
-// lanes-own-rows tiles, persistent over the (item, tile) units.
+// Unit (item, tile) of an item of at most GROUPED_SMALL_ROWS rows:
+// lanes-own-rows tiles.  Every thread calls it.
+__device__ __forceinline__ void grouped_small_unit(const uint8_t* __restrict__ images, int64_t expert_bytes,
+                                                   size_t scale_off, int64_t n, int64_t k, int kbp, const PartPlan& pl,
+                                                   const Prep& prep, const int* __restrict__ sorted,
+                                                   const int* __restrict__ items, const int32_t* __restrict__ x_index,
+                                                   float* y, int lds_x, int item, int tile, uint8_t* lds, int* s_map) {
+  float* red = reinterpret_cast<float*>(lds + lds_x);
+  const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
+  __syncthreads();  // the previous unit is done with s_map and LDS
+  if (threadIdx.x < cnt) {
+    const int a = sorted[start + threadIdx.x];
+    s_map[threadIdx.x] = x_index ? x_index[a] : a;
+    s_map[QG_MAX_ROWS + threadIdx.x] = a;
+  }
+  __syncthreads();
+  const uint8_t* img = images + (size_t)e * expert_bytes;
+  TileArgs ta;
+  ta.code = img;
+  ta.scale = reinterpret_cast<const uint16_t*>(img + scale_off);
+  ta.n = n;
+  ta.kbp = kbp;
+  ta.kb = (int)kb_of(k);
+  ta.k = k;
+  ta.row0 = (int64_t)tile * (WG >> pl.lgP);
+  ta.prep = prep;
+  ta.xf = nullptr;
+  ta.s_src = s_map;
+  ta.y = y;
+  ta.ldy = n;
+  ta.s_dst = s_map + QG_MAX_ROWS;
+  ta.lds_x = lds_x;
+  ta.pl = pl;
+  ta.ucx = 0;  // set per row count
+  if (cnt == 1) grouped_rows<1>(ta, lds, red);
+  else if (cnt == 2) grouped_rows<2>(ta, lds, red);
+}
+
+// Items of at most GROUPED_SMALL_ROWS rows (the plan puts them first), when
+// no item can have more: persistent over the (item, tile) units.
 __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__ images, int64_t expert_bytes,
                                                      size_t scale_off, int64_t n, int64_t k, int kbp, PartPlan pl,
                                                      Prep prep,
@@ -806,38 +844,9 @@ __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   const int units = header[2] * tiles;
-  float* red = reinterpret_cast<float*>(lds + lds_x);
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {  // uniform over the workgroup
-    const int item = u / tiles, tile = u - item * tiles;
-    const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
-    __syncthreads();  // the previous unit is done with s_map and LDS
-    if (threadIdx.x < cnt) {
-      const int a = sorted[start + threadIdx.x];
-      s_map[threadIdx.x] = x_index ? x_index[a] : a;
-      s_map[QG_MAX_ROWS + threadIdx.x] = a;
-    }
-    __syncthreads();
-    const uint8_t* img = images + (size_t)e * expert_bytes;
-    TileArgs ta;
-    ta.code = img;
-    ta.scale = reinterpret_cast<const uint16_t*>(img + scale_off);
-    ta.n = n;
-    ta.kbp = kbp;
-    ta.kb = (int)kb_of(k);
-    ta.k = k;
-    ta.row0 = (int64_t)tile * (WG >> pl.lgP);
-    ta.prep = prep;
-    ta.xf = nullptr;
-    ta.s_src = s_map;
-    ta.y = y;
-    ta.ldy = n;
-    ta.s_dst = s_map + QG_MAX_ROWS;
-    ta.lds_x = lds_x;
-    ta.pl = pl;
-    ta.ucx = 0;  // set per row count
-    if (cnt == 1) grouped_rows<1>(ta, lds, red);
-    else if (cnt == 2) grouped_rows<2>(ta, lds, red);
-  }
+  for (int u = blockIdx.x; u < units; u += gridDim.x)  // uniform over the workgroup
+    grouped_small_unit(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y, lds_x,
+                       u / tiles, u % tiles, lds, s_map);
 }
 
 // Rows of a grouped item in the pair kernel's tiles (one 16-row image tile per
@@ -852,51 +861,70 @@ __device__ __forceinline__ void grouped_mp_tile(const TileArgs& ta, int R, float
   }
 }
 
-// Rows per tile of grouped_mp_kernel.
+// Rows per pair-tile unit of a grouped launch.
 static inline int grouped_mp_rows(const PartPlan& pl) { return (WAVES / (pl.S * mp_w2(pl.H))) * TILE; }
 
-// Items of more than GROUPED_SMALL_ROWS rows, persistent over their (item,
-// tile) units.
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void grouped_mp_kernel(
-    const uint8_t* __restrict__ images, int64_t expert_bytes, size_t scale_off, int64_t n, int64_t k, int kbp,
-    PartPlan pl, Prep prep, const int* __restrict__ header, const int* __restrict__ sorted,
-    const int* __restrict__ items, const int32_t* __restrict__ x_index, float* y, int tiles) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_map[2 * QG_MAX_ROWS];
+// Unit (item, tile) of an item of more than GROUPED_SMALL_ROWS rows: the pair
+// tile, activation rows gathered.  Every thread calls it.
+__device__ __forceinline__ void grouped_big_unit(const uint8_t* __restrict__ images, int64_t expert_bytes,
+                                                 size_t scale_off, int64_t n, int64_t k, int kbp, const PartPlan& pl,
+                                                 const Prep& prep, const int* __restrict__ sorted,
+                                                 const int* __restrict__ items, const int32_t* __restrict__ x_index,
+                                                 float* y, int item, int tile, uint8_t* lds, int* s_map) {
   float* red = reinterpret_cast<float*>(lds);  // combine area, then the waves' staged scales
   uint16_t* scl = reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4);
-  const int nsmall = header[2], units = (header[0] - nsmall) * tiles;
   const int rpt = (WAVES / (pl.S * mp_w2(pl.H))) * TILE;
+  const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
+  __syncthreads();  // the previous unit is done with s_map and LDS
+  if (threadIdx.x < cnt) {
+    const int a = sorted[start + threadIdx.x];
+    s_map[threadIdx.x] = x_index ? x_index[a] : a;
+    s_map[QG_MAX_ROWS + threadIdx.x] = a;
+  }
+  __syncthreads();
+  const uint8_t* img = images + (size_t)e * expert_bytes;
+  TileArgs ta;
+  ta.code = img;
+  ta.scale = reinterpret_cast<const uint16_t*>(img + scale_off);
+  ta.n = n;
+  ta.kbp = kbp;
+  ta.kb = (int)kb_of(k);
+  ta.k = k;
+  ta.row0 = (int64_t)tile * rpt;
+  ta.prep = prep;
+  ta.xf = nullptr;
+  ta.s_src = s_map;
+  ta.y = y;
+  ta.ldy = n;
+  ta.s_dst = s_map + QG_MAX_ROWS;
+  ta.lds_x = 0;
+  ta.pl = pl;
+  ta.ucx = 0;
+  if (cnt > 8) grouped_mp_tile<2>(ta, cnt, red, scl);
+  else grouped_mp_tile<1>(ta, cnt, red, scl);
+}
+
+// Items of every size in one launch, persistent over the (item, tile) units:
+// those of the items of more than GROUPED_SMALL_ROWS rows (pair tiles, the
+// longer ones) first, then those of the small items (lanes-own-rows tiles).
+// The two kinds of unit share the dynamic LDS (max of their needs); the
+// small items' staged rows start at byte 0.
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void grouped_all_kernel(
+    const uint8_t* __restrict__ images, int64_t expert_bytes, size_t scale_off, int64_t n, int64_t k, int kbp,
+    PartPlan pl, Prep prep, const int* __restrict__ header, const int* __restrict__ sorted,
+    const int* __restrict__ items, const int32_t* __restrict__ x_index, float* y, int lds_x, int tiles_s,
+    int tiles_b) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_map[2 * QG_MAX_ROWS];
+  const int nsmall = header[2];
+  const int ub = (header[0] - nsmall) * tiles_b, units = ub + nsmall * tiles_s;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {  // uniform over the workgroup
-    const int item = nsmall + u / tiles, tile = u % tiles;
-    const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
-    __syncthreads();  // the previous unit is done with s_map
-    if (threadIdx.x < cnt) {
-      const int a = sorted[start + threadIdx.x];
-      s_map[threadIdx.x] = x_index ? x_index[a] : a;
-      s_map[QG_MAX_ROWS + threadIdx.x] = a;
-    }
-    __syncthreads();
-    const uint8_t* img = images + (size_t)e * expert_bytes;
-    TileArgs ta;
-    ta.code = img;
-    ta.scale = reinterpret_cast<const uint16_t*>(img + scale_off);
-    ta.n = n;
-    ta.kbp = kbp;
-    ta.kb = (int)kb_of(k);
-    ta.k = k;
-    ta.row0 = (int64_t)tile * rpt;
-    ta.prep = prep;
-    ta.xf = nullptr;
-    ta.s_src = s_map;
-    ta.y = y;
-    ta.ldy = n;
-    ta.s_dst = s_map + QG_MAX_ROWS;
-    ta.lds_x = 0;
-    ta.pl = pl;
-    ta.ucx = 0;
-    if (cnt > 8) grouped_mp_tile<2>(ta, cnt, red, scl);
-    else grouped_mp_tile<1>(ta, cnt, red, scl);
+    if (u < ub)
+      grouped_big_unit(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y,
+                       nsmall + u / tiles_b, u % tiles_b, lds, s_map);
+    else
+      grouped_small_unit(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y, lds_x,
+                         (u - ub) / tiles_s, (u - ub) % tiles_s, lds, s_map);
   }
 }
 
@@ -1082,20 +1110,21 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
   // small items: at most m of them; items of more rows: at most m / (GROUPED_SMALL_ROWS + 1)
   const int lx_s = lds_x_for(GROUPED_SMALL_ROWS);
   const size_t lds_s = (size_t)lx_s + WAVES * WAVE * GROUPED_SMALL_ROWS * 4;
-  const unsigned gs = persistent_grid(grouped_kernel, lds_s, (int64_t)m * tiles);
-  hipLaunchKernelGGL(grouped_kernel, dim3(gs), dim3(WG), lds_s, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv,
-                     header, sorted, items, x_index, y, lx_s, tiles);
-  if (int st = hip_status(hipGetLastError(), "grouped_kernel")) return st;
   const int mb = max_item_rows > GROUPED_SMALL_ROWS ? m / (GROUPED_SMALL_ROWS + 1) : 0;
-  if (mb > 0) {
-    const int rpt = grouped_mp_rows(pl);
-    const int tb = (int)((n + rpt - 1) / rpt);
-    const size_t lds_b = (size_t)WAVES * WAVE * MP_NV_MAX * 4 + (size_t)WAVES * (kbp / pl.S) * TILE * 2;
-    const unsigned gb = persistent_grid(grouped_mp_kernel, lds_b, (int64_t)mb * tb);
-    hipLaunchKernelGGL(grouped_mp_kernel, dim3(gb), dim3(WG), lds_b, s, (const uint8_t*)images, eb, so, n, k, kbp, pl,
-                       pv, header, sorted, items, x_index, y, tb);
-    if (int st = hip_status(hipGetLastError(), "grouped_mp_kernel")) return st;
+  if (mb == 0) {
+    const unsigned gs = persistent_grid(grouped_kernel, lds_s, (int64_t)m * tiles);
+    hipLaunchKernelGGL(grouped_kernel, dim3(gs), dim3(WG), lds_s, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv,
+                       header, sorted, items, x_index, y, lx_s, tiles);
+    return hip_status(hipGetLastError(), "grouped_kernel");
   }
+  // items of more than two rows possible: one launch for both kinds of unit
+  const int tb = (int)((n + grouped_mp_rows(pl) - 1) / grouped_mp_rows(pl));
+  const size_t lds_b = (size_t)WAVES * WAVE * MP_NV_MAX * 4 + (size_t)WAVES * (kbp / pl.S) * TILE * 2;
+  const size_t lds_a = lds_s > lds_b ? lds_s : lds_b;
+  const unsigned ga = persistent_grid(grouped_all_kernel, lds_a, (int64_t)m * tiles + (int64_t)mb * tb);
+  hipLaunchKernelGGL(grouped_all_kernel, dim3(ga), dim3(WG), lds_a, s, (const uint8_t*)images, eb, so, n, k, kbp, pl,
+                     pv, header, sorted, items, x_index, y, lx_s, tiles, tb);
+  if (int st = hip_status(hipGetLastError(), "grouped_all_kernel")) return st;
   return QG_OK;
 }
 
