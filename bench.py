@@ -485,7 +485,7 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
 
 def moe_sweep(torch, q, synth, L, sh, stream, timer):
     """Routed MoE step (qg_moe_step): router f16 GEMV, top-8 routing + plan, grouped gate/up, SwiGLU + q8,
-    grouped down, combine -- six launches."""
+    grouped down, combine -- six launches, five at 1-2 rows (SwiGLU + q8 inside the down launch)."""
     hidden, ffn, E, topk = 2048, 512, 256, 8
     nimg = E + 1  # index E: the shared expert
     gu_b = q.image_bytes(q.Q8_0, 2 * ffn, hidden)
@@ -531,7 +531,7 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
             uniq.append(len(set(expert.cpu().tolist())))
         u = sum(uniq) / nx
         wb = 2 * E * hidden + u * (gu_b + dn_b)
-        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms, 6)
+        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms, 5 if rows <= 2 else 6)
         e["unique_experts"] = round(u, 2)
         out.append(e)
     return out

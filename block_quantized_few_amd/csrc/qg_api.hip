@@ -416,9 +416,13 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
   if (int st = launch_grouped_planned(gu_images, n_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi,
                                       m, rows, gu, s))
     return st;
-  if (int st = launch_swiglu_q8(gu, m, ffn, w + M.hprep, s)) return st;
+  // at most two rows: the down launch takes the SwiGLU of the gate/up rows in
+  // its staging (one launch fewer); otherwise a launch quantizes it first
+  const bool glu = rows <= 2 && grouped_glu_fits(ffn);
+  if (!glu)
+    if (int st = launch_swiglu_q8(gu, m, ffn, w + M.hprep, s)) return st;
   if (int st = launch_grouped_planned(down_images, n_images, hidden, ffn, w + M.hprep, m, header, sorted, items,
-                                      nullptr, m, rows, o, s))
+                                      nullptr, m, rows, o, s, glu ? gu : nullptr))
     return st;
   if (int st = launch_moe_combine(o, wt, rows, slots, hidden, y, s)) return st;
   return ok();

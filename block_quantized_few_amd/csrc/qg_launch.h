@@ -55,9 +55,15 @@ int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, 
 // x_index == nullptr: the activation row of assignment a is a.
 // max_item_rows: an upper bound on the rows of one work item (the kernel for
 // items of more than two rows is launched only when it can have work).
+// glu: null, or the fp32 gate/up rows [m][2k] (gate values, then up values)
+// whose SwiGLU h = silu(g) * u, quantized in each tile's staging, is the
+// activation row of each assignment instead of a prepared row (prep unused);
+// requires max_item_rows <= 2 and grouped_glu_fits(k).
 int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int64_t k, const void* prep, int x_rows,
                            const int* header, const int* sorted, const int* items, const int32_t* x_index, int m,
-                           int max_item_rows, float* y, hipStream_t s);
+                           int max_item_rows, float* y, hipStream_t s, const float* glu = nullptr);
+// Whether two SwiGLU rows of length k fit a tile's staging area whole.
+bool grouped_glu_fits(int64_t k);
 
 // Fused MoE pieces: routing + plan + input quantization (one workgroup), and
 // SwiGLU quantized for the down projection.

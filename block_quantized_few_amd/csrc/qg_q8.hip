@@ -92,39 +92,68 @@ __device__ void stage_rl(uint8_t* lds, const Prep& prep, const int* s_src, int k
 // values loaded first can be quantized while the weight loads are in flight.
 constexpr int XQ_FIRST = 1;  // work items per thread whose loads are issued first
 
-struct XQuarter {
+// One work item's loaded values: eight consecutive columns of a row (a, c),
+// and with GLU the matching up values (ua, uc) of an interleaved gate/up row.
+template <bool GLU>
+struct XQuarterT {
   float4 a, c;
 };
+template <>
+struct XQuarterT<true> {
+  float4 a, c, ua, uc;
+};
+using XQuarter = XQuarterT<false>;
 
 // Work item e of R <= 2 rows: row r = e / (4 * nslot), without a division.
 __device__ __forceinline__ int xq_row(int e, int nslot) { return e >= 4 * nslot ? 1 : 0; }
 
-__device__ __forceinline__ XQuarter xq_load(const float* __restrict__ x, int64_t k, int kb, int nslot,
-                                            const PartPlan& pl, int e, int total) {
+// Row r of the fused staging is row r of x (rows k apart), or with GLU row
+// s_src[r] of gu (rows 2k apart: the gate values, then the up values), whose
+// SwiGLU the store takes.
+template <bool GLU = false>
+__device__ __forceinline__ XQuarterT<GLU> xq_load(const float* __restrict__ x, int64_t k, int kb, int nslot,
+                                                  const PartPlan& pl, int e, int total, const int* s_src = nullptr) {
   const int q = e & 3, blk = e >> 2;
   const int r = xq_row(e, nslot), slot = blk - r * nslot;
   const int b = slot_block(pl, 0, slot);
   const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-  XQuarter v;
+  XQuarterT<GLU> v;
   v.a = z;
   v.c = z;
+  if constexpr (GLU) {
+    v.ua = z;
+    v.uc = z;
+  }
   if (e < total) {  // uniform over a wave: total is a multiple of 64
     // pad blocks read the row's first quarter and use zeros
     const bool ok = b < kb;
-    const float4* src = reinterpret_cast<const float4*>(x + (ok ? (int64_t)r * k + (int64_t)b * QK + q * 8 : 0));
+    const int64_t row = GLU ? (int64_t)s_src[r] * 2 * k : (int64_t)r * k;
+    const float4* src = reinterpret_cast<const float4*>(x + row + (ok ? (int64_t)b * QK + q * 8 : 0));
     const float4 a = src[0], c = src[1];
     v.a = ok ? a : z;
     v.c = ok ? c : z;
+    if constexpr (GLU) {
+      const float4* up = src + k / 4;
+      const float4 ua = up[0], uc = up[1];
+      v.ua = ok ? ua : z;
+      v.uc = ok ? uc : z;
+    }
   }
   return v;
 }
 
-template <int FMT>
-__device__ __forceinline__ void xq_store(const XQuarter& xv, uint8_t* lds, int R, int nslot, int e, int total) {
+template <int FMT, bool GLU = false>
+__device__ __forceinline__ void xq_store(const XQuarterT<GLU>& xv, uint8_t* lds, int R, int nslot, int e, int total) {
   if (e >= total) return;  // whole quads leave together: total and the stride are multiples of 4
   const int q = e & 3, blk = e >> 2;
   const int r = xq_row(e, nslot), slot = blk - r * nslot;
-  const float v[8] = {xv.a.x, xv.a.y, xv.a.z, xv.a.w, xv.c.x, xv.c.y, xv.c.z, xv.c.w};
+  float v[8] = {xv.a.x, xv.a.y, xv.a.z, xv.a.w, xv.c.x, xv.c.y, xv.c.z, xv.c.w};
+  if constexpr (GLU) {
+    // h = silu(g) * u, the arithmetic of the stand-alone SwiGLU quantization
+    const float u[8] = {xv.ua.x, xv.ua.y, xv.ua.z, xv.ua.w, xv.uc.x, xv.uc.y, xv.uc.z, xv.uc.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
+  }
   unsigned lo, hi;
   float d;
   int sum;
@@ -137,23 +166,25 @@ __device__ __forceinline__ void xq_store(const XQuarter& xv, uint8_t* lds, int R
 }
 
 // First part: load this thread's first XQ_FIRST work items.
-__device__ __forceinline__ void stage_quantize_begin(XQuarter (&xv)[XQ_FIRST], const float* __restrict__ x,
-                                                     int64_t k, int kb, int R, int kbp, const PartPlan& pl) {
+template <bool GLU = false>
+__device__ __forceinline__ void stage_quantize_begin(XQuarterT<GLU> (&xv)[XQ_FIRST], const float* __restrict__ x,
+                                                     int64_t k, int kb, int R, int kbp, const PartPlan& pl,
+                                                     const int* s_src = nullptr) {
   const int total = R * kbp * 4;
 #pragma unroll
-  for (int j = 0; j < XQ_FIRST; j++) xv[j] = xq_load(x, k, kb, kbp, pl, threadIdx.x + j * WG, total);
+  for (int j = 0; j < XQ_FIRST; j++) xv[j] = xq_load<GLU>(x, k, kb, kbp, pl, threadIdx.x + j * WG, total, s_src);
 }
 
 // Second part: quantize them into LDS, then the rest of the work items.
-template <int FMT>
-__device__ __forceinline__ void stage_quantize_end(const XQuarter (&xv)[XQ_FIRST], uint8_t* lds,
+template <int FMT, bool GLU = false>
+__device__ __forceinline__ void stage_quantize_end(const XQuarterT<GLU> (&xv)[XQ_FIRST], uint8_t* lds,
                                                    const float* __restrict__ x, int64_t k, int kb, int R, int kbp,
-                                                   const PartPlan& pl) {
+                                                   const PartPlan& pl, const int* s_src = nullptr) {
   const int total = R * kbp * 4;
 #pragma unroll
-  for (int j = 0; j < XQ_FIRST; j++) xq_store<FMT>(xv[j], lds, R, kbp, threadIdx.x + j * WG, total);
+  for (int j = 0; j < XQ_FIRST; j++) xq_store<FMT, GLU>(xv[j], lds, R, kbp, threadIdx.x + j * WG, total);
   for (int e = threadIdx.x + XQ_FIRST * WG; e < total; e += WG) {
-    xq_store<FMT>(xq_load(x, k, kb, kbp, pl, e, total), lds, R, kbp, e, total);
+    xq_store<FMT, GLU>(xq_load<GLU>(x, k, kb, kbp, pl, e, total, s_src), lds, R, kbp, e, total);
   }
 }
 
@@ -225,7 +256,9 @@ __device__ __forceinline__ void compute_block(float (&acc)[R], const WBlock<FMT>
 // issued before the activation rows are staged (and, when they are quantized
 // here, after their fp32 loads, which the wave's in-order memory counter then
 // returns first).
-template <int FMT, int R, bool FUSED, int LA = rl_lookahead(FUSED, R)>
+// GLU (with FUSED): the fp32 rows are the SwiGLU of interleaved gate/up rows
+// ta.xf picked by ta.s_src (see xq_load).
+template <int FMT, int R, bool FUSED, int LA = rl_lookahead(FUSED, R), bool GLU = false>
 __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity, bool stage) {
   static_assert(!FUSED || R <= FUSE_MAX_ROWS, "fused quantization stages at most two rows");
   const PartPlan& pl = ta.pl;
@@ -251,8 +284,8 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
   const int bpart = s * pl.H * pl.BS + h;  // this lane's block at u = 0
   const int sbase = s * pl.H + h;          // its slot at u = 0 of a round
 
-  XQuarter xv[XQ_FIRST];
-  if (FUSED && stage) stage_quantize_begin(xv, ta.xf, ta.k, ta.kb, R, ta.kbp, pl);
+  XQuarterT<GLU> xv[XQ_FIRST];
+  if (FUSED && stage) stage_quantize_begin<GLU>(xv, ta.xf, ta.k, ta.kb, R, ta.kbp, pl, ta.s_src);
   WBlock<FMT> w[LA];
 #pragma unroll
   for (int j = 0; j < LA; j++) w[j] = load_block<FMT>(tcode, woff, tscale, soff, bpart + pl.H * j);  // BS >= 8
@@ -265,7 +298,7 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
       nslot = min(ucx, pl.BS - u) << pl.lgP;
       next_round = full ? pl.BS : u + ucx;
       __syncthreads();
-      if (FUSED) stage_quantize_end<FMT>(xv, lds, ta.xf, ta.k, ta.kb, R, ta.kbp, pl);
+      if (FUSED) stage_quantize_end<FMT, GLU>(xv, lds, ta.xf, ta.k, ta.kb, R, ta.kbp, pl, ta.s_src);
       else stage_rl<FMT, R>(lds, ta.prep, ta.s_src, ta.kbp, pl, u0, nslot);
       __syncthreads();
     }
@@ -788,19 +821,25 @@ __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __res
 
 constexpr int GROUPED_LA = 4;  // blocks in flight per lane in the small-item kernel
 
-template <int R>
+// GLU: the rows are the SwiGLU of gate/up rows ta.xf, quantized while staged
+// (all of kbp fits: the launcher checks).
+template <int R, bool GLU>
 __device__ __forceinline__ void grouped_rows(TileArgs ta, uint8_t* lds, float* red) {
   ta.ucx = rl_round(ta.lds_x, R, ta.pl, FMT_Q8);
-  rl_tile<FMT_Q8, R, false, GROUPED_LA>(ta, lds, red, 0, true);
+  rl_tile<FMT_Q8, R, GLU, GROUPED_LA, GLU>(ta, lds, red, 0, true);
 }
 
 // Unit (item, tile) of an item of at most GROUPED_SMALL_ROWS rows:
-// lanes-own-rows tiles.  Every thread calls it.
+// lanes-own-rows tiles.  Every thread calls it.  GLU: the activation row of
+// assignment a is the SwiGLU of row a of glu (gate values, then up values;
+// rows 2k wide), quantized in the tile's staging; prep is not read.
+template <bool GLU>
 __device__ __forceinline__ void grouped_small_unit(const uint8_t* __restrict__ images, int64_t expert_bytes,
                                                    size_t scale_off, int64_t n, int64_t k, int kbp, const PartPlan& pl,
                                                    const Prep& prep, const int* __restrict__ sorted,
                                                    const int* __restrict__ items, const int32_t* __restrict__ x_index,
-                                                   float* y, int lds_x, int item, int tile, uint8_t* lds, int* s_map) {
+                                                   float* y, int lds_x, int item, int tile, uint8_t* lds, int* s_map,
+                                                   const float* glu) {
   float* red = reinterpret_cast<float*>(lds + lds_x);
   const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
   __syncthreads();  // the previous unit is done with s_map and LDS
@@ -820,7 +859,7 @@ __device__ __forceinline__ void grouped_small_unit(const uint8_t* __restrict__ i
   ta.k = k;
   ta.row0 = (int64_t)tile * (WG >> pl.lgP);
   ta.prep = prep;
-  ta.xf = nullptr;
+  ta.xf = glu;
   ta.s_src = s_map;
   ta.y = y;
   ta.ldy = n;
@@ -828,25 +867,26 @@ __device__ __forceinline__ void grouped_small_unit(const uint8_t* __restrict__ i
   ta.lds_x = lds_x;
   ta.pl = pl;
   ta.ucx = 0;  // set per row count
-  if (cnt == 1) grouped_rows<1>(ta, lds, red);
-  else if (cnt == 2) grouped_rows<2>(ta, lds, red);
+  if (cnt == 1) grouped_rows<1, GLU>(ta, lds, red);
+  else if (cnt == 2) grouped_rows<2, GLU>(ta, lds, red);
 }
 
 // Items of at most GROUPED_SMALL_ROWS rows (the plan puts them first), when
 // no item can have more: persistent over the (item, tile) units.
+template <bool GLU>
 __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__ images, int64_t expert_bytes,
                                                      size_t scale_off, int64_t n, int64_t k, int kbp, PartPlan pl,
                                                      Prep prep,
                                                      const int* __restrict__ header, const int* __restrict__ sorted,
                                                      const int* __restrict__ items,
                                                      const int32_t* __restrict__ x_index, float* y, int lds_x,
-                                                     int tiles) {
+                                                     int tiles, const float* glu) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   const int units = header[2] * tiles;
   for (int u = blockIdx.x; u < units; u += gridDim.x)  // uniform over the workgroup
-    grouped_small_unit(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y, lds_x,
-                       u / tiles, u % tiles, lds, s_map);
+    grouped_small_unit<GLU>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y, lds_x,
+                            u / tiles, u % tiles, lds, s_map, glu);
 }
 
 // Rows of a grouped item in the pair kernel's tiles (one 16-row image tile per
@@ -923,8 +963,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void gr
       grouped_big_unit(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y,
                        nsmall + u / tiles_b, u % tiles_b, lds, s_map);
     else
-      grouped_small_unit(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y, lds_x,
-                         (u - ub) / tiles_s, (u - ub) % tiles_s, lds, s_map);
+      grouped_small_unit<false>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y,
+                                lds_x, (u - ub) / tiles_s, (u - ub) % tiles_s, lds, s_map, nullptr);
   }
 }
 
@@ -1090,9 +1130,13 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
   return hip_status(hipGetLastError(), mf ? "mp_set_kernel" : "rl_set_kernel");
 }
 
+bool grouped_glu_fits(int64_t k) {
+  return (size_t)GROUPED_SMALL_ROWS * kbp_of(k) * x_block_bytes(FMT_Q8) <= (size_t)LDS_X_RL;
+}
+
 int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int64_t k, const void* prep, int x_rows,
                            const int* header, const int* sorted, const int* items, const int32_t* x_index, int m,
-                           int max_item_rows, float* y, hipStream_t s) {
+                           int max_item_rows, float* y, hipStream_t s, const float* glu) {
   (void)n_experts;
   if (m == 0) return QG_OK;
   const int kbp = (int)kbp_of(k);
@@ -1111,10 +1155,13 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
   const int lx_s = lds_x_for(GROUPED_SMALL_ROWS);
   const size_t lds_s = (size_t)lx_s + WAVES * WAVE * GROUPED_SMALL_ROWS * 4;
   const int mb = max_item_rows > GROUPED_SMALL_ROWS ? m / (GROUPED_SMALL_ROWS + 1) : 0;
+  if (glu && (mb > 0 || !grouped_glu_fits(k)))
+    return fail(QG_ELAUNCH, "SwiGLU rows need items of at most two rows and k=%lld staged whole", (long long)k);
   if (mb == 0) {
-    const unsigned gs = persistent_grid(grouped_kernel, lds_s, (int64_t)m * tiles);
-    hipLaunchKernelGGL(grouped_kernel, dim3(gs), dim3(WG), lds_s, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv,
-                       header, sorted, items, x_index, y, lx_s, tiles);
+    auto kern = glu ? grouped_kernel<true> : grouped_kernel<false>;
+    const unsigned gs = persistent_grid(kern, lds_s, (int64_t)m * tiles);
+    hipLaunchKernelGGL(kern, dim3(gs), dim3(WG), lds_s, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv, header,
+                       sorted, items, x_index, y, lx_s, tiles, glu);
     return hip_status(hipGetLastError(), "grouped_kernel");
   }
   // items of more than two rows possible: one launch for both kinds of unit

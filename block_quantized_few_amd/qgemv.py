@@ -396,7 +396,7 @@ def moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared):
 
 
 def moe_step_fused(x, router_image, n_experts, topk, gu_images, down_images, ffn, shared=True, ws=None):
-    """The routed MoE step of moe_step in six launches (qg_moe_step).  Returns y and the routing
+    """The routed MoE step of moe_step in one library call (qg_moe_step).  Returns y and the routing
     (expert, weight) as [rows * slots] tensors, and the router logits."""
     _dev(x, torch.float32, "x")
     rows, hidden = x.shape

@@ -294,11 +294,12 @@ int qg_swiglu(const float* gu, int m, int64_t ffn, float* h, qg_stream stream);
 int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int64_t hidden, float* y,
                    qg_stream stream);
 
-/* A routed-MoE decode step in six launches, the composition of the calls
- * above: router logits (f16 lane: router_image is the F16 image of the
- * n_experts x hidden router), routing as
- * qg_moe_route, grouped gate/up GEMV, SwiGLU quantized for the down
- * projection, grouped down GEMV, weighted combine.  gu_images holds
+/* A routed-MoE decode step, the composition of the calls above: router
+ * logits (f16 lane: router_image is the F16 image of the n_experts x hidden
+ * router), routing as qg_moe_route, grouped gate/up GEMV, SwiGLU quantized
+ * for the down projection, grouped down GEMV, weighted combine.  Six
+ * launches; five at 1-2 rows, where the down GEMV quantizes the SwiGLU of
+ * the gate/up rows in its own staging.  gu_images holds
  * n_experts + shared Q8_0 images of [2*ffn][hidden] (gate rows, then up rows)
  * back to back; down_images the same experts' [hidden][ffn]; with shared = 1
  * image n_experts is an ungated shared expert joining every row with weight

@@ -76,10 +76,11 @@ def test_moe_step_matches_oracle(moe, rows):
         assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("rows", [1, 8, 9, 16])
+@pytest.mark.parametrize("rows", [1, 2, 8, 9, 16])
 def test_fused_moe_step_equals_composition(moe, rows):
-    """qg_moe_step (six launches, one plan for both grouped GEMVs, SwiGLU quantized in place) gives the
-    bits of the composition of the separate calls, call after call through the same workspace."""
+    """qg_moe_step (one plan for both grouped GEMVs; SwiGLU quantized in place, at 1-2 rows inside the down
+    launch's staging) gives the bits of the composition of the separate calls, call after call through the
+    same workspace."""
     log(f"fused moe rows={rows}")
     x = torch.from_numpy(gauss((rows, HIDDEN), 1.0, WL, 32 + rows).numpy()).cuda()
     y, (expert, _, weight), logits = q.moe_step(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN, shared_expert=E)
