@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 from block_quantized_few_amd import qgemv as q
-from helpers import TOL, bits, gauss, log, oracle_image, rel_err
+from helpers import TOL, bits, gauss, log, oracle_image, outliers, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -85,4 +85,26 @@ def test_q4_0_wide_tiles_at_16_rows():
     assert e <= TOL
     for r in (0, rows - 1):
         y1 = q.qgemv_q4_0(img, n, k, xd[r:r + 1].contiguous())
+        assert np.array_equal(bits(y[r]), bits(y1[0]))
+
+
+@pytest.mark.parametrize("rows", [5, 9])
+def test_q8_0_pair_tiles_over_rounds_with_ragged_edges(rows):
+    """Q8_0 pair tiles over several rounds of workgroups (the launch that carries each workgroup's next tile's
+    loads across its combine) on a matrix with a ragged last tile group (n = 40007: 626 tiles of 64 or 32
+    rows, two rounds) and padded blocks (k = 1056, 33 blocks; one lane part per wave part): sampled outputs,
+    the last rows among them, against the oracle, and rows 0 and R-1 against the same rows alone."""
+    n, k = 40007, 1056
+    w = gauss((n, k), 0.02, 31, rows).numpy()
+    blocks, img = oracle_image(O.Q8_0, w)
+    x = outliers((rows, k), 1.0, 31, 100 + rows).numpy()
+    xd = torch.from_numpy(x).cuda()
+    y = q.qgemv_q8_0(img, n, k, xd)
+    sel = np.unique(np.concatenate([np.arange(n - 40, n), np.random.default_rng(rows).choice(n, 200, replace=False)]))
+    yo = O.gemv_q_rows(O.Q8_0, blocks, n, k, x, sel, threads=8)
+    e = rel_err(y.cpu().numpy()[:, sel], yo, blocks, O.Q8_0, x, sel=sel)
+    log(f"Q8_0 {n}x{k} rows={rows} max rel err {e:.3e}")
+    assert e <= TOL
+    for r in (0, rows - 1):
+        y1 = q.qgemv_q8_0(img, n, k, xd[r:r + 1].contiguous())
         assert np.array_equal(bits(y[r]), bits(y1[0]))
