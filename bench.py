@@ -48,6 +48,10 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a plain elementwise kernel over 256 MiB (reads 256 MiB, writes 256 MiB) five "
                         "times, the known-size reference for the HBM byte counters")
+    p.add_argument("--profile", default=None, metavar="WORKLOAD:ROWS",
+                   help="time one sweep workload (lm-head-q8, lm-head-f16, lm-head-fp8, layer-1b, layer-3b, moe) at "
+                        "ROWS activation rows for --steps calls after warm-up, print it, and exit: a short program "
+                        "for rocprofv3")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                    help="reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) "
                         "of a --calibrate-copy run into profiles/traffic.json, then exit")
@@ -243,6 +247,9 @@ def main():
     timer = Timer(torch)
     if args.calibrate_copy:
         calibrate_copy(torch)
+    if args.profile:
+        profile_one(args, torch, q, synth, L, sh, stream, timer)
+        return
 
     # ------------------------------------------------------------ headline ---
     rows = 1
@@ -483,14 +490,16 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
     return out
 
 
-def moe_sweep(torch, q, synth, L, sh, stream, timer):
-    """Routed MoE step (qg_moe_step): router f16 GEMV, top-8 routing + plan, grouped gate/up, SwiGLU + q8,
-    grouped down, combine -- six launches, five at 1-2 rows (SwiGLU + q8 inside the down launch)."""
-    hidden, ffn, E, topk = 2048, 512, 256, 8
-    nimg = E + 1  # index E: the shared expert
+MOE_HIDDEN, MOE_FFN, MOE_E, MOE_TOPK = 2048, 512, 256, 8
+
+
+def moe_weights(torch, q, synth, copies=2):
+    """Two copies of the routed MoE's 256 Q8_0 experts plus the shared one (index 256), stacked, and the f16
+    router image."""
+    hidden, ffn, E = MOE_HIDDEN, MOE_FFN, MOE_E
+    nimg = E + 1
     gu_b = q.image_bytes(q.Q8_0, 2 * ffn, hidden)
     dn_b = q.image_bytes(q.Q8_0, hidden, ffn)
-    copies = 2
     gus, dns = [], []
     for c in range(copies):
         gu = torch.empty(nimg * gu_b, dtype=torch.uint8, device="cuda")
@@ -503,25 +512,41 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
         gus.append(gu)
         dns.append(dn)
     router = q.f16_image(synth.gaussian((E, hidden), 0.02, synth.tensor_seed(3, 0), device="cuda").half())
+    return {"router": router, "gu": gus, "dn": dns, "gu_b": gu_b, "dn_b": dn_b}
+
+
+def moe_call(torch, q, synth, L, sh, W, rows, nx=64):
+    """One qg_moe_step call per index i (weight copy i % copies, input i % nx) and the routed experts."""
+    hidden, ffn, E, topk = MOE_HIDDEN, MOE_FFN, MOE_E, MOE_TOPK
+    m = rows * (topk + 1)
+    xs = [synth.gaussian((rows, hidden), 1.0, synth.tensor_seed(3, 32 + rows, s), device="cuda") for s in range(nx)]
+    logits = torch.empty((rows, E), device="cuda")
+    expert = torch.empty(m, dtype=torch.int32, device="cuda")
+    wgt = torch.empty(m, device="cuda")
+    y = torch.empty((rows, hidden), device="cuda")
+    ws = torch.empty(q.moe_workspace_bytes(rows, E, hidden, ffn, topk, True), dtype=torch.uint8, device="cuda")
+    P = lambda t: t.data_ptr()
+    xps = [P(x) for x in xs]
+    copies = len(W["gu"])
+
+    def one(i):
+        c = i % copies
+        L.qg_moe_step(P(W["router"]), E, hidden, ffn, topk, 1, P(W["gu"][c]), P(W["dn"][c]), xps[i % nx], rows, P(y),
+                      P(logits), P(expert), P(wgt), P(ws), ws.numel(), sh)
+
+    # keep the inputs alive with the closure's owner
+    one.keep = (xs, logits, expert, wgt, y, ws)
+    return one, expert
+
+
+def moe_sweep(torch, q, synth, L, sh, stream, timer):
+    """Routed MoE step (qg_moe_step): router f16 GEMV, top-8 routing + plan, grouped gate/up, SwiGLU + q8,
+    grouped down, combine -- six launches, five at 1-2 rows (SwiGLU + q8 inside the down launch)."""
+    W = moe_weights(torch, q, synth)
     out = []
     for rows in (1, 8, 9, 16):
-        slots = topk + 1
-        m = rows * slots
         nx = 64
-        xs = [synth.gaussian((rows, hidden), 1.0, synth.tensor_seed(3, 32 + rows, s), device="cuda") for s in range(nx)]
-        logits = torch.empty((rows, E), device="cuda")
-        expert = torch.empty(m, dtype=torch.int32, device="cuda")
-        wgt = torch.empty(m, device="cuda")
-        y = torch.empty((rows, hidden), device="cuda")
-        ws = torch.empty(q.moe_workspace_bytes(rows, E, hidden, ffn, topk, True), dtype=torch.uint8, device="cuda")
-        P = lambda t: t.data_ptr()
-        xps = [P(x) for x in xs]
-
-        def one(i):
-            c = i % copies
-            L.qg_moe_step(P(router), E, hidden, ffn, topk, 1, P(gus[c]), P(dns[c]), xps[i % nx], rows, P(y),
-                          P(logits), P(expert), P(wgt), P(ws), ws.numel(), sh)
-
+        one, expert = moe_call(torch, q, synth, L, sh, W, rows, nx)
         ms = time_calls(torch, timer, stream, one, 128)
         # weight bytes actually streamed: router + every touched expert (the shared one included)
         uniq = []
@@ -530,11 +555,60 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
             torch.cuda.synchronize()
             uniq.append(len(set(expert.cpu().tolist())))
         u = sum(uniq) / nx
-        wb = 2 * E * hidden + u * (gu_b + dn_b)
-        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms, 5 if rows <= 2 else 6)
+        wb = 2 * MOE_E * MOE_HIDDEN + u * (W["gu_b"] + W["dn_b"])
+        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms,
+                  5 if rows <= 2 else 6)
         e["unique_experts"] = round(u, 2)
         out.append(e)
     return out
+
+
+def profile_one(args, torch, q, synth, L, sh, stream, timer):
+    """--profile WORKLOAD:ROWS: one workload of the sweep, --warmup untimed then --steps timed calls, for a
+    per-kernel profile (rocprofv3 --kernel-trace --stats, or one --pmc counter per run)."""
+    wl, rows = args.profile.split(":")
+    rows = int(rows)
+    n, k = 128256, 4096
+    if wl in ("lm-head-q8", "lm-head-f16", "lm-head-fp8"):
+        lane = wl[len("lm-head-"):]
+        imgs = []
+        for c in range(2):
+            w = synth.gaussian((n, k), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
+            imgs.append(q.f16_image(w.half()) if lane == "f16" else
+                        q.quantize_weights(q.Q8_0 if lane == "q8" else q.FP8, w))
+            del w
+        x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(4, 32 + rows), device="cuda")
+        y = torch.empty((rows, n), device="cuda")
+        p = [t.data_ptr() for t in imgs]
+        xp, yp = x.data_ptr(), y.data_ptr()
+        if lane == "q8":
+            ws = q.empty_ws(rows, k)
+            fn = lambda i: L.qgemv_q8_0(p[i % 2], n, k, xp, rows, yp, ws.data_ptr(), ws.numel(), sh)
+            wbytes = q.image_bytes(q.Q8_0, n, k)
+        elif lane == "f16":
+            fn = lambda i: L.gemv_f16(p[i % 2], n, k, xp, rows, yp, sh)
+            wbytes = 2 * n * k
+        else:
+            ws = q.prepare_fp8(x)
+            fn = lambda i: L.qgemv_fp8_prepared(p[i % 2], n, k, ws.data_ptr(), rows, yp, sh)
+            wbytes = q.image_bytes(q.FP8, n, k)
+    elif wl in ("layer-1b", "layer-3b"):
+        lay, fmt, wid = (LAYER_1B, q.Q8_0, 1) if wl == "layer-1b" else (LAYER_3B, q.Q4_0, 2)
+        ls = LayerSet(torch, q, synth, lay, fmt, wid, rows)
+        fn = lambda i: L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh)
+        wbytes = ls.wbytes
+    elif wl == "moe":
+        W = moe_weights(torch, q, synth)
+        fn, _ = moe_call(torch, q, synth, L, sh, W, rows)
+        wbytes = None
+    else:
+        raise SystemExit(f"--profile: unknown workload {wl!r}")
+    ms = time_calls(torch, timer, stream, fn, args.steps)
+    line = {"profile": wl, "rows": rows, "steps": args.steps, "us_per_call": round(ms * 1e3, 3)}
+    if wbytes:
+        line["weight_bytes"] = int(wbytes)
+        line["weight_gbps"] = round(wbytes / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
