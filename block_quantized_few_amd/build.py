@@ -18,7 +18,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wextra", "-Wno-unused-parameter", "-Wno-unused-function",
 ]
 
 

@@ -843,7 +843,7 @@ __device__ __forceinline__ void grouped_small_unit(const uint8_t* __restrict__ i
   float* red = reinterpret_cast<float*>(lds + lds_x);
   const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
   __syncthreads();  // the previous unit is done with s_map and LDS
-  if (threadIdx.x < cnt) {
+  if ((int)threadIdx.x < cnt) {
     const int a = sorted[start + threadIdx.x];
     s_map[threadIdx.x] = x_index ? x_index[a] : a;
     s_map[QG_MAX_ROWS + threadIdx.x] = a;
@@ -916,7 +916,7 @@ __device__ __forceinline__ void grouped_big_unit(const uint8_t* __restrict__ ima
   const int rpt = (WAVES / (pl.S * mp_w2(pl.H))) * TILE;
   const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
   __syncthreads();  // the previous unit is done with s_map and LDS
-  if (threadIdx.x < cnt) {
+  if ((int)threadIdx.x < cnt) {
     const int a = sorted[start + threadIdx.x];
     s_map[threadIdx.x] = x_index ? x_index[a] : a;
     s_map[QG_MAX_ROWS + threadIdx.x] = a;
@@ -987,7 +987,9 @@ int device_cus() {
 // loop over the remaining tiles) and no more than there are tiles.
 template <typename K>
 static unsigned persistent_grid(K kernel, size_t lds, int64_t tiles) {
-  if (lds > 48 * 1024) hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // a failure here makes the launch itself fail, which its caller reports
+  if (lds > 48 * 1024)
+    (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WG, lds) != hipSuccess || per_cu < 1) per_cu = 1;
   const int64_t g = (int64_t)device_cus() * per_cu;
@@ -1061,7 +1063,8 @@ static void launch_mp(SetArgs a, int rows, hipStream_t s) {
   if constexpr (FMT == FMT_Q8) {
     if (rn > 1) {
       auto kp = mp_set_kernel<FMT, G, false, true>;  // the occupancy of kn (128 registers at most)
-      if (ln > 48 * 1024) hipFuncSetAttribute((const void*)kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ln);
+      if (ln > 48 * 1024)
+        (void)hipFuncSetAttribute((const void*)kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ln);
       hipLaunchKernelGGL(kp, dim3(gn), dim3(WG), ln, s, a, rows);
       return;
     }
