@@ -58,6 +58,11 @@ int check_device() {
 
 using namespace qg;
 
+// The marker qg_device_supported looks for: present in the device code object
+// of every build of this library; its value is the version of the image
+// layouts and kernels the header declares.
+__device__ int qg_layout_marker = 1;
+
 extern "C" {
 
 const char* qg_status_string(int status) {
@@ -72,6 +77,22 @@ const char* qg_status_string(int status) {
     case QG_EDEVICE: return "not a gfx950 device";
     default: return "unknown status";
   }
+}
+
+int qg_device_supported(int device) {
+  int prev = -1, count = 0;
+  if (hipGetDevice(&prev) != hipSuccess || hipGetDeviceCount(&count) != hipSuccess) return 0;
+  if (device < 0 || device >= count) return 0;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess || strncmp(prop.gcnArchName, "gfx950", 6) != 0) return 0;
+  if (device != prev && hipSetDevice(device) != hipSuccess) return 0;
+  void* addr = nullptr;
+  size_t bytes = 0;
+  const bool ok = hipGetSymbolAddress(&addr, HIP_SYMBOL(qg_layout_marker)) == hipSuccess && addr != nullptr &&
+                  hipGetSymbolSize(&bytes, HIP_SYMBOL(qg_layout_marker)) == hipSuccess &&
+                  bytes == sizeof(qg_layout_marker);
+  if (device != prev && hipSetDevice(prev) != hipSuccess) return 0;
+  return ok ? 1 : 0;
 }
 
 int qg_last_error_detail(char* buf, size_t len) {

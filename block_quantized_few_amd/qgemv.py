@@ -58,6 +58,7 @@ _SIGS = {
     "qg_grouped_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64, C.c_int]),
     "qg_status_string": (C.c_char_p, [C.c_int]),
     "qg_last_error_detail": (C.c_int, [C.c_char_p, C.c_size_t]),
+    "qg_device_supported": (C.c_int, [C.c_int]),
     "qg_quantize_weights": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
     "qg_prepare_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qg_add_rmsnorm_prepare": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_float, C.c_int, C.c_int64,
@@ -183,6 +184,11 @@ def unpack_image(fmt, image, n, k):
         out = np.empty((n, k // 32, 34 if fmt == Q8_0 else 18), np.uint8)
     _check(lib().qg_unpack_image(fmt, image.ctypes.data_as(C.c_void_p), n, k, out.ctypes.data_as(C.c_void_p)))
     return out
+
+
+def device_supported(device=0):
+    """True when HIP device `device` is a gfx950 carrying this library's kernels (qg_device_supported)."""
+    return bool(lib().qg_device_supported(device))
 
 
 def status_string(status):

@@ -149,6 +149,16 @@ const char* qg_status_string(int status);
  * NUL-terminated; returns the status of that call (QG_OK if none failed). */
 int qg_last_error_detail(char* buf, size_t len);
 
+/* Capability probe: 1 when HIP device `device` is a gfx950 on which this
+ * library's code object carries its marker, a device global that stands for
+ * the image layouts and kernels declared here; 0 otherwise.  Any driver
+ * failure, the marker's name missing included, answers 0, never an error
+ * status (the drama page's series commits: a promise a code object carries
+ * in a device global, checked by the host before it relies on it).  Host
+ * only; launches nothing and leaves the calling thread's current device as
+ * it found it. */
+int qg_device_supported(int device);
+
 /* ---------------------------------------------------------------- device --- */
 
 /* Quantizes fp32 weights w [n][k] (device) into a device image of `fmt`

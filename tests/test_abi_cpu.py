@@ -243,3 +243,12 @@ def test_rows_zero_is_a_noop():
 def test_valid_call_without_gpu_reports_device():
     st, msg = _status("qgemv_q8_0", V(A), 64, 64, V(A), 1, V(A), V(A), 1 << 20, None)
     assert st == -7, msg
+
+
+def test_device_probe_answers_false_not_an_error():
+    # invalid device numbers are a failure of the driver query: 0, never a negative status
+    assert q.lib().qg_device_supported(-1) == 0
+    assert q.lib().qg_device_supported(1 << 20) == 0
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert q.device_supported(0) is False

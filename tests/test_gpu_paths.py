@@ -108,3 +108,12 @@ def test_q8_0_pair_tiles_over_rounds_with_ragged_edges(rows):
     for r in (0, rows - 1):
         y1 = q.qgemv_q8_0(img, n, k, xd[r:r + 1].contiguous())
         assert np.array_equal(bits(y[r]), bits(y1[0]))
+
+
+def test_device_probe_on_the_gpu():
+    """The capability probe finds the library's marker on the gfx950 it runs on, answers false for device
+    numbers that do not exist, and leaves the current device as it was."""
+    dev = torch.cuda.current_device()
+    assert q.device_supported(dev)
+    assert not q.device_supported(-1) and not q.device_supported(torch.cuda.device_count())
+    assert torch.cuda.current_device() == dev
