@@ -1072,18 +1072,28 @@ static void launch_mp(SetArgs a, int rows, hipStream_t s) {
   hipLaunchKernelGGL(kn, dim3(gn), dim3(WG), ln, s, a, rows);
 }
 
+// Launch order of a set's projections on the 1-2-row kernel: longer lane
+// chains (blocks per lane part) first, then longer rows.
+static bool rl_before(int64_t ka, int64_t kb) {
+  const int ba = part_plan((int)kbp_of(ka)).BS, bb = part_plan((int)kbp_of(kb)).BS;
+  return ba != bb ? ba > bb : ka > kb;
+}
+
 int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStream_t s) {
   SetArgs a;
   memset(&a, 0, sizeof a);
   a.count = count;
   const bool mf = prep_pairs(rows);  // 3..16 rows: the pair kernel
   // Tiles of projections with longer rows come first: their workgroups stage
-  // the most activation blocks, so they get the earliest start.  The order
-  // changes no result (each projection has its own output).
+  // the most activation blocks, so they get the earliest start; on the
+  // 1-2-row kernel those whose lanes walk more blocks come before them (the
+  // longest chains start first).  The order changes no result (each
+  // projection has its own output).
   int order[QG_MAX_SET];
   for (int i = 0; i < count; i++) order[i] = i;
+  auto before = [&](int64_t ka, int64_t kb) { return mf ? ka > kb : rl_before(ka, kb); };
   for (int i = 1; i < count; i++)
-    for (int j = i; j > 0 && projs[order[j]].k > projs[order[j - 1]].k; j--) {
+    for (int j = i; j > 0 && before(projs[order[j]].k, projs[order[j - 1]].k); j--) {
       const int t = order[j];
       order[j] = order[j - 1];
       order[j - 1] = t;
