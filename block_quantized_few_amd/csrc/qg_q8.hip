@@ -659,7 +659,8 @@ struct ProjDev {
   int tiles;
   int rows_per_tile;
   PartPlan pl;
-  int ucx;  // RL staging round
+  int ucx;   // RL staging round
+  int wide;  // pair kernel, per-projection width (MP_MIXED launches)
 };
 struct SetArgs {
   ProjDev p[QG_MAX_SET];
@@ -725,31 +726,50 @@ void rl_set_kernel(SetArgs a, int lds_x) {
   }
 }
 
-// PF: each workgroup's tiles of a projection in one mp_tile call, the next
-// tile's loads in flight while a tile is combined (for launches of several
-// rounds; it costs registers).
-template <int FMT, int G, bool WIDE, bool PF>
+// Width of a pair-kernel launch: every projection on narrow tiles, every one
+// on wide tiles, or each on its own (ProjDev::wide).
+enum { MP_NARROW = 0, MP_WIDE = 1, MP_MIXED = 2 };
+
+// The workgroup's tiles of one projection at width W (tiles row0, row0 +
+// stride, ...: cnt of them, one unless PF).
+template <int FMT, int G, bool W, bool PF>
+__device__ __forceinline__ void mp_tiles(const TileArgs& ta, int R, float* red, uint16_t* scl, int cnt,
+                                         int64_t stride) {
+  const int H = ta.pl.H;
+  if (H == 1) mp_tile<FMT, 1, G, mp_nt(1, G, W), false, PF>(ta, R, red, scl, cnt, stride);
+  else if (H == 2) mp_tile<FMT, 2, G, mp_nt(2, G, W), false, PF>(ta, R, red, scl, cnt, stride);
+  else if (H == 4) mp_tile<FMT, 4, G, mp_nt(4, G, W), false, PF>(ta, R, red, scl, cnt, stride);
+  else mp_tile<FMT, 8, G, mp_nt(8, G, W), false, PF>(ta, R, red, scl, cnt, stride);
+}
+
+// PF: each workgroup's narrow tiles of a projection in one mp_tile call, the
+// next tile's loads in flight while a tile is combined (for launches of
+// several rounds; it costs registers, so Q8_0 only).
+template <int FMT, int G, int WIDTH, bool PF>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp_set_kernel(SetArgs a, int R) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
   float* red = reinterpret_cast<float*>(lds);  // combine area, then the waves' staged scales
   uint16_t* scl = reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4);
-  constexpr bool MP_PF = PF && !WIDE && FMT == FMT_Q8;
+  constexpr bool MP_PF = PF && WIDTH == MP_NARROW && FMT == FMT_Q8;
   for (int tile = blockIdx.x; tile < a.total_tiles;) {
     int p = 0, t0 = tile;
     while (p + 1 < a.count && t0 >= a.p[p].tiles) t0 -= a.p[p++].tiles;
     const ProjDev& d = a.p[p];
     const TileArgs ta = tile_args(d, (int64_t)t0 * d.rows_per_tile, s_map, 0);
-    const PartPlan& pl = d.pl;
     // this workgroup's tiles of the projection, t0, t0 + G, ..., in one call
     // (narrow Q8_0 tiles; the others have no registers to spare for it)
     const int cnt = MP_PF ? (d.tiles - 1 - t0) / (int)gridDim.x + 1 : 1;
     const int64_t stride = (int64_t)gridDim.x * d.rows_per_tile;
-    if (pl.H == 1) mp_tile<FMT, 1, G, mp_nt(1, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
-    else if (pl.H == 2) mp_tile<FMT, 2, G, mp_nt(2, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
-    else if (pl.H == 4) mp_tile<FMT, 4, G, mp_nt(4, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
-    else mp_tile<FMT, 8, G, mp_nt(8, G, WIDE), false, MP_PF>(ta, R, red, scl, cnt, stride);
+    if constexpr (WIDTH == MP_NARROW) {
+      mp_tiles<FMT, G, false, MP_PF>(ta, R, red, scl, cnt, stride);
+    } else if constexpr (WIDTH == MP_WIDE) {
+      mp_tiles<FMT, G, true, false>(ta, R, red, scl, cnt, stride);
+    } else {
+      if (d.wide) mp_tiles<FMT, G, true, false>(ta, R, red, scl, cnt, stride);
+      else mp_tiles<FMT, G, false, false>(ta, R, red, scl, cnt, stride);
+    }
     tile += cnt * (int)gridDim.x;
   }
 }
@@ -1026,12 +1046,13 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
 // Tiles of the pair kernel at width `wide`; returns the LDS bytes it needs
 // (combine area, then each wave's staged scales: NT tiles of kbp/S blocks x
 // 16 fp16).
-static size_t mp_fill(SetArgs& a, int G, bool wide) {
+static size_t mp_fill(SetArgs& a, int G, int width) {
   int64_t tiles = 0;
   size_t sc = 0;
   for (int i = 0; i < a.count; i++) {
     ProjDev& d = a.p[i];
-    const int nt = mp_nt(d.pl.H, G, wide);
+    if (width != MP_MIXED) d.wide = width == MP_WIDE;
+    const int nt = mp_nt(d.pl.H, G, d.wide != 0);
     d.rows_per_tile = (WAVES / (d.pl.S * mp_w2(d.pl.H))) * TILE * nt;
     d.tiles = (int)((d.n + d.rows_per_tile - 1) / d.rows_per_tile);
     tiles += d.tiles;
@@ -1042,27 +1063,58 @@ static size_t mp_fill(SetArgs& a, int G, bool wide) {
   return (size_t)WAVES * WAVE * MP_NV_MAX * 4 + WAVES * sc;
 }
 
+// Weight bytes one wave of projection d streams per tile group on wide tiles.
+static int64_t mp_wide_wave_bytes(const ProjDev& d, int fmt, int G) {
+  return (int64_t)mp_nt(d.pl.H, G, true) * (d.kbp / (d.pl.S * mp_w2(d.pl.H))) * (fmt == FMT_Q8 ? 512 : 256);
+}
+
 // The pair kernel runs in rounds of the workgroups resident at once; a round
-// costs about a tile's latency chain.  Wide tiles win when they need fewer
-// rounds at 9-16 rows (half the activation-chunk loads), and at 3-8 rows
-// when they fit one round that narrow tiles overflow.  Narrow Q8_0 tiles over
-// several rounds take the kernel that prefetches across a workgroup's tiles.
+// costs about a tile's latency chain.  At 9-16 rows every projection takes
+// wide tiles when that needs fewer rounds (half the activation-chunk loads).
+// At 3-8 rows, when narrow tiles overflow one round, projections move to
+// wide tiles one at a time, those whose waves then stream the least first,
+// until the launch fits one round (a wave's stream is the latency chain that
+// ends the launch).  Narrow Q8_0 tiles over several rounds take the kernel
+// that prefetches across a workgroup's tiles.
 template <int FMT, int G>
 static void launch_mp(SetArgs a, int rows, hipStream_t s) {
-  auto kn = mp_set_kernel<FMT, G, false, false>;
-  auto kw = mp_set_kernel<FMT, G, true, false>;
+  auto kn = mp_set_kernel<FMT, G, MP_NARROW, false>;
+  auto kw = mp_set_kernel<FMT, G, MP_WIDE, false>;
   SetArgs aw = a;
-  const size_t ln = mp_fill(a, G, false), lw = mp_fill(aw, G, true);
+  const size_t ln = mp_fill(a, G, MP_NARROW), lw = mp_fill(aw, G, MP_WIDE);
   const unsigned gn = persistent_grid(kn, ln, a.total_tiles), gw = persistent_grid(kw, lw, aw.total_tiles);
   const int64_t rn = (a.total_tiles + gn - 1) / gn, rw = (aw.total_tiles + gw - 1) / gw;
-  const bool wide = G == 2 ? rw < rn : (rn > 1 && rw == 1);
-  if (wide) {
+  if (G == 2 && rw < rn) {
     hipLaunchKernelGGL(kw, dim3(gw), dim3(WG), lw, s, aw, rows);
     return;
   }
+  if constexpr (G == 1) {
+    // Widen projections, those whose waves then stream the least first,
+    // until the launch fits one round of resident workgroups.
+    auto km = mp_set_kernel<FMT, G, MP_MIXED, false>;
+    SetArgs am = a;
+    int order[QG_MAX_SET];
+    for (int i = 0; i < am.count; i++) order[i] = i;
+    for (int i = 1; i < am.count; i++)
+      for (int j = i; j > 0 && mp_wide_wave_bytes(am.p[order[j]], FMT, G) <
+                                   mp_wide_wave_bytes(am.p[order[j - 1]], FMT, G); j--) {
+        const int t = order[j];
+        order[j] = order[j - 1];
+        order[j - 1] = t;
+      }
+    for (int i = 0; i < am.count && rn > 1; i++) {
+      am.p[order[i]].wide = 1;
+      const size_t lm = mp_fill(am, G, MP_MIXED);
+      const unsigned gm = persistent_grid(km, lm, am.total_tiles);
+      if (am.total_tiles <= (int64_t)gm) {
+        hipLaunchKernelGGL(km, dim3(gm), dim3(WG), lm, s, am, rows);
+        return;
+      }
+    }
+  }
   if constexpr (FMT == FMT_Q8) {
     if (rn > 1) {
-      auto kp = mp_set_kernel<FMT, G, false, true>;  // the occupancy of kn (128 registers at most)
+      auto kp = mp_set_kernel<FMT, G, MP_NARROW, true>;  // the occupancy of kn (128 registers at most)
       if (ln > 48 * 1024)
         (void)hipFuncSetAttribute((const void*)kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ln);
       hipLaunchKernelGGL(kp, dim3(gn), dim3(WG), ln, s, a, rows);
