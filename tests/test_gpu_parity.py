@@ -70,7 +70,7 @@ def test_blockdots_bit_exact(fmt, ofmt, n, k, rows):
 
 # ------------------------------------------------------------- A2-A4 ---
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
-@pytest.mark.parametrize("n,k", [(1024, 1024), (1000, 800), (33, 96), (257, 4096)])
+@pytest.mark.parametrize("n,k", [(1024, 1024), (1000, 800), (33, 96), (257, 4096), (1, 32)])
 def test_qgemv_parity(fmt, ofmt, n, k):
     w = gauss((n, k), 0.02, 13, 5).numpy()
     blocks, img = oracle_image(ofmt, w)
@@ -157,7 +157,7 @@ def test_set_launch_equals_single_calls():
 
 
 # ------------------------------------------------------------- f16 lane ---
-@pytest.mark.parametrize("n,k", [(256, 2048), (1000, 800), (33, 104), (130, 4096)])
+@pytest.mark.parametrize("n,k", [(256, 2048), (1000, 800), (33, 104), (130, 4096), (1, 8)])
 def test_f16_parity(n, k):
     w = gauss((n, k), 0.02, 17, 12).numpy()
     w16, _ = O.f32_to_f16(w)
