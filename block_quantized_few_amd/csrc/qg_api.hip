@@ -320,6 +320,31 @@ int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64
   return ok();
 }
 
+int qgemv_fp8_grouped(const void* w_images, int64_t n_experts, int64_t n, int64_t k, const float* x, int x_rows,
+                      const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, size_t ws_bytes,
+                      qg_stream stream) {
+  if (n_experts < 1 || n_experts > (1 << 30)) return fail(QG_ESHAPE, "n_experts=%lld", (long long)n_experts);
+  if (m < 0 || m > QG_MAX_ASSIGN) return fail(QG_ESHAPE, "m=%d outside 0..%d", m, QG_MAX_ASSIGN);
+  if (int st = check_fp8_nk(n, k)) return st;
+  if (int st = check_image(w_images, "w_images")) return st;
+  if (m && check_y(y)) return check_y(y);
+  if (int st = check_x(x, x_rows, k, QG_MAX_PREP_ROWS)) return st;
+  if (m && (!expert || !x_index)) return fail(QG_EINVAL, "expert or x_index is null");
+  const GroupedLayout G = grouped_fp8_layout(x_rows, k, m);
+  if (int st = check_ws(ws, ws_bytes, G.total, "the FP8 grouped call")) return st;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  int* header = (int*)(w + G.header);
+  int* sorted = (int*)(w + G.sorted);
+  int* items = (int*)(w + G.items);
+  if (int st = launch_fp8_prepare(x, x_rows, k, w + G.prep, s)) return st;
+  if (int st = launch_grouped_plan(expert, x_index, m, n_experts, x_rows, header, sorted, items, s)) return st;
+  if (int st = launch_grouped_fp8(w_images, n, k, w + G.prep, x_rows, header, sorted, items, x_index, m, y, s))
+    return st;
+  return ok();
+}
+
 int qg_grouped_status(const void* ws, int32_t* bad, qg_stream stream) {
   if (!ws || !bad) return fail(QG_EINVAL, "null argument");
   if (int st = check_device()) return st;

@@ -293,4 +293,124 @@ int launch_gemv_fp8(const void* image, int64_t n, int64_t k, const void* ws, int
   return hip_status(hipGetLastError(), "gemv_fp8_kernel");
 }
 
+// ------------------------------------------------------------ grouped ---
+// Routed experts: persistent over the (item, tile group) units of the grouped
+// plan (items of at most 16 assignments of one expert).  A unit is a tile
+// group of gemv_fp8_kernel over the item's expert image, its activation
+// columns the item's rows gathered from the prepared rows through the row
+// map, its outputs written to the assignments' rows.  The group order and
+// the wave split are those of gemv_fp8_kernel for the same n (S set by the
+// tile count alike), so each assignment's output has the bits of the
+// one-row dense call on its row.
+template <int NT, int S, int LA>
+__global__ __launch_bounds__(S * WAVE) void grouped_fp8_kernel(
+    const uint8_t* __restrict__ images, int64_t expert_bytes, int64_t scale_off, int64_t N, int64_t K,
+    const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, const int* __restrict__ header,
+    const int* __restrict__ sorted, const int* __restrict__ items, const int32_t* __restrict__ x_index,
+    float* __restrict__ y, int64_t tgroups) {
+  __shared__ float red[S * NT * 4 * WAVE];
+  __shared__ int s_map[2 * QG_MAX_ROWS];  // activation row, then output row, of each column
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
+  const int i = lane & 15, q = lane >> 4;
+  const int64_t kg = K / F8_GROUP, tiles = (N + 15) / 16;
+  const int64_t g0 = kg * wave / S, g1 = kg * (wave + 1) / S;  // this wave's groups
+  const int64_t ng = g1 - g0;
+  const int64_t units = (int64_t)header[0] * tgroups;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {  // uniform over the workgroup
+    const int item = (int)(u / tgroups);
+    const int64_t grp = u - (int64_t)item * tgroups;
+    const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
+    __syncthreads();  // the previous unit is done with s_map and red
+    if ((int)threadIdx.x < cnt) {
+      const int a = sorted[start + threadIdx.x];
+      s_map[threadIdx.x] = x_index ? x_index[a] : a;
+      s_map[QG_MAX_ROWS + threadIdx.x] = a;
+    }
+    __syncthreads();
+    const uint8_t* img = images + (int64_t)e * expert_bytes;
+    const float* wsc = reinterpret_cast<const float*>(img + scale_off);
+    const int xr = s_map[i < cnt ? i : cnt - 1];  // columns past the item's rows read a real row, store nothing
+    const uint8_t* xc = xcodes + (int64_t)xr * K + 32 * q;
+    const float* xs = xscales + (int64_t)xr * kg;
+    const uint8_t* wt[NT];
+    const float* wsr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      int64_t tt = grp * NT + t;
+      tt = tt < tiles ? tt : tiles - 1;  // past the end: reread, store nothing
+      wt[t] = img + tt * kg * F8_STEP_BYTES + 16 * lane;
+      wsr[t] = wsc + (tt >> 3) * kg;
+    }
+    int64_t lc = g0 + (ng ? ((grp * NT >> 2) * F8_ROT) % ng : 0);
+    F8Step<NT> f[LA];
+#pragma unroll
+    for (int j = 0; j < LA; j++)
+      if (j < ng) {
+        f8_load<NT>(f[j], wt, wsr, xc, xs, lc);
+        lc = lc + 1 == g1 ? g0 : lc + 1;
+      }
+    v4f acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int64_t st = 0; st < ng; st += LA) {
+#pragma unroll
+      for (int j = 0; j < LA; j++) {
+        if (st + j < ng) {
+          f8_compute<NT>(acc, f[j]);
+          if (st + j + LA < ng) {
+            f8_load<NT>(f[j], wt, wsr, xc, xs, lc);
+            lc = lc + 1 == g1 ? g0 : lc + 1;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) red[((wave * NT + t) * 4 + v) * WAVE + lane] = acc[t][v];
+    __syncthreads();
+    if (wave == 0 && i < cnt) {
+      const int64_t orow = s_map[QG_MAX_ROWS + i];
+#pragma unroll
+      for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          float a = red[(t * 4 + v) * WAVE + lane];
+          for (int s2 = 1; s2 < S; s2++) a += red[((s2 * NT + t) * 4 + v) * WAVE + lane];
+          const int64_t row = (grp * NT + t) * 16 + 4 * q + v;
+          if (row < N) y[orow * N + row] = a;
+        }
+    }
+  }
+}
+
+template <int NT, int S, int LA>
+static void launch_grouped_fp8_t(const uint8_t* images, int64_t eb, int64_t so, int64_t n, int64_t k,
+                                 const uint8_t* xc, const float* xs, const int* header, const int* sorted,
+                                 const int* items, const int32_t* x_index, int m, float* y, hipStream_t s) {
+  auto kern = grouped_fp8_kernel<NT, S, LA>;
+  const int64_t tgroups = (f16_tiles(n) + NT - 1) / NT;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, S * WAVE, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t g = (int64_t)device_cus() * per_cu, units = (int64_t)m * tgroups;  // at most m items
+  hipLaunchKernelGGL(kern, dim3((unsigned)(units < g ? units : g)), dim3(S * WAVE), 0, s, images, eb, so, n, k, xc,
+                     xs, header, sorted, items, x_index, y, tgroups);
+}
+
+int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws, int x_rows, const int* header,
+                       const int* sorted, const int* items, const int32_t* x_index, int m, float* y, hipStream_t s) {
+  if (m == 0) return QG_OK;
+  const uint8_t* img = static_cast<const uint8_t*>(images);
+  const int64_t eb = (int64_t)fp8_image_bytes(n, k), so = (int64_t)fp8_scale_offset(n, k);
+  const uint8_t* xc = static_cast<const uint8_t*>(ws);
+  const float* xs = reinterpret_cast<const float*>(xc + fp8_ws_scale_offset(x_rows, k));
+  // S as launch_gemv_fp8 sets it for this n (the bits of the dense call)
+  const int64_t t16 = f16_tiles(n);
+  if (t16 >= 4096) launch_grouped_fp8_t<2, 2, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
+  else if (t16 >= 256) launch_grouped_fp8_t<1, 4, 4>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
+  else launch_grouped_fp8_t<1, 8, 4>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
+  return hip_status(hipGetLastError(), "grouped_fp8_kernel");
+}
+
 }  // namespace qg

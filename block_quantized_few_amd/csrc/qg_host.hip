@@ -122,6 +122,11 @@ size_t qg_workspace_bytes(int rows, int64_t k) {
   return prep_layout(rows, k).total;
 }
 
+size_t qg_fp8_grouped_workspace_bytes(int x_rows, int64_t k, int m) {
+  if (x_rows < 1 || x_rows > QG_MAX_PREP_ROWS || k < 128 || k % 128 || m < 0 || m > QG_MAX_ASSIGN) return 0;
+  return grouped_fp8_layout(x_rows, k, m).total;
+}
+
 size_t qg_grouped_workspace_bytes(int x_rows, int64_t k, int m) {
   if (x_rows < 1 || x_rows > QG_MAX_PREP_ROWS || k < QK || k % QK || m < 0 || m > QG_MAX_ASSIGN) return 0;
   return grouped_layout(x_rows, k, m).total;

@@ -49,6 +49,15 @@ bool fuses_quantization(int rows);
 // Grouped routed-expert Q8_0 GEMV (plan + GEMV; rows already prepared in ws).
 int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
                    const int32_t* x_index, int m, float* y, void* ws, hipStream_t s);
+// The grouped plan alone (one workgroup): header, sorted, items of at most
+// QG_MAX_ROWS assignments of one expert.
+int launch_grouped_plan(const int32_t* expert, const int32_t* x_index, int m, int64_t n_experts, int x_rows,
+                        int* header, int* sorted, int* items, hipStream_t s);
+// FP8 lane, grouped: the plan's items over n x k block-FP8 expert images
+// (expert_bytes apart), activation groups of x_rows rows at `ws` (the FP8
+// workspace layout), y [m][n].
+int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws, int x_rows, const int* header,
+                       const int* sorted, const int* items, const int32_t* x_index, int m, float* y, hipStream_t s);
 
 // Grouped GEMV on a plan already in `ws` (header, sorted, items at the
 // grouped layout's offsets) and rows prepared at `prep` in row order;

@@ -146,6 +146,14 @@ QG_HD GroupedLayout grouped_layout(int64_t x_rows, int64_t k, int64_t m) {
   return G;
 }
 
+// Workspace of the FP8 lane's grouped call: the same plan, then the FP8
+// activation groups of the x_rows rows (fp8_ws_bytes).
+QG_HD GroupedLayout grouped_fp8_layout(int64_t x_rows, int64_t k, int64_t m) {
+  GroupedLayout G = grouped_layout(x_rows, k, m);
+  G.total = G.prep + fp8_ws_bytes(x_rows, k);
+  return G;
+}
+
 // Workspace of a fused routed-MoE step (qg_moe_step): rows <= 16 input rows,
 // m = rows * slots assignments, slots = topk (+1 with a shared expert).
 constexpr int QG_MOE_MAX_M = 16 * 33;

@@ -1240,6 +1240,13 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
   return QG_OK;
 }
 
+int launch_grouped_plan(const int32_t* expert, const int32_t* x_index, int m, int64_t n_experts, int x_rows,
+                        int* header, int* sorted, int* items, hipStream_t s) {
+  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(1024), 0, s, expert, x_index, m, n_experts, x_rows, header,
+                     sorted, items);
+  return hip_status(hipGetLastError(), "grouped_plan_kernel");
+}
+
 int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
                    const int32_t* x_index, int m, float* y, void* ws, hipStream_t s) {
   const GroupedLayout G = grouped_layout(x_rows, k, m);
@@ -1247,9 +1254,7 @@ int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, 
   int* header = (int*)(w + G.header);
   int* sorted = (int*)(w + G.sorted);
   int* items = (int*)(w + G.items);
-  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(1024), 0, s, expert, x_index, m, n_experts, x_rows, header,
-                     sorted, items);
-  if (int st = hip_status(hipGetLastError(), "grouped_plan_kernel")) return st;
+  if (int st = launch_grouped_plan(expert, x_index, m, n_experts, x_rows, header, sorted, items, s)) return st;
   return launch_grouped_planned(images, n_experts, n, k, w + G.prep, x_rows, header, sorted, items, x_index, m,
                                 QG_MAX_ROWS, y, s);
 }

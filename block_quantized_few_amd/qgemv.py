@@ -77,6 +77,9 @@ _SIGS = {
     "qgemv_q8_0_grouped": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
                                      C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qg_grouped_status": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_void_p]),
+    "qg_fp8_grouped_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64, C.c_int]),
+    "qgemv_fp8_grouped": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
+                                    C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qg_moe_route": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                C.c_void_p]),
     "qg_swiglu": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p]),
@@ -357,6 +360,26 @@ def qgemv_q8_0_grouped(images, n_experts, n, k, x, expert, x_index, y=None, ws=N
         ws = torch.empty(grouped_workspace_bytes(x_rows, k, m), dtype=torch.uint8, device=x.device)
     _check(lib().qgemv_q8_0_grouped(_p(images), n_experts, n, k, _p(x), x_rows, _p(expert), _p(x_index), m, _p(y),
                                     _p(ws), ws.numel(), _stream()))
+    return y, ws
+
+
+def fp8_grouped_workspace_bytes(x_rows, k, m):
+    return lib().qg_fp8_grouped_workspace_bytes(x_rows, k, m)
+
+
+def qgemv_fp8_grouped(images, n_experts, n, k, x, expert, x_index, y=None, ws=None):
+    """FP8-lane grouped routed-expert GEMV (qgemv_fp8_grouped); returns (y [m][n], ws)."""
+    _dev(x, torch.float32, "x")
+    _dev(expert, torch.int32, "expert")
+    _dev(x_index, torch.int32, "x_index")
+    x_rows = x.shape[0]
+    m = expert.numel()
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, fp8_grouped_workspace_bytes(x_rows, k, m)), dtype=torch.uint8, device=x.device)
+    _check(lib().qgemv_fp8_grouped(_p(images), n_experts, n, k, _p(x), x_rows, _p(expert), _p(x_index), m, _p(y),
+                                   _p(ws), ws.numel(), _stream()))
     return y, ws
 
 

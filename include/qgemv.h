@@ -281,6 +281,19 @@ int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64
                        const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, size_t ws_bytes,
                        qg_stream stream);
 
+/* Grouped routed-expert GEMV, FP8 lane (the drama page's backbone runs its
+ * routed experts in block-FP8 with 1 x 128 FP8 activation groups): as
+ * qgemv_q8_0_grouped, with w_images n_experts FP8 images back to back, each
+ * qg_image_bytes(QG_FMT_FP8, n, k) bytes (k a multiple of 128), and the rows
+ * of x quantized into FP8 groups as qg_prepare_fp8 does.  Each assignment's
+ * y[j] has the bits of qgemv_fp8 on its row alone.  ws:
+ * qg_fp8_grouped_workspace_bytes(x_rows, k, m) bytes; qg_grouped_status reads
+ * its skipped count. */
+size_t qg_fp8_grouped_workspace_bytes(int x_rows, int64_t k, int m);
+int qgemv_fp8_grouped(const void* w_images, int64_t n_experts, int64_t n, int64_t k, const float* x, int x_rows,
+                      const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, size_t ws_bytes,
+                      qg_stream stream);
+
 /* Synchronizes `stream`, then reads the count of skipped assignments of the
  * last grouped call on `ws` into *bad (host). */
 int qg_grouped_status(const void* ws, int32_t* bad, qg_stream stream);

@@ -192,6 +192,20 @@ def test_validation_refuses_before_any_hip_call():
     assert st == -2 and "k=96" in msg
     st, msg = _status("qgemv_fp8", V(A), 64, 256, V(A), 0, V(A), V(A), 0, None)
     assert st == 0
+    # FP8 grouped: images, n_experts, n, k, x, x_rows, expert, x_index, m, y, ws, ws_bytes
+    st, msg = _status("qgemv_fp8_grouped", V(A), 8, 64, 96, V(A), 1, V(A), V(A), 4, V(A), V(A), MB, None)
+    assert st == -2 and "k=96" in msg
+    st, msg = _status("qgemv_fp8_grouped", V(A), 8, 64, 256, V(A), 1, V(A), V(A), q.MAX_ASSIGN + 1, V(A), V(A),
+                      MB, None)
+    assert st == -2
+    st, msg = _status("qgemv_fp8_grouped", V(A), 8, 64, 256, V(A), 2, V(A), V(A), 4, V(A), V(A), 100, None)
+    assert st == -5 and "ws_bytes=100" in msg
+    st, msg = _status("qgemv_fp8_grouped", V(A), 8, 64, 256, V(A), 2, None, V(A), 4, V(A), V(A), MB, None)
+    assert st == -1
+    # its workspace: the grouped plan (256-byte header, then 10 sorted indices and 10 items, each plane 256-byte
+    # aligned), then the FP8 groups of the 3 x rows
+    assert q.fp8_grouped_workspace_bytes(3, 256, 10) == 256 + 256 + 256 + q.fp8_workspace_bytes(3, 256)
+    assert q.fp8_grouped_workspace_bytes(3, 200, 10) == 0 and q.fp8_grouped_workspace_bytes(3, 256, -1) == 0
     # qg_add_rmsnorm_prepare: x, residual, gamma, eps, rows, k, h_out, y_out, ws, ws_bytes
     norm = lambda **kw: _status("qg_add_rmsnorm_prepare", V(kw.get("x", A)), None, V(kw.get("gamma", A)),
                                 C.c_float(kw.get("eps", 1e-5)), kw.get("rows", 2), kw.get("k", 2048), None,

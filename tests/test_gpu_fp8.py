@@ -115,3 +115,54 @@ def test_fp8_lm_head_sampled():
         # above 8 rows the launch takes wider tiles: the sums, and so the bits, stay those of a row alone
         for r in (0, rows - 1):
             assert torch.equal(yd[r], q.qgemv_fp8(img, n, k, xd[r:r + 1].contiguous())[0])
+
+
+@pytest.mark.parametrize("n,k", [(80, 512), (4096, 256), (65536, 128)])  # 8, 4 and 2 wave ranges of k
+def test_fp8_grouped_equals_dense_and_oracle(n, k):
+    """qgemv_fp8_grouped: each assignment has the bits of the one-row dense FP8 call on its row (items of 16, 2,
+    9, 5 and 1 assignments, an expert with 18 split over two items), a few assignments against the oracle, and
+    out-of-range entries skipped (their rows untouched) and counted."""
+    E, x_rows = 4, 20
+    codes, scales, imgs = [], [], []
+    for e in range(E):
+        c, s_ = O.quantize_fp8_weights(gauss((n, k), 0.02, 32, 10 * e + n % 7).numpy())
+        codes.append(c)
+        scales.append(s_)
+        imgs.append(torch.from_numpy(q.pack_fp8(c, s_)).cuda())
+    stacked = torch.cat(imgs)
+    x = outliers((x_rows, k), 1.0, 32, n).numpy()
+    xd = torch.from_numpy(x).cuda()
+    rng = np.random.default_rng(n)
+    expert = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate([18, 9, 5, 1])])
+    x_index = rng.integers(0, x_rows, size=expert.size).astype(np.int32)
+    perm = rng.permutation(expert.size)
+    expert, x_index = expert[perm], x_index[perm]
+    expert = np.concatenate([expert, [-1, 2]]).astype(np.int32)  # then two bad entries
+    x_index = np.concatenate([x_index, [0, x_rows]]).astype(np.int32)
+    m = expert.size
+    log(f"fp8 grouped n={n} k={k} m={m}")
+    y = torch.full((m, n), float("nan"), device="cuda")
+    _, ws = q.qgemv_fp8_grouped(stacked, E, n, k, xd, torch.from_numpy(expert).cuda(), torch.from_numpy(x_index).cuda(),
+                                y=y)
+    assert q.grouped_status(ws) == 2
+    yg = y.cpu().numpy()
+    assert np.all(np.isnan(yg[m - 2:]))
+    for j in range(m - 2):
+        dense = q.qgemv_fp8(imgs[expert[j]], n, k, xd[x_index[j]:x_index[j] + 1].contiguous())
+        assert np.array_equal(bits(y[j]), bits(dense[0])), (j, expert[j])
+    for j in (0, (m - 2) // 2, m - 3):
+        e = expert[j]
+        xr = x[x_index[j]:x_index[j] + 1]
+        yo = O.gemv_fp8(codes[e], scales[e], xr, threads=8)
+        xc, xs = O.quantize_fp8_acts(xr)
+        err = _err(yg[j:j + 1], yo, _dequant_w(codes[e], scales[e], n), _dequant_x(xc, xs))
+        assert err <= TOL, (j, err)
+
+
+def test_fp8_grouped_empty():
+    n, k = 64, 256
+    img = q.quantize_weights(q.FP8, gauss((n, k), 0.02, 33, 0, device="cuda"))
+    x = gauss((2, k), 1.0, 33, 1, device="cuda")
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    y, ws = q.qgemv_fp8_grouped(img, 1, n, k, x, empty, empty)
+    assert y.shape == (0, n) and q.grouped_status(ws) == 0
