@@ -487,6 +487,8 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
 
     out.extend(moe_sweep(torch, q, synth, L, sh, stream, timer))
     print(f"[bench] sweep moe done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    out.extend(grouped_sweep(torch, q, synth, L, sh, stream, timer))
+    print(f"[bench] sweep grouped done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     return out
 
 
@@ -560,6 +562,56 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
                   5 if rows <= 2 else 6)
         e["unique_experts"] = round(u, 2)
         out.append(e)
+    return out
+
+
+def grouped_sweep(torch, q, synth, L, sh, stream, timer):
+    """Grouped routed-expert GEMV alone at the MoE's gate/up shape (257 experts of 1024 x 2048: top-8 of 256 plus
+    a shared one per row), Q8_0 and FP8 lanes, 16 seeded routings and two weight copies in rotation; weight
+    bytes are those of the experts each call touches."""
+    import numpy as np
+
+    n, k, E, topk, nx = 2 * MOE_FFN, MOE_HIDDEN, MOE_E, MOE_TOPK, 16
+    out = []
+    for lane, fmt in (("q8_0", q.Q8_0), ("fp8", q.FP8)):
+        eb = q.image_bytes(fmt, n, k)
+        imgs = []
+        for c in range(2):
+            buf = torch.empty((E + 1) * eb, dtype=torch.uint8, device="cuda")
+            for e in range(E + 1):
+                w = synth.gaussian((n, k), 0.02, synth.tensor_seed(8, e, c), device="cuda")
+                q.quantize_weights(fmt, w, buf[e * eb:(e + 1) * eb])
+            imgs.append(buf)
+        for rows in (1, 8, 16):
+            m = rows * (topk + 1)
+            rng = np.random.default_rng(1000 + rows)
+            routes = []
+            for r_ in range(nx):
+                ex = np.concatenate([np.concatenate([rng.choice(E, topk, replace=False), [E]]) for _ in range(rows)])
+                routes.append(torch.from_numpy(ex.astype(np.int32)).cuda())
+            xi = torch.from_numpy(np.repeat(np.arange(rows), topk + 1).astype(np.int32)).cuda()
+            x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(8, 300 + rows), device="cuda")
+            y = torch.empty((m, n), device="cuda")
+            if fmt == q.FP8:
+                ws = torch.empty(q.fp8_grouped_workspace_bytes(rows, k, m), dtype=torch.uint8, device="cuda")
+                call = L.qgemv_fp8_grouped
+            else:
+                ws = torch.empty(q.grouped_workspace_bytes(rows, k, m), dtype=torch.uint8, device="cuda")
+                call = L.qgemv_q8_0_grouped
+            ip = [t.data_ptr() for t in imgs]
+            rp = [t.data_ptr() for t in routes]
+
+            def one(i, call=call, ip=ip, rp=rp, x=x, xi=xi, y=y, ws=ws, rows=rows, m=m):
+                call(ip[i % 2], E + 1, n, k, x.data_ptr(), rows, rp[i % nx], xi.data_ptr(), m, y.data_ptr(),
+                     ws.data_ptr(), ws.numel(), sh)
+
+            ms = time_calls(torch, timer, stream, one, 64)
+            u = sum(len(set(t.cpu().tolist())) for t in routes) / nx
+            e_ = entry("grouped gate/up 1024x2048, 256 experts top-8 + shared", lane, rows, u * eb, ms,
+                       3)
+            e_["unique_experts"] = round(u, 2)
+            out.append(e_)
+        del imgs
     return out
 
 
