@@ -453,6 +453,54 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
   return ok();
 }
 
+size_t qg_moe_fp8_workspace_bytes(int rows, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared) {
+  if (rows < 1 || check_moe(rows, n_experts, hidden, ffn, topk, shared) || hidden % 128 || ffn % 128) return 0;
+  return moe_layout(rows, n_experts, hidden, ffn, topk + shared, true).total;
+}
+
+int qg_moe_step_fp8(const void* router_image, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
+                    const void* gu_images, const void* down_images, const float* x, int rows, float* y, float* logits,
+                    int32_t* expert, float* weight, void* ws, size_t ws_bytes, qg_stream stream) {
+  if (int st = check_moe(rows, n_experts, hidden, ffn, topk, shared)) return st;
+  if (hidden % 128 || ffn % 128)
+    return fail(QG_ESHAPE, "hidden=%lld and ffn=%lld must be multiples of 128 (FP8 groups)", (long long)hidden,
+                (long long)ffn);
+  if (!router_image || !gu_images || !down_images || !x || !y) return fail(QG_EINVAL, "null buffer");
+  if (int st = check_image(router_image, "router_image")) return st;
+  if (int st = check_image(gu_images, "gu_images")) return st;
+  if (int st = check_image(down_images, "down_images")) return st;
+  if (int st = check_y(y)) return st;
+  if (!aligned(x, 16)) return fail(QG_EALIGN, "x %p is not 16-byte aligned", (const void*)x);
+  if (rows == 0) return ok();
+  const int slots = topk + shared, m = rows * slots;
+  const MoeLayout M = moe_layout(rows, n_experts, hidden, ffn, slots, true);
+  if (int st = check_ws(ws, ws_bytes, M.total, "the FP8 MoE step")) return st;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  float* lg = logits ? logits : (float*)(w + M.logits);
+  int32_t* ex = expert ? expert : (int32_t*)(w + M.expert);
+  float* wt = weight ? weight : (float*)(w + M.weight);
+  int32_t* xi = (int32_t*)(w + M.x_index);
+  int* header = (int*)(w + M.header);
+  int* sorted = (int*)(w + M.sorted);
+  int* items = (int*)(w + M.items);
+  float* gu = (float*)(w + M.gu);
+  float* o = (float*)(w + M.o);
+  if (int st = launch_gemv_f16(router_image, n_experts, hidden, x, rows, lg, s)) return st;
+  if (int st = launch_fp8_prepare(x, rows, hidden, w + M.xprep, s)) return st;
+  if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
+                               nullptr, hidden, nullptr, s))
+    return st;
+  if (int st = launch_grouped_fp8(gu_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi, m, gu, s))
+    return st;
+  if (int st = launch_swiglu_fp8(gu, m, ffn, w + M.hprep, s)) return st;
+  if (int st = launch_grouped_fp8(down_images, hidden, ffn, w + M.hprep, m, header, sorted, items, nullptr, m, o, s))
+    return st;
+  if (int st = launch_moe_combine(o, wt, rows, slots, hidden, y, s)) return st;
+  return ok();
+}
+
 int qg_quantize_rows_q8(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, qg_stream stream) {
   if (int st = check_x(x, rows, k, QG_MAX_PREP_ROWS)) return st;
   if (!qx || !dx || !sx) return fail(QG_EINVAL, "null output");

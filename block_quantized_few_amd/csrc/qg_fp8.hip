@@ -115,6 +115,18 @@ int launch_fp8_quantize_weights(const float* w, int64_t n, int64_t k, void* imag
 }
 
 // ---------------------------------------------------- activation groups ---
+// One 1 x 128 group by one wave, columns 2*lane and 2*lane + 1 in v: scale
+// amax / 448 to *scale, codes e4m3(v / scale) to codes[0..127].
+__device__ __forceinline__ void fp8_group_store(float2 v, int lane, uint8_t* __restrict__ codes,
+                                                float* __restrict__ scale) {
+  float am = fmaxf(fabsf(v.x), fabsf(v.y));
+  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  const float s = am / 448.0f;
+  const uint32_t c0 = s != 0.0f ? e4m3_code(v.x / s) : 0u, c1 = s != 0.0f ? e4m3_code(v.y / s) : 0u;
+  reinterpret_cast<uint16_t*>(codes)[lane] = (uint16_t)(c0 | (c1 << 8));
+  if (lane == 0) *scale = s;
+}
+
 // One wave per (row, group): two columns per lane.  Codes [rows][k] then fp32
 // scales [rows][k/128] (the FP8 workspace).
 __global__ __launch_bounds__(256) void fp8_prepare_kernel(const float* __restrict__ x, int rows, int64_t k, int64_t kg,
@@ -124,12 +136,30 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(const float* __restric
   if (wi >= (int64_t)rows * kg) return;  // whole waves
   const int64_t r = wi / kg, g = wi - r * kg;
   const float2 v = reinterpret_cast<const float2*>(x + r * k + g * F8_GROUP)[lane];
-  float am = fmaxf(fabsf(v.x), fabsf(v.y));
-  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-  const float s = am / 448.0f;
-  const uint32_t c0 = s != 0.0f ? e4m3_code(v.x / s) : 0u, c1 = s != 0.0f ? e4m3_code(v.y / s) : 0u;
-  reinterpret_cast<uint16_t*>(codes + r * k + g * F8_GROUP)[lane] = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) scales[wi] = s;
+  fp8_group_store(v, lane, codes + r * k + g * F8_GROUP, scales + wi);
+}
+
+// SwiGLU of m gate/up rows (gate values [0, ffn), up values [ffn, 2 ffn)),
+// h = silu(g) * u in the arithmetic of swiglu_kernel, into FP8 groups as
+// fp8_prepare_kernel writes them (the FP8 workspace of m rows of ffn).
+__global__ __launch_bounds__(256) void swiglu_fp8_kernel(const float* __restrict__ gu, int m, int64_t ffn, int64_t kg,
+                                                         uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int64_t wi = (int64_t)blockIdx.x * (256 / WAVE) + (threadIdx.x / WAVE);
+  const int lane = threadIdx.x % WAVE;
+  if (wi >= (int64_t)m * kg) return;  // whole waves
+  const int64_t j = wi / kg, g = wi - j * kg;
+  const float* row = gu + j * 2 * ffn + g * F8_GROUP + 2 * lane;
+  const float2 gv = *reinterpret_cast<const float2*>(row), uv = *reinterpret_cast<const float2*>(row + ffn);
+  const float2 h = make_float2(gv.x / (1.0f + expf(-gv.x)) * uv.x, gv.y / (1.0f + expf(-gv.y)) * uv.y);
+  fp8_group_store(h, lane, codes + j * ffn + g * F8_GROUP, scales + wi);
+}
+
+int launch_swiglu_fp8(const float* gu, int m, int64_t ffn, void* hws, hipStream_t s) {
+  const int64_t kg = ffn / F8_GROUP, waves = (int64_t)m * kg;
+  uint8_t* w = static_cast<uint8_t*>(hws);
+  hipLaunchKernelGGL(swiglu_fp8_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, gu, m, ffn, kg, w,
+                     reinterpret_cast<float*>(w + fp8_ws_scale_offset(m, ffn)));
+  return hip_status(hipGetLastError(), "swiglu_fp8_kernel");
 }
 
 int launch_fp8_prepare(const float* x, int rows, int64_t k, void* ws, hipStream_t s) {

@@ -80,6 +80,8 @@ int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int 
                     float* weight, int32_t* x_index, int* header, int* sorted, int* items, const float* x, int64_t k,
                     void* xprep, hipStream_t s);
 int launch_swiglu_q8(const float* gu, int m, int64_t ffn, void* hprep, hipStream_t s);
+// SwiGLU of m gate/up rows into the FP8 workspace of m rows of ffn (ffn % 128 == 0).
+int launch_swiglu_fp8(const float* gu, int m, int64_t ffn, void* hws, hipStream_t s);
 
 // f16 lane.
 int launch_gemv_f16(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s);

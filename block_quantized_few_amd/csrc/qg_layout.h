@@ -160,7 +160,9 @@ constexpr int QG_MOE_MAX_M = 16 * 33;
 struct MoeLayout {
   size_t header, expert, weight, x_index, sorted, items, logits, xprep, gu, hprep, o, total;
 };
-QG_HD MoeLayout moe_layout(int64_t rows, int64_t n_experts, int64_t hidden, int64_t ffn, int64_t slots) {
+// fp8: the input rows and h in FP8 groups (fp8_ws_bytes) instead of q8 rows.
+QG_HD MoeLayout moe_layout(int64_t rows, int64_t n_experts, int64_t hidden, int64_t ffn, int64_t slots,
+                           bool fp8 = false) {
   const int64_t m = rows * slots;
   MoeLayout M;
   M.header = 0;
@@ -171,9 +173,9 @@ QG_HD MoeLayout moe_layout(int64_t rows, int64_t n_experts, int64_t hidden, int6
   M.items = M.sorted + align256((size_t)m * 4);
   M.logits = M.items + align256((size_t)m * 12);
   M.xprep = M.logits + align256((size_t)rows * n_experts * 4);
-  M.gu = M.xprep + prep_layout_rows(rows, hidden).total;
+  M.gu = M.xprep + (fp8 ? fp8_ws_bytes(rows, hidden) : prep_layout_rows(rows, hidden).total);
   M.hprep = M.gu + align256((size_t)m * 2 * ffn * 4);
-  M.o = M.hprep + prep_layout_rows(m, ffn).total;
+  M.o = M.hprep + (fp8 ? fp8_ws_bytes(m, ffn) : prep_layout_rows(m, ffn).total);
   M.total = M.o + align256((size_t)m * hidden * 4);
   return M;
 }

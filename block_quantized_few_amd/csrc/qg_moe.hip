@@ -323,12 +323,21 @@ int launch_moe_route(const float* logits, int rows, int n_experts, int topk, int
 int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
                     float* weight, int32_t* x_index, int* header, int* sorted, int* items, const float* x, int64_t k,
                     void* xprep, hipStream_t s) {
-  const PrepLayout L = prep_layout_rows(rows, k);
-  uint8_t* w = (uint8_t*)xprep;
-  const int64_t quads = (int64_t)rows * kbp_of(k) * 4;  // input-row quantization: workgroups 1..
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1 + (unsigned)((quads + 1023) / 1024)), dim3(1024), 0, s, logits, rows, n_experts, topk, shared_expert, expert,
-                     weight, x_index, header, sorted, items, x, k, (int8_t*)(w + L.codes), (float*)(w + L.dx),
-                     (int*)(w + L.nsx));
+  // x null: routing and the plan only (one workgroup); else the input rows'
+  // A1 on workgroups 1..
+  const int64_t quads = x ? (int64_t)rows * kbp_of(k) * 4 : 0;
+  int8_t* xq = nullptr;
+  float* xd = nullptr;
+  int* xn = nullptr;
+  if (x) {
+    const PrepLayout L = prep_layout_rows(rows, k);
+    uint8_t* w = (uint8_t*)xprep;
+    xq = (int8_t*)(w + L.codes);
+    xd = (float*)(w + L.dx);
+    xn = (int*)(w + L.nsx);
+  }
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1 + (unsigned)((quads + 1023) / 1024)), dim3(1024), 0, s, logits, rows,
+                     n_experts, topk, shared_expert, expert, weight, x_index, header, sorted, items, x, k, xq, xd, xn);
   return hip_status(hipGetLastError(), "moe_plan_kernel");
 }
 

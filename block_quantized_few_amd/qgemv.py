@@ -88,6 +88,10 @@ _SIGS = {
     "qg_moe_step": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_size_t, C.c_void_p]),
+    "qg_moe_fp8_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_int]),
+    "qg_moe_step_fp8": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_size_t, C.c_void_p]),
     "qg_quantize_rows_q8": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_void_p]),
     "qgemv_blockdots": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
@@ -422,6 +426,45 @@ def moe_combine(o, weight, rows, slots, y=None):
 
 def moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared):
     return lib().qg_moe_workspace_bytes(rows, n_experts, hidden, ffn, topk, int(shared))
+
+
+def moe_fp8_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared):
+    return lib().qg_moe_fp8_workspace_bytes(rows, n_experts, hidden, ffn, topk, int(shared))
+
+
+def moe_step_fp8_fused(x, router_image, n_experts, topk, gu_images, down_images, ffn, shared=True, ws=None):
+    """The routed MoE step in the FP8 lane in one library call (qg_moe_step_fp8).  Returns y, the routing
+    (expert, weight) as [rows * slots] tensors, and the router logits."""
+    _dev(x, torch.float32, "x")
+    rows, hidden = x.shape
+    slots = topk + (1 if shared else 0)
+    dev = x.device
+    y = torch.empty((rows, hidden), dtype=torch.float32, device=dev)
+    logits = torch.empty((rows, n_experts), dtype=torch.float32, device=dev)
+    expert = torch.empty(rows * slots, dtype=torch.int32, device=dev)
+    weight = torch.empty(rows * slots, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(1, moe_fp8_workspace_bytes(rows, n_experts, hidden, ffn, topk, shared)),
+                         dtype=torch.uint8, device=dev)
+    _check(lib().qg_moe_step_fp8(_p(router_image), n_experts, hidden, ffn, topk, int(shared), _p(gu_images),
+                                 _p(down_images), _p(x), rows, _p(y), _p(logits), _p(expert), _p(weight), _p(ws),
+                                 ws.numel(), _stream()))
+    return y, (expert, weight), logits
+
+
+def moe_step_fp8(x, router_image, n_experts, topk, gu_images, down_images, ffn, shared_expert=None):
+    """The routed MoE step in the FP8 lane composed of library calls only (see moe_step)."""
+    rows, hidden = x.shape
+    n_images = n_experts + (1 if shared_expert is not None else 0)
+    logits = gemv_f16(router_image, n_experts, hidden, x)
+    expert, x_index, weight = moe_route(logits, topk, -1 if shared_expert is None else shared_expert)
+    m = expert.numel()
+    gu, _ = qgemv_fp8_grouped(gu_images, n_images, 2 * ffn, hidden, x, expert, x_index)
+    h = swiglu(gu, ffn)
+    ident = torch.arange(m, dtype=torch.int32, device=x.device)
+    o, _ = qgemv_fp8_grouped(down_images, n_images, hidden, ffn, h, expert, ident)
+    y = moe_combine(o, weight, rows, m // rows)
+    return y, (expert, x_index, weight), logits
 
 
 def moe_step_fused(x, router_image, n_experts, topk, gu_images, down_images, ffn, shared=True, ws=None):

@@ -338,6 +338,21 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
                 const void* gu_images, const void* down_images, const float* x, int rows, float* y, float* logits,
                 int32_t* expert, float* weight, void* ws, size_t ws_bytes, qg_stream stream);
 
+/* The routed-MoE step in the FP8 lane (the drama page's backbone: a 256-expert
+ * top-8 block-FP8 MoE with a shared expert, activations in dynamic 1 x 128
+ * FP8 groups): as qg_moe_step, with gu_images and down_images FP8 images
+ * (qg_image_bytes(QG_FMT_FP8, ...) each, back to back), the input rows and
+ * the SwiGLU rows quantized into FP8 groups, and the expert GEMVs those of
+ * qgemv_fp8_grouped.  hidden and ffn multiples of 128.  Seven launches.  The
+ * bits are those of the composition: the f16 router GEMV, qg_moe_route,
+ * qgemv_fp8_grouped on the gate/up images, qg_swiglu, qgemv_fp8_grouped on
+ * the down images (assignment j reading SwiGLU row j), qg_moe_combine.
+ * ws: qg_moe_fp8_workspace_bytes bytes. */
+size_t qg_moe_fp8_workspace_bytes(int rows, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared);
+int qg_moe_step_fp8(const void* router_image, int n_experts, int64_t hidden, int64_t ffn, int topk, int shared,
+                    const void* gu_images, const void* down_images, const float* x, int rows, float* y,
+                    float* logits, int32_t* expert, float* weight, void* ws, size_t ws_bytes, qg_stream stream);
+
 /* ------------------------------------------------------ test-only hooks --- */
 
 /* A1 in the plain layout: qx [rows][k] int8, dx [rows][k/32] fp32, sx

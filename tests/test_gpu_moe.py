@@ -99,3 +99,84 @@ def test_fused_moe_step_equals_composition(moe, rows):
     if rows > 1:
         yf1, _, _ = q.moe_step_fused(x[:1].contiguous(), moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN)
         assert torch.equal(yf1[0], yf[0])
+
+
+# ------------------------------------------------------------- FP8 lane ---
+# The routed step with block-FP8 experts and 1 x 128 FP8 activation groups (qg_moe_step_fp8), on a smaller
+# expert set: 64 experts of 256-wide FFNs over hidden 1024, top-8 and a shared expert.
+H8, F8, E8 = 1024, 256, 64
+WL8 = 34
+
+
+@pytest.fixture(scope="module")
+def moe8():
+    log("building FP8 MoE weights")
+    router = gauss((E8, H8), 0.02, WL8, 0, device="cuda")
+    r16 = router.half().view(torch.int16)
+    gu_q, dn_q, gu_imgs, dn_imgs = [], [], [], []
+    for e in range(E8 + 1):  # index E8 is the shared expert
+        g = gauss((F8, H8), 0.02, WL8, 1 + 3 * e).numpy()
+        u = gauss((F8, H8), 0.02, WL8, 2 + 3 * e).numpy()
+        d = gauss((H8, F8), 0.02, WL8, 3 + 3 * e).numpy()
+        # gate rows, then up rows: F8 is a multiple of 128, so the stacked matrix's 128 x 128 blocks are those of
+        # gate and of up
+        (gc, gs), (uc, us), (dc, ds) = (O.quantize_fp8_weights(a) for a in (g, u, d))
+        gu_q.append((np.concatenate([gc, uc]), np.concatenate([gs, us])))
+        dn_q.append((dc, ds))
+        gu_imgs.append(q.pack_fp8(*gu_q[-1]))
+        dn_imgs.append(q.pack_fp8(dc, ds))
+    return dict(r16=q.f16_image(r16), r16_np=r16.cpu().numpy().view(np.uint16), gu_q=gu_q, dn_q=dn_q,
+                gu=torch.from_numpy(np.concatenate(gu_imgs)).cuda(), dn=torch.from_numpy(np.concatenate(dn_imgs)).cuda())
+
+
+@pytest.mark.parametrize("rows", [1, 5, 16])
+def test_fp8_moe_step_equals_composition(moe8, rows):
+    """qg_moe_step_fp8 gives the bits of the composition of the separate calls (f16 router GEMV, routing,
+    FP8 grouped gate/up, SwiGLU, FP8 grouped down, combine), call after call through one workspace."""
+    log(f"fp8 moe rows={rows}")
+    x = torch.from_numpy(gauss((rows, H8), 1.0, WL8, 32 + rows).numpy()).cuda()
+    y, (expert, _, weight), logits = q.moe_step_fp8(x, moe8["r16"], E8, TOPK, moe8["gu"], moe8["dn"], F8,
+                                                    shared_expert=E8)
+    ws = torch.full((q.moe_fp8_workspace_bytes(rows, E8, H8, F8, TOPK, True),), 0xA5, dtype=torch.uint8,
+                    device="cuda")
+    for _ in range(2):
+        yf, (expert_f, weight_f), logits_f = q.moe_step_fp8_fused(x, moe8["r16"], E8, TOPK, moe8["gu"], moe8["dn"],
+                                                                  F8, ws=ws)
+        assert torch.equal(logits_f, logits) and torch.equal(expert_f, expert) and torch.equal(weight_f, weight)
+        assert torch.equal(yf, y)
+
+
+def _fp8_gemv_deq(codes, scales, n):
+    return O.e4m3_decode(codes) * np.repeat(np.repeat(scales.astype(np.float64), 128, 0)[:n], 128, 1)
+
+
+@pytest.mark.parametrize("rows", [1, 8])
+def test_fp8_moe_step_matches_oracle(moe8, rows):
+    """Against the oracle's pieces (parity unpinned as a whole, like the q8 step: the composition is this
+    build's reading): router logits and routing, FP8 gate/up GEMVs, SwiGLU in double, its rows quantized into
+    FP8 groups, FP8 down GEMVs, the weighted sum; within 2e-3 of sum over slots of p * sum|w_down||h|."""
+    x = gauss((rows, H8), 1.0, WL8, 48 + rows).numpy()
+    y, _, _ = q.moe_step_fp8_fused(torch.from_numpy(x).cuda(), moe8["r16"], E8, TOPK, moe8["gu"], moe8["dn"], F8)
+    yg = y.cpu().numpy().astype(np.float64)
+    logits_o = O.gemv_f16(moe8["r16_np"], x)
+    ex_o, p_o = O.route_topk(logits_o, TOPK)
+    for r in range(rows):
+        srt = np.sort(logits_o[r].astype(np.float64))[::-1]
+        if srt[TOPK - 1] - srt[TOPK] < 1e-4:
+            log(f"  row {r}: near-tie in routing, output not compared")
+            continue
+        yo = np.zeros(H8)
+        denom = np.zeros(H8)
+        for s, e in enumerate(list(ex_o[r]) + [E8]):
+            p = p_o[r, s] if e < E8 else 1.0
+            gc, gs = moe8["gu_q"][e]
+            gu = O.gemv_fp8(gc, gs, x[r:r + 1])[0]
+            h = O.swiglu(gu[:F8][None], gu[F8:][None]).astype(np.float32)
+            hc, hs = O.quantize_fp8_acts(h)
+            dc, ds = moe8["dn_q"][e]
+            yo += p * O.gemv_fp8(dc, ds, h)[0]
+            hd = O.e4m3_decode(hc) * np.repeat(hs.astype(np.float64), 128, 1)
+            denom += p * (np.abs(hd) @ np.abs(_fp8_gemv_deq(dc, ds, H8)).T)[0]
+        err = np.abs(yg[r] - yo) / denom
+        log(f"  row {r}: max rel err {err.max():.3e}")
+        assert err.max() <= TOL
