@@ -495,26 +495,27 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
 MOE_HIDDEN, MOE_FFN, MOE_E, MOE_TOPK = 2048, 512, 256, 8
 
 
-def moe_weights(torch, q, synth, copies=2):
-    """Two copies of the routed MoE's 256 Q8_0 experts plus the shared one (index 256), stacked, and the f16
-    router image."""
+def moe_weights(torch, q, synth, copies=2, fmt=None):
+    """Two copies of the routed MoE's 256 experts (Q8_0, or fmt) plus the shared one (index 256), stacked, and
+    the f16 router image."""
     hidden, ffn, E = MOE_HIDDEN, MOE_FFN, MOE_E
+    fmt = q.Q8_0 if fmt is None else fmt
     nimg = E + 1
-    gu_b = q.image_bytes(q.Q8_0, 2 * ffn, hidden)
-    dn_b = q.image_bytes(q.Q8_0, hidden, ffn)
+    gu_b = q.image_bytes(fmt, 2 * ffn, hidden)
+    dn_b = q.image_bytes(fmt, hidden, ffn)
     gus, dns = [], []
     for c in range(copies):
         gu = torch.empty(nimg * gu_b, dtype=torch.uint8, device="cuda")
         dn = torch.empty(nimg * dn_b, dtype=torch.uint8, device="cuda")
         for e in range(nimg):
             w = synth.gaussian((2 * ffn, hidden), 0.02, synth.tensor_seed(3, 1 + 3 * e, c), device="cuda")
-            q.quantize_weights(q.Q8_0, w, gu[e * gu_b:(e + 1) * gu_b])
+            q.quantize_weights(fmt, w, gu[e * gu_b:(e + 1) * gu_b])
             w = synth.gaussian((hidden, ffn), 0.02, synth.tensor_seed(3, 3 + 3 * e, c), device="cuda")
-            q.quantize_weights(q.Q8_0, w, dn[e * dn_b:(e + 1) * dn_b])
+            q.quantize_weights(fmt, w, dn[e * dn_b:(e + 1) * dn_b])
         gus.append(gu)
         dns.append(dn)
     router = q.f16_image(synth.gaussian((E, hidden), 0.02, synth.tensor_seed(3, 0), device="cuda").half())
-    return {"router": router, "gu": gus, "dn": dns, "gu_b": gu_b, "dn_b": dn_b}
+    return {"router": router, "gu": gus, "dn": dns, "gu_b": gu_b, "dn_b": dn_b, "fmt": fmt}
 
 
 def moe_call(torch, q, synth, L, sh, W, rows, nx=64):
@@ -526,15 +527,18 @@ def moe_call(torch, q, synth, L, sh, W, rows, nx=64):
     expert = torch.empty(m, dtype=torch.int32, device="cuda")
     wgt = torch.empty(m, device="cuda")
     y = torch.empty((rows, hidden), device="cuda")
-    ws = torch.empty(q.moe_workspace_bytes(rows, E, hidden, ffn, topk, True), dtype=torch.uint8, device="cuda")
+    fp8 = W["fmt"] == q.FP8
+    wsb = (q.moe_fp8_workspace_bytes if fp8 else q.moe_workspace_bytes)(rows, E, hidden, ffn, topk, True)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     P = lambda t: t.data_ptr()
     xps = [P(x) for x in xs]
     copies = len(W["gu"])
+    step = L.qg_moe_step_fp8 if fp8 else L.qg_moe_step
 
     def one(i):
         c = i % copies
-        L.qg_moe_step(P(W["router"]), E, hidden, ffn, topk, 1, P(W["gu"][c]), P(W["dn"][c]), xps[i % nx], rows, P(y),
-                      P(logits), P(expert), P(wgt), P(ws), ws.numel(), sh)
+        step(P(W["router"]), E, hidden, ffn, topk, 1, P(W["gu"][c]), P(W["dn"][c]), xps[i % nx], rows, P(y),
+             P(logits), P(expert), P(wgt), P(ws), ws.numel(), sh)
 
     # keep the inputs alive with the closure's owner
     one.keep = (xs, logits, expert, wgt, y, ws)
@@ -544,24 +548,26 @@ def moe_call(torch, q, synth, L, sh, W, rows, nx=64):
 def moe_sweep(torch, q, synth, L, sh, stream, timer):
     """Routed MoE step (qg_moe_step): router f16 GEMV, top-8 routing + plan, grouped gate/up, SwiGLU + q8,
     grouped down, combine -- six launches, five at 1-2 rows (SwiGLU + q8 inside the down launch)."""
-    W = moe_weights(torch, q, synth)
     out = []
-    for rows in (1, 8, 9, 16):
-        nx = 64
-        one, expert = moe_call(torch, q, synth, L, sh, W, rows, nx)
-        ms = time_calls(torch, timer, stream, one, 128)
-        # weight bytes actually streamed: router + every touched expert (the shared one included)
-        uniq = []
-        for s in range(nx):
-            one(s)
-            torch.cuda.synchronize()
-            uniq.append(len(set(expert.cpu().tolist())))
-        u = sum(uniq) / nx
-        wb = 2 * MOE_E * MOE_HIDDEN + u * (W["gu_b"] + W["dn_b"])
-        e = entry("routed moe step (256 experts top-8 + shared)", "q8_0 + f16 router", rows, wb, ms,
-                  5 if rows <= 2 else 6)
-        e["unique_experts"] = round(u, 2)
-        out.append(e)
+    for fmt, lane in ((q.Q8_0, "q8_0 + f16 router"), (q.FP8, "fp8 + f16 router")):
+        W = moe_weights(torch, q, synth, fmt=fmt)
+        for rows in (1, 8, 9, 16):
+            nx = 64
+            one, expert = moe_call(torch, q, synth, L, sh, W, rows, nx)
+            ms = time_calls(torch, timer, stream, one, 128)
+            # weight bytes actually streamed: router + every touched expert (the shared one included)
+            uniq = []
+            for s in range(nx):
+                one(s)
+                torch.cuda.synchronize()
+                uniq.append(len(set(expert.cpu().tolist())))
+            u = sum(uniq) / nx
+            wb = 2 * MOE_E * MOE_HIDDEN + u * (W["gu_b"] + W["dn_b"])
+            launches = 6 if fmt == q.FP8 else (5 if rows <= 2 else 6)
+            e = entry("routed moe step (256 experts top-8 + shared)", lane, rows, wb, ms, launches)
+            e["unique_experts"] = round(u, 2)
+            out.append(e)
+        del W
     return out
 
 

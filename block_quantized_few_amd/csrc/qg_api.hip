@@ -435,7 +435,7 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
   const int n_images = n_experts + shared;
   if (int st = launch_gemv_f16(router_image, n_experts, hidden, x, rows, lg, s)) return st;
   if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
-                               x, hidden, w + M.xprep, s))
+                               x, hidden, w + M.xprep, false, s))
     return st;
   // an expert meets a row at most once (distinct top-k picks, a separate shared image): items have <= rows rows
   if (int st = launch_grouped_planned(gu_images, n_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi,
@@ -488,9 +488,8 @@ int qg_moe_step_fp8(const void* router_image, int n_experts, int64_t hidden, int
   float* gu = (float*)(w + M.gu);
   float* o = (float*)(w + M.o);
   if (int st = launch_gemv_f16(router_image, n_experts, hidden, x, rows, lg, s)) return st;
-  if (int st = launch_fp8_prepare(x, rows, hidden, w + M.xprep, s)) return st;
   if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
-                               nullptr, hidden, nullptr, s))
+                               x, hidden, w + M.xprep, true, s))
     return st;
   if (int st = launch_grouped_fp8(gu_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi, m, gu, s))
     return st;

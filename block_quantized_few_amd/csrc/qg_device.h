@@ -99,6 +99,38 @@ __device__ __forceinline__ void quantize_quarter(const float (&v)[8], unsigned& 
   block_sum = s;
 }
 
+// E4M3 code of f: round to nearest even on the fp32 mantissa, magnitudes from
+// 448 up saturate to 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fabsf(f);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // subnormal: multiples of 2^-9 (8: min normal)
+  const uint32_t ab = __float_as_uint(a);
+  int e = (int)(ab >> 23) - 127;
+  uint32_t keep = (ab >> 20) & 7u;
+  const uint32_t rest = ab & 0xFFFFFu;
+  keep += (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ? 1u : 0u;
+  if (keep == 8u) {
+    keep = 0u;
+    e += 1;
+  }
+  if (e > 8 || (e == 8 && keep > 6u)) return sign | 0x7Eu;
+  return sign | ((uint32_t)(e + 7) << 3) | keep;
+}
+
+// One 1 x 128 group by one wave, columns 2*lane and 2*lane + 1 in v: scale
+// amax / 448 to *scale, codes e4m3(v / scale) to codes[0..127].
+__device__ __forceinline__ void fp8_group_store(float2 v, int lane, uint8_t* __restrict__ codes,
+                                                float* __restrict__ scale) {
+  float am = fmaxf(fabsf(v.x), fabsf(v.y));
+  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  const float s = am / 448.0f;
+  const uint32_t c0 = s != 0.0f ? e4m3_code(v.x / s) : 0u, c1 = s != 0.0f ? e4m3_code(v.y / s) : 0u;
+  reinterpret_cast<uint16_t*>(codes)[lane] = (uint16_t)(c0 | (c1 << 8));
+  if (lane == 0) *scale = s;
+}
+
 // Work items of a grouped GEMV of at most this many rows run in the
 // small-item kernel (few registers, many workgroups per CU); larger ones in
 // the kernel built for up to 16 rows.

@@ -36,26 +36,6 @@ constexpr int F8_HALF_U4 = 64;       // second 16 bytes of a lane: 1 KB on, in u
 constexpr int F8_E8M0_ONE = 127;     // MFMA operand scale 2^0
 constexpr int64_t F8_ROT = 7;        // start-group stride between neighbouring tile groups
 
-// E4M3 code of f: round to nearest even on the fp32 mantissa, magnitudes from
-// 448 up saturate to 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_code(float f) {
-  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
-  const float a = fabsf(f);
-  if (!(a < 448.0f)) return sign | 0x7Eu;
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // subnormal: multiples of 2^-9 (8: min normal)
-  const uint32_t ab = __float_as_uint(a);
-  int e = (int)(ab >> 23) - 127;
-  uint32_t keep = (ab >> 20) & 7u;
-  const uint32_t rest = ab & 0xFFFFFu;
-  keep += (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ? 1u : 0u;
-  if (keep == 8u) {
-    keep = 0u;
-    e += 1;
-  }
-  if (e > 8 || (e == 8 && keep > 6u)) return sign | 0x7Eu;
-  return sign | ((uint32_t)(e + 7) << 3) | keep;
-}
-
 // ------------------------------------------------------- weight image ---
 // One workgroup per (128-row block, group): thread t takes row t / 2, half t % 2
 // of the group (64 columns).
@@ -115,18 +95,6 @@ int launch_fp8_quantize_weights(const float* w, int64_t n, int64_t k, void* imag
 }
 
 // ---------------------------------------------------- activation groups ---
-// One 1 x 128 group by one wave, columns 2*lane and 2*lane + 1 in v: scale
-// amax / 448 to *scale, codes e4m3(v / scale) to codes[0..127].
-__device__ __forceinline__ void fp8_group_store(float2 v, int lane, uint8_t* __restrict__ codes,
-                                                float* __restrict__ scale) {
-  float am = fmaxf(fabsf(v.x), fabsf(v.y));
-  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-  const float s = am / 448.0f;
-  const uint32_t c0 = s != 0.0f ? e4m3_code(v.x / s) : 0u, c1 = s != 0.0f ? e4m3_code(v.y / s) : 0u;
-  reinterpret_cast<uint16_t*>(codes)[lane] = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) *scale = s;
-}
-
 // One wave per (row, group): two columns per lane.  Codes [rows][k] then fp32
 // scales [rows][k/128] (the FP8 workspace).
 __global__ __launch_bounds__(256) void fp8_prepare_kernel(const float* __restrict__ x, int rows, int64_t k, int64_t kg,
@@ -307,19 +275,36 @@ static void launch_fp8_t(const uint8_t* img, const float* wsc, int64_t n, int64_
                      rows, y, groups);
 }
 
+// Wave ranges of k (S) for an n x k FP8 GEMV: 2 on large n, 4 on mid-size, 8
+// on small, never more than k has 128-column groups.  The dense and grouped
+// launches take S from here, so a row's sums depend on n and k only.
+static int fp8_waves(int64_t t16, int64_t kg) {
+  int S = t16 >= 4096 ? 2 : t16 >= 256 ? 4 : 8;
+  while (S > 1 && S > kg) S >>= 1;
+  return S;
+}
+
 int launch_gemv_fp8(const void* image, int64_t n, int64_t k, const void* ws, int rows, float* y, hipStream_t s) {
   const uint8_t* img = static_cast<const uint8_t*>(image);
   const float* wsc = reinterpret_cast<const float*>(img + fp8_scale_offset(n, k));
   const uint8_t* xc = static_cast<const uint8_t*>(ws);
   const float* xs = reinterpret_cast<const float*>(xc + fp8_ws_scale_offset(rows, k));
   const int64_t t16 = f16_tiles(n);
-  // For each n the same S (so the same sums) at every row count; above 8 rows
-  // wider tiles share each activation load where there are tiles enough.
-  if (t16 >= 4096 && rows > 8) launch_fp8_t<4, 2, 2>(img, wsc, n, k, xc, xs, rows, y, s);
-  else if (t16 >= 4096) launch_fp8_t<2, 2, 2>(img, wsc, n, k, xc, xs, rows, y, s);
-  else if (t16 >= 512 && rows > 8) launch_fp8_t<2, 4, 2>(img, wsc, n, k, xc, xs, rows, y, s);
-  else if (t16 >= 256) launch_fp8_t<1, 4, 4>(img, wsc, n, k, xc, xs, rows, y, s);
-  else launch_fp8_t<1, 8, 4>(img, wsc, n, k, xc, xs, rows, y, s);
+  // For each n and k the same S (so the same sums) at every row count; above
+  // 8 rows wider tiles share each activation load where there are tiles enough.
+  switch (fp8_waves(t16, k / F8_GROUP)) {
+    case 8: launch_fp8_t<1, 8, 4>(img, wsc, n, k, xc, xs, rows, y, s); break;
+    case 4:
+      if (t16 >= 512 && rows > 8) launch_fp8_t<2, 4, 2>(img, wsc, n, k, xc, xs, rows, y, s);
+      else launch_fp8_t<1, 4, 4>(img, wsc, n, k, xc, xs, rows, y, s);
+      break;
+    case 2:
+      if (t16 >= 4096 && rows > 8) launch_fp8_t<4, 2, 2>(img, wsc, n, k, xc, xs, rows, y, s);
+      else if (t16 >= 4096) launch_fp8_t<2, 2, 2>(img, wsc, n, k, xc, xs, rows, y, s);
+      else launch_fp8_t<1, 2, 4>(img, wsc, n, k, xc, xs, rows, y, s);
+      break;
+    default: launch_fp8_t<2, 1, 2>(img, wsc, n, k, xc, xs, rows, y, s); break;
+  }
   return hip_status(hipGetLastError(), "gemv_fp8_kernel");
 }
 
@@ -435,13 +420,19 @@ int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws,
   const int64_t eb = (int64_t)fp8_image_bytes(n, k), so = (int64_t)fp8_scale_offset(n, k);
   const uint8_t* xc = static_cast<const uint8_t*>(ws);
   const float* xs = reinterpret_cast<const float*>(xc + fp8_ws_scale_offset(x_rows, k));
-  // S as launch_gemv_fp8 sets it for this n (the bits of the dense call); two
-  // tiles per unit on small experts, whose units are otherwise too short for
-  // their fixed costs (1024 x 2048 experts at 16 rows: 63.0 -> 51.8 us)
+  // S as launch_gemv_fp8 sets it for this n and k (the bits of the dense call);
+  // two tiles per unit on small experts, whose units are otherwise too short
+  // for their fixed costs (1024 x 2048 experts at 16 rows: 63.0 -> 51.8 us)
   const int64_t t16 = f16_tiles(n);
-  if (t16 >= 4096) launch_grouped_fp8_t<2, 2, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
-  else if (t16 >= 256) launch_grouped_fp8_t<1, 4, 4>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
-  else launch_grouped_fp8_t<2, 8, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
+  switch (fp8_waves(t16, k / F8_GROUP)) {
+    case 8: launch_grouped_fp8_t<2, 8, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s); break;
+    case 4:
+      if (t16 >= 256) launch_grouped_fp8_t<1, 4, 4>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
+      else launch_grouped_fp8_t<2, 4, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
+      break;
+    case 2: launch_grouped_fp8_t<2, 2, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s); break;
+    default: launch_grouped_fp8_t<2, 1, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s); break;
+  }
   return hip_status(hipGetLastError(), "grouped_fp8_kernel");
 }
 

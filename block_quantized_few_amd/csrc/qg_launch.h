@@ -76,9 +76,11 @@ bool grouped_glu_fits(int64_t k);
 
 // Fused MoE pieces: routing + plan + input quantization (one workgroup), and
 // SwiGLU quantized for the down projection.
+// x null: the plan only; fp8: x's FP8 groups into the FP8 workspace xprep
+// instead of q8 rows.
 int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
                     float* weight, int32_t* x_index, int* header, int* sorted, int* items, const float* x, int64_t k,
-                    void* xprep, hipStream_t s);
+                    void* xprep, bool fp8, hipStream_t s);
 int launch_swiglu_q8(const float* gu, int m, int64_t ffn, void* hprep, hipStream_t s);
 // SwiGLU of m gate/up rows into the FP8 workspace of m rows of ffn (ffn % 128 == 0).
 int launch_swiglu_fp8(const float* gu, int m, int64_t ffn, void* hws, hipStream_t s);

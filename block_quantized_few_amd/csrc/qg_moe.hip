@@ -153,7 +153,8 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
                                                         int* __restrict__ header,
                                                         int* __restrict__ sorted, int* __restrict__ items,
                                                         const float* __restrict__ x, int64_t k, int8_t* __restrict__ xq,
-                                                        float* __restrict__ xd, int* __restrict__ xn) {
+                                                        float* __restrict__ xd, int* __restrict__ xn,
+                                                        uint8_t* __restrict__ fcodes, float* __restrict__ fscales) {
   __shared__ int s_e[QG_MOE_MAX_M];
   __shared__ int s_pos[QG_MOE_MAX_M];
   __shared__ float s_w[QG_MOE_MAX_M];
@@ -163,6 +164,15 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
   __shared__ int s_wsum[1024 / WAVE];
   __shared__ int s_cnt[2];
   const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
+  if (blockIdx.x > 0 && fcodes) {
+    // workgroups 1..: the input rows' 1 x 128 FP8 groups, a wave per (row, group)
+    const int64_t kg = k / 128, e = (int64_t)(blockIdx.x - 1) * (nt / WAVE) + wave;
+    if (e >= (int64_t)rows * kg) return;  // whole waves
+    const int64_t r = e / kg, g = e - r * kg;
+    const float2 v = reinterpret_cast<const float2*>(x + r * k + g * 128)[lane];
+    fp8_group_store(v, lane, fcodes + r * k + g * 128, fscales + e);
+    return;
+  }
   if (blockIdx.x > 0) {
     // workgroups 1..: A1 of the input rows, row order, four lanes per 32-block
     const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
@@ -322,14 +332,19 @@ int launch_moe_route(const float* logits, int rows, int n_experts, int topk, int
 
 int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int shared_expert, int32_t* expert,
                     float* weight, int32_t* x_index, int* header, int* sorted, int* items, const float* x, int64_t k,
-                    void* xprep, hipStream_t s) {
+                    void* xprep, bool fp8, hipStream_t s) {
   // x null: routing and the plan only (one workgroup); else the input rows'
-  // A1 on workgroups 1..
-  const int64_t quads = x ? (int64_t)rows * kbp_of(k) * 4 : 0;
+  // A1 (or, fp8, their FP8 groups into the FP8 workspace) on workgroups 1..
+  const int64_t quads = x ? (fp8 ? (int64_t)rows * (k / 128) * WAVE : (int64_t)rows * kbp_of(k) * 4) : 0;
   int8_t* xq = nullptr;
   float* xd = nullptr;
   int* xn = nullptr;
-  if (x) {
+  uint8_t* fc = nullptr;
+  float* fs = nullptr;
+  if (x && fp8) {
+    fc = (uint8_t*)xprep;
+    fs = (float*)(fc + fp8_ws_scale_offset(rows, k));
+  } else if (x) {
     const PrepLayout L = prep_layout_rows(rows, k);
     uint8_t* w = (uint8_t*)xprep;
     xq = (int8_t*)(w + L.codes);
@@ -337,7 +352,8 @@ int launch_moe_plan(const float* logits, int rows, int n_experts, int topk, int 
     xn = (int*)(w + L.nsx);
   }
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1 + (unsigned)((quads + 1023) / 1024)), dim3(1024), 0, s, logits, rows,
-                     n_experts, topk, shared_expert, expert, weight, x_index, header, sorted, items, x, k, xq, xd, xn);
+                     n_experts, topk, shared_expert, expert, weight, x_index, header, sorted, items, x, k, xq, xd, xn,
+                     fc, fs);
   return hip_status(hipGetLastError(), "moe_plan_kernel");
 }
 
