@@ -358,11 +358,11 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
 // wave part, each taking PPW lane-part pairs, and NT 16-row image tiles that
 // share each step's activation chunk.  Two widths: narrow (more, smaller
 // tiles: more waves to hide latency) and wide (NT as large as 128 registers
-// allow: the activation chunk is loaded once per NT KB of weights, and fewer
-// tiles fit the workgroups resident at once).
+// allow without spilling: the activation chunk is loaded once per NT KB of
+// weights, and fewer tiles fit the workgroups resident at once).
 __host__ __device__ constexpr int mp_w2(int H) { return H >= 4 ? 2 : 1; }
 __host__ __device__ constexpr int mp_nt(int H, int G, bool wide) {
-  return wide ? (H == 2 || H == 4 ? (G == 2 ? 2 : 4) : (G == 2 ? 1 : 2)) : (H == 8 || G == 2 ? 1 : 2);
+  return wide ? (H == 2 || H == 4 ? (G == 2 ? 2 : 3) : (G == 2 ? 1 : 2)) : (H == 8 || G == 2 ? 1 : 2);
 }
 // block-pair steps in flight per wave (even: step j's lane-part pair is j & 1)
 __host__ __device__ constexpr int mp_la(int NT, int G) { return NT * G == 1 ? 4 : 2; }

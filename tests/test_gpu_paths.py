@@ -117,3 +117,26 @@ def test_device_probe_on_the_gpu():
     assert q.device_supported(dev)
     assert not q.device_supported(-1) and not q.device_supported(torch.cuda.device_count())
     assert torch.cuda.current_device() == dev
+
+
+@pytest.mark.parametrize("fmt,n,k,rows", [("q8_0", 20007, 4096, 5), ("q4_0", 40007, 2048, 8), ("q4_0", 20007, 4096, 3)])
+def test_wide_tiles_of_three_at_3_to_8_rows(fmt, n, k, rows):
+    """One projection whose narrow pair tiles (32 or 64 rows) overflow the workgroups resident at once on 256
+    CUs while its wide tiles (48 or 96 rows: three 16-row image tiles per wave) fit: the launch widens it, with
+    a ragged last tile. Sampled outputs, the last rows among them, against the oracle, and rows 0 and R-1
+    against the same rows alone."""
+    F = O.Q8_0 if fmt == "q8_0" else O.Q4_0
+    w = gauss((n, k), 0.02, 34, rows).numpy()
+    blocks, img = oracle_image(F, w)
+    x = outliers((rows, k), 1.0, 34, 100 + rows).numpy()
+    xd = torch.from_numpy(x).cuda()
+    call = q.qgemv_q8_0 if fmt == "q8_0" else q.qgemv_q4_0
+    y = call(img, n, k, xd)
+    sel = np.unique(np.concatenate([np.arange(n - 60, n), np.random.default_rng(n).choice(n, 200, replace=False)]))
+    yo = O.gemv_q_rows(F, blocks, n, k, x, sel, threads=8)
+    e = rel_err(y.cpu().numpy()[:, sel], yo, blocks, F, x, sel=sel)
+    log(f"{fmt} {n}x{k} rows={rows} max rel err {e:.3e}")
+    assert e <= TOL
+    for r in (0, rows - 1):
+        y1 = call(img, n, k, xd[r:r + 1].contiguous())
+        assert np.array_equal(bits(y[r]), bits(y1[0]))
