@@ -839,21 +839,26 @@ __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __res
   store_items_small_first(s_ie, s_is, s_ic, nv ? s_start[nv - 1] : 0, s_pos, s_cnt, items, header);
 }
 
-constexpr int GROUPED_LA = 4;  // blocks in flight per lane in the small-item kernel
+// Blocks in flight per lane in the small-item kernel: 4, or 8 (a lane's whole
+// chain: the partition gives every lane part at least 8 blocks) when there
+// are no more units than CUs, so each has a workgroup of its own and latency,
+// not occupancy, bounds the launch.
+constexpr int GROUPED_LA = 4;
+constexpr int GROUPED_LA_FEW = 8;
 
 // GLU: the rows are the SwiGLU of gate/up rows ta.xf, quantized while staged
 // (all of kbp fits: the launcher checks).
-template <int R, bool GLU>
+template <int R, bool GLU, int LA>
 __device__ __forceinline__ void grouped_rows(TileArgs ta, uint8_t* lds, float* red) {
   ta.ucx = rl_round(ta.lds_x, R, ta.pl, FMT_Q8);
-  rl_tile<FMT_Q8, R, GLU, GROUPED_LA, GLU>(ta, lds, red, 0, true);
+  rl_tile<FMT_Q8, R, GLU, LA, GLU>(ta, lds, red, 0, true);
 }
 
 // Unit (item, tile) of an item of at most GROUPED_SMALL_ROWS rows:
 // lanes-own-rows tiles.  Every thread calls it.  GLU: the activation row of
 // assignment a is the SwiGLU of row a of glu (gate values, then up values;
 // rows 2k wide), quantized in the tile's staging; prep is not read.
-template <bool GLU>
+template <bool GLU, int LA = GROUPED_LA>
 __device__ __forceinline__ void grouped_small_unit(const uint8_t* __restrict__ images, int64_t expert_bytes,
                                                    size_t scale_off, int64_t n, int64_t k, int kbp, const PartPlan& pl,
                                                    const Prep& prep, const int* __restrict__ sorted,
@@ -887,13 +892,13 @@ __device__ __forceinline__ void grouped_small_unit(const uint8_t* __restrict__ i
   ta.lds_x = lds_x;
   ta.pl = pl;
   ta.ucx = 0;  // set per row count
-  if (cnt == 1) grouped_rows<1, GLU>(ta, lds, red);
-  else if (cnt == 2) grouped_rows<2, GLU>(ta, lds, red);
+  if (cnt == 1) grouped_rows<1, GLU, LA>(ta, lds, red);
+  else if (cnt == 2) grouped_rows<2, GLU, LA>(ta, lds, red);
 }
 
 // Items of at most GROUPED_SMALL_ROWS rows (the plan puts them first), when
 // no item can have more: persistent over the (item, tile) units.
-template <bool GLU>
+template <bool GLU, int LA>
 __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__ images, int64_t expert_bytes,
                                                      size_t scale_off, int64_t n, int64_t k, int kbp, PartPlan pl,
                                                      Prep prep,
@@ -905,8 +910,8 @@ __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__
   __shared__ int s_map[2 * QG_MAX_ROWS];
   const int units = header[2] * tiles;
   for (int u = blockIdx.x; u < units; u += gridDim.x)  // uniform over the workgroup
-    grouped_small_unit<GLU>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y, lds_x,
-                            u / tiles, u % tiles, lds, s_map, glu);
+    grouped_small_unit<GLU, LA>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y,
+                                lds_x, u / tiles, u % tiles, lds, s_map, glu);
 }
 
 // Rows of a grouped item in the pair kernel's tiles (one 16-row image tile per
@@ -1223,7 +1228,10 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
   if (glu && (mb > 0 || !grouped_glu_fits(k)))
     return fail(QG_ELAUNCH, "SwiGLU rows need items of at most two rows and k=%lld staged whole", (long long)k);
   if (mb == 0) {
-    auto kern = glu ? grouped_kernel<true> : grouped_kernel<false>;
+    // at most m items, so at most m * tiles units
+    const bool few = (int64_t)m * tiles <= device_cus();
+    auto kern = glu ? (few ? grouped_kernel<true, GROUPED_LA_FEW> : grouped_kernel<true, GROUPED_LA>)
+                    : (few ? grouped_kernel<false, GROUPED_LA_FEW> : grouped_kernel<false, GROUPED_LA>);
     const unsigned gs = persistent_grid(kern, lds_s, (int64_t)m * tiles);
     hipLaunchKernelGGL(kern, dim3(gs), dim3(WG), lds_s, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv, header,
                        sorted, items, x_index, y, lx_s, tiles, glu);
