@@ -315,8 +315,7 @@ int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64
   if (int st = check_device()) return st;
   hipStream_t s = (hipStream_t)stream;
   const GroupedLayout G = grouped_layout(x_rows, k, m);
-  if (int st = launch_prepare(x, x_rows, k, (uint8_t*)ws + G.prep, prep_layout_rows(x_rows, k), s)) return st;
-  if (int st = launch_grouped(w_images, n_experts, n, k, x_rows, expert, x_index, m, y, ws, s)) return st;
+  if (int st = launch_grouped(w_images, n_experts, n, k, x, x_rows, expert, x_index, m, y, ws, s)) return st;
   return ok();
 }
 
@@ -338,8 +337,9 @@ int qgemv_fp8_grouped(const void* w_images, int64_t n_experts, int64_t n, int64_
   int* header = (int*)(w + G.header);
   int* sorted = (int*)(w + G.sorted);
   int* items = (int*)(w + G.items);
-  if (int st = launch_fp8_prepare(x, x_rows, k, w + G.prep, s)) return st;
-  if (int st = launch_grouped_plan(expert, x_index, m, n_experts, x_rows, header, sorted, items, s)) return st;
+  if (int st = launch_grouped_plan(expert, x_index, m, n_experts, x_rows, header, sorted, items, s, x, k, w + G.prep,
+                                   true))
+    return st;
   if (int st = launch_grouped_fp8(w_images, n, k, w + G.prep, x_rows, header, sorted, items, x_index, m, y, s))
     return st;
   return ok();

@@ -167,4 +167,46 @@ __device__ inline void store_items_small_first(const int* s_ie, const int* s_is,
   }
 }
 
+// Workgroups 1.. of a plan launch (workgroup 0 plans): the input rows' A1 in
+// row order, four lanes per 32-block (item (blockIdx.x - 1) * blockDim.x +
+// threadIdx.x of rows * kbp * 4; pad blocks quantize zeros).
+__device__ __forceinline__ void plan_prepare_q8(const float* __restrict__ x, int rows, int64_t k,
+                                                int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                int* __restrict__ xn) {
+  const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
+  const int e = (blockIdx.x - 1) * blockDim.x + threadIdx.x;
+  if (e >= rows * kbp * 4) return;  // rows * kbp * 4 is a multiple of 64: whole waves leave
+  const int q = e & 3, blk = e >> 2, r = blk / kbp, b = blk - r * kbp;
+  float v[8];
+  if (b < kb) {
+    const float4* src = reinterpret_cast<const float4*>(x + (int64_t)r * k + (int64_t)b * QK + q * 8);
+    const float4 a = src[0], c = src[1];
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = 0.0f;
+  }
+  unsigned lo, hi;
+  float d;
+  int sum;
+  quantize_quarter(v, lo, hi, d, sum);
+  *reinterpret_cast<uint2*>(xq + ((int64_t)r * kbp + b) * 32 + q * 8) = make_uint2(lo, hi);
+  if (q == 0) {
+    xd[r * kbp + b] = d;
+    xn[r * kbp + b] = -8 * sum;
+  }
+}
+
+// The same for the FP8 lane: the input rows' 1 x 128 groups, a wave per
+// (row, group).
+__device__ __forceinline__ void plan_prepare_fp8(const float* __restrict__ x, int rows, int64_t k,
+                                                 uint8_t* __restrict__ fcodes, float* __restrict__ fscales) {
+  const int lane = threadIdx.x % WAVE;
+  const int64_t kg = k / 128, e = (int64_t)(blockIdx.x - 1) * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+  if (e >= (int64_t)rows * kg) return;  // whole waves
+  const int64_t r = e / kg, g = e - r * kg;
+  const float2 v = reinterpret_cast<const float2*>(x + r * k + g * 128)[lane];
+  fp8_group_store(v, lane, fcodes + r * k + g * 128, fscales + e);
+}
+
 }  // namespace qg

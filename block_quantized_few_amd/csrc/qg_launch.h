@@ -46,13 +46,16 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
 // Whether rows this small are quantized inside the GEMV launch.
 bool fuses_quantization(int rows);
 
-// Grouped routed-expert Q8_0 GEMV (plan + GEMV; rows already prepared in ws).
-int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
-                   const int32_t* x_index, int m, float* y, void* ws, hipStream_t s);
-// The grouped plan alone (one workgroup): header, sorted, items of at most
-// QG_MAX_ROWS assignments of one expert.
+// Grouped routed-expert Q8_0 GEMV: the plan launch (which also quantizes the
+// x_rows fp32 rows into ws), then the GEMV.
+int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, const float* x, int x_rows,
+                   const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, hipStream_t s);
+// The grouped plan (workgroup 0): header, sorted, items of at most
+// QG_MAX_ROWS assignments of one expert; with x, workgroups 1.. quantize its
+// x_rows rows of length k into xprep (A1 rows, or with fp8 the FP8 groups).
 int launch_grouped_plan(const int32_t* expert, const int32_t* x_index, int m, int64_t n_experts, int x_rows,
-                        int* header, int* sorted, int* items, hipStream_t s);
+                        int* header, int* sorted, int* items, hipStream_t s, const float* x = nullptr, int64_t k = 0,
+                        void* xprep = nullptr, bool fp8 = false);
 // FP8 lane, grouped: the plan's items over n x k block-FP8 expert images
 // (expert_bytes apart), activation groups of x_rows rows at `ws` (the FP8
 // workspace layout), y [m][n].

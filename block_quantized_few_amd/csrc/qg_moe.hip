@@ -164,39 +164,9 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
   __shared__ int s_wsum[1024 / WAVE];
   __shared__ int s_cnt[2];
   const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
-  if (blockIdx.x > 0 && fcodes) {
-    // workgroups 1..: the input rows' 1 x 128 FP8 groups, a wave per (row, group)
-    const int64_t kg = k / 128, e = (int64_t)(blockIdx.x - 1) * (nt / WAVE) + wave;
-    if (e >= (int64_t)rows * kg) return;  // whole waves
-    const int64_t r = e / kg, g = e - r * kg;
-    const float2 v = reinterpret_cast<const float2*>(x + r * k + g * 128)[lane];
-    fp8_group_store(v, lane, fcodes + r * k + g * 128, fscales + e);
-    return;
-  }
   if (blockIdx.x > 0) {
-    // workgroups 1..: A1 of the input rows, row order, four lanes per 32-block
-    const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
-    const int e = (blockIdx.x - 1) * nt + tid;
-    if (e >= rows * kbp * 4) return;  // rows * kbp * 4 is a multiple of 64: whole waves leave
-    const int q = e & 3, blk = e >> 2, r = blk / kbp, b = blk - r * kbp;
-    float v[8];
-    if (b < kb) {
-      const float4* src = reinterpret_cast<const float4*>(x + (int64_t)r * k + (int64_t)b * QK + q * 8);
-      const float4 a = src[0], c = src[1];
-      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; i++) v[i] = 0.0f;
-    }
-    unsigned lo, hi;
-    float d;
-    int sum;
-    quantize_quarter(v, lo, hi, d, sum);
-    *reinterpret_cast<uint2*>(xq + ((int64_t)r * kbp + b) * 32 + q * 8) = make_uint2(lo, hi);
-    if (q == 0) {
-      xd[r * kbp + b] = d;
-      xn[r * kbp + b] = -8 * sum;
-    }
+    if (fcodes) plan_prepare_fp8(x, rows, k, fcodes, fscales);
+    else plan_prepare_q8(x, rows, k, xq, xd, xn);
     return;
   }
   // workgroup 0: routing and the plan

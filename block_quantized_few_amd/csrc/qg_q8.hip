@@ -781,7 +781,16 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp
 __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __restrict__ expert,
                                                             const int32_t* __restrict__ x_index, int m,
                                                             int64_t n_experts, int x_rows, int* __restrict__ header,
-                                                            int* __restrict__ sorted, int* __restrict__ items) {
+                                                            int* __restrict__ sorted, int* __restrict__ items,
+                                                            const float* __restrict__ x, int64_t k,
+                                                            int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                            int* __restrict__ xn, uint8_t* __restrict__ fcodes,
+                                                            float* __restrict__ fscales) {
+  if (blockIdx.x > 0) {  // the input rows' quantization
+    if (fcodes) plan_prepare_fp8(x, x_rows, k, fcodes, fscales);
+    else plan_prepare_q8(x, x_rows, k, xq, xd, xn);
+    return;
+  }
   __shared__ int s_e[QG_MAX_ASSIGN];
   __shared__ int s_pos[QG_MAX_ASSIGN];  // sorted position -> assignment
   __shared__ int s_start[QG_MAX_ASSIGN];  // 1 where a work item starts
@@ -1249,20 +1258,41 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
 }
 
 int launch_grouped_plan(const int32_t* expert, const int32_t* x_index, int m, int64_t n_experts, int x_rows,
-                        int* header, int* sorted, int* items, hipStream_t s) {
-  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(1024), 0, s, expert, x_index, m, n_experts, x_rows, header,
-                     sorted, items);
+                        int* header, int* sorted, int* items, hipStream_t s, const float* x, int64_t k, void* xprep,
+                        bool fp8) {
+  // x null: the plan only (one workgroup); else the input rows' A1 (or, fp8,
+  // their FP8 groups into the FP8 workspace) on workgroups 1..
+  const int64_t quads = x ? (fp8 ? (int64_t)x_rows * (k / 128) * WAVE : (int64_t)x_rows * kbp_of(k) * 4) : 0;
+  int8_t* xq = nullptr;
+  float* xd = nullptr;
+  int* xn = nullptr;
+  uint8_t* fc = nullptr;
+  float* fs = nullptr;
+  if (x && fp8) {
+    fc = (uint8_t*)xprep;
+    fs = (float*)(fc + fp8_ws_scale_offset(x_rows, k));
+  } else if (x) {
+    const PrepLayout L = prep_layout_rows(x_rows, k);
+    uint8_t* w = (uint8_t*)xprep;
+    xq = (int8_t*)(w + L.codes);
+    xd = (float*)(w + L.dx);
+    xn = (int*)(w + L.nsx);
+  }
+  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1 + (unsigned)((quads + 1023) / 1024)), dim3(1024), 0, s, expert,
+                     x_index, m, n_experts, x_rows, header, sorted, items, x, k, xq, xd, xn, fc, fs);
   return hip_status(hipGetLastError(), "grouped_plan_kernel");
 }
 
-int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, int x_rows, const int32_t* expert,
-                   const int32_t* x_index, int m, float* y, void* ws, hipStream_t s) {
+int launch_grouped(const void* images, int64_t n_experts, int64_t n, int64_t k, const float* x, int x_rows,
+                   const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, hipStream_t s) {
   const GroupedLayout G = grouped_layout(x_rows, k, m);
   uint8_t* w = (uint8_t*)ws;
   int* header = (int*)(w + G.header);
   int* sorted = (int*)(w + G.sorted);
   int* items = (int*)(w + G.items);
-  if (int st = launch_grouped_plan(expert, x_index, m, n_experts, x_rows, header, sorted, items, s)) return st;
+  if (int st = launch_grouped_plan(expert, x_index, m, n_experts, x_rows, header, sorted, items, s, x, k, w + G.prep,
+                                   false))
+    return st;
   return launch_grouped_planned(images, n_experts, n, k, w + G.prep, x_rows, header, sorted, items, x_index, m,
                                 QG_MAX_ROWS, y, s);
 }

@@ -276,7 +276,8 @@ int qg_prepare_rows_set(const qg_act* acts /*host*/, int count, int rows, qg_str
  * device int32 arrays; an entry out of range is skipped (y[j] untouched) and
  * counted in the workspace, readable with qg_grouped_status.  x [x_rows][k],
  * 1 <= x_rows <= QG_MAX_PREP_ROWS, 0 <= m <= QG_MAX_ASSIGN; with m == 0, y, expert
- * and x_index may be null and only the status words are written. */
+ * and x_index may be null and only the workspace is written.  Two launches:
+ * the plan (which also quantizes x into ws), then the GEMV. */
 int qgemv_q8_0_grouped(const void* w_images, int64_t n_experts, int64_t n, int64_t k, const float* x, int x_rows,
                        const int32_t* expert, const int32_t* x_index, int m, float* y, void* ws, size_t ws_bytes,
                        qg_stream stream);
