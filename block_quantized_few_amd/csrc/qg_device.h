@@ -174,9 +174,11 @@ __device__ __forceinline__ void plan_prepare_q8(const float* __restrict__ x, int
                                                 int8_t* __restrict__ xq, float* __restrict__ xd,
                                                 int* __restrict__ xn) {
   const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
-  const int e = (blockIdx.x - 1) * blockDim.x + threadIdx.x;
-  if (e >= rows * kbp * 4) return;  // rows * kbp * 4 is a multiple of 64: whole waves leave
-  const int q = e & 3, blk = e >> 2, r = blk / kbp, b = blk - r * kbp;
+  const int64_t e = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)rows * kbp * 4) return;  // a multiple of 64: whole waves leave
+  const int q = (int)(e & 3);
+  const int64_t blk = e >> 2, r = blk / kbp;
+  const int b = (int)(blk - r * kbp);
   float v[8];
   if (b < kb) {
     const float4* src = reinterpret_cast<const float4*>(x + (int64_t)r * k + (int64_t)b * QK + q * 8);
