@@ -703,8 +703,9 @@ __device__ __forceinline__ TileArgs tile_args(const ProjDev& d, int64_t row0, co
 // LA: blocks in flight per lane -- 2 when the launch fills the GPU (the many
 // waves give the memory parallelism; at most 80 registers, 96 for two Q8_0
 // rows, which would spill, so that three 512-thread workgroups fit a CU and a
-// layer's tiles are resident at once), 8 for launches of at most one
-// workgroup per CU (latency-bound: a lane's blocks all in flight at once).
+// layer's tiles are resident at once), 8 with one workgroup per CU (a
+// lane's blocks all in flight at once: launches of at most one tile per CU,
+// which are latency-bound, and one row over many rounds of tiles).
 template <int FMT, int R, bool FUSED, int LA>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(LA > 2 ? 2 : (FMT == FMT_Q8 && R == 2 ? 5 : 6))))
 void rl_set_kernel(SetArgs a, int lds_x) {
@@ -1035,8 +1036,13 @@ bool fuses_quantization(int rows) { return rows >= 1 && rows <= FUSE_MAX_ROWS; }
 template <int FMT, int R, bool FUSED>
 static void launch_rl(const SetArgs& a, int lds_x, hipStream_t s) {
   const size_t lds = (size_t)lds_x + 2 * WAVES * WAVE * R * 4;
-  bool small = a.total_tiles <= device_cus();
-  for (int i = 0; i < a.count; i++) small = small && a.p[i].ucx == a.p[i].pl.BS;  // staged whole (LA | rounds)
+  bool whole = true;  // every projection staged whole (LA need not divide a staging round)
+  for (int i = 0; i < a.count; i++) whole = whole && a.p[i].ucx == a.p[i].pl.BS;
+  // A lane's whole chain in flight, one workgroup per CU: for launches of at
+  // most one tile per CU, and for one row over four or more tiles per CU (one
+  // row of 128256 x 4096: 87 -> 85 us, of 65536 x 4096: 46.7 -> 45.0; equal at
+  // two tiles per CU; at two rows slower at every size).
+  const bool small = whole && (a.total_tiles <= device_cus() || (R == 1 && a.total_tiles >= 4 * device_cus()));
   if (small) {
     auto kern = rl_set_kernel<FMT, R, FUSED, 8>;
     hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, lds_x);
