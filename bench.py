@@ -232,7 +232,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py measures one GPU: this build runs the GEMV on a single MI355X and has no multi-GPU "
+        print("bench.py measures one GPU: the GEMV path runs on a single MI355X and has no multi-GPU "
               "path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch

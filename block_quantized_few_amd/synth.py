@@ -1,7 +1,7 @@
 """Seeded synthetic inputs: counter-based SplitMix64 feeding Box-Muller.
 
 This module holds no arithmetic of the quantized GEMV. It only draws the
-Gaussian tensors that both the HIP path and the CPU checker consume, so the
+Gaussian tensors that both the HIP path and the CPU oracle consume, so the
 same (seed, element index) always yields the same fp32 value on any device.
 
 Generator definitions (published, restated):

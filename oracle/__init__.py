@@ -1,4 +1,4 @@
-"""ctypes view of the CPU checker (qgemv_oracle.c).
+"""ctypes view of the CPU oracle (qgemv_oracle.c).
 
 TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
 CPU-baseline leg use it to produce expected values; the HIP library and its

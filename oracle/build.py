@@ -1,4 +1,4 @@
-"""Compile the CPU checker (qgemv_oracle.c) into oracle/liboracle.so with gcc.
+"""Compile the CPU oracle (qgemv_oracle.c) into oracle/liboracle.so with gcc.
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline load the result.

@@ -1,4 +1,4 @@
-"""Pins of the CPU checker against values fixed by the pages' formats and by mathematics.
+"""Pins of the CPU oracle against values fixed by the pages' formats and by mathematics.
 
 Each test ties one oracle function to something other than itself: hand-derived
 fixtures under tests/golden/, numpy's IEEE binary16 conversion, closed forms,
