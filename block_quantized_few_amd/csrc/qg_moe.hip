@@ -280,13 +280,27 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i4 * 4 >= hidden) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < slots; s++) {
-    const float wgt = weight[(int64_t)r * slots + s];
-    const float4 v = reinterpret_cast<const float4*>(o + ((int64_t)r * slots + s) * hidden)[i4];
-    acc.x = __builtin_fmaf(wgt, v.x, acc.x);
-    acc.y = __builtin_fmaf(wgt, v.y, acc.y);
-    acc.z = __builtin_fmaf(wgt, v.z, acc.z);
-    acc.w = __builtin_fmaf(wgt, v.w, acc.w);
+  // slots in order; each group of eight slots' loads issued together (a slot
+  // past the end re-reads the last one and is not used)
+  constexpr int B = 8;
+  for (int s0 = 0; s0 < slots; s0 += B) {
+    float wgt[B];
+    float4 v[B];
+#pragma unroll
+    for (int j = 0; j < B; j++) {
+      const int s = s0 + j < slots ? s0 + j : slots - 1;
+      wgt[j] = weight[(int64_t)r * slots + s];
+      v[j] = reinterpret_cast<const float4*>(o + ((int64_t)r * slots + s) * hidden)[i4];
+    }
+#pragma unroll
+    for (int j = 0; j < B; j++) {
+      if (s0 + j < slots) {
+        acc.x = __builtin_fmaf(wgt[j], v[j].x, acc.x);
+        acc.y = __builtin_fmaf(wgt[j], v[j].y, acc.y);
+        acc.z = __builtin_fmaf(wgt[j], v[j].z, acc.z);
+        acc.w = __builtin_fmaf(wgt[j], v[j].w, acc.w);
+      }
+    }
   }
   reinterpret_cast<float4*>(y + (int64_t)r * hidden)[i4] = acc;
 }
