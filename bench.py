@@ -439,7 +439,8 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
                                            for x, w in zip(ls.xs, ls.wss)])
                 L.qg_prepare_rows_set(acts, len(ls.xs), rows, sh)
                 pre = [ctypes_arr(q._Proj, [q._Proj(ls.imgs[c][i].data_ptr(), n_, k_,
-                                                    ls.wss[LAYER_SRC.get(nm, 0)].data_ptr(), ls.ys[i].data_ptr())
+                                                    ls.wss[LAYER_SRC.get(nm, 0)].data_ptr(),
+                                                    ls.wss[LAYER_SRC.get(nm, 0)].numel(), ls.ys[i].data_ptr())
                                             for i, (nm, n_, k_) in enumerate(ls.layer)]) for c in range(ls.copies)]
 
                 def gemv(i, pre=pre, rows=rows, fmt=fmt):
@@ -480,7 +481,7 @@ def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
         fp, fn = wsf.data_ptr(), wsf.numel()
         ms = time_calls(torch, timer, stream, lambda i: L.qgemv_fp8(pf[i % 2], n, k, xp, rows, yp, fp, fn, sh), 40)
         out.append(entry("lm head 128256x4096", "fp8", rows, f8b, ms, 2))
-        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_fp8_prepared(pf[i % 2], n, k, fp, rows, yp, sh), 40)
+        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_fp8_prepared(pf[i % 2], n, k, fp, fn, rows, yp, sh), 40)
         out.append(entry("lm head 128256x4096, prepared rows", "fp8", rows, f8b, ms, 1))
     del w16, q8, f8
     print(f"[bench] sweep lm head done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -648,7 +649,7 @@ def profile_one(args, torch, q, synth, L, sh, stream, timer):
             wbytes = 2 * n * k
         else:
             ws = q.prepare_fp8(x)
-            fn = lambda i: L.qgemv_fp8_prepared(p[i % 2], n, k, ws.data_ptr(), rows, yp, sh)
+            fn = lambda i: L.qgemv_fp8_prepared(p[i % 2], n, k, ws.data_ptr(), ws.numel(), rows, yp, sh)
             wbytes = q.image_bytes(q.FP8, n, k)
     elif wl in ("layer-1b", "layer-3b"):
         lay, fmt, wid = (LAYER_1B, q.Q8_0, 1) if wl == "layer-1b" else (LAYER_3B, q.Q4_0, 2)

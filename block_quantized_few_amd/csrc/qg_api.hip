@@ -115,15 +115,14 @@ int qg_prepare_fp8(const float* x, int rows, int64_t k, void* ws, size_t ws_byte
   return ok();
 }
 
-int qgemv_fp8_prepared(const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
+int qgemv_fp8_prepared(const void* w_image, int64_t n, int64_t k, const void* ws, size_t ws_bytes, int rows, float* y,
                        qg_stream stream) {
   if (int st = check_rows(rows)) return st;
   if (int st = check_fp8_nk(n, k)) return st;
   if (int st = check_image(w_image, "w_image")) return st;
   if (int st = check_y(y)) return st;
   if (rows == 0) return ok();
-  if (!ws) return fail(QG_EINVAL, "ws is null");
-  if (!aligned(ws, 256)) return fail(QG_EALIGN, "ws %p is not 256-byte aligned", ws);
+  if (int st = check_ws(ws, ws_bytes, fp8_ws_bytes(rows, k), "the FP8 activation rows")) return st;
   if (int st = check_device()) return st;
   if (int st = launch_gemv_fp8(w_image, n, k, ws, rows, y, (hipStream_t)stream)) return st;
   return ok();
@@ -187,16 +186,17 @@ int qg_prepare_rows_set(const qg_act* acts, int count, int rows, qg_stream strea
   return ok();
 }
 
-int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
-                   qg_stream stream) {
+int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, size_t ws_bytes, int rows,
+                   float* y, qg_stream stream) {
   if (int st = check_fmt(fmt)) return st;
   if (int st = check_rows(rows)) return st;
   if (int st = check_nk(n, k)) return st;
   if (int st = check_image(w_image, "w_image")) return st;
   if (int st = check_y(y)) return st;
   if (rows == 0) return ok();
-  if (!ws) return fail(QG_EINVAL, "ws is null");
-  if (!aligned(ws, 256)) return fail(QG_EALIGN, "ws %p is not 256-byte aligned", ws);
+  // the layout read depends on rows (row order at 1-2, pair order at 3-16): the
+  // workspace must hold that layout whole, or the kernel would read past it
+  if (int st = check_ws(ws, ws_bytes, prep_layout(rows, k).total, "the prepared rows")) return st;
   if (int st = check_device()) return st;
   ProjArg pa{w_image, n, k, ws, nullptr, y};
   if (int st = launch_qgemv_set(fmt, &pa, 1, rows, (hipStream_t)stream)) return st;
@@ -223,7 +223,10 @@ int qgemv_set(int fmt, const qg_proj* projs, int count, int rows, qg_stream stre
     if (int st = check_nk(p.n, p.k)) return fail(st, "projs[%d]: n=%lld k=%lld", i, (long long)p.n, (long long)p.k);
     if (int st = check_image(p.w_image, "w_image")) return fail(st, "projs[%d].w_image null or misaligned", i);
     if (int st = check_y(p.y)) return fail(st, "projs[%d].y null or misaligned", i);
-    if (!p.ws || !aligned(p.ws, 256)) return fail(QG_EALIGN, "projs[%d].ws null or misaligned", i);
+    if (rows) {
+      if (int st = check_ws(p.ws, p.ws_bytes, prep_layout(rows, p.k).total, "the prepared rows"))
+        return fail(st, "projs[%d].ws null, misaligned or small (%zu bytes)", i, p.ws_bytes);
+    }
     pa[i] = ProjArg{p.w_image, p.n, p.k, p.ws, nullptr, p.y};
   }
   if (rows == 0) return ok();

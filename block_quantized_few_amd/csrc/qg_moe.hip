@@ -270,9 +270,10 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g
   h[t] = g / (1.0f + expf(-g)) * u;
 }
 
-// Each thread writes 4 contiguous outputs from 16-byte loads; every sum runs
-// over the slots in order (the combine of the TensorFold drama page keeps each
-// sum's order the same way).
+// A thread owns four neighbouring outputs of a row and reads them as one
+// float4 per slot; it adds the slots strictly in slot order, so the result
+// does not depend on how the loads are grouped (the drama page, series
+// commits: its combine kernel was widened without changing any sum's order).
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ o,
                                                           const float* __restrict__ weight, int slots,
                                                           int64_t hidden, float* __restrict__ y) {

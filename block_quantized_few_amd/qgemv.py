@@ -32,7 +32,8 @@ class QGError(RuntimeError):
 
 
 class _Proj(C.Structure):
-    _fields_ = [("w_image", C.c_void_p), ("n", C.c_int64), ("k", C.c_int64), ("ws", C.c_void_p), ("y", C.c_void_p)]
+    _fields_ = [("w_image", C.c_void_p), ("n", C.c_int64), ("k", C.c_int64), ("ws", C.c_void_p),
+                ("ws_bytes", C.c_size_t), ("y", C.c_void_p)]
 
 
 class _ProjRows(C.Structure):
@@ -51,8 +52,8 @@ _SIGS = {
     "qg_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64]),
     "qg_fp8_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64]),
     "qg_prepare_fp8": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p]),
-    "qgemv_fp8_prepared": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
-                                     C.c_void_p]),
+    "qgemv_fp8_prepared": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_size_t, C.c_int,
+                                     C.c_void_p, C.c_void_p]),
     "qgemv_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                             C.c_size_t, C.c_void_p]),
     "qg_grouped_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int64, C.c_int]),
@@ -63,8 +64,8 @@ _SIGS = {
     "qg_prepare_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qg_add_rmsnorm_prepare": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_float, C.c_int, C.c_int64,
                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
-    "qgemv_prepared": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
-                                 C.c_void_p]),
+    "qgemv_prepared": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_size_t, C.c_int,
+                                 C.c_void_p, C.c_void_p]),
     "qgemv_q8_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                              C.c_size_t, C.c_void_p]),
     "qgemv_q4_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
@@ -242,7 +243,7 @@ def prepare_rows_set(xs, wss):
 def qgemv_prepared(fmt, image, n, k, ws, rows, y=None):
     if y is None:
         y = torch.empty((rows, n), dtype=torch.float32, device=image.device)
-    _check(lib().qgemv_prepared(fmt, _p(image), n, k, _p(ws), rows, _p(y), _stream()))
+    _check(lib().qgemv_prepared(fmt, _p(image), n, k, _p(ws), ws.numel(), rows, _p(y), _stream()))
     return y
 
 
@@ -285,7 +286,7 @@ def qgemv_fp8(image, n, k, x, y=None, ws=None):
 def qgemv_fp8_prepared(image, n, k, ws, rows, y=None):
     if y is None:
         y = torch.empty((rows, n), dtype=torch.float32, device=ws.device)
-    _check(lib().qgemv_fp8_prepared(_p(image), n, k, _p(ws), rows, _p(y), _stream()))
+    _check(lib().qgemv_fp8_prepared(_p(image), n, k, _p(ws), ws.numel(), rows, _p(y), _stream()))
     return y
 
 
@@ -338,7 +339,7 @@ def qgemv_set(fmt, projs, rows):
     """projs: list of (image, n, k, ws, y)."""
     arr = (_Proj * len(projs))()
     for i, (image, n, k, ws, y) in enumerate(projs):
-        arr[i] = _Proj(image.data_ptr(), n, k, ws.data_ptr(), y.data_ptr())
+        arr[i] = _Proj(image.data_ptr(), n, k, ws.data_ptr(), ws.numel(), y.data_ptr())
     _check(lib().qgemv_set(fmt, arr, len(projs), rows, _stream()))
 
 

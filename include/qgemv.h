@@ -117,14 +117,18 @@ enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3, QG_FMT_FP8 = 4 };
 
 /* ------------------------------------------------------------ host only --- */
 
-/* Bytes of the device image of an n x k matrix in `fmt` (Q8_0, Q4_0, F16:
- * the padded layouts above).  Returns 0 for an invalid format or shape. */
+/* Bytes of the device image of an n x k matrix in `fmt` (Q8_0, Q4_0, F16,
+ * FP8: the padded layouts above).  Returns 0 for an invalid format or shape,
+ * k included: K must come in whole blocks of the format (the llama-leg page,
+ * commit 8624bce: a block format's one-row form needs K in whole blocks). */
 size_t qg_image_bytes(int fmt, int64_t n, int64_t k);
 
 /* Host -> host.  Converts canonical blocks (Q8_0 / Q4_0, n * k/32 blocks, row
  * major; F16: the row-major [n][k] halfwords, k % 8 == 0) to the device
  * layout in `image` (qg_image_bytes bytes, host memory; copy it to the device
- * afterwards).  Padding is written as zeros. */
+ * afterwards).  Padding is written as zeros.  Both buffers belong to the
+ * caller; QG_EINVAL / QG_ESHAPE on a null pointer, unknown format or bad
+ * shape, nothing written then. */
 int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image);
 
 /* Host -> host inverse of qg_pack_image (padding is dropped). */
@@ -135,11 +139,16 @@ int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* bloc
 size_t qg_fp8_workspace_bytes(int rows, int64_t k);
 
 /* Bytes of the workspace that holds `rows` quantized activation rows of
- * length k (codes, scales and code sums).  0 for an invalid shape. */
+ * length k (codes, scales and code sums) in the order a GEMV of `rows` rows
+ * reads (row order at 1-2 rows, pair order at 3-16).  q8 activations are the
+ * audio-towers page's q8 lane (feature commit): int8 codes in 32-blocks with
+ * one scale each.  0 for an invalid shape (k not whole blocks, rows < 1). */
 size_t qg_workspace_bytes(int rows, int64_t k);
 
 /* Bytes of the workspace of qgemv_q8_0_grouped for x_rows activation rows of
- * length k and m assignments.  0 for an invalid shape. */
+ * length k and m assignments: the plan (assignments sorted by expert, work
+ * items of at most 16 of one expert) and the q8 rows.  0 for an invalid
+ * shape (m > QG_MAX_ASSIGN included). */
 size_t qg_grouped_workspace_bytes(int x_rows, int64_t k, int m);
 
 /* Static description of a status code. */
@@ -173,10 +182,10 @@ int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* ima
 int qg_prepare_rows(const float* x, int rows, int64_t k, void* ws, size_t ws_bytes, qg_stream stream);
 
 /* The step before a projection group, in one launch: residual add, RMS norm
- * and A1 (the drama page's backbone section: the add and norm before the MoE
- * write the normed rows' quantized groups in the order and rounding of the
- * separate quantization they replace; the llama-leg page's add+rms requant
- * arm).  Per row r of x [rows][k] (fp32):
+ * and A1.  The drama page (series commits) folds the activation quantization
+ * of the next projection into its add + norm launch with results equal to a
+ * separate quantization pass; the llama-leg page ("Not done") names a requant
+ * arm of its add+rms family.  Per row r of x [rows][k] (fp32):
  *   h = x + residual                    (residual may be null: h = x)
  *   y = h * (1 / sqrt(mean(h^2) + eps)) * gamma   (gamma [k])
  * in fp32: the sum of squares in a fixed order (per thread, then a wave tree,
@@ -191,16 +200,36 @@ int qg_add_rmsnorm_prepare(const float* x, const float* residual, const float* g
                            float* h_out, float* y_out, void* ws, size_t ws_bytes, qg_stream stream);
 
 /* q8 lane GEMV on rows already prepared in `ws` (by qg_prepare_rows with the
- * same rows and k): y [rows][n] fp32, row stride n.  fmt = Q8_0 or Q4_0. */
-int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
-                   qg_stream stream);
+ * same rows and k): y [rows][n] fp32, row stride n.  fmt = Q8_0 or Q4_0.
+ * ws_bytes is the workspace's size: smaller than qg_workspace_bytes(rows, k)
+ * is refused (QG_EWORKSPACE) rather than read past (the audio-towers page,
+ * router-GEMV commit: a launch never reads past what it was given). */
+int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, size_t ws_bytes, int rows,
+                   float* y, qg_stream stream);
 
-/* Q8_0 weights x q8 activations: qg_prepare_rows then qgemv_prepared.
- * x [rows][k] fp32, y [rows][n] fp32, ws of qg_workspace_bytes(rows, k). */
+/* Q8_0 weights x q8 activations: y [rows][n] = W . x for 0 <= rows <= 16.
+ * The q8 lane of the audio-towers page (feature commit: the default device
+ * lane; block-quantized weights against q8 activations, integer block dots);
+ * rows past eight tiled inside this one call and weight pass, each row equal
+ * to the row computed alone (the same page's router-GEMV commit; the
+ * llama-leg page, commit 16880fe: balanced groups past eight rows, never a
+ * weight pass a row); k in whole 32-blocks (llama-leg page, commit 8624bce).
+ *   w_image  device image (qg_quantize_weights / qg_pack_image), 256-aligned
+ *   x        [rows][k] fp32, device, 16-aligned, finite
+ *   y        [rows][n] fp32, device, written whole, nothing else written
+ *   ws       device scratch of ws_bytes >= qg_workspace_bytes(rows, k),
+ *            256-aligned, owned by the caller (rows 1-2 are quantized inside
+ *            the GEMV launch; the workspace is still checked)
+ * Errors (nothing launched): QG_EROWS for rows outside 0..16, QG_ESHAPE for
+ * n < 1 or k not whole blocks, QG_EINVAL / QG_EALIGN for null or misaligned
+ * pointers, QG_EWORKSPACE for a short workspace, QG_EDEVICE off gfx950. */
 int qgemv_q8_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
                size_t ws_bytes, qg_stream stream);
 
-/* Q4_0 weights x q8 activations; arguments as qgemv_q8_0. */
+/* Q4_0 weights x q8 activations; arguments, rows, tiling and errors as
+ * qgemv_q8_0 (the q8 lane of the audio-towers page's feature commit, with
+ * 4-bit weight blocks).  The codes stand for c - 8; each block dot starts
+ * from -8 * (sum of the activation codes). */
 int qgemv_q4_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
                size_t ws_bytes, qg_stream stream);
 
@@ -210,10 +239,15 @@ int qgemv_q4_0(const void* w_image, int64_t n, int64_t k, const float* x, int ro
 int qg_f16_image(const uint16_t* w, int64_t n, int64_t k, void* image, qg_stream stream);
 
 /* f16 lane: y [rows][n] = W [n][k] (fp16, as the F16 image w_image) . x
- * [rows][k] (fp32), fp32 products and sums; x enters the halfword products as
- * two halfword terms per value (about 22 significant bits, scaled by a power
- * of two per row and k range), so the result is fp32-accurate.  A row's bits
- * do not depend on the other rows of the call. */
+ * [rows][k] (fp32), fp32 products and sums -- the reference lane of the
+ * audio-towers page (feature commit: halfword weights, f32 accumulate).
+ * x enters the halfword products as two halfword terms per value (about 22
+ * significant bits, scaled by a power of two per row and k range), so the
+ * result is fp32-accurate.  A row's bits do not depend on the other rows of
+ * the call (router-GEMV commit).  The weights come as the F16 image
+ * (qg_f16_image from row-major halfwords, once, offline) rather than as the
+ * row-major matrix: a wave then reads 1 KB of consecutive bytes per load.
+ * rows 0..16, k % 8 == 0; errors as qgemv_q8_0 (no workspace). */
 int gemv_f16(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, qg_stream stream);
 
 /* FP8 lane, activation groups: x [rows][k] fp32 (1 <= rows <= 8192) into the
@@ -222,9 +256,10 @@ int qg_prepare_fp8(const float* x, int rows, int64_t k, void* ws, size_t ws_byte
 
 /* FP8 lane GEMV on rows prepared by qg_prepare_fp8 (same rows and k):
  * y [rows][n] fp32, 0 <= rows <= 16.  w_image: the FP8 image (qg_pack_image
- * or qg_quantize_weights with QG_FMT_FP8). */
-int qgemv_fp8_prepared(const void* w_image, int64_t n, int64_t k, const void* ws, int rows, float* y,
-                       qg_stream stream);
+ * or qg_quantize_weights with QG_FMT_FP8).  ws_bytes smaller than
+ * qg_fp8_workspace_bytes(rows, k) is refused (QG_EWORKSPACE). */
+int qgemv_fp8_prepared(const void* w_image, int64_t n, int64_t k, const void* ws, size_t ws_bytes, int rows,
+                       float* y, qg_stream stream);
 
 /* qg_prepare_fp8 then qgemv_fp8_prepared: x [rows][k] fp32, y [rows][n]. */
 int qgemv_fp8(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
@@ -232,13 +267,15 @@ int qgemv_fp8(const void* w_image, int64_t n, int64_t k, const float* x, int row
 
 /* Several independent q8-lane projections with the same row count in one
  * launch (a decode layer's Q/K/V/O/gate/up/down).  Each entry's rows must
- * already be prepared in its `ws`.  1 <= count <= QG_MAX_SET. */
+ * already be prepared in its `ws` (ws_bytes >= qg_workspace_bytes(rows, k),
+ * else QG_EWORKSPACE).  1 <= count <= QG_MAX_SET. */
 typedef struct {
   const void* w_image;
   int64_t n;
   int64_t k;
-  const void* ws; /* prepared rows for this projection's input */
-  float* y;       /* [rows][n] */
+  const void* ws;  /* prepared rows for this projection's input */
+  size_t ws_bytes; /* its size */
+  float* y;        /* [rows][n] */
 } qg_proj;
 int qgemv_set(int fmt, const qg_proj* projs /*host*/, int count, int rows, qg_stream stream);
 
@@ -269,7 +306,10 @@ typedef struct {
 } qg_act;
 int qg_prepare_rows_set(const qg_act* acts /*host*/, int count, int rows, qg_stream stream);
 
-/* Grouped routed-expert GEMV, Q8_0.  w_images holds n_experts device images
+/* Grouped routed-expert GEMV, Q8_0 (the llama-leg page, commit 2243ccc and
+ * "Observable behavior": a routed model steps several rows' picks in one
+ * N-row command; the drama page's backbone section: a 256-expert top-8 MoE
+ * with a shared expert).  w_images holds n_experts device images
  * back to back, each qg_image_bytes(Q8_0, n, k) bytes.  For assignment j < m:
  * y[j] = W_{expert[j]} . q8(x[x_index[j]]).  Each touched expert's weights are
  * streamed once for up to 16 of its assignments.  expert and x_index are

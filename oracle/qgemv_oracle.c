@@ -604,10 +604,10 @@ void orc_swiglu(const float* g, const float* u, int64_t count, float* h) {
   }
 }
 
-/* Residual add and RMS norm, the step before a projection group ([B] backbone
- * section: the add and norm before the MoE also write the normed rows'
- * quantized groups, in the order and rounding of the separate quantization
- * they replace; [C] lists the add+rms fold with its requant arm).
+/* Residual add and RMS norm, the step before a projection group ([B] series
+ * commits: the add + norm launch also emits the activation quantization that
+ * a separate pass used to produce, with equal results; [C] "Not done" names a
+ * requant arm in its add+rms family).
  *   h = x + residual (fp32 add; residual may be NULL: h = x)
  *   y = h / sqrt(mean(h^2) + eps) * gamma, evaluated in double.
  * h is returned in fp32 (one correctly rounded add, the same on any device),

@@ -170,8 +170,27 @@ def test_validation_refuses_before_any_hip_call():
     assert st == -4 and "w " in msg
     st, msg = _status("qg_f16_image", V(A), 64, 64, V(A + 16), None)
     assert st == -4 and "image" in msg
-    st, msg = _status("qgemv_prepared", 9, V(A), 64, 64, V(A), 1, V(A), None)
+    st, msg = _status("qgemv_prepared", 9, V(A), 64, 64, V(A), MB, 1, V(A), None)
     assert st == -1 and "fmt=9" in msg
+    # a workspace prepared for two rows (row order) is too small for three (pair order): refused, not read past
+    ws2 = q.workspace_bytes(2, 2048)
+    assert ws2 < q.workspace_bytes(3, 2048)
+    st, msg = _status("qgemv_prepared", q.Q8_0, V(A), 64, 2048, V(A), ws2, 3, V(A), None)
+    assert st == -5 and f"ws_bytes={ws2}" in msg
+    st, msg = _status("qgemv_prepared", q.Q4_0, V(A), 64, 2048, V(A), 100, 1, V(A), None)
+    assert st == -5 and "ws_bytes=100" in msg
+    st, msg = _status("qgemv_prepared", q.Q8_0, V(A), 64, 2048, None, MB, 1, V(A), None)
+    assert st == -1 and "workspace is null" in msg
+    st, msg = _status("qgemv_prepared", q.Q8_0, V(A), 64, 2048, V(A + 16), MB, 1, V(A), None)
+    assert st == -4
+    st, msg = _status("qgemv_prepared", q.Q8_0, V(A), 64, 2048, None, 0, 0, V(A), None)
+    assert st == 0  # rows == 0: a no-op, the workspace is not needed
+    # qgemv_set: each entry's workspace is checked against the layout its row count reads
+    projs = (q._Proj * 2)(q._Proj(A, 64, 2048, A, MB, A), q._Proj(A, 64, 2048, A, ws2, A))
+    st, msg = _status("qgemv_set", q.Q8_0, projs, 2, 3, None)
+    assert st == -5 and "projs[1]" in msg
+    st, msg = _status("qgemv_set", q.Q8_0, projs, 2, 2, None)
+    assert st == -7  # both workspaces hold two rows: a valid call, no GPU here
     st, msg = _status("qgemv_q8_0_grouped", V(A), 8, 64, 64, V(A), 1, V(A), V(A), q.MAX_ASSIGN + 1, V(A), V(A),
                       MB, None)
     assert st == -2
@@ -186,8 +205,13 @@ def test_validation_refuses_before_any_hip_call():
     assert st == -5 and "ws_bytes=100" in msg
     st, msg = _status("qg_prepare_fp8", V(A), 2, 200, V(A), MB, None)
     assert st == -2
-    st, msg = _status("qgemv_fp8_prepared", V(A + 16), 64, 256, V(A), 1, V(A), None)
+    st, msg = _status("qgemv_fp8_prepared", V(A + 16), 64, 256, V(A), MB, 1, V(A), None)
     assert st == -4 and "w_image" in msg
+    fb = q.fp8_workspace_bytes(4, 256)
+    st, msg = _status("qgemv_fp8_prepared", V(A), 64, 256, V(A), fb, 5, V(A), None)
+    assert st == -5 and f"ws_bytes={fb}" in msg
+    st, msg = _status("qgemv_fp8_prepared", V(A), 64, 256, V(A), fb, 4, V(A), None)
+    assert st == -7
     st, msg = _status("qg_quantize_weights", q.FP8, V(A), 64, 96, V(A), None)
     assert st == -2 and "k=96" in msg
     st, msg = _status("qgemv_fp8", V(A), 64, 256, V(A), 0, V(A), V(A), 0, None)

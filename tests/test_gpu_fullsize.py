@@ -1,9 +1,10 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times, on sampled outputs the oracle computes one by one.
 
-LM head 128256 x 4096 (Q8_0 and f16) at rows 1, 8, 16; the Llama-3.2-1B-shaped
-Q8_0 decode layer (seven projections, one set launch) at rows 1 and 16; the
-Llama-3.2-3B-shaped Q4_0 layer at rows 1, 2, 4, 8."""
+LM head 128256 x 4096 (Q8_0 and f16) at rows 1, 2, 8, 16; the Llama-3.2-1B-shaped
+Q8_0 decode layer (seven projections, one set launch) at rows 1 and 16, and at
+rows 1 and 2 straight from fp32 rows (quantized inside the GEMV launch, as the
+benchmark runs it); the Llama-3.2-3B-shaped Q4_0 layer at rows 1, 2, 4, 8."""
 import numpy as np
 import pytest
 import torch
@@ -34,7 +35,7 @@ def test_lm_head_q8_0():
     img = torch.from_numpy(q.pack_image(q.Q8_0, blocks, n, k)).cuda()
     sel = _sample(n, 512, 1)
     ys = {}
-    for rows in (1, 8, 16):
+    for rows in (1, 2, 8, 16):
         log(f"LM head Q8_0 rows={rows}")
         x = gauss((rows, k), 1.0, 4, 32 + rows).numpy()
         y = q.qgemv_q8_0(img, n, k, torch.from_numpy(x).cuda())
@@ -50,6 +51,11 @@ def test_lm_head_q8_0():
     assert np.array_equal(bits(y8), bits(ys[16][1][:8]))
     y1 = q.qgemv_q8_0(img, n, k, x16[:1].contiguous())
     assert np.array_equal(bits(y1), bits(ys[16][1][:1]))
+    # two rows (quantized inside the launch, many tiles per CU): each row has its bits alone
+    x2 = torch.from_numpy(ys[2][0]).cuda()
+    for r in range(2):
+        y1 = q.qgemv_q8_0(img, n, k, x2[r:r + 1].contiguous())
+        assert np.array_equal(bits(y1), bits(ys[2][1][r:r + 1])), r
 
 
 def test_lm_head_f16():
@@ -127,6 +133,47 @@ def test_llama1b_layer_q8_0_set():
         ys, xin = _run_set(q.Q8_0, O.Q8_0, LAYER_1B, blocks, imgs, rows, 1, full=rows == 1)
     log("1B layer Q8_0: rows 0 and 15 of 16 alone")
     _rows_alone(q.Q8_0, O.Q8_0, LAYER_1B, blocks, imgs, ys, xin, 1, (0, 15))
+
+
+def _run_set_rows(fmt, ofmt, layer, blocks, imgs, xin, sample=True):
+    """The layer straight from fp32 rows (qgemv_set_rows): at 1-2 rows one launch that quantizes its rows."""
+    xs = [torch.from_numpy(a).cuda() for a in xin]
+    rows = xs[0].shape[0]
+    src = {"wo": 1, "down": 2}
+    projs, outs = [], []
+    for i, (name, n, k) in enumerate(layer):
+        j = src.get(name, 0)
+        y = torch.full((rows, n), float("nan"), device="cuda")
+        outs.append(y)
+        projs.append((imgs[i], n, k, xs[j], None if rows <= q.FUSED_ROWS else q.empty_ws(rows, k), y))
+    q.qgemv_set_rows(fmt, projs, rows)
+    if sample:
+        for i, (name, n, k) in enumerate(layer):
+            x = xin[src.get(name, 0)]
+            sel = _sample(n, 256, 100 + i)
+            yo = O.gemv_q_rows(ofmt, blocks[i], n, k, x, sel, threads=16)
+            e = rel_err(outs[i].cpu().numpy()[:, sel], yo, blocks[i], ofmt, x, sel=sel)
+            log(f"  {name} {n}x{k} rows={rows} (fused) max rel err {e:.3e}")
+            assert e <= TOL
+    return outs
+
+
+@pytest.mark.parametrize("shape,rows", [("1b", 1), ("1b", 2), ("3b", 1), ("3b", 2)])
+def test_layer_fused_rows(shape, rows):
+    """The benchmark's launch: the 1B-shaped Q8_0 and 3B-shaped Q4_0 layers from fp32 rows at 1 and 2 rows,
+    outputs sampled against the oracle, and (2 rows) each row's bits equal to that row computed alone."""
+    fmt, ofmt, layer, wl = (q.Q8_0, O.Q8_0, LAYER_1B, 1) if shape == "1b" else (q.Q4_0, O.Q4_0, LAYER_3B, 2)
+    blocks, imgs = _layer(fmt, ofmt, layer, wl)
+    k_in, k_dn = layer[0][2], layer[6][2]
+    xin = (gauss((rows, k_in), 1.0, wl, 32 + rows).numpy(), gauss((rows, k_in), 1.0, wl, 48 + rows).numpy(),
+           gauss((rows, k_dn), 1.0, wl, 64 + rows).numpy())
+    log(f"{shape} layer from fp32 rows, rows={rows}")
+    ys = _run_set_rows(fmt, ofmt, layer, blocks, imgs, xin)
+    for r in range(rows if rows > 1 else 0):
+        one = tuple(np.ascontiguousarray(a[r:r + 1]) for a in xin)
+        y1 = _run_set_rows(fmt, ofmt, layer, blocks, imgs, one, sample=False)
+        for i, (name, _, _) in enumerate(layer):
+            assert np.array_equal(bits(ys[i][r]), bits(y1[i][0])), f"{name} row {r}"
 
 
 def test_llama3b_layer_q4_0_set():

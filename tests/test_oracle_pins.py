@@ -348,6 +348,93 @@ def test_moe_step_composes_its_pieces():
         assert np.array_equal(y[r], ref)
 
 
+def _moe_closed_form_case(E=256, topk=8, hidden=64, ffn=32, rows=3):
+    """A routed step whose routing is a closed form: router row e is zero but for column 0, which holds v_e
+    (an fp16-exact value), and every input row has x[r][0] = 1, so the f16 router GEMV gives logit e = v_e
+    exactly and p_e = exp(v_e) / sum_j exp(v_j).  The other columns of x are random."""
+    v = np.float32([((7 * e) % E) / 16.0 for e in range(E)])  # distinct, fp16-exact
+    router = np.zeros((E, hidden), np.float32)
+    router[:, 0] = v
+    r16, ovf = O.f32_to_f16(router)
+    assert not ovf
+    x = _rng_normal((rows, hidden), 1.0, 83)
+    x[:, 0] = 1.0
+    z = sum(math.exp(float(t)) for t in v)
+    top = sorted(range(E), key=lambda e: (-float(v[e]), e))[:topk]
+    p_top = [math.exp(float(v[e])) / z for e in top]
+    return r16, x, top, p_top, hidden, ffn, E, topk
+
+
+def test_moe_combine_closed_forms():
+    """The combine, pinned by closed forms rather than by its own formula.
+
+    W is one expert's weights.  With every routed expert equal to W and the shared expert equal to W, each row
+    is (1 + sum of the top-k softmax probabilities over all E) * o, o being W's FFN output on that row; with the
+    routed down projections zero it is o exactly (ungated shared expert, weight 1); with the shared expert zero
+    it is (sum of the top-k probabilities) * o.  Renormalising the weights over the k picks (sum = 1), or scaling
+    or gating the shared expert, fails one of these."""
+    r16, x, top, p_top, hidden, ffn, E, topk = _moe_closed_form_case()
+    q = lambda t, s: O.quantize_weights(O.Q8_0, _rng_normal(t, 0.02, s))
+    g, u, d = q((ffn, hidden), 11), q((ffn, hidden), 12), q((hidden, ffn), 13)
+    zg, zd = O.quantize_weights(O.Q8_0, np.zeros((ffn, hidden), np.float32)), \
+        O.quantize_weights(O.Q8_0, np.zeros((hidden, ffn), np.float32))
+    rep = lambda b: np.stack([b] * E)
+    # routing and weights are closed forms
+    y_a, ex, p, logits = O.moe_step(x, r16, topk, rep(g), rep(u), rep(d), ffn, g, u, d)
+    assert np.array_equal(logits, np.tile(r16.view(np.float16)[:, 0].astype(np.float32), (x.shape[0], 1)))
+    for r in range(x.shape[0]):
+        assert list(ex[r]) == top
+        assert np.allclose(p[r], p_top, rtol=1e-13, atol=0)
+    s = sum(p_top)
+    assert 0.05 < s < 0.95  # far from 1: a renormalised combine cannot pass for this one
+    # routed down projections zero: every routed output is exactly 0, the row is the shared expert's output
+    y_b, _, _, _ = O.moe_step(x, r16, topk, rep(g), rep(u), rep(zd), ffn, g, u, d)
+    o = y_b.astype(np.float64)
+    assert np.abs(o).max() > 0
+    # shared expert zero
+    y_c, _, _, _ = O.moe_step(x, r16, topk, rep(g), rep(u), rep(d), ffn, zg, zg, zd)
+    # each result is one rounding of a double sum: relative 2^-24 per element, plus the sum's own rounding
+    tol = lambda ref: 1e-6 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(y_a - (1.0 + s) * o) <= tol((1.0 + s) * o))
+    assert np.all(np.abs(y_c - s * o) <= tol(s * o))
+    # the alternatives fail: renormalised weights give 2 * o and o; a shared expert weighted like a pick gives
+    # less than (1 + s) * o
+    assert not np.all(np.abs(y_a - 2.0 * o) <= tol(2.0 * o))
+    assert not np.all(np.abs(y_c - o) <= tol(o))
+
+
+def test_moe_combine_picks_by_weight():
+    """Distinct routed experts: expert e's down projection is zero except for row e % hidden, which is a copy of W's
+    row 0 of the down projection, so each routed pick writes one output column of its own.  Column c of a row then
+    holds p of the pick that owns it times the same value o0 (W's first down output), and every column that no
+    pick owns holds the shared expert's output alone."""
+    r16, x, top, p_top, hidden, ffn, E, topk = _moe_closed_form_case(E=32, topk=4, hidden=64, ffn=32)
+    wg, wu = _rng_normal((ffn, hidden), 0.02, 21), _rng_normal((ffn, hidden), 0.02, 22)
+    wd = _rng_normal((hidden, ffn), 0.02, 23)
+    g, u = O.quantize_weights(O.Q8_0, wg), O.quantize_weights(O.Q8_0, wu)
+    downs = []
+    for e in range(E):
+        m = np.zeros((hidden, ffn), np.float32)
+        m[e % hidden] = wd[0]
+        downs.append(O.quantize_weights(O.Q8_0, m))
+    zg = O.quantize_weights(O.Q8_0, np.zeros((ffn, hidden), np.float32))
+    zd = O.quantize_weights(O.Q8_0, np.zeros((hidden, ffn), np.float32))
+    y, ex, p, _ = O.moe_step(x, r16, topk, np.stack([g] * E), np.stack([u] * E), np.stack(downs), ffn, zg, zg, zd)
+    # o0: W's FFN output in column 0 (the shared slot with W, every routed down projection zero)
+    m0 = np.zeros((hidden, ffn), np.float32)
+    m0[0] = wd[0]
+    d0 = O.quantize_weights(O.Q8_0, m0)
+    zdn = np.stack([zd] * E)
+    y0, _, _, _ = O.moe_step(x, r16, topk, np.stack([g] * E), np.stack([u] * E), zdn, ffn, g, u, d0)
+    o0 = y0[:, 0].astype(np.float64)
+    assert np.all(np.abs(o0) > 0)
+    for r in range(x.shape[0]):
+        owned = {e % hidden: pe for e, pe in zip(top, p_top)}
+        for c in range(hidden):
+            want = owned.get(c, 0.0) * o0[r]
+            assert abs(float(y[r, c]) - want) <= 1e-6 * abs(want), (r, c)
+
+
 # --------------------------------------------------------- FP8 lane ---
 def test_e4m3_hand_values():
     v = np.array([1.0, 448.0, 2 ** -6, 2 ** -9, 2 ** -10, 3 * 2 ** -10, 1.0625, 1.1875, 500.0, -2.5, 0.0, -0.0, 1e9],
