@@ -1,16 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the few-row block-quantized GEMV on one MI355X.
 
-Headline step: one decode layer of a Llama-3.2-1B-shaped model in the Q8_0
-lane at one activation row -- the seven projections Wq 2048x2048, Wk/Wv
-512x2048, Wo 2048x2048, gate/up 8192x2048, down 2048x8192 (64,618,496 weight
-bytes) with the q8 quantization of their three fp32 input rows, all in one
-launch.  The weights rotate through enough distinct copies (>= 1 GiB) that every
-step streams them from HBM, not from the 256 MB Infinity Cache.
+Headline step: the LM-head projection W 128256 x 4096 in the Q8_0 lane at 1, 8
+and 16 activation rows -- three calls of qgemv_q8_0, each streaming the whole
+558,170,112-byte weight image once (the rows the metric is quoted at).  Two
+weight copies alternate, so no call finds its image in the 256 MB Infinity
+Cache.  `value` is the weight bytes of the step over its time.
 
-Prints one JSON line: weight GB/s of the step (value), the roofline of the
-GEMV kernel measured with HIP events on its own stream, the CPU oracle timed on
-a bounded sample, and (unless --no-sweep) the other workloads at 1..16 rows.
+Beside it, on the same line:
+  * roofline      -- per row count, the GEMV kernel's average launch duration
+                     (HIP events on its stream) against its algorithmic bytes,
+                     and their sum over the step; HBM bytes from the committed
+                     rocprofv3 counter summaries when they match the source;
+  * read_ceiling  -- a plain streaming read of the same bytes (qg_read_probe),
+                     the achievable-read figure the GEMVs are also read against;
+  * secondary     -- the other workloads at their listed rows, each with its
+                     kernel's roofline: the Llama-3.2-1B-shaped Q8_0 layer (1
+                     row), the Llama-3.2-3B-shaped Q4_0 layer (1/2/4/8 rows),
+                     the LM head in the f16 lane and in Q4_0 (1/8/16), the
+                     1024 x 1024 Q8_0 GEMV (1 row), the routed MoE step
+                     (1/8/9/16 rows);
+  * cpu_baseline  -- the C oracle on a bounded slice of the headline workload,
+                     all cores and one core, median of five reps;
+  * sweep         -- (unless --no-sweep) every workload at 1/2/4/8/9/16 rows.
+Every timed form runs five reps; the median rep is reported with the slowest.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-cpu-baseline]
 """
@@ -20,6 +33,8 @@ import hashlib
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -28,7 +43,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "weight GB/s and % HBM roofline for Q8_0/Q4_0 GEMV at 1/8/16 rows"
+REPS = 5
 
+LM_N, LM_K = 128256, 4096
+HEAD_ROWS = (1, 8, 16)
 LAYER_1B = [("wq", 2048, 2048), ("wk", 512, 2048), ("wv", 512, 2048), ("wo", 2048, 2048), ("gate", 8192, 2048),
             ("up", 8192, 2048), ("down", 2048, 8192)]
 LAYER_3B = [("wq", 3072, 3072), ("wk", 1024, 3072), ("wv", 1024, 3072), ("wo", 3072, 3072), ("gate", 8192, 3072),
@@ -40,21 +58,27 @@ LAYER_SRC = {"wo": 1, "down": 2}
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=60)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--out", default=None, help="also write the JSON line (with the sweep) to this file")
+    p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a plain elementwise kernel over 256 MiB (reads 256 MiB, writes 256 MiB) five "
                         "times, the known-size reference for the HBM byte counters")
     p.add_argument("--profile", default=None, metavar="WORKLOAD:ROWS",
-                   help="time one sweep workload (lm-head-q8, lm-head-f16, lm-head-fp8, layer-1b, layer-3b, moe) at "
-                        "ROWS activation rows for --steps calls after warm-up, print it, and exit: a short program "
-                        "for rocprofv3")
-    p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
-                   help="reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) "
-                        "of a --calibrate-copy run into profiles/traffic.json, then exit")
+                   help="time one workload (lm-head-q8, lm-head-q8-prepared, lm-head-q4, lm-head-q4-prepared, "
+                        "lm-head-f16, lm-head-fp8, layer-1b, layer-3b, layer-1b-prepared, layer-3b-prepared, moe, "
+                        "read-probe) at ROWS rows for --steps calls after a short warm-up, print it, and exit: a "
+                        "short program for rocprofv3")
+    p.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "WORKLOAD"), default=None,
+                   help="reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) of a "
+                        "--calibrate-copy --profile run into the HBM bytes per launch of KERNEL, stored in "
+                        "profiles/traffic.json under KERNEL|WORKLOAD, then exit")
+    p.add_argument("--counters", nargs=3, metavar=("CSV", "KERNEL", "WORKLOAD"), default=None,
+                   help="reduce a rocprofv3 --pmc counter_collection.csv of a --profile run into the per-dispatch "
+                        "averages of its counters for KERNEL, stored in profiles/counters.json under "
+                        "KERNEL|WORKLOAD, then exit")
     return p.parse_args()
 
 
@@ -90,9 +114,19 @@ def ctypes_arr(struct, items):
     return arr
 
 
-def kernel_source_hash():
+# ------------------------------------------------------------ profiles ---
+PROFILED_SOURCES = {
+    "rl_set_kernel": ("qg_q8.hip", "qg_device.h", "qg_layout.h"),
+    "mp_set_kernel": ("qg_q8.hip", "qg_device.h", "qg_layout.h"),
+    "gemv_f16_kernel": ("qg_f16.hip", "qg_device.h", "qg_layout.h"),
+    "gemv_fp8_kernel": ("qg_fp8.hip", "qg_device.h", "qg_layout.h"),
+    "read_probe_kernel": ("qg_probe.hip", "qg_device.h"),
+}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
-    for f in ("qg_q8.hip", "qg_device.h", "qg_layout.h"):
+    for f in PROFILED_SOURCES.get(kernel, ("qg_q8.hip", "qg_device.h", "qg_layout.h")):
         with open(os.path.join(ROOT, "block_quantized_few_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -126,50 +160,122 @@ def pmc_per_dispatch(path, counter):
     return out
 
 
-def reduce_traffic(fetch_csv, write_csv):
-    """HBM bytes per launch of the headline kernel, from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by the factor that maps the same counter to the known bytes of the calibration kernel."""
+def _pick(d, pat, big=False):
+    vals = [v for name, vs in d.items() if pat in name for v in vs]
+    if big:
+        vals = [v for v in vals if v * 1024 > COPY_BYTES / 2]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel named like {pat!r} in the counter file")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _update_json(name, key, rec):
+    path = os.path.join(ROOT, "profiles", name)
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[key] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+def reduce_traffic(fetch_csv, write_csv, kernel, workload):
+    """HBM bytes per launch of `kernel`, from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the
+    factor that maps the same counter to the known bytes of the calibration kernel."""
     fetch = pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
     write = pmc_per_dispatch(write_csv, "WRITE_SIZE")
-
-    def pick(d, pat, big=False):
-        vals = [v for name, vs in d.items() if pat in name for v in vs]
-        if big:
-            vals = [v for v in vals if v * 1024 > COPY_BYTES / 2]
-        if not vals:
-            raise SystemExit(f"no dispatch of a kernel named like {pat!r} in the counter file")
-        return sum(vals) / len(vals), len(vals)
-
-    cf, _ = pick(fetch, "neg", big=True)
-    cw, _ = pick(write, "neg", big=True)
-    kf, nf = pick(fetch, "rl_set_kernel")
-    kw, nw = pick(write, "rl_set_kernel")
+    cf, _ = _pick(fetch, "neg", big=True)
+    cw, _ = _pick(write, "neg", big=True)
+    kf, nf = _pick(fetch, kernel)
+    kw, nw = _pick(write, kernel)
     ff, fw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
-    rec = {"rl_set_kernel|llama1b-layer-q8_0-rows1": {
-        "hbm_bytes_per_launch": round(kf * 1024 * ff + kw * 1024 * fw),
-        "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kw, 1), "dispatches": [nf, nw],
-        "calibration": {"kernel": "torch.neg over 256 MiB fp32", "known_bytes_each_way": COPY_BYTES,
-                        "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
-                        "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
-        "source_hash": kernel_source_hash()}}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    with open(path, "w") as f:
-        json.dump(rec, f, indent=1)
-        f.write("\n")
+    rec = {"hbm_bytes_per_launch": round(kf * 1024 * ff + kw * 1024 * fw),
+           "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kw, 1), "dispatches": [nf, nw],
+           "calibration": {"kernel": "torch.neg over 256 MiB fp32", "known_bytes_each_way": COPY_BYTES,
+                           "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                           "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
+           "source_hash": kernel_source_hash(kernel)}
+    _update_json("traffic.json", f"{kernel}|{workload}", rec)
     print(json.dumps(rec))
+
+
+def reduce_counters(csv_path, kernel, workload):
+    """Per-dispatch averages of every counter in a --pmc run, for the dispatches of `kernel`."""
+    import csv
+    names = set()
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            names.add(r["Counter_Name"])
+    avg = {}
+    for c in sorted(names):
+        v, n = _pick(pmc_per_dispatch(csv_path, c), kernel)
+        avg[c] = round(v, 1)
+    rec = {"avg_per_dispatch": avg, "dispatches": n, "source_hash": kernel_source_hash(kernel)}
+    _update_json("counters.json", f"{kernel}|{workload}", rec)
+    print(json.dumps(rec))
+
+
+def _read_profile(name, kernel, workload):
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        e = json.load(f).get(f"{kernel}|{workload}")
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return e
 
 
 def read_traffic(kernel, workload):
     """HBM bytes per launch from the committed PMC summary, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    e = rec.get(f"{kernel}|{workload}")
-    if not e or e.get("source_hash") != kernel_source_hash():
-        return None
-    return e.get("hbm_bytes_per_launch")
+    e = _read_profile("traffic.json", kernel, workload)
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def read_busy(kernel, workload):
+    """VALU-busy and MFMA-busy % from the committed counter summary, if taken on this kernel source: the
+    counters' per-dispatch averages as rocprofv3 reported them (its derived busy metrics when collected)."""
+    e = _read_profile("counters.json", kernel, workload)
+    return None if e is None else e["avg_per_dispatch"]
+
+
+# --------------------------------------------------------------- timing ---
+def time_reps(torch, timer, stream, fn, iters, reps=REPS):
+    """Per-rep average ms of `iters` back-to-back calls (HIP events on `stream`), `reps` reps after a warm-up."""
+    for i in range(min(iters, 5)):
+        fn(i)
+    torch.cuda.synchronize()
+    out = []
+    for rep in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        timer.hold(max(5.0, iters * 0.05))
+        a.record(stream)
+        for i in range(iters):
+            fn(rep * iters + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / iters)
+    return out
+
+
+def summarize(ms_reps):
+    return {"median_us": round(statistics.median(ms_reps) * 1e3, 3), "slowest_us": round(max(ms_reps) * 1e3, 3)}
+
+
+def roofline_entry(kernel, alg_bytes, ms_reps, traffic=None, ceiling=None, busy=None):
+    avg_ms = statistics.median(ms_reps)
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+    e = {"kernel": kernel, "bound": "hbm", "alg_bytes_per_launch": int(alg_bytes),
+         "avg_launch_us": round(avg_ms * 1e3, 3), "slowest_rep_us": round(max(ms_reps) * 1e3, 3),
+         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    if ceiling:
+        e["pct_of_read_ceiling"] = round(100.0 * achieved / ceiling, 1)
+    if busy:
+        e["counters"] = busy
+    return e
 
 
 # ------------------------------------------------------------------ layers ---
@@ -207,8 +313,21 @@ class LayerSet:
                 items.append(q._ProjRows(self.imgs[c][i].data_ptr(), n, k, self.xs[j].data_ptr(),
                                          self.wss[j].data_ptr(), self.wss[j].numel(), self.ys[i].data_ptr()))
             self.projs.append(ctypes_arr(q._ProjRows, items))
+        self.prepared = None
+        if rows > q.FUSED_ROWS:
+            # the GEMV launch alone, on rows quantized once beforehand
+            self.prepared = [ctypes_arr(q._Proj, [q._Proj(self.imgs[c][i].data_ptr(), n, k,
+                                                          self.wss[LAYER_SRC.get(nm, 0)].data_ptr(),
+                                                          self.wss[LAYER_SRC.get(nm, 0)].numel(), self.ys[i].data_ptr())
+                                                  for i, (nm, n, k) in enumerate(self.layer)])
+                             for c in range(self.copies)]
         # launches of one step: the GEMV set, plus one quantize launch above the fused row count
         self.launches = 1 if rows <= q.FUSED_ROWS else 2
+
+    def prepare(self, L, sh):
+        acts = ctypes_arr(self.q._Act, [self.q._Act(x.data_ptr(), x.shape[1], w.data_ptr(), w.numel())
+                                        for x, w in zip(self.xs, self.wss)])
+        L.qg_prepare_rows_set(acts, len(self.xs), self.rows, sh)
 
     def alg_bytes_gemv(self):
         """Algorithmic bytes of the GEMV launch: weights + activations + fp32 outputs.
@@ -225,10 +344,127 @@ class LayerSet:
         return self.wbytes + out + sum(self.rows * k * act for _, _n, k in self.layer)
 
 
+def q8_alg_bytes(q, fmt, n, k, rows, fused):
+    """Algorithmic bytes of one q8-lane GEMV launch: the image, the activation rows (fp32 when quantized inside
+    the launch, else q8 codes + fp32 scales (+ int32 code sums for Q4_0)), the fp32 outputs."""
+    act = 4.0 if fused else 1.0 + 4.0 / 32 + (4.0 / 32 if fmt == q.Q4_0 else 0.0)
+    return q.image_bytes(fmt, n, k) + rows * k * act + rows * n * 4
+
+
+class LmHead:
+    """The LM head 128256 x 4096 in one lane: two weight copies, activation rows, prepared workspaces."""
+
+    def __init__(self, torch, q, synth, lane):
+        self.torch, self.q, self.lane = torch, q, lane
+        self.fmt = {"q8_0": q.Q8_0, "q4_0": q.Q4_0, "f16": q.F16, "fp8": q.FP8}[lane]
+        self.imgs = []
+        for c in range(2):
+            w = synth.gaussian((LM_N, LM_K), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
+            self.imgs.append(q.f16_image(w.half()) if lane == "f16" else q.quantize_weights(self.fmt, w))
+            del w
+        self.ptrs = [t.data_ptr() for t in self.imgs]
+        self.wbytes = 2 * LM_N * LM_K if lane == "f16" else q.image_bytes(self.fmt, LM_N, LM_K)
+        self.rows = {}
+        self.keep = []
+
+    def at(self, synth, rows):
+        """(x, y, ws) for `rows` rows; ws is prepared (q8 pair/row order or FP8 groups) for the kernel-alone form."""
+        if rows not in self.rows:
+            torch, q = self.torch, self.q
+            x = synth.gaussian((rows, LM_K), 1.0, synth.tensor_seed(4, 32 + rows), device="cuda")
+            y = torch.empty((rows, LM_N), device="cuda")
+            if self.fmt == q.FP8:
+                ws = q.prepare_fp8(x)
+            elif self.fmt in (q.Q8_0, q.Q4_0):
+                ws = q.prepare_rows(x)
+            else:
+                ws = None
+            self.rows[rows] = (x, y, ws)
+        return self.rows[rows]
+
+    def call(self, L, sh, synth, rows):
+        """The public entry point at `rows` rows (fp32 rows in; quantization included)."""
+        x, y, _ = self.at(synth, rows)
+        q, p = self.q, self.ptrs
+        xp, yp = x.data_ptr(), y.data_ptr()
+        if self.fmt == q.F16:
+            return lambda i: L.gemv_f16(p[i % 2], LM_N, LM_K, xp, rows, yp, sh)
+        nb = q.fp8_workspace_bytes(rows, LM_K) if self.fmt == q.FP8 else q.workspace_bytes(rows, LM_K)
+        ws = self.torch.empty(max(1, nb), dtype=self.torch.uint8, device="cuda")
+        self.keep.append(ws)
+        wp, wn = ws.data_ptr(), ws.numel()
+        if self.fmt == q.FP8:
+            return lambda i: L.qgemv_fp8(p[i % 2], LM_N, LM_K, xp, rows, yp, wp, wn, sh)
+        fn = L.qgemv_q8_0 if self.fmt == q.Q8_0 else L.qgemv_q4_0
+        return lambda i: fn(p[i % 2], LM_N, LM_K, xp, rows, yp, wp, wn, sh)
+
+    def kernel_alone(self, L, sh, synth, rows):
+        """(fn, kernel name, algorithmic bytes): one GEMV launch per call.  At rows the library quantizes inside
+        the launch (q8 lane, 1-2 rows), and in the f16 lane, that is the entry point itself; otherwise the GEMV
+        on rows prepared once."""
+        q = self.q
+        x, y, ws = self.at(synth, rows)
+        p, yp = self.ptrs, y.data_ptr()
+        if self.fmt == q.F16:
+            return (self.call(L, sh, synth, rows), "gemv_f16_kernel",
+                    2 * LM_N * LM_K + rows * LM_K * 4 + rows * LM_N * 4)
+        if self.fmt == q.FP8:
+            wp, wn = ws.data_ptr(), ws.numel()
+            alg = self.wbytes + rows * LM_K * (1 + 4 / 128) + rows * LM_N * 4
+            return (lambda i: L.qgemv_fp8_prepared(p[i % 2], LM_N, LM_K, wp, wn, rows, yp, sh)), "gemv_fp8_kernel", alg
+        if rows <= q.FUSED_ROWS:
+            return self.call(L, sh, synth, rows), "rl_set_kernel", q8_alg_bytes(q, self.fmt, LM_N, LM_K, rows, True)
+        wp, wn = ws.data_ptr(), ws.numel()
+        return ((lambda i: L.qgemv_prepared(self.fmt, p[i % 2], LM_N, LM_K, wp, wn, rows, yp, sh)), "mp_set_kernel",
+                q8_alg_bytes(q, self.fmt, LM_N, LM_K, rows, False))
+
+
+# ---------------------------------------------------------- read ceiling ---
+def read_ceiling(torch, L, sh, stream, timer, sizes):
+    """Best bare-read bandwidth (qg_read_probe) for each byte count, over grids and loads in flight; sizes smaller
+    than 1 GiB rotate through slices of a 1 GiB buffer so that they stream from HBM."""
+    buf = torch.empty(max(1 << 30, 2 * max(sizes)) + 4096, dtype=torch.uint8, device="cuda")
+    base = (buf.data_ptr() + 255) // 256 * 256
+    sink = torch.empty(65536 * 8, dtype=torch.int32, device="cuda")
+    sp = sink.data_ptr()
+    out = []
+    for nbytes in sizes:
+        nb = nbytes // 256 * 256
+        slices = max(1, (buf.numel() - 4096) // nb)
+        cands = []
+        for grid in (256, 512, 1024, 2048, 4096):
+            for la in (2, 4, 8):
+                fn = lambda i, g=grid, la=la: L.qg_read_probe(C.c_void_p(base + (i % slices) * nb), nb, g, la, sp, sh)
+                ms = time_reps(torch, timer, stream, fn, 20, reps=1)[0]
+                cands.append((ms, grid, la))
+        _, grid, la = min(cands)
+        fn = lambda i: L.qg_read_probe(C.c_void_p(base + (i % slices) * nb), nb, grid, la, sp, sh)
+        reps = time_reps(torch, timer, stream, fn, 40)
+        med = statistics.median(reps)
+        out.append({"bytes": int(nb), "best_gbps": round(nb / (med * 1e-3) / 1e9, 1),
+                    "pct_hbm": round(100 * nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1), "grid": grid,
+                    "loads_in_flight": la, **summarize(reps), "rotating_slices": int(slices)})
+    del buf, sink
+    return {"kernel": "read_probe_kernel (qg_read_probe): 16-byte non-temporal loads, one contiguous range per "
+                      "512-thread workgroup; best of grids 256-4096 x 2/4/8 loads in flight", "sizes": out}
+
+
+def ceiling_for(rc, nbytes):
+    """The probe figure measured on the nearest byte count."""
+    if not rc:
+        return None
+    best = min(rc["sizes"], key=lambda e: abs(math.log(e["bytes"] / nbytes)))
+    return best["best_gbps"]
+
+
+# -------------------------------------------------------------------- main ---
 def main():
     args = parse()
     if args.traffic:
         reduce_traffic(*args.traffic)
+        return
+    if args.counters:
+        reduce_counters(*args.counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -250,25 +486,33 @@ def main():
     if args.profile:
         profile_one(args, torch, q, synth, L, sh, stream, timer)
         return
+    t_start = time.time()
+
+    def note(msg):
+        print(f"[bench {time.time() - t_start:6.1f}s] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------- ceilings ---
+    rc = read_ceiling(torch, L, sh, stream, timer,
+                      [q.image_bytes(q.Q8_0, LM_N, LM_K), sum(q.image_bytes(q.Q8_0, n, k) for _, n, k in LAYER_1B),
+                       sum(q.image_bytes(q.Q4_0, n, k) for _, n, k in LAYER_3B)])
+    note(f"read ceiling {[(e['bytes'], e['best_gbps']) for e in rc['sizes']]}")
 
     # ------------------------------------------------------------ headline ---
-    rows = 1
-    t_setup = time.time()
-    layer = LayerSet(torch, q, synth, LAYER_1B, q.Q8_0, 1, rows)
+    head = LmHead(torch, q, synth, "q8_0")
+    calls = {r: head.call(L, sh, synth, r) for r in HEAD_ROWS}
     torch.cuda.synchronize()
-    print(f"[bench] 1B layer Q8_0: {layer.copies} copies x {layer.wbytes} B ready in {time.time() - t_setup:.1f}s",
-          file=sys.stderr, flush=True)
+    note("LM head Q8_0 ready")
 
     def step(i):
-        L.qgemv_set_rows(q.Q8_0, layer.projs[i % layer.copies], 7, rows, sh)
+        for j, r in enumerate(HEAD_ROWS):
+            calls[r](3 * i + j)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    timer.hold(max(20.0, K * 0.08))
+    timer.hold(max(20.0, K * 0.4))
     start.record(stream)
     h0 = time.perf_counter()
     for i in range(K):
@@ -276,20 +520,31 @@ def main():
     host_ms = (time.perf_counter() - h0) * 1e3
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
-    # At one row the step is one launch of the GEMV kernel (quantization fused), so the events around the
-    # K back-to-back steps on the kernel's own stream also give its average launch duration.
-    assert layer.launches == 1
-    gemv_avg_ms = ms_per_step
-    # a host-side check that the layer outputs are finite (no silent garbage)
-    assert all(bool(torch.isfinite(y).all()) for y in layer.ys)
+    ms_per_step = start.elapsed_time(end) / K
+    for r in HEAD_ROWS:
+        assert bool(torch.isfinite(head.at(synth, r)[1]).all()), f"non-finite LM-head output at rows={r}"
+    step_bytes = head.wbytes * len(HEAD_ROWS)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    note(f"headline step {ms_per_step * 1e3:.1f} us")
 
-    value = layer.wbytes / (ms_per_step * 1e-3) / 1e9
-    alg = layer.alg_bytes_gemv()
-    achieved = alg / (gemv_avg_ms * 1e-3) / 1e9
-    kname = "rl_set_kernel<Q8_0, rows 1, fused quantization>"
-    traffic = read_traffic("rl_set_kernel", "llama1b-layer-q8_0-rows1")
+    # the step in five reps (median, slowest), and each row count's GEMV kernel alone
+    step_reps = time_reps(torch, timer, stream, step, max(10, K // 3))
+    ceil_lm = ceiling_for(rc, head.wbytes)
+    by_rows, alg_sum, us_sum = [], 0.0, 0.0
+    for r in HEAD_ROWS:
+        fn, kname, alg = head.kernel_alone(L, sh, synth, r)
+        reps = time_reps(torch, timer, stream, fn, 40)
+        wl = f"lm-head-q8_0-rows{r}"
+        e = {"rows": r, **roofline_entry(kname, alg, reps, read_traffic(kname, wl), ceil_lm, read_busy(kname, wl))}
+        e["weight_gbps"] = round(head.wbytes / (statistics.median(reps) * 1e-3) / 1e9, 1)
+        e["pct_hbm_weight"] = round(100 * e["weight_gbps"] / HBM_PEAK_GBPS, 1)
+        e["entry_point_us"] = summarize(time_reps(torch, timer, stream, calls[r], 40))
+        by_rows.append(e)
+        alg_sum += alg
+        us_sum += statistics.median(reps) * 1e3
+    note("headline rooflines done")
+    achieved = alg_sum / (us_sum * 1e-6) / 1e9
+    traffic = sum(e["traffic"] for e in by_rows) if all(e["traffic"] for e in by_rows) else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -304,23 +559,37 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "pct_hbm_roofline": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "config": {"workload": "llama-3.2-1b-shaped decode layer, Q8_0 weights, q8 activations",
-                   "rows": rows, "projections": [f"{nm} {n}x{k}" for nm, n, k in LAYER_1B],
-                   "weight_bytes_per_step": layer.wbytes, "rotation_copies": layer.copies,
-                   "launches_per_step": layer.launches, "parallelism": "single GPU"},
-        "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": int(alg), "avg_launch_us": round(gemv_avg_ms * 1e3, 3)},
+        "step_reps": summarize(step_reps),
+        "config": {"workload": "lm head 128256x4096, Q8_0 weights, q8 activations, at 1, 8 and 16 rows",
+                   "rows": list(HEAD_ROWS), "calls_per_step": len(HEAD_ROWS),
+                   "weight_bytes_per_call": head.wbytes, "weight_bytes_per_step": step_bytes,
+                   "rotation_copies": 2, "entry_point": "qgemv_q8_0 (fp32 rows in, quantization included)",
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "rl_set_kernel (1 row, quantization fused) + mp_set_kernel (8 and 16 rows, on "
+                               "prepared rows): the step's GEMV launches",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "alg_bytes_per_step": int(alg_sum), "kernel_us_per_step": round(us_sum, 3),
+                     "pct_of_read_ceiling": round(100 * achieved / ceil_lm, 1) if ceil_lm else None,
+                     "by_rows": by_rows},
+        "read_ceiling": rc,
         "host_enqueue_ms": round(host_ms, 3),
     }
+    del calls
+
+    # --------------------------------------------------------- secondary ---
+    result["secondary"] = secondary(torch, q, synth, L, sh, stream, timer, rc, note)
+    del head
 
     # ---------------------------------------------------------- CPU oracle ---
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(torch, synth, layer)
+        result["cpu_baseline"] = cpu_baseline(synth)
+        note("cpu baseline done")
 
     # --------------------------------------------------------------- sweep ---
     if not args.no_sweep:
-        result["sweep"] = sweep(torch, q, synth, L, sh, stream, timer, layer)
+        result["sweep"] = sweep(torch, q, synth, L, sh, stream, timer)
+        note("sweep done")
 
     line = json.dumps(result)
     print(line, flush=True)
@@ -329,167 +598,205 @@ def main():
             f.write(line + "\n")
 
 
-# ----------------------------------------------------------------- oracle ---
-def cpu_baseline(torch, synth, layer):
-    """The C oracle on the headline layer (copy 0, same rows), on the host's cores, for about 10 s."""
-    import oracle as O
-
-    threads = max(1, min(16, os.cpu_count() or 1))
-    blocks = []
-    for i, (_, n, k) in enumerate(LAYER_1B):
-        w = synth.gaussian((n, k), 0.02, synth.tensor_seed(1, i, 0), device="cuda").cpu().numpy()
-        blocks.append(O.quantize_weights(O.Q8_0, w))
-    xs = [x.cpu().numpy() for x in layer.xs]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for i, (name, n, k) in enumerate(LAYER_1B):
-            O.gemv_q(O.Q8_0, blocks[i], n, k, xs[LAYER_SRC.get(name, 0)], threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= 10.0:
-            break
-    return {"value": round(layer.wbytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "ms_per_step": round(el / reps * 1e3, 3),
-            "sample": f"the headline layer's 7 Q8_0 projections at rows={layer.rows}, {reps} reps in {el:.1f}s"}
-
-
-# ------------------------------------------------------------------ sweep ---
-def time_calls(torch, timer, stream, fn, iters):
-    for i in range(min(iters, 5)):
-        fn(i)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    timer.hold(max(10.0, iters * 0.1))
-    a.record(stream)
-    for i in range(iters):
-        fn(i)
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters
-
-
-def entry(workload, lane, rows, wbytes, ms, launches):
-    gbps = wbytes / (ms * 1e-3) / 1e9
-    return {"workload": workload, "lane": lane, "rows": rows, "weight_bytes": int(wbytes), "launches": launches,
-            "us_per_call": round(ms * 1e3, 3), "weight_gbps": round(gbps, 1),
-            "pct_hbm": round(100 * gbps / HBM_PEAK_GBPS, 1)}
-
-
-def sweep(torch, q, synth, L, sh, stream, timer, layer1b):
+# ------------------------------------------------------------ secondary ---
+def secondary(torch, q, synth, L, sh, stream, timer, rc, note):
     out = []
-    ROWSW = [1, 2, 4, 8, 9, 16]
-    t0 = time.time()
 
-    # Q8_0 1024x1024, one GEMV (quantize + GEMV launches)
+    # Llama-3.2-1B-shaped Q8_0 layer at one row (one launch: quantization fused)
+    ls = LayerSet(torch, q, synth, LAYER_1B, q.Q8_0, 1, 1)
+    out.append(layer_entry(torch, q, L, sh, stream, timer, rc, ls, "llama-3.2-1b-shaped decode layer", "q8_0", 1,
+                           "llama1b-layer-q8_0"))
+    del ls
+    note("1B layer done")
+
+    # Llama-3.2-3B-shaped Q4_0 layer at 1/2/4/8 rows
+    ls = LayerSet(torch, q, synth, LAYER_3B, q.Q4_0, 2, 1)
+    for rows in (1, 2, 4, 8):
+        ls.set_rows(rows, synth, 2)
+        out.append(layer_entry(torch, q, L, sh, stream, timer, rc, ls, "llama-3.2-3b-shaped decode layer", "q4_0",
+                               rows, "llama3b-layer-q4_0"))
+    del ls
+    note("3B layer done")
+
+    # LM head, the other lanes at 1/8/16 rows (f16: the workload's second lane; Q4_0: the metric's other format)
+    for lane in ("f16", "q4_0"):
+        h = LmHead(torch, q, synth, lane)
+        for rows in HEAD_ROWS:
+            fn, kname, alg = h.kernel_alone(L, sh, synth, rows)
+            reps = time_reps(torch, timer, stream, fn, 20)
+            wl = f"lm-head-{lane}-rows{rows}"
+            e = {"workload": "lm head 128256x4096", "lane": lane, "rows": rows, "weight_bytes": int(h.wbytes),
+                 "weight_gbps": round(h.wbytes / (statistics.median(reps) * 1e-3) / 1e9, 1),
+                 "roofline": roofline_entry(kname, alg, reps, read_traffic(kname, wl), ceiling_for(rc, h.wbytes),
+                                            read_busy(kname, wl))}
+            e["pct_hbm_weight"] = round(100 * e["weight_gbps"] / HBM_PEAK_GBPS, 1)
+            if lane != "f16" and rows > q.FUSED_ROWS:
+                e["entry_point_us"] = summarize(time_reps(torch, timer, stream, h.call(L, sh, synth, rows), 20))
+            out.append(e)
+        del h
+        note(f"LM head {lane} done")
+
+    # Q8_0 1024 x 1024 at one row (launch-bound: 1.1 MB), rotating copies of >= 1 GiB
     n = k = 1024
     wb = q.image_bytes(q.Q8_0, n, k)
     copies = math.ceil((1 << 30) / wb)
     big = synth.gaussian((copies * n, k), 0.02, synth.tensor_seed(0, 0), device="cuda")
     imgs = [q.quantize_weights(q.Q8_0, big[c * n:(c + 1) * n]) for c in range(copies)]
     del big
-    for rows in ROWSW:
-        x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(0, 32 + rows), device="cuda")
-        y = torch.empty((rows, n), device="cuda")
-        ws = q.empty_ws(rows, k)
-        xp, yp, wp, wn = x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel()
-        ptrs = [im.data_ptr() for im in imgs]
-        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_q8_0(ptrs[i % copies], n, k, xp, rows, yp, wp, wn, sh),
-                        400)
-        out.append(entry("q8_0 1024x1024", "q8_0", rows, wb, ms, 1 if rows <= q.FUSED_ROWS else 2))
+    x = synth.gaussian((1, k), 1.0, synth.tensor_seed(0, 33), device="cuda")
+    y = torch.empty((1, n), device="cuda")
+    ws = q.empty_ws(1, k)
+    ptrs = [im.data_ptr() for im in imgs]
+    reps = time_reps(torch, timer, stream,
+                     lambda i: L.qgemv_q8_0(ptrs[i % copies], n, k, x.data_ptr(), 1, y.data_ptr(), ws.data_ptr(),
+                                            ws.numel(), sh), 200)
+    out.append({"workload": "q8_0 gemv 1024x1024", "lane": "q8_0", "rows": 1, "weight_bytes": int(wb),
+                "launches": 1, **summarize(reps),
+                "weight_gbps": round(wb / (statistics.median(reps) * 1e-3) / 1e9, 1),
+                "roofline": roofline_entry("rl_set_kernel", q8_alg_bytes(q, q.Q8_0, n, k, 1, True), reps),
+                "note": "1.1 MB per call: a launch-bound size, timed back to back"})
     del imgs
-    print(f"[bench] sweep 1024x1024 done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    note("1024x1024 done")
 
-    # residual add + RMS norm + A1 in one launch (qg_add_rmsnorm_prepare), next to A1 alone (qg_prepare_rows)
-    # of the same rows; bytes: x, residual and gamma read, h and the workspace written
-    for k in (2048, 8192):
-        gamma = (1.0 + synth.gaussian((k,), 0.1, synth.tensor_seed(6, 2), device="cuda")).contiguous()
-        for rows in (1, 8, 16):
-            x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(6, 32 + rows), device="cuda")
-            res = synth.gaussian((rows, k), 0.5, synth.tensor_seed(6, 48 + rows), device="cuda")
-            h = torch.empty_like(x)
-            ws = q.empty_ws(rows, k)
-            xp, rp, gp, hp, wp, wn = x.data_ptr(), res.data_ptr(), gamma.data_ptr(), h.data_ptr(), ws.data_ptr(), ws.numel()
-            nb = 4 * rows * k * 3 + 4 * k + q.workspace_bytes(rows, k)
-            ms = time_calls(torch, timer, stream,
-                            lambda i: L.qg_add_rmsnorm_prepare(xp, rp, gp, 1e-5, rows, k, hp, None, wp, wn, sh), 400)
-            e = entry(f"add + rmsnorm + q8 prepare, k={k}", "fp32 -> q8", rows, nb, ms, 1)
-            e["note"] = "weight_bytes here: activation bytes moved"
-            out.append(e)
-            ms = time_calls(torch, timer, stream, lambda i: L.qg_prepare_rows(xp, rows, k, wp, wn, sh), 400)
-            e = entry(f"q8 prepare alone, k={k}", "fp32 -> q8", rows, 4 * rows * k + q.workspace_bytes(rows, k), ms, 1)
-            e["note"] = "weight_bytes here: activation bytes moved"
-            out.append(e)
-    print(f"[bench] sweep norm done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    # routed MoE step at 1/8/9/16 rows (six launches; five at 1-2 rows)
+    W = moe_weights(torch, q, synth)
+    for rows in (1, 8, 9, 16):
+        one, expert = moe_call(torch, q, synth, L, sh, W, rows)
+        reps = time_reps(torch, timer, stream, one, 64)
+        u = moe_unique(torch, one, expert)
+        wb = 2 * MOE_E * MOE_HIDDEN + u * (W["gu_b"] + W["dn_b"])
+        med = statistics.median(reps)
+        out.append({"workload": "routed moe step (256 experts top-8 + shared, hidden 2048, ffn 512)",
+                    "lane": "q8_0 + f16 router", "rows": rows, "launches": 5 if rows <= 2 else 6,
+                    "unique_experts": round(u, 2), "weight_bytes": int(wb), **summarize(reps),
+                    "weight_gbps": round(wb / (med * 1e-3) / 1e9, 1),
+                    "pct_hbm_weight": round(100 * wb / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)})
+    del W
+    note("moe done")
+    return out
 
+
+def layer_entry(torch, q, L, sh, stream, timer, rc, ls, name, lane, rows, wl_key):
+    """A decode layer's seven projections at `rows` rows: the set (ms per projection set, quantization
+    included) and its GEMV kernel's roofline (the set launch itself at 1-2 rows; otherwise the GEMV on rows
+    prepared once)."""
+    set_reps = time_reps(torch, timer, stream,
+                         lambda i: L.qgemv_set_rows(ls.fmt, ls.projs[i % ls.copies], 7, rows, sh), 100)
+    if ls.prepared is None:
+        kreps, kname = set_reps, "rl_set_kernel"
+    else:
+        ls.prepare(L, sh)
+        kreps = time_reps(torch, timer, stream,
+                          lambda i: L.qgemv_set(ls.fmt, ls.prepared[i % ls.copies], 7, rows, sh), 100)
+        kname = "mp_set_kernel"
+    wl = f"{wl_key}-rows{rows}"
+    med = statistics.median(set_reps)
+    return {"workload": f"{name} (7 projections)", "lane": lane, "rows": rows, "weight_bytes": int(ls.wbytes),
+            "launches": ls.launches, "ms_per_set": round(med, 5), "set_reps": summarize(set_reps),
+            "weight_gbps": round(ls.wbytes / (med * 1e-3) / 1e9, 1),
+            "pct_hbm_weight": round(100 * ls.wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+            "rotation_copies": ls.copies,
+            "roofline": roofline_entry(kname, ls.alg_bytes_gemv(), kreps, read_traffic(kname, wl),
+                                       ceiling_for(rc, ls.wbytes), read_busy(kname, wl))}
+
+
+# ----------------------------------------------------------------- oracle ---
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, avail
+
+
+def cpu_baseline(synth):
+    """The C oracle on a bounded slice of the headline workload: the first 16384 of the LM head's 128256 output
+    rows (4096 columns, Q8_0 blocks from the oracle's own quantizer) at 1, 8 and 16 activation rows, the three
+    calls as one step; five reps on all the cores this process may use (at most 16, the host share of one GPU)
+    and five on one core.  GB/s counts the slice's weight bytes, as the GPU figure counts the whole image's."""
+    import numpy as np
+
+    import oracle as O
+
+    model, nproc, avail = cpu_info()
+    threads = max(1, min(16, avail))
+    ns = 16384
+    w = synth.gaussian((ns, LM_K), 0.02, synth.tensor_seed(4, 0, 0)).numpy()
+    blocks = O.quantize_weights(O.Q8_0, w)
+    del w
+    xs = {r: synth.gaussian((r, LM_K), 1.0, synth.tensor_seed(4, 32 + r)).numpy() for r in HEAD_ROWS}
+    sbytes = ns * LM_K // 32 * 34
+
+    def run(th):
+        reps = []
+        for _ in range(REPS):
+            t0 = time.perf_counter()
+            for r in HEAD_ROWS:
+                O.gemv_q(O.Q8_0, blocks, ns, LM_K, xs[r], threads=th)
+            reps.append(time.perf_counter() - t0)
+        med = statistics.median(reps)
+        return {"value": round(len(HEAD_ROWS) * sbytes / med / 1e9, 3), "unit": "GB/s", "cores": th,
+                "ms_per_step": round(med * 1e3, 2), "slowest_ms": round(max(reps) * 1e3, 2)}
+
+    allc = run(threads)
+    one = run(1)
+    assert np.isfinite(O.gemv_q(O.Q8_0, blocks, ns, LM_K, xs[1], threads=threads)).all()
+    return {**allc, "kind": "oracle",
+            "sample": f"LM head rows 0..{ns - 1} of {LM_N} (x 4096, Q8_0, {sbytes} weight bytes) at rows 1, 8 and 16 "
+                      f"per step; median of {REPS} reps",
+            "single_core": one, "cpu_model": model, "nproc": nproc, "cores_available": avail}
+
+
+# ------------------------------------------------------------------ sweep ---
+def entry(workload, lane, rows, wbytes, ms_reps, launches):
+    ms = statistics.median(ms_reps)
+    gbps = wbytes / (ms * 1e-3) / 1e9
+    return {"workload": workload, "lane": lane, "rows": rows, "weight_bytes": int(wbytes), "launches": launches,
+            "us_per_call": round(ms * 1e3, 3), "slowest_rep_us": round(max(ms_reps) * 1e3, 3),
+            "weight_gbps": round(gbps, 1), "pct_hbm": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+
+
+def sweep(torch, q, synth, L, sh, stream, timer):
+    out = []
+    ROWSW = [1, 2, 4, 8, 9, 16]
     # decode layers (set launch): 1B Q8_0 and 3B Q4_0
-    for lname, lay, fmt, wl, lane, obj in (("llama-3.2-1b layer", LAYER_1B, q.Q8_0, 1, "q8_0", layer1b),
-                                           ("llama-3.2-3b layer", LAYER_3B, q.Q4_0, 2, "q4_0", None)):
-        ls = obj or LayerSet(torch, q, synth, lay, fmt, wl, 1)
+    for lname, lay, fmt, wl, lane in (("llama-3.2-1b layer", LAYER_1B, q.Q8_0, 1, "q8_0"),
+                                      ("llama-3.2-3b layer", LAYER_3B, q.Q4_0, 2, "q4_0")):
+        ls = LayerSet(torch, q, synth, lay, fmt, wl, 1)
         for rows in ROWSW:
             ls.set_rows(rows, synth, wl)
-
-            def one(i, ls=ls, rows=rows, fmt=fmt):
-                L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh)
-
-            ms = time_calls(torch, timer, stream, one, 200)
-            out.append(entry(f"{lname} (7 projections)", lane, rows, ls.wbytes, ms, ls.launches))
-            if rows > q.FUSED_ROWS:
-                # the GEMV launch alone, on rows quantized once beforehand
-                acts = ctypes_arr(q._Act, [q._Act(x.data_ptr(), x.shape[1], w.data_ptr(), w.numel())
-                                           for x, w in zip(ls.xs, ls.wss)])
-                L.qg_prepare_rows_set(acts, len(ls.xs), rows, sh)
-                pre = [ctypes_arr(q._Proj, [q._Proj(ls.imgs[c][i].data_ptr(), n_, k_,
-                                                    ls.wss[LAYER_SRC.get(nm, 0)].data_ptr(),
-                                                    ls.wss[LAYER_SRC.get(nm, 0)].numel(), ls.ys[i].data_ptr())
-                                            for i, (nm, n_, k_) in enumerate(ls.layer)]) for c in range(ls.copies)]
-
-                def gemv(i, pre=pre, rows=rows, fmt=fmt):
-                    L.qgemv_set(fmt, pre[i % len(pre)], 7, rows, sh)
-
-                ms = time_calls(torch, timer, stream, gemv, 200)
-                out.append(entry(f"{lname} (7 projections), prepared rows", lane, rows, ls.wbytes, ms, 1))
+            reps = time_reps(torch, timer, stream,
+                             lambda i: L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh), 100)
+            out.append(entry(f"{lname} (7 projections)", lane, rows, ls.wbytes, reps, ls.launches))
+            if ls.prepared is not None:
+                ls.prepare(L, sh)
+                reps = time_reps(torch, timer, stream,
+                                 lambda i: L.qgemv_set(fmt, ls.prepared[i % ls.copies], 7, rows, sh), 100)
+                out.append(entry(f"{lname} (7 projections), prepared rows", lane, rows, ls.wbytes, reps, 1))
         del ls
-        print(f"[bench] sweep {lname} done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    layer1b.set_rows(1, synth, 1)
-
-    # LM head 128256 x 4096, f16, Q8_0 and FP8 (block-FP8 weights, 1 x 128 activation groups), two copies each
-    n, k = 128256, 4096
-    w16 = []
-    q8 = []
-    f8 = []
-    for c in range(2):
-        w = synth.gaussian((n, k), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
-        w16.append(q.f16_image(w.half()))
-        q8.append(q.quantize_weights(q.Q8_0, w))
-        f8.append(q.quantize_weights(q.FP8, w))
-        del w
-    f8b = q.image_bytes(q.FP8, n, k)
-    for rows in (1, 2, 4, 8, 9, 16):
-        x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(4, 32 + rows), device="cuda")
-        y = torch.empty((rows, n), device="cuda")
-        ws = q.empty_ws(rows, k)
-        xp, yp, wp, wn = x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel()
-        p16 = [t.data_ptr() for t in w16]
-        p8 = [t.data_ptr() for t in q8]
-        pf = [t.data_ptr() for t in f8]
-        ms = time_calls(torch, timer, stream, lambda i: L.gemv_f16(p16[i % 2], n, k, xp, rows, yp, sh), 40)
-        out.append(entry("lm head 128256x4096", "f16", rows, 2 * n * k, ms, 1))
-        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_q8_0(p8[i % 2], n, k, xp, rows, yp, wp, wn, sh), 40)
-        out.append(entry("lm head 128256x4096", "q8_0", rows, q.image_bytes(q.Q8_0, n, k), ms,
-                         1 if rows <= q.FUSED_ROWS else 2))
-        wsf = q.prepare_fp8(x)
-        fp, fn = wsf.data_ptr(), wsf.numel()
-        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_fp8(pf[i % 2], n, k, xp, rows, yp, fp, fn, sh), 40)
-        out.append(entry("lm head 128256x4096", "fp8", rows, f8b, ms, 2))
-        ms = time_calls(torch, timer, stream, lambda i: L.qgemv_fp8_prepared(pf[i % 2], n, k, fp, fn, rows, yp, sh), 40)
-        out.append(entry("lm head 128256x4096, prepared rows", "fp8", rows, f8b, ms, 1))
-    del w16, q8, f8
-    print(f"[bench] sweep lm head done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-
+    # LM head in every lane
+    for lane in ("q8_0", "q4_0", "f16", "fp8"):
+        h = LmHead(torch, q, synth, lane)
+        for rows in ROWSW:
+            reps = time_reps(torch, timer, stream, h.call(L, sh, synth, rows), 20)
+            launches = 1 if lane == "f16" or (lane in ("q8_0", "q4_0") and rows <= q.FUSED_ROWS) else 2
+            out.append(entry("lm head 128256x4096", lane, rows, h.wbytes, reps, launches))
+            if launches == 2:
+                fn, _, _ = h.kernel_alone(L, sh, synth, rows)
+                out.append(entry("lm head 128256x4096, prepared rows", lane, rows, h.wbytes,
+                                 time_reps(torch, timer, stream, fn, 20), 1))
+        del h
     out.extend(moe_sweep(torch, q, synth, L, sh, stream, timer))
-    print(f"[bench] sweep moe done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     out.extend(grouped_sweep(torch, q, synth, L, sh, stream, timer))
-    print(f"[bench] sweep grouped done {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     return out
 
 
@@ -498,7 +805,8 @@ MOE_HIDDEN, MOE_FFN, MOE_E, MOE_TOPK = 2048, 512, 256, 8
 
 def moe_weights(torch, q, synth, copies=2, fmt=None):
     """Two copies of the routed MoE's 256 experts (Q8_0, or fmt) plus the shared one (index 256), stacked, and
-    the f16 router image."""
+    the f16 router image.  Each copy's gate/up and down weights are drawn as one tall matrix each (one
+    generator call), then quantized expert by expert into the stacked images."""
     hidden, ffn, E = MOE_HIDDEN, MOE_FFN, MOE_E
     fmt = q.Q8_0 if fmt is None else fmt
     nimg = E + 1
@@ -508,11 +816,13 @@ def moe_weights(torch, q, synth, copies=2, fmt=None):
     for c in range(copies):
         gu = torch.empty(nimg * gu_b, dtype=torch.uint8, device="cuda")
         dn = torch.empty(nimg * dn_b, dtype=torch.uint8, device="cuda")
+        w = synth.gaussian((nimg * 2 * ffn, hidden), 0.02, synth.tensor_seed(3, 1, c), device="cuda")
         for e in range(nimg):
-            w = synth.gaussian((2 * ffn, hidden), 0.02, synth.tensor_seed(3, 1 + 3 * e, c), device="cuda")
-            q.quantize_weights(fmt, w, gu[e * gu_b:(e + 1) * gu_b])
-            w = synth.gaussian((hidden, ffn), 0.02, synth.tensor_seed(3, 3 + 3 * e, c), device="cuda")
-            q.quantize_weights(fmt, w, dn[e * dn_b:(e + 1) * dn_b])
+            q.quantize_weights(fmt, w[e * 2 * ffn:(e + 1) * 2 * ffn], gu[e * gu_b:(e + 1) * gu_b])
+        w = synth.gaussian((nimg * hidden, ffn), 0.02, synth.tensor_seed(3, 3, c), device="cuda")
+        for e in range(nimg):
+            q.quantize_weights(fmt, w[e * hidden:(e + 1) * hidden], dn[e * dn_b:(e + 1) * dn_b])
+        del w
         gus.append(gu)
         dns.append(dn)
     router = q.f16_image(synth.gaussian((E, hidden), 0.02, synth.tensor_seed(3, 0), device="cuda").half())
@@ -543,29 +853,32 @@ def moe_call(torch, q, synth, L, sh, W, rows, nx=64):
 
     # keep the inputs alive with the closure's owner
     one.keep = (xs, logits, expert, wgt, y, ws)
+    one.nx = nx
     return one, expert
 
 
+def moe_unique(torch, one, expert):
+    """Average count of distinct experts (the shared one included) that a call touches, over the inputs."""
+    uniq = []
+    for s in range(one.nx):
+        one(s)
+        torch.cuda.synchronize()
+        uniq.append(len(set(expert.cpu().tolist())))
+    return sum(uniq) / len(uniq)
+
+
 def moe_sweep(torch, q, synth, L, sh, stream, timer):
-    """Routed MoE step (qg_moe_step): router f16 GEMV, top-8 routing + plan, grouped gate/up, SwiGLU + q8,
-    grouped down, combine -- six launches, five at 1-2 rows (SwiGLU + q8 inside the down launch)."""
+    """Routed MoE step (qg_moe_step) in the Q8_0 and FP8 lanes at 1/8/9/16 rows."""
     out = []
     for fmt, lane in ((q.Q8_0, "q8_0 + f16 router"), (q.FP8, "fp8 + f16 router")):
         W = moe_weights(torch, q, synth, fmt=fmt)
         for rows in (1, 8, 9, 16):
-            nx = 64
-            one, expert = moe_call(torch, q, synth, L, sh, W, rows, nx)
-            ms = time_calls(torch, timer, stream, one, 128)
-            # weight bytes actually streamed: router + every touched expert (the shared one included)
-            uniq = []
-            for s in range(nx):
-                one(s)
-                torch.cuda.synchronize()
-                uniq.append(len(set(expert.cpu().tolist())))
-            u = sum(uniq) / nx
+            one, expert = moe_call(torch, q, synth, L, sh, W, rows)
+            reps = time_reps(torch, timer, stream, one, 64)
+            u = moe_unique(torch, one, expert)
             wb = 2 * MOE_E * MOE_HIDDEN + u * (W["gu_b"] + W["dn_b"])
             launches = 6 if fmt == q.FP8 else (5 if rows <= 2 else 6)
-            e = entry("routed moe step (256 experts top-8 + shared)", lane, rows, wb, ms, launches)
+            e = entry("routed moe step (256 experts top-8 + shared)", lane, rows, wb, reps, launches)
             e["unique_experts"] = round(u, 2)
             out.append(e)
         del W
@@ -585,15 +898,16 @@ def grouped_sweep(torch, q, synth, L, sh, stream, timer):
         imgs = []
         for c in range(2):
             buf = torch.empty((E + 1) * eb, dtype=torch.uint8, device="cuda")
+            w = synth.gaussian(((E + 1) * n, k), 0.02, synth.tensor_seed(8, 0, c), device="cuda")
             for e in range(E + 1):
-                w = synth.gaussian((n, k), 0.02, synth.tensor_seed(8, e, c), device="cuda")
-                q.quantize_weights(fmt, w, buf[e * eb:(e + 1) * eb])
+                q.quantize_weights(fmt, w[e * n:(e + 1) * n], buf[e * eb:(e + 1) * eb])
+            del w
             imgs.append(buf)
         for rows in (1, 8, 16):
             m = rows * (topk + 1)
             rng = np.random.default_rng(1000 + rows)
             routes = []
-            for r_ in range(nx):
+            for _ in range(nx):
                 ex = np.concatenate([np.concatenate([rng.choice(E, topk, replace=False), [E]]) for _ in range(rows)])
                 routes.append(torch.from_numpy(ex.astype(np.int32)).cuda())
             xi = torch.from_numpy(np.repeat(np.arange(rows), topk + 1).astype(np.int32)).cuda()
@@ -612,10 +926,9 @@ def grouped_sweep(torch, q, synth, L, sh, stream, timer):
                 call(ip[i % 2], E + 1, n, k, x.data_ptr(), rows, rp[i % nx], xi.data_ptr(), m, y.data_ptr(),
                      ws.data_ptr(), ws.numel(), sh)
 
-            ms = time_calls(torch, timer, stream, one, 64)
+            reps = time_reps(torch, timer, stream, one, 64)
             u = sum(len(set(t.cpu().tolist())) for t in routes) / nx
-            e_ = entry("grouped gate/up 1024x2048, 256 experts top-8 + shared", lane, rows, u * eb, ms,
-                       3)
+            e_ = entry("grouped gate/up 1024x2048, 256 experts top-8 + shared", lane, rows, u * eb, reps, 2)
             e_["unique_experts"] = round(u, 2)
             out.append(e_)
         del imgs
@@ -623,46 +936,40 @@ def grouped_sweep(torch, q, synth, L, sh, stream, timer):
 
 
 def profile_one(args, torch, q, synth, L, sh, stream, timer):
-    """--profile WORKLOAD:ROWS: one workload of the sweep, --warmup untimed then --steps timed calls, for a
-    per-kernel profile (rocprofv3 --kernel-trace --stats, or one --pmc counter per run)."""
+    """--profile WORKLOAD:ROWS: one workload, a short warm-up then --steps timed calls, for a per-kernel profile
+    (rocprofv3 --kernel-trace --stats, or one --pmc counter set per run)."""
     wl, rows = args.profile.split(":")
     rows = int(rows)
-    n, k = 128256, 4096
-    if wl in ("lm-head-q8", "lm-head-f16", "lm-head-fp8"):
+    if wl.startswith("lm-head-"):
         lane = wl[len("lm-head-"):]
-        imgs = []
-        for c in range(2):
-            w = synth.gaussian((n, k), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
-            imgs.append(q.f16_image(w.half()) if lane == "f16" else
-                        q.quantize_weights(q.Q8_0 if lane == "q8" else q.FP8, w))
-            del w
-        x = synth.gaussian((rows, k), 1.0, synth.tensor_seed(4, 32 + rows), device="cuda")
-        y = torch.empty((rows, n), device="cuda")
-        p = [t.data_ptr() for t in imgs]
-        xp, yp = x.data_ptr(), y.data_ptr()
-        if lane == "q8":
-            ws = q.empty_ws(rows, k)
-            fn = lambda i: L.qgemv_q8_0(p[i % 2], n, k, xp, rows, yp, ws.data_ptr(), ws.numel(), sh)
-            wbytes = q.image_bytes(q.Q8_0, n, k)
-        elif lane == "f16":
-            fn = lambda i: L.gemv_f16(p[i % 2], n, k, xp, rows, yp, sh)
-            wbytes = 2 * n * k
-        else:
-            ws = q.prepare_fp8(x)
-            fn = lambda i: L.qgemv_fp8_prepared(p[i % 2], n, k, ws.data_ptr(), ws.numel(), rows, yp, sh)
-            wbytes = q.image_bytes(q.FP8, n, k)
-    elif wl in ("layer-1b", "layer-3b"):
-        lay, fmt, wid = (LAYER_1B, q.Q8_0, 1) if wl == "layer-1b" else (LAYER_3B, q.Q4_0, 2)
+        prepared = lane.endswith("-prepared")
+        lane = {"q8": "q8_0", "q4": "q4_0"}.get(lane.replace("-prepared", ""), lane.replace("-prepared", ""))
+        h = LmHead(torch, q, synth, lane)
+        fn = h.kernel_alone(L, sh, synth, rows)[0] if prepared else h.call(L, sh, synth, rows)
+        wbytes = h.wbytes
+    elif wl in ("layer-1b", "layer-3b", "layer-1b-prepared", "layer-3b-prepared"):
+        lay, fmt, wid = (LAYER_1B, q.Q8_0, 1) if wl.startswith("layer-1b") else (LAYER_3B, q.Q4_0, 2)
         ls = LayerSet(torch, q, synth, lay, fmt, wid, rows)
-        fn = lambda i: L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh)
+        if wl.endswith("-prepared") and ls.prepared is not None:
+            ls.prepare(L, sh)
+            fn = lambda i: L.qgemv_set(fmt, ls.prepared[i % ls.copies], 7, rows, sh)
+        else:
+            fn = lambda i: L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh)
         wbytes = ls.wbytes
     elif wl == "moe":
         W = moe_weights(torch, q, synth)
         fn, _ = moe_call(torch, q, synth, L, sh, W, rows)
         wbytes = None
+    elif wl == "read-probe":
+        nb = q.image_bytes(q.Q8_0, LM_N, LM_K)
+        buf = torch.empty(2 * nb + 512, dtype=torch.uint8, device="cuda")
+        base = (buf.data_ptr() + 255) // 256 * 256
+        sink = torch.empty(65536 * 8, dtype=torch.int32, device="cuda")
+        fn = lambda i: L.qg_read_probe(C.c_void_p(base + (i % 2) * nb), nb, 1024, 4, sink.data_ptr(), sh)
+        wbytes = nb
     else:
         raise SystemExit(f"--profile: unknown workload {wl!r}")
-    ms = time_calls(torch, timer, stream, fn, args.steps)
+    ms = statistics.median(time_reps(torch, timer, stream, fn, args.steps, reps=1))
     line = {"profile": wl, "rows": rows, "steps": args.steps, "us_per_call": round(ms * 1e3, 3)}
     if wbytes:
         line["weight_bytes"] = int(wbytes)

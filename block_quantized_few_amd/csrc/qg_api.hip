@@ -527,4 +527,17 @@ int qgemv_blockdots(int fmt, const void* w_image, int64_t n, int64_t k, const in
   return ok();
 }
 
+int qgemv_blockdots_pairs(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, size_t ws_bytes,
+                          int rows, int32_t* isum, qg_stream stream) {
+  if (int st = check_fmt(fmt)) return st;
+  if (rows < 3 || rows > QG_MAX_ROWS) return fail(QG_EROWS, "rows=%d outside 3..%d (pair order)", rows, QG_MAX_ROWS);
+  if (int st = check_nk(n, k)) return st;
+  if (int st = check_image(w_image, "w_image")) return st;
+  if (!isum) return fail(QG_EINVAL, "isum is null");
+  if (int st = check_ws(ws, ws_bytes, prep_layout(rows, k).total, "the prepared rows")) return st;
+  if (int st = check_device()) return st;
+  if (int st = launch_pair_blockdots(fmt, w_image, n, k, ws, rows, isum, (hipStream_t)stream)) return st;
+  return ok();
+}
+
 }  // extern "C"

@@ -29,6 +29,9 @@ int launch_prepare_set(const qg_act* acts, int count, int rows, hipStream_t s);
 int launch_quantize_plain(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, hipStream_t s);
 // Offline weight quantization into a device image.
 int launch_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, hipStream_t s);
+// A3 test hook of the pair kernel (3..16 rows): block dots from a pair-order workspace.
+int launch_pair_blockdots(int fmt, const void* image, int64_t n, int64_t k, const void* ws, int rows, int32_t* isum,
+                          hipStream_t s);
 // A3 test hook.
 int launch_blockdots(int fmt, const void* image, int64_t n, int64_t k, const int8_t* qx, int rows, int32_t* isum,
                      hipStream_t s);

@@ -403,6 +403,34 @@ struct MpAddr {
   bool gon;
 };
 
+// The exact int32 dots of one pair step: lane (i, q) holds 16 bytes of weight
+// codes (araw: Q8_0 codes, or Q4_0 packed nibbles whose half sh = 0 / 4 it
+// feeds) and 16 bytes of the activation chunk; c[v] is the dot of weight row
+// 4q + v with column i, starting from ns (Q4_0: -8 * sum of that column's
+// activation codes).
+template <int FMT>
+__device__ __forceinline__ v4i pair_dots(uint4 araw, uint4 x, int ns, int sh) {
+  uint4 av = araw;
+  if (FMT == FMT_Q4) {
+    av.x = (av.x >> sh) & 0x0F0F0F0Fu;
+    av.y = (av.y >> sh) & 0x0F0F0F0Fu;
+    av.z = (av.z >> sh) & 0x0F0F0F0Fu;
+    av.w = (av.w >> sh) & 0x0F0F0F0Fu;
+  }
+  const v4i a = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+  const v4i bx = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+  v4i c = {ns, ns, ns, ns};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx, c, 0, 0, 0);
+}
+
+// Lane offset of a pair step's weight bytes inside the two cells of blocks
+// (b, b + 1): Q8_0 lane (i, q) reads half q % 2 of block b + q / 2 of row i;
+// Q4_0 lanes q = 0, 1 read block b's 16 bytes of row i, q = 2, 3 block b + 1's.
+template <int FMT>
+__device__ __forceinline__ uint32_t pair_aoff(int i, int q) {
+  return FMT == FMT_Q8 ? (uint32_t)(q * 256 + i * 16) : (uint32_t)((q >> 1) * 256 + i * 16);
+}
+
 template <int FMT, int NT, int G, bool GATHER>
 __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad, int lane, int b) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
@@ -433,24 +461,13 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
                                            const MpAddr<NT>& ad, int sh) {
 #pragma unroll
   for (int t = 0; t < NT; t++) {
-    uint4 av = st.a[t];
-    if (FMT == FMT_Q4) {
-      av.x = (av.x >> sh) & 0x0F0F0F0Fu;
-      av.y = (av.y >> sh) & 0x0F0F0F0Fu;
-      av.z = (av.z >> sh) & 0x0F0F0F0Fu;
-      av.w = (av.w >> sh) & 0x0F0F0F0Fu;
-    }
-    const v4i a = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
     // fp16 scales of rows 4q .. 4q+3 of the lane's block, from the wave's staged copy
     const uint2 wv = *reinterpret_cast<const uint2*>(ad.sl[t] + (st.b - ad.sb0) * TILE + ad.soff);
     const float dw[4] = {h2f((uint16_t)(wv.x & 0xffff)), h2f((uint16_t)(wv.x >> 16)), h2f((uint16_t)(wv.y & 0xffff)),
                          h2f((uint16_t)(wv.y >> 16))};
 #pragma unroll
     for (int g = 0; g < G; g++) {
-      const v4i bx = {(int)st.x[g].x, (int)st.x[g].y, (int)st.x[g].z, (int)st.x[g].w};
-      const int ns = st.ns[g];
-      v4i c = {ns, ns, ns, ns};
-      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx, c, 0, 0, 0);
+      const v4i c = pair_dots<FMT>(st.a[t], st.x[g], st.ns[g], sh);
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const float f = (float)c[v], m = dw[v] * st.dx[g];
@@ -488,7 +505,7 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, in
   const uint16_t* scale[NT];
 #pragma unroll
   for (int t = 0; t < NT; t++) ad.sl[t] = scl + (wave * NT + t) * sc_stride;
-  ad.aoff = FMT == FMT_Q8 ? (uint32_t)(q * 256 + i * 16) : (uint32_t)((q >> 1) * 256 + i * 16);
+  ad.aoff = pair_aoff<FMT>(i, q);
   ad.soff = (uint32_t)((i >> 3) * 16 + 4 * q);
   ad.xc = reinterpret_cast<const uint8_t*>(ta.prep.codes);
   ad.xd = ta.prep.dx;
@@ -1001,6 +1018,56 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void gr
       grouped_small_unit<false>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y,
                                 lds_x, (u - ub) / tiles_s, (u - ub) % tiles_s, lds, s_map, nullptr);
   }
+}
+
+// ------------------------------------------------------ pair-dot hook ---
+
+// Test hook: the int32 dots of every (activation row, weight row, block) as the
+// pair kernel forms them -- the same weight and chunk operands, the same
+// matrix product (pair_dots) -- written out instead of scaled and summed.
+// One wave per (16-row tile, block pair, group of eight activation rows) of a
+// pair-order workspace; isum [rows][n][kb].
+template <int FMT>
+__global__ __launch_bounds__(256) void pair_blockdots_kernel(const uint8_t* __restrict__ code, int64_t n, int kbp,
+                                                             int kb, Prep prep, int groups, int rows,
+                                                             int* __restrict__ isum) {
+  constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int64_t pairs = kbp / 2, ntiles = np_of(n) / TILE;
+  if (wave >= ntiles * pairs * groups) return;  // whole waves leave together
+  const int lane = threadIdx.x & (WAVE - 1), i = lane & 15, q = lane >> 4;
+  const int g = (int)(wave % groups), p = (int)((wave / groups) % pairs);
+  const int64_t t = wave / (groups * pairs);
+  const uint4 a = ld16(code + ((size_t)t * kbp + 2 * p) * CB + pair_aoff<FMT>(i, q));
+  const size_t chunk = (size_t)p * groups + g;
+  const bool xon = (i < 8) == (q < 2);
+  const uint4 x = xon ? ld16(reinterpret_cast<const uint8_t*>(prep.codes) + (chunk * 64 + lane) * 16)
+                      : make_uint4(0u, 0u, 0u, 0u);
+  const int ns = FMT == FMT_Q4 ? prep.nsx[chunk * 16 + i] : 0;
+  const v4i c = pair_dots<FMT>(a, x, ns, (q & 1) * 4);
+  const int r = g * 8 + (i & 7), b = 2 * p + (i >> 3);
+  if (r >= rows || b >= kb) return;
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    const int64_t o = t * TILE + 4 * q + v;
+    if (o < n) isum[((int64_t)r * n + o) * kb + b] = c[v];
+  }
+}
+
+int launch_pair_blockdots(int fmt, const void* image, int64_t n, int64_t k, const void* ws, int rows, int32_t* isum,
+                          hipStream_t s) {
+  const PrepLayout L = prep_layout(rows, k);
+  const Prep pv = prep_view(ws, L);
+  const int kbp = (int)kbp_of(k), kb = (int)kb_of(k);
+  const int64_t waves = (np_of(n) / TILE) * (kbp / 2) * L.groups;
+  const unsigned g = (unsigned)((waves * WAVE + 255) / 256);
+  if (fmt == QG_FMT_Q8_0)
+    hipLaunchKernelGGL(pair_blockdots_kernel<FMT_Q8>, dim3(g), dim3(256), 0, s, (const uint8_t*)image, n, kbp, kb, pv,
+                       L.groups, rows, isum);
+  else
+    hipLaunchKernelGGL(pair_blockdots_kernel<FMT_Q4>, dim3(g), dim3(256), 0, s, (const uint8_t*)image, n, kbp, kb, pv,
+                       L.groups, rows, isum);
+  return hip_status(hipGetLastError(), "pair_blockdots_kernel");
 }
 
 // ------------------------------------------------------------- launchers ---

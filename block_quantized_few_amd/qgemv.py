@@ -95,6 +95,9 @@ _SIGS = {
                                   C.c_void_p, C.c_size_t, C.c_void_p]),
     "qg_quantize_rows_q8": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_void_p]),
+    "qgemv_blockdots_pairs": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_size_t, C.c_int,
+                                        C.c_void_p, C.c_void_p]),
+    "qg_read_probe": (C.c_int, [C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
     "qgemv_blockdots": (C.c_int, [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
                                   C.c_void_p]),
 }
@@ -502,6 +505,13 @@ def blockdots(fmt, image, n, k, qx):
     rows = qx.shape[0]
     isum = torch.empty((rows, n, k // 32), dtype=torch.int32, device=qx.device)
     _check(lib().qgemv_blockdots(fmt, _p(image), n, k, _p(qx), rows, _p(isum), _stream()))
+    return isum
+
+
+def blockdots_pairs(fmt, image, n, k, ws, rows):
+    """The 3..16-row kernel's block dots from a pair-order workspace (prepare_rows of `rows` rows)."""
+    isum = torch.empty((rows, n, k // 32), dtype=torch.int32, device=ws.device)
+    _check(lib().qgemv_blockdots_pairs(fmt, _p(image), n, k, _p(ws), ws.numel(), rows, _p(isum), _stream()))
     return isum
 
 

@@ -405,6 +405,28 @@ int qg_quantize_rows_q8(const float* x, int rows, int64_t k, int8_t* qx, float* 
 int qgemv_blockdots(int fmt, const void* w_image, int64_t n, int64_t k, const int8_t* qx, int rows, int32_t* isum,
                     qg_stream stream);
 
+/* A3 as the 3..16-row kernel forms it: isum [rows][n][k/32] int32, the exact
+ * block dots of the image's codes with rows prepared in ws by
+ * qg_prepare_rows(x, rows, k, ...) (pair order, ws_bytes >= its size), each
+ * from the same block-pair matrix product that kernel scales and sums
+ * (Q4_0: codes c - 8).  3 <= rows <= 16. */
+int qgemv_blockdots_pairs(int fmt, const void* w_image, int64_t n, int64_t k, const void* ws, size_t ws_bytes,
+                          int rows, int32_t* isum, qg_stream stream);
+
+/* ------------------------------------------------------ measurement hook --- */
+
+/* The achievable-read ceiling: reads `bytes` (a nonzero multiple of 16) at
+ * src (16-byte aligned) once with 16-byte non-temporal loads, the GEMV
+ * kernels' weight-load form, in `grid` workgroups of 512 threads (1..65536),
+ * each reading one contiguous range with `inflight` (1, 2, 4 or 8) loads per
+ * thread in flight, and stores an xor fold of what it read to sink
+ * (grid * 8 uint32, device; its values mean nothing).  Timing it over the
+ * same bytes as a GEMV's weight image gives the bare-read bandwidth that the
+ * GEMV is compared with beside the HBM data-sheet peak (the pages' one-row
+ * projections are weight-streaming passes: llama-leg page, commit 16880fe;
+ * drama page, series commits). */
+int qg_read_probe(const void* src, size_t bytes, int grid, int inflight, uint32_t* sink, qg_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -272,6 +272,29 @@ def test_validation_refuses_before_any_hip_call():
     assert q.status_string(-3) == "rows outside 0..16"
 
 
+def test_pair_blockdots_validation():
+    # fmt, image, n, k, ws, ws_bytes, rows, isum, stream
+    st, msg = _status("qgemv_blockdots_pairs", q.Q8_0, V(A), 64, 2048, V(A), 1 << 20, 2, V(A), None)
+    assert st == -3 and "rows=2" in msg
+    small = q.workspace_bytes(8, 2048)
+    st, msg = _status("qgemv_blockdots_pairs", q.Q4_0, V(A), 64, 2048, V(A), small, 9, V(A), None)
+    assert st == -5 and f"ws_bytes={small}" in msg
+    st, msg = _status("qgemv_blockdots_pairs", q.Q4_0, V(A), 64, 2048, V(A), small, 8, None, None)
+    assert st == -1
+
+
+def test_read_probe_validation():
+    # src, bytes, grid, inflight, sink, stream
+    st, msg = _status("qg_read_probe", V(A), 100, 256, 4, V(A), None)
+    assert st == -4 and "bytes=100" in msg
+    st, msg = _status("qg_read_probe", V(A), 1 << 20, 0, 4, V(A), None)
+    assert st == -1 and "grid=0" in msg
+    st, msg = _status("qg_read_probe", V(A), 1 << 20, 256, 3, V(A), None)
+    assert st == -1 and "inflight=3" in msg
+    st, msg = _status("qg_read_probe", None, 1 << 20, 256, 4, V(A), None)
+    assert st == -1
+
+
 def test_rows_zero_is_a_noop():
     st, _ = _status("qgemv_q8_0", V(A), 1024, 1024, V(A), 0, V(A), V(A), 0, None)
     assert st == 0

@@ -68,6 +68,21 @@ def test_blockdots_bit_exact(fmt, ofmt, n, k, rows):
     assert np.array_equal(got.cpu().numpy(), O.blockdots(ofmt, blocks, n, k, qx))
 
 
+@pytest.mark.parametrize("fmt,ofmt", FMTS)
+@pytest.mark.parametrize("n,k,rows", [(40, 96, 3), (77, 800, 8), (16, 8192, 16), (257, 2048, 9), (1024, 1024, 12)])
+def test_pair_blockdots_bit_exact(fmt, ofmt, n, k, rows):
+    """The 3..16-row kernel's int32 block dots (its block-pair matrix product on the pair-order workspace that
+    qg_prepare_rows writes) equal the oracle's, bit for bit."""
+    log(f"pair blockdots fmt={fmt} n={n} k={k} rows={rows}")
+    w = gauss((n, k), 0.02, 12, 5).numpy()
+    x = _special_blocks(outliers((rows, k), 1.0, 12, 6).numpy())
+    blocks, img = oracle_image(ofmt, w)
+    qx, _, _ = O.quantize_acts(x)
+    ws = q.prepare_rows(torch.from_numpy(x).cuda())
+    got = q.blockdots_pairs(fmt, img, n, k, ws, rows)
+    assert np.array_equal(got.cpu().numpy(), O.blockdots(ofmt, blocks, n, k, qx))
+
+
 # ------------------------------------------------------------- A2-A4 ---
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
 @pytest.mark.parametrize("n,k", [(1024, 1024), (1000, 800), (33, 96), (257, 4096), (1, 32)])
