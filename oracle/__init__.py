@@ -15,8 +15,11 @@ from . import build as _build
 
 Q8_0 = 1
 Q4_0 = 2
+Q4_K = 3
 QK = 32
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18}
+QK_K = 256
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144}
+BLOCK_WEIGHTS = {Q8_0: 32, Q4_0: 32, Q4_K: 256}
 
 _lib = None
 
@@ -36,7 +39,7 @@ def lib():
         L.orc_f32_to_f16.argtypes = [C.c_float, C.POINTER(C.c_int)]
         L.orc_f32_to_f16_array.argtypes = [p, p, i64, C.POINTER(C.c_int)]
         L.orc_f16_to_f32_array.argtypes = [p, p, i64]
-        for f in ("orc_quantize_q8_0", "orc_quantize_q4_0"):
+        for f in ("orc_quantize_q8_0", "orc_quantize_q4_0", "orc_quantize_q4_k"):
             getattr(L, f).restype = ci
             getattr(L, f).argtypes = [p, i64, i64, p]
         L.orc_dequantize.restype = ci
@@ -100,14 +103,14 @@ def f16_to_f32(h):
 
 # --------------------------------------------------------------- weights ---
 def quantize_weights(fmt, w):
-    """fp32 [n][k] -> canonical blocks, uint8 [n][k/32][block bytes]."""
+    """fp32 [n][k] -> canonical blocks, uint8 [n][k/32][block bytes] (Q4_K: [n][k/256][144])."""
     w = _c(w, np.float32)
     n, k = w.shape
-    out = np.zeros((n, k // QK, BLOCK_BYTES[fmt]), np.uint8)
-    f = lib().orc_quantize_q8_0 if fmt == Q8_0 else lib().orc_quantize_q4_0
+    out = np.zeros((n, k // BLOCK_WEIGHTS[fmt], BLOCK_BYTES[fmt]), np.uint8)
+    f = {Q8_0: lib().orc_quantize_q8_0, Q4_0: lib().orc_quantize_q4_0, Q4_K: lib().orc_quantize_q4_k}[fmt]
     rc = f(_ptr(w), n, k, _ptr(out))
     if rc == -1:
-        raise ValueError("k must be a multiple of 32")
+        raise ValueError(f"k must be a multiple of {BLOCK_WEIGHTS[fmt]}")
     if rc == -2:
         raise OverflowError("a block scale overflowed fp16")
     return out

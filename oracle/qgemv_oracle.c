@@ -46,10 +46,13 @@
 
 #define ORC_Q8_0 1
 #define ORC_Q4_0 2
+#define ORC_Q4_K 3
 
 #define QK 32
 #define Q8_BLOCK_BYTES 34
 #define Q4_BLOCK_BYTES 18
+#define QK_K 256
+#define Q4K_BLOCK_BYTES 144
 
 /* ---------------------------------------------------------------- fp16 --- */
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -184,6 +187,111 @@ int orc_quantize_q4_0(const float* w, int64_t n, int64_t k, uint8_t* blocks) {
   return overflow ? -2 : 0;
 }
 
+/* ------------------------------------------------ K-quant superblocks --- */
+/* Q4_K ([C] commit 8624bce: a superblock format's one-row form whose K comes
+ * in whole superblocks; the race bed of [C]'s body runs Q4_K_M weights).  The
+ * pages do not print the format; this is the published ggml K-quant Q4_K
+ * superblock, restated:
+ *   256 weights = 8 sub-blocks of 32.  Bytes: fp16 d at 0, fp16 dmin at 2,
+ *   twelve bytes at 4 holding eight 6-bit sub-scales sc[j] and eight 6-bit
+ *   sub-mins m[j], then 128 bytes of 4-bit codes q.
+ *   Scales byte s[0..11]: for j < 4, sc[j] = s[j] & 63 and m[j] = s[j+4] & 63;
+ *   for j >= 4, sc[j] = (s[j+4] & 15) | (s[j-4] >> 6) << 4 and
+ *   m[j] = (s[j+4] >> 4) | (s[j] >> 6) << 4.
+ *   Codes: weight 64p + l (p < 4, l < 32) in the low nibble of code byte
+ *   32p + l, weight 64p + 32 + l in its high nibble.
+ *   Weight value: w = d * sc[j] * q - dmin * m[j], j = the weight's sub-block.
+ * How a weight matrix is quantized into this format is a choice of the
+ * writer's (it does not change the format): the plainest one is taken here,
+ * per sub-block j (lo = min(0, min w), hi = max w):
+ *   s_j = (hi - lo) / 15, mn_j = -lo                       (fp32)
+ *   d = fp16(max_j s_j / 63), dmin = fp16(max_j mn_j / 63)
+ *   sc[j] = min(63, round(s_j / d)) (0 when d == 0), m[j] likewise with dmin
+ *   q = clamp(round((w + dmin*m[j]) / (d*sc[j])), 0, 15) (0 when d*sc[j] == 0)
+ * with IEEE fp32 divisions, round half away from zero, d*sc and dmin*m exact
+ * in fp32 (11-bit by 6-bit products). */
+
+static void q4k_scale_min(const uint8_t* sb, int j, int* sc, int* m) {
+  const uint8_t* s = sb + 4;
+  if (j < 4) {
+    *sc = s[j] & 63;
+    *m = s[j + 4] & 63;
+  } else {
+    *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+    *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+  }
+}
+
+static void q4k_put_scales(uint8_t* sb, const int sc[8], const int m[8]) {
+  uint8_t* s = sb + 4;
+  for (int j = 0; j < 4; j++) {
+    s[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+    s[j + 4] = (uint8_t)((m[j] & 63) | ((m[j + 4] >> 4) << 6));
+    s[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
+  }
+}
+
+/* Code (0..15) of weight i (0..255) of a superblock. */
+static int q4k_code(const uint8_t* sb, int i) {
+  const int p = i >> 6, l = i & 31, hi = (i >> 5) & 1;
+  const uint8_t byte = sb[16 + 32 * p + l];
+  return hi ? (byte >> 4) : (byte & 15);
+}
+
+int orc_quantize_q4_k(const float* w, int64_t n, int64_t k, uint8_t* blocks) {
+  if (k % QK_K) return -1;
+  int overflow = 0;
+  const int64_t ns = k / QK_K;
+  for (int64_t r = 0; r < n; r++)
+    for (int64_t b = 0; b < ns; b++) {
+      const float* v = w + r * k + b * QK_K;
+      uint8_t* out = blocks + (r * ns + b) * Q4K_BLOCK_BYTES;
+      float s[8], mn[8], smax = 0.0f, mmax = 0.0f;
+      for (int j = 0; j < 8; j++) {
+        float lo = 0.0f, hi = v[32 * j];
+        for (int i = 0; i < 32; i++) {
+          const float x = v[32 * j + i];
+          if (x < lo) lo = x;
+          if (x > hi) hi = x;
+        }
+        s[j] = (hi - lo) / 15.0f;
+        mn[j] = -lo;
+        if (s[j] > smax) smax = s[j];
+        if (mn[j] > mmax) mmax = mn[j];
+      }
+      const uint16_t d16 = orc_f32_to_f16(smax / 63.0f, &overflow);
+      const uint16_t m16 = orc_f32_to_f16(mmax / 63.0f, &overflow);
+      const float d = orc_f16_to_f32(d16), dmin = orc_f16_to_f32(m16);
+      int sc[8], m[8];
+      for (int j = 0; j < 8; j++) {
+        sc[j] = d != 0.0f ? clampi((int)roundf(s[j] / d), 0, 63) : 0;
+        m[j] = dmin != 0.0f ? clampi((int)roundf(mn[j] / dmin), 0, 63) : 0;
+      }
+      put_u16(out, d16);
+      put_u16(out + 2, m16);
+      q4k_put_scales(out, sc, m);
+      for (int j = 0; j < 8; j++) {
+        const float D = d * (float)sc[j], M = dmin * (float)m[j];
+        for (int i = 0; i < 32; i++) {
+          const int e = 32 * j + i;
+          const int q = D != 0.0f ? clampi((int)roundf((v[e] + M) / D), 0, 15) : 0;
+          const int p = e >> 6, l = e & 31;
+          uint8_t* byte = out + 16 + 32 * p + l;
+          *byte = (uint8_t)((e & 32) ? ((*byte & 15) | (q << 4)) : ((*byte & 0xF0) | q));
+        }
+      }
+    }
+  return overflow ? -2 : 0;
+}
+
+/* Sub-block j's scale d * sc[j] and offset dmin * m[j] of a superblock (exact). */
+static void q4k_dm(const uint8_t* sb, int j, double* D, double* M) {
+  int sc, m;
+  q4k_scale_min(sb, j, &sc, &m);
+  *D = (double)orc_f16_to_f32(get_u16(sb)) * (double)sc;
+  *M = (double)orc_f16_to_f32(get_u16(sb + 2)) * (double)m;
+}
+
 /* Code i of a canonical block, as the signed integer it stands for. */
 static int block_code(int fmt, const uint8_t* blk, int i) {
   if (fmt == ORC_Q8_0) return (int)(int8_t)blk[2 + i];
@@ -194,8 +302,22 @@ static int block_code(int fmt, const uint8_t* blk, int i) {
 
 static int block_bytes(int fmt) { return fmt == ORC_Q8_0 ? Q8_BLOCK_BYTES : Q4_BLOCK_BYTES; }
 
-/* Dequantized weights w_hat = d * code, in double (exact). */
+/* Dequantized weights w_hat = d * code (Q4_K: d*sc*q - dmin*m), in double (exact). */
 int orc_dequantize(int fmt, const uint8_t* blocks, int64_t n, int64_t k, double* w_hat) {
+  if (fmt == ORC_Q4_K) {
+    if (k % QK_K) return -1;
+    const int64_t ns = k / QK_K;
+    for (int64_t r = 0; r < n; r++)
+      for (int64_t b = 0; b < ns; b++) {
+        const uint8_t* sb = blocks + (r * ns + b) * Q4K_BLOCK_BYTES;
+        for (int i = 0; i < QK_K; i++) {
+          double D, M;
+          q4k_dm(sb, i >> 5, &D, &M);
+          w_hat[r * k + b * QK_K + i] = D * (double)q4k_code(sb, i) - M;
+        }
+      }
+    return 0;
+  }
   if (k % QK || (fmt != ORC_Q8_0 && fmt != ORC_Q4_0)) return -1;
   int64_t nb = k / QK;
   int bb = block_bytes(fmt);
@@ -235,9 +357,25 @@ int orc_quantize_acts(const float* x, int rows, int64_t k, int8_t* qx, float* dx
 /* ---------------------------------------------------------- block dots --- */
 
 /* isum[r][n][b] = sum_i code(w[n], b, i) * qx[r][32b + i], exact in int64,
- * stored as int32 (|isum| <= 32 * 127 * 127 fits). */
+ * stored as int32 (|isum| <= 32 * 127 * 127 fits).  Q4_K: b is a 32-weight
+ * sub-block and the code its raw 4-bit q (0..15); the sub-min's share,
+ * dmin * m * sum(qx), is not part of the integer dot. */
 int orc_blockdots(int fmt, const uint8_t* blocks, int64_t n, int64_t k, const int8_t* qx, int rows,
                   int32_t* isum) {
+  if (fmt == ORC_Q4_K) {
+    if (k % QK_K) return -1;
+    const int64_t ns = k / QK_K, nb = k / QK;
+    for (int r = 0; r < rows; r++)
+      for (int64_t o = 0; o < n; o++)
+        for (int64_t b = 0; b < nb; b++) {
+          const uint8_t* sb = blocks + (o * ns + b / 8) * Q4K_BLOCK_BYTES;
+          int64_t s = 0;
+          for (int i = 0; i < QK; i++)
+            s += (int64_t)q4k_code(sb, (int)(b % 8) * 32 + i) * (int64_t)qx[(int64_t)r * k + b * QK + i];
+          isum[((int64_t)r * n + o) * nb + b] = (int32_t)s;
+        }
+    return 0;
+  }
   if (k % QK || (fmt != ORC_Q8_0 && fmt != ORC_Q4_0)) return -1;
   int64_t nb = k / QK;
   int bb = block_bytes(fmt);
@@ -304,12 +442,35 @@ typedef struct {
 } qgemv_ctx;
 
 /* y[r][o] = sum_b d_w[o][b] * d_x[r][b] * isum[r][o][b], ascending b, in
- * double, rounded once to float. */
+ * double, rounded once to float.  Q4_K: the sum over 32-weight sub-blocks b of
+ * d_x[r][b] * (D_b * isum_b - M_b * sum(qx of block b)), D_b = d * sc, M_b =
+ * dmin * m of b's superblock -- the dot of the dequantized weights with the
+ * dequantized activations, sub-block by sub-block. */
 static void qgemv_range(void* p, int64_t lo, int64_t hi) {
   qgemv_ctx* c = (qgemv_ctx*)p;
   int bb = block_bytes(c->fmt);
   for (int64_t t = lo; t < hi; t++) {
     int64_t o = c->sel ? c->sel[t] : t;
+    if (c->fmt == ORC_Q4_K) {
+      const int64_t ns = c->k / QK_K;
+      for (int r = 0; r < c->rows; r++) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < c->nb; b++) {
+          const uint8_t* sb = c->blocks + (o * ns + b / 8) * Q4K_BLOCK_BYTES;
+          const int8_t* q = c->qx + (int64_t)r * c->k + b * QK;
+          int64_t s = 0, xs = 0;
+          for (int i = 0; i < QK; i++) {
+            s += (int64_t)q4k_code(sb, (int)(b % 8) * 32 + i) * (int64_t)q[i];
+            xs += q[i];
+          }
+          double D, M;
+          q4k_dm(sb, (int)(b % 8), &D, &M);
+          acc += (double)c->dx[(int64_t)r * c->nb + b] * (D * (double)s - M * (double)xs);
+        }
+        c->y[(int64_t)r * c->out_n + t] = (float)acc;
+      }
+      continue;
+    }
     for (int r = 0; r < c->rows; r++) {
       double acc = 0.0;
       for (int64_t b = 0; b < c->nb; b++) {
@@ -328,7 +489,8 @@ static void qgemv_range(void* p, int64_t lo, int64_t hi) {
 
 static int qgemv_common(int fmt, const uint8_t* blocks, int64_t n, int64_t k, const float* x, int rows,
                         const int64_t* sel, int64_t nsel, float* y, int threads) {
-  if (k % QK || (fmt != ORC_Q8_0 && fmt != ORC_Q4_0) || rows < 0) return -1;
+  if (k % QK || (fmt != ORC_Q8_0 && fmt != ORC_Q4_0 && fmt != ORC_Q4_K) || rows < 0) return -1;
+  if (fmt == ORC_Q4_K && k % QK_K) return -1;
   int64_t nb = k / QK;
   int8_t* qx = (int8_t*)malloc((size_t)(rows * k) + 1);
   float* dx = (float*)malloc(sizeof(float) * (size_t)(rows * nb) + 1);

@@ -577,3 +577,159 @@ def test_synth_matches_scalar_splitmix_and_is_gaussian():
     assert synth.splitmix64_scalar(0, 0) == 0xE220A8397B1DCDAF
     g = synth.gaussian((200000,), 2.0, seed).numpy().astype(np.float64)
     assert abs(g.mean()) < 0.03 and abs(g.std() - 2.0) < 0.02
+
+
+# ------------------------------------------------------ Q4_K superblocks ---
+def _q4k_golden():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "q4_k_hand_superblocks.json")) as f:
+        return json.load(f)
+
+
+def _q4k_codes():
+    return [(7 * i + i // 32) % 16 for i in range(256)]
+
+
+def _q4k_code_bytes(codes):
+    # byte 32p + l holds weight 64p + l (low nibble) and weight 64p + 32 + l (high nibble)
+    out = []
+    for p in range(4):
+        for l in range(32):
+            out.append(codes[64 * p + l] | (codes[64 * p + 32 + l] << 4))
+    return out
+
+
+def _q4k_block(case):
+    g = _q4k_golden()
+    c = g[case]
+    b = [c["d_f16"] & 255, c["d_f16"] >> 8, c["dmin_f16"] & 255, c["dmin_f16"] >> 8] + c["scale_bytes"] + \
+        _q4k_code_bytes(_q4k_codes())
+    return np.array(b, np.uint8).reshape(1, 1, 144)
+
+
+def test_q4_k_hand_superblock_decodes():
+    g = _q4k_golden()
+    codes = _q4k_codes()
+    cb = _q4k_code_bytes(codes)
+    for i, v in g["code_bytes_spot"].items():
+        assert cb[int(i)] == v, i
+    blk = _q4k_block("decode")
+    w = O.dequantize(O.Q4_K, blk, 1, 256)[0]
+    for i, v in g["decode"]["weights_spot"].items():
+        assert w[int(i)] == v, i
+    # every weight: the fields of the hand-packed bytes
+    dd = g["decode"]
+    for i in range(256):
+        j = i // 32
+        assert w[i] == dd["d"] * dd["sc"][j] * codes[i] - dd["dmin"] * dd["m"][j], i
+
+
+def test_q4_k_quantizer_recovers_hand_fields():
+    g = _q4k_golden()["quantize"]
+    codes = _q4k_codes()
+    w = np.array([[g["sc"][i // 32] * codes[i] - g["m"][i // 32] for i in range(256)]], np.float32)
+    blk = O.quantize_weights(O.Q4_K, w)
+    assert np.array_equal(blk, _q4k_block("quantize"))
+    assert np.array_equal(O.dequantize(O.Q4_K, blk, 1, 256), w.astype(np.float64))
+
+
+def test_q4_k_zero_and_positive_subblocks():
+    w = np.zeros((2, 512), np.float32)
+    w[1, :32] = np.linspace(0.5, 2.0, 32, dtype=np.float32)  # all positive: its sub-min is 0
+    w[1, 32:64] = -np.linspace(0.1, 1.0, 32, dtype=np.float32)
+    blk = O.quantize_weights(O.Q4_K, w)
+    assert not blk[0].any() and not blk[1, 1].any()  # all-zero superblocks: d = dmin = 0, every code 0
+    s = blk[1, 0, 4:16]
+    assert s[4] & 63 == 0  # m[0]
+    wh = O.dequantize(O.Q4_K, blk, 2, 512)
+    assert np.all(wh[0] == 0.0) and np.all(wh[1, 64:] == 0.0)
+
+
+def test_q4_k_whole_superblocks_only():
+    with pytest.raises(ValueError):
+        O.quantize_weights(O.Q4_K, np.zeros((2, 224), np.float32))
+    blk = O.quantize_weights(O.Q4_K, np.zeros((2, 256), np.float32))
+    with pytest.raises(AssertionError):
+        O.gemv_q(O.Q4_K, blk, 2, 224, np.zeros((1, 224), np.float32))
+
+
+def test_q4_k_gemv_integer_closed_form():
+    """The hand superblock fields scaled to d = dmin = 1 make every weight an integer; with integer activations
+    whose 32-blocks reach +-127 (so d_x = 1), y is the exact integer matrix-vector product."""
+    g = _q4k_golden()["quantize"]
+    codes = _q4k_codes()
+    n, k = 5, 512
+    rng = np.random.default_rng(44)
+    wi = np.zeros((n, k), np.int64)
+    for r in range(n):
+        for b in range(k // 256):
+            perm = rng.permutation(8)  # each superblock takes the hand fields in another sub-block order
+            for i in range(256):
+                j = perm[i // 32]
+                wi[r, 256 * b + i] = g["sc"][j] * codes[i] - g["m"][j]
+    blk = O.quantize_weights(O.Q4_K, wi.astype(np.float32))
+    assert np.array_equal(O.dequantize(O.Q4_K, blk, n, k), wi.astype(np.float64))
+    xi = rng.integers(-127, 128, size=(3, k))
+    xi[:, ::32] = 127
+    y = O.gemv_q(O.Q4_K, blk, n, k, xi.astype(np.float32))
+    assert np.array_equal(y, (xi @ wi.T).astype(np.float32))
+
+
+def _random_q4k(n, ns, seed):
+    rng = np.random.default_rng(seed)
+    blk = rng.integers(0, 256, size=(n, ns, 144), dtype=np.uint64).astype(np.uint8)
+    # finite positive scales: fp16 exponents 5..20 (2^-10 .. 2^5)
+    for o in (0, 2):
+        h = (rng.integers(5, 21, size=(n, ns)) << 10) | rng.integers(0, 1024, size=(n, ns))
+        blk[:, :, o] = h & 255
+        blk[:, :, o + 1] = h >> 8
+    return blk
+
+
+def test_q4_k_gemv_is_the_dequantized_dot():
+    """Random superblocks (any codes and 6-bit fields): y equals, to double rounding, the plain dot of the
+    dequantized weights with the dequantized q8 activations -- sub-min sign, sub-block index and block order
+    included."""
+    n, k, rows = 7, 768, 3
+    blk = _random_q4k(n, k // 256, 45)
+    x = _rng_normal((rows, k), 1.0, 46)
+    qx, dx, _ = O.quantize_acts(x)
+    xh = qx.astype(np.float64) * np.repeat(dx.astype(np.float64), 32, 1)
+    ref = xh @ O.dequantize(O.Q4_K, blk, n, k).T
+    y = O.gemv_q(O.Q4_K, blk, n, k, x).astype(np.float64)
+    scale = np.abs(xh) @ np.abs(O.dequantize(O.Q4_K, blk, n, k)).T
+    assert np.all(np.abs(y - ref) <= 1e-7 * scale + 1e-30)  # one fp32 rounding of a double sum
+
+
+def test_q4_k_blockdots_brute_force():
+    # with d = 1, every sc = 1 and m = 0 the dequantized weights are the raw codes themselves
+    n, k, rows = 4, 512, 3
+    blk = _random_q4k(n, k // 256, 47)
+    blk[:, :, 0:4] = [0x00, 0x3C, 0x00, 0x3C]
+    blk[:, :, 4:8] = 1
+    blk[:, :, 8:16] = [0, 0, 0, 0, 1, 1, 1, 1]
+    codes = O.dequantize(O.Q4_K, blk, n, k).astype(np.int64)
+    assert codes.min() >= 0 and codes.max() <= 15
+    qx = np.random.default_rng(48).integers(-127, 128, size=(rows, k)).astype(np.int8)
+    want = np.einsum("rnbi,rbi->rnb", np.broadcast_to(codes.reshape(1, n, k // 32, 32), (rows, n, k // 32, 32)),
+                     qx.astype(np.int64).reshape(rows, k // 32, 32))
+    assert np.array_equal(O.blockdots(O.Q4_K, blk, n, k, qx), want)
+
+
+def test_q4_k_quantizer_error_bound():
+    """Per element |w - w_hat| <= D/2 + 15*d/2 + dmin/2 (+ fp32 rounding): half a step of its sub-block, plus
+    what rounding d*sc down and dmin*m either way can clamp."""
+    n, k = 16, 1024
+    w = _rng_normal((n, k), 0.02, 49)
+    w[3, :256] += 0.05  # an all-positive superblock
+    blk = O.quantize_weights(O.Q4_K, w)
+    wh = O.dequantize(O.Q4_K, blk, n, k)
+    for r in range(n):
+        for b in range(k // 256):
+            sb = blk[r, b]
+            d = float(np.frombuffer(sb[0:2].tobytes(), np.float16)[0])
+            dmin = float(np.frombuffer(sb[2:4].tobytes(), np.float16)[0])
+            sc = [(sb[4 + j] & 63) if j < 4 else (sb[8 + j] & 15) | ((sb[j] >> 6) << 4) for j in range(8)]
+            for j in range(8):
+                seg = slice(256 * b + 32 * j, 256 * b + 32 * (j + 1))
+                bound = d * sc[j] / 2 + 7.5 * d + dmin / 2 + 1e-6
+                assert np.abs(wh[r, seg] - w[r, seg]).max() <= bound, (r, b, j)
