@@ -77,7 +77,7 @@ int qgemv_fmt(int fmt, const void* w_image, int64_t n, int64_t k, const float* x
   if (int st = check_device()) return st;
   hipStream_t s = (hipStream_t)stream;
   ProjArg pa{w_image, n, k, ws, nullptr, y};
-  if (fuses_quantization(rows)) {
+  if (fuses_quantization(fmt, rows, k)) {
     pa.x = x;
   } else if (int st = launch_prepare(x, rows, k, ws, prep_layout(rows, k), s)) {
     return st;
@@ -239,6 +239,9 @@ int qgemv_set_rows(int fmt, const qg_proj_rows* projs, int count, int rows, qg_s
   if (int st = check_fmt(fmt)) return st;
   if (!projs || count < 1 || count > QG_MAX_SET) return fail(QG_EINVAL, "count=%d outside 1..%d", count, QG_MAX_SET);
   if (int st = check_rows(rows)) return st;
+  // quantized inside the GEMV launch only when every projection's rows fit its staging area
+  bool fuse = true;
+  for (int i = 0; i < count; i++) fuse = fuse && fuses_quantization(fmt, rows, projs[i].k);
   ProjArg pa[QG_MAX_SET];
   for (int i = 0; i < count; i++) {
     const qg_proj_rows& p = projs[i];
@@ -248,7 +251,7 @@ int qgemv_set_rows(int fmt, const qg_proj_rows* projs, int count, int rows, qg_s
     if (rows) {
       if (int st = check_x(p.x, rows, p.k, QG_MAX_ROWS)) return fail(st, "projs[%d].x null, misaligned or bad", i);
     }
-    if (!fuses_quantization(rows) && rows) {
+    if (!fuse && rows) {
       if (int st = check_ws(p.ws, p.ws_bytes, prep_layout(rows, p.k).total, "projs[i]"))
         return fail(st, "projs[%d].ws missing or small (%zu bytes)", i, p.ws_bytes);
     }
@@ -257,7 +260,7 @@ int qgemv_set_rows(int fmt, const qg_proj_rows* projs, int count, int rows, qg_s
   if (rows == 0) return ok();
   if (int st = check_device()) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (fuses_quantization(rows)) {
+  if (fuse) {
     for (int i = 0; i < count; i++) pa[i].x = projs[i].x;
   } else {
     // one quantize launch for all distinct inputs

@@ -46,8 +46,10 @@ struct ProjArg {
 };
 // Q8_0/Q4_0 GEMV for 1..16 rows over up to QG_MAX_SET projections, one launch.
 int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStream_t s);
-// Whether rows this small are quantized inside the GEMV launch.
-bool fuses_quantization(int rows);
+// Whether `rows` rows of length k are quantized inside the GEMV launch (1-2
+// rows whose q8 blocks fit the launch's LDS staging area); otherwise the
+// caller quantizes them into the workspace first.
+bool fuses_quantization(int fmt, int rows, int64_t k);
 
 // Grouped routed-expert Q8_0 GEMV: the plan launch (which also quantizes the
 // x_rows fp32 rows into ws), then the GEMV.

@@ -1098,7 +1098,10 @@ static unsigned persistent_grid(K kernel, size_t lds, int64_t tiles) {
   return (unsigned)(tiles < g ? tiles : g);
 }
 
-bool fuses_quantization(int rows) { return rows >= 1 && rows <= FUSE_MAX_ROWS; }
+bool fuses_quantization(int fmt, int rows, int64_t k) {
+  const int f = fmt == QG_FMT_Q8_0 ? FMT_Q8 : FMT_Q4;
+  return rows >= 1 && rows <= FUSE_MAX_ROWS && (size_t)rows * kbp_of(k) * x_block_bytes(f) <= (size_t)LDS_X_RL;
+}
 
 template <int FMT, int R, bool FUSED>
 static void launch_rl(const SetArgs& a, int lds_x, hipStream_t s) {

@@ -219,7 +219,8 @@ int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const voi
  *   y        [rows][n] fp32, device, written whole, nothing else written
  *   ws       device scratch of ws_bytes >= qg_workspace_bytes(rows, k),
  *            256-aligned, owned by the caller (rows 1-2 are quantized inside
- *            the GEMV launch; the workspace is still checked)
+ *            the GEMV launch when they fit its staging area, as for
+ *            qgemv_set_rows; the workspace is checked either way)
  * Errors (nothing launched): QG_EROWS for rows outside 0..16, QG_ESHAPE for
  * n < 1 or k not whole blocks, QG_EINVAL / QG_EALIGN for null or misaligned
  * pointers, QG_EWORKSPACE for a short workspace, QG_EDEVICE off gfx950. */
@@ -281,7 +282,9 @@ int qgemv_set(int fmt, const qg_proj* projs /*host*/, int count, int rows, qg_st
 
 /* Several projections with the same row count straight from fp32 rows, the
  * whole decode-layer step in as few launches as the row count allows: for
- * rows <= QG_FUSED_ROWS the rows are quantized inside the GEMV launch (one
+ * rows <= QG_FUSED_ROWS whose q8 blocks fit the launch's 80 KiB staging area
+ * (every projection's k up to 72704 at one row and 36352 at two in Q8_0,
+ * 65536 and 32768 in Q4_0) the rows are quantized inside the GEMV launch (one
  * launch, ws unused and may be null); otherwise one launch quantizes every
  * distinct (x, ws) pair into its ws (qg_workspace_bytes(rows, k) bytes;
  * projections that share x may share ws) and a second runs all GEMVs.

@@ -11,6 +11,8 @@ from helpers import TOL, bits, gauss, log, oracle_image, outliers, rel_err
 
 pytestmark = pytest.mark.gpu
 
+FMTS = [(q.Q8_0, O.Q8_0), (q.Q4_0, O.Q4_0)]
+
 
 @pytest.mark.parametrize("E", [8, 64, 256, 300, 1000])
 def test_routing_matches_oracle(E):
@@ -140,3 +142,23 @@ def test_wide_tiles_of_three_at_3_to_8_rows(fmt, n, k, rows):
     for r in (0, rows - 1):
         y1 = call(img, n, k, xd[r:r + 1].contiguous())
         assert np.array_equal(bits(y[r]), bits(y1[0]))
+
+
+@pytest.mark.parametrize("fmt,ofmt", FMTS)
+@pytest.mark.parametrize("k", [40960, 73728])
+def test_long_rows_at_one_and_two_rows(fmt, ofmt, k):
+    """Rows too long for the GEMV launch's staging area (k = 73728: one row of Q8_0 blocks is 82944 bytes; k =
+    40960 at two rows) are quantized by a launch of their own into the workspace first; outputs match the
+    oracle and a row of a two-row call has its bits alone."""
+    n = 100
+    w = gauss((n, k), 0.02, 17, 1).numpy()
+    blocks, img = oracle_image(ofmt, w)
+    fn = q.qgemv_q8_0 if fmt == q.Q8_0 else q.qgemv_q4_0
+    x = gauss((2, k), 1.0, 17, 2).numpy()
+    xd = torch.from_numpy(x).cuda()
+    ws = torch.full((q.workspace_bytes(2, k),), 0x7F, dtype=torch.uint8, device="cuda")  # not zero: must be written
+    y2 = fn(img, n, k, xd, ws=ws)
+    y1 = fn(img, n, k, xd[1:2].contiguous(), ws=ws)
+    yo = O.gemv_q(ofmt, blocks, n, k, x, threads=8)
+    assert rel_err(y2.cpu().numpy(), yo, blocks, ofmt, x) <= TOL
+    assert np.array_equal(bits(y1[0]), bits(y2[1]))
