@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemv.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["qg_host.hip", "qg_api.hip", "qg_quant.hip", "qg_q8.hip", "qg_f16.hip", "qg_moe.hip", "qg_fp8.hip", "qg_probe.hip"]
+SOURCES = ["qg_host.hip", "qg_api.hip", "qg_quant.hip", "qg_q8.hip", "qg_f16.hip", "qg_moe.hip", "qg_fp8.hip", "qg_probe.hip", "qg_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

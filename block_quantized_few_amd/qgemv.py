@@ -68,6 +68,8 @@ _SIGS = {
                                  C.c_void_p, C.c_void_p]),
     "qgemv_q8_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                              C.c_size_t, C.c_void_p]),
+    "qgemv_q8_0_noalloc": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
+                                     C.c_void_p]),
     "qgemv_q4_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                              C.c_size_t, C.c_void_p]),
     "qg_f16_image": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
@@ -310,6 +312,20 @@ def add_rmsnorm_prepare(x, gamma, eps, residual=None, ws=None, h_out=None, y_out
 
 def qgemv_q8_0(image, n, k, x, y=None, ws=None):
     return _qgemv(lib().qgemv_q8_0, image, n, k, x, y, ws)
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def qgemv_q8_0_noalloc(image, n, k, x, y=None):
+    """qgemv_q8_0 on the library's static workspace (qgemv_q8_0_noalloc): no workspace argument, nothing
+    allocated by the library.  y is allocated here (by torch) unless given."""
+    _dev(x, torch.float32, "x")
+    rows = x.shape[0]
+    if y is None:
+        y = torch.empty((rows, n), dtype=torch.float32, device=x.device)
+    _check(lib().qgemv_q8_0_noalloc(_p(image), n, k, _p(x), rows, _p(y), _stream()))
+    return y
 
 
 def qgemv_q4_0(image, n, k, x, y=None, ws=None):

@@ -114,6 +114,7 @@ enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3, QG_FMT_FP8 = 4 };
 #define QG_MAX_ASSIGN 2048    /* assignments per grouped call */
 #define QG_MAX_SET 8          /* projections per qgemv_set call */
 #define QG_FUSED_ROWS 2       /* up to this many rows are quantized inside the GEMV launch */
+#define QG_NOALLOC_SCRATCH_BYTES (1u << 20) /* the static workspace of qgemv_q8_0_noalloc, per GPU */
 
 /* ------------------------------------------------------------ host only --- */
 
@@ -226,6 +227,21 @@ int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const voi
  * pointers, QG_EWORKSPACE for a short workspace, QG_EDEVICE off gfx950. */
 int qgemv_q8_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
                size_t ws_bytes, qg_stream stream);
+
+/* qgemv_q8_0 for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same bits, with the q8
+ * activation rows (3..16 rows) in a static device array of
+ * QG_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU until
+ * the process ends.  The call allocates and frees nothing.  A call whose
+ * qg_workspace_bytes(rows, k) exceeds that size is refused with
+ * QG_EWORKSPACE (every k <= 28672 fits at any row count); 1-2 rows use no
+ * workspace.  All calls on one GPU share the array: two calls that may
+ * overlap on one GPU (different streams, or different host threads without
+ * an ordering) race on it and must not be issued; calls ordered on one
+ * stream are safe.  Other arguments and errors as qgemv_q8_0. */
+int qgemv_q8_0_noalloc(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y,
+                       qg_stream stream);
 
 /* Q4_0 weights x q8 activations; arguments, rows, tiling and errors as
  * qgemv_q8_0 (the q8 lane of the audio-towers page's feature commit, with

@@ -283,6 +283,19 @@ def test_pair_blockdots_validation():
     assert st == -1
 
 
+def test_noalloc_validation():
+    # image, n, k, x, rows, y, stream: a call past the static workspace is refused before any HIP call
+    st, msg = _status("qgemv_q8_0_noalloc", V(A), 64, 28704, V(A), 16, V(A), None)
+    assert st == -5 and "28704" in msg
+    st, msg = _status("qgemv_q8_0_noalloc", V(A), 64, 2048, V(A), 17, V(A), None)
+    assert st == -3
+    st, msg = _status("qgemv_q8_0_noalloc", V(A), 0, 2048, V(A), 4, V(A), None)
+    assert st == -2
+    st, msg = _status("qgemv_q8_0_noalloc", V(A), 64, 2048, V(A), 0, V(A), None)
+    assert st == 0
+    assert q.workspace_bytes(16, 28672) <= q.NOALLOC_SCRATCH_BYTES < q.workspace_bytes(16, 28704)
+
+
 def test_read_probe_validation():
     # src, bytes, grid, inflight, sink, stream
     st, msg = _status("qg_read_probe", V(A), 100, 256, 4, V(A), None)
