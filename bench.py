@@ -340,14 +340,14 @@ class LayerSet:
             for name, _n, k in self.layer:
                 srcs[LAYER_SRC.get(name, 0)] = k
             return self.wbytes + out + sum(self.rows * k * 4 for k in srcs.values())
-        act = 1.0 + 4.0 / 32 + (4.0 / 32 if self.fmt == self.q.Q4_0 else 0.0)
+        act = 1.0 + 4.0 / 32 + (4.0 / 32 if self.fmt in (self.q.Q4_0, self.q.Q4_K) else 0.0)
         return self.wbytes + out + sum(self.rows * k * act for _, _n, k in self.layer)
 
 
 def q8_alg_bytes(q, fmt, n, k, rows, fused):
     """Algorithmic bytes of one q8-lane GEMV launch: the image, the activation rows (fp32 when quantized inside
     the launch, else q8 codes + fp32 scales (+ int32 code sums for Q4_0)), the fp32 outputs."""
-    act = 4.0 if fused else 1.0 + 4.0 / 32 + (4.0 / 32 if fmt == q.Q4_0 else 0.0)
+    act = 4.0 if fused else 1.0 + 4.0 / 32 + (4.0 / 32 if fmt in (q.Q4_0, q.Q4_K) else 0.0)
     return q.image_bytes(fmt, n, k) + rows * k * act + rows * n * 4
 
 
@@ -356,7 +356,7 @@ class LmHead:
 
     def __init__(self, torch, q, synth, lane):
         self.torch, self.q, self.lane = torch, q, lane
-        self.fmt = {"q8_0": q.Q8_0, "q4_0": q.Q4_0, "f16": q.F16, "fp8": q.FP8}[lane]
+        self.fmt = {"q8_0": q.Q8_0, "q4_0": q.Q4_0, "q4_k": q.Q4_K, "f16": q.F16, "fp8": q.FP8}[lane]
         self.imgs = []
         for c in range(2):
             w = synth.gaussian((LM_N, LM_K), 0.02, synth.tensor_seed(4, 0, c), device="cuda")
@@ -375,7 +375,7 @@ class LmHead:
             y = torch.empty((rows, LM_N), device="cuda")
             if self.fmt == q.FP8:
                 ws = q.prepare_fp8(x)
-            elif self.fmt in (q.Q8_0, q.Q4_0):
+            elif self.fmt in (q.Q8_0, q.Q4_0, q.Q4_K):
                 ws = q.prepare_rows(x)
             else:
                 ws = None
@@ -395,7 +395,7 @@ class LmHead:
         wp, wn = ws.data_ptr(), ws.numel()
         if self.fmt == q.FP8:
             return lambda i: L.qgemv_fp8(p[i % 2], LM_N, LM_K, xp, rows, yp, wp, wn, sh)
-        fn = L.qgemv_q8_0 if self.fmt == q.Q8_0 else L.qgemv_q4_0
+        fn = {q.Q8_0: L.qgemv_q8_0, q.Q4_0: L.qgemv_q4_0, q.Q4_K: L.qgemv_q4_k}[self.fmt]
         return lambda i: fn(p[i % 2], LM_N, LM_K, xp, rows, yp, wp, wn, sh)
 
     def kernel_alone(self, L, sh, synth, rows):
@@ -609,14 +609,15 @@ def secondary(torch, q, synth, L, sh, stream, timer, rc, note):
     del ls
     note("1B layer done")
 
-    # Llama-3.2-3B-shaped Q4_0 layer at 1/2/4/8 rows
-    ls = LayerSet(torch, q, synth, LAYER_3B, q.Q4_0, 2, 1)
-    for rows in (1, 2, 4, 8):
-        ls.set_rows(rows, synth, 2)
-        out.append(layer_entry(torch, q, L, sh, stream, timer, rc, ls, "llama-3.2-3b-shaped decode layer", "q4_0",
-                               rows, "llama3b-layer-q4_0"))
-    del ls
-    note("3B layer done")
+    # Llama-3.2-3B-shaped layer at 1/2/4/8 rows: Q4_0, and Q4_K (the K-quant superblock form)
+    for fmt, lane in ((q.Q4_0, "q4_0"), (q.Q4_K, "q4_k")):
+        ls = LayerSet(torch, q, synth, LAYER_3B, fmt, 2 if fmt == q.Q4_0 else 5, 1)
+        for rows in (1, 2, 4, 8):
+            ls.set_rows(rows, synth, 2 if fmt == q.Q4_0 else 5)
+            out.append(layer_entry(torch, q, L, sh, stream, timer, rc, ls, "llama-3.2-3b-shaped decode layer", lane,
+                                   rows, f"llama3b-layer-{lane}"))
+        del ls
+        note(f"3B layer {lane} done")
 
     # LM head, the other lanes at 1/8/16 rows (f16: the workload's second lane; Q4_0: the metric's other format)
     for lane in ("f16", "q4_0"):
@@ -770,7 +771,8 @@ def sweep(torch, q, synth, L, sh, stream, timer):
     ROWSW = [1, 2, 4, 8, 9, 16]
     # decode layers (set launch): 1B Q8_0 and 3B Q4_0
     for lname, lay, fmt, wl, lane in (("llama-3.2-1b layer", LAYER_1B, q.Q8_0, 1, "q8_0"),
-                                      ("llama-3.2-3b layer", LAYER_3B, q.Q4_0, 2, "q4_0")):
+                                      ("llama-3.2-3b layer", LAYER_3B, q.Q4_0, 2, "q4_0"),
+                                      ("llama-3.2-3b layer", LAYER_3B, q.Q4_K, 5, "q4_k")):
         ls = LayerSet(torch, q, synth, lay, fmt, wl, 1)
         for rows in ROWSW:
             ls.set_rows(rows, synth, wl)
@@ -784,11 +786,11 @@ def sweep(torch, q, synth, L, sh, stream, timer):
                 out.append(entry(f"{lname} (7 projections), prepared rows", lane, rows, ls.wbytes, reps, 1))
         del ls
     # LM head in every lane
-    for lane in ("q8_0", "q4_0", "f16", "fp8"):
+    for lane in ("q8_0", "q4_0", "q4_k", "f16", "fp8"):
         h = LmHead(torch, q, synth, lane)
         for rows in ROWSW:
             reps = time_reps(torch, timer, stream, h.call(L, sh, synth, rows), 20)
-            launches = 1 if lane == "f16" or (lane in ("q8_0", "q4_0") and rows <= q.FUSED_ROWS) else 2
+            launches = 1 if lane == "f16" or (lane in ("q8_0", "q4_0", "q4_k") and rows <= q.FUSED_ROWS) else 2
             out.append(entry("lm head 128256x4096", lane, rows, h.wbytes, reps, launches))
             if launches == 2:
                 fn, _, _ = h.kernel_alone(L, sh, synth, rows)
@@ -943,12 +945,15 @@ def profile_one(args, torch, q, synth, L, sh, stream, timer):
     if wl.startswith("lm-head-"):
         lane = wl[len("lm-head-"):]
         prepared = lane.endswith("-prepared")
-        lane = {"q8": "q8_0", "q4": "q4_0"}.get(lane.replace("-prepared", ""), lane.replace("-prepared", ""))
+        lane = {"q8": "q8_0", "q4": "q4_0", "q4k": "q4_k"}.get(lane.replace("-prepared", ""),
+                                                             lane.replace("-prepared", ""))
         h = LmHead(torch, q, synth, lane)
         fn = h.kernel_alone(L, sh, synth, rows)[0] if prepared else h.call(L, sh, synth, rows)
         wbytes = h.wbytes
-    elif wl in ("layer-1b", "layer-3b", "layer-1b-prepared", "layer-3b-prepared"):
-        lay, fmt, wid = (LAYER_1B, q.Q8_0, 1) if wl.startswith("layer-1b") else (LAYER_3B, q.Q4_0, 2)
+    elif wl in ("layer-1b", "layer-3b", "layer-1b-prepared", "layer-3b-prepared", "layer-3b-q4k",
+                "layer-3b-q4k-prepared"):
+        lay, fmt, wid = ((LAYER_1B, q.Q8_0, 1) if wl.startswith("layer-1b") else
+                         (LAYER_3B, q.Q4_K, 5) if wl.startswith("layer-3b-q4k") else (LAYER_3B, q.Q4_0, 2))
         ls = LayerSet(torch, q, synth, lay, fmt, wid, rows)
         if wl.endswith("-prepared") and ls.prepared is not None:
             ls.prepare(L, sh)

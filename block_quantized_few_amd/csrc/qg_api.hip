@@ -12,7 +12,8 @@ using namespace qg;
 namespace {
 
 int check_fmt(int fmt) {
-  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1) or Q4_0 (2)", fmt);
+  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0 && fmt != QG_FMT_Q4_K)
+    return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1), Q4_0 (2) or Q4_K (5)", fmt);
   return QG_OK;
 }
 
@@ -20,6 +21,15 @@ int check_nk(int64_t n, int64_t k) {
   if (n < 1 || n > (1LL << 31) - 16) return fail(QG_ESHAPE, "n=%lld outside 1..2^31-16", (long long)n);
   if (k < QK || k % QK || k > (1LL << 24))
     return fail(QG_ESHAPE, "k=%lld is not a positive multiple of 32 up to 2^24", (long long)k);
+  return QG_OK;
+}
+
+// k in whole blocks of the format: 32 weights, or a 256-weight superblock for
+// Q4_K (the llama-leg page, commit 8624bce).
+int check_nk_fmt(int fmt, int64_t n, int64_t k) {
+  if (int st = check_nk(n, k)) return st;
+  if (fmt == QG_FMT_Q4_K && k % QK_K)
+    return fail(QG_ESHAPE, "k=%lld is not a multiple of 256 (Q4_K superblocks)", (long long)k);
   return QG_OK;
 }
 
@@ -68,7 +78,7 @@ int check_ws(const void* ws, size_t have, size_t need, const char* what) {
 int qgemv_fmt(int fmt, const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
               size_t ws_bytes, qg_stream stream) {
   if (int st = check_rows(rows)) return st;
-  if (int st = check_nk(n, k)) return st;
+  if (int st = check_nk_fmt(fmt, n, k)) return st;
   if (int st = check_image(w_image, "w_image")) return st;
   if (int st = check_y(y)) return st;
   if (rows == 0) return ok();
@@ -93,7 +103,7 @@ extern "C" {
 int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, qg_stream stream) {
   if (fmt != QG_FMT_FP8)
     if (int st = check_fmt(fmt)) return st;
-  if (int st = fmt == QG_FMT_FP8 ? check_fp8_nk(n, k) : check_nk(n, k)) return st;
+  if (int st = fmt == QG_FMT_FP8 ? check_fp8_nk(n, k) : check_nk_fmt(fmt, n, k)) return st;
   if (!w) return fail(QG_EINVAL, "w is null");
   if (!aligned(w, 16)) return fail(QG_EALIGN, "w %p is not 16-byte aligned", (const void*)w);
   if (int st = check_image(image, "image")) return st;
@@ -190,7 +200,7 @@ int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const voi
                    float* y, qg_stream stream) {
   if (int st = check_fmt(fmt)) return st;
   if (int st = check_rows(rows)) return st;
-  if (int st = check_nk(n, k)) return st;
+  if (int st = check_nk_fmt(fmt, n, k)) return st;
   if (int st = check_image(w_image, "w_image")) return st;
   if (int st = check_y(y)) return st;
   if (rows == 0) return ok();
@@ -213,6 +223,11 @@ int qgemv_q4_0(const void* w_image, int64_t n, int64_t k, const float* x, int ro
   return qgemv_fmt(QG_FMT_Q4_0, w_image, n, k, x, rows, y, ws, ws_bytes, stream);
 }
 
+int qgemv_q4_k(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+               size_t ws_bytes, qg_stream stream) {
+  return qgemv_fmt(QG_FMT_Q4_K, w_image, n, k, x, rows, y, ws, ws_bytes, stream);
+}
+
 int qgemv_set(int fmt, const qg_proj* projs, int count, int rows, qg_stream stream) {
   if (int st = check_fmt(fmt)) return st;
   if (!projs || count < 1 || count > QG_MAX_SET) return fail(QG_EINVAL, "count=%d outside 1..%d", count, QG_MAX_SET);
@@ -220,7 +235,7 @@ int qgemv_set(int fmt, const qg_proj* projs, int count, int rows, qg_stream stre
   ProjArg pa[QG_MAX_SET];
   for (int i = 0; i < count; i++) {
     const qg_proj& p = projs[i];
-    if (int st = check_nk(p.n, p.k)) return fail(st, "projs[%d]: n=%lld k=%lld", i, (long long)p.n, (long long)p.k);
+    if (int st = check_nk_fmt(fmt, p.n, p.k)) return fail(st, "projs[%d]: n=%lld k=%lld", i, (long long)p.n, (long long)p.k);
     if (int st = check_image(p.w_image, "w_image")) return fail(st, "projs[%d].w_image null or misaligned", i);
     if (int st = check_y(p.y)) return fail(st, "projs[%d].y null or misaligned", i);
     if (rows) {
@@ -245,7 +260,7 @@ int qgemv_set_rows(int fmt, const qg_proj_rows* projs, int count, int rows, qg_s
   ProjArg pa[QG_MAX_SET];
   for (int i = 0; i < count; i++) {
     const qg_proj_rows& p = projs[i];
-    if (int st = check_nk(p.n, p.k)) return fail(st, "projs[%d]: n=%lld k=%lld", i, (long long)p.n, (long long)p.k);
+    if (int st = check_nk_fmt(fmt, p.n, p.k)) return fail(st, "projs[%d]: n=%lld k=%lld", i, (long long)p.n, (long long)p.k);
     if (int st = check_image(p.w_image, "w_image")) return fail(st, "projs[%d].w_image null or misaligned", i);
     if (int st = check_y(p.y)) return fail(st, "projs[%d].y null or misaligned", i);
     if (rows) {
@@ -519,7 +534,7 @@ int qgemv_blockdots(int fmt, const void* w_image, int64_t n, int64_t k, const in
                     qg_stream stream) {
   if (int st = check_fmt(fmt)) return st;
   if (int st = check_rows(rows)) return st;
-  if (int st = check_nk(n, k)) return st;
+  if (int st = check_nk_fmt(fmt, n, k)) return st;
   if (int st = check_image(w_image, "w_image")) return st;
   if (!isum) return fail(QG_EINVAL, "isum is null");
   if (!qx) return fail(QG_EINVAL, "qx is null");
@@ -534,7 +549,7 @@ int qgemv_blockdots_pairs(int fmt, const void* w_image, int64_t n, int64_t k, co
                           int rows, int32_t* isum, qg_stream stream) {
   if (int st = check_fmt(fmt)) return st;
   if (rows < 3 || rows > QG_MAX_ROWS) return fail(QG_EROWS, "rows=%d outside 3..%d (pair order)", rows, QG_MAX_ROWS);
-  if (int st = check_nk(n, k)) return st;
+  if (int st = check_nk_fmt(fmt, n, k)) return st;
   if (int st = check_image(w_image, "w_image")) return st;
   if (!isum) return fail(QG_EINVAL, "isum is null");
   if (int st = check_ws(ws, ws_bytes, prep_layout(rows, k).total, "the prepared rows")) return st;

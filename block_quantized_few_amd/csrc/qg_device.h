@@ -8,7 +8,10 @@
 namespace qg {
 
 constexpr int WAVE = 64;
-constexpr int FMT_Q8 = 1, FMT_Q4 = 2;
+constexpr int FMT_Q8 = 1, FMT_Q4 = 2, FMT_Q4K = 5;  // the QG_FMT_* values of the formats
+
+// Whether a format's codes are 4-bit nibbles (Q4_0: c - 8; Q4_K: raw q).
+__host__ __device__ constexpr bool nibble_fmt(int fmt) { return fmt == FMT_Q4 || fmt == FMT_Q4K; }
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -63,6 +66,29 @@ __device__ __forceinline__ int dot_q4(uint4 p, uint4 xl, uint4 xh, int nsx) {
   s = __builtin_amdgcn_sdot4((int)((p.z >> 4) & M), (int)xh.z, s, false);
   s = __builtin_amdgcn_sdot4((int)((p.w >> 4) & M), (int)xh.w, s, false);
   return s;
+}
+
+// Q4_K: sub-block j's (0..7) scale D = d * sc[j] and offset M = dmin * m[j]
+// from its superblock header h (h.x = d | dmin << 16, then the twelve bytes
+// of 6-bit fields: for j < 4, sc = byte j & 63 and m = byte j+4 & 63; for
+// j >= 4, sc = (byte j+4 & 15) | (byte j-4 >> 6) << 4 and m = (byte j+4 >> 4)
+// | (byte j >> 6) << 4).  Both products are exact in fp32.
+__device__ __forceinline__ void q4k_dm(uint4 h, int j, float& D, float& M) {
+  const int sh = (j & 3) * 8;
+  const unsigned a = (h.y >> sh) & 255u, b = (h.z >> sh) & 255u, c = (h.w >> sh) & 255u;
+  const unsigned sc = j < 4 ? (a & 63u) : ((c & 15u) | ((a >> 6) << 4));
+  const unsigned m = j < 4 ? (b & 63u) : ((c >> 4) | ((b >> 6) << 4));
+  D = h2f((uint16_t)(h.x & 0xffffu)) * (float)sc;
+  M = h2f((uint16_t)(h.x >> 16)) * (float)m;
+}
+
+// One Q4_K sub-block's share of an output: acc + dx * (D * isum - M * xsum),
+// isum the integer dot of the raw codes with the q8 codes and xsum the sum of
+// those q8 codes; the same operations in every kernel, so a row's bits do not
+// depend on which kernel or how many rows.
+__device__ __forceinline__ float q4k_acc(float acc, int isum, int xsum, float D, float M, float dx) {
+  const float t = __builtin_fmaf((float)isum, D, -((float)xsum * M));
+  return __builtin_fmaf(t, dx, acc);
 }
 
 // Cross-lane moves inside groups of four lanes (DPP quad permutes).

@@ -107,6 +107,7 @@ size_t qg_image_bytes(int fmt, int64_t n, int64_t k) {
   if (n < 1 || k < 1) return 0;
   if (fmt == QG_FMT_F16) return k % 8 ? 0 : (size_t)f16_image_bytes(n, k);
   if (fmt == QG_FMT_FP8) return k % 128 ? 0 : fp8_image_bytes(n, k);
+  if (fmt == QG_FMT_Q4_K) return k % QK_K ? 0 : image_total_bytes(fmt, n, k);
   if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0) return 0;
   if (k % QK) return 0;
   return image_total_bytes(fmt, n, k);
@@ -133,9 +134,14 @@ size_t qg_grouped_workspace_bytes(int x_rows, int64_t k, int m) {
 }
 
 static int check_pack_args(int fmt, const void* a, int64_t n, int64_t k, const void* b) {
-  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0 && fmt != QG_FMT_F16 && fmt != QG_FMT_FP8)
-    return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1), Q4_0 (2), F16 (3) or FP8 (4)", fmt);
+  if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4_0 && fmt != QG_FMT_F16 && fmt != QG_FMT_FP8 && fmt != QG_FMT_Q4_K)
+    return fail(QG_EINVAL, "fmt=%d is not Q8_0 (1), Q4_0 (2), F16 (3), FP8 (4) or Q4_K (5)", fmt);
   if (!a || !b) return fail(QG_EINVAL, "null buffer");
+  if (fmt == QG_FMT_Q4_K) {
+    if (n < 1 || k < QK_K || k % QK_K)
+      return fail(QG_ESHAPE, "n=%lld k=%lld (need n >= 1, k a positive multiple of 256)", (long long)n, (long long)k);
+    return QG_OK;
+  }
   if (fmt == QG_FMT_FP8) {
     if (n < 1 || k < 128 || k % 128)
       return fail(QG_ESHAPE, "n=%lld k=%lld (need n >= 1, k a positive multiple of 128)", (long long)n, (long long)k);
@@ -190,9 +196,45 @@ static void fp8_pack_host(uint8_t* canon, int64_t n, int64_t k, uint8_t* img, bo
   else memcpy(sc, canon + n * k, (size_t)(nb * kg * 4));
 }
 
+// Q4_K image <-> canonical superblocks: sub-block j of superblock s of row o
+// (canonical weights 32j .. 32j+31: the low nibbles of qs[32(j/2) ..] for even
+// j, the high nibbles for odd j) goes to the code cell of block 8s + j in the
+// Q4_0 nibble order; the 16-byte header to the header plane.
+static void q4k_pack_host(uint8_t* canon, int64_t n, int64_t k, uint8_t* img, bool unpack) {
+  const int64_t ns = k / QK_K, kbp = kbp_of(k);
+  uint8_t* hdr = img + image_scale_offset(FMT_ID_Q4K, n, k);
+  for (int64_t o = 0; o < n; o++)
+    for (int64_t s = 0; s < ns; s++) {
+      uint8_t* sb = canon + (o * ns + s) * Q4K_CANON;
+      uint8_t* h = hdr + q4k_header_offset(o, s, kbp);
+      if (unpack) memcpy(sb, h, 16);
+      else memcpy(h, sb, 16);
+      for (int j = 0; j < 8; j++) {
+        uint8_t* cell = img + cell_row_offset(FMT_ID_Q4K, o, 8 * s + j, kbp);
+        uint8_t* qs = sb + 16 + 32 * (j / 2);
+        const int hi = j & 1;
+        for (int l = 0; l < 16; l++) {
+          if (unpack) {
+            const int c0 = cell[l] & 15, c1 = cell[l] >> 4;  // codes l and l + 16 of the sub-block
+            qs[l] = (uint8_t)(hi ? ((qs[l] & 15) | (c0 << 4)) : ((qs[l] & 0xF0) | c0));
+            qs[l + 16] = (uint8_t)(hi ? ((qs[l + 16] & 15) | (c1 << 4)) : ((qs[l + 16] & 0xF0) | c1));
+          } else {
+            const int c0 = hi ? qs[l] >> 4 : qs[l] & 15, c1 = hi ? qs[l + 16] >> 4 : qs[l + 16] & 15;
+            cell[l] = (uint8_t)(c0 | (c1 << 4));
+          }
+        }
+      }
+    }
+}
+
 int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image) {
   int st = check_pack_args(fmt, blocks, n, k, image);
   if (st) return st;
+  if (fmt == QG_FMT_Q4_K) {
+    memset(image, 0, image_total_bytes(fmt, n, k));
+    q4k_pack_host((uint8_t*)blocks, n, k, (uint8_t*)image, false);
+    return ok();
+  }
   if (fmt == QG_FMT_FP8) {
     memset(image, 0, fp8_image_bytes(n, k));
     fp8_pack_host((uint8_t*)blocks, n, k, (uint8_t*)image, false);
@@ -223,6 +265,11 @@ int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image
 int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* blocks) {
   int st = check_pack_args(fmt, image, n, k, blocks);
   if (st) return st;
+  if (fmt == QG_FMT_Q4_K) {
+    memset(blocks, 0, (size_t)(n * (k / QK_K) * Q4K_CANON));
+    q4k_pack_host((uint8_t*)blocks, n, k, const_cast<uint8_t*>((const uint8_t*)image), true);
+    return ok();
+  }
   if (fmt == QG_FMT_FP8) {
     fp8_pack_host((uint8_t*)blocks, n, k, (uint8_t*)image, true);
     return ok();

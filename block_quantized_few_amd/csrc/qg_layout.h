@@ -18,6 +18,14 @@
 //   Scales (fp16) at the next 256-byte boundary: (t*kbp + b)*16 + i.
 // For n % 16 == 0 and k % 512 == 0 the image holds exactly the canonical bytes
 // per weight.
+//   Q4_K (k % 256 == 0): the code plane of Q4_0, sub-block b of a row (32
+//        weights, sub-block b % 8 of superblock b / 8) in one 16-byte cell with
+//        the Q4_0 nibble order (byte l: code l low, code l + 16 high); in place
+//        of the fp16 scales, the superblocks' 16-byte headers (fp16 d, fp16
+//        dmin, the twelve bytes of 6-bit sub-scales and sub-mins, as in the
+//        canonical block): tile t, superblock s, row i at byte
+//        ((t*(kbp/8) + s)*16 + i)*16 of that plane -- the same 2 bytes per
+//        32 weights, so the image also holds 144 bytes per 256 weights.
 //
 // Prepared activation rows (workspace of `rows` rows of length k), each plane
 // on a 256-byte boundary, pad blocks zero, in one of two orders:
@@ -54,6 +62,9 @@ constexpr int GROUP = 16;  // block padding unit
 constexpr int TILE = 16;   // rows per tile
 constexpr int Q8_CANON = 34;
 constexpr int Q4_CANON = 18;
+constexpr int QK_K = 256;       // weights per K-quant superblock
+constexpr int Q4K_CANON = 144;  // canonical Q4_K superblock bytes
+constexpr int FMT_ID_Q4K = 5;   // QG_FMT_Q4_K
 
 QG_HD int64_t kb_of(int64_t k) { return k / QK; }
 QG_HD int64_t kbp_of(int64_t k) { return ((k / QK + GROUP - 1) / GROUP) * GROUP; }
@@ -96,6 +107,10 @@ QG_HD size_t cell_row_offset(int fmt, int64_t o, int64_t b, int64_t kbp) {
 // Index (in fp16 units) of row o's scale of block b.
 QG_HD size_t scale_index(int64_t o, int64_t b, int64_t kbp) {
   return ((size_t)(o / TILE) * (size_t)kbp + (size_t)b) * TILE + (size_t)(o % TILE);
+}
+// Q4_K: byte offset, inside the scale plane, of row o's header of superblock s.
+QG_HD size_t q4k_header_offset(int64_t o, int64_t s, int64_t kbp) {
+  return (((size_t)(o / TILE) * (size_t)(kbp / 8) + (size_t)s) * TILE + (size_t)(o % TILE)) * 16;
 }
 
 struct PrepLayout {

@@ -35,7 +35,7 @@ constexpr int WAVES = WG / WAVE;
 constexpr int LDS_X_RL = 80 * 1024;   // staged rows, RL (leaves room for 2+ workgroups per CU)
 constexpr int FUSE_MAX_ROWS = 2;      // rows quantized inside the GEMV launch
 
-__host__ __device__ inline int x_block_bytes(int fmt) { return fmt == FMT_Q4 ? 40 : 36; }
+__host__ __device__ inline int x_block_bytes(int fmt) { return nibble_fmt(fmt) ? 40 : 36; }
 
 // Block index of staged slot `slot` of a chunk that starts at in-part index u0.
 // Slots are ordered (u, wave part, lane part), so lanes that step together read
@@ -77,7 +77,7 @@ __device__ void stage_rl(uint8_t* lds, const Prep& prep, const int* s_src, int k
     for (int e = tid; e < nslot; e += WG) {
       const int b = slot_block(pl, u0, e);
       ld[r * nslot + e] = prep.dx[src + b];
-      if (FMT == FMT_Q4) ln[r * nslot + e] = prep.nsx[src + b];
+      if (FMT != FMT_Q8) ln[r * nslot + e] = prep.nsx[src + b];
     }
   }
 }
@@ -161,7 +161,7 @@ __device__ __forceinline__ void xq_store(const XQuarterT<GLU>& xv, uint8_t* lds,
   *reinterpret_cast<uint2*>(lds + ((size_t)r * nslot + slot) * 32 + q * 8) = make_uint2(lo, hi);
   if (q == 0) {
     reinterpret_cast<float*>(lds + (size_t)R * nslot * 32)[r * nslot + slot] = d;
-    if (FMT == FMT_Q4) reinterpret_cast<int*>(lds + (size_t)R * nslot * 36)[r * nslot + slot] = -8 * sum;
+    if (FMT != FMT_Q8) reinterpret_cast<int*>(lds + (size_t)R * nslot * 36)[r * nslot + slot] = -8 * sum;
   }
 }
 
@@ -214,10 +214,14 @@ struct WBlock {
   uint4 lo;
   uint4 hi;  // Q8_0 high half
   uint16_t sc;
+  uint4 hdr;  // Q4_K: the 16-byte header of the block's superblock
 };
 
 // Block b of the lane's row.  The address is the tile's base (uniform) plus a
-// 32-bit lane offset, so the loads take the scalar-base form.
+// 32-bit lane offset, so the loads take the scalar-base form.  Q4_K: soff
+// points at the row's header of superblock 0 (fp16 units), superblocks 128
+// units apart; the lane parts of a row that step through one superblock read
+// the same 16 bytes.
 template <int FMT>
 __device__ __forceinline__ WBlock<FMT> load_block(const uint8_t* __restrict__ tcode, uint32_t woff,
                                                   const uint16_t* __restrict__ tscale, uint32_t soff, int b) {
@@ -225,17 +229,30 @@ __device__ __forceinline__ WBlock<FMT> load_block(const uint8_t* __restrict__ tc
   WBlock<FMT> w;
   w.lo = ld16_stream(tcode + (woff + (uint32_t)b * CB));
   if (FMT == FMT_Q8) w.hi = ld16_stream(tcode + (woff + (uint32_t)b * CB + 256));
-  w.sc = ld2_stream(tscale + (soff + (uint32_t)b * TILE));
+  if (FMT == FMT_Q4K) w.hdr = ld16_stream(tscale + (soff + (uint32_t)(b >> 3) * 128));
+  else w.sc = ld2_stream(tscale + (soff + (uint32_t)b * TILE));
   return w;
 }
 
 // acc[r] = fma(isum, dw * dx, acc[r]) for one block, its activation blocks at
-// staged slot `slot`.
+// staged slot `slot` (Q4_K: q4k_acc of sub-block `sub` of its superblock).
 template <int FMT, int R>
 __device__ __forceinline__ void compute_block(float (&acc)[R], const WBlock<FMT>& w, const uint8_t* lds, int nslot,
-                                              int slot) {
+                                              int slot, int sub) {
   const float* ld = reinterpret_cast<const float*>(lds + (size_t)R * nslot * 32);
   const int* ln = reinterpret_cast<const int*>(lds + (size_t)R * nslot * 36);
+  if constexpr (FMT == FMT_Q4K) {
+    float D, M;
+    q4k_dm(w.hdr, sub, D, M);
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const uint8_t* xb = lds + ((size_t)r * nslot + slot) * 32;
+      const uint4 xl = ld16(xb), xh = ld16(xb + 16);
+      const int isum = dot_q4(w.lo, xl, xh, 0);
+      acc[r] = q4k_acc(acc[r], isum, -(ln[r * nslot + slot] / 8), D, M, ld[r * nslot + slot]);
+    }
+    return;
+  }
   const float dw = h2f(w.sc);
 #pragma unroll
   for (int r = 0; r < R; r++) {
@@ -274,7 +291,7 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
   const uint16_t* tscale = ta.scale + scale_index(t0 * TILE, 0, ta.kbp);
   const uint32_t woff = (uint32_t)((rc >> 4) - t0) * (uint32_t)ta.kbp * (FMT == FMT_Q8 ? 512u : 256u) +
                         (uint32_t)(rc & 15) * 16u;
-  const uint32_t soff = (uint32_t)((rc >> 4) - t0) * (uint32_t)ta.kbp * 16u + (uint32_t)(rc & 15);
+  const uint32_t soff = (uint32_t)((rc >> 4) - t0) * (uint32_t)ta.kbp * 16u + (uint32_t)(rc & 15) * (FMT == FMT_Q4K ? 8u : 1u);
 
   float acc[R];
 #pragma unroll
@@ -306,7 +323,7 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
 #pragma unroll
     for (int j = 0; j < LA; j++) {
       if (u + j < pl.BS) {
-        compute_block<FMT, R>(acc, w[j], lds, nslot, slot + (j << pl.lgP));
+        compute_block<FMT, R>(acc, w[j], lds, nslot, slot + (j << pl.lgP), (bpart + pl.H * (u + j)) & 7);
         if (u + j + LA < pl.BS) w[j] = load_block<FMT>(tcode, woff, tscale, soff, bpart + pl.H * (u + j + LA));
       }
     }
@@ -361,8 +378,14 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
 // allow without spilling: the activation chunk is loaded once per NT KB of
 // weights, and fewer tiles fit the workgroups resident at once).
 __host__ __device__ constexpr int mp_w2(int H) { return H >= 4 ? 2 : 1; }
-__host__ __device__ constexpr int mp_nt(int H, int G, bool wide) {
+__host__ __device__ constexpr int mp_nt_base(int H, int G, bool wide) {
   return wide ? (H == 2 || H == 4 ? (G == 2 ? 2 : 3) : (G == 2 ? 1 : 2)) : (H == 8 || G == 2 ? 1 : 2);
+}
+// Q4_K keeps each tile's fp32 D and M in registers as well: its wide tiles of
+// two row groups take one tile fewer (two would spill).
+__host__ __device__ constexpr int mp_nt(int H, int G, bool wide, int fmt = FMT_Q8) {
+  return fmt == FMT_Q4K && wide && G == 2 && mp_nt_base(H, G, wide) > 1 ? mp_nt_base(H, G, wide) - 1
+                                                                        : mp_nt_base(H, G, wide);
 }
 // block-pair steps in flight per wave (even: step j's lane-part pair is j & 1)
 __host__ __device__ constexpr int mp_la(int NT, int G) { return NT * G == 1 ? 4 : 2; }
@@ -393,6 +416,7 @@ struct MpAddr {
   int groups;               // row groups in the workspace
   const uint16_t* sl[NT];   // the wave's staged scales of each tile (LDS), from block sb0 on
   int sb0;
+  int mplane;               // Q4_K: floats from the staged D plane to the M plane
   uint32_t soff;            // lane offset in a staged block pair (fp16 units)
   // Gathered row order (rows picked by the tile's s_src map): this lane's
   // element (row * kbp + its block's offset in the pair) per row group, and
@@ -411,7 +435,7 @@ struct MpAddr {
 template <int FMT>
 __device__ __forceinline__ v4i pair_dots(uint4 araw, uint4 x, int ns, int sh) {
   uint4 av = araw;
-  if (FMT == FMT_Q4) {
+  if (nibble_fmt(FMT)) {
     av.x = (av.x >> sh) & 0x0F0F0F0Fu;
     av.y = (av.y >> sh) & 0x0F0F0F0Fu;
     av.z = (av.z >> sh) & 0x0F0F0F0Fu;
@@ -443,7 +467,7 @@ __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad,
       const int64_t e = ad.gsrc[g] + b;
       st.x[g] = ad.gon ? ld16(ad.xc + (size_t)e * 32 + ad.ghalf) : make_uint4(0u, 0u, 0u, 0u);
       st.dx[g] = ad.xd[e];
-      st.ns[g] = FMT == FMT_Q4 ? ad.xn[e] : 0;
+      st.ns[g] = FMT != FMT_Q8 ? ad.xn[e] : 0;
     }
     return;
   }
@@ -452,13 +476,44 @@ __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad,
   for (int g = 0; g < G; g++) {
     st.x[g] = ad.xon ? ld16(ad.xc + ((chunk0 + g) * 64 + lane) * 16) : make_uint4(0u, 0u, 0u, 0u);
     st.dx[g] = ad.xd[(chunk0 + g) * 16 + (lane & 15)];
-    st.ns[g] = FMT == FMT_Q4 ? ad.xn[(chunk0 + g) * 16 + (lane & 15)] : 0;
+    st.ns[g] = FMT != FMT_Q8 ? ad.xn[(chunk0 + g) * 16 + (lane & 15)] : 0;
   }
 }
 
 template <int FMT, int NT, int G, int PP, bool SEQ>
 __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, const MpStep<NT, G>& st,
                                            const MpAddr<NT>& ad, int sh) {
+  if constexpr (FMT == FMT_Q4K) {
+    // D and M of rows 4q .. 4q+3 of the lane's block, staged as fp32 in the
+    // wave's LDS (D plane, then M plane, each [block][16 rows])
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      const float* dp = reinterpret_cast<const float*>(ad.sl[t]) + (st.b - ad.sb0) * TILE + ad.soff;
+      const float4 Dv = *reinterpret_cast<const float4*>(dp);
+      const float4 Mv = *reinterpret_cast<const float4*>(dp + ad.mplane);
+      const float D[4] = {Dv.x, Dv.y, Dv.z, Dv.w}, M[4] = {Mv.x, Mv.y, Mv.z, Mv.w};
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        const v4i c = pair_dots<FMT>(st.a[t], st.x[g], 0, sh);
+        const int xsum = -(st.ns[g] / 8);
+        const float dx = st.dx[g];
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          float& r = acc[t][PP == 1 ? 0 : pp][g][v];
+          const float tv = __builtin_fmaf((float)c[v], D[v], -((float)xsum * M[v]));
+          if (SEQ) {
+            // block b (this lane), then block b+1 (lane i ^ 8)
+            const float pt = lane_xor8(tv), pdx = lane_xor8(dx);
+            r = __builtin_fmaf(tv, dx, r);
+            r = __builtin_fmaf(pt, pdx, r);
+          } else {
+            r = __builtin_fmaf(tv, dx, r);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     // fp16 scales of rows 4q .. 4q+3 of the lane's block, from the wave's staged copy
@@ -485,11 +540,26 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
   }
 }
 
+// LDS of the pair kernel: the combine area (red; a wave's slice at wave * NV *
+// 64 floats) and the waves' staged scales (scl; a wave's NT tiles from
+// wave * NT * sc_stride).  Q4_K stages fp32 D and M, four times the bytes of
+// fp16 scales, so its set kernels give a wave one region for both (red_ws
+// floats = scl_ws / 2 fp16 units apart): a wave writes its combine values only
+// after its own step loop, and stages the next tile's scales only after the
+// combine's last barrier, so a workgroup needs the larger of the two per wave,
+// not their sum.
+struct MpLds {
+  float* red;
+  int red_ws;
+  uint16_t* scl;
+  int scl_ws;
+};
+
 // One MP tile: groups of S*W2 waves, each group NT 16-row image tiles; G
 // groups of eight activation rows from the pair-order workspace, or (GATHER)
 // from a row-order workspace through the tile's s_src map.
 template <int FMT, int H, int G, int NT, bool GATHER, bool PF = false>
-__device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, int count = 1, int64_t row_stride = 0) {
+__device__ void mp_tile(const TileArgs& ta, int R, const MpLds& ml, int count = 1, int64_t row_stride = 0) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
   constexpr bool SEQ = H == 1;
   constexpr int W2 = mp_w2(H);
@@ -500,13 +570,17 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, in
   const int g = wave / gw, wg = wave - g * gw, s = wg / W2, hw = wg - s * W2;
   const int i = lane & 15, q = lane >> 4;
   const int64_t ntiles = np_of(ta.n) / TILE;
-  const int sc_stride = pl.H * pl.BS * TILE;  // fp16 scales of one tile's wave part
+  // staged scales of one tile's wave part, in fp16 units: fp16 per (row, block); Q4_K fp32 D and M
+  const int sc_stride = pl.H * pl.BS * TILE * (FMT == FMT_Q4K ? 4 : 1);
   MpAddr<NT> ad;
   const uint16_t* scale[NT];
 #pragma unroll
-  for (int t = 0; t < NT; t++) ad.sl[t] = scl + (wave * NT + t) * sc_stride;
+  for (int t = 0; t < NT; t++)
+    ad.sl[t] = FMT == FMT_Q4K ? ml.scl + wave * ml.scl_ws + t * sc_stride : ml.scl + (wave * NT + t) * sc_stride;
+  float* red = ml.red;
   ad.aoff = pair_aoff<FMT>(i, q);
   ad.soff = (uint32_t)((i >> 3) * 16 + 4 * q);
+  ad.mplane = pl.H * pl.BS * TILE;
   ad.xc = reinterpret_cast<const uint8_t*>(ta.prep.codes);
   ad.xd = ta.prep.dx;
   ad.xn = ta.prep.nsx;
@@ -553,9 +627,11 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, in
       ad.code[t] = ta.code + ((size_t)it * ta.kbp) * CB;
       scale[t] = ta.scale + ((size_t)it * ta.kbp) * TILE;
     }
+    if constexpr (FMT != FMT_Q4K) {
 #pragma unroll
-    for (int t = 0; t < NT; t++)
-      if (lane < nsv) sv[t] = ld16(scale[t] + (size_t)ad.sb0 * TILE + lane * 8);
+      for (int t = 0; t < NT; t++)
+        if (lane < nsv) sv[t] = ld16(scale[t] + (size_t)ad.sb0 * TILE + lane * 8);
+    }
 #pragma unroll
     for (int jj = 0; jj < MP_LA; jj++)
       if (jj < nsteps) mp_load<FMT, NT, G, GATHER>(st[jj], ad, lane, blk(jj));
@@ -563,6 +639,31 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, in
   // The started tile's scales into the wave's LDS region (the wave is done
   // reading the previous tile's).
   auto stage = [&]() {
+    if constexpr (FMT == FMT_Q4K) {
+      // the headers of the superblocks the wave part touches, decoded into
+      // fp32 D and M per (block, row)
+      const int nblk = pl.H * pl.BS, sb_lo = ad.sb0 >> 3, nsb = ((ad.sb0 + nblk - 1) >> 3) - sb_lo + 1;
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+        const uint8_t* hb = reinterpret_cast<const uint8_t*>(scale[t]);
+        float* dst = reinterpret_cast<float*>(const_cast<uint16_t*>(ad.sl[t]));
+        for (int e = lane; e < nsb * TILE; e += WAVE) {
+          const int sbi = sb_lo + (e >> 4), row = e & 15;
+          const uint4 h = ld16(hb + ((size_t)sbi * TILE + row) * 16);
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const int b = sbi * 8 + j - ad.sb0;
+            if (b >= 0 && b < nblk) {
+              float D, M;
+              q4k_dm(h, j, D, M);
+              dst[b * TILE + row] = D;
+              dst[ad.mplane + b * TILE + row] = M;
+            }
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < NT; t++) {
       uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(ad.sl[t]));
@@ -621,7 +722,9 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, in
 #pragma unroll
         for (int gg = 0; gg < G; gg++)
 #pragma unroll
-          for (int v = 0; v < 4; v++) red[(wave * NV + (t * G + gg) * 4 + v) * WAVE + lane] = res[t][gg][v];
+          for (int v = 0; v < 4; v++)
+            red[(FMT == FMT_Q4K ? wave * ml.red_ws : wave * NV * WAVE) + ((t * G + gg) * 4 + v) * WAVE + lane] =
+                res[t][gg][v];
       __syncthreads();
       if (wg == 0) {
 #pragma unroll
@@ -634,8 +737,9 @@ __device__ void mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl, in
               const int w0 = g * gw;
               float x = 0.0f;
               for (int s2 = 0; s2 < pl.S; s2++) {
-                float part = red[(w0 + s2 * W2) * NV * WAVE + o];
-                if (W2 == 2) part = part + red[(w0 + s2 * W2 + 1) * NV * WAVE + o];
+                const int ws = FMT == FMT_Q4K ? ml.red_ws : NV * WAVE;
+                float part = red[(w0 + s2 * W2) * ws + o];
+                if (W2 == 2) part = part + red[(w0 + s2 * W2 + 1) * ws + o];
                 x = s2 == 0 ? part : x + part;
               }
               res[t][gg][v] = x;
@@ -683,6 +787,7 @@ struct SetArgs {
   ProjDev p[QG_MAX_SET];
   int count;
   int total_tiles;
+  int wave_lds;  // pair kernel: bytes of LDS per wave (combine slice and staged scales)
 };
 
 __device__ __forceinline__ void identity_map(int* s_map) {
@@ -751,13 +856,13 @@ enum { MP_NARROW = 0, MP_WIDE = 1, MP_MIXED = 2 };
 // The workgroup's tiles of one projection at width W (tiles row0, row0 +
 // stride, ...: cnt of them, one unless PF).
 template <int FMT, int G, bool W, bool PF>
-__device__ __forceinline__ void mp_tiles(const TileArgs& ta, int R, float* red, uint16_t* scl, int cnt,
+__device__ __forceinline__ void mp_tiles(const TileArgs& ta, int R, const MpLds& ml, int cnt,
                                          int64_t stride) {
   const int H = ta.pl.H;
-  if (H == 1) mp_tile<FMT, 1, G, mp_nt(1, G, W), false, PF>(ta, R, red, scl, cnt, stride);
-  else if (H == 2) mp_tile<FMT, 2, G, mp_nt(2, G, W), false, PF>(ta, R, red, scl, cnt, stride);
-  else if (H == 4) mp_tile<FMT, 4, G, mp_nt(4, G, W), false, PF>(ta, R, red, scl, cnt, stride);
-  else mp_tile<FMT, 8, G, mp_nt(8, G, W), false, PF>(ta, R, red, scl, cnt, stride);
+  if (H == 1) mp_tile<FMT, 1, G, mp_nt(1, G, W, FMT), false, PF>(ta, R, ml, cnt, stride);
+  else if (H == 2) mp_tile<FMT, 2, G, mp_nt(2, G, W, FMT), false, PF>(ta, R, ml, cnt, stride);
+  else if (H == 4) mp_tile<FMT, 4, G, mp_nt(4, G, W, FMT), false, PF>(ta, R, ml, cnt, stride);
+  else mp_tile<FMT, 8, G, mp_nt(8, G, W, FMT), false, PF>(ta, R, ml, cnt, stride);
 }
 
 // PF: each workgroup's narrow tiles of a projection in one mp_tile call, the
@@ -768,8 +873,13 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_map[2 * QG_MAX_ROWS];
   identity_map(s_map);
-  float* red = reinterpret_cast<float*>(lds);  // combine area, then the waves' staged scales
-  uint16_t* scl = reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4);
+  // Q4_K: one region of a.wave_lds bytes per wave for its combine slice and its staged scales; otherwise the
+  // combine area, then the staged scales
+  const MpLds ml = FMT == FMT_Q4K
+                       ? MpLds{reinterpret_cast<float*>(lds), a.wave_lds / 4, reinterpret_cast<uint16_t*>(lds),
+                               a.wave_lds / 2}
+                       : MpLds{reinterpret_cast<float*>(lds), 0,
+                               reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4), 0};
   constexpr bool MP_PF = PF && WIDTH == MP_NARROW && FMT == FMT_Q8;
   for (int tile = blockIdx.x; tile < a.total_tiles;) {
     int p = 0, t0 = tile;
@@ -781,12 +891,12 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mp
     const int cnt = MP_PF ? (d.tiles - 1 - t0) / (int)gridDim.x + 1 : 1;
     const int64_t stride = (int64_t)gridDim.x * d.rows_per_tile;
     if constexpr (WIDTH == MP_NARROW) {
-      mp_tiles<FMT, G, false, MP_PF>(ta, R, red, scl, cnt, stride);
+      mp_tiles<FMT, G, false, MP_PF>(ta, R, ml, cnt, stride);
     } else if constexpr (WIDTH == MP_WIDE) {
-      mp_tiles<FMT, G, true, false>(ta, R, red, scl, cnt, stride);
+      mp_tiles<FMT, G, true, false>(ta, R, ml, cnt, stride);
     } else {
-      if (d.wide) mp_tiles<FMT, G, true, false>(ta, R, red, scl, cnt, stride);
-      else mp_tiles<FMT, G, false, false>(ta, R, red, scl, cnt, stride);
+      if (d.wide) mp_tiles<FMT, G, true, false>(ta, R, ml, cnt, stride);
+      else mp_tiles<FMT, G, false, false>(ta, R, ml, cnt, stride);
     }
     tile += cnt * (int)gridDim.x;
   }
@@ -944,12 +1054,12 @@ __global__ __launch_bounds__(WG) void grouped_kernel(const uint8_t* __restrict__
 // Rows of a grouped item in the pair kernel's tiles (one 16-row image tile per
 // wave group), the activation rows gathered from the row-order workspace.
 template <int G>
-__device__ __forceinline__ void grouped_mp_tile(const TileArgs& ta, int R, float* red, uint16_t* scl) {
+__device__ __forceinline__ void grouped_mp_tile(const TileArgs& ta, int R, const MpLds& ml) {
   switch (ta.pl.H) {
-    case 1: mp_tile<FMT_Q8, 1, G, 1, true>(ta, R, red, scl); break;
-    case 2: mp_tile<FMT_Q8, 2, G, 1, true>(ta, R, red, scl); break;
-    case 4: mp_tile<FMT_Q8, 4, G, 1, true>(ta, R, red, scl); break;
-    default: mp_tile<FMT_Q8, 8, G, 1, true>(ta, R, red, scl); break;
+    case 1: mp_tile<FMT_Q8, 1, G, 1, true>(ta, R, ml); break;
+    case 2: mp_tile<FMT_Q8, 2, G, 1, true>(ta, R, ml); break;
+    case 4: mp_tile<FMT_Q8, 4, G, 1, true>(ta, R, ml); break;
+    default: mp_tile<FMT_Q8, 8, G, 1, true>(ta, R, ml); break;
   }
 }
 
@@ -963,8 +1073,9 @@ __device__ __forceinline__ void grouped_big_unit(const uint8_t* __restrict__ ima
                                                  const Prep& prep, const int* __restrict__ sorted,
                                                  const int* __restrict__ items, const int32_t* __restrict__ x_index,
                                                  float* y, int item, int tile, uint8_t* lds, int* s_map) {
-  float* red = reinterpret_cast<float*>(lds);  // combine area, then the waves' staged scales
-  uint16_t* scl = reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4);
+  // combine area, then the waves' staged scales
+  const MpLds ml{reinterpret_cast<float*>(lds), 0, reinterpret_cast<uint16_t*>(lds + WAVES * WAVE * MP_NV_MAX * 4),
+                 0};
   const int rpt = (WAVES / (pl.S * mp_w2(pl.H))) * TILE;
   const int e = items[3 * item], start = items[3 * item + 1], cnt = items[3 * item + 2];
   __syncthreads();  // the previous unit is done with s_map and LDS
@@ -992,8 +1103,8 @@ __device__ __forceinline__ void grouped_big_unit(const uint8_t* __restrict__ ima
   ta.lds_x = 0;
   ta.pl = pl;
   ta.ucx = 0;
-  if (cnt > 8) grouped_mp_tile<2>(ta, cnt, red, scl);
-  else grouped_mp_tile<1>(ta, cnt, red, scl);
+  if (cnt > 8) grouped_mp_tile<2>(ta, cnt, ml);
+  else grouped_mp_tile<1>(ta, cnt, ml);
 }
 
 // Items of every size in one launch, persistent over the (item, tile) units:
@@ -1064,6 +1175,9 @@ int launch_pair_blockdots(int fmt, const void* image, int64_t n, int64_t k, cons
   if (fmt == QG_FMT_Q8_0)
     hipLaunchKernelGGL(pair_blockdots_kernel<FMT_Q8>, dim3(g), dim3(256), 0, s, (const uint8_t*)image, n, kbp, kb, pv,
                        L.groups, rows, isum);
+  else if (fmt == QG_FMT_Q4_K)
+    hipLaunchKernelGGL(pair_blockdots_kernel<FMT_Q4K>, dim3(g), dim3(256), 0, s, (const uint8_t*)image, n, kbp, kb,
+                       pv, L.groups, rows, isum);
   else
     hipLaunchKernelGGL(pair_blockdots_kernel<FMT_Q4>, dim3(g), dim3(256), 0, s, (const uint8_t*)image, n, kbp, kb, pv,
                        L.groups, rows, isum);
@@ -1099,8 +1213,7 @@ static unsigned persistent_grid(K kernel, size_t lds, int64_t tiles) {
 }
 
 bool fuses_quantization(int fmt, int rows, int64_t k) {
-  const int f = fmt == QG_FMT_Q8_0 ? FMT_Q8 : FMT_Q4;
-  return rows >= 1 && rows <= FUSE_MAX_ROWS && (size_t)rows * kbp_of(k) * x_block_bytes(f) <= (size_t)LDS_X_RL;
+  return rows >= 1 && rows <= FUSE_MAX_ROWS && (size_t)rows * kbp_of(k) * x_block_bytes(fmt) <= (size_t)LDS_X_RL;
 }
 
 template <int FMT, int R, bool FUSED>
@@ -1114,7 +1227,9 @@ static void launch_rl(const SetArgs& a, int lds_x, hipStream_t s) {
   // two tiles per CU; at two rows slower at every size).
   const bool small = whole && (a.total_tiles <= device_cus() || (R == 1 && a.total_tiles >= 4 * device_cus()));
   if (small) {
-    auto kern = rl_set_kernel<FMT, R, FUSED, 8>;
+    // Q4_K holds each block's 16-byte superblock header too: six blocks in flight keep it within the
+    // registers of two workgroups per CU, where eight would leave one
+    auto kern = rl_set_kernel<FMT, R, FUSED, FMT == FMT_Q4K ? 6 : 8>;
     hipLaunchKernelGGL(kern, dim3(persistent_grid(kern, lds, a.total_tiles)), dim3(WG), lds, s, a, lds_x);
   } else {
     auto kern = rl_set_kernel<FMT, R, FUSED, 2>;
@@ -1133,29 +1248,38 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
   else launch_rl<FMT, 2, false>(a, lds_x, s);
 }
 
-// Tiles of the pair kernel at width `wide`; returns the LDS bytes it needs
-// (combine area, then each wave's staged scales: NT tiles of kbp/S blocks x
-// 16 fp16).
-static size_t mp_fill(SetArgs& a, int G, int width) {
+// Tiles of the pair kernel at width `wide`; returns the LDS bytes it needs:
+// the combine area (MP_NV_MAX floats per lane), then each wave's staged
+// scales (NT tiles of kbp/S blocks x 16 fp16); Q4_K (fp32 D and M per row and
+// block) one region per wave for either, whichever is larger.
+static size_t mp_fill(SetArgs& a, int G, int width, int fmt) {
   int64_t tiles = 0;
   size_t sc = 0;
   for (int i = 0; i < a.count; i++) {
     ProjDev& d = a.p[i];
     if (width != MP_MIXED) d.wide = width == MP_WIDE;
-    const int nt = mp_nt(d.pl.H, G, d.wide != 0);
+    const int nt = mp_nt(d.pl.H, G, d.wide != 0, fmt);
     d.rows_per_tile = (WAVES / (d.pl.S * mp_w2(d.pl.H))) * TILE * nt;
     d.tiles = (int)((d.n + d.rows_per_tile - 1) / d.rows_per_tile);
     tiles += d.tiles;
-    const size_t v = (size_t)nt * (d.kbp / d.pl.S) * TILE * 2;
+    // fp16 per (row, block); Q4_K fp32 D and M
+    const size_t v = (size_t)nt * (d.kbp / d.pl.S) * TILE * (fmt == FMT_Q4K ? 8 : 2);
     sc = v > sc ? v : sc;
   }
   a.total_tiles = (int)tiles;
-  return (size_t)WAVES * WAVE * MP_NV_MAX * 4 + WAVES * sc;
+  const size_t red = (size_t)MP_NV_MAX * WAVE * 4;
+  if (fmt != FMT_Q4K) {
+    a.wave_lds = 0;
+    return WAVES * red + WAVES * sc;
+  }
+  const size_t region = ((sc > red ? sc : red) + 15) / 16 * 16;
+  a.wave_lds = (int)region;
+  return (size_t)WAVES * region;
 }
 
 // Weight bytes one wave of projection d streams per tile group on wide tiles.
 static int64_t mp_wide_wave_bytes(const ProjDev& d, int fmt, int G) {
-  return (int64_t)mp_nt(d.pl.H, G, true) * (d.kbp / (d.pl.S * mp_w2(d.pl.H))) * (fmt == FMT_Q8 ? 512 : 256);
+  return (int64_t)mp_nt(d.pl.H, G, true, fmt) * (d.kbp / (d.pl.S * mp_w2(d.pl.H))) * (fmt == FMT_Q8 ? 512 : 256);
 }
 
 // The pair kernel runs in rounds of the workgroups resident at once; a round
@@ -1171,7 +1295,7 @@ static void launch_mp(SetArgs a, int rows, hipStream_t s) {
   auto kn = mp_set_kernel<FMT, G, MP_NARROW, false>;
   auto kw = mp_set_kernel<FMT, G, MP_WIDE, false>;
   SetArgs aw = a;
-  const size_t ln = mp_fill(a, G, MP_NARROW), lw = mp_fill(aw, G, MP_WIDE);
+  const size_t ln = mp_fill(a, G, MP_NARROW, FMT), lw = mp_fill(aw, G, MP_WIDE, FMT);
   const unsigned gn = persistent_grid(kn, ln, a.total_tiles), gw = persistent_grid(kw, lw, aw.total_tiles);
   const int64_t rn = (a.total_tiles + gn - 1) / gn, rw = (aw.total_tiles + gw - 1) / gw;
   if (G == 2 && rw < rn) {
@@ -1194,7 +1318,7 @@ static void launch_mp(SetArgs a, int rows, hipStream_t s) {
       }
     for (int i = 0; i < am.count && rn > 1; i++) {
       am.p[order[i]].wide = 1;
-      const size_t lm = mp_fill(am, G, MP_MIXED);
+      const size_t lm = mp_fill(am, G, MP_MIXED, FMT);
       const unsigned gm = persistent_grid(km, lm, am.total_tiles);
       if (am.total_tiles <= (int64_t)gm) {
         hipLaunchKernelGGL(km, dim3(gm), dim3(WG), lm, s, am, rows);
@@ -1273,13 +1397,16 @@ int launch_qgemv_set(int fmt, const ProjArg* projs, int count, int rows, hipStre
   if (mf) {
     if (rows <= 8) {
       if (fmt == FMT_Q8) launch_mp<FMT_Q8, 1>(a, rows, s);
+      else if (fmt == FMT_Q4K) launch_mp<FMT_Q4K, 1>(a, rows, s);
       else launch_mp<FMT_Q4, 1>(a, rows, s);
     } else {
       if (fmt == FMT_Q8) launch_mp<FMT_Q8, 2>(a, rows, s);
+      else if (fmt == FMT_Q4K) launch_mp<FMT_Q4K, 2>(a, rows, s);
       else launch_mp<FMT_Q4, 2>(a, rows, s);
     }
   } else {
     if (fmt == FMT_Q8) launch_rl_rows<FMT_Q8>(a, rows, fused, lds_x, s);
+    else if (fmt == FMT_Q4K) launch_rl_rows<FMT_Q4K>(a, rows, fused, lds_x, s);
     else launch_rl_rows<FMT_Q4>(a, rows, fused, lds_x, s);
   }
   return hip_status(hipGetLastError(), mf ? "mp_set_kernel" : "rl_set_kernel");

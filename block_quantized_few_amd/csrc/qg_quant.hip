@@ -180,6 +180,76 @@ __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __re
   scale[scale_index(o, b, kbp)] = d16;
 }
 
+// Q4_K superblock quantizer, one thread per (row, superblock) of the padded
+// image: per sub-block j (lo = min(0, min w), hi = max w) s_j = (hi - lo) / 15
+// and mn_j = -lo; d = fp16(max s / 63), dmin = fp16(max mn / 63); sc_j =
+// min(63, round(s_j / d)), m_j = min(63, round(mn_j / dmin)) (0 for a zero
+// scale); codes clamp(round((w + dmin*m_j) / (d*sc_j)), 0, 15) (0 when
+// d*sc_j == 0).  IEEE divisions, round half away from zero.  Pad rows and
+// superblocks are written as zeros.
+__global__ __launch_bounds__(256) void quantize_q4k_weights_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                                   int kbp, uint8_t* __restrict__ code,
+                                                                   uint8_t* __restrict__ hdr) {
+  const int sbp = kbp / 8, ns = (int)(k / QK_K);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= np_of(n) * sbp) return;
+  const int64_t o = t / sbp;
+  const int s = (int)(t % sbp);
+  uint4 h = make_uint4(0u, 0u, 0u, 0u);
+  unsigned cells[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; j++) cells[j][0] = cells[j][1] = cells[j][2] = cells[j][3] = 0u;
+  if (o < n && s < ns) {
+    const float* v = w + o * k + (int64_t)s * QK_K;
+    float sj[8], mnj[8], smax = 0.0f, mmax = 0.0f;
+    for (int j = 0; j < 8; j++) {
+      float lo = 0.0f, hi = v[32 * j];
+      for (int i = 0; i < 32; i++) {
+        const float x = v[32 * j + i];
+        lo = x < lo ? x : lo;
+        hi = x > hi ? x : hi;
+      }
+      sj[j] = (hi - lo) / 15.0f;
+      mnj[j] = -lo;
+      smax = sj[j] > smax ? sj[j] : smax;
+      mmax = mnj[j] > mmax ? mnj[j] : mmax;
+    }
+    const _Float16 dh = (_Float16)(smax / 63.0f), mh = (_Float16)(mmax / 63.0f);
+    const float d = (float)dh, dmin = (float)mh;
+    unsigned sc[8], m[8];
+    for (int j = 0; j < 8; j++) {
+      sc[j] = d != 0.0f ? (unsigned)fminf(fmaxf(roundf(sj[j] / d), 0.0f), 63.0f) : 0u;
+      m[j] = dmin != 0.0f ? (unsigned)fminf(fmaxf(roundf(mnj[j] / dmin), 0.0f), 63.0f) : 0u;
+    }
+    uint16_t d16, m16;
+    __builtin_memcpy(&d16, &dh, 2);
+    __builtin_memcpy(&m16, &mh, 2);
+    unsigned b[12];
+    for (int j = 0; j < 4; j++) {
+      b[j] = (sc[j] & 63u) | ((sc[j + 4] >> 4) << 6);
+      b[j + 4] = (m[j] & 63u) | ((m[j + 4] >> 4) << 6);
+      b[j + 8] = (sc[j + 4] & 15u) | ((m[j + 4] & 15u) << 4);
+    }
+    h.x = (unsigned)d16 | ((unsigned)m16 << 16);
+    h.y = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    h.z = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    h.w = b[8] | (b[9] << 8) | (b[10] << 16) | (b[11] << 24);
+    for (int j = 0; j < 8; j++) {
+      const float D = d * (float)sc[j], M = dmin * (float)m[j];
+      for (int i = 0; i < 32; i++) {
+        const unsigned q = D != 0.0f ? (unsigned)fminf(fmaxf(roundf((v[32 * j + i] + M) / D), 0.0f), 15.0f) : 0u;
+        const int l = i & 15;  // byte l of the cell: code l low, code l + 16 high
+        cells[j][l >> 2] |= (q << ((i >> 4) * 4)) << (8 * (l & 3));
+      }
+    }
+  }
+  *reinterpret_cast<uint4*>(hdr + q4k_header_offset(o, s, kbp)) = h;
+#pragma unroll
+  for (int j = 0; j < 8; j++)
+    *reinterpret_cast<uint4*>(code + cell_row_offset(FMT_Q4K, o, 8 * s + j, kbp)) =
+        make_uint4(cells[j][0], cells[j][1], cells[j][2], cells[j][3]);
+}
+
 // isum[r][o][b]: the exact block dot of the image's codes with qx (plain).
 template <int FMT>
 __global__ __launch_bounds__(256) void blockdots_kernel(const uint8_t* __restrict__ code, int64_t n, int kbp, int kb,
@@ -194,6 +264,8 @@ __global__ __launch_bounds__(256) void blockdots_kernel(const uint8_t* __restric
   int s;
   if (FMT == FMT_Q8) {
     s = dot_q8(ld16(p), ld16(p + 256), xl, xh);
+  } else if (FMT == FMT_Q4K) {
+    s = dot_q4(ld16(p), xl, xh, 0);  // raw codes: the sub-min's share is not part of the integer dot
   } else {
     int qsum = 0;
     for (int i = 0; i < 32; i++) qsum += xq[i];
@@ -366,6 +438,11 @@ int launch_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void*
   uint8_t* img = (uint8_t*)image;
   uint16_t* scale = (uint16_t*)(img + image_scale_offset(fmt, n, k));
   const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
+  if (fmt == FMT_Q4K) {
+    hipLaunchKernelGGL(quantize_q4k_weights_kernel, dim3(grid1(np_of(n) * (kbp / 8), 256)), dim3(256), 0, s, w, n, k,
+                       kbp, img, (uint8_t*)scale);
+    return hip_status(hipGetLastError(), "quantize_q4k_weights_kernel");
+  }
   const unsigned g = grid1(np_of(n) * kbp, 256);
   if (fmt == FMT_Q8)
     hipLaunchKernelGGL(quantize_weights_kernel<FMT_Q8>, dim3(g), dim3(256), 0, s, w, n, k, kb, kbp, img, scale);
@@ -381,6 +458,8 @@ int launch_blockdots(int fmt, const void* image, int64_t n, int64_t k, const int
   const uint8_t* img = (const uint8_t*)image;
   if (fmt == FMT_Q8)
     hipLaunchKernelGGL(blockdots_kernel<FMT_Q8>, dim3(g), dim3(256), 0, s, img, n, kbp, kb, qx, rows, k, isum);
+  else if (fmt == FMT_Q4K)
+    hipLaunchKernelGGL(blockdots_kernel<FMT_Q4K>, dim3(g), dim3(256), 0, s, img, n, kbp, kb, qx, rows, k, isum);
   else
     hipLaunchKernelGGL(blockdots_kernel<FMT_Q4>, dim3(g), dim3(256), 0, s, img, n, kbp, kb, qx, rows, k, isum);
   return hip_status(hipGetLastError(), "blockdots_kernel");

@@ -13,7 +13,7 @@ import os
 import numpy as np
 import torch
 
-Q8_0, Q4_0, F16, FP8 = 1, 2, 3, 4
+Q8_0, Q4_0, F16, FP8, Q4_K = 1, 2, 3, 4, 5
 MAX_ROWS = 16
 MAX_PREP_ROWS = 8192
 MAX_ASSIGN = 2048
@@ -71,6 +71,8 @@ _SIGS = {
     "qgemv_q8_0_noalloc": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p,
                                      C.c_void_p]),
     "qgemv_q4_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
+                             C.c_size_t, C.c_void_p]),
+    "qgemv_q4_k": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                              C.c_size_t, C.c_void_p]),
     "qg_f16_image": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
     "gemv_f16": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]),
@@ -193,6 +195,8 @@ def unpack_image(fmt, image, n, k):
         out = np.empty(n * k + ((n + 127) // 128) * (k // 128) * 4, np.uint8)
     elif fmt == F16:
         out = np.empty((n, k), np.uint16)
+    elif fmt == Q4_K:
+        out = np.empty((n, k // 256, 144), np.uint8)
     else:
         out = np.empty((n, k // 32, 34 if fmt == Q8_0 else 18), np.uint8)
     _check(lib().qg_unpack_image(fmt, image.ctypes.data_as(C.c_void_p), n, k, out.ctypes.data_as(C.c_void_p)))
@@ -330,6 +334,10 @@ def qgemv_q8_0_noalloc(image, n, k, x, y=None):
 
 def qgemv_q4_0(image, n, k, x, y=None, ws=None):
     return _qgemv(lib().qgemv_q4_0, image, n, k, x, y, ws)
+
+
+def qgemv_q4_k(image, n, k, x, y=None, ws=None):
+    return _qgemv(lib().qgemv_q4_k, image, n, k, x, y, ws)
 
 
 def f16_image(w16, out=None):

@@ -31,6 +31,20 @@
  *         `rows`: a row computed inside a batch of 16 has the same bits as the
  *         row computed alone.
  *
+ *   Q4_K: K-quant superblocks of 256 weights (the llama-leg page's Q4_K_M
+ *         race bed and its commit 8624bce, a superblock format's one-row form
+ *         with K in whole superblocks; the pages do not print the format, so
+ *         the published ggml Q4_K layout is taken): canonical block
+ *         {uint16 d; uint16 dmin; uint8 scales[12]; uint8 qs[128]} = 144
+ *         bytes, eight 32-weight sub-blocks j with 6-bit sub-scale sc[j] and
+ *         sub-min m[j] (for j < 4: sc = scales[j] & 63, m = scales[j+4] & 63;
+ *         for j >= 4: sc = (scales[j+4] & 15) | (scales[j-4] >> 6) << 4,
+ *         m = (scales[j+4] >> 4) | (scales[j] >> 6) << 4), weight 64p + l in
+ *         the low nibble of qs[32p + l] and weight 64p + 32 + l in its high
+ *         nibble (p < 4, l < 32); w = d * sc[j] * q - dmin * m[j].  y adds per
+ *         sub-block d_x * (d*sc * isum - dmin*m * s_x), isum the exact int32
+ *         dot of the raw codes q (0..15).  k must be a multiple of 256.
+ *
  * Device image.  Weights live on the device in the library's own layout,
  * made either by qg_pack_image (from canonical blocks, on the host) or by
  * qg_quantize_weights (from fp32 weights, on the device): rows in tiles of 16,
@@ -107,7 +121,7 @@ enum {
   QG_EDEVICE = -7     /* the current device is not a gfx950 GPU */
 };
 
-enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3, QG_FMT_FP8 = 4 };
+enum { QG_FMT_Q8_0 = 1, QG_FMT_Q4_0 = 2, QG_FMT_F16 = 3, QG_FMT_FP8 = 4, QG_FMT_Q4_K = 5 };
 
 #define QG_MAX_ROWS 16        /* activation rows per GEMV call */
 #define QG_MAX_PREP_ROWS 8192 /* rows one qg_prepare_rows call quantizes */
@@ -172,7 +186,12 @@ int qg_device_supported(int device);
 /* ---------------------------------------------------------------- device --- */
 
 /* Quantizes fp32 weights w [n][k] (device) into a device image of `fmt`
- * (Q8_0 or Q4_0) by the block rules above.  Requires max|w|/qmax to fit fp16.
+ * (Q8_0, Q4_0, Q4_K or FP8) by the block rules above (Q4_K, per 32-weight
+ * sub-block j with lo = min(0, min w) and hi = max w: s_j = (hi - lo)/15,
+ * mn_j = -lo; d = fp16(max s / 63), dmin = fp16(max mn / 63); sc = min(63,
+ * round(s_j / d)), m = min(63, round(mn_j / dmin)); q = clamp(round((w +
+ * dmin*m) / (d*sc)), 0, 15) -- the format does not fix a quantizer; this is
+ * the plainest one).  Requires max|w|/qmax to fit fp16.
  * Offline preparation, not part of the per-token path. */
 int qg_quantize_weights(int fmt, const float* w, int64_t n, int64_t k, void* image, qg_stream stream);
 
@@ -201,7 +220,7 @@ int qg_add_rmsnorm_prepare(const float* x, const float* residual, const float* g
                            float* h_out, float* y_out, void* ws, size_t ws_bytes, qg_stream stream);
 
 /* q8 lane GEMV on rows already prepared in `ws` (by qg_prepare_rows with the
- * same rows and k): y [rows][n] fp32, row stride n.  fmt = Q8_0 or Q4_0.
+ * same rows and k): y [rows][n] fp32, row stride n.  fmt = Q8_0, Q4_0 or Q4_K.
  * ws_bytes is the workspace's size: smaller than qg_workspace_bytes(rows, k)
  * is refused (QG_EWORKSPACE) rather than read past (the audio-towers page,
  * router-GEMV commit: a launch never reads past what it was given). */
@@ -226,6 +245,16 @@ int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const voi
  * n < 1 or k not whole blocks, QG_EINVAL / QG_EALIGN for null or misaligned
  * pointers, QG_EWORKSPACE for a short workspace, QG_EDEVICE off gfx950. */
 int qgemv_q8_0(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
+               size_t ws_bytes, qg_stream stream);
+
+/* Q4_K superblocks x q8 activations; arguments, rows, tiling and errors as
+ * qgemv_q8_0, with k a multiple of 256 (QG_ESHAPE otherwise): the one-row and
+ * N-row form of a K-quant superblock format whose K comes in whole
+ * superblocks (the llama-leg page, commit 8624bce; its race bed's Q4_K_M
+ * weights, body and Validation).  Per 32-weight sub-block the exact int32 dot
+ * of the raw codes with the q8 codes, then d_x * (d*sc * isum - dmin*m * s_x)
+ * in fp32, in a fixed order that does not depend on `rows`. */
+int qgemv_q4_k(const void* w_image, int64_t n, int64_t k, const float* x, int rows, float* y, void* ws,
                size_t ws_bytes, qg_stream stream);
 
 /* qgemv_q8_0 for callers that cannot allocate device memory or pass a
@@ -420,7 +449,8 @@ int qg_moe_step_fp8(const void* router_image, int n_experts, int64_t hidden, int
 int qg_quantize_rows_q8(const float* x, int rows, int64_t k, int8_t* qx, float* dx, int32_t* sx, qg_stream stream);
 
 /* A3 alone: isum [rows][n][k/32] int32 = exact block dots of the image's codes
- * with qx [rows][k] (plain layout), rows <= 16. */
+ * with qx [rows][k] (plain layout), rows <= 16 (Q4_K: the raw 4-bit codes of
+ * each 32-weight sub-block). */
 int qgemv_blockdots(int fmt, const void* w_image, int64_t n, int64_t k, const int8_t* qx, int rows, int32_t* isum,
                     qg_stream stream);
 

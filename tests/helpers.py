@@ -34,7 +34,7 @@ def oracle_image(fmt, w_np):
 def rel_err(y_gpu, y_orc, blocks, fmt, x_np, sel=None):
     """max |dy| / sum_k |w_hat[o][k]| |x[r][k]| over all (r, o); sel picks output rows of blocks."""
     n = blocks.shape[0]
-    k = blocks.shape[1] * 32
+    k = blocks.shape[1] * O.BLOCK_WEIGHTS[fmt]
     b = blocks if sel is None else blocks[sel]
     what = O.dequantize(fmt, b, b.shape[0], k)
     denom = np.abs(x_np.astype(np.float64)) @ np.abs(what).T

@@ -326,3 +326,54 @@ def test_device_probe_answers_false_not_an_error():
     import torch
     if torch.cuda.device_count() == 0:
         assert q.device_supported(0) is False
+
+
+# ---------------------------------------------------------------- Q4_K ---
+@pytest.mark.parametrize("n,k", [(5, 256), (17, 768), (40, 3072), (3, 8192)])
+def test_q4_k_pack_unpack_roundtrip(n, k):
+    w = synth.gaussian((n, k), 0.02, synth.tensor_seed(9, 3)).numpy()
+    blocks = O.quantize_weights(O.Q4_K, w)
+    img = q.pack_image(q.Q4_K, blocks, n, k)
+    assert img.size == q.image_bytes(q.Q4_K, n, k)
+    assert np.array_equal(q.unpack_image(q.Q4_K, img, n, k), blocks)
+
+
+def test_q4_k_image_layout_of_one_superblock():
+    # row o, superblock s: header at the scale plane + ((t*(kbp/8) + s)*16 + i)*16; sub-block j of it in the
+    # code cell of block 8s + j at (t*kbp + 8s + j)*256 + 16*i, byte l = code l | code l+16 << 4
+    n, k = 40, 1024  # kb = kbp = 32, sbp = 4, three tiles
+    blocks = np.zeros((n, k // 256, 144), np.uint8)
+    o, s = 21, 2
+    blocks[o, s, :16] = np.arange(100, 116, dtype=np.uint8)  # header bytes
+    codes = [(3 * i + 1) % 16 for i in range(256)]
+    for p in range(4):
+        for l in range(32):
+            blocks[o, s, 16 + 32 * p + l] = codes[64 * p + l] | (codes[64 * p + 32 + l] << 4)
+    img = q.pack_image(q.Q4_K, blocks, n, k)
+    t, i = o // 16, o % 16
+    plane = (3 * 32 * 256 + 255) // 256 * 256  # three tiles of 32 cells
+    h = plane + ((t * 4 + s) * 16 + i) * 16
+    assert list(img[h:h + 16]) == list(range(100, 116))
+    for j in range(8):
+        cell = (t * 32 + 8 * s + j) * 256 + 16 * i
+        want = [codes[32 * j + l] | (codes[32 * j + l + 16] << 4) for l in range(16)]
+        assert list(img[cell:cell + 16]) == want, j
+    assert int(img.sum()) == sum(range(100, 116)) + sum(
+        codes[32 * j + l] | (codes[32 * j + l + 16] << 4) for j in range(8) for l in range(16))
+
+
+def test_q4_k_sizes_and_refusals():
+    assert q.image_bytes(q.Q4_K, 3072, 3072) == 3072 * 3072 // 256 * 144
+    assert q.image_bytes(q.Q4_K, 128256, 4096) == 128256 * 4096 // 256 * 144
+    assert q.image_bytes(q.Q4_K, 16, 224) == 0 and q.image_bytes(q.Q4_K, 16, 288) == 0
+    MB = 1 << 20
+    st, msg = _status("qgemv_q4_k", V(A), 64, 288, V(A), 1, V(A), V(A), MB, None)
+    assert st == -2 and "k=288" in msg and "256" in msg
+    st, msg = _status("qgemv_q4_k", V(A), 64, 512, V(A), 17, V(A), V(A), MB, None)
+    assert st == -3
+    st, msg = _status("qgemv_prepared", q.Q4_K, V(A), 64, 288, V(A), MB, 4, V(A), None)
+    assert st == -2
+    st, msg = _status("qg_quantize_weights", q.Q4_K, V(A), 64, 288, V(A), None)
+    assert st == -2
+    st, msg = _status("qgemv_q4_k", V(A), 64, 512, V(A), 1, V(A), V(A), MB, None)
+    assert st == -7  # a valid call: no GPU here
