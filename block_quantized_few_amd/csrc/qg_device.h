@@ -82,6 +82,14 @@ __device__ __forceinline__ void q4k_dm(uint4 h, int j, float& D, float& M) {
   M = h2f((uint16_t)(h.x >> 16)) * (float)m;
 }
 
+// Q4_K: sub-block j's 6-bit sub-scale and sub-min from a header (as q4k_dm).
+__device__ __forceinline__ void q4k_scm(uint4 h, int j, unsigned& sc, unsigned& m) {
+  const int sh = (j & 3) * 8;
+  const unsigned a = (h.y >> sh) & 255u, b = (h.z >> sh) & 255u, c = (h.w >> sh) & 255u;
+  sc = j < 4 ? (a & 63u) : ((c & 15u) | ((a >> 6) << 4));
+  m = j < 4 ? (b & 63u) : ((c >> 4) | ((b >> 6) << 4));
+}
+
 // One Q4_K sub-block's share of an output: acc + dx * (D * isum - M * xsum),
 // isum the integer dot of the raw codes with the q8 codes and xsum the sum of
 // those q8 codes; the same operations in every kernel, so a row's bits do not

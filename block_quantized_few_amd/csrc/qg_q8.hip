@@ -381,11 +381,11 @@ __host__ __device__ constexpr int mp_w2(int H) { return H >= 4 ? 2 : 1; }
 __host__ __device__ constexpr int mp_nt_base(int H, int G, bool wide) {
   return wide ? (H == 2 || H == 4 ? (G == 2 ? 2 : 3) : (G == 2 ? 1 : 2)) : (H == 8 || G == 2 ? 1 : 2);
 }
-// Q4_K keeps each tile's fp32 D and M in registers as well: its wide tiles of
-// two row groups take one tile fewer (two would spill).
+// Q4_K decodes each tile's sub-block scales and offsets in registers as well:
+// its wide tiles take one tile fewer (as many would spill).
 __host__ __device__ constexpr int mp_nt(int H, int G, bool wide, int fmt = FMT_Q8) {
-  return fmt == FMT_Q4K && wide && G == 2 && mp_nt_base(H, G, wide) > 1 ? mp_nt_base(H, G, wide) - 1
-                                                                        : mp_nt_base(H, G, wide);
+  return fmt == FMT_Q4K && wide && mp_nt_base(H, G, wide) > 1 ? mp_nt_base(H, G, wide) - 1
+                                                              : mp_nt_base(H, G, wide);
 }
 // block-pair steps in flight per wave (even: step j's lane-part pair is j & 1)
 __host__ __device__ constexpr int mp_la(int NT, int G) { return NT * G == 1 ? 4 : 2; }
@@ -416,7 +416,7 @@ struct MpAddr {
   int groups;               // row groups in the workspace
   const uint16_t* sl[NT];   // the wave's staged scales of each tile (LDS), from block sb0 on
   int sb0;
-  int mplane;               // Q4_K: floats from the staged D plane to the M plane
+  int mplane;               // Q4_K: fp16 units from the staged (sc, m) plane to the (d, dmin) plane
   uint32_t soff;            // lane offset in a staged block pair (fp16 units)
   // Gathered row order (rows picked by the tile's s_src map): this lane's
   // element (row * kbp + its block's offset in the pair) per row group, and
@@ -484,14 +484,24 @@ template <int FMT, int NT, int G, int PP, bool SEQ>
 __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, const MpStep<NT, G>& st,
                                            const MpAddr<NT>& ad, int sh) {
   if constexpr (FMT == FMT_Q4K) {
-    // D and M of rows 4q .. 4q+3 of the lane's block, staged as fp32 in the
-    // wave's LDS (D plane, then M plane, each [block][16 rows])
+    // rows 4q .. 4q+3 of the lane's block bb from the wave's staged copy: their
+    // 6-bit (sc, m) pairs ([block][16 rows] of sc | m << 8), and the fp32 d and
+    // dmin of bb's superblock ([superblock][16 rows] of (d, dmin))
+    const int bb = st.b + ((threadIdx.x & 15) >> 3);
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      const float* dp = reinterpret_cast<const float*>(ad.sl[t]) + (st.b - ad.sb0) * TILE + ad.soff;
-      const float4 Dv = *reinterpret_cast<const float4*>(dp);
-      const float4 Mv = *reinterpret_cast<const float4*>(dp + ad.mplane);
-      const float D[4] = {Dv.x, Dv.y, Dv.z, Dv.w}, M[4] = {Mv.x, Mv.y, Mv.z, Mv.w};
+      const uint2 sm = *reinterpret_cast<const uint2*>(ad.sl[t] + (st.b - ad.sb0) * TILE + ad.soff);
+      const float* ddp = reinterpret_cast<const float*>(ad.sl[t] + ad.mplane) +
+                         (((bb >> 3) - (ad.sb0 >> 3)) * TILE + (int)(ad.soff & 15u)) * 2;
+      const float4 d01 = *reinterpret_cast<const float4*>(ddp), d23 = *reinterpret_cast<const float4*>(ddp + 4);
+      const unsigned s4[4] = {sm.x & 0xffffu, sm.x >> 16, sm.y & 0xffffu, sm.y >> 16};
+      const float dv[4] = {d01.x, d01.z, d23.x, d23.z}, mv[4] = {d01.y, d01.w, d23.y, d23.w};
+      float D[4], M[4];
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        D[v] = dv[v] * (float)(s4[v] & 255u);
+        M[v] = mv[v] * (float)(s4[v] >> 8);
+      }
 #pragma unroll
       for (int g = 0; g < G; g++) {
         const v4i c = pair_dots<FMT>(st.a[t], st.x[g], 0, sh);
@@ -542,8 +552,9 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
 
 // LDS of the pair kernel: the combine area (red; a wave's slice at wave * NV *
 // 64 floats) and the waves' staged scales (scl; a wave's NT tiles from
-// wave * NT * sc_stride).  Q4_K stages fp32 D and M, four times the bytes of
-// fp16 scales, so its set kernels give a wave one region for both (red_ws
+// wave * NT * sc_stride).  Q4_K stages more (a (sc, m) pair per row and
+// block, fp32 d and dmin per row and superblock), so its set kernels give a
+// wave one region for both (red_ws
 // floats = scl_ws / 2 fp16 units apart): a wave writes its combine values only
 // after its own step loop, and stages the next tile's scales only after the
 // combine's last barrier, so a workgroup needs the larger of the two per wave,
@@ -570,8 +581,9 @@ __device__ void mp_tile(const TileArgs& ta, int R, const MpLds& ml, int count = 
   const int g = wave / gw, wg = wave - g * gw, s = wg / W2, hw = wg - s * W2;
   const int i = lane & 15, q = lane >> 4;
   const int64_t ntiles = np_of(ta.n) / TILE;
-  // staged scales of one tile's wave part, in fp16 units: fp16 per (row, block); Q4_K fp32 D and M
-  const int sc_stride = pl.H * pl.BS * TILE * (FMT == FMT_Q4K ? 4 : 1);
+  // staged scales of one tile's wave part, in fp16 units: fp16 per (row, block); Q4_K a (sc, m) byte pair per
+  // (row, block), then fp32 (d, dmin) per (row, superblock touched: at most H*BS/8 + 2)
+  const int sc_stride = pl.H * pl.BS * TILE + (FMT == FMT_Q4K ? (pl.H * pl.BS / 8 + 2) * TILE * 4 : 0);
   MpAddr<NT> ad;
   const uint16_t* scale[NT];
 #pragma unroll
@@ -580,7 +592,7 @@ __device__ void mp_tile(const TileArgs& ta, int R, const MpLds& ml, int count = 
   float* red = ml.red;
   ad.aoff = pair_aoff<FMT>(i, q);
   ad.soff = (uint32_t)((i >> 3) * 16 + 4 * q);
-  ad.mplane = pl.H * pl.BS * TILE;
+  ad.mplane = pl.H * pl.BS * TILE;  // Q4_K: fp16 units from the (sc, m) plane to the (d, dmin) plane
   ad.xc = reinterpret_cast<const uint8_t*>(ta.prep.codes);
   ad.xd = ta.prep.dx;
   ad.xn = ta.prep.nsx;
@@ -640,24 +652,25 @@ __device__ void mp_tile(const TileArgs& ta, int R, const MpLds& ml, int count = 
   // reading the previous tile's).
   auto stage = [&]() {
     if constexpr (FMT == FMT_Q4K) {
-      // the headers of the superblocks the wave part touches, decoded into
-      // fp32 D and M per (block, row)
+      // the headers of the superblocks the wave part touches: each block's
+      // (sc, m) pair per row, and each superblock's fp32 (d, dmin) per row
       const int nblk = pl.H * pl.BS, sb_lo = ad.sb0 >> 3, nsb = ((ad.sb0 + nblk - 1) >> 3) - sb_lo + 1;
 #pragma unroll
       for (int t = 0; t < NT; t++) {
         const uint8_t* hb = reinterpret_cast<const uint8_t*>(scale[t]);
-        float* dst = reinterpret_cast<float*>(const_cast<uint16_t*>(ad.sl[t]));
+        uint16_t* smd = const_cast<uint16_t*>(ad.sl[t]);
+        float2* ddd = reinterpret_cast<float2*>(smd + ad.mplane);
         for (int e = lane; e < nsb * TILE; e += WAVE) {
           const int sbi = sb_lo + (e >> 4), row = e & 15;
           const uint4 h = ld16(hb + ((size_t)sbi * TILE + row) * 16);
+          ddd[e] = make_float2(h2f((uint16_t)(h.x & 0xffffu)), h2f((uint16_t)(h.x >> 16)));
 #pragma unroll
           for (int j = 0; j < 8; j++) {
             const int b = sbi * 8 + j - ad.sb0;
             if (b >= 0 && b < nblk) {
-              float D, M;
-              q4k_dm(h, j, D, M);
-              dst[b * TILE + row] = D;
-              dst[ad.mplane + b * TILE + row] = M;
+              unsigned sc, m;
+              q4k_scm(h, j, sc, m);
+              smd[b * TILE + row] = (uint16_t)(sc | (m << 8));
             }
           }
         }
@@ -1250,8 +1263,9 @@ static void launch_rl_rows(const SetArgs& a, int rows, bool fused, int lds_x, hi
 
 // Tiles of the pair kernel at width `wide`; returns the LDS bytes it needs:
 // the combine area (MP_NV_MAX floats per lane), then each wave's staged
-// scales (NT tiles of kbp/S blocks x 16 fp16); Q4_K (fp32 D and M per row and
-// block) one region per wave for either, whichever is larger.
+// scales (NT tiles of kbp/S blocks x 16 fp16); Q4_K (a 6-bit (sc, m) pair per
+// row and block, fp32 (d, dmin) per row and superblock) one region per wave
+// for either, whichever is larger.
 static size_t mp_fill(SetArgs& a, int G, int width, int fmt) {
   int64_t tiles = 0;
   size_t sc = 0;
@@ -1262,8 +1276,9 @@ static size_t mp_fill(SetArgs& a, int G, int width, int fmt) {
     d.rows_per_tile = (WAVES / (d.pl.S * mp_w2(d.pl.H))) * TILE * nt;
     d.tiles = (int)((d.n + d.rows_per_tile - 1) / d.rows_per_tile);
     tiles += d.tiles;
-    // fp16 per (row, block); Q4_K fp32 D and M
-    const size_t v = (size_t)nt * (d.kbp / d.pl.S) * TILE * (fmt == FMT_Q4K ? 8 : 2);
+    // fp16 per (row, block); Q4_K a (sc, m) pair per (row, block) and fp32 (d, dmin) per (row, superblock)
+    const size_t hbs = (size_t)(d.kbp / d.pl.S);
+    const size_t v = (size_t)nt * (hbs * TILE * 2 + (fmt == FMT_Q4K ? (hbs / 8 + 2) * TILE * 8 : 0));
     sc = v > sc ? v : sc;
   }
   a.total_tiles = (int)tiles;
