@@ -454,14 +454,36 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
   float* gu = (float*)(w + M.gu);
   float* o = (float*)(w + M.o);
   const int n_images = n_experts + shared;
-  if (int st = launch_gemv_f16(router_image, n_experts, hidden, x, rows, lg, s)) return st;
-  if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
-                               x, hidden, w + M.xprep, false, s))
-    return st;
-  // an expert meets a row at most once (distinct top-k picks, a separate shared image): items have <= rows rows
-  if (int st = launch_grouped_planned(gu_images, n_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi,
-                                      m, rows, gu, s))
-    return st;
+  // the router logits, and beside them the input rows' A1
+  if (int st = launch_moe_router(router_image, n_experts, hidden, x, rows, lg, w + M.xprep, s)) return st;
+  // the plan and the gate/up GEMV (an expert meets a row at most once:
+  // distinct top-k picks, a separate shared image).  Up to 8 rows (a row a
+  // wave) every workgroup of the gate/up launch routes the rows itself,
+  // which costs less than a launch of its own; with more rows a plan launch
+  // does it once.
+  if (rows <= MOE_UP_PLAN_ROWS) {
+    MoeUp up;
+    up.logits = lg;
+    up.rows = rows;
+    up.E = n_experts;
+    up.topk = topk;
+    up.shared = shared;
+    up.expert = ex;
+    up.weight = wt;
+    up.x_index = xi;
+    up.header = header;
+    up.sorted = sorted;
+    up.items = items;
+    up.plan_off = 0;
+    if (int st = launch_moe_up(gu_images, 2 * ffn, hidden, w + M.xprep, up, gu, s)) return st;
+  } else {
+    if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted,
+                                 items, nullptr, 0, nullptr, false, s))
+      return st;
+    if (int st = launch_grouped_planned(gu_images, n_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items,
+                                        xi, m, rows, gu, s))
+      return st;
+  }
   // at most two rows: the down launch takes the SwiGLU of the gate/up rows in
   // its staging (one launch fewer); otherwise a launch quantizes it first
   const bool glu = rows <= 2 && grouped_glu_fits(ffn);

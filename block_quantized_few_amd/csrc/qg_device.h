@@ -201,14 +201,14 @@ __device__ inline void store_items_small_first(const int* s_ie, const int* s_is,
   }
 }
 
-// Workgroups 1.. of a plan launch (workgroup 0 plans): the input rows' A1 in
-// row order, four lanes per 32-block (item (blockIdx.x - 1) * blockDim.x +
-// threadIdx.x of rows * kbp * 4; pad blocks quantize zeros).
+// Workgroup `wg` of those that quantize a launch's input rows beside its
+// other work: the rows' A1 in row order, four lanes per 32-block (item
+// wg * blockDim.x + threadIdx.x of rows * kbp * 4; pad blocks quantize zeros).
 __device__ __forceinline__ void plan_prepare_q8(const float* __restrict__ x, int rows, int64_t k,
                                                 int8_t* __restrict__ xq, float* __restrict__ xd,
-                                                int* __restrict__ xn) {
+                                                int* __restrict__ xn, int wg) {
   const int kb = (int)kb_of(k), kbp = (int)kbp_of(k);
-  const int64_t e = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
+  const int64_t e = (int64_t)wg * blockDim.x + threadIdx.x;
   if (e >= (int64_t)rows * kbp * 4) return;  // a multiple of 64: whole waves leave
   const int q = (int)(e & 3);
   const int64_t blk = e >> 2, r = blk / kbp;
@@ -236,9 +236,9 @@ __device__ __forceinline__ void plan_prepare_q8(const float* __restrict__ x, int
 // The same for the FP8 lane: the input rows' 1 x 128 groups, a wave per
 // (row, group).
 __device__ __forceinline__ void plan_prepare_fp8(const float* __restrict__ x, int rows, int64_t k,
-                                                 uint8_t* __restrict__ fcodes, float* __restrict__ fscales) {
+                                                 uint8_t* __restrict__ fcodes, float* __restrict__ fscales, int wg) {
   const int lane = threadIdx.x % WAVE;
-  const int64_t kg = k / 128, e = (int64_t)(blockIdx.x - 1) * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+  const int64_t kg = k / 128, e = (int64_t)wg * (blockDim.x / WAVE) + threadIdx.x / WAVE;
   if (e >= (int64_t)rows * kg) return;  // whole waves
   const int64_t r = e / kg, g = e - r * kg;
   const float2 v = reinterpret_cast<const float2*>(x + r * k + g * 128)[lane];

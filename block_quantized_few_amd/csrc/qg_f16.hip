@@ -97,11 +97,11 @@ __device__ __forceinline__ void fm_compute(v4f (&c)[NT], const FmStep<NT>& st, f
 }
 
 // NT 16-row tiles per workgroup step (a tile group), S waves (k ranges), LA
-// steps in flight; persistent over tile groups.
+// steps in flight; the workgroup takes groups first, first + stride, ...
 template <int NT, int S, int LA>
-__global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __restrict__ img, int64_t N, int64_t K,
-                                                            const float* __restrict__ x, int R,
-                                                            float* __restrict__ y, int64_t groups) {
+__device__ __forceinline__ void gemv_f16_groups(const uint16_t* __restrict__ img, int64_t N, int64_t K,
+                                                const float* __restrict__ x, int R, float* __restrict__ y,
+                                                int64_t groups, int64_t first, int64_t stride) {
   __shared__ float red[S * NT * 4 * WAVE];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
   const int i = lane & 15, q = lane >> 4;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __re
         lc = lc + 1 == s1 ? s0 : lc + 1;
       }
   };
-  if (blockIdx.x < groups) start(blockIdx.x);
+  if (first < groups) start(first);
 
   // the scale of this column over the wave's k range (from the steps in flight
   // when they cover it, else from a pass of its own)
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __re
                  fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
   };
   float amax = 0.0f;
-  if (nst <= LA && blockIdx.x < groups) {
+  if (nst <= LA && first < groups) {
 #pragma unroll
     for (int j = 0; j < LA; j++)
       if (j < nst) amax = fmaxf(amax, amax8(f[j].x[0], f[j].x[1]));  // zeros past k
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __re
   const int se = min(max(15 - ex, -126), 126);
   const float scale = ldexpf(1.0f, se);
 
-  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+  for (int64_t grp = first; grp < groups; grp += stride) {
     v4f c[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) c[t] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __re
       }
     }
     // every step is consumed: the next group's first loads fly during the reduction
-    if (grp + gridDim.x < groups) start(grp + gridDim.x);
+    if (grp + stride < groups) start(grp + stride);
     // k ranges left to right (each scaled back first)
     __syncthreads();
 #pragma unroll
@@ -196,6 +196,14 @@ __global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __re
         }
     }
   }
+}
+
+// Persistent over tile groups.
+template <int NT, int S, int LA>
+__global__ __launch_bounds__(S * WAVE) void gemv_f16_kernel(const uint16_t* __restrict__ img, int64_t N, int64_t K,
+                                                            const float* __restrict__ x, int R,
+                                                            float* __restrict__ y, int64_t groups) {
+  gemv_f16_groups<NT, S, LA>(img, N, K, x, R, y, groups, blockIdx.x, gridDim.x);
 }
 
 template <int NT, int S, int LA>
@@ -218,6 +226,37 @@ int launch_gemv_f16(const void* image, int64_t n, int64_t k, const float* x, int
   else if (t16 >= 256) launch_f16<1, 4, 4>(img, n, k, x, rows, y, s);
   else launch_f16<1, 16, 4>(img, n, k, x, rows, y, s);
   return hip_status(hipGetLastError(), "gemv_f16_kernel");
+}
+
+// The router of a routed MoE step: workgroups 0 .. gemv_wgs - 1 run the f16
+// GEMV of the router image (n < 4096 rows: the 16-wave form launch_gemv_f16
+// takes for that size, so the logits have its bits); the others quantize the
+// input rows (A1, row order) for the expert GEMVs.
+__global__ __launch_bounds__(16 * WAVE) void moe_router_kernel(const uint16_t* __restrict__ img, int64_t N, int64_t K,
+                                                               const float* __restrict__ x, int R,
+                                                               float* __restrict__ y, int64_t groups, int gemv_wgs,
+                                                               int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                               int* __restrict__ xn) {
+  if ((int)blockIdx.x < gemv_wgs) {
+    gemv_f16_groups<1, 16, 4>(img, N, K, x, R, y, groups, blockIdx.x, gemv_wgs);
+    return;
+  }
+  plan_prepare_q8(x, R, K, xq, xd, xn, (int)blockIdx.x - gemv_wgs);
+}
+
+int launch_moe_router(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, void* xprep,
+                      hipStream_t s) {
+  const int64_t groups = f16_tiles(n);
+  if (groups >= 256) return fail(QG_ELAUNCH, "router of %lld experts: at most 4095", (long long)n);
+  const PrepLayout L = prep_layout_rows(rows, k);
+  uint8_t* w = static_cast<uint8_t*>(xprep);
+  const int64_t quads = (int64_t)rows * kbp_of(k) * 4;
+  const unsigned a1 = (unsigned)((quads + 1023) / 1024);
+  hipLaunchKernelGGL(moe_router_kernel, dim3((unsigned)groups + a1), dim3(16 * WAVE), 0, s,
+                     static_cast<const uint16_t*>(image), n, k, x, rows, y, groups, (int)groups,
+                     reinterpret_cast<int8_t*>(w + L.codes), reinterpret_cast<float*>(w + L.dx),
+                     reinterpret_cast<int*>(w + L.nsx));
+  return hip_status(hipGetLastError(), "moe_router_kernel");
 }
 
 }  // namespace qg

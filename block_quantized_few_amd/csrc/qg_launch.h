@@ -79,6 +79,30 @@ int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws,
 int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int64_t k, const void* prep, int x_rows,
                            const int* header, const int* sorted, const int* items, const int32_t* x_index, int m,
                            int max_item_rows, float* y, hipStream_t s, const float* glu = nullptr);
+
+// The plan of a routed MoE step as the gate/up launch computes it: from the
+// router logits [rows][E] (top-k, a shared expert E when `shared`); the
+// launch's workgroup 0 stores it (expert, weight, x_index [rows * slots],
+// header, sorted, items).
+struct MoeUp {
+  const float* logits;
+  int rows, E, topk, shared;
+  int32_t* expert;
+  float* weight;
+  int32_t* x_index;
+  int* header;
+  int* sorted;
+  int* items;
+  int plan_off;  // set by the launcher
+};
+// Rows up to which the gate/up launch of a routed MoE step plans for itself
+// (one row a wave of its workgroups) instead of after a plan launch.
+constexpr int MOE_UP_PLAN_ROWS = 8;
+// The gate/up launch of a routed MoE step: the plan, then the grouped GEMV of
+// the (E + shared) n x k images on the input rows prepared at prep (row
+// order, rows rows), outputs y [rows * slots][n].
+int launch_moe_up(const void* images, int64_t n, int64_t k, const void* prep, const MoeUp& up, float* y,
+                  hipStream_t s);
 // Whether two SwiGLU rows of length k fit a tile's staging area whole.
 bool grouped_glu_fits(int64_t k);
 
@@ -95,6 +119,10 @@ int launch_swiglu_fp8(const float* gu, int m, int64_t ffn, void* hws, hipStream_
 
 // f16 lane.
 int launch_gemv_f16(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s);
+// Routed MoE step, first launch: the f16 router GEMV (n < 4096; the bits of
+// launch_gemv_f16) into y, beside it the A1 of x into xprep (row order).
+int launch_moe_router(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, void* xprep,
+                      hipStream_t s);
 int launch_f16_pack(const uint16_t* w, int64_t n, int64_t k, void* image, hipStream_t s);
 int launch_fp8_quantize_weights(const float* w, int64_t n, int64_t k, void* image, hipStream_t s);
 int launch_fp8_prepare(const float* x, int rows, int64_t k, void* ws, hipStream_t s);

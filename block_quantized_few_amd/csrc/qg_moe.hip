@@ -5,125 +5,9 @@
 #include "qg_device.h"
 #include "qg_internal.h"
 #include "qg_launch.h"
+#include "qg_route.h"
 
 namespace qg {
-
-constexpr int ROUTE_MAX_E = 1024;
-constexpr int ROUTE_PER_LANE = ROUTE_MAX_E / WAVE;
-
-// Wave-wide reductions without LDS: DPP within each row of 16 lanes (pairs,
-// quads, half-row mirror, row mirror: every lane of the row ends with the
-// row's value), then the four rows' values read from lanes 0, 16, 32, 48 and
-// combined as (r0 . r1) . (r2 . r3).  Every lane gets the same bits.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ float lane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
-}
-
-// (value, index) with the larger value, ties to the lower index (selects,
-// no branches).
-__device__ __forceinline__ void pick(float& v, int& i, float ov, int oi) {
-  const bool better = (ov > v) | ((ov == v) & (oi < i));
-  v = better ? ov : v;
-  i = better ? oi : i;
-}
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  pick(v, i, dpp_f<CTRL>(v), dpp_i<CTRL>(i));
-}
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<0xB1>(v, i);
-  argmax_step<0x4E>(v, i);
-  argmax_step<0x141>(v, i);
-  argmax_step<0x140>(v, i);
-  float v0 = lane_f(v, 0), v2 = lane_f(v, 32);
-  int i0 = __builtin_amdgcn_readlane(i, 0), i2 = __builtin_amdgcn_readlane(i, 32);
-  pick(v0, i0, lane_f(v, 16), __builtin_amdgcn_readlane(i, 16));
-  pick(v2, i2, lane_f(v, 48), __builtin_amdgcn_readlane(i, 48));
-  pick(v0, i0, v2, i2);
-  v = v0;
-  i = i0;
-}
-
-// Routing of one row by one wave: softmax over the E logits in fp32 (max
-// subtracted; each lane sums its experts in index order, then the fixed
-// wave_sum tree), and the topk experts by logit, ties to the lower index, in
-// descending order, written to ex[] / wt[] (lane k writes pick k).  NPER:
-// logits per lane (E <= 64 * NPER).
-template <int NPER>
-__device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  float l[NPER];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NPER; i++) {
-    const int e = lane + WAVE * i;
-    l[i] = e < E ? lrow[e] : -INFINITY;
-    mx = fmaxf(mx, l[i]);
-  }
-  mx = wave_max(mx);
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NPER; i++) {
-    const float t = expf(l[i] - mx);
-    sum += lane + WAVE * i < E ? t : 0.0f;
-  }
-  sum = wave_sum(sum);
-  float mv = 0.0f;  // this lane's pick (lane k: the k-th)
-  int mi = 0;
-  unsigned avail = 0;  // bit i: entry i is a real expert not picked yet
-#pragma unroll
-  for (int i = 0; i < NPER; i++) avail |= (lane + WAVE * i < E ? 1u : 0u) << i;
-  for (int k = 0; k < topk; k++) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < NPER; i++) {
-      const int e = lane + WAVE * i;
-      const bool ok = (avail >> i) & 1u;
-      const bool better = ok & ((l[i] > bv) | ((l[i] == bv) & (e < bi)));
-      bv = better ? l[i] : bv;
-      bi = better ? e : bi;
-    }
-    wave_argmax(bv, bi);
-    avail &= ~((bi % WAVE == lane ? 1u : 0u) << (bi / WAVE));
-    mv = lane == k ? bv : mv;  // lane k keeps pick k
-    mi = lane == k ? bi : mi;
-  }
-  if (lane < topk) {
-    ex[lane] = mi;
-    wt[lane] = expf(mv - mx) / sum;
-  }
-}
-
-__device__ __forceinline__ void route_row(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
-  if (E <= 4 * WAVE) route_row_n<4>(lrow, E, topk, ex, wt);
-  else if (E <= 8 * WAVE) route_row_n<8>(lrow, E, topk, ex, wt);
-  else route_row_n<ROUTE_PER_LANE>(lrow, E, topk, ex, wt);
-}
 
 // One wave per row.
 __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__ logits, int E, int topk,
@@ -142,11 +26,10 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
   }
 }
 
-// The plan of a routed MoE step, one workgroup: route every row (a wave per
-// row), then order the assignments by (expert, index) into work items of at
-// most 16 rows of one expert (the grouped GEMV's plan; the down projection
-// reuses it).  Workgroups 1.. quantize the input rows into row order (A1)
-// meanwhile.
+// The plan of a routed MoE step, one workgroup (moe_plan_block): route every
+// row, order the assignments by expert into work items (the grouped GEMV's
+// plan; the down projection reuses it).  Workgroups 1.. quantize the input
+// rows into row order (A1) meanwhile.
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict__ logits, int rows, int E, int topk,
                                                         int shared_expert, int32_t* __restrict__ expert,
                                                         float* __restrict__ weight, int32_t* __restrict__ x_index,
@@ -155,76 +38,16 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
                                                         const float* __restrict__ x, int64_t k, int8_t* __restrict__ xq,
                                                         float* __restrict__ xd, int* __restrict__ xn,
                                                         uint8_t* __restrict__ fcodes, float* __restrict__ fscales) {
-  __shared__ int s_e[QG_MOE_MAX_M];
-  __shared__ int s_pos[QG_MOE_MAX_M];
-  __shared__ float s_w[QG_MOE_MAX_M];
-  __shared__ int s_ie[QG_MOE_MAX_M], s_is[QG_MOE_MAX_M], s_ic[QG_MOE_MAX_M];  // work items
-  __shared__ unsigned s_mask[ROUTE_MAX_E + 1];  // bit r: row r picked expert e
-  __shared__ int s_off[ROUTE_MAX_E + 1];        // (assignments, touched experts) before expert e, packed
-  __shared__ int s_wsum[1024 / WAVE];
-  __shared__ int s_cnt[2];
-  const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
+  __shared__ __align__(16) uint8_t s_plan[plan_lds_bytes(QG_MOE_MAX_M, ROUTE_MAX_E)];
   if (blockIdx.x > 0) {
-    if (fcodes) plan_prepare_fp8(x, rows, k, fcodes, fscales);
-    else plan_prepare_q8(x, rows, k, xq, xd, xn);
+    if (fcodes) plan_prepare_fp8(x, rows, k, fcodes, fscales, blockIdx.x - 1);
+    else plan_prepare_q8(x, rows, k, xq, xd, xn, blockIdx.x - 1);
     return;
   }
-  // workgroup 0: routing and the plan
-  const int slots = topk + (shared_expert >= 0 ? 1 : 0);
-  const int m = rows * slots;
-  for (int r = wave; r < rows; r += nt / WAVE) {
-    route_row(logits + (int64_t)r * E, E, topk, s_e + r * slots, s_w + r * slots);
-    if (lane == 0 && shared_expert >= 0) {
-      s_e[r * slots + topk] = shared_expert;
-      s_w[r * slots + topk] = 1.0f;
-    }
-  }
-  // Counting sort by expert.  An expert meets a row at most once (distinct
-  // top-k picks; the shared expert is index E), so with rows <= 16 every
-  // touched expert is one work item, and an assignment's place among its
-  // expert's is the number of earlier rows in the expert's row mask.
-  const int ne = E + 1;  // experts 0..E-1 and the shared expert E
-  for (int e = tid; e < ne; e += nt) s_mask[e] = 0u;
-  __syncthreads();
-  for (int j = tid; j < m; j += nt) atomicOr(&s_mask[s_e[j]], 1u << (j / slots));
-  __syncthreads();
-  // exclusive scan over experts of (count | touched << 16), two experts per thread
-  const int e0 = 2 * tid, e1 = e0 + 1;
-  const unsigned m0 = e0 < ne ? s_mask[e0] : 0u, m1 = e1 < ne ? s_mask[e1] : 0u;
-  const int v0 = __popc(m0) | (m0 ? 1 << 16 : 0), v1 = __popc(m1) | (m1 ? 1 << 16 : 0);
-  int inc = v0 + v1;  // inclusive scan within the wave
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    inc += lane >= off ? o : 0;
-  }
-  if (lane == WAVE - 1) s_wsum[wave] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; w++) base += s_wsum[w];
-  const int ex0 = base + inc - (v0 + v1);  // before expert e0
-  if (e0 < ne) s_off[e0] = ex0;
-  if (e1 < ne) s_off[e1] = ex0 + v0;
-  __syncthreads();
-  int nitems = 0;
-  for (int w = 0; w < nt / WAVE; w++) nitems += s_wsum[w];
-  nitems >>= 16;
-  for (int j = tid; j < m; j += nt) {
-    const int e = s_e[j], r = j / slots;
-    const unsigned mk = s_mask[e];
-    const int rank = (s_off[e] & 0xffff) + __popc(mk & ((1u << r) - 1u));
-    expert[j] = e;
-    weight[j] = s_w[j];
-    x_index[j] = r;
-    sorted[rank] = j;
-    if (mk & ((1u << r) - 1u)) continue;  // the expert's first row makes its item
-    const int item = s_off[e] >> 16;
-    s_ie[item] = e;
-    s_is[item] = s_off[e] & 0xffff;
-    s_ic[item] = __popc(mk);
-  }
-  if (tid == 0) header[1] = 0;
-  __syncthreads();
-  store_items_small_first(s_ie, s_is, s_ic, nitems, s_pos, s_cnt, items, header);
+  const int slots = topk + (shared_expert >= 0 ? 1 : 0), m = rows * slots;
+  const PlanLds P = plan_carve(s_plan, m, E);
+  moe_plan_block(logits, rows, E, topk, shared_expert >= 0, P);
+  plan_store(P, m, expert, weight, x_index, header, sorted, items);
 }
 
 // SwiGLU of m assignments, h = silu(g) * u in fp32, quantized at once into

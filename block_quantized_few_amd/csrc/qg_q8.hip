@@ -27,6 +27,7 @@
 #include "qg_device.h"
 #include "qg_internal.h"
 #include "qg_launch.h"
+#include "qg_route.h"
 
 namespace qg {
 
@@ -928,8 +929,8 @@ __global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* __res
                                                             int* __restrict__ xn, uint8_t* __restrict__ fcodes,
                                                             float* __restrict__ fscales) {
   if (blockIdx.x > 0) {  // the input rows' quantization
-    if (fcodes) plan_prepare_fp8(x, x_rows, k, fcodes, fscales);
-    else plan_prepare_q8(x, x_rows, k, xq, xd, xn);
+    if (fcodes) plan_prepare_fp8(x, x_rows, k, fcodes, fscales, blockIdx.x - 1);
+    else plan_prepare_q8(x, x_rows, k, xq, xd, xn, blockIdx.x - 1);
     return;
   }
   __shared__ int s_e[QG_MAX_ASSIGN];
@@ -1140,6 +1141,51 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void gr
                        nsmall + u / tiles_b, u % tiles_b, lds, s_map);
     else
       grouped_small_unit<false>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, sorted, items, x_index, y,
+                                lds_x, (u - ub) / tiles_s, (u - ub) % tiles_s, lds, s_map, nullptr);
+  }
+}
+
+// ------------------------------------------------- routed MoE gate/up ---
+
+// The gate/up launch of a routed MoE step: every workgroup computes the
+// step's plan from the router logits (moe_plan_block: the same plan in each),
+// workgroup 0 stores it for the later launches, and the workgroups take the
+// (item, tile) units as the grouped kernels do, the plan read from LDS.  The
+// activation row of assignment j is row j / slots of the prepared input.
+template <int LA>
+__global__ __launch_bounds__(WG) void moe_up_small_kernel(const uint8_t* __restrict__ images, int64_t expert_bytes,
+                                                          size_t scale_off, int64_t n, int64_t k, int kbp,
+                                                          PartPlan pl, Prep prep, float* y, int lds_x, int tiles,
+                                                          MoeUp up) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_map[2 * QG_MAX_ROWS];
+  const int m = up.rows * (up.topk + up.shared);
+  const PlanLds P = plan_carve(lds + up.plan_off, m, up.E);
+  moe_plan_block(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
+  if (blockIdx.x == 0) plan_store(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
+  const int units = P.misc[1] * tiles;  // every item is small (rows <= 2)
+  for (int u = blockIdx.x; u < units; u += gridDim.x)
+    grouped_small_unit<false, LA>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, P.sorted, P.items, P.xi, y,
+                                  lds_x, u / tiles, u % tiles, lds, s_map, nullptr);
+}
+
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void moe_up_all_kernel(
+    const uint8_t* __restrict__ images, int64_t expert_bytes, size_t scale_off, int64_t n, int64_t k, int kbp,
+    PartPlan pl, Prep prep, float* y, int lds_x, int tiles_s, int tiles_b, MoeUp up) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_map[2 * QG_MAX_ROWS];
+  const int m = up.rows * (up.topk + up.shared);
+  const PlanLds P = plan_carve(lds + up.plan_off, m, up.E);
+  moe_plan_block(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
+  if (blockIdx.x == 0) plan_store(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
+  const int nsmall = P.misc[1];
+  const int ub = (P.misc[0] - nsmall) * tiles_b, units = ub + nsmall * tiles_s;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    if (u < ub)
+      grouped_big_unit(images, expert_bytes, scale_off, n, k, kbp, pl, prep, P.sorted, P.items, P.xi, y,
+                       nsmall + u / tiles_b, u % tiles_b, lds, s_map);
+    else
+      grouped_small_unit<false>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, P.sorted, P.items, P.xi, y,
                                 lds_x, (u - ub) / tiles_s, (u - ub) % tiles_s, lds, s_map, nullptr);
   }
 }
@@ -1473,6 +1519,43 @@ int launch_grouped_planned(const void* images, int64_t n_experts, int64_t n, int
                      pv, header, sorted, items, x_index, y, lx_s, tiles, tb);
   if (int st = hip_status(hipGetLastError(), "grouped_all_kernel")) return st;
   return QG_OK;
+}
+
+int launch_moe_up(const void* images, int64_t n, int64_t k, const void* prep, const MoeUp& up_in, float* y,
+                  hipStream_t s) {
+  MoeUp up = up_in;
+  const int slots = up.topk + up.shared, m = up.rows * slots;
+  const int kbp = (int)kbp_of(k);
+  const PartPlan pl = part_plan(kbp);
+  const int tiles = (int)((n + WG / pl.P - 1) / (WG / pl.P));
+  const int64_t eb = (int64_t)image_total_bytes(QG_FMT_Q8_0, n, k);
+  const size_t so = image_scale_offset(QG_FMT_Q8_0, n, k);
+  const Prep pv = prep_view(prep, prep_layout_rows(up.rows, k));
+  const size_t need = (size_t)GROUPED_SMALL_ROWS * kbp * x_block_bytes(FMT_Q8);
+  const int lx_s = (int)((need < (size_t)LDS_X_RL ? need : (size_t)LDS_X_RL) + 15) / 16 * 16;
+  const size_t lds_s = (size_t)lx_s + WAVES * WAVE * GROUPED_SMALL_ROWS * 4;
+  const size_t plan = plan_lds_bytes(m, up.E);
+  if (up.rows <= GROUPED_SMALL_ROWS) {
+    // every item is small: at most m of them, m * tiles units
+    up.plan_off = (int)((lds_s + 15) / 16 * 16);
+    const size_t lds = (size_t)up.plan_off + plan;
+    const bool few = (int64_t)m * tiles <= device_cus();
+    auto kern = few ? moe_up_small_kernel<GROUPED_LA_FEW> : moe_up_small_kernel<GROUPED_LA>;
+    const unsigned g = persistent_grid(kern, lds, (int64_t)m * tiles);
+    hipLaunchKernelGGL(kern, dim3(g), dim3(WG), lds, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv, y, lx_s,
+                       tiles, up);
+    return hip_status(hipGetLastError(), "moe_up_small_kernel");
+  }
+  const int tb = (int)((n + grouped_mp_rows(pl) - 1) / grouped_mp_rows(pl));
+  const size_t lds_b = (size_t)WAVES * WAVE * MP_NV_MAX * 4 + (size_t)WAVES * (kbp / pl.S) * TILE * 2;
+  const size_t lds_a = lds_s > lds_b ? lds_s : lds_b;
+  up.plan_off = (int)((lds_a + 15) / 16 * 16);
+  const size_t lds = (size_t)up.plan_off + plan;
+  const int mb = m / (GROUPED_SMALL_ROWS + 1);  // items of more than two rows: at most this many
+  const unsigned g = persistent_grid(moe_up_all_kernel, lds, (int64_t)m * tiles + (int64_t)mb * tb);
+  hipLaunchKernelGGL(moe_up_all_kernel, dim3(g), dim3(WG), lds, s, (const uint8_t*)images, eb, so, n, k, kbp, pl, pv,
+                     y, lx_s, tiles, tb, up);
+  return hip_status(hipGetLastError(), "moe_up_all_kernel");
 }
 
 int launch_grouped_plan(const int32_t* expert, const int32_t* x_index, int m, int64_t n_experts, int x_rows,
