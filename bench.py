@@ -16,7 +16,8 @@ Beside it, on the same line:
                      the achievable-read figure the GEMVs are also read against;
   * secondary     -- the other workloads at their listed rows, each with its
                      kernel's roofline: the Llama-3.2-1B-shaped Q8_0 layer (1
-                     row), the Llama-3.2-3B-shaped Q4_0 layer (1/2/4/8 rows),
+                     row), the Llama-3.2-3B-shaped layer in Q4_0 and in Q4_K
+                     (1/2/4/8 rows),
                      the LM head in the f16 lane and in Q4_0 (1/8/16), the
                      1024 x 1024 Q8_0 GEMV (1 row), the routed MoE step
                      (1/8/9/16 rows);
