@@ -232,8 +232,9 @@ int qgemv_prepared(int fmt, const void* w_image, int64_t n, int64_t k, const voi
  * lane; block-quantized weights against q8 activations, integer block dots);
  * rows past eight tiled inside this one call and weight pass, each row equal
  * to the row computed alone (the same page's router-GEMV commit; the
- * llama-leg page, commit 16880fe: balanced groups past eight rows, never a
- * weight pass a row); k in whole 32-blocks (llama-leg page, commit 8624bce).
+ * llama-leg page, commit 16880fe: balanced groups past eight rows rather
+ * than one more read of the weights for every extra row); k in whole
+ * 32-blocks (llama-leg page, commit 8624bce).
  *   w_image  device image (qg_quantize_weights / qg_pack_image), 256-aligned
  *   x        [rows][k] fp32, device, 16-aligned, finite
  *   y        [rows][n] fp32, device, written whole, nothing else written
