@@ -1,7 +1,7 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times, on sampled outputs the oracle computes one by one.
 
-LM head 128256 x 4096 (Q8_0 and f16) at rows 1, 2, 8, 16; the Llama-3.2-1B-shaped
+LM head 128256 x 4096 (Q8_0, Q4_0, Q4_K and f16) at rows 1, 2, 8, 16; the Llama-3.2-1B-shaped
 Q8_0 decode layer (seven projections, one set launch) at rows 1 and 16, and at
 rows 1 and 2 straight from fp32 rows (quantized inside the GEMV launch, as the
 benchmark runs it); the Llama-3.2-3B-shaped Q4_0 layer at rows 1, 2, 4, 8."""
@@ -56,6 +56,36 @@ def test_lm_head_q8_0():
     for r in range(2):
         y1 = q.qgemv_q8_0(img, n, k, x2[r:r + 1].contiguous())
         assert np.array_equal(bits(y1), bits(ys[2][1][r:r + 1])), r
+
+
+@pytest.mark.parametrize("fmt,ofmt,wl", [(q.Q4_0, O.Q4_0, 6), (q.Q4_K, O.Q4_K, 7)])
+def test_lm_head_4bit(fmt, ofmt, wl):
+    """The LM head in the 4-bit formats at rows 1, 2, 8 and 16 through the entry point (quantization fused at
+    1-2 rows; the pair kernel's wide tiles at 16): sampled outputs against the oracle, and the rows of the
+    16-row call equal to the same rows in calls of 8 and 1."""
+    n, k = 128256, 4096
+    log(f"LM head fmt={fmt}: weights")
+    w = gauss((n, k), 0.02, wl, 0, device="cuda").cpu().numpy()
+    blocks = O.quantize_weights(ofmt, w)
+    del w
+    img = torch.from_numpy(q.pack_image(fmt, blocks, n, k)).cuda()
+    call = q.qgemv_q4_0 if fmt == q.Q4_0 else q.qgemv_q4_k
+    sel = _sample(n, 384, 3 + wl)
+    ys = {}
+    for rows in (1, 2, 8, 16):
+        log(f"LM head fmt={fmt} rows={rows}")
+        x = gauss((rows, k), 1.0, wl, 32 + rows).numpy()
+        y = call(img, n, k, torch.from_numpy(x).cuda())
+        yo = O.gemv_q_rows(ofmt, blocks, n, k, x, sel, threads=16)
+        e = rel_err(y.cpu().numpy()[:, sel], yo, blocks, ofmt, x, sel=sel)
+        log(f"  max rel err {e:.3e}")
+        assert e <= TOL
+        ys[rows] = (x, y)
+    x16 = torch.from_numpy(ys[16][0]).cuda()
+    y8 = call(img, n, k, x16[:8].contiguous())
+    assert np.array_equal(bits(y8), bits(ys[16][1][:8]))
+    y1 = call(img, n, k, x16[15:16].contiguous())
+    assert np.array_equal(bits(y1), bits(ys[16][1][15:16]))
 
 
 def test_lm_head_f16():
