@@ -433,6 +433,17 @@ struct MpAddr {
 // feeds) and 16 bytes of the activation chunk; c[v] is the dot of weight row
 // 4q + v with column i, starting from ns (Q4_0: -8 * sum of that column's
 // activation codes).
+// f32(half `hi` of the two fp16 in h2) * b, rounded once (the product h2f(h) * b), in one
+// mixed-precision FMA with a negative-zero addend.
+__device__ __forceinline__ float mul_h_f(uint32_t h2, int hi, float b) {
+  float d;
+  if (hi)
+    asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h2), "v"(b));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h2), "v"(b));
+  return d;
+}
+
 template <int FMT>
 __device__ __forceinline__ v4i pair_dots(uint4 araw, uint4 x, int ns, int sh) {
   uint4 av = araw;
@@ -529,14 +540,12 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
   for (int t = 0; t < NT; t++) {
     // fp16 scales of rows 4q .. 4q+3 of the lane's block, from the wave's staged copy
     const uint2 wv = *reinterpret_cast<const uint2*>(ad.sl[t] + (st.b - ad.sb0) * TILE + ad.soff);
-    const float dw[4] = {h2f((uint16_t)(wv.x & 0xffff)), h2f((uint16_t)(wv.x >> 16)), h2f((uint16_t)(wv.y & 0xffff)),
-                         h2f((uint16_t)(wv.y >> 16))};
 #pragma unroll
     for (int g = 0; g < G; g++) {
       const v4i c = pair_dots<FMT>(st.a[t], st.x[g], st.ns[g], sh);
 #pragma unroll
       for (int v = 0; v < 4; v++) {
-        const float f = (float)c[v], m = dw[v] * st.dx[g];
+        const float f = (float)c[v], m = mul_h_f(v < 2 ? wv.x : wv.y, v & 1, st.dx[g]);
         float& r = acc[t][PP == 1 ? 0 : pp][g][v];
         if (SEQ) {
           // block b (this lane), then block b+1 (lane i ^ 8)
