@@ -428,11 +428,6 @@ struct MpAddr {
   bool gon;
 };
 
-// The exact int32 dots of one pair step: lane (i, q) holds 16 bytes of weight
-// codes (araw: Q8_0 codes, or Q4_0 packed nibbles whose half sh = 0 / 4 it
-// feeds) and 16 bytes of the activation chunk; c[v] is the dot of weight row
-// 4q + v with column i, starting from ns (Q4_0: -8 * sum of that column's
-// activation codes).
 // f32(half `hi` of the two fp16 in h2) * b, rounded once (the product h2f(h) * b), in one
 // mixed-precision FMA with a negative-zero addend.
 __device__ __forceinline__ float mul_h_f(uint32_t h2, int hi, float b) {
@@ -444,6 +439,11 @@ __device__ __forceinline__ float mul_h_f(uint32_t h2, int hi, float b) {
   return d;
 }
 
+// The exact int32 dots of one pair step: lane (i, q) holds 16 bytes of weight
+// codes (araw: Q8_0 codes, or Q4_0 packed nibbles whose half sh = 0 / 4 it
+// feeds) and 16 bytes of the activation chunk; c[v] is the dot of weight row
+// 4q + v with column i, starting from ns (Q4_0: -8 * sum of that column's
+// activation codes).
 template <int FMT>
 __device__ __forceinline__ v4i pair_dots(uint4 araw, uint4 x, int ns, int sh) {
   uint4 av = araw;
