@@ -31,6 +31,17 @@ __device__ __forceinline__ uint2 ld8_stream(const void* p) {
 }
 __device__ __forceinline__ uint16_t ld2_stream(const uint16_t* p) { return __builtin_nontemporal_load(p); }
 
+// f32(half `hi` of the two fp16 in h2) * b, rounded once (the product h2f(h) * b), in one
+// mixed-precision FMA with a negative-zero addend.
+__device__ __forceinline__ float mul_h_f(uint32_t h2, int hi, float b) {
+  float d;
+  if (hi)
+    asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h2), "v"(b));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h2), "v"(b));
+  return d;
+}
+
 __device__ __forceinline__ float h2f(uint16_t h) {
   _Float16 v;
   __builtin_memcpy(&v, &h, 2);
@@ -78,8 +89,8 @@ __device__ __forceinline__ void q4k_dm(uint4 h, int j, float& D, float& M) {
   const unsigned a = (h.y >> sh) & 255u, b = (h.z >> sh) & 255u, c = (h.w >> sh) & 255u;
   const unsigned sc = j < 4 ? (a & 63u) : ((c & 15u) | ((a >> 6) << 4));
   const unsigned m = j < 4 ? (b & 63u) : ((c >> 4) | ((b >> 6) << 4));
-  D = h2f((uint16_t)(h.x & 0xffffu)) * (float)sc;
-  M = h2f((uint16_t)(h.x >> 16)) * (float)m;
+  D = mul_h_f(h.x, 0, (float)sc);
+  M = mul_h_f(h.x, 1, (float)m);
 }
 
 // Q4_K: sub-block j's 6-bit sub-scale and sub-min from a header (as q4k_dm).

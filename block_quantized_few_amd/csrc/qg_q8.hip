@@ -428,17 +428,6 @@ struct MpAddr {
   bool gon;
 };
 
-// f32(half `hi` of the two fp16 in h2) * b, rounded once (the product h2f(h) * b), in one
-// mixed-precision FMA with a negative-zero addend.
-__device__ __forceinline__ float mul_h_f(uint32_t h2, int hi, float b) {
-  float d;
-  if (hi)
-    asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h2), "v"(b));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h2), "v"(b));
-  return d;
-}
-
 // The exact int32 dots of one pair step: lane (i, q) holds 16 bytes of weight
 // codes (araw: Q8_0 codes, or Q4_0 packed nibbles whose half sh = 0 / 4 it
 // feeds) and 16 bytes of the activation chunk; c[v] is the dot of weight row
