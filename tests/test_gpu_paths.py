@@ -144,7 +144,7 @@ def test_wide_tiles_of_three_at_3_to_8_rows(fmt, n, k, rows):
         assert np.array_equal(bits(y[r]), bits(y1[0]))
 
 
-@pytest.mark.parametrize("fmt,ofmt", FMTS)
+@pytest.mark.parametrize("fmt,ofmt", FMTS + [(q.Q4_K, O.Q4_K)])
 @pytest.mark.parametrize("k", [40960, 73728])
 def test_long_rows_at_one_and_two_rows(fmt, ofmt, k):
     """Rows too long for the GEMV launch's staging area (k = 73728: one row of Q8_0 blocks is 82944 bytes; k =
@@ -152,8 +152,9 @@ def test_long_rows_at_one_and_two_rows(fmt, ofmt, k):
     oracle and a row of a two-row call has its bits alone."""
     n = 100
     w = gauss((n, k), 0.02, 17, 1).numpy()
-    blocks, img = oracle_image(ofmt, w)
-    fn = q.qgemv_q8_0 if fmt == q.Q8_0 else q.qgemv_q4_0
+    blocks = O.quantize_weights(ofmt, w)
+    img = torch.from_numpy(q.pack_image(fmt, blocks, n, k)).cuda()
+    fn = {q.Q8_0: q.qgemv_q8_0, q.Q4_0: q.qgemv_q4_0, q.Q4_K: q.qgemv_q4_k}[fmt]
     x = gauss((2, k), 1.0, 17, 2).numpy()
     xd = torch.from_numpy(x).cuda()
     ws = torch.full((q.workspace_bytes(2, k),), 0x7F, dtype=torch.uint8, device="cuda")  # not zero: must be written
