@@ -721,7 +721,7 @@ def cpu_info():
 
 
 def cpu_baseline(synth):
-    """The C oracle on a bounded slice of the headline workload: the first 16384 of the LM head's 128256 output
+    """The C oracle on a bounded slice of the headline workload: the first 32768 of the LM head's 128256 output
     rows (4096 columns, Q8_0 blocks from the oracle's own quantizer) at 1, 8 and 16 activation rows, the three
     calls as one step; five reps on all the cores this process may use (at most 16, the host share of one GPU)
     and five on one core.  GB/s counts the slice's weight bytes, as the GPU figure counts the whole image's."""
@@ -731,7 +731,7 @@ def cpu_baseline(synth):
 
     model, nproc, avail = cpu_info()
     threads = max(1, min(16, avail))
-    ns = 16384
+    ns = 32768
     w = synth.gaussian((ns, LM_K), 0.02, synth.tensor_seed(4, 0, 0)).numpy()
     blocks = O.quantize_weights(O.Q8_0, w)
     del w
