@@ -725,53 +725,54 @@ __device__ void mp_tile(const TileArgs& ta, int R, const MpLds& ml, int count = 
     const int64_t row_out = wrow0;
     const bool more = PF && c + 1 < count;
     if (more) start(ta.row0 + (int64_t)(c + 1) * row_stride);
-    // then the W2 pair groups of a wave part (the tree's upper level), then wave parts left to right
-    bool store = true;
     if (gw > 1) {
+      // the wave's values to the combine area
       constexpr int NV = NT * G * 4;
+      const int ws = FMT == FMT_Q4K ? ml.red_ws : NV * WAVE;
 #pragma unroll
       for (int t = 0; t < NT; t++)
 #pragma unroll
         for (int gg = 0; gg < G; gg++)
 #pragma unroll
-          for (int v = 0; v < 4; v++)
-            red[(FMT == FMT_Q4K ? wave * ml.red_ws : wave * NV * WAVE) + ((t * G + gg) * 4 + v) * WAVE + lane] =
-                res[t][gg][v];
+          for (int v = 0; v < 4; v++) red[wave * ws + ((t * G + gg) * 4 + v) * WAVE + lane] = res[t][gg][v];
       __syncthreads();
-      if (wg == 0) {
-#pragma unroll
-        for (int t = 0; t < NT; t++)
-#pragma unroll
-          for (int gg = 0; gg < G; gg++)
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-              const int o = ((t * G + gg) * 4 + v) * WAVE + lane;
-              const int w0 = g * gw;
-              float x = 0.0f;
-              for (int s2 = 0; s2 < pl.S; s2++) {
-                const int ws = FMT == FMT_Q4K ? ml.red_ws : NV * WAVE;
-                float part = red[(w0 + s2 * W2) * ws + o];
-                if (W2 == 2) part = part + red[(w0 + s2 * W2 + 1) * ws + o];
-                x = s2 == 0 ? part : x + part;
-              }
-              res[t][gg][v] = x;
-            }
+      // One output per thread, over all groups of the workgroup: value o of
+      // lane li + 16 lq (li < 8) of each wave of the group, summed as the W2
+      // pair groups of a wave part (the tree's upper level), then the wave
+      // parts left to right.
+      constexpr int OUT = NV * 32;
+      const int ngroups = WAVES / gw;
+#pragma unroll 1
+      for (int e = threadIdx.x; e < ngroups * OUT; e += WG) {
+        const int gi = e / OUT, r = e - gi * OUT, o = r >> 5, li = r & 7, lq = (r >> 3) & 3;
+        const int t = o / (G * 4), gg = (o >> 2) % G, v = o & 3;
+        const int ar = gg * 8 + li;  // activation row of the output's column
+        const int64_t row = row_out + (int64_t)(gi - g) * TILE * NT + t * TILE + 4 * lq + v;
+        if (ar >= R || row >= ta.n) continue;
+        const int w0 = gi * gw, off = o * WAVE + lq * 16 + li;
+        float x = 0.0f;
+        for (int s2 = 0; s2 < pl.S; s2++) {
+          float part = red[(w0 + s2 * W2) * ws + off];
+          if (W2 == 2) part = part + red[(w0 + s2 * W2 + 1) * ws + off];
+          x = s2 == 0 ? part : x + part;
+        }
+        ta.y[(int64_t)ta.s_dst[ar] * ta.ldy + row] = x;
       }
       __syncthreads();  // the combine area is free for the next tile
-      store = wg == 0;
-    }
-    if (store && i < 8) {
+    } else {
+      if (i < 8) {
 #pragma unroll
-      for (int gg = 0; gg < G; gg++) {
-        const int ar = gg * 8 + i;  // activation row of this lane's column
-        if (ar < R) {
+        for (int gg = 0; gg < G; gg++) {
+          const int ar = gg * 8 + i;  // activation row of this lane's column
+          if (ar < R) {
 #pragma unroll
-          for (int t = 0; t < NT; t++)
+            for (int t = 0; t < NT; t++)
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-              const int64_t row = row_out + t * TILE + 4 * q + v;
-              if (row < ta.n) ta.y[(int64_t)ta.s_dst[ar] * ta.ldy + row] = res[t][gg][v];
-            }
+              for (int v = 0; v < 4; v++) {
+                const int64_t row = row_out + t * TILE + 4 * q + v;
+                if (row < ta.n) ta.y[(int64_t)ta.s_dst[ar] * ta.ldy + row] = res[t][gg][v];
+              }
+          }
         }
       }
     }
