@@ -43,29 +43,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
-// (value, index) with the larger value, ties to the lower index (selects,
-// no branches).
-__device__ __forceinline__ void pick(float& v, int& i, float ov, int oi) {
-  const bool better = (ov > v) | ((ov == v) & (oi < i));
-  v = better ? ov : v;
-  i = better ? oi : i;
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  pick(v, i, dpp_f<CTRL>(v), dpp_i<CTRL>(i));
-}
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<0xB1>(v, i);
-  argmax_step<0x4E>(v, i);
-  argmax_step<0x141>(v, i);
-  argmax_step<0x140>(v, i);
-  float v0 = lane_f(v, 0), v2 = lane_f(v, 32);
-  int i0 = __builtin_amdgcn_readlane(i, 0), i2 = __builtin_amdgcn_readlane(i, 32);
-  pick(v0, i0, lane_f(v, 16), __builtin_amdgcn_readlane(i, 16));
-  pick(v2, i2, lane_f(v, 48), __builtin_amdgcn_readlane(i, 48));
-  pick(v0, i0, v2, i2);
-  v = v0;
-  i = i0;
+
+// (va, ia) ahead of (vb, ib): the larger logit, ties to the lower index.
+__device__ __forceinline__ void order2(float& va, int& ia, float& vb, int& ib) {
+  const bool swap = (vb > va) | ((vb == va) & (ib < ia));
+  const float tv = va;
+  const int ti = ia;
+  va = swap ? vb : va;
+  ia = swap ? ib : ia;
+  vb = swap ? tv : vb;
+  ib = swap ? ti : ib;
 }
 
 // Routing of one row by one wave: softmax over the E logits in fp32 (max
@@ -73,6 +68,13 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 // wave_sum tree), and the topk experts by logit, ties to the lower index, in
 // descending order, written to ex[] / wt[] (lane k writes pick k).  NPER:
 // logits per lane (E <= 64 * NPER).
+//
+// Selection: each lane orders its own entries once (expert lane + 64 i; past
+// E, or a NaN logit, never picked: -inf with an index above every expert's),
+// so its best remaining entry is always its first.  A pick is the wave's
+// largest first entry; the lanes holding that value are found by ballot, and
+// of several (equal logits) the lowest expert index wins.  The winner's lane
+// then moves its next entry up.
 template <int NPER>
 __device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
   const int lane = threadIdx.x & (WAVE - 1);
@@ -92,24 +94,36 @@ __device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int
     sum += lane + WAVE * i < E ? t : 0.0f;
   }
   sum = wave_sum(sum);
+  float sv[NPER];
+  int si[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; i++) {
+    const int e = lane + WAVE * i;
+    const bool ok = (e < E) & (l[i] == l[i]);
+    sv[i] = ok ? l[i] : -INFINITY;
+    si[i] = ok ? e : 0x7fffffff;
+  }
+#pragma unroll
+  for (int i = 1; i < NPER; i++)
+#pragma unroll
+    for (int j = i; j > 0; j--) order2(sv[j - 1], si[j - 1], sv[j], si[j]);
   float mv = 0.0f;  // this lane's pick (lane k: the k-th)
   int mi = 0;
-  unsigned avail = 0;  // bit i: entry i is a real expert not picked yet
-#pragma unroll
-  for (int i = 0; i < NPER; i++) avail |= (lane + WAVE * i < E ? 1u : 0u) << i;
   for (int k = 0; k < topk; k++) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    const float bv = wave_max(sv[0]);
+    const unsigned long long at = __ballot(sv[0] == bv);
+    int bi;
+    if (__popcll(at) == 1) bi = __builtin_amdgcn_readlane(si[0], (int)__builtin_ctzll(at));
+    else bi = wave_min_i(sv[0] == bv ? si[0] : 0x7fffffff);
+    if (si[0] == bi) {  // the winner's lane: its next entry first
 #pragma unroll
-    for (int i = 0; i < NPER; i++) {
-      const int e = lane + WAVE * i;
-      const bool ok = (avail >> i) & 1u;
-      const bool better = ok & ((l[i] > bv) | ((l[i] == bv) & (e < bi)));
-      bv = better ? l[i] : bv;
-      bi = better ? e : bi;
+      for (int i = 0; i + 1 < NPER; i++) {
+        sv[i] = sv[i + 1];
+        si[i] = si[i + 1];
+      }
+      sv[NPER - 1] = -INFINITY;
+      si[NPER - 1] = 0x7fffffff;
     }
-    wave_argmax(bv, bi);
-    avail &= ~((bi % WAVE == lane ? 1u : 0u) << (bi / WAVE));
     mv = lane == k ? bv : mv;  // lane k keeps pick k
     mi = lane == k ? bi : mi;
   }

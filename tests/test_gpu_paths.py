@@ -26,12 +26,15 @@ def test_routing_matches_oracle(E):
         a, b = rng.choice(E, size=2, replace=False)
         logits[r, b] = logits[r, a]
         logits[r, (a + 1) % E] = logits[r].max()
-    for topk in sorted({1, min(8, E), min(32, E)}):
-        log(f"routing E={E} topk={topk}")
-        ex, _, wt = q.moe_route(torch.from_numpy(logits).cuda(), topk)
-        ex_o, p_o = O.route_topk(logits, topk)
-        assert np.array_equal(ex.cpu().numpy().reshape(rows, topk), ex_o)
-        assert np.allclose(wt.cpu().numpy().reshape(rows, topk), p_o, rtol=1e-5, atol=1e-9)
+    # and logits on a coarse grid: many experts share each value, so most picks break a tie
+    coarse = (np.round(logits * 2.0) / 2.0).astype(np.float32)
+    for lg, kind in ((logits, "gauss"), (coarse, "coarse")):
+        for topk in sorted({1, min(8, E), min(32, E)}):
+            log(f"routing E={E} topk={topk} logits={kind}")
+            ex, _, wt = q.moe_route(torch.from_numpy(lg).cuda(), topk)
+            ex_o, p_o = O.route_topk(lg, topk)
+            assert np.array_equal(ex.cpu().numpy().reshape(rows, topk), ex_o)
+            assert np.allclose(wt.cpu().numpy().reshape(rows, topk), p_o, rtol=1e-5, atol=1e-9)
 
 
 @pytest.mark.parametrize("k", [512, 2048, 3072, 4096, 8192])
