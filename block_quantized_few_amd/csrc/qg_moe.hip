@@ -97,16 +97,19 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g
 // float4 per slot; it adds the slots strictly in slot order, so the result
 // does not depend on how the loads are grouped (the drama page, series
 // commits: its combine kernel was widened without changing any sum's order).
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ o,
-                                                          const float* __restrict__ weight, int slots,
-                                                          int64_t hidden, float* __restrict__ y) {
+constexpr int COMBINE_WG = 128;
+constexpr int COMBINE_BATCH = 16;  // slots whose loads are issued together
+
+__global__ __launch_bounds__(COMBINE_WG) void moe_combine_kernel(const float* __restrict__ o,
+                                                                 const float* __restrict__ weight, int slots,
+                                                                 int64_t hidden, float* __restrict__ y) {
   const int r = blockIdx.y;
   const int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i4 * 4 >= hidden) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // slots in order; each group of eight slots' loads issued together (a slot
-  // past the end re-reads the last one and is not used)
-  constexpr int B = 8;
+  // slots in order; each batch's loads issued together (a slot past the end
+  // re-reads the last one and is not used)
+  constexpr int B = COMBINE_BATCH;
   for (int s0 = 0; s0 < slots; s0 += B) {
     float wgt[B];
     float4 v[B];
@@ -181,8 +184,8 @@ int launch_swiglu(const float* gu, int m, int64_t ffn, float* h, hipStream_t s) 
 
 int launch_moe_combine(const float* o, const float* weight, int rows, int slots, int64_t hidden, float* y,
                        hipStream_t s) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(grid1(hidden / 4, 256), rows), dim3(256), 0, s, o, weight, slots, hidden,
-                     y);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(grid1(hidden / 4, COMBINE_WG), rows), dim3(COMBINE_WG), 0, s, o, weight,
+                     slots, hidden, y);
   return hip_status(hipGetLastError(), "moe_combine_kernel");
 }
 
