@@ -485,8 +485,13 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
       return st;
   }
   // at most two rows: the down launch takes the SwiGLU of the gate/up rows in
-  // its staging (one launch fewer); otherwise a launch quantizes it first
+  // its staging (one launch fewer), and where the shape allows it the combine
+  // too; otherwise a launch quantizes the SwiGLU first
   const bool glu = rows <= 2 && grouped_glu_fits(ffn);
+  if (glu && moe_down_combine_fits(rows, slots, hidden, ffn)) {
+    if (int st = launch_moe_down_combine(down_images, n_images, hidden, ffn, gu, ex, wt, rows, slots, y, s)) return st;
+    return ok();
+  }
   if (!glu)
     if (int st = launch_swiglu_q8(gu, m, ffn, w + M.hprep, s)) return st;
   if (int st = launch_grouped_planned(down_images, n_images, hidden, ffn, w + M.hprep, m, header, sorted, items,

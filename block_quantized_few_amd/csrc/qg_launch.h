@@ -105,6 +105,12 @@ int launch_moe_up(const void* images, int64_t n, int64_t k, const void* prep, co
                   hipStream_t s);
 // Whether two SwiGLU rows of length k fit a tile's staging area whole.
 bool grouped_glu_fits(int64_t k);
+// The down projection of every assignment and the weighted combine in one
+// launch (one or two rows; false: the shape needs the grouped launch and the
+// combine launch).
+bool moe_down_combine_fits(int rows, int slots, int64_t hidden, int64_t ffn);
+int launch_moe_down_combine(const void* images, int n_images, int64_t hidden, int64_t ffn, const float* gu,
+                            const int32_t* expert, const float* weight, int rows, int slots, float* y, hipStream_t s);
 
 // Fused MoE pieces: routing + plan + input quantization (one workgroup), and
 // SwiGLU quantized for the down projection.

@@ -1189,6 +1189,201 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mo
   }
 }
 
+// ------------------------------------------------ MoE down and combine ---
+//
+// One or two rows: the down projection of every assignment and the weighted
+// combine in one launch.  Workgroup w takes output rows 16w .. 16w+15 (one
+// image tile) of every assignment.  A wave task is NA = 4/H assignments and one
+// wave part s; lane h * (64/H) + 16 j + i is lane part h of row i for the
+// task's assignment j.  The activation row of assignment a is the SwiGLU of its
+// gate/up row, quantized in staging as the grouped launch's staging does it.
+// A lane sums its blocks in order, the lane parts and then the wave parts
+// follow the lanes-own-rows kernel's tree, so each assignment's output has the
+// bits of the one-row dense call; the slots then add up in the combine
+// kernel's order (fma of weight and output, slot by slot from zero).
+struct DownCombine {
+  const uint8_t* images;
+  int64_t expert_bytes;
+  size_t scale_off;
+  int n_images;
+  int64_t n;  // hidden: output rows, a multiple of 16
+  int kbp;
+  PartPlan pl;
+  const float* gu;  // [m][2 ffn]: gate values, then up values
+  int64_t ffn;
+  const int32_t* expert;
+  const float* weight;
+  int rows, slots;
+  int tasks;  // ceil(m / NA) * S
+  int waves;  // of the workgroup: the tasks', or more for the staging
+  int qpt;    // staging quarters per thread (1 or 2)
+  float* y;
+};
+
+constexpr int MDC_LA = 8;          // blocks in flight per lane
+constexpr int MDC_MAX_WAVES = 12;  // one wave task per wave; three waves a SIMD (170 registers)
+
+__global__ __launch_bounds__(MDC_MAX_WAVES * WAVE) void moe_down_combine_kernel(DownCombine a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int m = a.rows * a.slots, kbp = a.kbp;
+  const PartPlan& pl = a.pl;
+  uint8_t* xq = lds;                                                  // [m][kbp] x 32 codes
+  float* xd = reinterpret_cast<float*>(lds + (size_t)m * kbp * 32);  // [m][kbp] scales
+  float* red = xd + (size_t)m * kbp;                                  // [m][16][S] wave-part sums
+  const int nt = (int)blockDim.x, tid = (int)threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (WAVE - 1);
+  const int lg_rpw = 6 - pl.lgH, na = 1 << (lg_rpw - 4);
+  const int h = lane >> lg_rpw, j = (lane >> 4) & (na - 1), i = lane & 15;
+  const int s = wave & (pl.S - 1), ag = wave >> pl.lgS;
+  const int aa = ag * na + j;
+  const bool on = wave < a.tasks && aa < m;
+  // the lane's expert (the plan's), then the staging's gate/up values, then the weights
+  int e = a.expert[on ? aa : 0];
+  const int nq = m * kbp * 4;  // staging quarters: (assignment, block, quarter)
+  const int64_t nblk = a.ffn / QK;
+  // quarter t's eight gate and eight up values (zeros past the rows' blocks):
+  // four 16-byte loads, always issued (a quarter past the rows reads row 0's),
+  // so the expert's load before them is waited for alone
+  auto gu_load = [&](int t, float (&gv)[8], float (&uv)[8]) {
+    const int blk = t >> 2, q = t & 3, ai = blk / kbp, b = blk - ai * kbp;
+    const bool ld = t < nq && b < nblk;
+    const float* g = a.gu + ((int64_t)(ld ? ai : 0) * 2 * a.ffn + (int64_t)(ld ? b : 0) * QK + q * 8);
+    const float4 g0 = *reinterpret_cast<const float4*>(g), g1 = *reinterpret_cast<const float4*>(g + 4);
+    const float4 u0 = *reinterpret_cast<const float4*>(g + a.ffn), u1 = *reinterpret_cast<const float4*>(g + a.ffn + 4);
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int v = 0; v < 8; v++) {
+      gv[v] = ld ? gg[v] : 0.0f;
+      uv[v] = ld ? uu[v] : 0.0f;
+    }
+  };
+  // SwiGLU, then the q8 block (four lanes a block, as the SwiGLU kernel)
+  auto stage = [&](int t, const float (&gv)[8], const float (&uv)[8]) {
+    float v[8];
+#pragma unroll
+    for (int x = 0; x < 8; x++) v[x] = gv[x] / (1.0f + expf(-gv[x])) * uv[x];
+    unsigned lo, hi;
+    float d;
+    int sum;
+    quantize_quarter(v, lo, hi, d, sum);  // whole quads: nt is a multiple of 64
+    if (t < nq) {
+      *reinterpret_cast<uint2*>(xq + (size_t)(t >> 2) * 32 + (t & 3) * 8) = make_uint2(lo, hi);
+      if ((t & 3) == 0) xd[t >> 2] = d;
+    }
+  };
+  float gv[8], uv[8], gv2[8], uv2[8];
+  gu_load(tid, gv, uv);
+  gu_load(tid + nt, gv2, uv2);  // a second round's (two rows), always loaded: no branch around loads
+  const bool ev = (unsigned)e < (unsigned)a.n_images;  // a plan entry out of range adds nothing
+  e = ev ? e : 0;
+  const int64_t row0 = (int64_t)blockIdx.x * TILE;
+  const uint8_t* img = a.images + (size_t)e * (size_t)a.expert_bytes;
+  const size_t c0 = (size_t)(row0 >> 4) * (size_t)kbp;  // the tile's first cell
+  const uint8_t* tcode = img + c0 * 512;
+  const uint16_t* tscale = reinterpret_cast<const uint16_t*>(img + a.scale_off) + c0 * TILE;
+  const uint32_t woff = (uint32_t)i * 16u, soff = (uint32_t)i;
+  const int bpart = s * pl.H * pl.BS + h;
+  const bool task = wave < a.tasks;  // uniform: waves past the tasks only stage
+  WBlock<FMT_Q8> w[MDC_LA];
+  if (task) {
+#pragma unroll
+    for (int u = 0; u < MDC_LA; u++)
+      if (u < pl.BS) w[u] = load_block<FMT_Q8>(tcode, woff, tscale, soff, bpart + pl.H * u);
+  }
+  // (the quarters' values were loaded before the weights)
+  stage(tid, gv, uv);
+  if (a.qpt > 1) stage(tid + nt, gv2, uv2);
+  __syncthreads();
+  float acc = 0.0f;
+  const int ac = on ? aa : 0;
+  const uint8_t* xa = xq + (size_t)ac * kbp * 32;
+  const float* da = xd + (size_t)ac * kbp;
+  for (int u = 0; task && u < pl.BS; u += MDC_LA) {
+#pragma unroll
+    for (int v = 0; v < MDC_LA; v++) {
+      if (u + v < pl.BS) {
+        const int b = bpart + pl.H * (u + v);
+        const uint4 xl = ld16(xa + (size_t)b * 32), xh = ld16(xa + (size_t)b * 32 + 16);
+        const int isum = dot_q8(w[v].lo, w[v].hi, xl, xh);
+        acc = __builtin_fmaf((float)isum, h2f(w[v].sc) * da[b], acc);
+        if (u + v + MDC_LA < pl.BS) w[v] = load_block<FMT_Q8>(tcode, woff, tscale, soff, b + pl.H * MDC_LA);
+      }
+    }
+  }
+  // lane parts: ((h0 + h1) + (h2 + h3)); then the wave parts through LDS
+  for (int off = 1 << lg_rpw; off < WAVE; off <<= 1) acc += __shfl_xor(acc, off);
+  if (on && h == 0) red[((size_t)aa * TILE + i) * pl.S + s] = ev ? acc : 0.0f;
+  __syncthreads();
+  if (tid < a.rows * TILE) {
+    const int r = tid >> 4, ri = tid & 15;
+    float y = 0.0f;
+    for (int sl = 0; sl < a.slots; sl++) {
+      const int as = r * a.slots + sl;
+      const float* rp = red + ((size_t)as * TILE + ri) * pl.S;
+      float v = rp[0];
+      for (int s2 = 1; s2 < pl.S; s2++) v += rp[s2];
+      y = __builtin_fmaf(a.weight[as], v, y);
+    }
+    a.y[(int64_t)r * a.n + row0 + ri] = y;
+  }
+}
+
+// Whether the one-launch down projection and combine takes this step, and its
+// launch shape.
+static bool down_combine_shape(int rows, int slots, int64_t hidden, int64_t ffn, DownCombine& dc, size_t& lds) {
+  if (rows < 1 || rows > 2 || hidden % TILE) return false;
+  const int kbp = (int)kbp_of(ffn);
+  const PartPlan pl = part_plan(kbp);
+  if (pl.H > 4) return false;  // rows of a wave part: 64 / H >= 16
+  const int m = rows * slots, na = 4 / pl.H;
+  const int tasks = (m + na - 1) / na * pl.S;
+  const int quads = (m * kbp * 4 + WAVE - 1) / WAVE;  // staging waves at one quarter a thread
+  const int waves = tasks > (quads + 1) / 2 ? tasks : (quads + 1) / 2;
+  if (waves > MDC_MAX_WAVES) return false;
+  lds = (size_t)m * kbp * 36 + (size_t)m * TILE * pl.S * 4;
+  if (lds > 64 * 1024) return false;
+  dc.n = hidden;
+  dc.kbp = kbp;
+  dc.pl = pl;
+  dc.ffn = ffn;
+  dc.rows = rows;
+  dc.slots = slots;
+  dc.tasks = tasks;
+  dc.waves = waves;
+  dc.qpt = waves * WAVE >= m * kbp * 4 ? 1 : 2;
+  return true;
+}
+
+bool moe_down_combine_fits(int rows, int slots, int64_t hidden, int64_t ffn) {
+  DownCombine dc;
+  size_t lds = 0;
+  return down_combine_shape(rows, slots, hidden, ffn, dc, lds);
+}
+
+int launch_moe_down_combine(const void* images, int n_images, int64_t hidden, int64_t ffn, const float* gu,
+                            const int32_t* expert, const float* weight, int rows, int slots, float* y,
+                            hipStream_t s) {
+  DownCombine dc;
+  size_t lds = 0;
+  if (!down_combine_shape(rows, slots, hidden, ffn, dc, lds))
+    return fail(QG_ELAUNCH, "no one-launch down projection for rows=%d slots=%d ffn=%lld", rows, slots,
+                (long long)ffn);
+  dc.images = (const uint8_t*)images;
+  dc.expert_bytes = (int64_t)image_total_bytes(QG_FMT_Q8_0, hidden, ffn);
+  dc.scale_off = image_scale_offset(QG_FMT_Q8_0, hidden, ffn);
+  dc.n_images = n_images;
+  dc.gu = gu;
+  dc.expert = expert;
+  dc.weight = weight;
+  dc.y = y;
+  if (lds > 48 * 1024)
+    (void)hipFuncSetAttribute((const void*)moe_down_combine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+  hipLaunchKernelGGL(moe_down_combine_kernel, dim3((unsigned)(hidden / TILE)), dim3(dc.waves * WAVE), lds, s, dc);
+  return hip_status(hipGetLastError(), "moe_down_combine_kernel");
+}
+
 // ------------------------------------------------------ pair-dot hook ---
 
 // Test hook: the int32 dots of every (activation row, weight row, block) as the

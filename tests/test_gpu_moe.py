@@ -115,6 +115,21 @@ def test_fused_moe_step_equals_composition(moe, rows):
         assert torch.equal(yf1[0], yf[0])
 
 
+@pytest.mark.parametrize("rows,topk", [(1, 4), (2, 4), (1, 32), (2, 32)])
+def test_fused_moe_step_other_topk(moe, rows, topk):
+    """At 1-2 rows the step's down projection and combine run as one launch when the assignments fit one
+    workgroup's waves (top-4 here), and as the grouped launch plus the combine launch when they do not
+    (top-32); both give the composition's bits."""
+    log(f"fused moe rows={rows} topk={topk}")
+    x = torch.from_numpy(gauss((rows, HIDDEN), 1.0, WL, 48 + rows).numpy()).cuda()
+    y, (expert, _, weight), logits = q.moe_step(x, moe["r16"], E, topk, moe["gu"], moe["dn"], FFN, shared_expert=E)
+    yf, (expert_f, weight_f), logits_f = q.moe_step_fused(x, moe["r16"], E, topk, moe["gu"], moe["dn"], FFN)
+    assert torch.equal(logits_f, logits)
+    assert torch.equal(expert_f, expert)
+    assert torch.equal(weight_f, weight)
+    assert torch.equal(yf, y)
+
+
 # ------------------------------------------------------------- FP8 lane ---
 # The routed step with block-FP8 experts and 1 x 128 FP8 activation groups (qg_moe_step_fp8), on a smaller
 # expert set: 64 experts of 256-wide FFNs over hidden 1024, top-8 and a shared expert.
