@@ -742,8 +742,13 @@ __device__ void mp_tile(const TileArgs& ta, int R, const MpLds& ml, int count = 
       // parts left to right.
       constexpr int OUT = NV * 32;
       const int ngroups = WAVES / gw;
+      // (the thread index through an opaque copy: the indexes below are then
+      // formed here, not hoisted out of the tile loops, where they would hold
+      // registers through the step loop)
+      int e0;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(e0) : "v"((int)threadIdx.x));
 #pragma unroll 1
-      for (int e = threadIdx.x; e < ngroups * OUT; e += WG) {
+      for (int e = e0; e < ngroups * OUT; e += WG) {
         const int gi = e / OUT, r = e - gi * OUT, o = r >> 5, li = r & 7, lq = (r >> 3) & 3;
         const int t = o / (G * 4), gg = (o >> 2) % G, v = o & 3;
         const int ar = gg * 8 + li;  // activation row of the output's column
