@@ -62,9 +62,8 @@ __device__ __forceinline__ int dot_q8(uint4 wl, uint4 wh, uint4 xl, uint4 xh) {
   return s;
 }
 
-// Exact int32 dot of one Q4_0 block (16 packed bytes) with one q8 block.  The
-// raw codes c in [0,15] enter the dot as they are; the -8 offset is folded in
-// through the start value nsx = -8 * sum(q_x).
+// Exact int32 dot of 16 packed bytes of raw 4-bit codes c in [0,15] (Q4_K's)
+// with one q8 block, from the start value nsx.
 __device__ __forceinline__ int dot_q4(uint4 p, uint4 xl, uint4 xh, int nsx) {
   const unsigned M = 0x0F0F0F0Fu;
   int s = nsx;
@@ -76,6 +75,24 @@ __device__ __forceinline__ int dot_q4(uint4 p, uint4 xl, uint4 xh, int nsx) {
   s = __builtin_amdgcn_sdot4((int)((p.y >> 4) & M), (int)xh.y, s, false);
   s = __builtin_amdgcn_sdot4((int)((p.z >> 4) & M), (int)xh.z, s, false);
   s = __builtin_amdgcn_sdot4((int)((p.w >> 4) & M), (int)xh.w, s, false);
+  return s;
+}
+
+// Sixteen times the exact int32 dot of one Q4_0 image block with one q8 block.
+// The image keeps each code c as c XOR 8, the 4-bit two's complement of
+// c - 8; moved to the high half of its byte, a nibble is the int8 16 (c - 8).
+// (The products stay exact: |16 * 32 * 8 * 127| < 2^24.)
+__device__ __forceinline__ int dot_q4s16(uint4 p, uint4 xl, uint4 xh) {
+  const unsigned H = 0xF0F0F0F0u;
+  int s = 0;
+  s = __builtin_amdgcn_sdot4((int)((p.x << 4) & H), (int)xl.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)((p.y << 4) & H), (int)xl.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)((p.z << 4) & H), (int)xl.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)((p.w << 4) & H), (int)xl.w, s, false);
+  s = __builtin_amdgcn_sdot4((int)(p.x & H), (int)xh.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)(p.y & H), (int)xh.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)(p.z & H), (int)xh.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)(p.w & H), (int)xh.w, s, false);
   return s;
 }
 

@@ -258,6 +258,8 @@ int qg_pack_image(int fmt, const void* blocks, int64_t n, int64_t k, void* image
       uint8_t* cell = dst + cell_row_offset(fmt, o, b, kbp);
       memcpy(cell, blk + 2, 16);
       if (fmt == QG_FMT_Q8_0) memcpy(cell + 256, blk + 18, 16);
+      else
+        for (int l = 0; l < 16; l++) cell[l] ^= 0x88;  // Q4_0 codes kept as c XOR 8
     }
   return ok();
 }
@@ -292,6 +294,8 @@ int qg_unpack_image(int fmt, const void* image, int64_t n, int64_t k, void* bloc
       const uint8_t* cell = src + cell_row_offset(fmt, o, b, kbp);
       memcpy(blk + 2, cell, 16);
       if (fmt == QG_FMT_Q8_0) memcpy(blk + 18, cell + 256, 16);
+      else
+        for (int l = 0; l < 16; l++) blk[2 + l] ^= 0x88;
     }
   return ok();
 }

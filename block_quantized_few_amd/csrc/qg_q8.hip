@@ -260,8 +260,12 @@ __device__ __forceinline__ void compute_block(float (&acc)[R], const WBlock<FMT>
     const uint8_t* xb = lds + ((size_t)r * nslot + slot) * 32;
     const uint4 xl = ld16(xb), xh = ld16(xb + 16);
     const float dxr = ld[r * nslot + slot];
-    const int isum = FMT == FMT_Q8 ? dot_q8(w.lo, w.hi, xl, xh) : dot_q4(w.lo, xl, xh, ln[r * nslot + slot]);
-    acc[r] = __builtin_fmaf((float)isum, dw * dxr, acc[r]);
+    if constexpr (FMT == FMT_Q8) {
+      acc[r] = __builtin_fmaf((float)dot_q8(w.lo, w.hi, xl, xh), dw * dxr, acc[r]);
+    } else {
+      // sixteen times the dot against dx / 16: the product and the sum are those of the dot against dx
+      acc[r] = __builtin_fmaf((float)dot_q4s16(w.lo, xl, xh), dw * (dxr * 0.0625f), acc[r]);
+    }
   }
 }
 
@@ -436,7 +440,16 @@ struct MpAddr {
 template <int FMT>
 __device__ __forceinline__ v4i pair_dots(uint4 araw, uint4 x, int ns, int sh) {
   uint4 av = araw;
-  if (nibble_fmt(FMT)) {
+  if constexpr (FMT == FMT_Q4) {
+    // codes kept as c XOR 8: the lane's nibble to the high half of each byte
+    // (a 64-bit shift moves two words; the mask clears what crosses), the int8
+    // 16 (c - 8), so the product is sixteen times the dot and needs no start value
+    const uint64_t lo = ((uint64_t)av.y << 32 | av.x) << (4 - sh), hi = ((uint64_t)av.w << 32 | av.z) << (4 - sh);
+    av.x = (uint32_t)lo & 0xF0F0F0F0u;
+    av.y = (uint32_t)(lo >> 32) & 0xF0F0F0F0u;
+    av.z = (uint32_t)hi & 0xF0F0F0F0u;
+    av.w = (uint32_t)(hi >> 32) & 0xF0F0F0F0u;
+  } else if constexpr (FMT == FMT_Q4K) {
     av.x = (av.x >> sh) & 0x0F0F0F0Fu;
     av.y = (av.y >> sh) & 0x0F0F0F0Fu;
     av.z = (av.z >> sh) & 0x0F0F0F0Fu;
@@ -468,7 +481,7 @@ __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad,
       const int64_t e = ad.gsrc[g] + b;
       st.x[g] = ad.gon ? ld16(ad.xc + (size_t)e * 32 + ad.ghalf) : make_uint4(0u, 0u, 0u, 0u);
       st.dx[g] = ad.xd[e];
-      st.ns[g] = FMT != FMT_Q8 ? ad.xn[e] : 0;
+      st.ns[g] = FMT == FMT_Q4K ? ad.xn[e] : 0;
     }
     return;
   }
@@ -477,7 +490,7 @@ __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad,
   for (int g = 0; g < G; g++) {
     st.x[g] = ad.xon ? ld16(ad.xc + ((chunk0 + g) * 64 + lane) * 16) : make_uint4(0u, 0u, 0u, 0u);
     st.dx[g] = ad.xd[(chunk0 + g) * 16 + (lane & 15)];
-    st.ns[g] = FMT != FMT_Q8 ? ad.xn[(chunk0 + g) * 16 + (lane & 15)] : 0;
+    st.ns[g] = FMT == FMT_Q4K ? ad.xn[(chunk0 + g) * 16 + (lane & 15)] : 0;
   }
 }
 
@@ -532,9 +545,11 @@ __device__ __forceinline__ void mp_compute(float (&acc)[NT][PP][G][4], int pp, c
 #pragma unroll
     for (int g = 0; g < G; g++) {
       const v4i c = pair_dots<FMT>(st.a[t], st.x[g], st.ns[g], sh);
+      // Q4_0: sixteen times the dots against dx / 16 (the same products and sums)
+      const float dxg = FMT == FMT_Q4 ? st.dx[g] * 0.0625f : st.dx[g];
 #pragma unroll
       for (int v = 0; v < 4; v++) {
-        const float f = (float)c[v], m = mul_h_f(v < 2 ? wv.x : wv.y, v & 1, st.dx[g]);
+        const float f = (float)c[v], m = mul_h_f(v < 2 ? wv.x : wv.y, v & 1, dxg);
         float& r = acc[t][PP == 1 ? 0 : pp][g][v];
         if (SEQ) {
           // block b (this lane), then block b+1 (lane i ^ 8)
@@ -1412,14 +1427,13 @@ __global__ __launch_bounds__(256) void pair_blockdots_kernel(const uint8_t* __re
   const bool xon = (i < 8) == (q < 2);
   const uint4 x = xon ? ld16(reinterpret_cast<const uint8_t*>(prep.codes) + (chunk * 64 + lane) * 16)
                       : make_uint4(0u, 0u, 0u, 0u);
-  const int ns = FMT == FMT_Q4 ? prep.nsx[chunk * 16 + i] : 0;
-  const v4i c = pair_dots<FMT>(a, x, ns, (q & 1) * 4);
+  const v4i c = pair_dots<FMT>(a, x, 0, (q & 1) * 4);  // Q4_0: sixteen times the dots
   const int r = g * 8 + (i & 7), b = 2 * p + (i >> 3);
   if (r >= rows || b >= kb) return;
 #pragma unroll
   for (int v = 0; v < 4; v++) {
     const int64_t o = t * TILE + 4 * q + v;
-    if (o < n) isum[((int64_t)r * n + o) * kb + b] = c[v];
+    if (o < n) isum[((int64_t)r * n + o) * kb + b] = FMT == FMT_Q4 ? c[v] >> 4 : c[v];
   }
 }
 

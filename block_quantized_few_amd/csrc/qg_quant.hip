@@ -170,7 +170,8 @@ __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __re
           lo = (int)fminf(fmaxf(roundf(v[i] / dq), -8.0f), 7.0f) + 8;
           hi = (int)fminf(fmaxf(roundf(v[i + 16] / dq), -8.0f), 7.0f) + 8;
         }
-        packed[i >> 2] |= ((unsigned)(lo | (hi << 4))) << (8 * (i & 3));
+        // the image keeps c XOR 8 (the 4-bit two's complement of c - 8)
+        packed[i >> 2] |= ((unsigned)((lo ^ 8) | ((hi ^ 8) << 4))) << (8 * (i & 3));
       }
     }
   }
@@ -267,9 +268,7 @@ __global__ __launch_bounds__(256) void blockdots_kernel(const uint8_t* __restric
   } else if (FMT == FMT_Q4K) {
     s = dot_q4(ld16(p), xl, xh, 0);  // raw codes: the sub-min's share is not part of the integer dot
   } else {
-    int qsum = 0;
-    for (int i = 0; i < 32; i++) qsum += xq[i];
-    s = dot_q4(ld16(p), xl, xh, -8 * qsum);
+    s = dot_q4s16(ld16(p), xl, xh) >> 4;  // sixteen times the dot, exactly
   }
   isum[t] = s;
 }

@@ -90,7 +90,9 @@ def test_pack_layout_of_one_q4_block():
     blocks[5, 3, 2:18] = np.arange(16, dtype=np.uint8) * 17
     img = q.pack_image(q.Q4_0, blocks, n, k)
     cell = (0 * 16 + 3) * 256 + 16 * 5
-    assert list(img[cell:cell + 16]) == list(np.arange(16) * 17)
+    # the image keeps each code c as c XOR 8 (the 4-bit two's complement of c - 8), nibble order unchanged
+    assert list(img[cell:cell + 16]) == list((np.arange(16) * 17) ^ 0x88)
+    assert np.array_equal(q.unpack_image(q.Q4_0, img, n, k), blocks)
 
 
 @pytest.mark.parametrize("n,k", [(16, 32), (33, 104), (5, 8), (40, 200)])
