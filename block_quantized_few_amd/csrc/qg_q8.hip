@@ -472,23 +472,32 @@ __device__ __forceinline__ uint32_t pair_aoff(int i, int q) {
 template <int FMT, int NT, int G, bool GATHER>
 __device__ __forceinline__ void mp_load(MpStep<NT, G>& st, const MpAddr<NT>& ad, int lane, int b) {
   constexpr int CB = FMT == FMT_Q8 ? 512 : 256;
+  // (offsets from the tile's uniform base fit 32 bits: the scalar-base load
+  // form; Q4_K, whose decode holds more registers, measured slower with it)
 #pragma unroll
-  for (int t = 0; t < NT; t++) st.a[t] = ld16_stream(ad.code[t] + (size_t)b * CB + ad.aoff);
+  for (int t = 0; t < NT; t++)
+    st.a[t] = FMT == FMT_Q4K ? ld16_stream(ad.code[t] + (size_t)b * CB + ad.aoff)
+                             : ld16_stream(ad.code[t] + (uint32_t)(b * CB + (int)ad.aoff));
   st.b = b;
   if (GATHER) {
 #pragma unroll
     for (int g = 0; g < G; g++) {
       const int64_t e = ad.gsrc[g] + b;
-      st.x[g] = ad.gon ? ld16(ad.xc + (size_t)e * 32 + ad.ghalf) : make_uint4(0u, 0u, 0u, 0u);
+      if (ad.gon) st.x[g] = ld16(ad.xc + (size_t)e * 32 + ad.ghalf);  // the other lanes keep their zeros
       st.dx[g] = ad.xd[e];
       st.ns[g] = FMT == FMT_Q4K ? ad.xn[e] : 0;
     }
     return;
   }
-  const size_t chunk0 = (size_t)(b >> 1) * ad.groups;
+  const uint32_t chunk0 = (uint32_t)(b >> 1) * (uint32_t)ad.groups;
 #pragma unroll
   for (int g = 0; g < G; g++) {
-    st.x[g] = ad.xon ? ld16(ad.xc + ((chunk0 + g) * 64 + lane) * 16) : make_uint4(0u, 0u, 0u, 0u);
+    // the lanes whose 16 bytes of the chunk are the zeros keep the zeros set
+    // when the step registers were cleared (a masked load leaves them as they are)
+    if constexpr (FMT == FMT_Q4K)
+      st.x[g] = ad.xon ? ld16(ad.xc + (size_t)(((chunk0 + g) * 64 + lane) * 16)) : make_uint4(0u, 0u, 0u, 0u);
+    else if (ad.xon)
+      st.x[g] = ld16(ad.xc + (uint32_t)(((chunk0 + g) * 64 + lane) * 16));
     st.dx[g] = ad.xd[(chunk0 + g) * 16 + (lane & 15)];
     st.ns[g] = FMT == FMT_Q4K ? ad.xn[(chunk0 + g) * 16 + (lane & 15)] : 0;
   }
@@ -641,6 +650,10 @@ __device__ void mp_tile(const TileArgs& ta, int R, const MpLds& ml, int count = 
   constexpr int MP_LA = mp_la(NT, G);
   uint4 sv[NT];
   MpStep<NT, G> st[MP_LA];
+#pragma unroll
+  for (int jj = 0; jj < MP_LA; jj++)
+#pragma unroll
+    for (int g = 0; g < G; g++) st[jj].x[g] = make_uint4(0u, 0u, 0u, 0u);
   int64_t wrow0 = 0;  // first row of this group's tiles
   // Points the wave at the tile group starting at row0 and issues its scale
   // loads and its first MP_LA steps.
