@@ -314,7 +314,7 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
   __builtin_amdgcn_sched_barrier(0);
   int u0 = 0, nslot = ucx << pl.lgP;
   int next_round = (!full || stage) ? 0 : pl.BS;  // u at which activation rows are (re)staged
-  for (int u = 0; u < pl.BS; u += LA) {
+  auto restage = [&](int u) {
     if (u == next_round) {
       u0 = u;
       nslot = min(ucx, pl.BS - u) << pl.lgP;
@@ -324,6 +324,25 @@ __device__ bool rl_tile(const TileArgs& ta, uint8_t* lds, float* red, int parity
       else stage_rl<FMT, R>(lds, ta.prep, ta.s_src, ta.kbp, pl, u0, nslot);
       __syncthreads();
     }
+  };
+  int u = 0;
+  // Rounds whose every block has a next block to load: no branch around the
+  // loads, so the block registers need no copies at a join (a copy would
+  // wait for the load just issued and leave one block in flight).  (Q4_K,
+  // whose header decode holds more registers, spilled with the second loop
+  // at two rows: it keeps the one loop below.)
+  for (; FMT != FMT_Q4K && u + 2 * LA <= pl.BS; u += LA) {
+    restage(u);
+    const int slot = ((u - u0) << pl.lgP) + sbase;
+#pragma unroll
+    for (int j = 0; j < LA; j++) {
+      compute_block<FMT, R>(acc, w[j], lds, nslot, slot + (j << pl.lgP), (bpart + pl.H * (u + j)) & 7);
+      w[j] = load_block<FMT>(tcode, woff, tscale, soff, bpart + pl.H * (u + j + LA));
+    }
+  }
+  // the last fewer than 2 LA blocks
+  for (; u < pl.BS; u += LA) {
+    restage(u);
     const int slot = ((u - u0) << pl.lgP) + sbase;
 #pragma unroll
     for (int j = 0; j < LA; j++) {
