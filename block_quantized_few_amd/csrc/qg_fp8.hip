@@ -216,19 +216,32 @@ __global__ __launch_bounds__(S * WAVE) void gemv_fp8_kernel(const uint8_t* __res
       wsr[t] = wsc + (tt >> 3) * kg;  // 8 tiles per 128-row block
     }
     lc = g0 + (ng ? ((grp * NT >> 2) * F8_ROT) % ng : 0);
+    // (no bounds branch, which would make the step loop wait for every load in
+    // flight: a wave with fewer than LA groups loads groups of its range again,
+    // or the last group when it has none, and never uses the extra copies)
 #pragma unroll
-    for (int j = 0; j < LA; j++)
-      if (j < ng) {
-        f8_load<NT>(f[j], wt, wsr, xc, xs, lc);
-        lc = lc + 1 == g1 ? g0 : lc + 1;
-      }
+    for (int j = 0; j < LA; j++) {
+      f8_load<NT>(f[j], wt, wsr, xc, xs, lc < kg ? lc : kg - 1);
+      if (ng) lc = lc + 1 == g1 ? g0 : lc + 1;
+    }
   };
   if (blockIdx.x < tgroups) start(blockIdx.x);
   for (int64_t grp = blockIdx.x; grp < tgroups; grp += gridDim.x) {
     v4f acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
-    for (int64_t st = 0; st < ng; st += LA) {
+    int64_t st = 0;
+    // rounds whose every group has a next group to load: no branch around the loads
+    for (; st + 2 * LA <= ng; st += LA) {
+#pragma unroll
+      for (int j = 0; j < LA; j++) {
+        f8_compute<NT>(acc, f[j]);
+        f8_load<NT>(f[j], wt, wsr, xc, xs, lc);
+        lc = lc + 1 == g1 ? g0 : lc + 1;
+        __builtin_amdgcn_sched_barrier(0);  // each group's loads ahead of the next group's product
+      }
+    }
+    for (; st < ng; st += LA) {
 #pragma unroll
       for (int j = 0; j < LA; j++) {
         if (st + j < ng) {
