@@ -70,7 +70,7 @@ def parse():
     p.add_argument("--profile", default=None, metavar="WORKLOAD:ROWS",
                    help="time one workload (lm-head-q8, lm-head-q8-prepared, lm-head-q4, lm-head-q4-prepared, "
                         "lm-head-f16, lm-head-fp8, layer-1b, layer-3b, layer-1b-prepared, layer-3b-prepared, moe, "
-                        "read-probe) at ROWS rows for --steps calls after a short warm-up, print it, and exit: a "
+                        "moe-fp8, read-probe) at ROWS rows for --steps calls after a short warm-up, print it, and exit: a "
                         "short program for rocprofv3")
     p.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "WORKLOAD"), default=None,
                    help="reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) of a "
@@ -962,8 +962,8 @@ def profile_one(args, torch, q, synth, L, sh, stream, timer):
         else:
             fn = lambda i: L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh)
         wbytes = ls.wbytes
-    elif wl == "moe":
-        W = moe_weights(torch, q, synth)
+    elif wl in ("moe", "moe-fp8"):
+        W = moe_weights(torch, q, synth, fmt=q.FP8 if wl == "moe-fp8" else None)
         fn, _ = moe_call(torch, q, synth, L, sh, W, rows)
         wbytes = None
     elif wl == "read-probe":
