@@ -15,16 +15,18 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
                                                        int32_t* __restrict__ x_index, float* __restrict__ weight) {
   const int r = blockIdx.x, lane = threadIdx.x;
   const int slots = topk + (shared_expert >= 0 ? 1 : 0);
-  __shared__ int s_ex[32];
-  __shared__ float s_wt[32];
-  route_row(logits + (int64_t)r * E, E, topk, s_ex, s_wt);
+  int ex;
+  float wt;
+  route_row(logits + (int64_t)r * E, E, topk, ex, wt);  // lane k < topk: pick k
   if (lane < slots) {
     const bool sh = lane == topk;
-    expert[(int64_t)r * slots + lane] = sh ? shared_expert : s_ex[lane];
+    expert[(int64_t)r * slots + lane] = sh ? shared_expert : ex;
     x_index[(int64_t)r * slots + lane] = r;
-    weight[(int64_t)r * slots + lane] = sh ? 1.0f : s_wt[lane];
+    weight[(int64_t)r * slots + lane] = sh ? 1.0f : wt;
   }
 }
+
+static_assert(QG_MAX_ROWS <= 1024 / WAVE, "the plan launch routes a row a wave");
 
 // The plan of a routed MoE step, one workgroup (moe_plan_block): route every
 // row, order the assignments by expert into work items (the grouped GEMV's
@@ -46,8 +48,8 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const float* __restrict_
   }
   const int slots = topk + (shared_expert >= 0 ? 1 : 0), m = rows * slots;
   const PlanLds P = plan_carve(s_plan, m, E);
-  moe_plan_block(logits, rows, E, topk, shared_expert >= 0, P);
-  plan_store(P, m, expert, weight, x_index, header, sorted, items);
+  moe_plan_block<1024>(logits, rows, E, topk, shared_expert >= 0, P);
+  plan_store<1024>(P, m, expert, weight, x_index, header, sorted, items);
 }
 
 // SwiGLU of m assignments, h = silu(g) * u in fp32, quantized at once into

@@ -1224,6 +1224,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void gr
 
 // ------------------------------------------------- routed MoE gate/up ---
 
+static_assert(MOE_UP_PLAN_ROWS <= WAVES, "the gate/up launch routes a row a wave");
+
 // The gate/up launch of a routed MoE step: every workgroup computes the
 // step's plan from the router logits (moe_plan_block: the same plan in each),
 // workgroup 0 stores it for the later launches, and the workgroups take the
@@ -1238,8 +1240,8 @@ __global__ __launch_bounds__(WG) void moe_up_small_kernel(const uint8_t* __restr
   __shared__ int s_map[2 * QG_MAX_ROWS];
   const int m = up.rows * (up.topk + up.shared);
   const PlanLds P = plan_carve(lds + up.plan_off, m, up.E);
-  moe_plan_block(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
-  if (blockIdx.x == 0) plan_store(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
+  moe_plan_block<WG>(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
+  if (blockIdx.x == 0) plan_store<WG>(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
   const int units = P.misc[1] * tiles;  // every item is small (rows <= 2)
   for (int u = blockIdx.x; u < units; u += gridDim.x)
     grouped_small_unit<false, LA>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, P.sorted, P.items, P.xi, y,
@@ -1253,8 +1255,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mo
   __shared__ int s_map[2 * QG_MAX_ROWS];
   const int m = up.rows * (up.topk + up.shared);
   const PlanLds P = plan_carve(lds + up.plan_off, m, up.E);
-  moe_plan_block(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
-  if (blockIdx.x == 0) plan_store(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
+  moe_plan_block<WG>(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
+  if (blockIdx.x == 0) plan_store<WG>(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
   const int nsmall = P.misc[1];
   const int ub = (P.misc[0] - nsmall) * tiles_b, units = ub + nsmall * tiles_s;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {

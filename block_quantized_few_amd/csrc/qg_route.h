@@ -4,6 +4,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <climits>
+
 #include "qg_device.h"
 
 namespace qg {
@@ -52,41 +54,84 @@ __device__ __forceinline__ int wave_min_i(int v) {
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
-// (va, ia) ahead of (vb, ib): the larger logit, ties to the lower index.
-__device__ __forceinline__ void order2(float& va, int& ia, float& vb, int& ib) {
-  const bool swap = (vb > va) | ((vb == va) & (ib < ia));
-  const float tv = va;
-  const int ti = ia;
-  va = swap ? vb : va;
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Inclusive sum over the lanes: within each row of 16 by shifts of 1, 2, 4
+// and 8 lanes (lanes shifted in from before the row read 0), then each row
+// adds the totals of the rows before it.
+__device__ __forceinline__ unsigned wave_scan_u(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);
+  const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)v, 15);
+  const unsigned r1 = (unsigned)__builtin_amdgcn_readlane((int)v, 31);
+  const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = (threadIdx.x & (WAVE - 1)) >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// A logit as a signed integer of the same order (-0 taken as +0, so equal
+// logits have equal keys; a NaN never gets here), and back.
+__device__ __forceinline__ int logit_key(float v) {
+  const int b = __float_as_int(v + 0.0f);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float key_logit(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
+
+// (ka, ia) ahead of (kb, ib): the larger key, ties to the lower index.
+__device__ __forceinline__ void order2(int& ka, int& ia, int& kb, int& ib) {
+  const bool swap = (kb > ka) | ((kb == ka) & (ib < ia));
+  const int tk = ka, ti = ia;
+  ka = swap ? kb : ka;
   ia = swap ? ib : ia;
-  vb = swap ? tv : vb;
+  kb = swap ? tk : kb;
   ib = swap ? ti : ib;
 }
 
 // Routing of one row by one wave: softmax over the E logits in fp32 (max
 // subtracted; each lane sums its experts in index order, then the fixed
 // wave_sum tree), and the topk experts by logit, ties to the lower index, in
-// descending order, written to ex[] / wt[] (lane k writes pick k).  NPER:
-// logits per lane (E <= 64 * NPER).
+// descending order: lane k < topk gets pick k.  NPER: logits per lane
+// (E <= 64 * NPER); route_load issues the row's loads, route_pick the rest.
 //
-// Selection: each lane orders its own entries once (expert lane + 64 i; past
-// E, or a NaN logit, never picked: -inf with an index above every expert's),
-// so its best remaining entry is always its first.  A pick is the wave's
-// largest first entry; the lanes holding that value are found by ballot, and
-// of several (equal logits) the lowest expert index wins.  The winner's lane
-// then moves its next entry up.
+// Selection on integer keys of the logits (logit_key): each lane orders its
+// own entries once (expert lane + 64 i; a NaN logit ranks as -inf with its own
+// index, so a row of NaN picks experts 0, 1, ...; past E: -inf with an index
+// above every expert's, never picked as topk <= E), so its best remaining
+// entry is always its first.  A pick is the wave's largest first key; the
+// lanes holding it are found by ballot, and of several (equal logits) the
+// lowest expert index wins.  The winner's lane then moves its next entry up.
 template <int NPER>
-__device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
+__device__ __forceinline__ void route_load(const float* __restrict__ lrow, int E, float (&l)[NPER]) {
   const int lane = threadIdx.x & (WAVE - 1);
-  float l[NPER];
-  float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NPER; i++) {
     const int e = lane + WAVE * i;
     l[i] = e < E ? lrow[e] : -INFINITY;
-    mx = fmaxf(mx, l[i]);
   }
-  mx = wave_max(mx);
+}
+
+template <int NPER>
+__device__ __forceinline__ void route_pick(const float (&l)[NPER], int E, int topk, int& ex, float& wt) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int sk[NPER], si[NPER];
+  int kmax = INT_MIN;
+#pragma unroll
+  for (int i = 0; i < NPER; i++) {
+    const int e = lane + WAVE * i;
+    sk[i] = logit_key((e < E) & (l[i] == l[i]) ? l[i] : -INFINITY);
+    si[i] = e < E ? e : 0x7fffffff;
+    kmax = max(kmax, sk[i]);
+  }
+  const float mx = key_logit(wave_max_i(kmax));  // the largest logit (NaN aside)
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < NPER; i++) {
@@ -94,46 +139,41 @@ __device__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int
     sum += lane + WAVE * i < E ? t : 0.0f;
   }
   sum = wave_sum(sum);
-  float sv[NPER];
-  int si[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; i++) {
-    const int e = lane + WAVE * i;
-    const bool ok = (e < E) & (l[i] == l[i]);
-    sv[i] = ok ? l[i] : -INFINITY;
-    si[i] = ok ? e : 0x7fffffff;
-  }
 #pragma unroll
   for (int i = 1; i < NPER; i++)
 #pragma unroll
-    for (int j = i; j > 0; j--) order2(sv[j - 1], si[j - 1], sv[j], si[j]);
-  float mv = 0.0f;  // this lane's pick (lane k: the k-th)
-  int mi = 0;
+    for (int j = i; j > 0; j--) order2(sk[j - 1], si[j - 1], sk[j], si[j]);
+  int mk = 0, mi = 0;  // this lane's pick (lane k: the k-th)
   for (int k = 0; k < topk; k++) {
-    const float bv = wave_max(sv[0]);
-    const unsigned long long at = __ballot(sv[0] == bv);
+    const int bk = wave_max_i(sk[0]);
+    const unsigned long long at = __ballot(sk[0] == bk);
     int bi;
     if (__popcll(at) == 1) bi = __builtin_amdgcn_readlane(si[0], (int)__builtin_ctzll(at));
-    else bi = wave_min_i(sv[0] == bv ? si[0] : 0x7fffffff);
-    if (si[0] == bi) {  // the winner's lane: its next entry first
+    else bi = wave_min_i(sk[0] == bk ? si[0] : 0x7fffffff);
+    const bool win = si[0] == bi;  // the winner's lane: its next entry first
 #pragma unroll
-      for (int i = 0; i + 1 < NPER; i++) {
-        sv[i] = sv[i + 1];
-        si[i] = si[i + 1];
-      }
-      sv[NPER - 1] = -INFINITY;
-      si[NPER - 1] = 0x7fffffff;
+    for (int i = 0; i + 1 < NPER; i++) {
+      sk[i] = win ? sk[i + 1] : sk[i];
+      si[i] = win ? si[i + 1] : si[i];
     }
-    mv = lane == k ? bv : mv;  // lane k keeps pick k
+    sk[NPER - 1] = win ? INT_MIN : sk[NPER - 1];
+    si[NPER - 1] = win ? 0x7fffffff : si[NPER - 1];
+    mk = lane == k ? bk : mk;
     mi = lane == k ? bi : mi;
   }
-  if (lane < topk) {
-    ex[lane] = mi;
-    wt[lane] = expf(mv - mx) / sum;
-  }
+  ex = mi;
+  wt = expf(key_logit(mk) - mx) / sum;
 }
 
-__device__ __forceinline__ void route_row(const float* __restrict__ lrow, int E, int topk, int* ex, float* wt) {
+template <int NPER>
+__device__ __forceinline__ void route_row_n(const float* __restrict__ lrow, int E, int topk, int& ex, float& wt) {
+  float l[NPER];
+  route_load<NPER>(lrow, E, l);
+  route_pick<NPER>(l, E, topk, ex, wt);
+}
+
+// lane k < topk: pick k of row lrow
+__device__ __forceinline__ void route_row(const float* __restrict__ lrow, int E, int topk, int& ex, float& wt) {
   if (E <= 4 * WAVE) route_row_n<4>(lrow, E, topk, ex, wt);
   else if (E <= 8 * WAVE) route_row_n<8>(lrow, E, topk, ex, wt);
   else route_row_n<ROUTE_PER_LANE>(lrow, E, topk, ex, wt);
@@ -154,7 +194,6 @@ struct PlanLds {
   float* w;        // [m] its weight
   unsigned* mask;  // [E + 1] bit r: row r picked the expert
   unsigned* off;   // [E + 1] before expert e: assignments | touched experts << 10 | small items << 21
-  unsigned* wsum;  // [16] per-wave sums of the scan
   int* items;      // [3 m] (expert, first sorted position, rows)
   int* sorted;     // [m]
   int* xi;         // [m] activation row of assignment j
@@ -162,9 +201,9 @@ struct PlanLds {
 };
 
 // Bytes of a plan's LDS (16-byte multiple): e, w, items (3), sorted, xi: 7 m
-// words; mask, off: 2 (E + 1); wsum 16; misc 2 (the carve below, in order).
+// words; mask, off: 2 (E + 1); misc 2 (the carve below, in order).
 __host__ __device__ constexpr size_t plan_lds_bytes(int m, int E) {
-  return ((size_t)(7 * m + 2 * (E + 1) + 16 + 2) * 4 + 15) / 16 * 16;
+  return ((size_t)(7 * m + 2 * (E + 1) + 2) * 4 + 15) / 16 * 16;
 }
 
 __device__ inline PlanLds plan_carve(uint8_t* p, int m, int E) {
@@ -174,63 +213,74 @@ __device__ inline PlanLds plan_carve(uint8_t* p, int m, int E) {
   P.w = reinterpret_cast<float*>(b + m);
   P.mask = reinterpret_cast<unsigned*>(b + 2 * m);
   P.off = P.mask + (E + 1);
-  P.wsum = P.off + (E + 1);
-  P.items = reinterpret_cast<int*>(P.wsum + 16);
+  P.items = reinterpret_cast<int*>(P.off + (E + 1));
   P.sorted = P.items + 3 * m;
   P.xi = P.sorted + m;
   P.misc = P.xi + m;
   return P;
 }
 
-// The plan into P (every thread of the workgroup calls it; at most 16 waves;
-// rows <= 16, rows * slots <= QG_MOE_MAX_M, E <= ROUTE_MAX_E).  Ends with a
-// barrier.
-__device__ inline void moe_plan_block(const float* __restrict__ logits, int rows, int E, int topk, bool shared,
-                                      const PlanLds& P) {
-  const int tid = threadIdx.x, nt = blockDim.x, wave = tid / WAVE, lane = tid % WAVE;
+// Packed counts of an expert's mask: assignments | touched << 10 | small item << 21.
+__device__ __forceinline__ unsigned plan_val(unsigned mk) {
+  const unsigned c = __popc(mk);
+  return c | (mk ? 1u << 10 : 0u) | (mk && c <= (unsigned)GROUPED_SMALL_ROWS ? 1u << 21 : 0u);
+}
+
+// The plan into P (every thread of the NTH-thread workgroup calls it; a row
+// a wave: rows <= NTH / 64 <= 16; rows * slots <= QG_MOE_MAX_M,
+// E <= ROUTE_MAX_E).  Ends with a barrier.
+template <int NTH, int NPER>
+__device__ void moe_plan_n(const float* __restrict__ logits, int rows, int E, int topk, bool shared,
+                           const PlanLds& P) {
+  const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
   const int slots = topk + (shared ? 1 : 0), m = rows * slots, ne = E + 1;
-  for (int r = wave; r < rows; r += nt / WAVE) {
-    route_row(logits + (int64_t)r * E, E, topk, P.e + r * slots, P.w + r * slots);
-    if (lane == 0 && shared) {
-      P.e[r * slots + topk] = E;
-      P.w[r * slots + topk] = 1.0f;
+  const bool routes = wave < rows;  // wave r routes row r
+  float l[NPER];
+  if (routes) route_load<NPER>(logits + (int64_t)wave * E, E, l);
+  for (int e = tid; e < ne; e += NTH) P.mask[e] = 0u;
+  __syncthreads();
+  if (routes) {
+    int ex;
+    float wt;
+    route_pick<NPER>(l, E, topk, ex, wt);
+    if (lane < slots) {  // lane topk: the shared expert
+      const bool sh = lane == topk;
+      const int e = sh ? E : ex;
+      P.e[wave * slots + lane] = e;
+      P.w[wave * slots + lane] = sh ? 1.0f : wt;
+      atomicOr(&P.mask[e], 1u << wave);
     }
   }
-  for (int e = tid; e < ne; e += nt) P.mask[e] = 0u;
   __syncthreads();
-  for (int j = tid; j < m; j += nt) atomicOr(&P.mask[P.e[j]], 1u << (j / slots));
-  __syncthreads();
-  // exclusive scan over experts of their (assignments, touched, small item)
-  // counts: thread t takes experts t*c .. t*c + c - 1
-  auto val = [](unsigned mk) {
-    const unsigned c = __popc(mk);
-    return c | (mk ? 1u << 10 : 0u) | (mk && c <= (unsigned)GROUPED_SMALL_ROWS ? 1u << 21 : 0u);
-  };
-  const int c = (ne + nt - 1) / nt, e0 = tid * c;
-  unsigned loc = 0;
-  for (int i = 0; i < c; i++)
-    if (e0 + i < ne) loc += val(P.mask[e0 + i]);
-  unsigned inc = loc;  // inclusive within the wave
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const unsigned v = __shfl_up(inc, o);
-    inc += lane >= o ? v : 0u;
-  }
-  if (lane == WAVE - 1) P.wsum[wave] = inc;
-  __syncthreads();
-  unsigned run = 0, total = 0;
-  for (int w = 0; w < nt / WAVE; w++) {
-    run += w < wave ? P.wsum[w] : 0u;
-    total += P.wsum[w];
-  }
-  run += inc - loc;
-  for (int i = 0; i < c; i++)
-    if (e0 + i < ne) {
-      P.off[e0 + i] = run;
-      run += val(P.mask[e0 + i]);
+  // exclusive scan over experts of their packed counts, by one wave: lane t
+  // takes experts t*c .. t*c + c - 1 (c <= NPER + 1), its masks read at once
+  if (wave == 0) {
+    constexpr int C = NPER + 1;
+    const int c = (ne + WAVE - 1) / WAVE, e0 = lane * c;
+    unsigned v[C];
+    unsigned loc = 0;
+#pragma unroll
+    for (int i = 0; i < C; i++) {
+      const unsigned mk = P.mask[min(e0 + i, ne - 1)];
+      v[i] = (i < c) & (e0 + i < ne) ? plan_val(mk) : 0u;
+      loc += v[i];
     }
+    const unsigned inc = wave_scan_u(loc);
+    unsigned run = inc - loc;
+#pragma unroll
+    for (int i = 0; i < C; i++)
+      if ((i < c) & (e0 + i < ne)) {
+        P.off[e0 + i] = run;
+        run += v[i];
+      }
+    if (lane == WAVE - 1) {
+      P.misc[0] = (int)((inc >> 10) & 2047u);
+      P.misc[1] = (int)(inc >> 21);
+    }
+  }
   __syncthreads();
-  const int nitems = (int)((total >> 10) & 2047u), nsmall = (int)(total >> 21);
-  for (int j = tid; j < m; j += nt) {
+  const int nsmall = P.misc[1];
+  for (int j = tid; j < m; j += NTH) {
     const int e = P.e[j], r = j / slots;
     const unsigned mk = P.mask[e], o = P.off[e], below = mk & ((1u << r) - 1u);
     const int start = (int)(o & 1023u);
@@ -243,19 +293,24 @@ __device__ inline void moe_plan_block(const float* __restrict__ logits, int rows
     P.items[3 * dst + 1] = start;
     P.items[3 * dst + 2] = cnt;
   }
-  if (tid == 0) {
-    P.misc[0] = nitems;
-    P.misc[1] = nsmall;
-  }
   __syncthreads();
+}
+
+template <int NTH>
+__device__ inline void moe_plan_block(const float* __restrict__ logits, int rows, int E, int topk, bool shared,
+                                      const PlanLds& P) {
+  if (E <= 4 * WAVE) moe_plan_n<NTH, 4>(logits, rows, E, topk, shared, P);
+  else if (E <= 8 * WAVE) moe_plan_n<NTH, 8>(logits, rows, E, topk, shared, P);
+  else moe_plan_n<NTH, ROUTE_PER_LANE>(logits, rows, E, topk, shared, P);
 }
 
 // The plan's global copies: the step's expert / weight / x_index outputs
 // (expert E is the shared one), and the grouped GEMV's header, sorted, items.
+template <int NTH>
 __device__ inline void plan_store(const PlanLds& P, int m, int32_t* __restrict__ expert, float* __restrict__ weight,
                                   int32_t* __restrict__ x_index, int* __restrict__ header, int* __restrict__ sorted,
                                   int* __restrict__ items) {
-  const int tid = threadIdx.x, nt = blockDim.x, ni = P.misc[0];
+  const int tid = threadIdx.x, nt = NTH, ni = P.misc[0];
   for (int j = tid; j < m; j += nt) {
     expert[j] = P.e[j];
     weight[j] = P.w[j];

@@ -130,6 +130,24 @@ def test_fused_moe_step_other_topk(moe, rows, topk):
     assert torch.equal(yf, y)
 
 
+@pytest.mark.parametrize("rows", [2, 8, 16])
+def test_fused_moe_step_with_a_nan_row(moe, rows):
+    """A NaN input row routes to experts 0..7 (its logits are NaN) and the step runs through; the other rows
+    keep the bits they have with that row finite (each assignment's output is the one-row call's, whatever
+    the plan around it)."""
+    log(f"fused moe rows={rows} with a NaN row")
+    x = torch.from_numpy(gauss((rows, HIDDEN), 1.0, WL, 64 + rows).numpy()).cuda()
+    yf, _, _ = q.moe_step_fused(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN)
+    xn = x.clone()
+    xn[rows // 2] = float("nan")
+    yn, (expert_n, _), _ = q.moe_step_fused(xn, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN)
+    ex = expert_n.cpu().numpy().reshape(rows, TOPK + 1)
+    assert np.array_equal(ex[rows // 2], np.array(list(range(TOPK)) + [E]))
+    keep = [r for r in range(rows) if r != rows // 2]
+    assert torch.equal(yn[keep], yf[keep])
+    assert torch.isnan(yn[rows // 2]).all()
+
+
 # ------------------------------------------------------------- FP8 lane ---
 # The routed step with block-FP8 experts and 1 x 128 FP8 activation groups (qg_moe_step_fp8), on a smaller
 # expert set: 64 experts of 256-wide FFNs over hidden 1024, top-8 and a shared expert.

@@ -37,6 +37,36 @@ def test_routing_matches_oracle(E):
             assert np.allclose(wt.cpu().numpy().reshape(rows, topk), p_o, rtol=1e-5, atol=1e-9)
 
 
+def test_routing_of_nan_logits():
+    """A NaN logit ranks as -inf with its own index: a row of NaN picks experts 0..topk-1 (what the oracle's
+    strict comparison picks for it too), a row with some NaN picks the largest finite logits, NaN and -inf
+    tie by index, and every expert id is in range; the weights of a row with a NaN are NaN (its softmax sum
+    is)."""
+    E, topk = 256, 8
+    rng = np.random.default_rng(5)
+    lg = rng.permutation(E).astype(np.float32)[None, :].repeat(4, 0)  # distinct finite values
+    lg[0, :] = np.nan
+    nan_at = rng.choice(E, size=100, replace=False)
+    lg[1, nan_at] = np.nan
+    lg[2, :] = -np.inf
+    lg[2, ::3] = np.nan  # only -inf and NaN: ties by index
+    lg[3, :] = np.nan
+    lg[3, 200:205] = np.arange(5, dtype=np.float32)  # five finite, then the NaN / -inf tail by index
+    log("routing of NaN logits")
+    ex, _, wt = q.moe_route(torch.from_numpy(lg).cuda(), topk)
+    ex = ex.cpu().numpy().reshape(4, topk)
+    wt = wt.cpu().numpy().reshape(4, topk)
+    assert np.array_equal(ex[0], np.arange(topk))
+    ex_o, _ = O.route_topk(lg[:1], topk)
+    assert np.array_equal(ex[0], ex_o[0])
+    fin = np.where(np.isnan(lg[1]), -np.inf, lg[1])
+    assert np.array_equal(ex[1], np.argsort(-fin, kind="stable")[:topk])
+    assert np.array_equal(ex[2], np.arange(topk))
+    assert np.array_equal(ex[3], np.array([204, 203, 202, 201, 200, 0, 1, 2]))
+    assert np.all((ex >= 0) & (ex < E))
+    assert np.all(np.isnan(wt[[0, 1, 3]]))
+
+
 @pytest.mark.parametrize("k", [512, 2048, 3072, 4096, 8192])
 def test_grouped_items_on_every_tile_shape(k):
     """Work items of 16, 9, 5, 3 and 1-2 rows (the pair tile with two row groups, with one, and the lean
