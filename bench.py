@@ -660,7 +660,7 @@ def secondary(torch, q, synth, L, sh, stream, timer, rc, note):
     del imgs
     note("1024x1024 done")
 
-    # routed MoE step at 1/8/9/16 rows (three launches at 1-2 rows, five up to 8 rows, six beyond)
+    # routed MoE step at 1/8/9/16 rows (three launches at 1-2 rows, four up to 8 rows, six beyond)
     W = moe_weights(torch, q, synth)
     for rows in (1, 8, 9, 16):
         one, expert = moe_call(torch, q, synth, L, sh, W, rows)
@@ -669,7 +669,7 @@ def secondary(torch, q, synth, L, sh, stream, timer, rc, note):
         wb = 2 * MOE_E * MOE_HIDDEN + u * (W["gu_b"] + W["dn_b"])
         med = statistics.median(reps)
         out.append({"workload": "routed moe step (256 experts top-8 + shared, hidden 2048, ffn 512)",
-                    "lane": "q8_0 + f16 router", "rows": rows, "launches": 3 if rows <= 2 else 5 if rows <= 8 else 6,
+                    "lane": "q8_0 + f16 router", "rows": rows, "launches": 3 if rows <= 2 else 4 if rows <= 8 else 6,
                     "unique_experts": round(u, 2), "weight_bytes": int(wb), **summarize(reps),
                     "weight_gbps": round(wb / (med * 1e-3) / 1e9, 1),
                     "pct_hbm_weight": round(100 * wb / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)})

@@ -451,6 +451,13 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
   int* header = (int*)(w + M.header);
   int* sorted = (int*)(w + M.sorted);
   int* items = (int*)(w + M.items);
+  // 3-8 rows: the items cut to at most two rows as well (the gate/up launch's
+  // plan stores them), for a down launch that takes the SwiGLU in its staging;
+  // their header beside the plan's.  (With more rows the experts that many
+  // rows meet would be read too many times over.)
+  const bool split = rows > 2 && rows <= MOE_UP_PLAN_ROWS && grouped_glu_fits(ffn);
+  int* dheader = split ? header + 16 : nullptr;
+  int* ditems = split ? (int*)(w + M.ditems) : nullptr;
   float* gu = (float*)(w + M.gu);
   float* o = (float*)(w + M.o);
   const int n_images = n_experts + shared;
@@ -474,6 +481,8 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
     up.header = header;
     up.sorted = sorted;
     up.items = items;
+    up.dheader = dheader;
+    up.ditems = ditems;
     up.plan_off = 0;
     if (int st = launch_moe_up(gu_images, 2 * ffn, hidden, w + M.xprep, up, gu, s)) return st;
   } else {
@@ -484,19 +493,27 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
                                         xi, m, rows, gu, s))
       return st;
   }
-  // at most two rows: the down launch takes the SwiGLU of the gate/up rows in
-  // its staging (one launch fewer), and where the shape allows it the combine
-  // too; otherwise a launch quantizes the SwiGLU first
+  // the down launch takes the SwiGLU of the gate/up rows in its staging (one
+  // launch fewer): at most two rows on the plan's items, and where the shape
+  // allows it the combine too; 3-8 rows on the items cut to two rows (an
+  // expert of c rows read ceil(c / 2) times); otherwise a launch quantizes
+  // the SwiGLU first
   const bool glu = rows <= 2 && grouped_glu_fits(ffn);
   if (glu && moe_down_combine_fits(rows, slots, hidden, ffn)) {
     if (int st = launch_moe_down_combine(down_images, n_images, hidden, ffn, gu, ex, wt, rows, slots, y, s)) return st;
     return ok();
   }
-  if (!glu)
-    if (int st = launch_swiglu_q8(gu, m, ffn, w + M.hprep, s)) return st;
-  if (int st = launch_grouped_planned(down_images, n_images, hidden, ffn, w + M.hprep, m, header, sorted, items,
-                                      nullptr, m, rows, o, s, glu ? gu : nullptr))
-    return st;
+  if (split) {
+    if (int st = launch_grouped_planned(down_images, n_images, hidden, ffn, w + M.hprep, m, dheader, sorted, ditems,
+                                        nullptr, m, 2, o, s, gu))
+      return st;
+  } else {
+    if (!glu)
+      if (int st = launch_swiglu_q8(gu, m, ffn, w + M.hprep, s)) return st;
+    if (int st = launch_grouped_planned(down_images, n_images, hidden, ffn, w + M.hprep, m, header, sorted, items,
+                                        nullptr, m, rows, o, s, glu ? gu : nullptr))
+      return st;
+  }
   if (int st = launch_moe_combine(o, wt, rows, slots, hidden, y, s)) return st;
   return ok();
 }

@@ -93,6 +93,8 @@ struct MoeUp {
   int* header;
   int* sorted;
   int* items;
+  int* dheader;  // the plan's items cut to at most two rows, or null (plan_store)
+  int* ditems;
   int plan_off;  // set by the launcher
 };
 // Rows up to which the gate/up launch of a routed MoE step plans for itself

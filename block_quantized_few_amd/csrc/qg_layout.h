@@ -173,7 +173,7 @@ QG_HD GroupedLayout grouped_fp8_layout(int64_t x_rows, int64_t k, int64_t m) {
 // m = rows * slots assignments, slots = topk (+1 with a shared expert).
 constexpr int QG_MOE_MAX_M = 16 * 33;
 struct MoeLayout {
-  size_t header, expert, weight, x_index, sorted, items, logits, xprep, gu, hprep, o, total;
+  size_t header, expert, weight, x_index, sorted, items, ditems, logits, xprep, gu, hprep, o, total;
 };
 // fp8: the input rows and h in FP8 groups (fp8_ws_bytes) instead of q8 rows.
 QG_HD MoeLayout moe_layout(int64_t rows, int64_t n_experts, int64_t hidden, int64_t ffn, int64_t slots,
@@ -186,7 +186,8 @@ QG_HD MoeLayout moe_layout(int64_t rows, int64_t n_experts, int64_t hidden, int6
   M.x_index = M.weight + align256((size_t)m * 4);
   M.sorted = M.x_index + align256((size_t)m * 4);
   M.items = M.sorted + align256((size_t)m * 4);
-  M.logits = M.items + align256((size_t)m * 12);
+  M.ditems = M.items + align256((size_t)m * 12);
+  M.logits = M.ditems + align256((size_t)m * 12);
   M.xprep = M.logits + align256((size_t)rows * n_experts * 4);
   M.gu = M.xprep + (fp8 ? fp8_ws_bytes(rows, hidden) : prep_layout_rows(rows, hidden).total);
   M.hprep = M.gu + align256((size_t)m * 2 * ffn * 4);

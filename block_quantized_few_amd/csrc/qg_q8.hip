@@ -1241,7 +1241,8 @@ __global__ __launch_bounds__(WG) void moe_up_small_kernel(const uint8_t* __restr
   const int m = up.rows * (up.topk + up.shared);
   const PlanLds P = plan_carve(lds + up.plan_off, m, up.E);
   moe_plan_block<WG>(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
-  if (blockIdx.x == 0) plan_store<WG>(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
+  if (blockIdx.x == 0) plan_store<WG>(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items, up.dheader,
+                                     up.ditems);
   const int units = P.misc[1] * tiles;  // every item is small (rows <= 2)
   for (int u = blockIdx.x; u < units; u += gridDim.x)
     grouped_small_unit<false, LA>(images, expert_bytes, scale_off, n, k, kbp, pl, prep, P.sorted, P.items, P.xi, y,
@@ -1256,7 +1257,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mo
   const int m = up.rows * (up.topk + up.shared);
   const PlanLds P = plan_carve(lds + up.plan_off, m, up.E);
   moe_plan_block<WG>(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
-  if (blockIdx.x == 0) plan_store<WG>(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
+  if (blockIdx.x == 0) plan_store<WG>(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items, up.dheader,
+                                     up.ditems);
   const int nsmall = P.misc[1];
   const int ub = (P.misc[0] - nsmall) * tiles_b, units = ub + nsmall * tiles_s;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {

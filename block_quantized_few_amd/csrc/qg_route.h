@@ -306,10 +306,15 @@ __device__ inline void moe_plan_block(const float* __restrict__ logits, int rows
 
 // The plan's global copies: the step's expert / weight / x_index outputs
 // (expert E is the shared one), and the grouped GEMV's header, sorted, items.
+// With ditems: the items again, each of c > GROUPED_SMALL_ROWS rows cut into
+// ceil(c / 2) items of two rows (the last of c - 2 (ceil(c / 2) - 1)), in item
+// order, and their header (count, 0, count: every one small) at dheader, for
+// a down launch that quantizes the SwiGLU in its staging.
 template <int NTH>
 __device__ inline void plan_store(const PlanLds& P, int m, int32_t* __restrict__ expert, float* __restrict__ weight,
                                   int32_t* __restrict__ x_index, int* __restrict__ header, int* __restrict__ sorted,
-                                  int* __restrict__ items) {
+                                  int* __restrict__ items, int* __restrict__ dheader = nullptr,
+                                  int* __restrict__ ditems = nullptr) {
   const int tid = threadIdx.x, nt = NTH, ni = P.misc[0];
   for (int j = tid; j < m; j += nt) {
     expert[j] = P.e[j];
@@ -322,6 +327,31 @@ __device__ inline void plan_store(const PlanLds& P, int m, int32_t* __restrict__
     header[0] = ni;
     header[1] = 0;
     header[2] = P.misc[1];
+  }
+  if (ditems && tid < WAVE) {  // one wave, 64 items a pass, places by a scan of the pieces
+    const int lane = tid;
+    int base = 0;
+    for (int c0 = 0; c0 < ni; c0 += WAVE) {
+      const int i = c0 + lane;
+      const int cnt = i < ni ? P.items[3 * i + 2] : 0;
+      const unsigned pieces = (unsigned)(cnt + 1) >> 1;
+      const unsigned inc = wave_scan_u(pieces);
+      if (i < ni) {
+        const int e = P.items[3 * i], start = P.items[3 * i + 1];
+        int* d = ditems + 3 * (base + (int)(inc - pieces));
+        for (int p = 0; p < (int)pieces; p++) {
+          d[3 * p] = e;
+          d[3 * p + 1] = start + 2 * p;
+          d[3 * p + 2] = min(2, cnt - 2 * p);
+        }
+      }
+      base += __builtin_amdgcn_readlane((int)inc, WAVE - 1);
+    }
+    if (lane == 0) {
+      dheader[0] = base;
+      dheader[1] = 0;
+      dheader[2] = base;
+    }
   }
 }
 

@@ -411,10 +411,12 @@ int qg_moe_combine(const float* o, const float* weight, int rows, int slots, int
  * logits (f16 lane: router_image is the F16 image of the n_experts x hidden
  * router), routing as qg_moe_route, grouped gate/up GEMV, SwiGLU quantized
  * for the down projection, grouped down GEMV, weighted combine.  Six
- * launches at 9-16 rows; five at 3-8 rows, where the gate/up launch routes
- * the rows itself; three at 1-2 rows, where the down launch also quantizes
- * the SwiGLU of the gate/up rows in its staging and, when the assignments fit
- * one workgroup, combines them (four when they do not).  gu_images holds
+ * launches at 9-16 rows; four at 3-8 rows, where the gate/up launch routes
+ * the rows itself and the down launch quantizes the SwiGLU of the gate/up
+ * rows in its staging (on the work items cut to two rows, so an expert that
+ * c rows meet is read ceil(c/2) times); three at 1-2 rows, where the down
+ * launch does the same and, when the assignments fit one workgroup, combines
+ * them (four when they do not).  gu_images holds
  * n_experts + shared Q8_0 images of [2*ffn][hidden] (gate rows, then up rows)
  * back to back; down_images the same experts' [hidden][ffn]; with shared = 1
  * image n_experts is an ungated shared expert joining every row with weight

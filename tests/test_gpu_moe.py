@@ -90,11 +90,12 @@ def test_moe_step_matches_oracle(moe, rows):
     assert near_ties <= 1, near_ties
 
 
-@pytest.mark.parametrize("rows", [1, 2, 8, 9, 16])
+@pytest.mark.parametrize("rows", [1, 2, 3, 8, 9, 16])
 def test_fused_moe_step_equals_composition(moe, rows):
-    """qg_moe_step (one plan for both grouped GEMVs; SwiGLU quantized in place, at 1-2 rows inside the down
-    launch's staging) gives the bits of the composition of the separate calls, call after call through the
-    same workspace."""
+    """qg_moe_step (one plan for both grouped GEMVs; SwiGLU quantized in place, at 1-8 rows inside the down
+    launch's staging, at 3-8 rows on the work items cut to two rows: at 3 rows the shared expert's item
+    becomes a piece of two rows and one of one) gives the bits of the composition of the separate calls,
+    call after call through the same workspace."""
     log(f"fused moe rows={rows}")
     x = torch.from_numpy(gauss((rows, HIDDEN), 1.0, WL, 32 + rows).numpy()).cuda()
     y, (expert, _, weight), logits = q.moe_step(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN, shared_expert=E)
