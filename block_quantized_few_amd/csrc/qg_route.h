@@ -237,6 +237,35 @@ __device__ void moe_plan_n(const float* __restrict__ logits, int rows, int E, in
   const bool routes = wave < rows;  // wave r routes row r
   float l[NPER];
   if (routes) route_load<NPER>(logits + (int64_t)wave * E, E, l);
+  if (rows == 1) {
+    // one row: its slots' experts are distinct, so every item is one
+    // assignment (small), at its expert's rank among the slots, found by
+    // wave 0 from its own lanes
+    if (wave == 0) {
+      int ex;
+      float wt;
+      route_pick<NPER>(l, E, topk, ex, wt);
+      const bool sh = lane == topk;
+      const int e = lane < topk ? ex : sh ? E : INT_MAX;
+      int rank = 0;
+      for (int i = 0; i < slots; i++) rank += __builtin_amdgcn_readlane(e, i) < e;
+      if (lane < slots) {
+        P.e[lane] = e;
+        P.w[lane] = sh ? 1.0f : wt;
+        P.xi[lane] = 0;
+        P.sorted[rank] = lane;
+        P.items[3 * rank] = e;
+        P.items[3 * rank + 1] = rank;
+        P.items[3 * rank + 2] = 1;
+      }
+      if (lane == 0) {
+        P.misc[0] = slots;
+        P.misc[1] = slots;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   for (int e = tid; e < ne; e += NTH) P.mask[e] = 0u;
   __syncthreads();
   if (routes) {
