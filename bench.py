@@ -314,14 +314,12 @@ class LayerSet:
                 items.append(q._ProjRows(self.imgs[c][i].data_ptr(), n, k, self.xs[j].data_ptr(),
                                          self.wss[j].data_ptr(), self.wss[j].numel(), self.ys[i].data_ptr()))
             self.projs.append(ctypes_arr(q._ProjRows, items))
-        self.prepared = None
-        if rows > q.FUSED_ROWS:
-            # the GEMV launch alone, on rows quantized once beforehand
-            self.prepared = [ctypes_arr(q._Proj, [q._Proj(self.imgs[c][i].data_ptr(), n, k,
-                                                          self.wss[LAYER_SRC.get(nm, 0)].data_ptr(),
-                                                          self.wss[LAYER_SRC.get(nm, 0)].numel(), self.ys[i].data_ptr())
-                                                  for i, (nm, n, k) in enumerate(self.layer)])
-                             for c in range(self.copies)]
+        # the GEMV launch alone, on rows quantized once beforehand (as a model's fused norm step leaves them)
+        self.prepared = [ctypes_arr(q._Proj, [q._Proj(self.imgs[c][i].data_ptr(), n, k,
+                                                      self.wss[LAYER_SRC.get(nm, 0)].data_ptr(),
+                                                      self.wss[LAYER_SRC.get(nm, 0)].numel(), self.ys[i].data_ptr())
+                                              for i, (nm, n, k) in enumerate(self.layer)])
+                         for c in range(self.copies)]
         # launches of one step: the GEMV set, plus one quantize launch above the fused row count
         self.launches = 1 if rows <= q.FUSED_ROWS else 2
 
@@ -684,7 +682,7 @@ def layer_entry(torch, q, L, sh, stream, timer, rc, ls, name, lane, rows, wl_key
     prepared once)."""
     set_reps = time_reps(torch, timer, stream,
                          lambda i: L.qgemv_set_rows(ls.fmt, ls.projs[i % ls.copies], 7, rows, sh), 100)
-    if ls.prepared is None:
+    if rows <= q.FUSED_ROWS:
         kreps, kname = set_reps, "rl_set_kernel"
     else:
         ls.prepare(L, sh)
@@ -780,11 +778,10 @@ def sweep(torch, q, synth, L, sh, stream, timer):
             reps = time_reps(torch, timer, stream,
                              lambda i: L.qgemv_set_rows(fmt, ls.projs[i % ls.copies], 7, rows, sh), 100)
             out.append(entry(f"{lname} (7 projections)", lane, rows, ls.wbytes, reps, ls.launches))
-            if ls.prepared is not None:
-                ls.prepare(L, sh)
-                reps = time_reps(torch, timer, stream,
-                                 lambda i: L.qgemv_set(fmt, ls.prepared[i % ls.copies], 7, rows, sh), 100)
-                out.append(entry(f"{lname} (7 projections), prepared rows", lane, rows, ls.wbytes, reps, 1))
+            ls.prepare(L, sh)
+            reps = time_reps(torch, timer, stream,
+                             lambda i: L.qgemv_set(fmt, ls.prepared[i % ls.copies], 7, rows, sh), 100)
+            out.append(entry(f"{lname} (7 projections), prepared rows", lane, rows, ls.wbytes, reps, 1))
         del ls
     # LM head in every lane
     for lane in ("q8_0", "q4_0", "q4_k", "f16", "fp8"):
@@ -956,7 +953,7 @@ def profile_one(args, torch, q, synth, L, sh, stream, timer):
         lay, fmt, wid = ((LAYER_1B, q.Q8_0, 1) if wl.startswith("layer-1b") else
                          (LAYER_3B, q.Q4_K, 5) if wl.startswith("layer-3b-q4k") else (LAYER_3B, q.Q4_0, 2))
         ls = LayerSet(torch, q, synth, lay, fmt, wid, rows)
-        if wl.endswith("-prepared") and ls.prepared is not None:
+        if wl.endswith("-prepared"):
             ls.prepare(L, sh)
             fn = lambda i: L.qgemv_set(fmt, ls.prepared[i % ls.copies], 7, rows, sh)
         else:
