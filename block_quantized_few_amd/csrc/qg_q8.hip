@@ -151,8 +151,10 @@ __device__ __forceinline__ void xq_store(const XQuarterT<GLU>& xv, uint8_t* lds,
   float v[8] = {xv.a.x, xv.a.y, xv.a.z, xv.a.w, xv.c.x, xv.c.y, xv.c.z, xv.c.w};
   if constexpr (GLU) {
     // h = silu(g) * u, the arithmetic of the stand-alone SwiGLU quantization
+    // (two values at a time: all eight at once held 44 more registers, a
+    // workgroup per CU fewer in the grouped launch)
     const float u[8] = {xv.ua.x, xv.ua.y, xv.ua.z, xv.ua.w, xv.uc.x, xv.uc.y, xv.uc.z, xv.uc.w};
-#pragma unroll
+#pragma unroll 2
     for (int i = 0; i < 8; i++) v[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
   }
   unsigned lo, hi;
