@@ -131,6 +131,44 @@ def test_fused_moe_step_other_topk(moe, rows, topk):
     assert torch.equal(yf, y)
 
 
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 8, 9, 16])
+def test_fused_moe_step_plan(moe, rows):
+    """The plan qg_moe_step leaves in its workspace, against the plan rebuilt on the host from its routing:
+    assignments ordered by (expert, assignment), one work item per touched expert (those of at most two rows
+    first, each class by expert index) and, at 3-8 rows, the items cut to pieces of two rows.  (Offsets of
+    the workspace's header, sorted and item arrays as the library lays them out: header 256 bytes, then
+    expert, weight, x_index, sorted, items, cut items, each 256-byte aligned.)"""
+    log(f"fused moe plan rows={rows}")
+    x = torch.from_numpy(gauss((rows, HIDDEN), 1.0, WL, 80 + rows).numpy()).cuda()
+    nb = q.moe_workspace_bytes(rows, E, HIDDEN, FFN, TOPK, True)
+    ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+    _, (expert, _), _ = q.moe_step_fused(x, moe["r16"], E, TOPK, moe["gu"], moe["dn"], FFN, ws=ws)
+    ex = expert.cpu().numpy().astype(np.int64)
+    m = ex.size
+    w = ws.cpu().numpy().view(np.int32)
+    o_sorted = 256 + 3 * _a256(4 * m)
+    o_items = o_sorted + _a256(4 * m)
+    o_ditems = o_items + _a256(12 * m)
+    order = sorted(range(m), key=lambda j: (ex[j], j))
+    assert np.array_equal(w[o_sorted // 4:o_sorted // 4 + m], np.array(order))
+    heads = {}
+    for pos, j in enumerate(order):
+        heads.setdefault(ex[j], [pos, 0])[1] += 1
+    small = [(e, st, c) for e, (st, c) in sorted(heads.items()) if c <= 2]
+    big = [(e, st, c) for e, (st, c) in sorted(heads.items()) if c > 2]
+    items = small + big
+    assert list(w[:3]) == [len(items), 0, len(small)]
+    assert np.array_equal(w[o_items // 4:o_items // 4 + 3 * len(items)].reshape(-1, 3), np.array(items))
+    if 3 <= rows <= 8:
+        pieces = [(e, st + 2 * p, min(2, c - 2 * p)) for e, st, c in items for p in range((c + 1) // 2)]
+        assert list(w[16:19]) == [len(pieces), 0, len(pieces)]
+        assert np.array_equal(w[o_ditems // 4:o_ditems // 4 + 3 * len(pieces)].reshape(-1, 3), np.array(pieces))
+
+
 @pytest.mark.parametrize("rows", [2, 8, 16])
 def test_fused_moe_step_with_a_nan_row(moe, rows):
     """A NaN input row routes to experts 0..7 (its logits are NaN) and the step runs through; the other rows
