@@ -131,6 +131,39 @@ def test_fused_moe_step_other_topk(moe, rows, topk):
     assert torch.equal(yf, y)
 
 
+@pytest.mark.parametrize("n_experts", [100, 1000])
+def test_fused_moe_step_other_expert_counts(n_experts):
+    """Expert counts that take the routing's 4- and 16-logits-per-lane forms (100 is not a multiple of 64;
+    1000 plans over 1001 images, the scan's lanes taking 16 experts each), at 1-16 rows and top-8 / top-32,
+    on small experts (hidden 256, ffn 128): the fused step gives the composition's bits, and its routing
+    matches the oracle's."""
+    hidden, ffn, wl = 256, 128, 6
+    router = gauss((n_experts, hidden), 0.05, wl, 0, device="cuda")
+    r16 = q.f16_image(router.half().view(torch.int16))
+    g = gauss(((n_experts + 1) * 2 * ffn, hidden), 0.02, wl, 1, device="cuda")
+    d = gauss(((n_experts + 1) * hidden, ffn), 0.02, wl, 2, device="cuda")
+    gu_b, dn_b = q.image_bytes(q.Q8_0, 2 * ffn, hidden), q.image_bytes(q.Q8_0, hidden, ffn)
+    gu = torch.empty((n_experts + 1) * gu_b, dtype=torch.uint8, device="cuda")
+    dn = torch.empty((n_experts + 1) * dn_b, dtype=torch.uint8, device="cuda")
+    for e in range(n_experts + 1):
+        q.quantize_weights(q.Q8_0, g[e * 2 * ffn:(e + 1) * 2 * ffn], gu[e * gu_b:(e + 1) * gu_b])
+        q.quantize_weights(q.Q8_0, d[e * hidden:(e + 1) * hidden], dn[e * dn_b:(e + 1) * dn_b])
+    for topk in (8, 32):
+        for rows in (1, 2, 3, 8, 9, 16):
+            log(f"fused moe E={n_experts} topk={topk} rows={rows}")
+            x = torch.from_numpy(gauss((rows, hidden), 1.0, wl, 16 + rows).numpy()).cuda()
+            y, (expert, _, weight), logits = q.moe_step(x, r16, n_experts, topk, gu, dn, ffn,
+                                                        shared_expert=n_experts)
+            yf, (expert_f, weight_f), logits_f = q.moe_step_fused(x, r16, n_experts, topk, gu, dn, ffn)
+            assert torch.equal(logits_f, logits)
+            assert torch.equal(expert_f, expert)
+            assert torch.equal(weight_f, weight)
+            assert torch.equal(yf, y)
+            ex_o, _ = O.route_topk(logits.cpu().numpy(), topk)
+            ex = expert.cpu().numpy().reshape(rows, topk + 1)
+            assert np.array_equal(ex[:, :topk], ex_o)
+
+
 def _a256(n):
     return (n + 255) // 256 * 256
 
