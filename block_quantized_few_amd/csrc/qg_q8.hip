@@ -1276,10 +1276,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void mo
 // ------------------------------------------------ MoE down and combine ---
 //
 // One or two rows: the down projection of every assignment and the weighted
-// combine in one launch.  Workgroup w takes output rows 16w .. 16w+15 (one
-// image tile) of every assignment.  A wave task is NA = 4/H assignments and one
-// wave part s; lane h * (64/H) + 16 j + i is lane part h of row i for the
-// task's assignment j.  The activation row of assignment a is the SwiGLU of its
+// combine in one launch.  Workgroup w takes output rows RT w .. RT w + RT - 1
+// (RT = 8 or 16: half an image tile or one) of every assignment.  A wave task
+// is NA = (64/H)/RT assignments and one wave part s; lane h * (64/H) + RT j + i
+// is lane part h of row i for the task's assignment j.  The activation row of assignment a is the SwiGLU of its
 // gate/up row, quantized in staging as the grouped launch's staging does it.
 // A lane sums its blocks in order, the lane parts and then the wave parts
 // follow the lanes-own-rows kernel's tree, so each assignment's output has the
@@ -1306,18 +1306,24 @@ struct DownCombine {
 
 constexpr int MDC_LA = 8;          // blocks in flight per lane
 constexpr int MDC_MAX_WAVES = 12;  // one wave task per wave; three waves a SIMD (170 registers)
+// output rows a workgroup: half an image tile at one row (twice the
+// workgroups over the CUs; at two rows each would stage twice the SwiGLU
+// values for as many weights), the whole tile at two
+__host__ __device__ constexpr int mdc_lgrt(int rows) { return rows == 1 ? 3 : 4; }
 
+template <int LG>  // rows per workgroup: 1 << LG (8 or 16) of an image tile
 __global__ __launch_bounds__(MDC_MAX_WAVES * WAVE) void moe_down_combine_kernel(DownCombine a) {
+  constexpr int RT = 1 << LG;
   extern __shared__ __align__(16) uint8_t lds[];
   const int m = a.rows * a.slots, kbp = a.kbp;
   const PartPlan& pl = a.pl;
   uint8_t* xq = lds;                                                  // [m][kbp] x 32 codes
   float* xd = reinterpret_cast<float*>(lds + (size_t)m * kbp * 32);  // [m][kbp] scales
-  float* red = xd + (size_t)m * kbp;                                  // [m][16][S] wave-part sums
+  float* red = xd + (size_t)m * kbp;                                  // [m][RT][S] wave-part sums
   const int nt = (int)blockDim.x, tid = (int)threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (WAVE - 1);
-  const int lg_rpw = 6 - pl.lgH, na = 1 << (lg_rpw - 4);
-  const int h = lane >> lg_rpw, j = (lane >> 4) & (na - 1), i = lane & 15;
+  const int lg_rpw = 6 - pl.lgH, na = 1 << (lg_rpw - LG);
+  const int h = lane >> lg_rpw, j = (lane >> LG) & (na - 1), i = lane & (RT - 1);
   const int s = wave & (pl.S - 1), ag = wave >> pl.lgS;
   const int aa = ag * na + j;
   const bool on = wave < a.tasks && aa < m;
@@ -1361,12 +1367,13 @@ __global__ __launch_bounds__(MDC_MAX_WAVES * WAVE) void moe_down_combine_kernel(
   gu_load(tid + nt, gv2, uv2);  // a second round's (two rows), always loaded: no branch around loads
   const bool ev = (unsigned)e < (unsigned)a.n_images;  // a plan entry out of range adds nothing
   e = ev ? e : 0;
-  const int64_t row0 = (int64_t)blockIdx.x * TILE;
+  const int64_t row0 = (int64_t)blockIdx.x * RT;
   const uint8_t* img = a.images + (size_t)e * (size_t)a.expert_bytes;
   const size_t c0 = (size_t)(row0 >> 4) * (size_t)kbp;  // the tile's first cell
   const uint8_t* tcode = img + c0 * 512;
   const uint16_t* tscale = reinterpret_cast<const uint16_t*>(img + a.scale_off) + c0 * TILE;
-  const uint32_t woff = (uint32_t)i * 16u, soff = (uint32_t)i;
+  const int ti = (int)(row0 & 15) + i;  // the lane's row in the image tile
+  const uint32_t woff = (uint32_t)ti * 16u, soff = (uint32_t)ti;
   const int bpart = s * pl.H * pl.BS + h;
   const bool task = wave < a.tasks;  // uniform: waves past the tasks only stage
   WBlock<FMT_Q8> w[MDC_LA];
@@ -1397,14 +1404,14 @@ __global__ __launch_bounds__(MDC_MAX_WAVES * WAVE) void moe_down_combine_kernel(
   }
   // lane parts: ((h0 + h1) + (h2 + h3)); then the wave parts through LDS
   for (int off = 1 << lg_rpw; off < WAVE; off <<= 1) acc += __shfl_xor(acc, off);
-  if (on && h == 0) red[((size_t)aa * TILE + i) * pl.S + s] = ev ? acc : 0.0f;
+  if (on && h == 0) red[((size_t)aa * RT + i) * pl.S + s] = ev ? acc : 0.0f;
   __syncthreads();
-  if (tid < a.rows * TILE) {
-    const int r = tid >> 4, ri = tid & 15;
+  if (tid < a.rows * RT) {
+    const int r = tid >> LG, ri = tid & (RT - 1);
     float y = 0.0f;
     for (int sl = 0; sl < a.slots; sl++) {
       const int as = r * a.slots + sl;
-      const float* rp = red + ((size_t)as * TILE + ri) * pl.S;
+      const float* rp = red + ((size_t)as * RT + ri) * pl.S;
       float v = rp[0];
       for (int s2 = 1; s2 < pl.S; s2++) v += rp[s2];
       y = __builtin_fmaf(a.weight[as], v, y);
@@ -1417,15 +1424,16 @@ __global__ __launch_bounds__(MDC_MAX_WAVES * WAVE) void moe_down_combine_kernel(
 // launch shape.
 static bool down_combine_shape(int rows, int slots, int64_t hidden, int64_t ffn, DownCombine& dc, size_t& lds) {
   if (rows < 1 || rows > 2 || hidden % TILE) return false;
+  const int rt = 1 << mdc_lgrt(rows);
   const int kbp = (int)kbp_of(ffn);
   const PartPlan pl = part_plan(kbp);
-  if (pl.H > 4) return false;  // rows of a wave part: 64 / H >= 16
-  const int m = rows * slots, na = 4 / pl.H;
+  if (pl.H > 4) return false;  // rows of a wave part (64 / H) at least 16
+  const int m = rows * slots, na = (WAVE / pl.H) / rt;
   const int tasks = (m + na - 1) / na * pl.S;
   const int quads = (m * kbp * 4 + WAVE - 1) / WAVE;  // staging waves at one quarter a thread
   const int waves = tasks > (quads + 1) / 2 ? tasks : (quads + 1) / 2;
   if (waves > MDC_MAX_WAVES) return false;
-  lds = (size_t)m * kbp * 36 + (size_t)m * TILE * pl.S * 4;
+  lds = (size_t)m * kbp * 36 + (size_t)m * rt * pl.S * 4;
   if (lds > 64 * 1024) return false;
   dc.n = hidden;
   dc.kbp = kbp;
@@ -1461,10 +1469,11 @@ int launch_moe_down_combine(const void* images, int n_images, int64_t hidden, in
   dc.expert = expert;
   dc.weight = weight;
   dc.y = y;
+  const int lg = mdc_lgrt(rows);
+  auto kern = lg == 3 ? moe_down_combine_kernel<3> : moe_down_combine_kernel<4>;
   if (lds > 48 * 1024)
-    (void)hipFuncSetAttribute((const void*)moe_down_combine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
-  hipLaunchKernelGGL(moe_down_combine_kernel, dim3((unsigned)(hidden / TILE)), dim3(dc.waves * WAVE), lds, s, dc);
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(hidden >> lg)), dim3(dc.waves * WAVE), lds, s, dc);
   return hip_status(hipGetLastError(), "moe_down_combine_kernel");
 }
 
