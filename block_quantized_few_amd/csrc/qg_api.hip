@@ -552,12 +552,35 @@ int qg_moe_step_fp8(const void* router_image, int n_experts, int64_t hidden, int
   int* items = (int*)(w + M.items);
   float* gu = (float*)(w + M.gu);
   float* o = (float*)(w + M.o);
-  if (int st = launch_gemv_f16(router_image, n_experts, hidden, x, rows, lg, s)) return st;
-  if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted, items,
-                               x, hidden, w + M.xprep, true, s))
-    return st;
-  if (int st = launch_grouped_fp8(gu_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi, m, gu, s))
-    return st;
+  if (rows <= MOE_UP_PLAN_ROWS && moe_up_fp8_fits(2 * ffn, hidden, rows)) {
+    // the router launch with the input rows' FP8 groups beside it, then the
+    // gate/up launch planning for itself (a row a wave): no plan launch
+    if (int st = launch_moe_router(router_image, n_experts, hidden, x, rows, lg, w + M.xprep, s, true)) return st;
+    MoeUp up;
+    up.logits = lg;
+    up.rows = rows;
+    up.E = n_experts;
+    up.topk = topk;
+    up.shared = shared;
+    up.expert = ex;
+    up.weight = wt;
+    up.x_index = xi;
+    up.header = header;
+    up.sorted = sorted;
+    up.items = items;
+    up.dheader = nullptr;
+    up.ditems = nullptr;
+    up.plan_off = 0;
+    if (int st = launch_moe_up_fp8(gu_images, 2 * ffn, hidden, w + M.xprep, up, gu, s)) return st;
+  } else {
+    if (int st = launch_gemv_f16(router_image, n_experts, hidden, x, rows, lg, s)) return st;
+    if (int st = launch_moe_plan(lg, rows, n_experts, topk, shared ? n_experts : -1, ex, wt, xi, header, sorted,
+                                 items, x, hidden, w + M.xprep, true, s))
+      return st;
+    if (int st = launch_grouped_fp8(gu_images, 2 * ffn, hidden, w + M.xprep, rows, header, sorted, items, xi, m,
+                                    gu, s))
+      return st;
+  }
   if (int st = launch_swiglu_fp8(gu, m, ffn, w + M.hprep, s)) return st;
   if (int st = launch_grouped_fp8(down_images, hidden, ffn, w + M.hprep, m, header, sorted, items, nullptr, m, o, s))
     return st;

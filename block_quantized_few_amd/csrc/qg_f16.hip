@@ -236,26 +236,42 @@ __global__ __launch_bounds__(16 * WAVE) void moe_router_kernel(const uint16_t* _
                                                                const float* __restrict__ x, int R,
                                                                float* __restrict__ y, int64_t groups, int gemv_wgs,
                                                                int8_t* __restrict__ xq, float* __restrict__ xd,
-                                                               int* __restrict__ xn) {
+                                                               int* __restrict__ xn, uint8_t* __restrict__ fcodes,
+                                                               float* __restrict__ fscales) {
   if ((int)blockIdx.x < gemv_wgs) {
     gemv_f16_groups<1, 16, 4>(img, N, K, x, R, y, groups, blockIdx.x, gemv_wgs);
     return;
   }
-  plan_prepare_q8(x, R, K, xq, xd, xn, (int)blockIdx.x - gemv_wgs);
+  if (fcodes) plan_prepare_fp8(x, R, K, fcodes, fscales, (int)blockIdx.x - gemv_wgs);
+  else plan_prepare_q8(x, R, K, xq, xd, xn, (int)blockIdx.x - gemv_wgs);
 }
 
 int launch_moe_router(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, void* xprep,
-                      hipStream_t s) {
+                      hipStream_t s, bool fp8) {
   const int64_t groups = f16_tiles(n);
   if (groups >= 256) return fail(QG_ELAUNCH, "router of %lld experts: at most 4095", (long long)n);
-  const PrepLayout L = prep_layout_rows(rows, k);
   uint8_t* w = static_cast<uint8_t*>(xprep);
-  const int64_t quads = (int64_t)rows * kbp_of(k) * 4;
+  int8_t* xq = nullptr;
+  float* xd = nullptr;
+  int* xn = nullptr;
+  uint8_t* fc = nullptr;
+  float* fs = nullptr;
+  // threads of the A1 workgroups: four a 32-block, or (FP8) a wave a 1 x 128 group
+  int64_t quads;
+  if (fp8) {
+    fc = w;
+    fs = reinterpret_cast<float*>(w + fp8_ws_scale_offset(rows, k));
+    quads = (int64_t)rows * (k / 128) * WAVE;
+  } else {
+    const PrepLayout L = prep_layout_rows(rows, k);
+    xq = reinterpret_cast<int8_t*>(w + L.codes);
+    xd = reinterpret_cast<float*>(w + L.dx);
+    xn = reinterpret_cast<int*>(w + L.nsx);
+    quads = (int64_t)rows * kbp_of(k) * 4;
+  }
   const unsigned a1 = (unsigned)((quads + 1023) / 1024);
   hipLaunchKernelGGL(moe_router_kernel, dim3((unsigned)groups + a1), dim3(16 * WAVE), 0, s,
-                     static_cast<const uint16_t*>(image), n, k, x, rows, y, groups, (int)groups,
-                     reinterpret_cast<int8_t*>(w + L.codes), reinterpret_cast<float*>(w + L.dx),
-                     reinterpret_cast<int*>(w + L.nsx));
+                     static_cast<const uint16_t*>(image), n, k, x, rows, y, groups, (int)groups, xq, xd, xn, fc, fs);
   return hip_status(hipGetLastError(), "moe_router_kernel");
 }
 

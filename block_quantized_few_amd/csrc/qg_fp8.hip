@@ -24,6 +24,7 @@
 #include "qg_device.h"
 #include "qg_internal.h"
 #include "qg_launch.h"
+#include "qg_route.h"
 
 namespace qg {
 
@@ -330,20 +331,23 @@ int launch_gemv_fp8(const void* image, int64_t n, int64_t k, const void* ws, int
 // the wave split are those of gemv_fp8_kernel for the same n (S set by the
 // tile count alike), so each assignment's output has the bits of the
 // one-row dense call on its row.
+// The (item, tile group) units of a grouped FP8 launch, nitems items of the
+// plan (sorted, items, x_index: global memory, or the workgroup's LDS).
+// Every thread calls it.
 template <int NT, int S, int LA>
-__global__ __launch_bounds__(S * WAVE) void grouped_fp8_kernel(
-    const uint8_t* __restrict__ images, int64_t expert_bytes, int64_t scale_off, int64_t N, int64_t K,
-    const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, const int* __restrict__ header,
-    const int* __restrict__ sorted, const int* __restrict__ items, const int32_t* __restrict__ x_index,
-    float* __restrict__ y, int64_t tgroups) {
-  __shared__ float red[S * NT * 4 * WAVE];
-  __shared__ int s_map[2 * QG_MAX_ROWS];  // activation row, then output row, of each column
+__device__ __forceinline__ void grouped_fp8_units(const uint8_t* __restrict__ images, int64_t expert_bytes,
+                                                  int64_t scale_off, int64_t N, int64_t K,
+                                                  const uint8_t* __restrict__ xcodes,
+                                                  const float* __restrict__ xscales, int nitems,
+                                                  const int* __restrict__ sorted, const int* __restrict__ items,
+                                                  const int32_t* __restrict__ x_index, float* __restrict__ y,
+                                                  int64_t tgroups, float* red, int* s_map) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
   const int i = lane & 15, q = lane >> 4;
   const int64_t kg = K / F8_GROUP, tiles = (N + 15) / 16;
   const int64_t g0 = kg * wave / S, g1 = kg * (wave + 1) / S;  // this wave's groups
   const int64_t ng = g1 - g0;
-  const int64_t units = (int64_t)header[0] * tgroups;
+  const int64_t units = (int64_t)nitems * tgroups;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {  // uniform over the workgroup
     const int item = (int)(u / tgroups);
     const int64_t grp = u - (int64_t)item * tgroups;
@@ -413,6 +417,40 @@ __global__ __launch_bounds__(S * WAVE) void grouped_fp8_kernel(
 }
 
 template <int NT, int S, int LA>
+__global__ __launch_bounds__(S * WAVE) void grouped_fp8_kernel(
+    const uint8_t* __restrict__ images, int64_t expert_bytes, int64_t scale_off, int64_t N, int64_t K,
+    const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, const int* __restrict__ header,
+    const int* __restrict__ sorted, const int* __restrict__ items, const int32_t* __restrict__ x_index,
+    float* __restrict__ y, int64_t tgroups) {
+  __shared__ float red[S * NT * 4 * WAVE];
+  __shared__ int s_map[2 * QG_MAX_ROWS];  // activation row, then output row, of each column
+  grouped_fp8_units<NT, S, LA>(images, expert_bytes, scale_off, N, K, xcodes, xscales, header[0], sorted, items,
+                               x_index, y, tgroups, red, s_map);
+}
+
+// The FP8 MoE step's gate/up launch up to S rows (a row a wave): every
+// workgroup computes the step's plan from the router logits (moe_plan_block,
+// the same plan in each) into its LDS, workgroup 0 stores it for the down
+// launch, and the units run as in grouped_fp8_kernel on the plan in LDS.
+template <int NT, int S, int LA>
+__global__ __launch_bounds__(S * WAVE) void moe_up_fp8_kernel(const uint8_t* __restrict__ images,
+                                                               int64_t expert_bytes, int64_t scale_off, int64_t N,
+                                                               int64_t K, const uint8_t* __restrict__ xcodes,
+                                                               const float* __restrict__ xscales,
+                                                               float* __restrict__ y, int64_t tgroups, MoeUp up) {
+  __shared__ float red[S * NT * 4 * WAVE];
+  __shared__ int s_map[2 * QG_MAX_ROWS];
+  extern __shared__ __align__(16) uint8_t lds[];  // the plan
+  const int m = up.rows * (up.topk + up.shared);
+  const PlanLds P = plan_carve(lds, m, up.E);
+  moe_plan_block<S * WAVE>(up.logits, up.rows, up.E, up.topk, up.shared != 0, P);
+  if (blockIdx.x == 0)
+    plan_store<S * WAVE>(P, m, up.expert, up.weight, up.x_index, up.header, up.sorted, up.items);
+  grouped_fp8_units<NT, S, LA>(images, expert_bytes, scale_off, N, K, xcodes, xscales, P.misc[0], P.sorted,
+                               P.items, P.xi, y, tgroups, red, s_map);
+}
+
+template <int NT, int S, int LA>
 static void launch_grouped_fp8_t(const uint8_t* images, int64_t eb, int64_t so, int64_t n, int64_t k,
                                  const uint8_t* xc, const float* xs, const int* header, const int* sorted,
                                  const int* items, const int32_t* x_index, int m, float* y, hipStream_t s) {
@@ -447,6 +485,47 @@ int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws,
     default: launch_grouped_fp8_t<2, 1, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s); break;
   }
   return hip_status(hipGetLastError(), "grouped_fp8_kernel");
+}
+
+template <int NT, int S, int LA>
+static void launch_moe_up_fp8_t(const uint8_t* images, int64_t eb, int64_t so, int64_t n, int64_t k,
+                                const uint8_t* xc, const float* xs, const MoeUp& up, float* y, hipStream_t s) {
+  auto kern = moe_up_fp8_kernel<NT, S, LA>;
+  const int64_t tgroups = (f16_tiles(n) + NT - 1) / NT;
+  const int m = up.rows * (up.topk + up.shared);
+  const size_t lds = plan_lds_bytes(m, up.E);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, S * WAVE, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t g = (int64_t)device_cus() * per_cu, units = (int64_t)m * tgroups;  // at most m items
+  hipLaunchKernelGGL(kern, dim3((unsigned)(units < g ? units : g)), dim3(S * WAVE), lds, s, images, eb, so, n, k, xc,
+                     xs, y, tgroups, up);
+}
+
+bool moe_up_fp8_fits(int64_t n, int64_t k, int rows) {
+  return rows >= 1 && rows <= fp8_waves(f16_tiles(n), k / F8_GROUP);
+}
+
+int launch_moe_up_fp8(const void* images, int64_t n, int64_t k, const void* xprep, const MoeUp& up, float* y,
+                      hipStream_t s) {
+  if (!moe_up_fp8_fits(n, k, up.rows))
+    return fail(QG_ELAUNCH, "the FP8 gate/up launch plans at most a row a wave: rows=%d", up.rows);
+  const uint8_t* img = static_cast<const uint8_t*>(images);
+  const int64_t eb = (int64_t)fp8_image_bytes(n, k), so = (int64_t)fp8_scale_offset(n, k);
+  const uint8_t* xc = static_cast<const uint8_t*>(xprep);
+  const float* xs = reinterpret_cast<const float*>(xc + fp8_ws_scale_offset(up.rows, k));
+  // the tiling of launch_grouped_fp8 (the same bits)
+  const int64_t t16 = f16_tiles(n);
+  switch (fp8_waves(t16, k / F8_GROUP)) {
+    case 8: launch_moe_up_fp8_t<2, 8, 2>(img, eb, so, n, k, xc, xs, up, y, s); break;
+    case 4:
+      if (t16 >= 256) launch_moe_up_fp8_t<1, 4, 4>(img, eb, so, n, k, xc, xs, up, y, s);
+      else launch_moe_up_fp8_t<2, 4, 2>(img, eb, so, n, k, xc, xs, up, y, s);
+      break;
+    case 2: launch_moe_up_fp8_t<2, 2, 2>(img, eb, so, n, k, xc, xs, up, y, s); break;
+    default: launch_moe_up_fp8_t<2, 1, 2>(img, eb, so, n, k, xc, xs, up, y, s); break;
+  }
+  return hip_status(hipGetLastError(), "moe_up_fp8_kernel");
 }
 
 }  // namespace qg

@@ -128,8 +128,15 @@ int launch_swiglu_fp8(const float* gu, int m, int64_t ffn, void* hws, hipStream_
 // f16 lane.
 int launch_gemv_f16(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, hipStream_t s);
 // Routed MoE step, first launch: the f16 router GEMV (n < 4096; the bits of
-// launch_gemv_f16) into y, beside it the A1 of x into xprep (row order).
+// launch_gemv_f16) into y, beside it the A1 of x into xprep (row order), or
+// with fp8 its 1 x 128 FP8 groups (the FP8 workspace layout).
 int launch_moe_router(const void* image, int64_t n, int64_t k, const float* x, int rows, float* y, void* xprep,
+                      hipStream_t s, bool fp8 = false);
+// The FP8 MoE step's gate/up launch planning for itself, as launch_moe_up
+// (a row a wave: whether rows fit the launch's waves, moe_up_fp8_fits); xprep
+// holds the input rows' FP8 groups.
+bool moe_up_fp8_fits(int64_t n, int64_t k, int rows);
+int launch_moe_up_fp8(const void* images, int64_t n, int64_t k, const void* xprep, const MoeUp& up, float* y,
                       hipStream_t s);
 int launch_f16_pack(const uint16_t* w, int64_t n, int64_t k, void* image, hipStream_t s);
 int launch_fp8_quantize_weights(const float* w, int64_t n, int64_t k, void* image, hipStream_t s);

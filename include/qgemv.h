@@ -437,7 +437,10 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
  * FP8 groups): as qg_moe_step, with gu_images and down_images FP8 images
  * (qg_image_bytes(QG_FMT_FP8, ...) each, back to back), the input rows and
  * the SwiGLU rows quantized into FP8 groups, and the expert GEMVs those of
- * qgemv_fp8_grouped.  hidden and ffn multiples of 128.  Six launches.  The
+ * qgemv_fp8_grouped.  hidden and ffn multiples of 128.  Six launches; five
+ * when the rows fit the gate/up launch's waves (up to 8 rows on the usual
+ * shapes), which then plans for itself beside the router launch's FP8 input
+ * groups.  The
  * bits are those of the composition: the f16 router GEMV, qg_moe_route,
  * qgemv_fp8_grouped on the gate/up images, qg_swiglu, qgemv_fp8_grouped on
  * the down images (assignment j reading SwiGLU row j), qg_moe_combine.
