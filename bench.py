@@ -877,7 +877,8 @@ def moe_sweep(torch, q, synth, L, sh, stream, timer):
             reps = time_reps(torch, timer, stream, one, 64)
             u = moe_unique(torch, one, expert)
             wb = 2 * MOE_E * MOE_HIDDEN + u * (W["gu_b"] + W["dn_b"])
-            launches = (5 if rows <= 8 else 6) if fmt == q.FP8 else (3 if rows <= 2 else 4 if rows <= 8 else 6)
+            launches = ((4 if rows == 1 else 5 if rows <= 8 else 6) if fmt == q.FP8 else
+                        (3 if rows <= 2 else 4 if rows <= 8 else 6))
             e = entry("routed moe step (256 experts top-8 + shared)", lane, rows, wb, reps, launches)
             e["unique_experts"] = round(u, 2)
             out.append(e)

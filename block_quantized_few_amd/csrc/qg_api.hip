@@ -581,8 +581,15 @@ int qg_moe_step_fp8(const void* router_image, int n_experts, int64_t hidden, int
                                     gu, s))
       return st;
   }
-  if (int st = launch_swiglu_fp8(gu, m, ffn, w + M.hprep, s)) return st;
-  if (int st = launch_grouped_fp8(down_images, hidden, ffn, w + M.hprep, m, header, sorted, items, nullptr, m, o, s))
+  // one row: the down launch takes the SwiGLU of the gate/up rows in its
+  // staging (the rows' FP8 groups in LDS; each unit makes its item's, so with
+  // more rows that costs more than the launch it saves); else a launch
+  // makes them
+  const bool glu = rows == 1 && fp8_glu_fits(ffn);
+  if (!glu)
+    if (int st = launch_swiglu_fp8(gu, m, ffn, w + M.hprep, s)) return st;
+  if (int st = launch_grouped_fp8(down_images, hidden, ffn, w + M.hprep, m, header, sorted, items, nullptr, m, o, s,
+                                  glu ? gu : nullptr))
     return st;
   if (int st = launch_moe_combine(o, wt, rows, slots, hidden, y, s)) return st;
   return ok();

@@ -331,17 +331,27 @@ int launch_gemv_fp8(const void* image, int64_t n, int64_t k, const void* ws, int
 // the wave split are those of gemv_fp8_kernel for the same n (S set by the
 // tile count alike), so each assignment's output has the bits of the
 // one-row dense call on its row.
+// LDS of a grouped FP8 launch that takes the SwiGLU in its staging: the FP8
+// groups of up to 16 rows of k (codes, then fp32 scales).
+static inline size_t fp8_glu_lds_bytes(int64_t k) { return (size_t)QG_MAX_ROWS * ((size_t)k + (size_t)(k / F8_GROUP) * 4); }
+bool fp8_glu_fits(int64_t k) { return fp8_glu_lds_bytes(k) <= 40 * 1024; }
+
 // The (item, tile group) units of a grouped FP8 launch, nitems items of the
 // plan (sorted, items, x_index: global memory, or the workgroup's LDS).
-// Every thread calls it.
-template <int NT, int S, int LA>
+// Every thread calls it.  GLU: a unit's activation rows are the SwiGLU of
+// the item's gate/up rows of glu ([m][2K]: gate values, then up values),
+// put in FP8 groups in the workgroup's LDS (hst: codes [16][K], then scales
+// [16][K/128]) with the arithmetic of swiglu_fp8_kernel, so the SwiGLU
+// launch goes; xcodes / xscales are not read.
+template <int NT, int S, int LA, bool GLU = false>
 __device__ __forceinline__ void grouped_fp8_units(const uint8_t* __restrict__ images, int64_t expert_bytes,
                                                   int64_t scale_off, int64_t N, int64_t K,
                                                   const uint8_t* __restrict__ xcodes,
                                                   const float* __restrict__ xscales, int nitems,
                                                   const int* __restrict__ sorted, const int* __restrict__ items,
                                                   const int32_t* __restrict__ x_index, float* __restrict__ y,
-                                                  int64_t tgroups, float* red, int* s_map) {
+                                                  int64_t tgroups, float* red, int* s_map,
+                                                  const float* __restrict__ glu = nullptr, uint8_t* hst = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
   const int i = lane & 15, q = lane >> 4;
   const int64_t kg = K / F8_GROUP, tiles = (N + 15) / 16;
@@ -361,9 +371,28 @@ __device__ __forceinline__ void grouped_fp8_units(const uint8_t* __restrict__ im
     __syncthreads();
     const uint8_t* img = images + (int64_t)e * expert_bytes;
     const float* wsc = reinterpret_cast<const float*>(img + scale_off);
-    const int xr = s_map[i < cnt ? i : cnt - 1];  // columns past the item's rows read a real row, store nothing
-    const uint8_t* xc = xcodes + (int64_t)xr * K + 32 * q;
-    const float* xs = xscales + (int64_t)xr * kg;
+    const uint8_t* xc;
+    const float* xs;
+    if constexpr (GLU) {
+      // a wave per (row, group) of the item's rows
+      float* hsc = reinterpret_cast<float*>(hst + QG_MAX_ROWS * K);
+      const int kgi = (int)kg;
+      for (int w = wave; w < cnt * kgi; w += S) {
+        const int r = w / kgi, gi = w - r * kgi;
+        const float* row = glu + (int64_t)s_map[r] * 2 * K + gi * F8_GROUP + 2 * lane;
+        const float2 gv = *reinterpret_cast<const float2*>(row), uv = *reinterpret_cast<const float2*>(row + K);
+        const float2 h = make_float2(gv.x / (1.0f + expf(-gv.x)) * uv.x, gv.y / (1.0f + expf(-gv.y)) * uv.y);
+        fp8_group_store(h, lane, hst + (int64_t)r * K + gi * F8_GROUP, hsc + r * kgi + gi);
+      }
+      __syncthreads();
+      const int xr = i < cnt ? i : cnt - 1;  // columns past the item's rows read a real row, store nothing
+      xc = hst + (int64_t)xr * K + 32 * q;
+      xs = hsc + (int64_t)xr * kg;
+    } else {
+      const int xr = s_map[i < cnt ? i : cnt - 1];  // columns past the item's rows read a real row, store nothing
+      xc = xcodes + (int64_t)xr * K + 32 * q;
+      xs = xscales + (int64_t)xr * kg;
+    }
     const uint8_t* wt[NT];
     const float* wsr[NT];
 #pragma unroll
@@ -416,16 +445,17 @@ __device__ __forceinline__ void grouped_fp8_units(const uint8_t* __restrict__ im
   }
 }
 
-template <int NT, int S, int LA>
+template <int NT, int S, int LA, bool GLU>
 __global__ __launch_bounds__(S * WAVE) void grouped_fp8_kernel(
     const uint8_t* __restrict__ images, int64_t expert_bytes, int64_t scale_off, int64_t N, int64_t K,
     const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, const int* __restrict__ header,
     const int* __restrict__ sorted, const int* __restrict__ items, const int32_t* __restrict__ x_index,
-    float* __restrict__ y, int64_t tgroups) {
+    float* __restrict__ y, int64_t tgroups, const float* __restrict__ glu) {
   __shared__ float red[S * NT * 4 * WAVE];
   __shared__ int s_map[2 * QG_MAX_ROWS];  // activation row, then output row, of each column
-  grouped_fp8_units<NT, S, LA>(images, expert_bytes, scale_off, N, K, xcodes, xscales, header[0], sorted, items,
-                               x_index, y, tgroups, red, s_map);
+  extern __shared__ __align__(16) uint8_t hst[];  // GLU: the SwiGLU rows' FP8 groups
+  grouped_fp8_units<NT, S, LA, GLU>(images, expert_bytes, scale_off, N, K, xcodes, xscales, header[0], sorted,
+                                    items, x_index, y, tgroups, red, s_map, glu, hst);
 }
 
 // The FP8 MoE step's gate/up launch up to S rows (a row a wave): every
@@ -453,20 +483,24 @@ __global__ __launch_bounds__(S * WAVE) void moe_up_fp8_kernel(const uint8_t* __r
 template <int NT, int S, int LA>
 static void launch_grouped_fp8_t(const uint8_t* images, int64_t eb, int64_t so, int64_t n, int64_t k,
                                  const uint8_t* xc, const float* xs, const int* header, const int* sorted,
-                                 const int* items, const int32_t* x_index, int m, float* y, hipStream_t s) {
-  auto kern = grouped_fp8_kernel<NT, S, LA>;
+                                 const int* items, const int32_t* x_index, int m, float* y, hipStream_t s,
+                                 const float* glu) {
+  auto kern = glu ? grouped_fp8_kernel<NT, S, LA, true> : grouped_fp8_kernel<NT, S, LA, false>;
+  const size_t lds = glu ? fp8_glu_lds_bytes(k) : 0;
   const int64_t tgroups = (f16_tiles(n) + NT - 1) / NT;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, S * WAVE, 0) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, S * WAVE, lds) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int64_t g = (int64_t)device_cus() * per_cu, units = (int64_t)m * tgroups;  // at most m items
-  hipLaunchKernelGGL(kern, dim3((unsigned)(units < g ? units : g)), dim3(S * WAVE), 0, s, images, eb, so, n, k, xc,
-                     xs, header, sorted, items, x_index, y, tgroups);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(units < g ? units : g)), dim3(S * WAVE), lds, s, images, eb, so, n, k, xc,
+                     xs, header, sorted, items, x_index, y, tgroups, glu);
 }
 
 int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws, int x_rows, const int* header,
-                       const int* sorted, const int* items, const int32_t* x_index, int m, float* y, hipStream_t s) {
+                       const int* sorted, const int* items, const int32_t* x_index, int m, float* y, hipStream_t s,
+                       const float* glu) {
   if (m == 0) return QG_OK;
+  if (glu && !fp8_glu_fits(k)) return fail(QG_ELAUNCH, "SwiGLU rows staged in LDS: k=%lld too long", (long long)k);
   const uint8_t* img = static_cast<const uint8_t*>(images);
   const int64_t eb = (int64_t)fp8_image_bytes(n, k), so = (int64_t)fp8_scale_offset(n, k);
   const uint8_t* xc = static_cast<const uint8_t*>(ws);
@@ -476,13 +510,13 @@ int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws,
   // for their fixed costs (1024 x 2048 experts at 16 rows: 63.0 -> 51.8 us)
   const int64_t t16 = f16_tiles(n);
   switch (fp8_waves(t16, k / F8_GROUP)) {
-    case 8: launch_grouped_fp8_t<2, 8, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s); break;
+    case 8: launch_grouped_fp8_t<2, 8, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s, glu); break;
     case 4:
-      if (t16 >= 256) launch_grouped_fp8_t<1, 4, 4>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
-      else launch_grouped_fp8_t<2, 4, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s);
+      if (t16 >= 256) launch_grouped_fp8_t<1, 4, 4>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s, glu);
+      else launch_grouped_fp8_t<2, 4, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s, glu);
       break;
-    case 2: launch_grouped_fp8_t<2, 2, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s); break;
-    default: launch_grouped_fp8_t<2, 1, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s); break;
+    case 2: launch_grouped_fp8_t<2, 2, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s, glu); break;
+    default: launch_grouped_fp8_t<2, 1, 2>(img, eb, so, n, k, xc, xs, header, sorted, items, x_index, m, y, s, glu); break;
   }
   return hip_status(hipGetLastError(), "grouped_fp8_kernel");
 }

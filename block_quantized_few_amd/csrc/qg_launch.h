@@ -65,7 +65,11 @@ int launch_grouped_plan(const int32_t* expert, const int32_t* x_index, int m, in
 // (expert_bytes apart), activation groups of x_rows rows at `ws` (the FP8
 // workspace layout), y [m][n].
 int launch_grouped_fp8(const void* images, int64_t n, int64_t k, const void* ws, int x_rows, const int* header,
-                       const int* sorted, const int* items, const int32_t* x_index, int m, float* y, hipStream_t s);
+                       const int* sorted, const int* items, const int32_t* x_index, int m, float* y, hipStream_t s,
+                       const float* glu = nullptr);
+// Whether a grouped FP8 launch of this k can take the SwiGLU of gate/up rows
+// in its staging (glu: the rows' FP8 groups kept in LDS).
+bool fp8_glu_fits(int64_t k);
 
 // Grouped GEMV on a plan already in `ws` (header, sorted, items at the
 // grouped layout's offsets) and rows prepared at `prep` in row order;

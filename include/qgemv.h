@@ -440,7 +440,8 @@ int qg_moe_step(const void* router_image, int n_experts, int64_t hidden, int64_t
  * qgemv_fp8_grouped.  hidden and ffn multiples of 128.  Six launches; five
  * when the rows fit the gate/up launch's waves (up to 8 rows on the usual
  * shapes), which then plans for itself beside the router launch's FP8 input
- * groups.  The
+ * groups; four at one row, where the down launch also takes the SwiGLU of the
+ * gate/up rows in its staging (ffn up to 2048).  The
  * bits are those of the composition: the f16 router GEMV, qg_moe_route,
  * qgemv_fp8_grouped on the gate/up images, qg_swiglu, qgemv_fp8_grouped on
  * the down images (assignment j reading SwiGLU row j), qg_moe_combine.

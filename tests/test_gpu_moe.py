@@ -251,8 +251,9 @@ def moe8():
 @pytest.mark.parametrize("rows", [1, 2, 5, 8, 9, 16])
 def test_fp8_moe_step_equals_composition(moe8, rows):
     """qg_moe_step_fp8 (up to 8 rows the gate/up launch plans for itself, beside the router launch's FP8 input
-    groups) gives the bits of the composition of the separate calls (f16 router GEMV, routing, FP8 grouped
-    gate/up, SwiGLU, FP8 grouped down, combine), call after call through one workspace."""
+    groups; at one row the down launch makes the SwiGLU's FP8 groups in its staging) gives the bits of the
+    composition of the separate calls (f16 router GEMV, routing, FP8 grouped gate/up, SwiGLU, FP8 grouped down,
+    combine), call after call through one workspace."""
     log(f"fp8 moe rows={rows}")
     x = torch.from_numpy(gauss((rows, H8), 1.0, WL8, 32 + rows).numpy()).cuda()
     y, (expert, _, weight), logits = q.moe_step_fp8(x, moe8["r16"], E8, TOPK, moe8["gu"], moe8["dn"], F8,
