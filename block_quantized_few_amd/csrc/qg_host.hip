@@ -37,20 +37,20 @@ int hip_status(hipError_t e, const char* what) {
 
 int check_device() {
   static std::mutex mu;
-  static std::vector<int> verdict;  // per device: 0 unknown, 1 gfx950, -1 other
+  static std::vector<int> arch_ok;  // per device: 0 unknown, 1 gfx950, -1 other
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(QG_EDEVICE, "no HIP device: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lk(mu);
-  if ((int)verdict.size() <= dev) verdict.resize(dev + 1, 0);
-  if (verdict[dev] == 0) {
+  if ((int)arch_ok.size() <= dev) arch_ok.resize(dev + 1, 0);
+  if (arch_ok[dev] == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(QG_EDEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-    verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-    if (verdict[dev] < 0) return fail(QG_EDEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (arch_ok[dev] < 0) return fail(QG_EDEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
   }
-  if (verdict[dev] < 0) return fail(QG_EDEVICE, "device %d is not gfx950", dev);
+  if (arch_ok[dev] < 0) return fail(QG_EDEVICE, "device %d is not gfx950", dev);
   return QG_OK;
 }
 
