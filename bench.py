@@ -320,8 +320,8 @@ class LayerSet:
                                                       self.wss[LAYER_SRC.get(nm, 0)].numel(), self.ys[i].data_ptr())
                                               for i, (nm, n, k) in enumerate(self.layer)])
                          for c in range(self.copies)]
-        # launches of one step: the GEMV set, plus one quantize launch above the fused row count
-        self.launches = 1 if rows <= q.FUSED_ROWS else 2
+        # launches of one step: the GEMV set, plus one quantize launch where the set does not quantize inside
+        self.launches = 1 if q.set_fuses(self.fmt, rows) else 2
 
     def prepare(self, L, sh):
         acts = ctypes_arr(self.q._Act, [self.q._Act(x.data_ptr(), x.shape[1], w.data_ptr(), w.numel())
@@ -331,10 +331,10 @@ class LayerSet:
     def alg_bytes_gemv(self):
         """Algorithmic bytes of the GEMV launch: weights + activations + fp32 outputs.
 
-        Fused (rows <= FUSED_ROWS): each distinct fp32 activation set is read once.  Otherwise the launch
+        Quantizing inside (set_fuses): each distinct fp32 activation set is read once.  Otherwise the launch
         reads q8 rows (codes + fp32 scales, + int32 code sums for Q4_0) per projection."""
         out = sum(self.rows * n * 4 for _, n, _k in self.layer)
-        if self.rows <= self.q.FUSED_ROWS:
+        if self.q.set_fuses(self.fmt, self.rows):
             srcs = {}
             for name, _n, k in self.layer:
                 srcs[LAYER_SRC.get(name, 0)] = k
@@ -678,17 +678,17 @@ def secondary(torch, q, synth, L, sh, stream, timer, rc, note):
 
 def layer_entry(torch, q, L, sh, stream, timer, rc, ls, name, lane, rows, wl_key):
     """A decode layer's seven projections at `rows` rows: the set (ms per projection set, quantization
-    included) and its GEMV kernel's roofline (the set launch itself at 1-2 rows; otherwise the GEMV on rows
-    prepared once)."""
+    included) and its GEMV kernel's roofline (the set launch itself where it quantizes inside; otherwise the GEMV
+    on rows prepared once)."""
     set_reps = time_reps(torch, timer, stream,
                          lambda i: L.qgemv_set_rows(ls.fmt, ls.projs[i % ls.copies], 7, rows, sh), 100)
-    if rows <= q.FUSED_ROWS:
+    if q.set_fuses(ls.fmt, rows):
         kreps, kname = set_reps, "rl_set_kernel"
     else:
         ls.prepare(L, sh)
         kreps = time_reps(torch, timer, stream,
                           lambda i: L.qgemv_set(ls.fmt, ls.prepared[i % ls.copies], 7, rows, sh), 100)
-        kname = "mp_set_kernel"
+        kname = "rl_set_kernel" if rows <= q.FUSED_ROWS else "mp_set_kernel"
     wl = f"{wl_key}-rows{rows}"
     med = statistics.median(set_reps)
     return {"workload": f"{name} (7 projections)", "lane": lane, "rows": rows, "weight_bytes": int(ls.wbytes),

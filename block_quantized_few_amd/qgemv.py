@@ -20,6 +20,12 @@ MAX_ASSIGN = 2048
 MAX_SET = 8
 FUSED_ROWS = 2
 
+
+def set_fuses(fmt, rows):
+    """Whether qgemv_set_rows quantizes inside its GEMV launch when every projection brings a workspace (and its
+    rows fit the launch's staging area): at 1-2 rows, except Q4_0 and Q4_K at two rows."""
+    return 1 <= rows <= FUSED_ROWS and not (rows == 2 and fmt != Q8_0)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 _lib = None

@@ -244,21 +244,23 @@ def test_grouped_empty_assignment_list():
 
 
 def test_set_rows_equals_single_calls():
-    """The fp32-rows set launch (quantization fused for 1-2 rows, one shared quantize launch otherwise) gives
-    the same bits as one call per projection."""
+    """The fp32-rows set launch (quantization inside it at 1-2 rows, one shared quantize launch otherwise, and
+    for Q4_0 at two rows when every projection brings a workspace) gives the same bits as one call per
+    projection."""
     layer = [(2048, 1024), (512, 1024), (1024, 4096), (300, 800)]
     for fmt, ofmt in FMTS:
         imgs = [oracle_image(ofmt, gauss((n, k), 0.02, 21, i).numpy())[1] for i, (n, k) in enumerate(layer)]
         for rows in (1, 2, 3, 5, 16):
-            log(f"set_rows fmt={fmt} rows={rows}")
             xs = {k: torch.from_numpy(gauss((rows, k), 1.0, 21, 32 + k % 97).numpy()).cuda() for _, k in layer}
-            wss = {k: q.empty_ws(rows, k) for _, k in layer}
-            projs, singles = [], []
             fn = q.qgemv_q8_0 if fmt == q.Q8_0 else q.qgemv_q4_0
-            for (n, k), img in zip(layer, imgs):
-                y = torch.full((rows, n), float("nan"), device="cuda")
-                projs.append((img, n, k, xs[k], None if rows <= q.FUSED_ROWS else wss[k], y))
-                singles.append(fn(img, n, k, xs[k]))
-            q.qgemv_set_rows(fmt, projs, rows)
-            for p, ys in zip(projs, singles):
-                assert np.array_equal(bits(p[5]), bits(ys))
+            singles = [fn(img, n, k, xs[k]) for (n, k), img in zip(layer, imgs)]
+            for with_ws in ((False, True) if rows <= q.FUSED_ROWS else (True,)):
+                log(f"set_rows fmt={fmt} rows={rows} workspaces={with_ws}")
+                wss = {k: q.empty_ws(rows, k) for _, k in layer}
+                projs = []
+                for (n, k), img in zip(layer, imgs):
+                    y = torch.full((rows, n), float("nan"), device="cuda")
+                    projs.append((img, n, k, xs[k], wss[k] if with_ws else None, y))
+                q.qgemv_set_rows(fmt, projs, rows)
+                for p, ys in zip(projs, singles):
+                    assert np.array_equal(bits(p[5]), bits(ys))
