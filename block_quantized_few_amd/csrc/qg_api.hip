@@ -258,14 +258,16 @@ int qgemv_set_rows(int fmt, const qg_proj_rows* projs, int count, int rows, qg_s
   bool fuse = true;
   for (int i = 0; i < count; i++) fuse = fuse && fuses_quantization(fmt, rows, projs[i].k);
   // Q4_0 and Q4_K at two rows: when every projection brings a workspace large
-  // enough, one quantize launch and the GEMV on prepared rows beat quantizing
-  // inside the set launch, whose workgroups (about one tile each) each stage
-  // their projection's two rows against few weight bytes (3B-shaped set: Q4_0
+  // enough and aligned (else, as at one row, ws is not used), one quantize
+  // launch and the GEMV on prepared rows beat quantizing inside the set
+  // launch, whose workgroups (about one tile each) each stage their
+  // projection's two rows against few weight bytes (3B-shaped set: Q4_0
   // 18.2 -> 17.2 us, Q4_K 23.1 -> 20.4); the results are the same bits
   if (fuse && rows == 2 && fmt != QG_FMT_Q8_0) {
     bool all_ws = true;
     for (int i = 0; i < count; i++)
-      all_ws = all_ws && projs[i].ws && projs[i].ws_bytes >= prep_layout(rows, projs[i].k).total;
+      all_ws = all_ws && projs[i].ws && aligned(projs[i].ws, 256) &&
+               projs[i].ws_bytes >= prep_layout(rows, projs[i].k).total;
     fuse = !all_ws;
   }
   ProjArg pa[QG_MAX_SET];

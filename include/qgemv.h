@@ -335,8 +335,9 @@ int qgemv_set(int fmt, const qg_proj* projs /*host*/, int count, int rows, qg_st
  * distinct (x, ws) pair into its ws (qg_workspace_bytes(rows, k) bytes;
  * projections that share x may share ws) and a second runs all GEMVs.  Q4_0
  * and Q4_K at two rows take the two launches whenever every projection
- * brings a ws of at least qg_workspace_bytes(rows, k) (faster there), and the
- * one launch when any does not; the outputs are the same bits either way.
+ * brings a 256-aligned ws of at least qg_workspace_bytes(rows, k) (faster
+ * there), and the one launch when any does not; the outputs are the same
+ * bits either way.
  * 1 <= count <= QG_MAX_SET. */
 typedef struct {
   const void* w_image;

@@ -254,13 +254,16 @@ def test_set_rows_equals_single_calls():
             xs = {k: torch.from_numpy(gauss((rows, k), 1.0, 21, 32 + k % 97).numpy()).cuda() for _, k in layer}
             fn = q.qgemv_q8_0 if fmt == q.Q8_0 else q.qgemv_q4_0
             singles = [fn(img, n, k, xs[k]) for (n, k), img in zip(layer, imgs)]
-            for with_ws in ((False, True) if rows <= q.FUSED_ROWS else (True,)):
+            # workspaces: none, of this row count's size, or (two rows) of one row's size, which the set does
+            # not use, quantizing inside the launch as it does without
+            for with_ws in (("none", "full") + (("small",) if rows == 2 else ()) if rows <= q.FUSED_ROWS
+                            else ("full",)):
                 log(f"set_rows fmt={fmt} rows={rows} workspaces={with_ws}")
-                wss = {k: q.empty_ws(rows, k) for _, k in layer}
+                wss = {k: q.empty_ws(1 if with_ws == "small" else rows, k) for _, k in layer}
                 projs = []
                 for (n, k), img in zip(layer, imgs):
                     y = torch.full((rows, n), float("nan"), device="cuda")
-                    projs.append((img, n, k, xs[k], wss[k] if with_ws else None, y))
+                    projs.append((img, n, k, xs[k], None if with_ws == "none" else wss[k], y))
                 q.qgemv_set_rows(fmt, projs, rows)
                 for p, ys in zip(projs, singles):
                     assert np.array_equal(bits(p[5]), bits(ys))
